@@ -1,0 +1,421 @@
+"""Plain CPU oracle of the DFlash drafter hot path (numpy, fp64).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's
+CPU-baseline leg may import this module. The GPU library never calls it and
+shares no code with it.
+
+Sources (the four web pages on DFlash):
+  [Tut]  A3-dflash tutorial (CCODING04 llm-paper-tutorials)
+  [Sum]  papercache summary "DFlash: Block Diffusion for Flash Speculative Decoding"
+  [Note] tom-jerr paper-reading notes "DFLASH"
+  [Code] txtmix code-reading article on the z-lab dflash repository
+
+Every function below is the plain definition of one step, written in fp64
+with numpy; matrix products use numpy's matmul as a library step. Inputs that
+are stored in bf16 on the GPU arrive here as float arrays holding the same
+bf16 values.
+
+Readings taken where the pages are silent (also listed in the design notes):
+  * decoder layer = pre-norm RMSNorm -> attention -> residual, RMSNorm ->
+    SwiGLU -> residual; final RMSNorm before the LM head; no biases; no QK norm;
+  * RoPE is rotate-half over pairs (d, d + hd/2), inv_freq_d = theta^(-2d/hd);
+  * GQA: query head a reads kv head a // (Hq/Hkv);
+  * argmax ties go to the lowest index (numpy.argmax / torch.argmax rule);
+  * Philox4x64-10 counter layout and the inverse-CDF sampler of verify_pq.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def target_layer_ids(n_target_layers: int, n_feat: int) -> List[int]:
+    """[Code] section 5 (build_target_layer_ids): n_feat ids spread evenly over
+    the 0-based range 1 .. n_target_layers-3; the middle layer if n_feat == 1.
+    Grid points are rounded to the nearest integer (halves up)."""
+    if n_feat == 1:
+        return [n_target_layers // 2]
+    lo, hi = 1.0, float(n_target_layers - 3)
+    step = (hi - lo) / (n_feat - 1)
+    return [int(np.floor(lo + i * step + 0.5)) for i in range(n_feat)]
+
+
+def rms_norm(x, gain, eps):
+    """[Tut] section 2.1.1 (SimpleRMSNorm): x / sqrt(mean(x^2) + eps) * gain,
+    eps inside the square root, gain applied after the division."""
+    x = np.asarray(x, dtype=F64)
+    rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x / rms * np.asarray(gain, dtype=F64)
+
+
+def linear(x, w, chunk_rows: int = 16384):
+    """y = x @ w.T for a weight in [out, in] layout (nn.Linear convention).
+
+    The output columns are computed in slices of ``chunk_rows`` weight rows only
+    to bound the fp64 temporary; each output is the same full dot product."""
+    x = np.asarray(x, dtype=F64)
+    n_out = w.shape[0]
+    out = np.empty(x.shape[:-1] + (n_out,), dtype=F64)
+    for r0 in range(0, n_out, chunk_rows):
+        wc = np.asarray(w[r0:r0 + chunk_rows], dtype=F64)
+        out[..., r0:r0 + chunk_rows] = x @ wc.T
+    return out
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def softmax(x, axis=-1):
+    x = np.asarray(x, dtype=F64)
+    m = np.max(x, axis=axis, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# S1: target-context fusion
+# ----------------------------------------------------------------------------
+
+def fuse_context(feats: Sequence, w_c, gain, eps: float = 1e-6):
+    """H_t = RMSNorm(W_c [H^(l1); ...; H^(l5)]).
+
+    [Tut] section 2.1.1 (concat of the sampled layers along the hidden axis,
+    then the fc projection and RMSNorm) and section 2.1.2 (the H_t equation);
+    [Code] section 5 (extract_context_feature, fc, hidden_norm).
+    feats: n arrays [T, D] in increasing layer order; w_c: [D, n*D].
+    """
+    c = np.concatenate([np.asarray(f, dtype=F64) for f in feats], axis=-1)
+    y = linear(c, w_c)
+    return rms_norm(y, gain, eps)
+
+
+# ----------------------------------------------------------------------------
+# rotary position embedding
+# ----------------------------------------------------------------------------
+
+def rope_inv_freq(head_dim: int, theta: float):
+    d = np.arange(head_dim // 2, dtype=F64)
+    return theta ** (-2.0 * d / head_dim)
+
+
+def apply_rope(x, positions, theta: float):
+    """Rotate-half RoPE on the last axis: for d < hd/2 the pair (x_d, x_{d+hd/2})
+    is rotated by angle pos * theta^(-2d/hd). x: [T, H, hd]; positions: [T]."""
+    x = np.asarray(x, dtype=F64)
+    hd = x.shape[-1]
+    half = hd // 2
+    ang = np.asarray(positions, dtype=F64)[:, None] * rope_inv_freq(hd, theta)[None, :]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# S2 / S10: KV injection into the draft cache, trim and append
+# ----------------------------------------------------------------------------
+
+def inject_kv(ctx_feat, wk, wv, pos0: int, n_kv_heads: int, head_dim: int,
+              theta: float):
+    """Per-layer K/V of the fused context: K = RoPE(W_K H_t), V = W_V H_t.
+
+    [Tut] section 2.1.2 (the target feature enters only as K and V entries of
+    every draft layer); [Code] section 5 (k_ctx = k_proj(target_hidden)).
+    Context row t sits at absolute position pos0 + t.
+    Returns K, V as [T, Hkv, hd].
+    """
+    T = ctx_feat.shape[0]
+    k = linear(ctx_feat, wk).reshape(T, n_kv_heads, head_dim)
+    v = linear(ctx_feat, wv).reshape(T, n_kv_heads, head_dim)
+    k = apply_rope(k, np.arange(pos0, pos0 + T), theta)
+    return k, v
+
+
+@dataclass
+class DraftCache:
+    """One sequence's draft KV cache: per layer, the context rows' K and V.
+
+    [Sum] section 4.1 and [Code] section 5: projected target features are kept
+    in the draft model's KV cache and reused across drafting rounds; [Code]
+    section 9: after verification the cache is cropped back to the accepted
+    prefix. Rows at positions >= len are not part of the cache.
+    """
+    n_layers: int
+    k: List[np.ndarray] = field(default_factory=list)
+    v: List[np.ndarray] = field(default_factory=list)
+
+    def __post_init__(self):
+        if not self.k:
+            self.k = [None] * self.n_layers
+            self.v = [None] * self.n_layers
+
+    @property
+    def len(self) -> int:
+        return 0 if self.k[0] is None else int(self.k[0].shape[0])
+
+    def trim(self, keep: int):
+        if keep < 0 or keep > self.len:
+            raise ValueError("trim beyond the cache length")
+        for i in range(self.n_layers):
+            if self.k[i] is not None:
+                self.k[i] = self.k[i][:keep]
+                self.v[i] = self.v[i][:keep]
+
+    def append(self, layer: int, k, v, pos0: int):
+        """Write rows at positions pos0.. after dropping everything >= pos0."""
+        if self.k[layer] is None:
+            if pos0 != 0:
+                raise ValueError("first append must start at position 0")
+            self.k[layer], self.v[layer] = np.asarray(k, F64), np.asarray(v, F64)
+            return
+        if pos0 > self.k[layer].shape[0]:
+            raise ValueError("append past the cache length")
+        self.k[layer] = np.concatenate([self.k[layer][:pos0], np.asarray(k, F64)])
+        self.v[layer] = np.concatenate([self.v[layer][:pos0], np.asarray(v, F64)])
+
+
+def cache_inject(cache: DraftCache, ctx_feat, layers_w, cfg, pos0: int):
+    """Trim the cache to pos0 and append the K/V of ctx_feat in every layer."""
+    for i, lw in enumerate(layers_w):
+        k, v = inject_kv(ctx_feat, lw["wk"], lw["wv"], pos0, cfg.n_kv_heads,
+                         cfg.head_dim, cfg.rope_theta)
+        cache.append(i, k, v, pos0)
+
+
+# ----------------------------------------------------------------------------
+# S5: block attention
+# ----------------------------------------------------------------------------
+
+def block_attention(q, k, v):
+    """o = softmax(q k^T / sqrt(hd)) v with no mask, grouped-query heads.
+
+    q: [B, Hq, hd]; k, v: [S+B, Hkv, hd] = context rows then the block's own
+    rows ([Code] section 5: torch.cat([k_ctx, k_noise], dim=1)). Every block
+    position sees every key: the draft's full-attention layers are not causal
+    ([Code] section 6). Query head a uses kv head a // (Hq/Hkv).
+    """
+    B, Hq, hd = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    o = np.empty((B, Hq, hd), dtype=F64)
+    for a in range(Hq):
+        g = a // G
+        s = (np.asarray(q[:, a, :], F64) @ np.asarray(k[:, g, :], F64).T) / np.sqrt(hd)
+        o[:, a, :] = softmax(s, axis=-1) @ np.asarray(v[:, g, :], F64)
+    return o
+
+
+# ----------------------------------------------------------------------------
+# S3-S8: one draft forward over a block
+# ----------------------------------------------------------------------------
+
+def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
+                anchors: Sequence[int], block_len: Optional[int] = None):
+    """One parallel forward of the drafter over [anchor, mask x (block_len-1)].
+
+    [Code] section 6 (block = last confirmed token + block_size-1 mask tokens,
+    one forward fills every masked position, no iterative denoising) and
+    section 9 (positions continue from the context; the LM head is applied to
+    the block rows after the anchor, argmax gives the draft tokens);
+    [Tut] section 2.1.2 (Q from the draft only, K/V = [context ; block]);
+    [Tut] section 2.2.3 / [Code] section 3 (embedding and LM head are the
+    target's, shared and frozen).
+
+    caches[s] holds sequence s's context K/V; its length S_s is the anchor's
+    position. Returns a dict with
+      draft  [n_seq, block_len-1] int   argmax tokens of rows 1..block_len-1
+      hidden [L, n_seq, block_len, D]   residual stream after each layer
+      logits [n_seq, block_len-1, V]
+      gap    [n_seq, block_len-1]       top-1 minus top-2 logit
+    """
+    B = cfg.block_size if block_len is None else block_len
+    L, D = cfg.n_layers, cfg.hidden
+    Hq, Hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    eps, theta = cfg.rms_eps, cfg.rope_theta
+    n_seq = len(anchors)
+    hidden = np.empty((L, n_seq, B, D), dtype=F64)
+    out_draft = np.zeros((n_seq, max(B - 1, 0)), dtype=np.int64)
+    out_logits = np.zeros((n_seq, max(B - 1, 0), cfg.vocab), dtype=F64)
+    out_gap = np.zeros((n_seq, max(B - 1, 0)), dtype=F64)
+    embed = weights["embed"]
+    for s in range(n_seq):
+        S = caches[s].len
+        ids = [int(anchors[s])] + [cfg.mask_token_id] * (B - 1)
+        x = np.asarray(embed[ids], dtype=F64)            # [B, D]
+        pos = np.arange(S, S + B)
+        for i, lw in enumerate(weights["layers"]):
+            h = rms_norm(x, lw["attn_norm"], eps)
+            q = linear(h, lw["wq"]).reshape(B, Hq, hd)
+            kb = linear(h, lw["wk"]).reshape(B, Hkv, hd)
+            vb = linear(h, lw["wv"]).reshape(B, Hkv, hd)
+            q = apply_rope(q, pos, theta)
+            kb = apply_rope(kb, pos, theta)
+            if S > 0:
+                k_all = np.concatenate([caches[s].k[i], kb])
+                v_all = np.concatenate([caches[s].v[i], vb])
+            else:
+                k_all, v_all = kb, vb
+            o = block_attention(q, k_all, v_all).reshape(B, Hq * hd)
+            x = x + linear(o, lw["wo"])
+            h2 = rms_norm(x, lw["mlp_norm"], eps)
+            x = x + linear(silu(linear(h2, lw["w_gate"])) * linear(h2, lw["w_up"]),
+                           lw["w_down"])
+            hidden[i, s] = x
+        if B > 1:
+            z = rms_norm(x[1:], weights["final_norm"], eps)
+            logits = linear(z, weights["lm_head"])
+            out_logits[s] = logits
+            out_draft[s] = np.argmax(logits, axis=-1)
+            top2 = np.sort(logits, axis=-1)[:, -2:]
+            out_gap[s] = top2[:, 1] - top2[:, 0]
+    return {"draft": out_draft, "hidden": hidden, "logits": out_logits,
+            "gap": out_gap}
+
+
+# ----------------------------------------------------------------------------
+# S9: greedy verification
+# ----------------------------------------------------------------------------
+
+def verify_greedy(block_ids, target_logits):
+    """Longest matching prefix plus one bonus token.
+
+    [Code] section 8: posterior = argmax(target logits); the acceptance length
+    is the cumulative product of (block[1:] == posterior[:-1]) summed; the bonus
+    is posterior[acceptance]. tau = acceptance + 1, in 1..len(block)
+    ([Sum] section 3.1; [Code] section 4: tau counts the bonus token).
+    block_ids: [B] ints (anchor then drafts); target_logits: [B, V].
+    Returns (tau, bonus).
+    """
+    posterior = np.argmax(np.asarray(target_logits), axis=-1)
+    match = np.asarray(block_ids)[1:] == posterior[:-1]
+    accepted = int(np.cumprod(match.astype(np.int64)).sum())
+    return accepted + 1, int(posterior[accepted])
+
+
+# ----------------------------------------------------------------------------
+# Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+# as 1, 2, 3", SC 2011), written from the paper's round function
+# ----------------------------------------------------------------------------
+
+_M64 = (1 << 64) - 1
+_PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+_PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+
+
+def philox4x64_10(counter, key):
+    """One Philox4x64 block with 10 rounds. counter: 4 words, key: 2 words."""
+    x0, x1, x2, x3 = (int(c) & _M64 for c in counter)
+    k0, k1 = (int(k) & _M64 for k in key)
+    for _ in range(10):
+        p0 = _PHILOX_M[0] * x0
+        p1 = _PHILOX_M[1] * x2
+        x0, x1, x2, x3 = (((p1 >> 64) ^ x1 ^ k0) & _M64, p1 & _M64,
+                          ((p0 >> 64) ^ x3 ^ k1) & _M64, p0 & _M64)
+        k0 = (k0 + _PHILOX_W[0]) & _M64
+        k1 = (k1 + _PHILOX_W[1]) & _M64
+    return x0, x1, x2, x3
+
+
+PURPOSE_ACCEPT, PURPOSE_RESAMPLE, PURPOSE_DRAFT = 0, 1, 2
+
+
+def philox_uniform(seed: int, row: int, seq: int, purpose: int) -> float:
+    """u in [0, 1) from word 0 of block counter (row, seq, purpose, 0), key
+    (seed, 0): u = (w >> 11) * 2^-53."""
+    w = philox4x64_10((row, seq, purpose, 0), (seed, 0))[0]
+    return (w >> 11) * (2.0 ** -53)
+
+
+def sample_inverse_cdf(weights, u: float):
+    """Smallest v with sum_{w <= v} weights[w] > u * sum(weights), running sums
+    in vocab order in fp64. Returns (token, margin) where margin is the fp64
+    distance of u*sum to the nearest of the two bracketing running sums."""
+    r = np.asarray(weights, dtype=F64)
+    c = np.cumsum(r)
+    target = u * c[-1]
+    v = int(np.searchsorted(c, target, side="right"))
+    v = min(v, len(r) - 1)
+    lo = c[v - 1] if v > 0 else 0.0
+    margin = min(abs(c[v] - target), abs(target - lo))
+    return v, margin
+
+
+# ----------------------------------------------------------------------------
+# S11: p/q rejection-sampling verification
+# ----------------------------------------------------------------------------
+
+def verify_pq_with_uniforms(block_ids, target_logits, draft_logits,
+                            temperature: float, u_accept, u_resample):
+    """Speculative-sampling verification of one drafted block, uniforms given.
+
+    [Code] section 8 (_rejection_sample): the drafted token at row j is kept
+    with probability p/q (p the target's, q the draft's probability of that
+    token); acceptance stops at the first rejection (cumprod prefix); at a
+    rejection the replacement is drawn from max(p - q, 0) renormalised; when
+    the whole block is kept the bonus token comes from the target's
+    distribution at the last row. Probabilities are softmax(logits / T) in fp64.
+
+    Row j (0-based, j < gamma) is accepted iff u_accept[j] < p_j(x)/q_j(x) with
+    x = block_ids[j+1]; the replacement at row j or the bonus at row gamma is
+    sample_inverse_cdf(weights, u_resample[row]).
+    Returns (tau, bonus, diag); diag holds |p/q - u| per tested row and the
+    inverse-CDF margin of the final draw (relative to the weights' sum).
+    """
+    T = np.asarray(target_logits, dtype=F64) / temperature
+    Q = np.asarray(draft_logits, dtype=F64) / temperature
+    ids = [int(t) for t in block_ids]
+    gamma = len(ids) - 1
+    diag = {"ratio_margin": [], "cdf_margin": None}
+    for j in range(gamma):
+        p = softmax(T[j])
+        q = softmax(Q[j])
+        tok = ids[j + 1]
+        ratio = p[tok] / q[tok]
+        u = float(u_accept[j])
+        diag["ratio_margin"].append(abs(ratio - u))
+        if not (u < ratio):
+            resid = np.maximum(p - q, 0.0)
+            tok2, margin = sample_inverse_cdf(resid, float(u_resample[j]))
+            diag["cdf_margin"] = margin / resid.sum()
+            return j + 1, tok2, diag
+    p = softmax(T[gamma])
+    tok2, margin = sample_inverse_cdf(p, float(u_resample[gamma]))
+    diag["cdf_margin"] = margin / p.sum()
+    return gamma + 1, tok2, diag
+
+
+def verify_pq(block_ids, target_logits, draft_logits, temperature: float,
+              seed: int, row_offset: int = 0, seq: int = 0):
+    """verify_pq_with_uniforms with Philox uniforms: the accept test of row j
+    uses philox_uniform(seed, row_offset + j, seq, 0), the replacement or bonus
+    draw at row j uses philox_uniform(seed, row_offset + j, seq, 1)."""
+    B = len(block_ids)
+    ua = [philox_uniform(seed, row_offset + j, seq, PURPOSE_ACCEPT)
+          for j in range(B - 1)]
+    ur = [philox_uniform(seed, row_offset + j, seq, PURPOSE_RESAMPLE)
+          for j in range(B)]
+    return verify_pq_with_uniforms(block_ids, target_logits, draft_logits,
+                                   temperature, ua, ur)
+
+
+def sample_draft_tokens(draft_logits, temperature: float, seed: int,
+                        row_offset: int = 0, seq: int = 0):
+    """Draft tokens x_j ~ q_j = softmax(draft_logits[j] / T) by inverse CDF with
+    philox_uniform(seed, row_offset + j, seq, 2) ([Code] section 6: the masked
+    positions are filled by sampling from the draft distribution when not
+    greedy). Returns (tokens, margins)."""
+    toks, margins = [], []
+    for j in range(draft_logits.shape[0]):
+        q = softmax(np.asarray(draft_logits[j], F64) / temperature)
+        u = philox_uniform(seed, row_offset + j, seq, PURPOSE_DRAFT)
+        t, m = sample_inverse_cdf(q, u)
+        toks.append(t)
+        margins.append(m)
+    return np.array(toks, dtype=np.int64), np.array(margins)
