@@ -1,0 +1,269 @@
+"""Throughput of the DFlash drafter hot path on one MI355X.
+
+One step is one speculative round of the Qwen3-8B-shaped drafter (hidden 4096,
+5 draft layers, 32/8 heads of 128, SwiGLU 12288, vocab 151936, block 16) at a
+2048-token context:
+  draft_block  - embed [anchor, 15 x mask], 5 layers, LM head + argmax;
+  verify       - greedy, against planted target logits (tau ~ min(Geom(0.25), 16));
+  append       - fuse the tau accepted rows' 5 target hidden states, inject their
+                 K/V at positions 2048.., then trim the cache back to 2048 so every
+                 step drafts at the same context length.
+tau is read back to the host each round to size the append, as a host-driven
+loop must. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0) with the metric, the roofline of the dominant
+kernel (timed live with HIP events on the handle's stream) and the CPU oracle
+timed on a bounded sample on the host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft-block forward µs & blocks/s (block 16, ctx 2048); % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+STAGE_BITS = {"gate_up": 4, "lm_head": 6, "fuse_context": 7, "inject_kv": 8}
+
+
+def stage_bytes(dc, M):
+    """Algorithmic HBM bytes of one launch per stage (weights + activations)."""
+    D, F, V = dc.hidden, dc.ffn, dc.vocab
+    qd, kvd = dc.q_dim, dc.kv_dim
+    g = dc.block_size - 1
+    return {
+        "gate_up": 2 * F * D * 2 + M * D * 2 * 2 + M * F * 2 * 2,
+        "lm_head": V * D * 2 + g * D * 2 * 2,
+        "qkv": (qd + 2 * kvd) * D * 2,
+        "o_proj": D * qd * 2,
+        "down_proj": D * F * 2,
+    }
+
+
+def draft_block_bytes(dc, ctx):
+    D, F, V, L = dc.hidden, dc.ffn, dc.vocab, dc.n_layers
+    qd, kvd = dc.q_dim, dc.kv_dim
+    per_layer = ((qd + 2 * kvd) * D + D * qd + 2 * F * D + D * F) * 2
+    kv = L * 2 * (ctx + dc.block_size) * kvd * 2
+    return L * per_layer + V * D * 2 + kv
+
+
+def cpu_baseline(dc, w, feats_np, ctx_cache_fn, planted, budget_s=30.0):
+    """One speculative round of the oracle on host cores: draft forward at the
+    2048-token context, greedy verify, fuse + inject of the accepted rows."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+    f = lambda t: t.float().cpu().numpy()  # noqa: E731
+    wn = {k: f(v) for k, v in w.items() if k != "layers"}
+    wn["layers"] = [{k: f(v) for k, v in lw.items()} for lw in w["layers"]]
+    cache = ctx_cache_fn(wn)
+    anchor, logits, tau_rows = planted
+    t0 = time.perf_counter()
+    rounds = 0
+    while True:
+        out = O.draft_block(dc, wn, [cache], [anchor])
+        block = np.concatenate([[anchor], out["draft"][0]])
+        tau, _ = O.verify_greedy(block, logits)
+        H = O.fuse_context([x[:tau] for x in feats_np], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
+        S = cache.len
+        O.cache_inject(cache, H, wn["layers"], dc, S)
+        cache.trim(S)
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el > budget_s / 2 or rounds >= 3:
+            break
+    return {"value": rounds / el, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{rounds} full speculative round(s) of the numpy fp64 oracle at the "
+                      f"same workload (draft forward at ctx {cache.len}, greedy verify, "
+                      f"fuse+inject of the accepted rows), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-all", action="store_true",
+                    help="also time every stage once after the timed region")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+              "has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from block_diffusion_drafter_layer_amd import binding as B
+    from block_diffusion_drafter_layer_amd.drafter import Drafter, config_from
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dc = synth.CONFIGS[1]
+    S0, Bsz = dc.ctx_len, dc.block_size
+    print(f"[bench] workload {dc.name}: generating weights", file=sys.stderr, flush=True)
+    w = synth.make_weights(dc, device=dev)
+    d = Drafter(config_from(dc), w, max_seqs=1, max_tokens=S0, device=dev)
+    kv = d.new_kv(S0 + 64)
+
+    # prefill: fuse + inject the 2048-token context (timed separately)
+    feats = synth.make_feats(dc, S0, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(2):
+        kv.kv.len = 0
+        ev[0].record()
+        ctx = d.fuse_context(feats)
+        ev[1].record()
+        d.inject_kv(kv, ctx, 0)
+        ev[2].record()
+    torch.cuda.synchronize()
+    fuse_us = ev[0].elapsed_time(ev[1]) * 1e3
+    inject_us = ev[1].elapsed_time(ev[2]) * 1e3
+    assert kv.len == S0
+
+    anchors = torch.from_numpy(synth.make_anchor(dc)).to(dev)
+    block, _, _ = d.draft_block([kv], anchors)
+    torch.cuda.synchronize()
+    blk = block.cpu().numpy()[0]
+    taus = synth.planted_taus(dc, 64)
+    n_plant = 16
+    planted = []
+    for j in range(n_plant):
+        lg = synth.make_target_logits(dc, Bsz, round_index=j, device=dev)
+        synth.plant_agreement(lg, blk, int(taus[j]) - 1)
+        planted.append(lg.unsqueeze(0).contiguous())
+    app_feats = [synth.make_feats(dc, Bsz, round_index=100 + j, device=dev) for j in range(n_plant)]
+    app_ctx = torch.empty(Bsz, dc.hidden, dtype=torch.bfloat16, device=dev)
+    tau_t = torch.empty(1, dtype=torch.int32, device=dev)
+    bonus_t = torch.empty(1, dtype=torch.int32, device=dev)
+    blk_out = torch.empty(1, Bsz, dtype=torch.int32, device=dev)
+
+    def step(j):
+        d.draft_block([kv], anchors, block_out=blk_out)
+        d.verify(blk_out, planted[j % n_plant], tau=tau_t, bonus=bonus_t)
+        tau = int(tau_t.item())
+        f = [x[:tau] for x in app_feats[j % n_plant]]
+        B.dflash_fuse_context(d.h, [x.data_ptr() for x in f], f[0].stride(0), tau, app_ctx.data_ptr())
+        d.inject_kv(kv, app_ctx[:tau], S0)
+        d.kv_trim(kv, S0)
+        return tau
+
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+
+    mask = (1 << STAGE_BITS["gate_up"]) | (1 << STAGE_BITS["lm_head"])
+    B.dflash_profile_enable(d.h, mask, 8 * (args.steps + 1))
+    dstart = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    dend = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    tau_sum = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        dstart[j].record()
+        d.draft_block([kv], anchors, block_out=blk_out)
+        dend[j].record()
+        d.verify(blk_out, planted[j % n_plant], tau=tau_t, bonus=bonus_t)
+        tau = int(tau_t.item())
+        f = [x[:tau] for x in app_feats[j % n_plant]]
+        B.dflash_fuse_context(d.h, [x.data_ptr() for x in f], f[0].stride(0), tau, app_ctx.data_ptr())
+        d.inject_kv(kv, app_ctx[:tau], S0)
+        d.kv_trim(kv, S0)
+        tau_sum += tau
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    recs = B.dflash_profile_read(d.h, 8 * (args.steps + 1))
+    B.dflash_profile_enable(d.h, 0, 0)
+    draft_us = float(np.median([a.elapsed_time(b) for a, b in zip(dstart, dend)])) * 1e3
+
+    per_stage = {}
+    for name, ms in recs:
+        per_stage.setdefault(name, []).append(ms)
+    sb = stage_bytes(dc, Bsz)
+    tot = {k: sum(v) for k, v in per_stage.items()}
+    dom = max(tot, key=tot.get)
+    avg_ms = float(np.mean(per_stage[dom]))
+    achieved = sb[dom] / (avg_ms * 1e-3) / 1e9
+
+    stages_all = None
+    if args.profile_all:
+        B.dflash_profile_enable(d.h, (1 << 10) - 1, 256)
+        for j in range(3):
+            step(j)
+        torch.cuda.synchronize()
+        recs = B.dflash_profile_read(d.h, 256)
+        B.dflash_profile_enable(d.h, 0, 0)
+        acc = {}
+        for name, ms in recs:
+            acc.setdefault(name, []).append(ms * 1e3)
+        stages_all = {k: round(float(np.sum(v)) / 3, 2) for k, v in acc.items()}
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = args.steps / elapsed
+    dbytes = draft_block_bytes(dc, S0)
+    fuse_flops = 2.0 * S0 * dc.n_feat * dc.hidden * dc.hidden
+    inject_flops = 2.0 * S0 * dc.hidden * 2 * dc.kv_dim * dc.n_layers
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": dc.name, "block_size": Bsz, "ctx_len": S0, "n_seqs": 1,
+                   "hidden": dc.hidden, "draft_layers": dc.n_layers, "vocab": dc.vocab,
+                   "step": "draft_block + greedy verify + fuse/inject of accepted rows + trim"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": sb[dom]},
+        "draft_block_us": round(draft_us, 1),
+        "draft_block_hbm_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "mean_tau": round(tau_sum / args.steps, 3),
+        "prefill_fuse_us": round(fuse_us, 1),
+        "prefill_fuse_mfma_frac": round(fuse_flops / (fuse_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_inject_us": round(inject_us, 1),
+        "prefill_inject_mfma_frac": round(inject_flops / (inject_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+    }
+    if stages_all:
+        result["stage_us_per_step"] = stages_all
+
+    if not args.no_cpu_baseline:
+        import oracle as O
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        feats_np = [x.float().cpu().numpy() for x in app_feats[0]]
+
+        def ctx_cache(wn):
+            # the timed sample does not depend on the context values: seeded
+            # synthetic K/V rows stand in for the prefilled cache
+            c = O.DraftCache(dc.n_layers)
+            for i in range(dc.n_layers):
+                k, v = synth.gen.make_context_kv(dc, i, S0)
+                c.append(i, k.double().numpy(), v.double().numpy(), 0)
+            return c
+
+        result["cpu_baseline"] = cpu_baseline(
+            dc, w, feats_np, ctx_cache,
+            (int(blk[0]), planted[0][0].cpu().numpy(), None))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

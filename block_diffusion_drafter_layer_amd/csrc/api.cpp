@@ -1,0 +1,520 @@
+// Host side of the C ABI declared in include/dflash.h: argument checks,
+// workspace carving and the launch order of each call. Everything the calls
+// compute runs in the HIP kernels of this directory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dflash.h"
+#include "launch.h"
+
+using namespace dfl;
+
+namespace {
+
+thread_local std::string g_err;
+
+dflash_status fail(dflash_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dflash_status dev_fail(hipError_t e, const char* what) {
+  return fail(DFLASH_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+dflash_config normalized(const dflash_config& c) {
+  dflash_config n = c;
+  if (n.block_size == 0) n.block_size = 16;
+  if (!(n.rms_eps > 0.f)) n.rms_eps = 1e-6f;
+  if (!(n.rope_theta > 0.f)) n.rope_theta = 1e6f;
+  return n;
+}
+
+dflash_status check_config(const dflash_config& c) {
+  if (c.hidden <= 0 || c.hidden % 64)
+    return fail(DFLASH_E_CONFIG, "hidden=%d must be a positive multiple of 64", c.hidden);
+  if (c.n_feat_layers < 1 || c.n_feat_layers > kMaxFeat)
+    return fail(DFLASH_E_CONFIG, "n_feat_layers=%d outside 1..%d", c.n_feat_layers, kMaxFeat);
+  if (c.n_layers < 1 || c.n_layers > kMaxLayers)
+    return fail(DFLASH_E_CONFIG, "n_layers=%d outside 1..%d", c.n_layers, kMaxLayers);
+  if (!(c.head_dim == 16 || c.head_dim == 32 || c.head_dim == 64 || c.head_dim == 128))
+    return fail(DFLASH_E_CONFIG, "head_dim=%d not in {16,32,64,128}", c.head_dim);
+  if (c.n_kv_heads < 1 || c.n_kv_heads > 16 || c.n_heads < c.n_kv_heads ||
+      c.n_heads % c.n_kv_heads || c.n_heads / c.n_kv_heads > 16)
+    return fail(DFLASH_E_CONFIG, "heads %d/%d: need n_heads %% n_kv_heads == 0, group <= 16, n_kv_heads <= 16",
+                c.n_heads, c.n_kv_heads);
+  if ((c.n_heads * c.head_dim) % 32 || ((c.n_heads + 2 * c.n_kv_heads) * c.head_dim) % 32)
+    return fail(DFLASH_E_CONFIG, "q and qkv widths must be multiples of 32");
+  if (c.ffn <= 0 || c.ffn % 32) return fail(DFLASH_E_CONFIG, "ffn=%d must be a positive multiple of 32", c.ffn);
+  if (c.vocab < 2) return fail(DFLASH_E_CONFIG, "vocab=%d", c.vocab);
+  if (c.block_size < 1 || c.block_size > 16)
+    return fail(DFLASH_E_CONFIG, "block_size=%d outside 1..16", c.block_size);
+  if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab)
+    return fail(DFLASH_E_CONFIG, "mask_token_id=%d is required and must lie in [0, vocab)", c.mask_token_id);
+  if (!std::isfinite(c.rms_eps) || !std::isfinite(c.rope_theta) || c.rope_theta <= 1.f)
+    return fail(DFLASH_E_CONFIG, "rms_eps / rope_theta invalid");
+  return DFLASH_OK;
+}
+
+int32_t row_capacity(const dflash_config& c, int32_t max_ctx) {
+  return (int32_t)align_up((size_t)max_ctx + (size_t)c.block_size, 64);
+}
+
+struct Layout {
+  size_t x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
+  size_t total;
+};
+
+Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens) {
+  const size_t Mmax = (size_t)max_seqs * c.block_size;
+  const size_t D = c.hidden, qd = (size_t)c.n_heads * c.head_dim, F = c.ffn;
+  const size_t G = c.n_heads / c.n_kv_heads;
+  const size_t lm_tiles = ((size_t)c.vocab + skinny_tile_cols() - 1) / skinny_tile_cols();
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.x = take(Mmax * D * 4);
+  L.xh = take(Mmax * D * 2);
+  L.xl = take(Mmax * D * 2);
+  L.ssq = take(Mmax * (D / 32) * 4);
+  L.q = take(Mmax * qd * 2);
+  L.q_lo = take(Mmax * qd * 2);
+  L.ob_h = take(Mmax * qd * 2);
+  L.ob_l = take(Mmax * qd * 2);
+  L.act_h = take(Mmax * F * 2);
+  L.act_l = take(Mmax * F * 2);
+  L.lm_part = take(lm_tiles * Mmax * 8);
+  L.att_acc = take((size_t)kAttnSlotCap * G * 16 * c.head_dim * 4);
+  L.att_ml = take((size_t)kAttnSlotCap * G * 16 * 2 * 4);
+  L.vpart = take(2 * Mmax * kVerifyMaxSplits * 16);
+  // per-row partial sums of y^2: 128-column tiles (tiled GEMM) or 32-column
+  // groups (streaming path for few rows)
+  L.fuse_ssq = take(std::max((size_t)max_tokens * ((D + kGemmTile - 1) / kGemmTile),
+                             (size_t)std::min(max_tokens, kContextRowsStreaming) * (D / 32)) * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+enum Stage { ST_EMBED, ST_QKV, ST_ATTN, ST_OPROJ, ST_GATEUP, ST_DOWN, ST_LM, ST_FUSE, ST_INJECT,
+             ST_VERIFY, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"embed", "qkv", "attention", "o_proj", "gate_up",
+                                     "down_proj", "lm_head", "fuse_context", "inject_kv", "verify"};
+
+struct Profiler {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> ev;   // 2 per record
+  std::vector<int32_t> stage;
+  int32_t n = 0;
+};
+
+struct dflash_handle {
+  Profiler prof;
+  dflash_config cfg;
+  dflash_weights w;
+  std::vector<dflash_layer_weights> layers;
+  hipStream_t stream = nullptr;
+  unsigned char* ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t max_seqs = 0, max_tokens = 0;
+  Layout lay{};
+};
+
+// Launch `fn` as stage `st`, bracketed by timing events when that stage is
+// being profiled.
+template <class Fn>
+static hipError_t timed(dflash_handle* h, int st, Fn&& fn) {
+  Profiler& P = h->prof;
+  const bool on = (P.mask >> st) & 1u && 2 * (size_t)(P.n + 1) <= P.ev.size();
+  if (on) hipEventRecord(P.ev[2 * P.n], h->stream);
+  hipError_t e = fn();
+  if (on) {
+    hipEventRecord(P.ev[2 * P.n + 1], h->stream);
+    P.stage[P.n] = st;
+    ++P.n;
+  }
+  return e;
+}
+
+static void profiler_release(Profiler& P) {
+  for (hipEvent_t e : P.ev) hipEventDestroy(e);
+  P.ev.clear();
+  P.stage.clear();
+  P.n = 0;
+  P.mask = 0;
+}
+
+extern "C" {
+
+const char* dflash_stage_name(int32_t stage) {
+  return stage >= 0 && stage < ST_COUNT ? kStageNames[stage] : "unknown";
+}
+
+dflash_status dflash_profile_enable(dflash_handle* h, uint32_t stage_mask, int32_t max_records) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is NULL");
+  if (stage_mask && (max_records < 1 || max_records > (1 << 20)))
+    return fail(DFLASH_E_SHAPE, "max_records=%d outside 1..2^20", max_records);
+  profiler_release(h->prof);
+  if (!stage_mask) return DFLASH_OK;
+  h->prof.ev.resize(2 * (size_t)max_records);
+  for (size_t i = 0; i < h->prof.ev.size(); ++i) {
+    hipError_t e = hipEventCreate(&h->prof.ev[i]);
+    if (e != hipSuccess) {
+      h->prof.ev.resize(i);
+      profiler_release(h->prof);
+      return dev_fail(e, "hipEventCreate");
+    }
+  }
+  h->prof.stage.assign(max_records, -1);
+  h->prof.mask = stage_mask;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_profile_read(dflash_handle* h, int32_t cap, int32_t* stage_out, float* ms_out,
+                                  int32_t* n_out) {
+  if (!h || !n_out) return fail(DFLASH_E_NULL, "handle and n_out are required");
+  if (cap > 0 && (!stage_out || !ms_out)) return fail(DFLASH_E_NULL, "output arrays are required");
+  Profiler& P = h->prof;
+  const int32_t n = std::min(P.n, std::max(cap, 0));
+  for (int32_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(P.ev[2 * i + 1]);
+    if (e != hipSuccess) return dev_fail(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]);
+    if (e != hipSuccess) return dev_fail(e, "hipEventElapsedTime");
+    stage_out[i] = P.stage[i];
+    ms_out[i] = ms;
+  }
+  *n_out = n;
+  P.n = 0;
+  return DFLASH_OK;
+}
+
+const char* dflash_status_str(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_NULL: return "null pointer";
+    case DFLASH_E_CONFIG: return "invalid configuration";
+    case DFLASH_E_SHAPE: return "size out of range";
+    case DFLASH_E_CAPACITY: return "capacity exceeded";
+    case DFLASH_E_ALIGN: return "misaligned pointer or stride";
+    case DFLASH_E_DEVICE: return "device error";
+    case DFLASH_E_STATE: return "invalid state";
+  }
+  return "unknown status";
+}
+
+const char* dflash_last_error(void) { return g_err.c_str(); }
+
+dflash_status dflash_target_layer_ids(int32_t n_target_layers, int32_t n_feat, int32_t* out) {
+  if (!out) return fail(DFLASH_E_NULL, "out is NULL");
+  if (n_feat < 1 || n_target_layers < 4 || (n_feat > 1 && n_target_layers - 4 < n_feat - 1))
+    return fail(DFLASH_E_SHAPE, "cannot pick %d distinct layers of %d", n_feat, n_target_layers);
+  if (n_feat == 1) {
+    out[0] = n_target_layers / 2;
+    return DFLASH_OK;
+  }
+  const double lo = 1.0, hi = (double)(n_target_layers - 3);
+  for (int i = 0; i < n_feat; ++i)
+    out[i] = (int32_t)std::floor(lo + (hi - lo) * i / (n_feat - 1) + 0.5);
+  return DFLASH_OK;
+}
+
+size_t dflash_kv_bytes(const dflash_config* cfg, int32_t max_ctx) {
+  if (!cfg || max_ctx < 0) return 0;
+  const dflash_config c = normalized(*cfg);
+  if (check_config(c) != DFLASH_OK) return 0;
+  return (size_t)c.n_layers * 2 * c.n_kv_heads * (size_t)row_capacity(c, max_ctx) * c.head_dim * 2;
+}
+
+int32_t dflash_kv_row_capacity(const dflash_config* cfg, int32_t max_ctx) {
+  if (!cfg || max_ctx < 0) return 0;
+  const dflash_config c = normalized(*cfg);
+  if (check_config(c) != DFLASH_OK) return 0;
+  return row_capacity(c, max_ctx);
+}
+
+size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t max_seqs, int32_t max_tokens) {
+  if (!cfg || max_seqs < 1 || max_seqs > kMaxSeqs || max_tokens < 0) return 0;
+  const dflash_config c = normalized(*cfg);
+  if (check_config(c) != DFLASH_OK) return 0;
+  return make_layout(c, max_seqs, max_tokens).total;
+}
+
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w, void* stream,
+                            dflash_handle** out) {
+  if (!cfg || !w || !out) return fail(DFLASH_E_NULL, "cfg, weights and out are required");
+  const dflash_config c = normalized(*cfg);
+  dflash_status st = check_config(c);
+  if (st != DFLASH_OK) return st;
+  const void* mats[] = {w->w_c, w->ctx_norm, w->embed, w->lm_head, w->final_norm};
+  for (const void* p : mats) {
+    if (!p) return fail(DFLASH_E_NULL, "a model-level weight pointer is NULL");
+    if (!aligned(p, 16)) return fail(DFLASH_E_ALIGN, "weights must be 16-byte aligned");
+  }
+  if (!w->layers) return fail(DFLASH_E_NULL, "layers is NULL");
+  for (int i = 0; i < c.n_layers; ++i) {
+    const dflash_layer_weights& l = w->layers[i];
+    const void* lp[] = {l.wq, l.wk, l.wv, l.wo, l.w_gate, l.w_up, l.w_down, l.attn_norm, l.mlp_norm};
+    for (const void* p : lp) {
+      if (!p) return fail(DFLASH_E_NULL, "layer %d has a NULL weight", i);
+      if (!aligned(p, 16)) return fail(DFLASH_E_ALIGN, "layer %d weight not 16-byte aligned", i);
+    }
+  }
+  dflash_handle* h = new dflash_handle();
+  h->cfg = c;
+  h->w = *w;
+  h->layers.assign(w->layers, w->layers + c.n_layers);
+  h->w.layers = h->layers.data();
+  h->stream = (hipStream_t)stream;
+  *out = h;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_destroy(dflash_handle* h) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is NULL");
+  profiler_release(h->prof);
+  delete h;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_stream(dflash_handle* h, void* stream) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is NULL");
+  h->stream = (hipStream_t)stream;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_workspace(dflash_handle* h, void* ws, size_t bytes, int32_t max_seqs,
+                                   int32_t max_tokens) {
+  if (!h || !ws) return fail(DFLASH_E_NULL, "handle and workspace are required");
+  if (!aligned(ws, 256)) return fail(DFLASH_E_ALIGN, "workspace must be 256-byte aligned");
+  if (max_seqs < 1 || max_seqs > kMaxSeqs || max_tokens < 0)
+    return fail(DFLASH_E_SHAPE, "max_seqs=%d outside 1..%d or max_tokens=%d < 0", max_seqs, kMaxSeqs, max_tokens);
+  const Layout L = make_layout(h->cfg, max_seqs, max_tokens);
+  if (bytes < L.total)
+    return fail(DFLASH_E_CAPACITY, "workspace of %zu bytes, %zu needed", bytes, L.total);
+  h->ws = (unsigned char*)ws;
+  h->ws_bytes = bytes;
+  h->max_seqs = max_seqs;
+  h->max_tokens = max_tokens;
+  h->lay = L;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats, int64_t ld,
+                                  int32_t n_tokens, void* ctx_out) {
+  if (!h || !feats || !ctx_out) return fail(DFLASH_E_NULL, "handle, feats and ctx_out are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_tokens < 1 || n_tokens > h->max_tokens)
+    return fail(DFLASH_E_SHAPE, "n_tokens=%d outside 1..%d", n_tokens, h->max_tokens);
+  if (ld < c.hidden || ld % 8) return fail(DFLASH_E_ALIGN, "ld=%lld must be >= hidden and a multiple of 8", (long long)ld);
+  FuseLaunch F{};
+  for (int i = 0; i < c.n_feat_layers; ++i) {
+    if (!feats[i]) return fail(DFLASH_E_NULL, "feats[%d] is NULL", i);
+    if (!aligned(feats[i], 16)) return fail(DFLASH_E_ALIGN, "feats[%d] not 16-byte aligned", i);
+    F.feats[i] = (const bf16_t*)feats[i];
+  }
+  if (!aligned(ctx_out, 16)) return fail(DFLASH_E_ALIGN, "ctx_out not 16-byte aligned");
+  F.n_feat = c.n_feat_layers;
+  F.ld = ld;
+  F.T = n_tokens;
+  F.D = c.hidden;
+  F.w_c = (const bf16_t*)h->w.w_c;
+  F.gain = (const bf16_t*)h->w.ctx_norm;
+  F.eps = c.rms_eps;
+  F.out = (bf16_t*)ctx_out;
+  F.ssq = (float*)(h->ws + h->lay.fuse_ssq);
+  const bool rows = n_tokens <= kContextRowsStreaming;
+  hipError_t e = timed(h, ST_FUSE, [&] {
+    return rows ? launch_fuse_rows(F, h->stream) : launch_fuse(F, h->stream);
+  });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "fuse_context");
+}
+
+static dflash_status check_kv(const dflash_handle* h, const dflash_kv* kv, const char* name) {
+  if (!kv || !kv->base) return fail(DFLASH_E_NULL, "%s: kv or kv->base is NULL", name);
+  if (!aligned(kv->base, 256)) return fail(DFLASH_E_ALIGN, "%s: kv->base not 256-byte aligned", name);
+  if (kv->max_ctx < 0 || kv->len < 0 || kv->len > kv->max_ctx)
+    return fail(DFLASH_E_SHAPE, "%s: len=%d max_ctx=%d", name, kv->len, kv->max_ctx);
+  (void)h;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_inject_kv(dflash_handle* h, dflash_kv* kv, const void* ctx_feat,
+                               int32_t n_tokens, int32_t pos0) {
+  if (!h || !ctx_feat) return fail(DFLASH_E_NULL, "handle and ctx_feat are required");
+  dflash_status st = check_kv(h, kv, "inject_kv");
+  if (st != DFLASH_OK) return st;
+  const dflash_config& c = h->cfg;
+  if (n_tokens < 1 || n_tokens > h->max_tokens)
+    return fail(DFLASH_E_SHAPE, "n_tokens=%d outside 1..%d", n_tokens, h->max_tokens);
+  if (pos0 < 0 || pos0 > kv->len)
+    return fail(DFLASH_E_SHAPE, "pos0=%d must lie in 0..len=%d", pos0, kv->len);
+  if ((int64_t)pos0 + n_tokens > kv->max_ctx)
+    return fail(DFLASH_E_CAPACITY, "pos0+n_tokens=%lld exceeds max_ctx=%d", (long long)pos0 + n_tokens, kv->max_ctx);
+  if (!aligned(ctx_feat, 16)) return fail(DFLASH_E_ALIGN, "ctx_feat not 16-byte aligned");
+  InjectLaunch I{};
+  I.ctx = (const bf16_t*)ctx_feat;
+  I.T = n_tokens; I.D = c.hidden; I.L = c.n_layers; I.Hkv = c.n_kv_heads; I.hd = c.head_dim;
+  I.pos0 = pos0; I.cap = row_capacity(c, kv->max_ctx);
+  I.log2_theta = std::log2((double)c.rope_theta);
+  for (int i = 0; i < c.n_layers; ++i) {
+    I.wk[i] = (const bf16_t*)h->layers[i].wk;
+    I.wv[i] = (const bf16_t*)h->layers[i].wv;
+  }
+  I.kv = (bf16_t*)kv->base;
+  const bool rows = n_tokens <= kContextRowsStreaming;
+  hipError_t e = timed(h, ST_INJECT, [&] {
+    return rows ? launch_inject_rows(I, h->stream) : launch_inject(I, h->stream);
+  });
+  if (e != hipSuccess) return dev_fail(e, "inject_kv");
+  kv->len = pos0 + n_tokens;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_kv_trim(dflash_handle* h, dflash_kv* kv, int32_t keep_len) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is NULL");
+  dflash_status st = check_kv(h, kv, "kv_trim");
+  if (st != DFLASH_OK) return st;
+  if (keep_len < 0 || keep_len > kv->len)
+    return fail(DFLASH_E_SHAPE, "keep_len=%d must lie in 0..len=%d", keep_len, kv->len);
+  kv->len = keep_len;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                 const int32_t* anchor_ids, int32_t block_len, int32_t* block_out,
+                                 float* hidden_out, float* logits_out) {
+  if (!h || !kvs || !anchor_ids || !block_out)
+    return fail(DFLASH_E_NULL, "handle, kvs, anchor_ids and block_out are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if ((hidden_out && !aligned(hidden_out, 4)) || (logits_out && !aligned(logits_out, 4)))
+    return fail(DFLASH_E_ALIGN, "optional outputs must be 4-byte aligned");
+  SeqTable seqs{};
+  int max_keys = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    dflash_status st = check_kv(h, kvs[s], "draft_block");
+    if (st != DFLASH_OK) return st;
+    seqs.s[s].kv = (bf16_t*)kvs[s]->base;
+    seqs.s[s].cap = row_capacity(c, kvs[s]->max_ctx);
+    seqs.s[s].len = kvs[s]->len;
+    max_keys = std::max(max_keys, kvs[s]->len + block_len);
+  }
+  const Layout& Ly = h->lay;
+  unsigned char* ws = h->ws;
+  DraftLaunch L{};
+  L.M = n_seqs * block_len; L.n_seqs = n_seqs; L.Bl = block_len;
+  L.D = c.hidden; L.Hq = c.n_heads; L.Hkv = c.n_kv_heads; L.hd = c.head_dim; L.F = c.ffn;
+  L.V = c.vocab; L.mask_id = c.mask_token_id; L.eps = c.rms_eps;
+  L.log2_theta = std::log2((double)c.rope_theta);
+  L.embed = (const bf16_t*)h->w.embed;
+  L.gain0 = (const bf16_t*)h->layers[0].attn_norm;
+  L.anchors = anchor_ids; L.block_out = block_out; L.seqs = &seqs;
+  L.x = (float*)(ws + Ly.x); L.xh = (bf16_t*)(ws + Ly.xh); L.xl = (bf16_t*)(ws + Ly.xl);
+  L.ssq = (float*)(ws + Ly.ssq); L.q = (bf16_t*)(ws + Ly.q); L.q_lo = (bf16_t*)(ws + Ly.q_lo);
+  L.ob_h = (bf16_t*)(ws + Ly.ob_h); L.ob_l = (bf16_t*)(ws + Ly.ob_l);
+  L.act_h = (bf16_t*)(ws + Ly.act_h); L.act_l = (bf16_t*)(ws + Ly.act_l);
+  L.lm_part = (uint64_t*)(ws + Ly.lm_part);
+  L.att_acc = (float*)(ws + Ly.att_acc); L.att_ml = (float*)(ws + Ly.att_ml);
+  // split each sequence's keys so the grid has ~512 workgroups
+  const int pairs = n_seqs * c.n_kv_heads;
+  const int max_splits = std::max(1, std::min(kAttnMaxSplits, kAttnSlotCap / pairs));
+  int splits = std::min(max_splits, std::max(1, (512 + pairs - 1) / pairs));
+  int kps = (int)align_up((size_t)((max_keys + splits - 1) / splits), 32);
+  kps = std::max(kps, 64);
+  splits = (max_keys + kps - 1) / kps;
+  L.att_splits = splits; L.att_keys_per_split = kps;
+
+  hipStream_t st = h->stream;
+  hipError_t e = timed(h, ST_EMBED, [&] { return launch_embed(L, st); });
+  if (e != hipSuccess) return dev_fail(e, "embed");
+  for (int i = 0; i < c.n_layers; ++i) {
+    const dflash_layer_weights& lw = h->layers[i];
+    e = timed(h, ST_QKV, [&] {
+      return launch_qkv(L, i, (const bf16_t*)lw.wq, (const bf16_t*)lw.wk, (const bf16_t*)lw.wv, st);
+    });
+    if (e != hipSuccess) return dev_fail(e, "qkv");
+    e = timed(h, ST_ATTN, [&] { return launch_attention(L, i, st); });
+    if (e != hipSuccess) return dev_fail(e, "attention");
+    e = timed(h, ST_OPROJ, [&] {
+      return launch_resid(L, (const bf16_t*)lw.wo, L.ob_h, L.ob_l, c.n_heads * c.head_dim,
+                          (const bf16_t*)lw.mlp_norm, nullptr, st);
+    });
+    if (e != hipSuccess) return dev_fail(e, "o_proj");
+    e = timed(h, ST_GATEUP, [&] {
+      return launch_swiglu(L, (const bf16_t*)lw.w_gate, (const bf16_t*)lw.w_up, st);
+    });
+    if (e != hipSuccess) return dev_fail(e, "gate_up");
+    const bf16_t* gnext = (const bf16_t*)(i + 1 < c.n_layers ? h->layers[i + 1].attn_norm
+                                                              : h->w.final_norm);
+    float* hid = hidden_out ? hidden_out + (size_t)i * L.M * c.hidden : nullptr;
+    e = timed(h, ST_DOWN, [&] {
+      return launch_resid(L, (const bf16_t*)lw.w_down, L.act_h, L.act_l, c.ffn, gnext, hid, st);
+    });
+    if (e != hipSuccess) return dev_fail(e, "down_proj");
+  }
+  if (block_len > 1) {
+    e = timed(h, ST_LM, [&] { return launch_lm(L, (const bf16_t*)h->w.lm_head, logits_out, st); });
+    if (e != hipSuccess) return dev_fail(e, "lm_head");
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                            const int32_t* block_ids, const float* target_logits,
+                            const float* draft_logits, float temperature, uint64_t seed,
+                            uint64_t philox_offset, int32_t* tau_out, int32_t* bonus_out) {
+  if (!h || !block_ids || !target_logits || !tau_out || !bonus_out)
+    return fail(DFLASH_E_NULL, "handle, block_ids, target_logits, tau_out and bonus_out are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "temperature must be finite and >= 0");
+  const bool greedy = temperature == 0.f;
+  if (!greedy && block_len > 1 && !draft_logits)
+    return fail(DFLASH_E_NULL, "draft_logits are required when temperature > 0");
+  if (greedy && draft_logits)
+    return fail(DFLASH_E_SHAPE, "draft_logits must be NULL when temperature == 0");
+  if (c.vocab % 4 == 0 && !aligned(target_logits, 16))
+    return fail(DFLASH_E_ALIGN, "target_logits not 16-byte aligned");
+  VerifyLaunch P{};
+  P.n_seqs = n_seqs; P.Bl = block_len; P.V = c.vocab;
+  P.block_ids = block_ids; P.target = target_logits; P.draft = draft_logits;
+  P.temperature = (double)temperature; P.seed = seed; P.offset = philox_offset;
+  P.tau = tau_out; P.bonus = bonus_out;
+  P.part = h->ws + h->lay.vpart;
+  const int rows = greedy ? n_seqs * block_len : n_seqs * (2 * block_len - 1);
+  P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
+  hipError_t e = timed(h, ST_VERIFY, [&] {
+    return greedy ? launch_verify_greedy(P, h->stream) : launch_verify_pq(P, h->stream);
+  });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "verify");
+}
+
+}  // extern "C"

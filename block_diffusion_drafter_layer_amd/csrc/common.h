@@ -1,0 +1,127 @@
+// Shared device helpers for the gfx950 kernels of the DFlash hot path:
+// bf16 storage conversions, the 16x16x32 bf16 MFMA, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfl {
+
+typedef uint16_t bf16_t;  // storage type: raw bf16 bits
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kMaxSeqs = 64;
+
+__device__ __forceinline__ float bf2f(bf16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// v = hi + lo with hi = bf16(v), lo = bf16(v - hi): the pair carries ~16
+// significant bits, so a product against exact bf16 weights through two
+// MFMAs is close to fp32 accurate.
+__device__ __forceinline__ void split_bf16(float v, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(v);
+  lo = f2bf(v - bf2f(hi));
+}
+
+// 16 bytes (8 bf16) from global memory as an MFMA operand.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t* p) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// D[i][j] += sum_k A[i][k] B[k][j], 16x16x32, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16] and
+// holds D[4*(l/16) + e][l%16], e = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Order-preserving key for (value, index) argmax with the lowest index
+// winning ties: larger key <=> larger value, or equal value and lower index.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint64_t)(0xffffffffu - idx);
+}
+__device__ __forceinline__ uint32_t argmax_key_index(uint64_t k) {
+  return 0xffffffffu - (uint32_t)(k & 0xffffffffu);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) {
+  return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = umax64(v, w);
+  }
+  return v;
+}
+
+// RoPE angle for position `pos` and pair index d of a head of size hd:
+// pos * theta^(-2d/hd), formed and reduced modulo 2*pi in fp64, then cos/sin
+// in fp32 of the reduced angle.
+__device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_theta,
+                                        float& c, float& s) {
+  double inv = exp2(-2.0 * (double)d / (double)hd * log2_theta);
+  double a = (double)pos * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  a -= two_pi * rint(a / two_pi);
+  sincosf((float)a, &s, &c);
+}
+
+// One sequence of a draft call: its KV buffer and the context length.
+struct SeqDesc {
+  bf16_t* kv;     // base of the sequence's KV buffer
+  int32_t cap;    // row capacity of each head plane
+  int32_t len;    // context positions (the anchor sits at position len)
+};
+struct SeqTable {
+  SeqDesc s[kMaxSeqs];
+};
+
+}  // namespace dfl

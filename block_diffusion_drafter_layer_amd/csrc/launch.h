@@ -1,0 +1,104 @@
+// Internal launch interface between the host ABI (api.cpp) and the kernels.
+// Every launcher only enqueues on the given stream and returns the launch
+// status; shapes have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dfl {
+
+constexpr int kMaxLayers = 16;
+constexpr int kMaxFeat = 8;
+constexpr int kAttnMaxSplits = 64;
+constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots
+constexpr int kVerifyMaxSplits = 64;
+constexpr int kGemmTile = 128;
+
+// Workspace pointers and shapes of one draft forward.
+struct DraftLaunch {
+  int M, n_seqs, Bl;
+  int D, Hq, Hkv, hd, F, V, mask_id;
+  float eps;
+  double log2_theta;
+  const bf16_t* embed;
+  const bf16_t* gain0;      // attn_norm of layer 0
+  const int32_t* anchors;
+  int32_t* block_out;
+  const SeqTable* seqs;
+  // workspace
+  float* x;                 // [M][D]
+  bf16_t *xh, *xl;          // [M][D]
+  float* ssq;               // [M][D/32]
+  bf16_t *q, *q_lo;         // [M][Hq*hd] query after RoPE, hi/lo
+  bf16_t *ob_h, *ob_l;      // [M][Hq*hd]
+  bf16_t *act_h, *act_l;    // [M][F]
+  uint64_t* lm_part;        // [ceil(V/32)][M]
+  float* att_acc;           // [slots*G][16][hd]
+  float* att_ml;            // [slots*G][16][2]
+  int att_splits, att_keys_per_split;
+};
+
+int skinny_tile_cols();
+int skinny_max_rows();
+
+hipError_t launch_embed(const DraftLaunch& L, hipStream_t st);
+hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
+                      const bf16_t* wk, const bf16_t* wv, hipStream_t st);
+hipError_t launch_attention(const DraftLaunch& L, int layer, hipStream_t st);
+hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
+                        const bf16_t* al, int K, const bf16_t* gain_next,
+                        float* hidden, hipStream_t st);
+hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
+                         hipStream_t st);
+hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
+                     hipStream_t st);
+
+// Context fusion: y = [f_0 .. f_{n-1}] W_c^T (bf16 into out), then RMSNorm.
+struct FuseLaunch {
+  const bf16_t* feats[kMaxFeat];
+  int n_feat;
+  int64_t ld;
+  int T, D;
+  const bf16_t* w_c;
+  const bf16_t* gain;
+  float eps;
+  bf16_t* out;        // [T][D]
+  float* ssq;         // [T][ceil(D/128)]
+};
+hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
+hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
+hipError_t launch_fuse_normalize(bf16_t* out, const float* ssq, int n_parts, int T, int D,
+                                 const bf16_t* gain, float eps, hipStream_t st);
+
+// KV injection of T context rows at positions pos0.. into every layer.
+struct InjectLaunch {
+  const bf16_t* ctx;  // [T][D]
+  int T, D, L, Hkv, hd, pos0, cap;
+  double log2_theta;
+  const bf16_t* wk[kMaxLayers];
+  const bf16_t* wv[kMaxLayers];
+  bf16_t* kv;
+};
+hipError_t launch_inject(const InjectLaunch& I, hipStream_t st);       // tiled MFMA GEMM
+hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st);  // few rows: streaming
+constexpr int kContextRowsStreaming = 64;  // row counts up to this use the streaming kernels
+
+// Verification.
+struct VerifyLaunch {
+  int n_seqs, Bl, V;
+  const int32_t* block_ids;
+  const float* target;
+  const float* draft;
+  double temperature;
+  uint64_t seed, offset;
+  int32_t *tau, *bonus;
+  void* part;          // workspace for per-split partials
+  int splits;
+};
+hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
+hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
+
+}  // namespace dfl

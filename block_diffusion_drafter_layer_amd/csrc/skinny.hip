@@ -1,0 +1,572 @@
+// Weight-streaming GEMMs of the draft forward (few activation rows, wide
+// weights): Y[m][n] = sum_k X[m][k] W[n][k], X given as a bf16 hi/lo pair,
+// W bf16 in nn.Linear [out, in] layout, read straight from HBM into MFMA
+// operand registers (16 bytes per lane, no LDS staging). The K range of a
+// workgroup's columns is split over its waves and reduced through LDS; each
+// use has its own fused epilogue:
+//   qkv    - RMSNorm row scale, RoPE on q/k, q to the workspace, k/v into the
+//            sequence's KV cache (txtmix article section 5: q from the draft
+//            tokens, k/v of the block appended after the context);
+//   resid  - o_proj / down_proj: x += y, the next RMSNorm's input (x*gain as a
+//            bf16 hi/lo pair) and per-32-column sums of x^2;
+//   swiglu - gate/up pairs: silu(g)*u (spec decoder layer);
+//   lm     - final RMSNorm row scale, optional logits, per-tile argmax keys
+//            (txtmix article section 9: LM head on the rows after the anchor).
+// Also here: the block embedding (section 6: anchor + mask tokens) and the
+// argmax reduction that writes the drafted block.
+#include "common.h"
+#include "launch.h"
+
+namespace dfl {
+
+struct SkinnyA {
+  const bf16_t* xh;   // activations hi [rows_in, lda]
+  const bf16_t* xl;   // activations lo (unused when the kernel has no lo half)
+  int lda;
+  // optional k-segmentation: k in [j*seg_k, (j+1)*seg_k) reads seg[j] (the
+  // context fusion reads each target layer's array in place); seg_k = K and
+  // seg[0] = xh otherwise
+  const bf16_t* seg[kMaxFeat];
+  int seg_k;
+  int M;              // output rows
+  int K;              // contraction length (multiple of 32)
+  // output row m reads input row (m / a_group) * a_stride + a_off + m % a_group
+  int a_group, a_stride, a_off;
+  const float* ssq;   // optional: per-row partial sums of x^2 [rows_in][ssq_ld]
+  int ssq_ld;
+  float eps;
+};
+
+__device__ __forceinline__ int in_row(const SkinnyA& a, int m) {
+  return (m / a.a_group) * a.a_stride + a.a_off + (m % a.a_group);
+}
+
+// dim of virtual column vi inside a head: each 16-wide group holds the dims
+// 8t..8t+7 and hd/2+8t..hd/2+8t+7 so a RoPE pair shares a group
+__device__ __forceinline__ int paired_dim(int vi, int hd) {
+  int t = vi >> 4, j = vi & 15;
+  return j < 8 ? (t << 3) + j : (hd >> 1) + (t << 3) + (j - 8);
+}
+
+// ---------------------------------------------------------------------------
+// epilogues
+// ---------------------------------------------------------------------------
+
+struct EpiQKV {
+  struct P {
+    const bf16_t *wq, *wk, *wv;
+    int D, Hq, Hkv, hd, Bl, layer;
+    double log2_theta;
+    bf16_t* q_out;     // [M][Hq*hd] hi
+    bf16_t* q_lo;      // [M][Hq*hd] lo
+    SeqTable seqs;
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
+    if (vc < qd) {
+      int h = vc / p.hd, d = paired_dim(vc % p.hd, p.hd);
+      return p.wq + (size_t)(h * p.hd + d) * p.D;
+    }
+    vc -= qd;
+    if (vc < kvd) {
+      int h = vc / p.hd, d = paired_dim(vc % p.hd, p.hd);
+      return p.wk + (size_t)(h * p.hd + d) * p.D;
+    }
+    vc -= kvd;
+    return p.wv + (size_t)vc * p.D;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+                             int vc0, int m0, int M) {
+    const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
+    constexpr int NG = VC / 16;
+    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
+      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const int s = m / p.Bl, r = m % p.Bl;
+      const SeqDesc sd = p.seqs.s[s];
+      const int pos = sd.len + r;
+      const float x1 = tile[ml][c * 16 + j] * rs[ml];
+      const float x2 = tile[ml][c * 16 + j + 8] * rs[ml];
+      const int vc = vc0 + c * 16;
+      if (vc >= qd + 2 * kvd) continue;
+      const size_t plane = (size_t)sd.cap * p.hd;
+      if (vc < qd + kvd) {
+        const bool is_q = vc < qd;
+        const int vcl = is_q ? vc : vc - qd;
+        const int h = vcl / p.hd;
+        const int d = ((vcl % p.hd) >> 1) + j;  // group t covers dims 8t+j
+        float cs, sn;
+        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        const float o1 = x1 * cs - x2 * sn;
+        const float o2 = x2 * cs + x1 * sn;
+        if (is_q) {
+          const size_t qi = (size_t)m * qd + h * p.hd + d;
+          split_bf16(o1, p.q_out[qi], p.q_lo[qi]);
+          split_bf16(o2, p.q_out[qi + p.hd / 2], p.q_lo[qi + p.hd / 2]);
+        } else {
+          bf16_t* k = sd.kv + (size_t)((2 * p.layer) * p.Hkv + h) * plane +
+                      (size_t)pos * p.hd;
+          k[d] = f2bf(o1);
+          k[d + p.hd / 2] = f2bf(o2);
+        }
+      } else {
+        const int vi = vc - qd - kvd;
+        const int h = vi / p.hd, d0 = vi % p.hd + j;
+        bf16_t* v = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + h) * plane;
+        v[(size_t)d0 * sd.cap + pos] = f2bf(x1);
+        v[(size_t)(d0 + 8) * sd.cap + pos] = f2bf(x2);
+      }
+    }
+  }
+};
+
+struct EpiResid {
+  struct P {
+    const bf16_t* w;     // [N=D][K]
+    int K, D;
+    float* x;            // [M][D] residual stream, updated in place
+    bf16_t *xh, *xl;     // [M][D] next RMSNorm input x*gain, hi/lo
+    const bf16_t* gain;  // [D]
+    float* ssq;          // [M][D/32]
+    float* hidden;       // optional [M][D]
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    return p.w + (size_t)vc * p.K;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*,
+                             int vc0, int m0, int M) {
+    static_assert(VC == 32, "one 32-column norm group per workgroup");
+    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
+      const int ml = e / VC, c = e % VC;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const int n = vc0 + c;
+      const size_t i = (size_t)m * p.D + n;
+      const float xn = p.x[i] + tile[ml][c];
+      p.x[i] = xn;
+      if (p.hidden) p.hidden[i] = xn;
+      split_bf16(xn * bf2f(p.gain[n]), p.xh[i], p.xl[i]);
+      tile[ml][c] = xn * xn;
+    }
+    __syncthreads();
+    const int ng = p.D / 32;
+    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+      float s = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < VC; ++c) s += tile[ml][c];
+      p.ssq[(size_t)(m0 + ml) * ng + vc0 / 32] = s;
+    }
+  }
+};
+
+struct EpiSwiglu {
+  struct P {
+    const bf16_t *wg, *wu;  // [F][D]
+    int K, F;
+    bf16_t *ah, *al;        // [M][F] activation hi/lo
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    const int t = vc >> 4, j = vc & 15;
+    const int f = (t << 3) + (j & 7);
+    return (j < 8 ? p.wg : p.wu) + (size_t)f * p.K;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+                             int vc0, int m0, int M) {
+    constexpr int NG = VC / 16;
+    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
+      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const float g = tile[ml][c * 16 + j] * rs[ml];
+      const float u = tile[ml][c * 16 + j + 8] * rs[ml];
+      const float a = g / (1.f + expf(-g)) * u;
+      const int f = ((vc0 >> 4) + c) * 8 + j;
+      const size_t i = (size_t)m * p.F + f;
+      split_bf16(a, p.ah[i], p.al[i]);
+    }
+  }
+};
+
+struct EpiLM {
+  struct P {
+    const bf16_t* w;   // [V][K]
+    int K, V;
+    float* logits;     // optional [M][V]
+    uint64_t* part;    // [n_tiles][M] argmax keys
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    return p.w + (size_t)(vc < p.V ? vc : p.V - 1) * p.K;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+                             int vc0, int m0, int M) {
+    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
+      const int ml = e / VC, c = e % VC;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const int v = vc0 + c;
+      const float z = tile[ml][c] * rs[ml];
+      tile[ml][c] = z;
+      if (p.logits && v < p.V) p.logits[(size_t)m * p.V + v] = z;
+    }
+    __syncthreads();
+    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+      uint64_t best = 0;
+      for (int c = 0; c < VC; ++c) {
+        const int v = vc0 + c;
+        if (v < p.V) best = umax64(best, argmax_key(tile[ml][c], (uint32_t)v));
+      }
+      p.part[(size_t)blockIdx.x * M + m0 + ml] = best;
+    }
+  }
+};
+
+// Context fusion for a few rows (the accepted rows appended each round):
+// y = [h_1 .. h_n] W_c^T as bf16 plus per-32-column sums of y^2; the RMSNorm
+// pass runs afterwards.
+struct EpiFuseRows {
+  struct P {
+    const bf16_t* w;  // W_c [D][K]
+    int K, D;
+    bf16_t* out;      // [M][D]
+    float* ssq;       // [M][D/32]
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+                             int M) {
+    static_assert(VC == 32, "one 32-column norm group per workgroup");
+    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
+      const int ml = e / VC, c = e % VC;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const float y = tile[ml][c];
+      p.out[(size_t)m * p.D + vc0 + c] = f2bf(y);
+      tile[ml][c] = y * y;
+    }
+    __syncthreads();
+    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+      float s = 0.f;
+      for (int c = 0; c < VC; ++c) s += tile[ml][c];
+      p.ssq[(size_t)(m0 + ml) * (p.D / 32) + vc0 / 32] = s;
+    }
+  }
+};
+
+// KV injection for a few rows: virtual columns run over every layer's K and
+// V; within K heads the RoPE pairs share a 16-column group as in EpiQKV.
+struct EpiInjectRows {
+  struct P {
+    const bf16_t* wk[kMaxLayers];
+    const bf16_t* wv[kMaxLayers];
+    int D, Hkv, hd, pos0, cap;
+    double log2_theta;
+    bf16_t* kv;
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    const int kvd = p.Hkv * p.hd;
+    const int i = vc / (2 * kvd), r = vc % (2 * kvd);
+    if (r < kvd) {
+      const int h = r / p.hd, d = paired_dim(r % p.hd, p.hd);
+      return p.wk[i] + (size_t)(h * p.hd + d) * p.D;
+    }
+    return p.wv[i] + (size_t)(r - kvd) * p.D;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+                             int M) {
+    const int kvd = p.Hkv * p.hd;
+    const size_t plane = (size_t)p.cap * p.hd;
+    constexpr int NG = VC / 16;
+    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
+      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const int pos = p.pos0 + m;
+      const int vc = vc0 + c * 16;
+      const int i = vc / (2 * kvd), r = vc % (2 * kvd);
+      const float x1 = tile[ml][c * 16 + j], x2 = tile[ml][c * 16 + j + 8];
+      if (r < kvd) {
+        const int h = r / p.hd, d = ((r % p.hd) >> 1) + j;
+        float cs, sn;
+        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        bf16_t* k = p.kv + (size_t)((2 * i) * p.Hkv + h) * plane + (size_t)pos * p.hd;
+        k[d] = f2bf(x1 * cs - x2 * sn);
+        k[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
+      } else {
+        const int h = (r - kvd) / p.hd, d0 = (r - kvd) % p.hd + j;
+        bf16_t* v = p.kv + (size_t)((2 * i + 1) * p.Hkv + h) * plane;
+        v[(size_t)d0 * p.cap + pos] = f2bf(x1);
+        v[(size_t)(d0 + 8) * p.cap + pos] = f2bf(x2);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the streaming GEMM
+// ---------------------------------------------------------------------------
+
+template <int MT, int NCT, int NW, int U, bool LO, class Epi>
+__global__ void __launch_bounds__(NW * 64)
+skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
+  constexpr int VC = 16 * NCT;
+  constexpr int ROWS = 16 * MT;
+  __shared__ float red[NW][MT * NCT * 4][64];
+  __shared__ float tile[ROWS][VC + 1];
+  __shared__ float rs[ROWS];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int vc0 = blockIdx.x * VC;
+  const int m0 = blockIdx.y * ROWS;
+  const int kq = 8 * (lane >> 4);
+
+  const bf16_t* wr[NCT];
+#pragma unroll
+  for (int c = 0; c < NCT; ++c) {
+    int vc = vc0 + c * 16 + (lane & 15);
+    vc = vc < n_vcols ? vc : n_vcols - 1;
+    wr[c] = Epi::wrow(ep, vc) + kq;
+  }
+  size_t aoff[MT];
+  bool av[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = m0 + m * 16 + (lane & 15);
+    av[m] = row < a.M;
+    aoff[m] = av[m] ? (size_t)in_row(a, row) * a.lda + kq : 0;
+  }
+
+  f32x4 acc[MT][NCT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KS = a.K >> 5;
+  for (int ks0 = w; ks0 < KS; ks0 += NW * U) {
+    bf16x8 bq[U][NCT], xh[U][MT], xl[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = ks0 + u * NW;
+      if (ks < KS) {
+        const int k = ks * 32;
+        const int sg = k / a.seg_k;
+        const bf16_t* hb = a.seg[sg] + (k - sg * a.seg_k);
+#pragma unroll
+        for (int c = 0; c < NCT; ++c) bq[u][c] = ld_bf16x8(wr[c] + k);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          xh[u][m] = av[m] ? ld_bf16x8(hb + aoff[m]) : zero_bf16x8();
+          if (LO) xl[u][m] = av[m] ? ld_bf16x8(a.xl + aoff[m] + k) : zero_bf16x8();
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ks0 + u * NW < KS) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int c = 0; c < NCT; ++c) {
+            acc[m][c] = mfma16x16x32(xh[u][m], bq[u][c], acc[m][c]);
+            if (LO) acc[m][c] = mfma16x16x32(xl[u][m], bq[u][c], acc[m][c]);
+          }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int c = 0; c < NCT; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[w][(m * NCT + c) * 4 + e][lane] = acc[m][c][e];
+
+  // RMSNorm row scale from the producer's per-32-column sums of x^2
+  for (int row = w; row < ROWS; row += NW) {
+    float s = 0.f;
+    if (a.ssq && m0 + row < a.M) {
+      const float* q = a.ssq + (size_t)in_row(a, m0 + row) * a.ssq_ld;
+      for (int g = lane; g < a.ssq_ld; g += 64) s += q[g];
+      s = wave_sum(s);
+    }
+    if (lane == 0) rs[row] = a.ssq ? rsqrtf(s / (float)a.K + a.eps) : 1.f;
+  }
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < MT * NCT * 256; e += NW * 64) {
+    const int l = e & 63, q4 = (e >> 6) & 3, c = (e >> 8) % NCT, m = e / (256 * NCT);
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) s += red[ww][(m * NCT + c) * 4 + q4][l];
+    tile[m * 16 + (l >> 4) * 4 + q4][c * 16 + (l & 15)] = s;
+  }
+  __syncthreads();
+  Epi::template run<ROWS, VC>(ep, tile, rs, vc0, m0, a.M);
+}
+
+// ---------------------------------------------------------------------------
+// embedding of the block and the drafted-token reduction
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256)
+embed_block(const bf16_t* E, int V, int D, const int32_t* anchors, int mask_id,
+            int Bl, const bf16_t* gain, float* x, bf16_t* xh, bf16_t* xl,
+            float* ssq, int32_t* block_out) {
+  const int m = blockIdx.x, s = m / Bl, r = m % Bl;
+  int id = r == 0 ? anchors[s] : mask_id;
+  id = id < 0 ? 0 : (id >= V ? V - 1 : id);  // keep the gather in bounds
+  if (r == 0 && threadIdx.x == 0) block_out[s * Bl] = id;
+  const bf16_t* e = E + (size_t)id * D;
+  for (int n0 = 0; n0 < D; n0 += 256) {
+    const int n = n0 + threadIdx.x;
+    float sq = 0.f;
+    if (n < D) {
+      const float v = bf2f(e[n]);
+      const size_t i = (size_t)m * D + n;
+      x[i] = v;
+      split_bf16(v * bf2f(gain[n]), xh[i], xl[i]);
+      sq = v * v;
+    }
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+    if (n < D && (threadIdx.x & 31) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+lm_argmax_reduce(const uint64_t* part, int n_tiles, int M_lm, int Bl,
+                 int32_t* block_out) {
+  const int m = blockIdx.x;
+  uint64_t best = 0;
+  for (int t = threadIdx.x; t < n_tiles; t += 256) best = umax64(best, part[(size_t)t * M_lm + m]);
+  best = wave_max_u64(best);
+  __shared__ uint64_t wbest[4];
+  if ((threadIdx.x & 63) == 0) wbest[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = umax64(umax64(wbest[0], wbest[1]), umax64(wbest[2], wbest[3]));
+    const int g = Bl - 1;
+    block_out[(m / g) * Bl + 1 + (m % g)] = (int32_t)argmax_key_index(best);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+constexpr int kNCT = 2, kNW = 8, kU = 4;
+constexpr int kVC = 16 * kNCT;
+
+template <class Epi, bool LO = true>
+hipError_t launch_skinny(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
+                         hipStream_t st) {
+  const int tiles = (n_vcols + kVC - 1) / kVC;
+  // MT row tiles of 16 per workgroup; more rows than 64 take several row
+  // blocks (grid.y), each streaming the weights again
+  if (a.M <= 16)
+    hipLaunchKernelGGL((skinny_gemm<1, kNCT, kNW, kU, LO, Epi>), dim3(tiles, 1), dim3(kNW * 64), 0, st, a, ep, n_vcols);
+  else if (a.M <= 32)
+    hipLaunchKernelGGL((skinny_gemm<2, kNCT, kNW, kU, LO, Epi>), dim3(tiles, 1), dim3(kNW * 64), 0, st, a, ep, n_vcols);
+  else
+    hipLaunchKernelGGL((skinny_gemm<4, kNCT, kNW, 2, LO, Epi>), dim3(tiles, (a.M + 63) / 64), dim3(kNW * 64), 0, st, a, ep, n_vcols);
+  return hipGetLastError();
+}
+
+SkinnyA make_a(const bf16_t* xh, const bf16_t* xl, int lda, int M, int K,
+               const float* ssq, int ssq_ld, float eps) {
+  SkinnyA a;
+  a.xh = xh; a.xl = xl; a.lda = lda; a.M = M; a.K = K;
+  for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = xh;
+  a.seg_k = K;
+  a.a_group = M > 0 ? M : 1; a.a_stride = 0; a.a_off = 0;
+  a.ssq = ssq; a.ssq_ld = ssq_ld; a.eps = eps;
+  return a;
+}
+}  // namespace
+
+int skinny_tile_cols() { return kVC; }
+int skinny_max_rows() { return 64; }
+
+hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
+  SkinnyA a = make_a(F.feats[0], nullptr, (int)F.ld, F.T, F.n_feat * F.D, nullptr, 0, F.eps);
+  for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = i < F.n_feat ? F.feats[i] : F.feats[0];
+  a.seg_k = F.D;
+  EpiFuseRows::P p;
+  p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.out = F.out; p.ssq = F.ssq;
+  hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, st);
+  if (e != hipSuccess) return e;
+  return launch_fuse_normalize(F.out, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
+}
+
+hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
+  SkinnyA a = make_a(I.ctx, nullptr, I.D, I.T, I.D, nullptr, 0, 0.f);
+  EpiInjectRows::P p;
+  for (int i = 0; i < kMaxLayers; ++i) {
+    p.wk[i] = i < I.L ? I.wk[i] : I.wk[0];
+    p.wv[i] = i < I.L ? I.wv[i] : I.wv[0];
+  }
+  p.D = I.D; p.Hkv = I.Hkv; p.hd = I.hd; p.pos0 = I.pos0; p.cap = I.cap;
+  p.log2_theta = I.log2_theta; p.kv = I.kv;
+  return launch_skinny<EpiInjectRows, false>(a, p, I.L * 2 * I.Hkv * I.hd, st);
+}
+
+hipError_t launch_embed(const DraftLaunch& L, hipStream_t st) {
+  hipLaunchKernelGGL(embed_block, dim3(L.M), dim3(256), 0, st, L.embed, L.V, L.D,
+                     L.anchors, L.mask_id, L.Bl, L.gain0, L.x, L.xh, L.xl, L.ssq,
+                     L.block_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
+                      const bf16_t* wk, const bf16_t* wv, hipStream_t st) {
+  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+  EpiQKV::P p;
+  p.wq = wq; p.wk = wk; p.wv = wv; p.D = L.D; p.Hq = L.Hq; p.Hkv = L.Hkv;
+  p.hd = L.hd; p.Bl = L.Bl; p.layer = layer; p.log2_theta = L.log2_theta;
+  p.q_out = L.q; p.q_lo = L.q_lo; p.seqs = *L.seqs;
+  return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, st);
+}
+
+hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
+                        const bf16_t* al, int K, const bf16_t* gain_next,
+                        float* hidden, hipStream_t st) {
+  SkinnyA a = make_a(ah, al, K, L.M, K, nullptr, 0, L.eps);
+  EpiResid::P p;
+  p.w = w; p.K = K; p.D = L.D; p.x = L.x; p.xh = L.xh; p.xl = L.xl;
+  p.gain = gain_next; p.ssq = L.ssq; p.hidden = hidden;
+  return launch_skinny<EpiResid>(a, p, L.D, st);
+}
+
+hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
+                         hipStream_t st) {
+  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+  EpiSwiglu::P p;
+  p.wg = wg; p.wu = wu; p.K = L.D; p.F = L.F; p.ah = L.act_h; p.al = L.act_l;
+  return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, st);
+}
+
+hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
+                     hipStream_t st) {
+  const int g = L.Bl - 1;
+  const int M_lm = L.n_seqs * g;
+  SkinnyA a = make_a(L.xh, L.xl, L.D, M_lm, L.D, L.ssq, L.D / 32, L.eps);
+  a.a_group = g; a.a_stride = L.Bl; a.a_off = 1;
+  EpiLM::P p;
+  p.w = w_lm; p.K = L.D; p.V = L.V; p.logits = logits; p.part = L.lm_part;
+  hipError_t e = launch_skinny<EpiLM>(a, p, L.V, st);
+  if (e != hipSuccess) return e;
+  const int tiles = (L.V + kVC - 1) / kVC;
+  hipLaunchKernelGGL(lm_argmax_reduce, dim3(M_lm), dim3(256), 0, st, L.lm_part,
+                     tiles, M_lm, L.Bl, L.block_out);
+  return hipGetLastError();
+}
+
+}  // namespace dfl

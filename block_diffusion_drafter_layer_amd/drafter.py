@@ -1,0 +1,119 @@
+"""Torch-side convenience around the C ABI: device memory and streams only.
+
+``Drafter`` owns a handle, its workspace tensor and helper constructors for
+KV-cache buffers; each method is one ABI call. Nothing here computes any part
+of the method.
+"""
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import binding as B
+
+
+class KVCache:
+    """A dflash_kv plus the device tensor that backs it."""
+
+    def __init__(self, cfg: B.dflash_config, max_ctx: int, device):
+        nbytes = B.dflash_kv_bytes(cfg, max_ctx)
+        if nbytes == 0:
+            raise ValueError("invalid config or max_ctx for a KV cache")
+        self.buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=device)
+        self.kv = B.dflash_kv(self.buf.data_ptr(), max_ctx, 0)
+        self.cap = B.dflash_kv_row_capacity(cfg, max_ctx)
+        self.n_layers, self.n_kv_heads, self.head_dim = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+
+    @property
+    def len(self) -> int:
+        return self.kv.len
+
+    def planes(self):
+        """View [L, 2, Hkv, cap*hd]: K planes are [cap, hd], V planes [hd, cap]."""
+        return self.buf.view(self.n_layers, 2, self.n_kv_heads, self.cap * self.head_dim)
+
+    def k_view(self, layer: int):
+        """[Hkv, cap, hd] view of one layer's K (position-major)."""
+        return self.planes()[layer, 0].view(self.n_kv_heads, self.cap, self.head_dim)
+
+    def v_view(self, layer: int):
+        """[Hkv, hd, cap] view of one layer's V (dim-major)."""
+        return self.planes()[layer, 1].view(self.n_kv_heads, self.head_dim, self.cap)
+
+
+class Drafter:
+    def __init__(self, cfg: B.dflash_config, weights: Dict, max_seqs: int = 1,
+                 max_tokens: int = 2048, device="cuda", stream: Optional[torch.cuda.Stream] = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.weights = B.Weights(weights)
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        self.h = B.dflash_create(cfg, self.weights.struct, self.stream.cuda_stream)
+        nbytes = B.dflash_workspace_bytes(cfg, max_seqs, max_tokens)
+        if nbytes == 0:
+            raise ValueError("invalid workspace request")
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        B.dflash_set_workspace(self.h, self.ws.data_ptr(), nbytes, max_seqs, max_tokens)
+        self.max_seqs, self.max_tokens = max_seqs, max_tokens
+
+    def close(self):
+        if self.h is not None:
+            B.dflash_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_kv(self, max_ctx: int) -> KVCache:
+        return KVCache(self.cfg, max_ctx, self.device)
+
+    def fuse_context(self, feats: Sequence[torch.Tensor], out: Optional[torch.Tensor] = None):
+        T, ld = feats[0].shape[0], feats[0].stride(0)
+        if out is None:
+            out = torch.empty(T, self.cfg.hidden, dtype=torch.bfloat16, device=self.device)
+        B.dflash_fuse_context(self.h, [f.data_ptr() for f in feats], ld, T, out.data_ptr())
+        return out
+
+    def inject_kv(self, kv: KVCache, ctx_feat: torch.Tensor, pos0: Optional[int] = None):
+        pos0 = kv.len if pos0 is None else pos0
+        B.dflash_inject_kv(self.h, kv.kv, ctx_feat.data_ptr(), ctx_feat.shape[0], pos0)
+
+    def kv_trim(self, kv: KVCache, keep: int):
+        B.dflash_kv_trim(self.h, kv.kv, keep)
+
+    def draft_block(self, kvs: Sequence[KVCache], anchors: torch.Tensor, block_len: Optional[int] = None,
+                    block_out: Optional[torch.Tensor] = None, hidden: bool = False,
+                    logits: bool = False):
+        bl = self.cfg.block_size if block_len is None else block_len
+        n = len(kvs)
+        if block_out is None:
+            block_out = torch.empty(n, bl, dtype=torch.int32, device=self.device)
+        hid = (torch.empty(self.cfg.n_layers, n * bl, self.cfg.hidden, dtype=torch.float32,
+                           device=self.device) if hidden else None)
+        lg = (torch.empty(n, max(bl - 1, 0), self.cfg.vocab, dtype=torch.float32, device=self.device)
+              if logits and bl > 1 else None)
+        B.dflash_draft_block(self.h, [k.kv for k in kvs], anchors.data_ptr(), bl, block_out.data_ptr(),
+                             hid.data_ptr() if hid is not None else 0,
+                             lg.data_ptr() if lg is not None else 0)
+        return block_out, hid, lg
+
+    def verify(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
+               draft_logits: Optional[torch.Tensor] = None, temperature: float = 0.0,
+               seed: int = 0, philox_offset: int = 0, tau: Optional[torch.Tensor] = None,
+               bonus: Optional[torch.Tensor] = None):
+        n, bl = block_ids.shape
+        tau = torch.empty(n, dtype=torch.int32, device=self.device) if tau is None else tau
+        bonus = torch.empty(n, dtype=torch.int32, device=self.device) if bonus is None else bonus
+        B.dflash_verify(self.h, n, bl, block_ids.data_ptr(), target_logits.data_ptr(),
+                        draft_logits.data_ptr() if draft_logits is not None else 0,
+                        temperature, seed, philox_offset, tau.data_ptr(), bonus.data_ptr())
+        return tau, bonus
+
+
+def config_from(dc) -> B.dflash_config:
+    """dflash_config from a workload description (synth.DraftConfig)."""
+    return B.make_config(dc.hidden, dc.n_feat, dc.n_layers, dc.n_heads, dc.n_kv_heads,
+                         dc.head_dim, dc.ffn, dc.vocab, dc.block_size, dc.mask_token_id,
+                         dc.rms_eps, dc.rope_theta)

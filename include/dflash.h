@@ -1,0 +1,273 @@
+/*
+ * dflash.h - C ABI of the DFlash drafter hot path on MI355X (gfx950).
+ *
+ * DFlash drafts a whole block in one forward pass: the anchor token (the last
+ * confirmed token) followed by block_size-1 mask tokens, conditioned on a
+ * fused feature of the target model's hidden states that is injected as extra
+ * K/V entries into every draft layer; the drafted block is then verified
+ * against the target's logits.
+ *
+ * Sources: the four web pages on DFlash, cited as
+ *   [Tut]  A3-dflash tutorial (CCODING04 llm-paper-tutorials)
+ *   [Sum]  papercache summary "DFlash: Block Diffusion for Flash Speculative Decoding"
+ *   [Note] tom-jerr paper-reading notes "DFLASH"
+ *   [Code] txtmix code-reading article on the z-lab dflash repository
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     allocates no device memory: scratch space comes from the workspace the
+ *     caller hands over with dflash_set_workspace.
+ *   - Weights are borrowed for the handle's lifetime and never written.
+ *     Matrices are bf16, row-major, nn.Linear layout [out_features, in_features].
+ *   - Calls only enqueue work on the handle's HIP stream; results are valid
+ *     after that stream is synchronised. Host-side metadata (dflash_kv.len) is
+ *     updated when the call returns.
+ *   - All argument checks run on the host before anything is enqueued. On any
+ *     error nothing is written and every dflash_kv.len is unchanged.
+ *   - DFLASH_E_DEVICE reports a failed HIP launch; the handle should then be
+ *     destroyed.
+ *   - A handle is not re-entrant: use one handle per host thread and stream.
+ *   - dflash_last_error() returns a thread-local text for the last failure.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_E_NULL = 1,      /* a required pointer is NULL */
+  DFLASH_E_CONFIG = 2,    /* configuration invalid or unsupported */
+  DFLASH_E_SHAPE = 3,     /* a size or index argument is out of range */
+  DFLASH_E_CAPACITY = 4,  /* a cache or the workspace is too small */
+  DFLASH_E_ALIGN = 5,     /* a pointer or stride is not suitably aligned */
+  DFLASH_E_DEVICE = 6,    /* a HIP call failed */
+  DFLASH_E_STATE = 7      /* call made in the wrong state (e.g. no workspace) */
+} dflash_status;
+
+/*
+ * Model dimensions and the draft configuration. The required keys mirror the
+ * checkpoint's dflash_config ([Code] section 11): mask_token_id has no
+ * default (a negative value is DFLASH_E_CONFIG); block_size defaults to 16.
+ * Supported: hidden % 64 == 0, head_dim in {16, 32, 64, 128},
+ * n_heads % n_kv_heads == 0 with n_heads / n_kv_heads <= 16, ffn % 32 == 0, (n_heads + 2*n_kv_heads)*head_dim % 32 == 0,
+ * 1 <= block_size <= 16, n_feat_layers in 1..8.
+ */
+typedef struct dflash_config {
+  int32_t hidden;         /* D: hidden size of target and draft */
+  int32_t n_feat_layers;  /* number of fused target layers (5 on the pages) */
+  int32_t n_layers;       /* draft decoder layers */
+  int32_t n_heads;        /* query heads */
+  int32_t n_kv_heads;     /* key/value heads (grouped-query attention) */
+  int32_t head_dim;
+  int32_t ffn;            /* SwiGLU intermediate size */
+  int32_t vocab;
+  int32_t block_size;     /* 0 -> 16 */
+  int32_t mask_token_id;  /* required, 0 <= id < vocab */
+  float rms_eps;          /* <= 0 -> 1e-6 */
+  float rope_theta;       /* <= 0 -> 1e6 */
+} dflash_config;
+
+/* One draft decoder layer (pre-norm attention + SwiGLU MLP), bf16. */
+typedef struct dflash_layer_weights {
+  const void* wq;         /* [n_heads*head_dim, D] */
+  const void* wk;         /* [n_kv_heads*head_dim, D] */
+  const void* wv;         /* [n_kv_heads*head_dim, D] */
+  const void* wo;         /* [D, n_heads*head_dim] */
+  const void* w_gate;     /* [ffn, D] */
+  const void* w_up;       /* [ffn, D] */
+  const void* w_down;     /* [D, ffn] */
+  const void* attn_norm;  /* [D] RMSNorm gain before attention */
+  const void* mlp_norm;   /* [D] RMSNorm gain before the MLP */
+} dflash_layer_weights;
+
+/*
+ * All parameters. The embedding and LM head are the target's own, shared and
+ * frozen ([Tut] section 2.2.3; [Code] section 3). w_c is the fusion matrix
+ * W_c of [Tut] section 2.1.2, D x (n_feat_layers*D).
+ */
+typedef struct dflash_weights {
+  const void* w_c;         /* [D, n_feat_layers*D] */
+  const void* ctx_norm;    /* [D] RMSNorm gain of the fused feature */
+  const void* embed;       /* [vocab, D] */
+  const void* lm_head;     /* [vocab, D] */
+  const void* final_norm;  /* [D] RMSNorm gain before the LM head */
+  const dflash_layer_weights* layers;  /* host array [n_layers], copied */
+} dflash_weights;
+
+/*
+ * One sequence's draft KV cache: the context K/V of every draft layer
+ * ([Sum] section 4.1: the projected target features are kept in the draft
+ * model's KV cache and reused across drafting rounds).
+ *
+ * `base` is a caller-allocated device buffer of dflash_kv_bytes(cfg, max_ctx)
+ * bytes, 256-byte aligned. With cap = dflash_kv_row_capacity(cfg, max_ctx),
+ * H = n_kv_heads, hd = head_dim, the bf16 elements are laid out as
+ *   K (after RoPE): layer i, head g, position p, dim d at
+ *       ((2*i + 0)*H + g)*cap*hd + p*hd + d
+ *   V:              layer i, head g, position p, dim d at
+ *       ((2*i + 1)*H + g)*cap*hd + d*cap + p
+ * i.e. K is position-major and V dim-major within each head. Positions
+ * len .. len+block_size-1 are scratch rows used by dflash_draft_block for the
+ * block's own K/V; positions >= len are never part of the context.
+ * `len` is host metadata: the number of context positions held.
+ */
+typedef struct dflash_kv {
+  void* base;
+  int32_t max_ctx;   /* context positions the buffer can hold */
+  int32_t len;       /* current context length */
+} dflash_kv;
+
+typedef struct dflash_handle dflash_handle;
+
+/* Bytes of a KV buffer for max_ctx context positions (plus block scratch). */
+size_t dflash_kv_bytes(const dflash_config* cfg, int32_t max_ctx);
+/* Row capacity `cap` used in the layout above (>= max_ctx + block_size). */
+int32_t dflash_kv_row_capacity(const dflash_config* cfg, int32_t max_ctx);
+
+/*
+ * Workspace bytes for draft calls of up to max_seqs sequences and fuse/inject
+ * calls of up to max_tokens rows. 0 on an invalid config.
+ */
+size_t dflash_workspace_bytes(const dflash_config* cfg, int32_t max_seqs,
+                              int32_t max_tokens);
+
+/*
+ * Create a handle. `stream` is a hipStream_t (NULL = the default stream).
+ * Copies the config and the weight pointers; validates them (DFLASH_E_CONFIG,
+ * DFLASH_E_NULL, DFLASH_E_ALIGN for matrices not 16-byte aligned).
+ */
+dflash_status dflash_create(const dflash_config* cfg, const dflash_weights* w,
+                            void* stream, dflash_handle** out);
+dflash_status dflash_destroy(dflash_handle* h);
+dflash_status dflash_set_stream(dflash_handle* h, void* stream);
+
+/*
+ * Hand over the workspace: a device buffer of at least
+ * dflash_workspace_bytes(cfg, max_seqs, max_tokens) bytes, 256-byte aligned,
+ * owned by the caller and not touched by anyone else while the handle uses it.
+ */
+dflash_status dflash_set_workspace(dflash_handle* h, void* ws, size_t bytes,
+                                   int32_t max_seqs, int32_t max_tokens);
+
+/*
+ * Context fusion ([Tut] sections 2.1.1-2.1.2; [Code] section 5):
+ *   ctx_out[t] = RMSNorm(W_c [h_1[t]; ...; h_n[t]]) * ctx_norm, eps inside the
+ *   square root.
+ * feats: host array of n_feat_layers device pointers, each bf16 [n_tokens, ld]
+ * (row stride ld elements, ld >= D, ld % 8 == 0), in increasing layer order;
+ * the concatenation is never materialised. ctx_out: bf16 [n_tokens, D].
+ * 1 <= n_tokens <= max_tokens of the workspace.
+ */
+dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats,
+                                  int64_t ld, int32_t n_tokens, void* ctx_out);
+
+/*
+ * KV injection ([Tut] section 2.1.2: K_i = [W_i^K H_t ; ...],
+ * V_i = [W_i^V H_t ; ...]; [Code] section 5): for every draft layer i and
+ * t < n_tokens, K = RoPE(wk_i ctx_feat[t], pos0 + t) and V = wv_i ctx_feat[t]
+ * are written at position pos0 + t. The cache is first cut back to pos0
+ * (0 <= pos0 <= kv->len), so a trim of rejected positions followed by an
+ * append of the accepted prefix is one call ([Code] section 9).
+ * On success kv->len = pos0 + n_tokens (<= kv->max_ctx, else DFLASH_E_CAPACITY).
+ * ctx_feat: bf16 [n_tokens, D]; 1 <= n_tokens <= max_tokens.
+ */
+dflash_status dflash_inject_kv(dflash_handle* h, dflash_kv* kv,
+                               const void* ctx_feat, int32_t n_tokens,
+                               int32_t pos0);
+
+/* Trim: kv->len = keep_len (0 <= keep_len <= kv->len). Host only. */
+dflash_status dflash_kv_trim(dflash_handle* h, dflash_kv* kv, int32_t keep_len);
+
+/*
+ * One draft forward over n_seqs blocks ([Code] sections 6 and 9;
+ * [Tut] section 2.1.2):
+ *   block row r of sequence s holds anchor_ids[s] (r = 0) or mask_token_id,
+ *   at position kvs[s]->len + r; every row attends, without any mask, to the
+ *   sequence's context K/V and to the block's own K/V; the LM head and argmax
+ *   are applied to rows 1..block_len-1.
+ * anchor_ids: device int32 [n_seqs].
+ * block_out:  device int32 [n_seqs, block_len] - column 0 is the anchor,
+ *             columns 1.. the drafted tokens (lowest index on exact ties);
+ *             this is the block dflash_verify takes.
+ * hidden_out: optional device fp32 [n_layers, n_seqs*block_len, D] - residual
+ *             stream after every layer (row s*block_len + r).
+ * logits_out: optional device fp32 [n_seqs, block_len-1, vocab].
+ * 1 <= n_seqs <= max_seqs; 1 <= block_len <= block_size; each kvs[s]->len is
+ * left unchanged (the block's K/V go to scratch rows).
+ */
+dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs,
+                                 dflash_kv* const* kvs,
+                                 const int32_t* anchor_ids, int32_t block_len,
+                                 int32_t* block_out, float* hidden_out,
+                                 float* logits_out);
+
+/*
+ * Verification of n_seqs drafted blocks against the target's logits.
+ * temperature == 0: greedy ([Code] section 8): posterior = argmax of each
+ *   target row (lowest index on ties); accepted a = length of the prefix with
+ *   block[j+1] == posterior[j]; bonus = posterior[a]; tau = a + 1.
+ * temperature > 0: p/q rejection sampling ([Code] section 8): with
+ *   p_j = softmax(target_logits[j]/T), q_j = softmax(draft_logits[j]/T) in fp64,
+ *   row j is accepted iff u_j < p_j(x)/q_j(x), x = block[j+1]; at the first
+ *   rejection the bonus is drawn from max(p_j - q_j, 0) normalised; when all
+ *   rows are accepted it is drawn from p_{block_len-1}. Uniforms come from
+ *   Philox4x64-10 with key (seed, 0) and counter
+ *   (philox_offset + row, sequence, purpose, 0), purpose 0 = accept test,
+ *   1 = replacement/bonus draw; u = (word0 >> 11) * 2^-53. A draw picks the
+ *   smallest v whose running fp64 sum in vocab order exceeds u * total.
+ * block_ids:     device int32 [n_seqs, block_len]
+ * target_logits: device fp32 [n_seqs, block_len, vocab]
+ * draft_logits:  device fp32 [n_seqs, block_len-1, vocab]; NULL iff T == 0
+ * tau_out, bonus_out: device int32 [n_seqs]; 1 <= tau <= block_len.
+ * 1 <= n_seqs <= max_seqs; 1 <= block_len <= block_size.
+ */
+dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                            const int32_t* block_ids, const float* target_logits,
+                            const float* draft_logits, float temperature,
+                            uint64_t seed, uint64_t philox_offset,
+                            int32_t* tau_out, int32_t* bonus_out);
+
+/*
+ * Host helper ([Code] section 5, build_target_layer_ids): n_feat target layer
+ * indices spread evenly over 1 .. n_target_layers-3 (0-based), rounded to
+ * nearest; the middle layer when n_feat == 1. out: host int32 [n_feat].
+ */
+dflash_status dflash_target_layer_ids(int32_t n_target_layers, int32_t n_feat,
+                                      int32_t* out);
+
+/*
+ * Optional timing of the launches a handle makes (tracing). Stages:
+ *   0 embed, 1 qkv, 2 attention (split + merge), 3 o_proj, 4 gate_up,
+ *   5 down_proj, 6 lm_head (GEMM + argmax reduction), 7 fuse_context,
+ *   8 inject_kv, 9 verify.
+ * With bit k of stage_mask set, every launch of stage k is bracketed by two
+ * hipEvents recorded on the handle's stream, up to max_records launches
+ * (later ones are not recorded). The events are host-side objects created
+ * here; no device memory is allocated. stage_mask 0 disables timing and
+ * releases the events. Enabling clears previous records.
+ */
+dflash_status dflash_profile_enable(dflash_handle* h, uint32_t stage_mask,
+                                    int32_t max_records);
+/*
+ * Read the records made since enabling (waits for their events): up to
+ * `cap` entries of stage id and elapsed milliseconds, in launch order;
+ * *n_out receives the number of records. Clears the records.
+ */
+dflash_status dflash_profile_read(dflash_handle* h, int32_t cap, int32_t* stage_out,
+                                  float* ms_out, int32_t* n_out);
+const char* dflash_stage_name(int32_t stage);
+
+const char* dflash_status_str(dflash_status s);
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -1,0 +1,162 @@
+"""The C ABI on the host: the library loads, exports every declared symbol,
+and rejects bad arguments before anything reaches the device.
+
+No call here launches GPU work: every checked path returns during host-side
+validation (weights are fake, never dereferenced, aligned addresses)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import oracle as O
+from block_diffusion_drafter_layer_amd import binding as B
+from block_diffusion_drafter_layer_amd.drafter import config_from
+from synth import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dflash.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 14
+    lib = C.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(8):
+        assert B.dflash_status_str(s) and B.dflash_status_str(s) != "unknown status"
+
+
+def _cfg(i=1, **kw):
+    c = config_from(CONFIGS[i])
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_kv_and_workspace_sizes():
+    c = _cfg(1)
+    cap = B.dflash_kv_row_capacity(c, 2048)
+    assert cap >= 2048 + 16 and cap % 64 == 0
+    assert B.dflash_kv_bytes(c, 2048) == 5 * 2 * 8 * cap * 128 * 2
+    assert B.dflash_workspace_bytes(c, 1, 2048) > 0
+    assert B.dflash_workspace_bytes(c, 2, 2048) > B.dflash_workspace_bytes(c, 1, 2048)
+    bad = _cfg(1, mask_token_id=-1)
+    assert B.dflash_kv_bytes(bad, 2048) == 0 and B.dflash_workspace_bytes(bad, 1, 16) == 0
+
+
+def test_target_layer_ids_helper_matches_rule():
+    for n in (16, 28, 36, 48, 64):
+        assert B.dflash_target_layer_ids(n, 5) == O.target_layer_ids(n, 5)
+    assert B.dflash_target_layer_ids(36, 1) == [18]
+    with pytest.raises(B.DflashError):
+        B.dflash_target_layer_ids(6, 5)
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced
+
+
+def _weights(n_layers, null=None, misalign=None):
+    layers = (B.dflash_layer_weights * n_layers)()
+    for i in range(n_layers):
+        for f, _ in B.dflash_layer_weights._fields_:
+            setattr(layers[i], f, FAKE)
+    w = B.dflash_weights(FAKE, FAKE, FAKE, FAKE, FAKE, C.cast(layers, C.POINTER(B.dflash_layer_weights)))
+    if null:
+        setattr(w, null, None)
+    if misalign:
+        setattr(w, misalign, FAKE + 2)
+    return w, layers
+
+
+def test_create_rejects_bad_configs_and_weights():
+    c = _cfg(1)
+    w, keep = _weights(c.n_layers)
+    for field, val in [("mask_token_id", -1), ("mask_token_id", c.vocab), ("head_dim", 96),
+                       ("hidden", 100), ("n_kv_heads", 5), ("block_size", 17), ("ffn", 100)]:
+        bad = _cfg(1, **{field: val})
+        with pytest.raises(B.DflashError) as e:
+            B.dflash_create(bad, w)
+        assert e.value.status == 2, field
+    wn, k2 = _weights(c.n_layers, null="lm_head")
+    with pytest.raises(B.DflashError) as e:
+        B.dflash_create(c, wn)
+    assert e.value.status == 1
+    wa, k3 = _weights(c.n_layers, misalign="embed")
+    with pytest.raises(B.DflashError) as e:
+        B.dflash_create(c, wa)
+    assert e.value.status == 5
+
+
+def _handle(i=1):
+    c = _cfg(i)
+    w, keep = _weights(c.n_layers)
+    h = B.dflash_create(c, w)
+    return c, h, (w, keep)
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+        return 0
+    except B.DflashError as e:
+        return e.status
+
+
+def test_calls_before_workspace_and_workspace_checks():
+    c, h, keep = _handle()
+    kv = B.dflash_kv(FAKE, 2048, 100)
+    assert _status(B.dflash_draft_block, h, [kv], FAKE, 16, FAKE) == 7
+    assert _status(B.dflash_fuse_context, h, [FAKE] * 5, c.hidden, 10, FAKE) == 7
+    need = B.dflash_workspace_bytes(c, 2, 64)
+    assert _status(B.dflash_set_workspace, h, FAKE, need - 1, 2, 64) == 4
+    assert _status(B.dflash_set_workspace, h, FAKE + 16, need, 2, 64) == 5
+    assert _status(B.dflash_set_workspace, h, FAKE, need, 0, 64) == 3
+    assert _status(B.dflash_set_workspace, h, FAKE, need, 2, 64) == 0
+    B.dflash_destroy(h)
+
+
+def test_argument_errors_leave_cache_lengths_unchanged():
+    c, h, keep = _handle()
+    B.dflash_set_workspace(h, FAKE, B.dflash_workspace_bytes(c, 2, 64), 2, 64)
+    kv = B.dflash_kv(FAKE, 256, 100)
+    # draft_block
+    assert _status(B.dflash_draft_block, h, [], FAKE, 16, FAKE) == 3
+    assert _status(B.dflash_draft_block, h, [kv, kv, kv], FAKE, 16, FAKE) == 3
+    assert _status(B.dflash_draft_block, h, [kv], FAKE, 17, FAKE) == 3
+    assert _status(B.dflash_draft_block, h, [kv], FAKE, 0, FAKE) == 3
+    assert _status(B.dflash_draft_block, h, [B.dflash_kv(FAKE, 50, 51)], FAKE, 16, FAKE) == 3
+    assert _status(B.dflash_draft_block, h, [B.dflash_kv(None, 50, 5)], FAKE, 16, FAKE) == 1
+    assert _status(B.dflash_draft_block, h, [B.dflash_kv(FAKE + 64, 50, 5)], FAKE, 16, FAKE) == 5
+    # inject: pos0 beyond len, capacity, too many tokens, bad pointers
+    assert _status(B.dflash_inject_kv, h, kv, FAKE, 10, 101) == 3
+    assert _status(B.dflash_inject_kv, h, B.dflash_kv(FAKE, 120, 100), FAKE, 64, 100) == 4
+    assert _status(B.dflash_inject_kv, h, kv, FAKE, 65, 0) == 3
+    assert _status(B.dflash_inject_kv, h, kv, FAKE + 2, 4, 0) == 5
+    assert _status(B.dflash_inject_kv, h, kv, FAKE, 0, 0) == 3
+    assert kv.len == 100
+    # fuse: n_tokens and ld
+    assert _status(B.dflash_fuse_context, h, [FAKE] * 5, c.hidden, 65, FAKE) == 3
+    assert _status(B.dflash_fuse_context, h, [FAKE] * 5, c.hidden - 8, 10, FAKE) == 5
+    assert _status(B.dflash_fuse_context, h, [FAKE] * 4 + [0], c.hidden, 10, FAKE) == 1
+    # verify
+    assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE, 0, -1.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE, 0, 1.0, 0, 0, FAKE, FAKE) == 1
+    assert _status(B.dflash_verify, h, 3, 16, FAKE, FAKE, 0, 0.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE + 4, 0, 0.0, 0, 0, FAKE, FAKE) == 5
+    # trim is host metadata only
+    assert _status(B.dflash_kv_trim, h, kv, 101) == 3
+    assert kv.len == 100
+    assert _status(B.dflash_kv_trim, h, kv, 37) == 0
+    assert kv.len == 37
+    B.dflash_destroy(h)

@@ -1,0 +1,109 @@
+"""GPU parity of context fusion (S1), KV injection (S2) and trim/append (S10)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_helpers import DEV, assert_close_rms, make, np32, poisoned_kv, say
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _fuse_check(dc, T, rows=None, gains="random", ld_pad=0):
+    say(f"fuse: config {dc.name} T={T} ld_pad={ld_pad}")
+    d, w = make(dc, max_tokens=T, gains=gains)
+    feats = synth.make_feats(dc, T, device=DEV)
+    if ld_pad:
+        feats = [torch.nn.functional.pad(f, (0, ld_pad))[:, :dc.hidden] for f in feats]
+    out = d.fuse_context(feats)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if rows is None else rows
+    ref = O.fuse_context([np32(f)[rows] for f in feats], np32(w["w_c"]), np32(w["ctx_norm"]), dc.rms_eps)
+    return assert_close_rms(np32(out)[rows], ref, what="fused context")
+
+
+def test_fuse_tiny():
+    _fuse_check(CONFIGS[0], 10)
+
+
+def test_fuse_ragged_tiles_and_row_stride():
+    # 300 rows: three 128-row tiles, the last one ragged; padded row stride
+    dc = CONFIGS[0].shrink(hidden=192, index=93)
+    _fuse_check(dc, 300, ld_pad=24)
+
+
+def test_fuse_d2048_sampled_rows():
+    dc = CONFIGS[4]
+    rng = np.random.default_rng(0)
+    _fuse_check(dc, 2048, rows=np.sort(rng.choice(2048, 96, replace=False)), gains="ones")
+
+
+@pytest.mark.slow
+def test_fuse_qwen_shape_sampled_rows():
+    dc = CONFIGS[1]
+    rng = np.random.default_rng(1)
+    _fuse_check(dc, 2048, rows=np.sort(rng.choice(2048, 64, replace=False)), gains="ones")
+
+
+def _inject_check(dc, T, pos0_chunks, rows=None, gains="ones"):
+    say(f"inject: config {dc.name} T={T} chunks={pos0_chunks}")
+    d, w = make(dc, max_tokens=max(pos0_chunks) if pos0_chunks else T, gains=gains)
+    ctx = synth.make_feats(dc, T, device=DEV)[0]  # any bf16 [T, D] context feature
+    kv = poisoned_kv(d, T + 32)
+    p = 0
+    for n in pos0_chunks:
+        d.inject_kv(kv, ctx[p:p + n], p)
+        p += n
+    assert kv.len == T
+    torch.cuda.synchronize()
+    rows = np.arange(T) if rows is None else rows
+    ctx_np = np32(ctx)
+    worst = 0.0
+    for i, lw in enumerate(w["layers"]):
+        for t in rows:
+            k, v = O.inject_kv(ctx_np[t:t + 1], np32(lw["wk"]), np32(lw["wv"]), int(t),
+                               dc.n_kv_heads, dc.head_dim, dc.rope_theta)
+            gk = np32(kv.k_view(i)[:, t, :])
+            gv = np32(kv.v_view(i)[:, :, t])
+            worst = max(worst, assert_close_rms(gk, k[0], what=f"K layer {i} row {t}"),
+                        assert_close_rms(gv, v[0], what=f"V layer {i} row {t}"))
+    return worst
+
+
+def test_inject_tiny_incremental():
+    _inject_check(CONFIGS[0], 10, [4, 3, 3])
+
+
+def test_inject_ragged_tiles():
+    dc = CONFIGS[1].shrink(hidden=256, n_layers=2, n_heads=4, n_kv_heads=2, ffn=512, vocab=512, index=94)
+    _inject_check(dc, 300, [300])
+
+
+def test_inject_qwen_shape_sampled_rows():
+    dc = CONFIGS[1]
+    rng = np.random.default_rng(2)
+    _inject_check(dc, 2048, [2048], rows=np.sort(rng.choice(2048, 24, replace=False)))
+
+
+def test_trim_then_append_overwrites_rejected_rows():
+    dc = CONFIGS[0]
+    d, w = make(dc, max_tokens=32)
+    ctx = synth.make_feats(dc, 30, device=DEV)[1]
+    junk = synth.make_feats(dc, 16, device=DEV)[2]
+    kv = poisoned_kv(d, 40)
+    d.inject_kv(kv, ctx[:10], 0)
+    S = 10
+    for tau in (3, 1, 5):
+        d.inject_kv(kv, junk[:6], S)      # a later-rejected write past S
+        d.kv_trim(kv, S)
+        d.inject_kv(kv, ctx[S:S + tau], S)
+        S += tau
+    assert kv.len == S == 19
+    ref = poisoned_kv(d, 40)
+    d.inject_kv(ref, ctx[:S], 0)
+    torch.cuda.synchronize()
+    for i in range(dc.n_layers):
+        assert_close_rms(np32(kv.k_view(i)[:, :S]), np32(ref.k_view(i)[:, :S]), tol=1e-2)
+        assert_close_rms(np32(kv.v_view(i)[:, :, :S]), np32(ref.v_view(i)[:, :, :S]), tol=1e-2)

@@ -1,0 +1,116 @@
+"""GPU parity of the draft forward (S3-S8) against the oracle: every layer's
+residual stream within 3e-2 x RMS, drafted tokens identical except where the
+oracle's top-2 gap is below 1e-2. KV buffers are filled with NaN first, so any
+read of a row outside [0, len + block_len) would show up as non-finite."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_helpers import (DEV, assert_hidden, assert_tokens, fill_context, make, np32,
+                         oracle_cache, poisoned_kv, say, synthetic_context, weights_np)
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dc, lens, bl=None, gains="ones", logits=False, max_ctx=None, oracle_seqs=None):
+    bl = dc.block_size if bl is None else bl
+    n = len(lens)
+    say(f"draft: config {dc.name} seqs={n} lens={list(lens)[:4]}... block_len={bl}")
+    d, w = make(dc, max_seqs=n, gains=gains)
+    kvs, ctxs = [], []
+    for s, S in enumerate(lens):
+        kv = poisoned_kv(d, max_ctx or max(lens) + 8)
+        ctx = synthetic_context(dc, S, seq=s)
+        if S:
+            fill_context(kv, ctx)
+        kvs.append(kv)
+        ctxs.append(ctx)
+    anchors = synth.make_anchor(dc, n=n)
+    block, hid, lg = d.draft_block(kvs, torch.from_numpy(anchors).to(DEV), bl, hidden=True, logits=logits)
+    torch.cuda.synchronize()
+    assert [k.len for k in kvs] == list(lens)
+    wn = weights_np(w)
+    sel = range(n) if oracle_seqs is None else oracle_seqs
+    hid = np32(hid).reshape(dc.n_layers, n, bl, dc.hidden)
+    block = block.cpu().numpy()
+    assert (block[:, 0] == anchors).all()
+    worst, flips = 0.0, 0
+    for s in sel:
+        orc = O.draft_block(dc, wn, [oracle_cache(dc, ctxs[s])], [int(anchors[s])], bl)
+        worst = max(worst, assert_hidden(hid[:, s:s + 1].reshape(dc.n_layers, bl, -1), orc["hidden"],
+                                         what=f"seq {s}"))
+        if bl > 1:
+            flips += assert_tokens(block[s:s + 1], orc, what=f"seq {s}")
+            if logits:
+                ref = orc["logits"][0]
+                g = np32(lg[s])
+                err = np.abs(g - ref).max()
+                assert err < 5e-2, f"logits max-abs {err}"
+    say(f"  worst hidden err / rms = {worst:.2e}, tolerated token flips = {flips}")
+    return worst
+
+
+def test_tiny_with_context():
+    _run(CONFIGS[0], [10], gains="random", logits=True)
+
+
+def test_tiny_empty_context():
+    _run(CONFIGS[0], [0], gains="random")
+
+
+def test_tiny_short_block_and_single_row():
+    _run(CONFIGS[0], [10], bl=3)
+    _run(CONFIGS[0], [10], bl=1)
+
+
+def test_tiny_ragged_sequences():
+    _run(CONFIGS[0].shrink(n_layers=2, index=95), [10, 3, 37, 0], gains="random")
+
+
+def test_mid_shape_multi_split_attention():
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024,
+                           vocab=4096, index=96)
+    _run(dc, [300, 1031], gains="random", logits=True)
+
+
+def test_mid_shape_head_dim_64_group_8():
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=16, n_kv_heads=2, head_dim=64,
+                           ffn=1024, vocab=2000, block_size=8, index=97)
+    _run(dc, [77], gains="random")
+
+
+def test_d2048_block8_full_size():
+    _run(CONFIGS[4], [2048], logits=True)
+
+
+def test_qwen_shape_block16_ctx2048_full_size():
+    _run(CONFIGS[1], [2048], logits=True)
+
+
+def test_qwen_shape_32_ragged_sequences_sampled():
+    dc = CONFIGS[3]
+    lens = synth.ragged_lengths(32)
+    _run(dc, list(lens), max_ctx=4096 + 8, oracle_seqs=[0, int(np.argmax(lens)), 31])
+
+
+def test_chained_fuse_inject_draft_tiny():
+    dc = CONFIGS[0]
+    say("chained fuse -> inject -> draft: tiny")
+    d, w = make(dc, gains="random")
+    feats = synth.make_feats(dc, dc.ctx_len, device=DEV)
+    ctx = d.fuse_context(feats)
+    kv = poisoned_kv(d, 32)
+    d.inject_kv(kv, ctx, 0)
+    anchors = synth.make_anchor(dc)
+    block, hid, _ = d.draft_block([kv], torch.from_numpy(anchors).to(DEV), hidden=True)
+    torch.cuda.synchronize()
+    wn = weights_np(w)
+    H = O.fuse_context([np32(f) for f in feats], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
+    cache = O.DraftCache(dc.n_layers)
+    O.cache_inject(cache, H, wn["layers"], dc, 0)
+    orc = O.draft_block(dc, wn, [cache], [int(anchors[0])])
+    assert_hidden(np32(hid), orc["hidden"])
+    assert_tokens(block.cpu().numpy(), orc)

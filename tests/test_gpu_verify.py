@@ -1,0 +1,99 @@
+"""GPU parity of verification (S9 greedy, S11 p/q) against the oracle.
+
+tau and bonus must be bit-exact; for p/q, rows whose accept test has
+|p/q - u| < 1e-4 or whose final draw lies within 1e-12 (relative) of a CDF
+boundary are excluded, as those decisions may flip under rounding order."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_helpers import DEV, make, say
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _greedy_case(dc, n_seqs, bl, rng, agreements):
+    ids = rng.integers(0, dc.vocab - 1, size=(n_seqs, bl)).astype(np.int32)
+    lg = torch.randn(n_seqs, bl, dc.vocab, generator=torch.Generator().manual_seed(int(rng.integers(1 << 30))))
+    for s in range(n_seqs):
+        synth.plant_agreement(lg[s], ids[s], agreements[s])
+    return ids, lg
+
+
+@pytest.mark.parametrize("ci,n_seqs,bl", [(0, 1, 4), (0, 3, 2), (1, 1, 16), (1, 4, 16), (1, 2, 9),
+                                          (0, 2, 1), (4, 1, 8)])
+def test_greedy_matches_oracle(ci, n_seqs, bl):
+    dc = CONFIGS[ci]
+    say(f"greedy verify: config {dc.name} n_seqs={n_seqs} block_len={bl}")
+    d, _ = make(dc, max_seqs=n_seqs)
+    rng = np.random.default_rng(100 + ci * 10 + bl)
+    for trial in range(6):
+        agree = [int(rng.integers(0, bl)) for _ in range(n_seqs)]
+        if trial == 0:
+            agree = [0] * n_seqs
+        if trial == 1:
+            agree = [bl - 1] * n_seqs
+        ids, lg = _greedy_case(dc, n_seqs, bl, rng, agree)
+        tau, bonus = d.verify(torch.from_numpy(ids).to(DEV), lg.to(DEV))
+        tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+        for s in range(n_seqs):
+            t, b = O.verify_greedy(ids[s], lg[s].numpy())
+            assert (tau[s], bonus[s]) == (t, b), (trial, s)
+            assert t == agree[s] + 1
+
+
+def test_greedy_ties_take_lowest_index():
+    dc = CONFIGS[0]
+    d, _ = make(dc, max_seqs=1)
+    lg = torch.zeros(1, 4, dc.vocab)
+    lg[0, :, 7] = 1.0
+    lg[0, :, 3] = 1.0
+    lg[0, :, 900] = 1.0
+    ids = torch.tensor([[5, 3, 3, 7]], dtype=torch.int32)
+    tau, bonus = d.verify(ids.to(DEV), lg.to(DEV))
+    assert O.verify_greedy(ids[0].numpy(), lg[0].numpy()) == (3, 3)
+    assert (int(tau[0]), int(bonus[0])) == (3, 3)
+
+
+def _pq_case(dc, bl, seed, rng):
+    V = dc.vocab
+    g = torch.Generator().manual_seed(seed)
+    T = torch.randn(bl, V, generator=g)
+    Q = torch.randn(bl - 1, V, generator=g)
+    return T, Q
+
+
+@pytest.mark.parametrize("ci,bl,temp", [(4, 8, 1.0), (0, 4, 1.0), (0, 4, 0.7), (4, 3, 1.5), (0, 1, 1.0)])
+def test_pq_matches_oracle(ci, bl, temp):
+    dc = CONFIGS[ci]
+    say(f"p/q verify: config {dc.name} block_len={bl} temperature={temp}")
+    d, _ = make(dc, max_seqs=2)
+    rng = np.random.default_rng(7)
+    checked = 0
+    for trial in range(8):
+        T, Q = [], []
+        ids = []
+        for s in range(2):
+            t, q = _pq_case(dc, bl, 1000 * trial + s, rng)
+            # drafted tokens x_j ~ q_j (the rule assumes drafts come from q)
+            x, _ = O.sample_draft_tokens(q.numpy(), temp, seed=trial, seq=s) if bl > 1 else (np.zeros(0, np.int64), None)
+            ids.append(np.concatenate([[int(rng.integers(0, dc.vocab))], x]).astype(np.int32))
+            T.append(t); Q.append(q)
+        ids = np.stack(ids)
+        Tt = torch.stack(T).to(DEV)
+        Qt = torch.stack(Q).to(DEV) if bl > 1 else None
+        seed, off = 11 + trial, 3 * trial
+        tau, bonus = d.verify(torch.from_numpy(ids).to(DEV), Tt, Qt, temperature=temp, seed=seed,
+                              philox_offset=off)
+        tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+        for s in range(2):
+            t, b, diag = O.verify_pq(ids[s], T[s].numpy(), Q[s].numpy() if bl > 1 else np.zeros((0, dc.vocab)),
+                                     temp, seed, off, s)
+            if min(diag["ratio_margin"] or [1.0]) < 1e-4 or diag["cdf_margin"] < 1e-12:
+                continue
+            assert (tau[s], bonus[s]) == (t, b), (trial, s, diag)
+            checked += 1
+    assert checked >= 12
