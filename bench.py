@@ -95,6 +95,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-all", action="store_true",
                     help="also time every stage once after the timed region")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
@@ -110,6 +112,16 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_reference:
+        n = 1 << 29  # 1 GiB of bf16 read, 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_reference_bytes_read": 2 * n, "copy_reference_bytes_written": 2 * n,
+                          "copies": 3}), flush=True)
+        return
     dc = synth.CONFIGS[1]
     S0, Bsz = dc.ctx_len, dc.block_size
     print(f"[bench] workload {dc.name}: generating weights", file=sys.stderr, flush=True)

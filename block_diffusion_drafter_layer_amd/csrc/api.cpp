@@ -75,8 +75,10 @@ int32_t row_capacity(const dflash_config& c, int32_t max_ctx) {
   return (int32_t)align_up((size_t)max_ctx + (size_t)c.block_size, 64);
 }
 
+constexpr size_t kSplitPartFloats = (size_t)kSplitMaxWG * 32 * 64;  // <= 32 rows x 64 columns each
+
 struct Layout {
-  size_t x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
+  size_t split_part, x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
   size_t total;
 };
 
@@ -88,6 +90,7 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   Layout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  L.split_part = take(kSplitPartFloats * 4);
   L.x = take(Mmax * D * 4);
   L.xh = take(Mmax * D * 2);
   L.xl = take(Mmax * D * 2);
@@ -142,10 +145,10 @@ template <class Fn>
 static hipError_t timed(dflash_handle* h, int st, Fn&& fn) {
   Profiler& P = h->prof;
   const bool on = (P.mask >> st) & 1u && 2 * (size_t)(P.n + 1) <= P.ev.size();
-  if (on) hipEventRecord(P.ev[2 * P.n], h->stream);
+  if (on) (void)hipEventRecord(P.ev[2 * P.n], h->stream);
   hipError_t e = fn();
   if (on) {
-    hipEventRecord(P.ev[2 * P.n + 1], h->stream);
+    (void)hipEventRecord(P.ev[2 * P.n + 1], h->stream);
     P.stage[P.n] = st;
     ++P.n;
   }
@@ -153,11 +156,18 @@ static hipError_t timed(dflash_handle* h, int st, Fn&& fn) {
 }
 
 static void profiler_release(Profiler& P) {
-  for (hipEvent_t e : P.ev) hipEventDestroy(e);
+  for (hipEvent_t e : P.ev) (void)hipEventDestroy(e);
   P.ev.clear();
   P.stage.clear();
   P.n = 0;
   P.mask = 0;
+}
+
+static SplitWs split_ws(const dflash_handle* h) {
+  SplitWs w;
+  w.part = (float*)(h->ws + h->lay.split_part);
+  w.part_floats = kSplitPartFloats;
+  return w;
 }
 
 extern "C" {
@@ -341,6 +351,7 @@ dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats, in
   F.eps = c.rms_eps;
   F.out = (bf16_t*)ctx_out;
   F.ssq = (float*)(h->ws + h->lay.fuse_ssq);
+  F.split = split_ws(h);
   const bool rows = n_tokens <= kContextRowsStreaming;
   hipError_t e = timed(h, ST_FUSE, [&] {
     return rows ? launch_fuse_rows(F, h->stream) : launch_fuse(F, h->stream);
@@ -380,6 +391,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, dflash_kv* kv, const void* ctx_
     I.wv[i] = (const bf16_t*)h->layers[i].wv;
   }
   I.kv = (bf16_t*)kv->base;
+  I.split = split_ws(h);
   const bool rows = n_tokens <= kContextRowsStreaming;
   hipError_t e = timed(h, ST_INJECT, [&] {
     return rows ? launch_inject_rows(I, h->stream) : launch_inject(I, h->stream);
@@ -438,13 +450,21 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* co
   L.act_h = (bf16_t*)(ws + Ly.act_h); L.act_l = (bf16_t*)(ws + Ly.act_l);
   L.lm_part = (uint64_t*)(ws + Ly.lm_part);
   L.att_acc = (float*)(ws + Ly.att_acc); L.att_ml = (float*)(ws + Ly.att_ml);
-  // split each sequence's keys so the grid has ~512 workgroups
+  L.split = split_ws(h);
+  // split each sequence's keys so that the grid holds ~1024 waves (one per
+  // SIMD) where the context allows, in whole 32-key chunks; each workgroup
+  // runs G query-head waves times 2 key columns when G <= 4
   const int pairs = n_seqs * c.n_kv_heads;
+  const int G = c.n_heads / c.n_kv_heads;
+  const int WG_waves = G <= 4 ? 2 * G : G;
   const int max_splits = std::max(1, std::min(kAttnMaxSplits, kAttnSlotCap / pairs));
-  int splits = std::min(max_splits, std::max(1, (512 + pairs - 1) / pairs));
-  int kps = (int)align_up((size_t)((max_keys + splits - 1) / splits), 32);
-  kps = std::max(kps, 64);
+  int splits = std::min(max_splits, std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves)));
+  int kps = std::max(32, max_keys / splits / 32 * 32);
   splits = (max_keys + kps - 1) / kps;
+  if (splits > max_splits) {
+    kps = (int)align_up((size_t)((max_keys + max_splits - 1) / max_splits), 32);
+    splits = (max_keys + kps - 1) / kps;
+  }
   L.att_splits = splits; L.att_keys_per_split = kps;
 
   hipStream_t st = h->stream;

@@ -31,15 +31,109 @@ struct AttnArgs {
   SeqTable seqs;
 };
 
-template <int HD, int MAXG>
-__global__ void __launch_bounds__(MAXG * 64)
+template <int HD>
+struct Chunk {
+  static constexpr int KSTEPS = (HD + 31) / 32;  // head_dim 16 pads k to 32 with zeros
+  static constexpr int HT = HD / 16;
+  bf16x8 kf[2][KSTEPS];
+  u32x4 v[HT];
+};
+
+// K rows of the chunk as the A operand of S^T = K Q^T (keys permuted so each
+// lane group ends up with 8 consecutive keys) and the V^T rows for the same
+// keys. Addresses stay inside the cache; out-of-range keys are masked later.
+template <int HD>
+__device__ __forceinline__ void load_chunk(Chunk<HD>& c, int c0, int n_keys, const bf16_t* kbase,
+                                           const bf16_t* vbase, int cap, int ql, int lg) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    int key = c0 + (ql >> 2) * 8 + t * 4 + (ql & 3);
+    key = key < n_keys ? key : n_keys - 1;
+    const bf16_t* kr = kbase + (size_t)key * HD + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < Chunk<HD>::KSTEPS; ++ks)
+      c.kf[t][ks] = (ks * 32 + 8 * lg < HD) ? ld_bf16x8(kr + ks * 32) : zero_bf16x8();
+  }
+  const int kl = c0 + 8 * lg;
+  const int kl_ld = kl < n_keys ? kl : 0;
+#pragma unroll
+  for (int h = 0; h < Chunk<HD>::HT; ++h)
+    c.v[h] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(h * 16 + ql) * cap + kl_ld);
+}
+
+template <int HD>
+__device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke, const bf16x8* qf,
+                                              const bf16x8* qfl, float scale_log2, int lg,
+                                              float& m_run, float& l_run, f32x4* acc) {
+  constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
+  f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      st[t] = mfma16x16x32(c.kf[t][ks], qf[ks], st[t]);
+      st[t] = mfma16x16x32(c.kf[t][ks], qfl[ks], st[t]);
+    }
+  }
+  const int kl = c0 + 8 * lg;
+  float sc[8];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = (kl + 4 * t + e < ke) ? st[t][e] * scale_log2 : -INFINITY;
+      sc[4 * t + e] = v;
+      mloc = fmaxf(mloc, v);
+    }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+  const float m_new = fmaxf(m_run, mloc);
+  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  float pr[8], psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+    psum += pr[i];
+  }
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+  bf16x8 pf, pfl;
+  pack_split_bf16x8(pr, pf, pfl);
+  // keys past the range contribute zero V, never NaN
+  const int nvalid = ke - kl;
+  uint32_t keep[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    keep[i] = ((2 * i < nvalid) ? 0x0000ffffu : 0u) | ((2 * i + 1 < nvalid) ? 0xffff0000u : 0u);
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+    acc[h] *= alpha;
+    u32x4 raw = c.v[h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) raw[i] &= keep[i];
+    const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
+    acc[h] = mfma16x16x32(vf, pf, acc[h]);
+    acc[h] = mfma16x16x32(vf, pfl, acc[h]);
+  }
+}
+
+// Workgroup = G query-head waves x W key columns for one (key range, kv head,
+// sequence). Column c of the range's 32-key chunks goes to key column c % W.
+// The W partial softmax states of a head are merged through LDS, so one
+// partial per (range, head) reaches memory.
+template <int HD, int G, int W, bool PIPE>
+__global__ void __launch_bounds__(G * W * 64)
 attn_split(AttnArgs p) {
-  constexpr int KSTEPS = (HD + 31) / 32;  // head_dim 16 pads k to 32 with zeros
-  constexpr int HT = HD / 16;
+  constexpr int KSTEPS = Chunk<HD>::KSTEPS;
+  constexpr int HT = Chunk<HD>::HT;
+  __shared__ float lds_acc[(W > 1 ? W - 1 : 1) * G][16 * HD];
+  __shared__ float lds_ml[(W > 1 ? W - 1 : 1) * G][16][2];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int G = p.Hq / p.Hkv;
-  const int a = g * G + w;
+  const int gi = w % G, wi = w / G;
+  const int a = g * G + gi;
   const int ql = lane & 15, lg = lane >> 4;
   const SeqDesc sd = p.seqs.s[s];
   const int n_keys = sd.len + p.Bl;
@@ -49,6 +143,7 @@ attn_split(AttnArgs p) {
   const bf16_t* kbase = sd.kv + (size_t)((2 * p.layer) * p.Hkv + g) * plane;
   const bf16_t* vbase = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + g) * plane;
 
+  // the queries and the first chunk are requested together
   bf16x8 qf[KSTEPS], qfl[KSTEPS];
   const bool qv = ql < p.Bl;
   const size_t qoff = ((size_t)(s * p.Bl + (qv ? ql : 0)) * p.Hq + a) * HD + 8 * lg;
@@ -58,90 +153,73 @@ attn_split(AttnArgs p) {
     qf[ks] = in ? ld_bf16x8(p.q + qoff + ks * 32) : zero_bf16x8();
     qfl[ks] = in ? ld_bf16x8(p.q_lo + qoff + ks * 32) : zero_bf16x8();
   }
-
   f32x4 acc[HT];
 #pragma unroll
   for (int h = 0; h < HT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int c0 = kb; c0 < ke; c0 += 32) {
-    // issue this chunk's K and V loads together; V does not depend on the
-    // scores. Lane group lg holds keys c0 + 8*lg .. +7 of both.
-    const int kl = c0 + 8 * lg;
-    const int kl_ld = kl < n_keys ? kl : 0;  // in-bounds address, masked below
-    const int nvalid = ke - kl;
-    bf16x8 kf[2][KSTEPS];
-    u32x4 vraw[HT];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      int key = c0 + (ql >> 2) * 8 + t * 4 + (ql & 3);
-      key = key < n_keys ? key : n_keys - 1;
-      const bf16_t* kr = kbase + (size_t)key * HD + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        kf[t][ks] = (ks * 32 + 8 * lg < HD) ? ld_bf16x8(kr + ks * 32) : zero_bf16x8();
-    }
-#pragma unroll
-    for (int h = 0; h < HT; ++h)
-      vraw[h] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(h * 16 + ql) * sd.cap + kl_ld);
-
-    f32x4 st[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        st[t] = mfma16x16x32(kf[t][ks], qf[ks], st[t]);
-        st[t] = mfma16x16x32(kf[t][ks], qfl[ks], st[t]);
-      }
-    }
-    float sc[8];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = (kl + 4 * t + e < ke) ? st[t][e] * p.scale_log2 : -INFINITY;
-        sc[4 * t + e] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    float pr[8], psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = exp2f(sc[i] - m_new);
-      psum += pr[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    float prl[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) prl[i] = pr[i] - bf2f(f2bf(pr[i]));
-    const bf16x8 pf = pack_bf16x8(pr);
-    const bf16x8 pfl = pack_bf16x8(prl);
-
-    // keys past the range (or past the cache) contribute zero V, never NaN
-    uint32_t keep[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      keep[i] = ((2 * i < nvalid) ? 0x0000ffffu : 0u) | ((2 * i + 1 < nvalid) ? 0xffff0000u : 0u);
-#pragma unroll
-    for (int h = 0; h < HT; ++h) {
-      acc[h] *= alpha;
-      u32x4 raw = vraw[h];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) raw[i] &= keep[i];
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, raw);
-      acc[h] = mfma16x16x32(vf, pf, acc[h]);
-      acc[h] = mfma16x16x32(vf, pfl, acc[h]);
+  constexpr int STEP = 32 * W;
+  int c0 = kb + 32 * wi;
+  if (!PIPE) {  // one register stage
+    for (; c0 < ke; c0 += STEP) {
+      Chunk<HD> ca;
+      load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
+      process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
     }
   }
-
+  // two register stages: the next chunk of this column is in flight while
+  // the current one is processed
+  Chunk<HD> ca, cb;
+  if (PIPE && c0 < ke) load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
+  while (PIPE && c0 < ke) {
+    const bool n1 = c0 + STEP < ke;
+    if (n1) load_chunk<HD>(cb, c0 + STEP, n_keys, kbase, vbase, sd.cap, ql, lg);
+    process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+    if (!n1) break;
+    c0 += STEP;
+    const bool n2 = c0 + STEP < ke;
+    if (n2) load_chunk<HD>(ca, c0 + STEP, n_keys, kbase, vbase, sd.cap, ql, lg);
+    process_chunk<HD>(cb, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+    if (!n2) break;
+    c0 += STEP;
+  }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
+
+  if (W > 1) {
+    if (wi > 0) {
+      const int slot = (wi - 1) * G + gi;
+#pragma unroll
+      for (int h = 0; h < HT; ++h)
+        *reinterpret_cast<f32x4*>(&lds_acc[slot][ql * HD + h * 16 + 4 * lg]) = acc[h];
+      if (lg == 0) {
+        lds_ml[slot][ql][0] = m_run;
+        lds_ml[slot][ql][1] = l_run;
+      }
+    }
+    __syncthreads();
+    if (wi > 0) return;
+    float mm[W], sc[W];
+    mm[0] = m_run;
+#pragma unroll
+    for (int j = 1; j < W; ++j) mm[j] = lds_ml[(j - 1) * G + gi][ql][0];
+    float M = mm[0];
+#pragma unroll
+    for (int j = 1; j < W; ++j) M = fmaxf(M, mm[j]);
+#pragma unroll
+    for (int j = 0; j < W; ++j) sc[j] = mm[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mm[j] - M);
+    l_run *= sc[0];
+#pragma unroll
+    for (int j = 1; j < W; ++j) l_run += sc[j] * lds_ml[(j - 1) * G + gi][ql][1];
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+      acc[h] *= sc[0];
+#pragma unroll
+      for (int j = 1; j < W; ++j)
+        acc[h] += sc[j] * *reinterpret_cast<const f32x4*>(&lds_acc[(j - 1) * G + gi][ql * HD + h * 16 + 4 * lg]);
+    }
+    m_run = M;
+  }
   const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
   float* out = p.acc + slot * 16 * HD + (size_t)ql * HD;
 #pragma unroll
@@ -153,50 +231,42 @@ attn_split(AttnArgs p) {
   }
 }
 
+// One workgroup per (block row, query head, sequence), one thread per output
+// dim (at least one wave): every split's (m, l) goes through LDS and every
+// split's accumulator value is requested before any is used.
 template <int HD>
-__global__ void __launch_bounds__(256)
-attn_merge(const float* acc, const float* ml, int Hq, int Bl, int splits,
-           bf16_t* ob_h, bf16_t* ob_l) {
-  const int a = blockIdx.x, s = blockIdx.y;
-  __shared__ float sm[kAttnMaxSplits][16], sl[kAttnMaxSplits][16];
-  __shared__ float wgt[kAttnMaxSplits][16];
+__global__ void __launch_bounds__(HD < 64 ? 64 : HD)
+attn_merge(const float* __restrict__ acc, const float* __restrict__ ml, int Hq, int Bl,
+           int splits, bf16_t* __restrict__ ob_h, bf16_t* __restrict__ ob_l) {
+  constexpr int NT = HD < 64 ? 64 : HD;
+  const int r = blockIdx.x, a = blockIdx.y, s = blockIdx.z;
+  const int d = threadIdx.x;
+  __shared__ float sw[kAttnMaxSplits];
+  __shared__ float sl[kAttnMaxSplits];
   const size_t slot0 = (size_t)(s * Hq + a) * splits;
-  // every (split, row) statistic is loaded by its own thread
-  for (int e = threadIdx.x; e < splits * 16; e += 256) {
-    const int k = e / 16, r = e % 16;
-    sm[k][r] = ml[((slot0 + k) * 16 + r) * 2];
-    sl[k][r] = ml[((slot0 + k) * 16 + r) * 2 + 1];
+  for (int k = threadIdx.x; k < splits; k += NT) {
+    sw[k] = ml[((slot0 + k) * 16 + r) * 2];
+    sl[k] = ml[((slot0 + k) * 16 + r) * 2 + 1];
   }
+  constexpr int BATCH = 16;
+  float v[BATCH];
+  float o = 0.f;
   __syncthreads();
-  if (threadIdx.x < Bl) {
-    const int r = threadIdx.x;
-    float M = -INFINITY;
-    for (int k = 0; k < splits; ++k) M = fmaxf(M, sm[k][r]);
-    float Lsum = 0.f;
-    for (int k = 0; k < splits; ++k) {
-      const float wk = sm[k][r] == -INFINITY ? 0.f : exp2f(sm[k][r] - M);
-      wgt[k][r] = wk;
-      Lsum += wk * sl[k][r];
-    }
-    const float inv = 1.f / Lsum;
-    for (int k = 0; k < splits; ++k) wgt[k][r] *= inv;
+  float M = -INFINITY;
+  for (int k = 0; k < splits; ++k) M = fmaxf(M, sw[k]);
+  float Lsum = 0.f;
+  for (int k = 0; k < splits; ++k) Lsum += (sw[k] == -INFINITY ? 0.f : exp2f(sw[k] - M)) * sl[k];
+  for (int k0 = 0; k0 < splits; k0 += BATCH) {
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+      v[k] = (k0 + k < splits && d < HD) ? acc[((slot0 + k0 + k) * 16 + r) * HD + d] : 0.f;
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k)
+      if (k0 + k < splits && sw[k0 + k] != -INFINITY) o += exp2f(sw[k0 + k] - M) * v[k];
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < Bl * HD; e += 256) {
-    const int r = e / HD, d = e % HD;
-    const float* src = acc + (slot0 * 16 + r) * HD + d;
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;  // independent chains keep loads in flight
-    int k = 0;
-    for (; k + 4 <= splits; k += 4) {
-      o0 += wgt[k][r] * src[(size_t)k * 16 * HD];
-      o1 += wgt[k + 1][r] * src[(size_t)(k + 1) * 16 * HD];
-      o2 += wgt[k + 2][r] * src[(size_t)(k + 2) * 16 * HD];
-      o3 += wgt[k + 3][r] * src[(size_t)(k + 3) * 16 * HD];
-    }
-    for (; k < splits; ++k) o0 += wgt[k][r] * src[(size_t)k * 16 * HD];
-    const float o = (o0 + o1) + (o2 + o3);
+  if (d < HD) {
     const size_t i = ((size_t)(s * Bl + r) * Hq + a) * HD + d;
-    split_bf16(o, ob_h[i], ob_l[i]);
+    split_bf16(o / Lsum, ob_h[i], ob_l[i]);
   }
 }
 
@@ -209,19 +279,23 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)HD));
   p.seqs = *L.seqs;
   const int G = L.Hq / L.Hkv;
-  const dim3 grid(L.att_splits, L.Hkv, L.n_seqs), block(G * 64);
-  // the launch bound follows the group size so small groups keep the full
-  // register file
-  if (G <= 4)
-    hipLaunchKernelGGL((attn_split<HD, 4>), grid, block, 0, st, p);
-  else if (G <= 8)
-    hipLaunchKernelGGL((attn_split<HD, 8>), grid, block, 0, st, p);
-  else
-    hipLaunchKernelGGL((attn_split<HD, 16>), grid, block, 0, st, p);
+  const dim3 grid(L.att_splits, L.Hkv, L.n_seqs);
+  // G query-head waves; groups of up to 4 heads also get two key columns
+  // (head_dim 128 in 512-thread groups keeps a single register stage: two
+  // stages would not fit the 256 registers a wave gets there)
+  constexpr bool P2 = HD < 128;
+  switch (G) {
+    case 1: hipLaunchKernelGGL((attn_split<HD, 1, 2, true>), grid, dim3(128), 0, st, p); break;
+    case 2: hipLaunchKernelGGL((attn_split<HD, 2, 2, true>), grid, dim3(256), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_split<HD, 4, 2, P2>), grid, dim3(512), 0, st, p); break;
+    case 8: hipLaunchKernelGGL((attn_split<HD, 8, 1, P2>), grid, dim3(512), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((attn_split<HD, 16, 1, false>), grid, dim3(1024), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge<HD>, dim3(L.Hq, L.n_seqs), dim3(256), 0, st, L.att_acc,
-                     L.att_ml, L.Hq, L.Bl, L.att_splits, L.ob_h, L.ob_l);
+  hipLaunchKernelGGL(attn_merge<HD>, dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st,
+                     L.att_acc, L.att_ml, L.Hq, L.Bl, L.att_splits, L.ob_h, L.ob_l);
   return hipGetLastError();
 }
 

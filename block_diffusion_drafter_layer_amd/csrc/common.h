@@ -20,12 +20,18 @@ __device__ __forceinline__ float bf2f(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32); NaN stays NaN.
 __device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (low half = a), one conversion instruction
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // v = hi + lo with hi = bf16(v), lo = bf16(v - hi): the pair carries ~16
@@ -50,9 +56,21 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) r[i] = f2bf2(v[2 * i], v[2 * i + 1]);
   return __builtin_bit_cast(bf16x8, r);
+}
+
+// hi/lo pair of 8 values packed as two MFMA operands
+__device__ __forceinline__ void pack_split_bf16x8(const float* v, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f2bf2(v[2 * i], v[2 * i + 1]);
+    const float h0 = __uint_as_float(h[i] << 16), h1 = __uint_as_float(h[i] & 0xffff0000u);
+    l[i] = f2bf2(v[2 * i] - h0, v[2 * i + 1] - h1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // D[i][j] += sum_k A[i][k] B[k][j], 16x16x32, bf16 inputs, fp32 accumulate.

@@ -199,8 +199,8 @@ gemm_tile(GemmA a, typename Epi::P p, int N) {
 static_assert(BM * (BN + 1) * 4 <= 2 * 2 * BM * LDK * 2, "output tile fits the stage buffers");
 
 __global__ void __launch_bounds__(256)
-fuse_normalize(bf16_t* out, const float* ssq, int n_tiles, int D, const bf16_t* gain,
-               float eps) {
+fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ ssq, int n_tiles, int D,
+               const bf16_t* __restrict__ gain, float eps) {
   const int m = blockIdx.x;
   __shared__ float rs;
   if (threadIdx.x < 64) {
@@ -211,6 +211,7 @@ fuse_normalize(bf16_t* out, const float* ssq, int n_tiles, int D, const bf16_t* 
   }
   __syncthreads();
   const float r = rs;
+#pragma unroll 4
   for (int n = threadIdx.x; n < D; n += 256) {
     bf16_t* o = out + (size_t)m * D + n;
     *o = f2bf(bf2f(*o) * r * bf2f(gain[n]));

@@ -12,10 +12,18 @@ namespace dfl {
 
 constexpr int kMaxLayers = 16;
 constexpr int kMaxFeat = 8;
-constexpr int kAttnMaxSplits = 64;
+constexpr int kAttnMaxSplits = 128;
 constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots
 constexpr int kVerifyMaxSplits = 64;
 constexpr int kGemmTile = 128;
+
+// Split-K scratch of the streaming GEMMs: fp32 partial tiles.
+constexpr int kSplitMaxWG = 1024;     // capacity: partial tiles of <= 32 x 64
+constexpr int kSplitTargetWG = 512;   // split narrow matrices up to this grid
+struct SplitWs {
+  float* part;
+  size_t part_floats;
+};
 
 // Workspace pointers and shapes of one draft forward.
 struct DraftLaunch {
@@ -39,6 +47,7 @@ struct DraftLaunch {
   float* att_acc;           // [slots*G][16][hd]
   float* att_ml;            // [slots*G][16][2]
   int att_splits, att_keys_per_split;
+  SplitWs split;
 };
 
 int skinny_tile_cols();
@@ -66,7 +75,8 @@ struct FuseLaunch {
   const bf16_t* gain;
   float eps;
   bf16_t* out;        // [T][D]
-  float* ssq;         // [T][ceil(D/128)]
+  float* ssq;         // [T][ceil(D/128)] (tiled) or [T][D/32] (few rows)
+  SplitWs split;
 };
 hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
@@ -81,6 +91,7 @@ struct InjectLaunch {
   const bf16_t* wk[kMaxLayers];
   const bf16_t* wv[kMaxLayers];
   bf16_t* kv;
+  SplitWs split;
 };
 hipError_t launch_inject(const InjectLaunch& I, hipStream_t st);       // tiled MFMA GEMM
 hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st);  // few rows: streaming

@@ -1,9 +1,14 @@
 // Weight-streaming GEMMs of the draft forward (few activation rows, wide
 // weights): Y[m][n] = sum_k X[m][k] W[n][k], X given as a bf16 hi/lo pair,
 // W bf16 in nn.Linear [out, in] layout, read straight from HBM into MFMA
-// operand registers (16 bytes per lane, no LDS staging). The K range of a
-// workgroup's columns is split over its waves and reduced through LDS; each
-// use has its own fused epilogue:
+// operand registers (16 bytes per lane, no LDS staging). A workgroup owns
+// 16*NCT columns; its waves interleave the 32-wide k steps of its K range and
+// are reduced through LDS. Narrow matrices also split K over workgroups: each
+// writes an fp32 partial tile and a second, small kernel sums the partials of
+// a column block in split order (deterministic) and runs the epilogue. (A
+// last-arriving-workgroup reduction inside one launch needs a device-scope
+// fence per workgroup, which on this chip writes back and invalidates an XCD's
+// L2 - far more costly than the extra launch.) Each use has its own epilogue:
 //   qkv    - RMSNorm row scale, RoPE on q/k, q to the workspace, k/v into the
 //            sequence's KV cache (txtmix article section 5: q from the draft
 //            tokens, k/v of the block appended after the context);
@@ -131,6 +136,7 @@ struct EpiResid {
     const bf16_t* gain;  // [D]
     float* ssq;          // [M][D/32]
     float* hidden;       // optional [M][D]
+    int n_vcols;         // D
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     return p.w + (size_t)vc * p.K;
@@ -138,12 +144,12 @@ struct EpiResid {
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float*,
                              int vc0, int m0, int M) {
-    static_assert(VC == 32, "one 32-column norm group per workgroup");
+    static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
     for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
       const int ml = e / VC, c = e % VC;
       const int m = m0 + ml;
-      if (m >= M) continue;
       const int n = vc0 + c;
+      if (m >= M || n >= p.n_vcols) continue;
       const size_t i = (size_t)m * p.D + n;
       const float xn = p.x[i] + tile[ml][c];
       p.x[i] = xn;
@@ -153,11 +159,13 @@ struct EpiResid {
     }
     __syncthreads();
     const int ng = p.D / 32;
-    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+    for (int e = threadIdx.x; e < ROWS * (VC / 32); e += blockDim.x) {
+      const int ml = e / (VC / 32), g = e % (VC / 32);
+      if (m0 + ml >= M || vc0 + g * 32 >= p.n_vcols) continue;
       float s = 0.f;
 #pragma unroll 8
-      for (int c = 0; c < VC; ++c) s += tile[ml][c];
-      p.ssq[(size_t)(m0 + ml) * ng + vc0 / 32] = s;
+      for (int c = 0; c < 32; ++c) s += tile[ml][g * 32 + c];
+      p.ssq[(size_t)(m0 + ml) * ng + vc0 / 32 + g] = s;
     }
   }
 };
@@ -167,6 +175,7 @@ struct EpiSwiglu {
     const bf16_t *wg, *wu;  // [F][D]
     int K, F;
     bf16_t *ah, *al;        // [M][F] activation hi/lo
+    int n_vcols;            // 2F
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     const int t = vc >> 4, j = vc & 15;
@@ -180,7 +189,7 @@ struct EpiSwiglu {
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
       const int m = m0 + ml;
-      if (m >= M) continue;
+      if (m >= M || vc0 + c * 16 >= p.n_vcols) continue;
       const float g = tile[ml][c * 16 + j] * rs[ml];
       const float u = tile[ml][c * 16 + j + 8] * rs[ml];
       const float a = g / (1.f + expf(-g)) * u;
@@ -220,7 +229,7 @@ struct EpiLM {
         const int v = vc0 + c;
         if (v < p.V) best = umax64(best, argmax_key(tile[ml][c], (uint32_t)v));
       }
-      p.part[(size_t)blockIdx.x * M + m0 + ml] = best;
+      p.part[(size_t)(vc0 / VC) * M + m0 + ml] = best;
     }
   }
 };
@@ -234,25 +243,28 @@ struct EpiFuseRows {
     int K, D;
     bf16_t* out;      // [M][D]
     float* ssq;       // [M][D/32]
+    int n_vcols;      // D
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
                              int M) {
-    static_assert(VC == 32, "one 32-column norm group per workgroup");
+    static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
     for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
       const int ml = e / VC, c = e % VC;
       const int m = m0 + ml;
-      if (m >= M) continue;
+      if (m >= M || vc0 + c >= p.n_vcols) continue;
       const float y = tile[ml][c];
       p.out[(size_t)m * p.D + vc0 + c] = f2bf(y);
       tile[ml][c] = y * y;
     }
     __syncthreads();
-    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+    for (int e = threadIdx.x; e < ROWS * (VC / 32); e += blockDim.x) {
+      const int ml = e / (VC / 32), g = e % (VC / 32);
+      if (m0 + ml >= M || vc0 + g * 32 >= p.n_vcols) continue;
       float s = 0.f;
-      for (int c = 0; c < VC; ++c) s += tile[ml][c];
-      p.ssq[(size_t)(m0 + ml) * (p.D / 32) + vc0 / 32] = s;
+      for (int c = 0; c < 32; ++c) s += tile[ml][g * 32 + c];
+      p.ssq[(size_t)(m0 + ml) * (p.D / 32) + vc0 / 32 + g] = s;
     }
   }
 };
@@ -266,6 +278,7 @@ struct EpiInjectRows {
     int D, Hkv, hd, pos0, cap;
     double log2_theta;
     bf16_t* kv;
+    int n_vcols;     // L * 2 * Hkv * hd
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     const int kvd = p.Hkv * p.hd;
@@ -288,6 +301,7 @@ struct EpiInjectRows {
       if (m >= M) continue;
       const int pos = p.pos0 + m;
       const int vc = vc0 + c * 16;
+      if (vc >= p.n_vcols) continue;
       const int i = vc / (2 * kvd), r = vc % (2 * kvd);
       const float x1 = tile[ml][c * 16 + j], x2 = tile[ml][c * 16 + j + 8];
       if (r < kvd) {
@@ -311,9 +325,31 @@ struct EpiInjectRows {
 // the streaming GEMM
 // ---------------------------------------------------------------------------
 
+struct SplitK {
+  int ksplit;        // workgroups sharing one column block's K range
+  int steps;         // 32-wide k steps per split
+  float* part;       // [col block][split][ROWS][VC] fp32 partial tiles
+};
+
+// RMSNorm row scale of the tile rows from the producer's per-32-column sums
+// of x^2 (one wave per row); 1 when the GEMM has no input norm.
+template <int ROWS>
+__device__ __forceinline__ void row_scales(const SkinnyA& a, int m0, float* rs) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int row = w; row < ROWS; row += nw) {
+    float s = 0.f;
+    if (a.ssq && m0 + row < a.M) {
+      const float* q = a.ssq + (size_t)in_row(a, m0 + row) * a.ssq_ld;
+      for (int g = lane; g < a.ssq_ld; g += 64) s += q[g];
+      s = wave_sum(s);
+    }
+    if (lane == 0) rs[row] = a.ssq ? rsqrtf(s / (float)a.K + a.eps) : 1.f;
+  }
+}
+
 template <int MT, int NCT, int NW, int U, bool LO, class Epi>
 __global__ void __launch_bounds__(NW * 64)
-skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
+skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, SplitK sk) {
   constexpr int VC = 16 * NCT;
   constexpr int ROWS = 16 * MT;
   __shared__ float red[NW][MT * NCT * 4][64];
@@ -322,7 +358,8 @@ skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int vc0 = blockIdx.x * VC;
+  const int cb = blockIdx.x / sk.ksplit, ksi = blockIdx.x % sk.ksplit;
+  const int vc0 = cb * VC;
   const int m0 = blockIdx.y * ROWS;
   const int kq = 8 * (lane >> 4);
 
@@ -349,12 +386,14 @@ skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
     for (int c = 0; c < NCT; ++c) acc[m][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KS = a.K >> 5;
-  for (int ks0 = w; ks0 < KS; ks0 += NW * U) {
+  const int kbeg = ksi * sk.steps;
+  const int kend = min(kbeg + sk.steps, KS);
+  for (int ks0 = kbeg + w; ks0 < kend; ks0 += NW * U) {
     bf16x8 bq[U][NCT], xh[U][MT], xl[U][MT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = ks0 + u * NW;
-      if (ks < KS) {
+      if (ks < kend) {
         const int k = ks * 32;
         const int sg = k / a.seg_k;
         const bf16_t* hb = a.seg[sg] + (k - sg * a.seg_k);
@@ -369,7 +408,7 @@ skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (ks0 + u * NW < KS) {
+      if (ks0 + u * NW < kend) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -387,17 +426,6 @@ skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
     for (int c = 0; c < NCT; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[w][(m * NCT + c) * 4 + e][lane] = acc[m][c][e];
-
-  // RMSNorm row scale from the producer's per-32-column sums of x^2
-  for (int row = w; row < ROWS; row += NW) {
-    float s = 0.f;
-    if (a.ssq && m0 + row < a.M) {
-      const float* q = a.ssq + (size_t)in_row(a, m0 + row) * a.ssq_ld;
-      for (int g = lane; g < a.ssq_ld; g += 64) s += q[g];
-      s = wave_sum(s);
-    }
-    if (lane == 0) rs[row] = a.ssq ? rsqrtf(s / (float)a.K + a.eps) : 1.f;
-  }
   __syncthreads();
 
   for (int e = threadIdx.x; e < MT * NCT * 256; e += NW * 64) {
@@ -408,43 +436,103 @@ skinny_gemm(SkinnyA a, typename Epi::P ep, int n_vcols) {
     tile[m * 16 + (l >> 4) * 4 + q4][c * 16 + (l & 15)] = s;
   }
   __syncthreads();
+
+  if (sk.ksplit > 1) {  // publish this split's partial tile for the finisher
+    float* mine = sk.part + ((size_t)cb * sk.ksplit + ksi) * ROWS * VC;
+    for (int e = threadIdx.x; e < ROWS * VC; e += NW * 64) mine[e] = tile[e / VC][e % VC];
+    return;
+  }
+  row_scales<ROWS>(a, m0, rs);
+  __syncthreads();
   Epi::template run<ROWS, VC>(ep, tile, rs, vc0, m0, a.M);
+}
+
+// Sum of a column block's split partials, in split order, then the epilogue.
+constexpr int kFinishBatch = 8;
+template <int MT, int NCT, class Epi>
+__global__ void __launch_bounds__(256)
+skinny_finish(SkinnyA a, typename Epi::P ep, SplitK sk) {
+  constexpr int VC = 16 * NCT;
+  constexpr int ROWS = 16 * MT;
+  __shared__ float tile[ROWS][VC + 1];
+  __shared__ float rs[ROWS];
+  const int cb = blockIdx.x;
+  const float* __restrict__ all = sk.part + (size_t)cb * sk.ksplit * ROWS * VC;
+  // every partial of this thread's elements is loaded before any is summed:
+  // one memory round trip instead of one per split
+  constexpr int EPT = ROWS * VC / 256;
+  static_assert(ROWS * VC % 256 == 0, "whole elements per thread");
+  for (int k0 = 0; k0 < sk.ksplit; k0 += kFinishBatch) {
+    float v[kFinishBatch][EPT];
+#pragma unroll
+    for (int k = 0; k < kFinishBatch; ++k)
+#pragma unroll
+      for (int j = 0; j < EPT; ++j)
+        v[k][j] = k0 + k < sk.ksplit ? all[(size_t)(k0 + k) * ROWS * VC + threadIdx.x + 256 * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = threadIdx.x + 256 * j;
+      float acc = k0 ? tile[e / VC][e % VC] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kFinishBatch; ++k) acc += v[k][j];  // split order
+      tile[e / VC][e % VC] = acc;
+    }
+  }
+  row_scales<ROWS>(a, 0, rs);
+  __syncthreads();
+  Epi::template run<ROWS, VC>(ep, tile, rs, cb * VC, 0, a.M);
 }
 
 // ---------------------------------------------------------------------------
 // embedding of the block and the drafted-token reduction
 // ---------------------------------------------------------------------------
 
+// One workgroup per (row, 1024 columns); every thread owns 4 adjacent columns
+// and makes a single round trip. 8 threads cover one 32-column norm group.
 __global__ void __launch_bounds__(256)
-embed_block(const bf16_t* E, int V, int D, const int32_t* anchors, int mask_id,
-            int Bl, const bf16_t* gain, float* x, bf16_t* xh, bf16_t* xl,
-            float* ssq, int32_t* block_out) {
-  const int m = blockIdx.x, s = m / Bl, r = m % Bl;
+embed_block(const bf16_t* __restrict__ E, int V, int D, const int32_t* __restrict__ anchors,
+            int mask_id, int Bl, const bf16_t* __restrict__ gain, float* __restrict__ x,
+            bf16_t* __restrict__ xh, bf16_t* __restrict__ xl, float* __restrict__ ssq,
+            int32_t* __restrict__ block_out) {
+  const int m = blockIdx.y, s = m / Bl, r = m % Bl;
   int id = r == 0 ? anchors[s] : mask_id;
   id = id < 0 ? 0 : (id >= V ? V - 1 : id);  // keep the gather in bounds
-  if (r == 0 && threadIdx.x == 0) block_out[s * Bl] = id;
-  const bf16_t* e = E + (size_t)id * D;
-  for (int n0 = 0; n0 < D; n0 += 256) {
-    const int n = n0 + threadIdx.x;
-    float sq = 0.f;
-    if (n < D) {
-      const float v = bf2f(e[n]);
-      const size_t i = (size_t)m * D + n;
-      x[i] = v;
-      split_bf16(v * bf2f(gain[n]), xh[i], xl[i]);
-      sq = v * v;
-    }
+  if (r == 0 && blockIdx.x == 0 && threadIdx.x == 0) block_out[s * Bl] = id;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  float sq = 0.f;
+  if (n < D) {
+    const uint2 ev = *reinterpret_cast<const uint2*>(E + (size_t)id * D + n);
+    const uint2 gv = *reinterpret_cast<const uint2*>(gain + n);
+    const bf16_t e4[4] = {(bf16_t)(ev.x & 0xffff), (bf16_t)(ev.x >> 16), (bf16_t)(ev.y & 0xffff),
+                          (bf16_t)(ev.y >> 16)};
+    const bf16_t g4[4] = {(bf16_t)(gv.x & 0xffff), (bf16_t)(gv.x >> 16), (bf16_t)(gv.y & 0xffff),
+                          (bf16_t)(gv.y >> 16)};
+    float4 xv;
+    bf16_t hi[4], lo[4];
+    float* xp = reinterpret_cast<float*>(&xv);
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) sq += __shfl_xor(sq, o, kWave);
-    if (n < D && (threadIdx.x & 31) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
+    for (int i = 0; i < 4; ++i) {
+      xp[i] = bf2f(e4[i]);
+      split_bf16(xp[i] * bf2f(g4[i]), hi[i], lo[i]);
+      sq += xp[i] * xp[i];
+    }
+    const size_t o = (size_t)m * D + n;
+    *reinterpret_cast<float4*>(x + o) = xv;
+    *reinterpret_cast<uint2*>(xh + o) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(xl + o) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
   }
+  sq += __shfl_xor(sq, 1, kWave);
+  sq += __shfl_xor(sq, 2, kWave);
+  sq += __shfl_xor(sq, 4, kWave);
+  if (n < D && (threadIdx.x & 7) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
 }
 
 __global__ void __launch_bounds__(256)
-lm_argmax_reduce(const uint64_t* part, int n_tiles, int M_lm, int Bl,
-                 int32_t* block_out) {
+lm_argmax_reduce(const uint64_t* __restrict__ part, int n_tiles, int M_lm, int Bl,
+                 int32_t* __restrict__ block_out) {
   const int m = blockIdx.x;
   uint64_t best = 0;
+#pragma unroll 8
   for (int t = threadIdx.x; t < n_tiles; t += 256) best = umax64(best, part[(size_t)t * M_lm + m]);
   best = wave_max_u64(best);
   __shared__ uint64_t wbest[4];
@@ -462,22 +550,42 @@ lm_argmax_reduce(const uint64_t* part, int n_tiles, int M_lm, int Bl,
 // ---------------------------------------------------------------------------
 
 namespace {
-constexpr int kNCT = 2, kNW = 8, kU = 4;
-constexpr int kVC = 16 * kNCT;
+constexpr int kNW = 8;
+
+// Column tiles per wave and the K split: few rows take wide tiles (the
+// activation fragments are reused across NCT weight tiles) and narrow
+// matrices split K so that the grid holds ~512-1024 workgroups.
+template <class Epi, bool LO, int MT, int NCT, int U>
+hipError_t launch_cfg(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const SplitWs& ws,
+                      hipStream_t st) {
+  constexpr int VC = 16 * NCT, ROWS = 16 * MT;
+  const int blocks = (n_vcols + VC - 1) / VC;
+  const int row_blocks = (a.M + ROWS - 1) / ROWS;
+  const int KS = a.K / 32;
+  int ks = 1;
+  if (row_blocks == 1 && ws.part)
+    while (blocks * ks * 2 <= kSplitTargetWG && KS / (ks * 2) >= 2 * kNW &&
+           (size_t)blocks * ks * 2 * ROWS * VC <= ws.part_floats)
+      ks *= 2;
+  SplitK sk;
+  sk.ksplit = ks;
+  sk.steps = (KS + ks - 1) / ks;
+  sk.part = ws.part;
+  hipLaunchKernelGGL((skinny_gemm<MT, NCT, kNW, U, LO, Epi>), dim3(blocks * ks, row_blocks),
+                     dim3(kNW * 64), 0, st, a, ep, n_vcols, sk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  hipLaunchKernelGGL((skinny_finish<MT, NCT, Epi>), dim3(blocks), dim3(256), 0, st, a, ep, sk);
+  return hipGetLastError();
+}
 
 template <class Epi, bool LO = true>
 hipError_t launch_skinny(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
-                         hipStream_t st) {
-  const int tiles = (n_vcols + kVC - 1) / kVC;
-  // MT row tiles of 16 per workgroup; more rows than 64 take several row
-  // blocks (grid.y), each streaming the weights again
-  if (a.M <= 16)
-    hipLaunchKernelGGL((skinny_gemm<1, kNCT, kNW, kU, LO, Epi>), dim3(tiles, 1), dim3(kNW * 64), 0, st, a, ep, n_vcols);
-  else if (a.M <= 32)
-    hipLaunchKernelGGL((skinny_gemm<2, kNCT, kNW, kU, LO, Epi>), dim3(tiles, 1), dim3(kNW * 64), 0, st, a, ep, n_vcols);
-  else
-    hipLaunchKernelGGL((skinny_gemm<4, kNCT, kNW, 2, LO, Epi>), dim3(tiles, (a.M + 63) / 64), dim3(kNW * 64), 0, st, a, ep, n_vcols);
-  return hipGetLastError();
+                         const SplitWs& ws, hipStream_t st) {
+  if (a.M <= 16) return launch_cfg<Epi, LO, 1, 4, 4>(a, ep, n_vcols, ws, st);
+  if (a.M <= 32) return launch_cfg<Epi, LO, 2, 4, 2>(a, ep, n_vcols, ws, st);
+  // more rows: 64-row blocks over grid.y, each streaming the weights again
+  return launch_cfg<Epi, LO, 4, 2, 2>(a, ep, n_vcols, ws, st);
 }
 
 SkinnyA make_a(const bf16_t* xh, const bf16_t* xl, int lda, int M, int K,
@@ -492,7 +600,7 @@ SkinnyA make_a(const bf16_t* xh, const bf16_t* xl, int lda, int M, int K,
 }
 }  // namespace
 
-int skinny_tile_cols() { return kVC; }
+int skinny_tile_cols() { return 32; }  // narrowest column block of any configuration
 int skinny_max_rows() { return 64; }
 
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
@@ -500,8 +608,8 @@ hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
   for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = i < F.n_feat ? F.feats[i] : F.feats[0];
   a.seg_k = F.D;
   EpiFuseRows::P p;
-  p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.out = F.out; p.ssq = F.ssq;
-  hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, st);
+  p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.out = F.out; p.ssq = F.ssq; p.n_vcols = F.D;
+  hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, F.split, st);
   if (e != hipSuccess) return e;
   return launch_fuse_normalize(F.out, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
 }
@@ -514,12 +622,12 @@ hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
     p.wv[i] = i < I.L ? I.wv[i] : I.wv[0];
   }
   p.D = I.D; p.Hkv = I.Hkv; p.hd = I.hd; p.pos0 = I.pos0; p.cap = I.cap;
-  p.log2_theta = I.log2_theta; p.kv = I.kv;
-  return launch_skinny<EpiInjectRows, false>(a, p, I.L * 2 * I.Hkv * I.hd, st);
+  p.log2_theta = I.log2_theta; p.kv = I.kv; p.n_vcols = I.L * 2 * I.Hkv * I.hd;
+  return launch_skinny<EpiInjectRows, false>(a, p, I.L * 2 * I.Hkv * I.hd, I.split, st);
 }
 
 hipError_t launch_embed(const DraftLaunch& L, hipStream_t st) {
-  hipLaunchKernelGGL(embed_block, dim3(L.M), dim3(256), 0, st, L.embed, L.V, L.D,
+  hipLaunchKernelGGL(embed_block, dim3((L.D + 1023) / 1024, L.M), dim3(256), 0, st, L.embed, L.V, L.D,
                      L.anchors, L.mask_id, L.Bl, L.gain0, L.x, L.xh, L.xl, L.ssq,
                      L.block_out);
   return hipGetLastError();
@@ -532,7 +640,7 @@ hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
   p.wq = wq; p.wk = wk; p.wv = wv; p.D = L.D; p.Hq = L.Hq; p.Hkv = L.Hkv;
   p.hd = L.hd; p.Bl = L.Bl; p.layer = layer; p.log2_theta = L.log2_theta;
   p.q_out = L.q; p.q_lo = L.q_lo; p.seqs = *L.seqs;
-  return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, st);
+  return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, L.split, st);
 }
 
 hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
@@ -541,16 +649,16 @@ hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
   SkinnyA a = make_a(ah, al, K, L.M, K, nullptr, 0, L.eps);
   EpiResid::P p;
   p.w = w; p.K = K; p.D = L.D; p.x = L.x; p.xh = L.xh; p.xl = L.xl;
-  p.gain = gain_next; p.ssq = L.ssq; p.hidden = hidden;
-  return launch_skinny<EpiResid>(a, p, L.D, st);
+  p.gain = gain_next; p.ssq = L.ssq; p.hidden = hidden; p.n_vcols = L.D;
+  return launch_skinny<EpiResid>(a, p, L.D, L.split, st);
 }
 
 hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
                          hipStream_t st) {
   SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
   EpiSwiglu::P p;
-  p.wg = wg; p.wu = wu; p.K = L.D; p.F = L.F; p.ah = L.act_h; p.al = L.act_l;
-  return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, st);
+  p.wg = wg; p.wu = wu; p.K = L.D; p.F = L.F; p.ah = L.act_h; p.al = L.act_l; p.n_vcols = 2 * L.F;
+  return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, L.split, st);
 }
 
 hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
@@ -561,9 +669,23 @@ hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
   a.a_group = g; a.a_stride = L.Bl; a.a_off = 1;
   EpiLM::P p;
   p.w = w_lm; p.K = L.D; p.V = L.V; p.logits = logits; p.part = L.lm_part;
-  hipError_t e = launch_skinny<EpiLM>(a, p, L.V, st);
+  // the LM head never splits K (its vocab gives thousands of column blocks);
+  // one argmax key per column block and row goes to lm_part
+  const SplitWs none{};
+  hipError_t e;
+  int vc;
+  if (M_lm <= 16) {
+    e = launch_cfg<EpiLM, true, 1, 8, 2>(a, p, L.V, none, st);
+    vc = 128;
+  } else if (M_lm <= 32) {
+    e = launch_cfg<EpiLM, true, 2, 4, 2>(a, p, L.V, none, st);
+    vc = 64;
+  } else {
+    e = launch_cfg<EpiLM, true, 4, 2, 2>(a, p, L.V, none, st);
+    vc = 32;
+  }
   if (e != hipSuccess) return e;
-  const int tiles = (L.V + kVC - 1) / kVC;
+  const int tiles = (L.V + vc - 1) / vc;
   hipLaunchKernelGGL(lm_argmax_reduce, dim3(M_lm), dim3(256), 0, st, L.lm_part,
                      tiles, M_lm, L.Bl, L.block_out);
   return hipGetLastError();

@@ -46,7 +46,7 @@ __device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t row, ui
 // greedy
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-row_argmax_part(const float* logits, int V, int splits, uint64_t* part) {
+row_argmax_part(const float* __restrict__ logits, int V, int splits, uint64_t* __restrict__ part) {
   const int split = blockIdx.x, row = blockIdx.y;
   const int chunk = ((V + splits - 1) / splits + 3) & ~3;
   const int v0 = split * chunk, v1 = min(v0 + chunk, V);
@@ -72,13 +72,15 @@ row_argmax_part(const float* logits, int V, int splits, uint64_t* part) {
 }
 
 __global__ void __launch_bounds__(64)
-greedy_accept(const uint64_t* part, int splits, int Bl, const int32_t* block,
-              int32_t* tau, int32_t* bonus) {
+greedy_accept(const uint64_t* __restrict__ part, int splits, int Bl,
+              const int32_t* __restrict__ block, int32_t* __restrict__ tau,
+              int32_t* __restrict__ bonus) {
   const int s = blockIdx.x, j = threadIdx.x;
   __shared__ int32_t post[64];
   if (j < Bl) {
     uint64_t best = 0;
     const uint64_t* p = part + (size_t)(s * Bl + j) * splits;
+#pragma unroll 8
     for (int k = 0; k < splits; ++k) best = umax64(best, p[k]);
     post[j] = (int32_t)argmax_key_index(best);
   }
