@@ -77,6 +77,22 @@ int32_t row_capacity(const dflash_config& c, int32_t max_ctx) {
 
 constexpr size_t kSplitPartFloats = (size_t)kSplitMaxWG * 32 * 64;  // <= 32 rows x 64 columns each
 
+// split buffer: the register-streaming kernel's partial tiles, or the
+// LDS-staged kernel's [pair][slice][16][32] partials of the largest GEMM
+size_t split_floats(const dflash_config& c) {
+  const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const int nf = c.n_feat_layers > 0 ? c.n_feat_layers : 1;
+  size_t f = kSplitPartFloats;
+  f = std::max(f, stream_part_floats(qd + 2 * kvd, c.hidden));
+  f = std::max(f, stream_part_floats(c.hidden, qd));
+  f = std::max(f, stream_part_floats(2 * c.ffn, c.hidden));
+  f = std::max(f, stream_part_floats(c.hidden, c.ffn));
+  f = std::max(f, stream_part_floats(c.vocab, c.hidden));
+  f = std::max(f, stream_part_floats(c.hidden, nf * c.hidden));
+  f = std::max(f, stream_part_floats(c.n_layers * 2 * kvd, c.hidden));
+  return f;
+}
+
 struct Layout {
   size_t split_part, x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
   size_t total;
@@ -90,7 +106,7 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   Layout L{};
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
-  L.split_part = take(kSplitPartFloats * 4);
+  L.split_part = take(split_floats(c) * 4);
   L.x = take(Mmax * D * 4);
   L.xh = take(Mmax * D * 2);
   L.xl = take(Mmax * D * 2);
@@ -166,7 +182,7 @@ static void profiler_release(Profiler& P) {
 static SplitWs split_ws(const dflash_handle* h) {
   SplitWs w;
   w.part = (float*)(h->ws + h->lay.split_part);
-  w.part_floats = kSplitPartFloats;
+  w.part_floats = split_floats(h->cfg);
   return w;
 }
 

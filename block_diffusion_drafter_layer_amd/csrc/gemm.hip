@@ -1,8 +1,10 @@
 // Dense context-side GEMMs on bf16 MFMA: C[m][n] = sum_k A[m][k] B[n][k] with
-// both operands K-contiguous, 128x128 output tiles, BK = 64, LDS double
-// buffering, four waves each owning a 64x64 quarter (4x4 tiles of
-// 16x16x32 MFMAs). Rows of LDS tiles are padded to 72 elements (144 bytes) so
-// the 16 rows read by one MFMA operand fall in distinct bank groups.
+// both operands K-contiguous. Output tiles of BM x 128 (BM = 256 or 128),
+// BK = 64, LDS double buffering, four waves in a 2x2 arrangement each owning
+// a (BM/2) x 64 block of 32x32x16 MFMA tiles: a 128x64 wave block reads
+// 6 KB of LDS per 262 kFLOP, which keeps the LDS under its bandwidth at full
+// MFMA rate. LDS rows are padded to 72 elements (144 bytes). The output tile
+// goes through LDS in 128-row halves for the epilogue.
 //
 // A is read through a segmented loader so the fusion GEMM never materialises
 // the concatenation of the target layers (A3-dflash tutorial section 2.1.1:
@@ -45,7 +47,7 @@ struct EpiFuse {
       const int m = m0 + r, n = n0 + c;
       if (m < M && n < p.N) p.out[(size_t)m * p.N + n] = f2bf(C[r][c]);
     }
-    for (int r = threadIdx.x; r < BM; r += kThreads) {
+    for (int r = threadIdx.x; r < BM && n0 < p.N; r += kThreads) {
       const int m = m0 + r;
       if (m >= M) continue;
       float s = 0.f;
@@ -104,99 +106,138 @@ struct EpiInject {
   }
 };
 
-template <class Epi>
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// D[i][j] += sum_k A[i][k] B[k][j], 32x32x16, bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32] and
+// holds D[8*(v/4) + 4*(l/32) + v%4][l%32] in item v.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int TBM, class Epi>
 __global__ void __launch_bounds__(kThreads)
 gemm_tile(GemmA a, typename Epi::P p, int N) {
-  // two stages of A and B tiles; reused as the fp32 output tile at the end
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BM * LDK * 2];
-  bf16_t (*As)[BM][LDK] = reinterpret_cast<bf16_t (*)[BM][LDK]>(smem);
-  bf16_t (*Bs)[BN][LDK] = reinterpret_cast<bf16_t (*)[BN][LDK]>(smem + 2 * BM * LDK * 2);
+  constexpr int WM = TBM / 2;          // rows per wave
+  constexpr int TI = WM / 32, TJ = 2;  // 32x32 tiles per wave
+  constexpr int ALD = TBM * BK / 8 / kThreads;  // 16-byte chunks per thread
+  constexpr int BLD = BN * BK / 8 / kThreads;
+  constexpr int STAGE = (TBM + BN) * LDK;        // bf16 elements per stage
+  static_assert(128 * (BN + 1) * 4 <= 2 * STAGE * 2, "epilogue half tile fits");
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * BN;
   const int KT = a.K / BK;
+  auto As = [&](int st, int r, int k) -> bf16_t* { return smem + st * STAGE + r * LDK + k; };
+  auto Bs = [&](int st, int r, int k) -> bf16_t* { return smem + st * STAGE + (TBM + r) * LDK + k; };
 
-  // this thread's four 16-byte chunks of each tile: row = c / 8, k = (c % 8) * 8
-  const bf16_t* brow[4];
-  int arow_off[4];
-  int crow[4], ck[4];
+  int arow[ALD], acol[ALD], brow_i[BLD], bcol[BLD];
+  int64_t aoff[ALD];
+  const bf16_t* bptr[BLD];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < ALD; ++i) {
     const int c = tid + i * kThreads;
-    crow[i] = c >> 3;
-    ck[i] = (c & 7) * 8;
-    int m = m0 + crow[i];
+    arow[i] = c >> 3;
+    acol[i] = (c & 7) * 8;
+    int m = m0 + arow[i];
     m = m < a.M ? m : a.M - 1;
-    arow_off[i] = m;
-    int n = n0 + crow[i];
+    aoff[i] = (int64_t)m * a.ld + acol[i];
+  }
+#pragma unroll
+  for (int i = 0; i < BLD; ++i) {
+    const int c = tid + i * kThreads;
+    brow_i[i] = c >> 3;
+    bcol[i] = (c & 7) * 8;
+    int n = n0 + brow_i[i];
     n = n < N ? n : N - 1;
-    brow[i] = Epi::wrow(p, n) + ck[i];
+    bptr[i] = Epi::wrow(p, n) + bcol[i];
   }
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[ALD], rb[BLD];
   auto gload = [&](int kt) {
     const int k0 = kt * BK;
     const int sgi = k0 / a.seg_k, kin = k0 - sgi * a.seg_k;
-    const bf16_t* base = a.seg[sgi];
+    const bf16_t* base = a.seg[sgi] + kin;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(base + (size_t)arow_off[i] * a.ld + kin + ck[i]);
-      rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + k0);
-    }
+    for (int i = 0; i < ALD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(base + aoff[i]);
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + k0);
   };
   auto sstore = [&](int st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(&As[st][crow[i]][ck[i]]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[st][crow[i]][ck[i]]) = rb[i];
-    }
+    for (int i = 0; i < ALD; ++i) *reinterpret_cast<u32x4*>(As(st, arow[i], acol[i])) = ra[i];
+#pragma unroll
+    for (int i = 0; i < BLD; ++i) *reinterpret_cast<u32x4*>(Bs(st, brow_i[i], bcol[i])) = rb[i];
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   gload(0);
   sstore(0);
   __syncthreads();
+  const int lr = lane & 31, lk = 8 * (lane >> 5);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8 af[4], bfr[4];
-      const int kk = ks * 32 + 8 * (lane >> 4);
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[cur][wm * 64 + i * 16 + (lane & 15)][kk]));
+      for (int i = 0; i < TI; ++i)
+        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As(cur, wm * WM + i * 32 + lr, ks * 16 + lk)));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Bs[cur][wn * 64 + j * 16 + (lane & 15)][kk]));
+      for (int j = 0; j < TJ; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs(cur, wn * 64 + j * 32 + lr, ks * 16 + lk)));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
     }
     if (kt + 1 < KT) sstore(cur ^ 1);
     __syncthreads();
   }
 
+  // epilogue in 128-row halves of the tile
   float (*C)[BN + 1] = reinterpret_cast<float (*)[BN + 1]>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int half = 0; half < TBM / 128; ++half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < TI; ++i) {
+      const int r0 = wm * WM + i * 32;  // tile row of this 32x32 block
+      if (r0 / 128 != half) continue;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        C[wm * 64 + i * 16 + 4 * (lane >> 4) + e][wn * 64 + j * 16 + (lane & 15)] = acc[i][j][e];
-  __syncthreads();
-  Epi::run(p, C, m0, n0, a.M);
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          C[r0 % 128 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3)][wn * 64 + j * 32 + lr] = acc[i][j][v];
+    }
+    __syncthreads();
+    Epi::run(p, C, m0 + half * 128, n0, a.M);
+    __syncthreads();
+  }
 }
 
-static_assert(BM * (BN + 1) * 4 <= 2 * 2 * BM * LDK * 2, "output tile fits the stage buffers");
+
+// 256-row tiles when the grid still fills the chip evenly, else 128-row tiles
+template <class Epi>
+static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, int M,
+                               hipStream_t st) {
+  const int nb = (N + BN - 1) / BN;
+  const int t256 = nb * ((M + 255) / 256);
+  if (t256 >= 1024 || (t256 >= 256 && t256 % 256 == 0))
+    hipLaunchKernelGGL((gemm_tile<256, Epi>), dim3(nb, (M + 255) / 256), dim3(kThreads), 0, st, a, p, N);
+  else
+    hipLaunchKernelGGL((gemm_tile<128, Epi>), dim3(nb, (M + 127) / 128), dim3(kThreads), 0, st, a, p, N);
+  return hipGetLastError();
+}
 
 __global__ void __launch_bounds__(256)
 fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ ssq, int n_tiles, int D,
@@ -225,9 +266,7 @@ hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st) {
   EpiFuse::P p;
   p.w = F.w_c; p.K = a.K; p.N = F.D; p.out = F.out; p.ssq = F.ssq;
   p.n_tiles = (F.D + BN - 1) / BN;
-  dim3 grid(p.n_tiles, (F.T + BM - 1) / BM);
-  hipLaunchKernelGGL(gemm_tile<EpiFuse>, grid, dim3(kThreads), 0, st, a, p, F.D);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_tiled<EpiFuse>(a, p, F.D, F.T, st);
   if (e != hipSuccess) return e;
   return launch_fuse_normalize(F.out, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
 }
@@ -249,9 +288,7 @@ hipError_t launch_inject(const InjectLaunch& I, hipStream_t st) {
   }
   p.K = I.D; p.N = I.L * 2 * I.Hkv * I.hd; p.Hkv = I.Hkv; p.hd = I.hd; p.pos0 = I.pos0;
   p.cap = I.cap; p.log2_theta = I.log2_theta; p.kv = I.kv;
-  dim3 grid((p.N + BN - 1) / BN, (I.T + BM - 1) / BM);
-  hipLaunchKernelGGL(gemm_tile<EpiInject>, grid, dim3(kThreads), 0, st, a, p, p.N);
-  return hipGetLastError();
+  return launch_tiled<EpiInject>(a, p, p.N, I.T, st);
 }
 
 }  // namespace dfl

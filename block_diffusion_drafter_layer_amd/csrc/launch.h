@@ -52,6 +52,8 @@ struct DraftLaunch {
 
 int skinny_tile_cols();
 int skinny_max_rows();
+// split-buffer floats the LDS-staged streaming GEMM needs for [rows<=16] x [K] -> [n_vcols]
+size_t stream_part_floats(int n_vcols, int K);
 
 hipError_t launch_embed(const DraftLaunch& L, hipStream_t st);
 hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,

@@ -19,6 +19,8 @@
 //            (txtmix article section 9: LM head on the rows after the anchor).
 // Also here: the block embedding (section 6: anchor + mask tokens) and the
 // argmax reduction that writes the drafted block.
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -79,6 +81,19 @@ struct EpiQKV {
     }
     vc -= kvd;
     return p.wv + (size_t)vc * p.D;
+  }
+  // row r8 of the 8-column group starting at vc8 (a multiple of 8): the
+  // matrix and head follow from vc8 alone
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
+    if (vc8 < qd + kvd) {
+      const bool is_q = vc8 < qd;
+      const int vcl = is_q ? vc8 : vc8 - qd;
+      const int h = vcl / p.hd;
+      const int d = paired_dim(vcl % p.hd + r8, p.hd);
+      return (is_q ? p.wq : p.wk) + (size_t)(h * p.hd + d) * p.D;
+    }
+    return p.wv + (size_t)(vc8 - qd - kvd + r8) * p.D;
   }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
@@ -141,6 +156,9 @@ struct EpiResid {
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     return p.w + (size_t)vc * p.K;
   }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return p.w + (size_t)(vc8 + r8) * p.K;
+  }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float*,
                              int vc0, int m0, int M) {
@@ -182,6 +200,9 @@ struct EpiSwiglu {
     const int f = (t << 3) + (j & 7);
     return (j < 8 ? p.wg : p.wu) + (size_t)f * p.K;
   }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return ((vc8 & 8) ? p.wu : p.wg) + (size_t)((vc8 >> 4) * 8 + r8) * p.K;
+  }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
                              int vc0, int m0, int M) {
@@ -209,6 +230,9 @@ struct EpiLM {
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     return p.w + (size_t)(vc < p.V ? vc : p.V - 1) * p.K;
+  }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return wrow(p, vc8 + r8);
   }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
@@ -246,6 +270,9 @@ struct EpiFuseRows {
     int n_vcols;      // D
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return p.w + (size_t)(vc8 + r8) * p.K;
+  }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
                              int M) {
@@ -288,6 +315,15 @@ struct EpiInjectRows {
       return p.wk[i] + (size_t)(h * p.hd + d) * p.D;
     }
     return p.wv[i] + (size_t)(r - kvd) * p.D;
+  }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    const int kvd = p.Hkv * p.hd;
+    const int i = vc8 / (2 * kvd), r = vc8 % (2 * kvd);
+    if (r < kvd) {
+      const int h = r / p.hd, d = paired_dim(r % p.hd + r8, p.hd);
+      return p.wk[i] + (size_t)(h * p.hd + d) * p.D;
+    }
+    return p.wv[i] + (size_t)(r - kvd + r8) * p.D;
   }
   template <int ROWS, int VC>
   __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
@@ -484,6 +520,173 @@ skinny_finish(SkinnyA a, typename Epi::P ep, SplitK sk) {
 }
 
 // ---------------------------------------------------------------------------
+// LDS-staged streaming GEMM for up to 16 activation rows
+// ---------------------------------------------------------------------------
+// The weights arrive by direct global->LDS loads of whole 128-byte row
+// segments (8 rows per wave instruction) into a ring of R slots per wave and
+// are read back as MFMA B fragments through an XOR swizzle that keeps the
+// 16-byte lane reads free of bank conflicts. (Loading the fragment layout
+// straight into registers touches 16 rows x 64 bytes per instruction, which
+// streams measurably slower.) The workgroup's K slice of the activations
+// sits in LDS in fragment order. Each wave owns whole units - one 16-column
+// tile over the slice - so the loop has no barrier; a barrier would wait for
+// every direct load in flight. Units go round-robin over the waves of the
+// workgroups that share a slice; the grid is one workgroup per CU. Each unit
+// writes an fp32 partial tile; the finisher sums the slices in order and
+// runs the epilogue.
+
+constexpr int kSW = 8;             // waves per workgroup
+constexpr int kStreamGrid = 256;   // workgroups: one per CU
+constexpr int kItem = 2048;        // ring slot: 16 weight rows x 64 k (bf16)
+
+// s_waitcnt immediate for vmcnt <= n (0..15), expcnt and lgkmcnt left open
+#define DFL_VMCNT(n) (0xF70 | (n))
+#define DFL_LGKM0 0xC07F
+
+// Two 16-byte LDS reads, complete on return. Written as inline assembly so
+// the compiler's wait-count pass does not treat them as possibly aliasing
+// the direct loads still in flight into other ring slots (it would drain
+// every outstanding load before each read); explicit vmcnt waits order the
+// ring instead.
+__device__ __forceinline__ void ring_read2(u32x4& x, u32x4& y, const void* px, const void* py) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x), "=&v"(y)
+               : "v"((uint32_t)(uintptr_t)px), "v"((uint32_t)(uintptr_t)py)
+               : "memory");
+}
+
+// 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
+// wave-uniform). A plain function: inside a kernel template the builtin
+// keeps the host pass from emitting the launch stub.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+template <int R>
+__device__ __forceinline__ void wait_vm_tail(int n) {
+  // n = direct-load instructions allowed to stay in flight (2 per item)
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(0)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(2)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(4)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(6)); break;
+    case 8: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(8)); break;
+    default: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(10)); break;
+  }
+}
+
+template <int KCM, int R, bool LO, class Epi>
+__global__ void __launch_bounds__(kSW * 64)
+stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* __restrict__ part) {
+  static_assert(2 * (R - 1) <= 10, "vmcnt thresholds of wait_vm_tail");
+  __shared__ __attribute__((aligned(16))) u32x4 As[KCM / 32][2][64];     // [k step][hi, lo][lane]
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kSW][R][kItem];
+  const int lane = threadIdx.x & 63;
+  // wave-uniform in a scalar register: the matrix and segment choices below
+  // then compile to scalar selects, never to per-lane loads of kernel
+  // arguments (a vector load in the loop would wait for every direct load)
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int slice = blockIdx.x % ks;
+  const int k0 = slice * kc;
+  const int nsteps = kc >> 5;
+
+  // the slice of the activations, in MFMA A-fragment order: wave w fills
+  // fragments w, w + 8, ... (each one k step, hi or lo); every load is issued
+  // before the first store
+  {
+    constexpr int PER = KCM / 32 * 2 / kSW;
+    u32x4 v[PER];
+    const int m = lane & 15;
+    const bool mv = m < a.M;
+    const size_t row = (size_t)in_row(a, mv ? m : 0) * a.lda;
+    // unconditional loads from clamped addresses, zeroed at the store, so
+    // that all of them are in flight together
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int fr = w + u * kSW, hl = fr & 1;
+      const int st = min(fr >> 1, nsteps - 1);
+      const int kst = k0 + st * 32;
+      const int k = kst + 8 * (lane >> 4);
+      if (LO && hl) {
+        v[u] = *reinterpret_cast<const u32x4*>(a.xl + row + k);
+      } else {
+        const int sg = kst / a.seg_k;
+        v[u] = *reinterpret_cast<const u32x4*>(a.seg[sg] + row + (k - sg * a.seg_k));
+      }
+    }
+    // stores of steps past the slice land in unused slots (fr / 2 < KCM / 32)
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int fr = w + u * kSW, hl = fr & 1;
+      const bool keep = mv && (hl == 0 || LO);
+      As[fr >> 1][hl][lane] = keep ? v[u] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+
+  const int gw = (blockIdx.x / ks) * kSW + w;  // wave within the slice's group
+  const int Wg = (gridDim.x / ks) * kSW;
+  const int n_tiles = (n_vcols + 15) >> 4;
+  const int units = gw < n_tiles ? (n_tiles - gw + Wg - 1) / Wg : 0;
+  const int ipu = kc >> 6;                      // ring items per unit
+  const int n_items = units * ipu;
+  uint8_t* my_ring = &ring[w][0][0];
+
+  // direct loads of item t: rows r = 8q + lane/8, 16-byte chunk lane%8 of the
+  // slot row holds the row's chunk (lane%8) ^ ((r/2)%8)
+  auto issue = [&](int t) {
+    const int j = t / ipu, i = t - j * ipu;
+    const int tile = gw + j * Wg;
+    const int kk = k0 + i * 64;
+    uint8_t* slot = my_ring + (t % R) * kItem;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = 8 * q + (lane >> 3);
+      int vc8 = tile * 16 + 8 * q;                       // uniform group start
+      vc8 = vc8 < n_vcols ? vc8 : ((n_vcols - 1) >> 3) << 3;
+      int r8 = lane >> 3;
+      r8 = vc8 + r8 < n_vcols ? r8 : n_vcols - 1 - vc8;  // ragged last group
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      dma16(Epi::wrow8(ep, vc8, r8) + kk + c * 8, slot + q * 1024);
+    }
+  };
+
+  const int pre = n_items < R - 1 ? n_items : R - 1;
+  for (int t = 0; t < pre; ++t) issue(t);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int br = lane & 15;
+  for (int t = 0; t < n_items; ++t) {
+    // the slot refilled below was read in the previous iteration
+    __builtin_amdgcn_s_waitcnt(DFL_LGKM0);
+    if (t + R - 1 < n_items) {
+      issue(t + R - 1);
+      __builtin_amdgcn_s_waitcnt(DFL_VMCNT(2 * (R - 1)));
+    } else {
+      wait_vm_tail<R>(2 * (n_items - 1 - t));
+    }
+    const uint8_t* slot = my_ring + (t % R) * kItem + br * 128;
+    const int i = t % ipu;
+    const int c0 = lane >> 4, sw = (br >> 1) & 7;
+    u32x4 b[2];
+    ring_read2(b[0], b[1], slot + ((c0 ^ sw) << 4), slot + (((c0 + 4) ^ sw) << 4));
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int st = 2 * i + sub;
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[sub]);
+      acc = mfma16x16x32(__builtin_bit_cast(bf16x8, As[st][0][lane]), bb, acc);
+      if (LO) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, As[st][1][lane]), bb, acc);
+    }
+    if (i == ipu - 1) {  // unit complete: its partial tile, layout [pair][split][16][32]
+      const int tile = gw + (t / ipu) * Wg;
+      float* dst = part + ((size_t)(tile >> 1) * ks + slice) * 512 + (tile & 1) * 16 + br;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[(4 * (lane >> 4) + e) * 32] = acc[e];
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // embedding of the block and the drafted-token reduction
 // ---------------------------------------------------------------------------
 
@@ -579,9 +782,59 @@ hipError_t launch_cfg(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, 
   return hipGetLastError();
 }
 
+// Split of K for the LDS-staged kernel: slices of at most 1024 (the LDS
+// activation buffer), a power of two dividing the grid, chosen so the units
+// (16-column tiles x slices) spread evenly over the grid's waves.
+bool stream_plan(int M, int n_vcols, int K, int& ks_out) {
+  if (M < 1 || M > 16 || K % 64) return false;
+  const int tiles = (n_vcols + 15) / 16;
+  const double waves = (double)kStreamGrid * kSW;
+  int best = 0;
+  double best_eff = 0.0;
+  for (int ks = 1; ks <= kStreamGrid; ks *= 2) {
+    if (K % ks || (K / ks) % 64 || K / ks > 1024) continue;
+    const double units = (double)tiles * ks;
+    const double per = std::ceil(units / waves);
+    const double eff = units / (waves * per);
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
+    if (eff >= 0.9) break;
+  }
+  if (!best) return false;
+  ks_out = best;
+  return true;
+}
+
+template <class Epi, bool LO>
+hipError_t launch_stream(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, int ks,
+                         const SplitWs& ws, hipStream_t st) {
+  const int kc = a.K / ks;
+  if (kc <= 512)
+    hipLaunchKernelGGL((stream_gemm<512, 6, LO, Epi>), dim3(kStreamGrid), dim3(kSW * 64), 0, st,
+                       a, ep, n_vcols, ks, kc, ws.part);
+  else
+    hipLaunchKernelGGL((stream_gemm<1024, 4, LO, Epi>), dim3(kStreamGrid), dim3(kSW * 64), 0, st,
+                       a, ep, n_vcols, ks, kc, ws.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SplitK sk;
+  sk.ksplit = ks;
+  sk.steps = kc / 32;
+  sk.part = ws.part;
+  hipLaunchKernelGGL((skinny_finish<1, 2, Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, sk);
+  return hipGetLastError();
+}
+
+// true when launch_skinny takes the LDS-staged kernel for this shape
+bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
+  if (!ws.part || !stream_plan(a.M, n_vcols, a.K, ks)) return false;
+  return (size_t)((n_vcols + 31) / 32) * ks * 512 <= ws.part_floats;
+}
+
 template <class Epi, bool LO = true>
 hipError_t launch_skinny(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
                          const SplitWs& ws, hipStream_t st) {
+  int ks;
+  if (uses_stream(a, n_vcols, ws, ks)) return launch_stream<Epi, LO>(a, ep, n_vcols, ks, ws, st);
   if (a.M <= 16) return launch_cfg<Epi, LO, 1, 4, 4>(a, ep, n_vcols, ws, st);
   if (a.M <= 32) return launch_cfg<Epi, LO, 2, 4, 2>(a, ep, n_vcols, ws, st);
   // more rows: 64-row blocks over grid.y, each streaming the weights again
@@ -602,6 +855,12 @@ SkinnyA make_a(const bf16_t* xh, const bf16_t* xl, int lda, int M, int K,
 
 int skinny_tile_cols() { return 32; }  // narrowest column block of any configuration
 int skinny_max_rows() { return 64; }
+
+size_t stream_part_floats(int n_vcols, int K) {
+  int ks;
+  if (!stream_plan(16, n_vcols, K, ks)) return 0;
+  return (size_t)((n_vcols + 31) / 32) * ks * 512;
+}
 
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
   SkinnyA a = make_a(F.feats[0], nullptr, (int)F.ld, F.T, F.n_feat * F.D, nullptr, 0, F.eps);
@@ -669,18 +928,24 @@ hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
   a.a_group = g; a.a_stride = L.Bl; a.a_off = 1;
   EpiLM::P p;
   p.w = w_lm; p.K = L.D; p.V = L.V; p.logits = logits; p.part = L.lm_part;
-  // the LM head never splits K (its vocab gives thousands of column blocks);
-  // one argmax key per column block and row goes to lm_part
-  const SplitWs none{};
   hipError_t e;
-  int vc;
-  if (M_lm <= 16) {
+  int vc, ks;
+  if (uses_stream(a, L.V, L.split, ks)) {
+    // LDS-staged kernel and finisher: one argmax key per 32 columns and row
+    e = launch_stream<EpiLM, true>(a, p, L.V, ks, L.split, st);
+    vc = 32;
+  } else if (M_lm <= 16) {
+    // the register-streaming kernel never splits the LM head's K (its vocab
+    // gives thousands of column blocks); one key per column block and row
+    const SplitWs none{};
     e = launch_cfg<EpiLM, true, 1, 8, 2>(a, p, L.V, none, st);
     vc = 128;
   } else if (M_lm <= 32) {
+    const SplitWs none{};
     e = launch_cfg<EpiLM, true, 2, 4, 2>(a, p, L.V, none, st);
     vc = 64;
   } else {
+    const SplitWs none{};
     e = launch_cfg<EpiLM, true, 4, 2, 2>(a, p, L.V, none, st);
     vc = 32;
   }

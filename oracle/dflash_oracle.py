@@ -80,7 +80,7 @@ def softmax(x, axis=-1):
 
 
 # ----------------------------------------------------------------------------
-# S1: target-context fusion
+# Target-context fusion
 # ----------------------------------------------------------------------------
 
 def fuse_context(feats: Sequence, w_c, gain, eps: float = 1e-6):
@@ -119,7 +119,7 @@ def apply_rope(x, positions, theta: float):
 
 
 # ----------------------------------------------------------------------------
-# S2 / S10: KV injection into the draft cache, trim and append
+# KV injection into the draft cache, trim and append
 # ----------------------------------------------------------------------------
 
 def inject_kv(ctx_feat, wk, wv, pos0: int, n_kv_heads: int, head_dim: int,
@@ -190,7 +190,7 @@ def cache_inject(cache: DraftCache, ctx_feat, layers_w, cfg, pos0: int):
 
 
 # ----------------------------------------------------------------------------
-# S5: block attention
+# Block attention
 # ----------------------------------------------------------------------------
 
 def block_attention(q, k, v):
@@ -213,7 +213,7 @@ def block_attention(q, k, v):
 
 
 # ----------------------------------------------------------------------------
-# S3-S8: one draft forward over a block
+# One draft forward over a block
 # ----------------------------------------------------------------------------
 
 def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
@@ -280,7 +280,7 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
 
 
 # ----------------------------------------------------------------------------
-# S9: greedy verification
+# Greedy verification
 # ----------------------------------------------------------------------------
 
 def verify_greedy(block_ids, target_logits):
@@ -348,7 +348,7 @@ def sample_inverse_cdf(weights, u: float):
 
 
 # ----------------------------------------------------------------------------
-# S11: p/q rejection-sampling verification
+# p/q rejection-sampling verification
 # ----------------------------------------------------------------------------
 
 def verify_pq_with_uniforms(block_ids, target_logits, draft_logits,

@@ -1,4 +1,4 @@
-"""GPU parity of context fusion (S1), KV injection (S2) and trim/append (S10)."""
+"""GPU parity of context fusion, KV injection and trim/append of the draft KV cache."""
 import numpy as np
 import pytest
 import torch
@@ -47,6 +47,32 @@ def test_fuse_qwen_shape_sampled_rows():
     _fuse_check(dc, 2048, rows=np.sort(rng.choice(2048, 64, replace=False)), gains="ones")
 
 
+@pytest.mark.slow
+def test_fuse_qwen_shape_8192_rows_sampled():
+    # 256-row tiles: 32 x 32 of them
+    dc = CONFIGS[2]
+    rng = np.random.default_rng(3)
+    rows = np.sort(np.concatenate([rng.choice(8192, 40, replace=False), [0, 8191]]))
+    _fuse_check(dc, 8192, rows=np.unique(rows), gains="random")
+
+
+def test_fuse_qwen_shape_ragged_rows():
+    # 2148 rows: 17 row tiles of 128, the last one ragged
+    dc = CONFIGS[1]
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.choice(2048, 24, replace=False), np.arange(2040, 2148, 9), [2147]]))
+    _fuse_check(dc, 2148, rows=rows, gains="random")
+
+
+def test_fuse_many_rows_narrow_hidden():
+    # 16484 rows of a 640-wide hidden state (5 column tiles, ragged last row tile)
+    dc = CONFIGS[1].shrink(hidden=640, index=95)
+    T = 16384 + 100
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(T, 40, replace=False), [T - 1, T - 100]]))
+    _fuse_check(dc, T, rows=rows, gains="random")
+
+
 def _inject_check(dc, T, pos0_chunks, rows=None, gains="ones"):
     say(f"inject: config {dc.name} T={T} chunks={pos0_chunks}")
     d, w = make(dc, max_tokens=max(pos0_chunks) if pos0_chunks else T, gains=gains)
@@ -85,6 +111,14 @@ def test_inject_qwen_shape_sampled_rows():
     dc = CONFIGS[1]
     rng = np.random.default_rng(2)
     _inject_check(dc, 2048, [2048], rows=np.sort(rng.choice(2048, 24, replace=False)))
+
+
+def test_inject_qwen_shape_ragged_rows():
+    # 2148 rows: a ragged last row tile
+    dc = CONFIGS[1]
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([rng.choice(2048, 10, replace=False), [2047, 2048, 2100, 2147]]))
+    _inject_check(dc, 2148, [2148], rows=rows)
 
 
 def test_trim_then_append_overwrites_rejected_rows():

@@ -1,4 +1,4 @@
-"""GPU parity of the draft forward (S3-S8) against the oracle: every layer's
+"""GPU parity of the draft forward against the oracle: every layer's
 residual stream within 3e-2 x RMS, drafted tokens identical except where the
 oracle's top-2 gap is below 1e-2. KV buffers are filled with NaN first, so any
 read of a row outside [0, len + block_len) would show up as non-finite."""

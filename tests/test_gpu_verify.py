@@ -1,4 +1,4 @@
-"""GPU parity of verification (S9 greedy, S11 p/q) against the oracle.
+"""GPU parity of verification (greedy and p/q) against the oracle.
 
 tau and bonus must be bit-exact; for p/q, rows whose accept test has
 |p/q - u| < 1e-4 or whose final draw lies within 1e-12 (relative) of a CDF

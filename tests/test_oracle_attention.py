@@ -1,4 +1,4 @@
-"""Pins of the oracle's block attention (S5)."""
+"""Pins of the oracle's block attention."""
 import math
 
 import numpy as np

@@ -1,4 +1,4 @@
-"""Pins of the oracle's full draft forward (S3-S8).
+"""Pins of the oracle's full draft forward.
 
 The pages print no values for a draft forward (no trained weights exist), so
 the forward is pinned by an independent fp64 composition written with torch

@@ -1,4 +1,4 @@
-"""Pins of the oracle's context fusion (S1) against the pages and mathematics."""
+"""Pins of the oracle's context fusion against the pages and mathematics."""
 import os
 
 import numpy as np

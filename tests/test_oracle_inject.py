@@ -1,4 +1,4 @@
-"""Pins of the oracle's RoPE, KV injection (S2) and trim/append (S10)."""
+"""Pins of the oracle's RoPE, KV injection and trim/append."""
 import math
 
 import numpy as np

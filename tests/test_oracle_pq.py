@@ -1,4 +1,4 @@
-"""Pins of the oracle's p/q rejection-sampling verification (S11) and its RNG."""
+"""Pins of the oracle's p/q rejection-sampling verification and its RNG."""
 import math
 
 import numpy as np

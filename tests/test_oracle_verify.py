@@ -1,4 +1,4 @@
-"""Pins of the oracle's greedy verification (S9)."""
+"""Pins of the oracle's greedy verification."""
 import numpy as np
 import torch
 
