@@ -522,37 +522,60 @@ skinny_finish(SkinnyA a, typename Epi::P ep, SplitK sk) {
 // ---------------------------------------------------------------------------
 // LDS-staged streaming GEMM for up to 16 activation rows
 // ---------------------------------------------------------------------------
-// The weights arrive by direct global->LDS loads of whole 128-byte row
-// segments (8 rows per wave instruction) into a ring of R slots per wave and
-// are read back as MFMA B fragments through an XOR swizzle that keeps the
-// 16-byte lane reads free of bank conflicts. (Loading the fragment layout
-// straight into registers touches 16 rows x 64 bytes per instruction, which
-// streams measurably slower.) The workgroup's K slice of the activations
-// sits in LDS in fragment order. Each wave owns whole units - one 16-column
-// tile over the slice - so the loop has no barrier; a barrier would wait for
-// every direct load in flight. Units go round-robin over the waves of the
-// workgroups that share a slice; the grid is one workgroup per CU. Each unit
-// writes an fp32 partial tile; the finisher sums the slices in order and
-// runs the epilogue.
+// The weights arrive by direct global->LDS loads into a ring of R slots per
+// wave. A slot holds 16 weight rows x 256 k (8 KB); each load instruction
+// fetches 512 contiguous bytes of two rows, so DRAM sees long row bursts
+// (fewer, longer bursts measured faster than 128-byte pieces, and those
+// faster than the MFMA operand layout loaded straight into registers). The
+// rows are read back as MFMA B fragments through an XOR swizzle (16-byte
+// chunk c of row r stored at chunk c ^ r) that keeps the lane reads free of
+// bank conflicts. The workgroup's K slice of the activations sits in LDS in
+// fragment order. Each wave owns whole units - one 16-column tile over the
+// slice - so the loop has no barrier: a barrier would wait for every direct
+// load in flight. Units go round-robin over the waves of the workgroups that
+// share a slice; the grid is one workgroup per CU. Each unit leaves an fp32
+// partial tile; the finisher sums the slices in order and runs the epilogue.
 
-constexpr int kSW = 8;             // waves per workgroup
-constexpr int kStreamGrid = 256;   // workgroups: one per CU
-constexpr int kItem = 2048;        // ring slot: 16 weight rows x 64 k (bf16)
+constexpr int kSW = 4;             // waves per workgroup
+constexpr int kCUs = 256;          // the grid: at most one workgroup per CU
+constexpr int kItemK = 256;        // k per ring slot
+constexpr int kItem = 16 * kItemK * 2;  // ring slot bytes
+constexpr int kItemLoads = kItem / 1024;  // direct-load instructions per slot
+constexpr int kSliceMax = 1024;    // k per workgroup slice (LDS activation buffer)
+#ifndef DFL_STREAM_RING
+#define DFL_STREAM_RING 3
+#endif
+#ifndef DFL_STREAM_BATCH
+#define DFL_STREAM_BATCH 4
+#endif
+constexpr int kStreamRing = DFL_STREAM_RING;    // ring slots per wave
+constexpr int kStreamBatch = DFL_STREAM_BATCH;  // units per batch of partial stores
 
-// s_waitcnt immediate for vmcnt <= n (0..15), expcnt and lgkmcnt left open
-#define DFL_VMCNT(n) (0xF70 | (n))
+// s_waitcnt immediate for vmcnt <= n (0..63), expcnt and lgkmcnt left open
+#define DFL_VMCNT(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0xF70)
 #define DFL_LGKM0 0xC07F
 
-// Two 16-byte LDS reads, complete on return. Written as inline assembly so
-// the compiler's wait-count pass does not treat them as possibly aliasing
-// the direct loads still in flight into other ring slots (it would drain
-// every outstanding load before each read); explicit vmcnt waits order the
-// ring instead.
-__device__ __forceinline__ void ring_read2(u32x4& x, u32x4& y, const void* px, const void* py) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x), "=&v"(y)
-               : "v"((uint32_t)(uintptr_t)px), "v"((uint32_t)(uintptr_t)py)
-               : "memory");
+// The eight 16-byte B-fragment reads of one ring slot (k steps 0..7 of row
+// r = lane % 16: chunk 4s + lane / 16, stored at that chunk ^ r), complete on
+// return. Inline assembly, so that the compiler's wait-count pass does not
+// treat them as possibly aliasing the direct loads still in flight into the
+// other ring slots (it would drain every outstanding load before each read);
+// explicit vmcnt waits order the ring instead. Activation reads the compiler
+// issued before this block are complete on return as well.
+__device__ __forceinline__ void ring_read8(u32x4 (&b)[8], const uint8_t* row, int c0, int r) {
+  const uint32_t base = (uint32_t)(uintptr_t)row;
+  uint32_t ad[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) ad[s] = base + ((((4 * s) + c0) ^ r) << 4);
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]),
+        "=&v"(b[6]), "=&v"(b[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7])
+      : "memory");
 }
 
 // 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
@@ -562,24 +585,22 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
 
-template <int R>
-__device__ __forceinline__ void wait_vm_tail(int n) {
-  // n = direct-load instructions allowed to stay in flight (2 per item)
-  switch (n) {
+// wait until at most n direct loads (whole slots) are in flight
+__device__ __forceinline__ void wait_vm_slots(int slots_after) {
+  switch (slots_after) {
     case 0: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(0)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(2)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(4)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(6)); break;
-    case 8: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(8)); break;
-    default: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(10)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(kItemLoads)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(2 * kItemLoads)); break;
+    default: __builtin_amdgcn_s_waitcnt(DFL_VMCNT(3 * kItemLoads)); break;
   }
 }
 
-template <int KCM, int R, bool LO, class Epi>
+template <int R, int UB, bool LO, class Epi>
 __global__ void __launch_bounds__(kSW * 64)
 stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* __restrict__ part) {
-  static_assert(2 * (R - 1) <= 10, "vmcnt thresholds of wait_vm_tail");
-  __shared__ __attribute__((aligned(16))) u32x4 As[KCM / 32][2][64];     // [k step][hi, lo][lane]
+  static_assert(R >= 2 && R - 1 <= 3, "slots in flight handled by wait_vm_slots");
+  static_assert(kItemK == 256, "ring_read8 covers 8 k steps per slot");
+  __shared__ __attribute__((aligned(16))) u32x4 As[kSliceMax / 32][2][64];  // [k step][hi, lo][lane]
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSW][R][kItem];
   const int lane = threadIdx.x & 63;
   // wave-uniform in a scalar register: the matrix and segment choices below
@@ -590,11 +611,42 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
   const int k0 = slice * kc;
   const int nsteps = kc >> 5;
 
+  const int gw = (blockIdx.x / ks) * kSW + w;  // wave within the slice's group
+  const int Wg = (gridDim.x / ks) * kSW;
+  const int n_tiles = (n_vcols + 15) >> 4;
+  const int units = gw < n_tiles ? (n_tiles - gw + Wg - 1) / Wg : 0;
+  const int ipu = kc / kItemK;                  // ring slots per unit
+  const int n_items = units * ipu;
+  uint8_t* my_ring = &ring[w][0][0];
+
+  // direct loads of slot t: instruction q covers rows 2q and 2q + 1 (lanes
+  // 0-31 and 32-63), 512 bytes each; chunk position p of row r receives the
+  // row's chunk p ^ r
+  auto issue = [&](int t) {
+    const int j = t / ipu, i = t - j * ipu;
+    const int tile = gw + j * Wg;
+    const int kk = k0 + i * kItemK;
+    uint8_t* slot = my_ring + (t % R) * kItem;
+    const int hi = lane >> 5, pos = lane & 31;
+#pragma unroll
+    for (int q = 0; q < kItemLoads; ++q) {
+      const int r = 2 * q + hi;
+      int vc8 = tile * 16 + ((2 * q) & ~7);              // uniform 8-row group
+      vc8 = vc8 < n_vcols ? vc8 : ((n_vcols - 1) >> 3) << 3;
+      int r8 = ((2 * q) & 7) + hi;
+      r8 = vc8 + r8 < n_vcols ? r8 : n_vcols - 1 - vc8;  // ragged last group
+      dma16(Epi::wrow8(ep, vc8, r8) + kk + ((pos ^ r) << 3), slot + q * 1024);
+    }
+  };
+  // the weight stream starts before the activations are in place
+  const int pre = n_items < R - 1 ? n_items : R - 1;
+  for (int t = 0; t < pre; ++t) issue(t);
+
   // the slice of the activations, in MFMA A-fragment order: wave w fills
-  // fragments w, w + 8, ... (each one k step, hi or lo); every load is issued
-  // before the first store
+  // fragments w, w + kSW, ... (each one k step, hi or lo); every load is
+  // issued before the first store
   {
-    constexpr int PER = KCM / 32 * 2 / kSW;
+    constexpr int PER = kSliceMax / 32 * 2 / kSW;
     u32x4 v[PER];
     const int m = lane & 15;
     const bool mv = m < a.M;
@@ -614,7 +666,7 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
         v[u] = *reinterpret_cast<const u32x4*>(a.seg[sg] + row + (k - sg * a.seg_k));
       }
     }
-    // stores of steps past the slice land in unused slots (fr / 2 < KCM / 32)
+    // steps past the slice land in unused slots (fr / 2 < kSliceMax / 32)
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int fr = w + u * kSW, hl = fr & 1;
@@ -624,64 +676,54 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
   }
   __syncthreads();
 
-  const int gw = (blockIdx.x / ks) * kSW + w;  // wave within the slice's group
-  const int Wg = (gridDim.x / ks) * kSW;
-  const int n_tiles = (n_vcols + 15) >> 4;
-  const int units = gw < n_tiles ? (n_tiles - gw + Wg - 1) / Wg : 0;
-  const int ipu = kc >> 6;                      // ring items per unit
-  const int n_items = units * ipu;
-  uint8_t* my_ring = &ring[w][0][0];
-
-  // direct loads of item t: rows r = 8q + lane/8, 16-byte chunk lane%8 of the
-  // slot row holds the row's chunk (lane%8) ^ ((r/2)%8)
-  auto issue = [&](int t) {
-    const int j = t / ipu, i = t - j * ipu;
-    const int tile = gw + j * Wg;
-    const int kk = k0 + i * 64;
-    uint8_t* slot = my_ring + (t % R) * kItem;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int r = 8 * q + (lane >> 3);
-      int vc8 = tile * 16 + 8 * q;                       // uniform group start
-      vc8 = vc8 < n_vcols ? vc8 : ((n_vcols - 1) >> 3) << 3;
-      int r8 = lane >> 3;
-      r8 = vc8 + r8 < n_vcols ? r8 : n_vcols - 1 - vc8;  // ragged last group
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      dma16(Epi::wrow8(ep, vc8, r8) + kk + c * 8, slot + q * 1024);
-    }
-  };
-
-  const int pre = n_items < R - 1 ? n_items : R - 1;
-  for (int t = 0; t < pre; ++t) issue(t);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int br = lane & 15;
-  for (int t = 0; t < n_items; ++t) {
-    // the slot refilled below was read in the previous iteration
+  const int c0 = lane >> 4;
+  auto step = [&](int t, int i, f32x4& acc) {
+    // the slot refilled below was read in the previous step
     __builtin_amdgcn_s_waitcnt(DFL_LGKM0);
     if (t + R - 1 < n_items) {
       issue(t + R - 1);
-      __builtin_amdgcn_s_waitcnt(DFL_VMCNT(2 * (R - 1)));
+      __builtin_amdgcn_s_waitcnt(DFL_VMCNT((R - 1) * kItemLoads));
     } else {
-      wait_vm_tail<R>(2 * (n_items - 1 - t));
+      wait_vm_slots(n_items - 1 - t);
     }
-    const uint8_t* slot = my_ring + (t % R) * kItem + br * 128;
-    const int i = t % ipu;
-    const int c0 = lane >> 4, sw = (br >> 1) & 7;
-    u32x4 b[2];
-    ring_read2(b[0], b[1], slot + ((c0 ^ sw) << 4), slot + (((c0 + 4) ^ sw) << 4));
+    const uint8_t* row = my_ring + (t % R) * kItem + br * (kItemK * 2);
+    // activation fragments of the slot's 8 k steps, then its weight
+    // fragments: one LDS round trip for all of them
+    u32x4 ah[8], al[8];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int st = 2 * i + sub;
-      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[sub]);
-      acc = mfma16x16x32(__builtin_bit_cast(bf16x8, As[st][0][lane]), bb, acc);
-      if (LO) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, As[st][1][lane]), bb, acc);
+    for (int s8 = 0; s8 < 8; ++s8) {
+      ah[s8] = As[i * 8 + s8][0][lane];
+      if (LO) al[s8] = As[i * 8 + s8][1][lane];
     }
-    if (i == ipu - 1) {  // unit complete: its partial tile, layout [pair][split][16][32]
-      const int tile = gw + (t / ipu) * Wg;
-      float* dst = part + ((size_t)(tile >> 1) * ks + slice) * 512 + (tile & 1) * 16 + br;
+    u32x4 b[8];
+    ring_read8(b, row, c0, br);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[(4 * (lane >> 4) + e) * 32] = acc[e];
-      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, b[s8]);
+      acc = mfma16x16x32(__builtin_bit_cast(bf16x8, ah[s8]), bb, acc);
+      if (LO) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, al[s8]), bb, acc);
+    }
+  };
+  // units in batches of UB whose partial tiles are stored together, each as
+  // one contiguous kilobyte in MFMA lane order (layout [tile][split][lane][4]:
+  // lane l, item e holds row 4 (l / 16) + e, column l % 16): a store makes the
+  // following ring waits wait for it as well, so fewer, larger batches keep
+  // the stream flowing
+  for (int jb = 0; jb < units; jb += UB) {
+    f32x4 acc[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jb + u < units)
+        for (int i = 0; i < ipu; ++i) step((jb + u) * ipu + i, i, acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (jb + u < units) {
+        const int tile = gw + (jb + u) * Wg;
+        *reinterpret_cast<f32x4*>(part + ((size_t)tile * ks + slice) * 256 + lane * 4) = acc[u];
+      }
     }
   }
 }
@@ -782,21 +824,68 @@ hipError_t launch_cfg(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, 
   return hipGetLastError();
 }
 
-// Split of K for the LDS-staged kernel: slices of at most 1024 (the LDS
-// activation buffer), a power of two dividing the grid, chosen so the units
-// (16-column tiles x slices) spread evenly over the grid's waves.
+// Sum of a 32-column pair's slice partials of the LDS-staged kernel, in slice
+// order, then the epilogue. The row norms' sums of squares are fetched
+// together with the partials.
+template <class Epi>
+__global__ void __launch_bounds__(256)
+stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ part) {
+  __shared__ float tile[16][33];
+  __shared__ float rs[16];
+  const int t = threadIdx.x, pair = blockIdx.x;
+  // thread t: element t of both tiles of the pair ([lane][4] order)
+  const int ln = t >> 2, e = t & 3;
+  const int m = 4 * (ln >> 4) + e, n = ln & 15;
+  // row scales: wave w sums rows 4w..4w+3 (16 lanes each)
+  const int lane = t & 63, w = t >> 6;
+  const int srow = 4 * w + (lane >> 4);
+  float sq = 0.f;
+  if (a.ssq && srow < a.M) {
+    const float* q = a.ssq + (size_t)in_row(a, srow) * a.ssq_ld;
+    for (int g = lane & 15; g < a.ssq_ld; g += 16) sq += q[g];
+  }
+  const float* p0 = part + ((size_t)(2 * pair) * ks) * 256 + t;
+  const float* p1 = p0 + (size_t)ks * 256;
+  float s0 = 0.f, s1 = 0.f;
+  for (int k0 = 0; k0 < ks; k0 += kFinishBatch) {
+    float v0[kFinishBatch], v1[kFinishBatch];
+#pragma unroll
+    for (int k = 0; k < kFinishBatch; ++k) {
+      v0[k] = k0 + k < ks ? p0[(size_t)(k0 + k) * 256] : 0.f;
+      v1[k] = k0 + k < ks ? p1[(size_t)(k0 + k) * 256] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kFinishBatch; ++k) { s0 += v0[k]; s1 += v1[k]; }  // slice order
+  }
+  tile[m][n] = s0;
+  tile[m][16 + n] = s1;
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+  if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
+  __syncthreads();
+  Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
+}
+
+// Split of K for the LDS-staged kernel: slices of whole ring slots and at
+// most kSliceMax (the LDS activation buffer), chosen so the units (16-column
+// tiles x slices) spread evenly over the waves of the grid, which holds
+// ks * floor(kCUs / ks) workgroups.
+int stream_grid(int ks) { return ks * (kCUs / ks); }
+
 bool stream_plan(int M, int n_vcols, int K, int& ks_out) {
-  if (M < 1 || M > 16 || K % 64) return false;
+  if (M < 1 || M > 16 || K % kItemK) return false;
   const int tiles = (n_vcols + 15) / 16;
-  const double waves = (double)kStreamGrid * kSW;
   int best = 0;
   double best_eff = 0.0;
-  for (int ks = 1; ks <= kStreamGrid; ks *= 2) {
-    if (K % ks || (K / ks) % 64 || K / ks > 1024) continue;
+  for (int ks = 1; ks <= kCUs; ++ks) {
+    if (K % ks || (K / ks) % kItemK || K / ks > kSliceMax) continue;
+    const double waves = (double)stream_grid(ks) * kSW;
     const double units = (double)tiles * ks;
     const double per = std::ceil(units / waves);
-    const double eff = units / (waves * per);
-    if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
+    // time ~ per-wave units x slice length; fewer slices also mean less
+    // partial traffic, so ties go to the smaller split
+    const double eff = units / (waves * per) * ((double)stream_grid(ks) / kCUs);
+    if (eff > best_eff + 0.02) { best_eff = eff; best = ks; }
     if (eff >= 0.9) break;
   }
   if (!best) return false;
@@ -808,26 +897,19 @@ template <class Epi, bool LO>
 hipError_t launch_stream(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, int ks,
                          const SplitWs& ws, hipStream_t st) {
   const int kc = a.K / ks;
-  if (kc <= 512)
-    hipLaunchKernelGGL((stream_gemm<512, 6, LO, Epi>), dim3(kStreamGrid), dim3(kSW * 64), 0, st,
-                       a, ep, n_vcols, ks, kc, ws.part);
-  else
-    hipLaunchKernelGGL((stream_gemm<1024, 4, LO, Epi>), dim3(kStreamGrid), dim3(kSW * 64), 0, st,
-                       a, ep, n_vcols, ks, kc, ws.part);
+  hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, LO, Epi>), dim3(stream_grid(ks)),
+                     dim3(kSW * 64), 0, st, a, ep, n_vcols, ks, kc, ws.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  SplitK sk;
-  sk.ksplit = ks;
-  sk.steps = kc / 32;
-  sk.part = ws.part;
-  hipLaunchKernelGGL((skinny_finish<1, 2, Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, sk);
+  hipLaunchKernelGGL((stream_finish<Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, ks,
+                     ws.part);
   return hipGetLastError();
 }
 
 // true when launch_skinny takes the LDS-staged kernel for this shape
 bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
   if (!ws.part || !stream_plan(a.M, n_vcols, a.K, ks)) return false;
-  return (size_t)((n_vcols + 31) / 32) * ks * 512 <= ws.part_floats;
+  return (size_t)((n_vcols + 31) / 32) * 2 * ks * 256 <= ws.part_floats;
 }
 
 template <class Epi, bool LO = true>
@@ -859,7 +941,7 @@ int skinny_max_rows() { return 64; }
 size_t stream_part_floats(int n_vcols, int K) {
   int ks;
   if (!stream_plan(16, n_vcols, K, ks)) return 0;
-  return (size_t)((n_vcols + 31) / 32) * ks * 512;
+  return (size_t)((n_vcols + 31) / 32) * 2 * ks * 256;
 }
 
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
