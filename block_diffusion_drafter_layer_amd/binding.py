@@ -94,6 +94,7 @@ def _load():
         "dflash_profile_enable": (C.c_int, [P, C.c_uint32, I32]),
         "dflash_profile_read": (C.c_int, [P, I32, C.POINTER(I32), C.POINTER(F32), C.POINTER(I32)]),
         "dflash_stage_name": (C.c_char_p, [I32]),
+        "dflash_copy_bytes": (C.c_int, [P, P, SZ, P]),
         "dflash_status_str": (C.c_char_p, [C.c_int]),
         "dflash_last_error": (C.c_char_p, []),
     }
@@ -183,7 +184,11 @@ def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
 
 
 STAGES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down_proj", "lm_head",
-          "fuse_context", "inject_kv", "verify")
+          "fuse_context", "inject_kv", "verify", "lm_argmax")
+
+
+def dflash_copy_bytes(dst: int, src: int, nbytes: int, stream: int = 0):
+    return _check(_lib.dflash_copy_bytes(C.c_void_p(dst), C.c_void_p(src), nbytes, C.c_void_p(stream)))
 
 
 def dflash_profile_enable(h, stage_mask: int, max_records: int = 0):

@@ -132,9 +132,10 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
 }  // namespace
 
 enum Stage { ST_EMBED, ST_QKV, ST_ATTN, ST_OPROJ, ST_GATEUP, ST_DOWN, ST_LM, ST_FUSE, ST_INJECT,
-             ST_VERIFY, ST_COUNT };
+             ST_VERIFY, ST_LM_ARGMAX, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"embed", "qkv", "attention", "o_proj", "gate_up",
-                                     "down_proj", "lm_head", "fuse_context", "inject_kv", "verify"};
+                                     "down_proj", "lm_head", "fuse_context", "inject_kv", "verify",
+                                     "lm_argmax"};
 
 struct Profiler {
   uint32_t mask = 0;
@@ -187,6 +188,15 @@ static SplitWs split_ws(const dflash_handle* h) {
 }
 
 extern "C" {
+
+dflash_status dflash_copy_bytes(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!bytes) return DFLASH_OK;
+  if (!dst || !src) return fail(DFLASH_E_NULL, "copy: null pointer");
+  if (((uintptr_t)dst | (uintptr_t)src | bytes) & 15)
+    return fail(DFLASH_E_ALIGN, "copy: pointers and size must be multiples of 16 bytes");
+  hipError_t e = launch_copy_bytes(dst, src, bytes, (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "copy");
+}
 
 const char* dflash_stage_name(int32_t stage) {
   return stage >= 0 && stage < ST_COUNT ? kStageNames[stage] : "unknown";
@@ -469,18 +479,17 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* co
   L.split = split_ws(h);
   // split each sequence's keys so that the grid holds ~1024 waves (one per
   // SIMD) where the context allows, in whole 32-key chunks; each workgroup
-  // runs G query-head waves times 2 key columns when G <= 4
+  // runs G query-head waves, times 2 key columns when G <= 2
   const int pairs = n_seqs * c.n_kv_heads;
   const int G = c.n_heads / c.n_kv_heads;
-  const int WG_waves = G <= 4 ? 2 * G : G;
+  const int WG_waves = G <= 2 ? 2 * G : G;
   const int max_splits = std::max(1, std::min(kAttnMaxSplits, kAttnSlotCap / pairs));
+  // (the last split also takes the remainder, so the block's own keys do not
+  // add a nearly empty split)
   int splits = std::min(max_splits, std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves)));
   int kps = std::max(32, max_keys / splits / 32 * 32);
-  splits = (max_keys + kps - 1) / kps;
-  if (splits > max_splits) {
-    kps = (int)align_up((size_t)((max_keys + max_splits - 1) / max_splits), 32);
-    splits = (max_keys + kps - 1) / kps;
-  }
+  if (max_keys / kps > max_splits) kps = (int)align_up((size_t)((max_keys + max_splits - 1) / max_splits), 32);
+  splits = std::max(1, max_keys / kps);
   L.att_splits = splits; L.att_keys_per_split = kps;
 
   hipStream_t st = h->stream;
@@ -514,6 +523,10 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* co
   if (block_len > 1) {
     e = timed(h, ST_LM, [&] { return launch_lm(L, (const bf16_t*)h->w.lm_head, logits_out, st); });
     if (e != hipSuccess) return dev_fail(e, "lm_head");
+    e = timed(h, ST_LM_ARGMAX, [&] {
+      return launch_lm_argmax(L, (const bf16_t*)h->w.lm_head, logits_out, st);
+    });
+    if (e != hipSuccess) return dev_fail(e, "lm_argmax");
   }
   return DFLASH_OK;
 }

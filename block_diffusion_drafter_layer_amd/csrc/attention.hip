@@ -138,7 +138,7 @@ attn_split(AttnArgs p) {
   const SeqDesc sd = p.seqs.s[s];
   const int n_keys = sd.len + p.Bl;
   const int kb = split * p.kps;
-  const int ke = min(kb + p.kps, n_keys);
+  const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);  // last: the rest
   const size_t plane = (size_t)sd.cap * HD;
   const bf16_t* kbase = sd.kv + (size_t)((2 * p.layer) * p.Hkv + g) * plane;
   const bf16_t* vbase = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + g) * plane;
@@ -234,35 +234,49 @@ attn_split(AttnArgs p) {
 // One workgroup per (block row, query head, sequence), one thread per output
 // dim (at least one wave): every split's (m, l) goes through LDS and every
 // split's accumulator value is requested before any is used.
+// One workgroup per (block row, query head, sequence), one thread per output
+// dim (at least one wave). The (m, l) pairs go through LDS; the first
+// kMergeBatch accumulator values are requested before the barrier, from
+// clamped indices so that the loads are straight-line code (the weights of
+// indices past the last split are zero).
+constexpr int kMergeBatch = 32;
 template <int HD>
 __global__ void __launch_bounds__(HD < 64 ? 64 : HD)
 attn_merge(const float* __restrict__ acc, const float* __restrict__ ml, int Hq, int Bl,
            int splits, bf16_t* __restrict__ ob_h, bf16_t* __restrict__ ob_l) {
   constexpr int NT = HD < 64 ? 64 : HD;
+  constexpr int STRIDE = 16 * HD;  // floats between the splits of one (row, dim)
   const int r = blockIdx.x, a = blockIdx.y, s = blockIdx.z;
   const int d = threadIdx.x;
   __shared__ float sw[kAttnMaxSplits];
   __shared__ float sl[kAttnMaxSplits];
   const size_t slot0 = (size_t)(s * Hq + a) * splits;
+  const float* pb = acc + (slot0 * 16 + r) * HD + (d < HD ? d : HD - 1);
+  const int last = splits - 1;
+  float v[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k, last) * STRIDE];
   for (int k = threadIdx.x; k < splits; k += NT) {
     sw[k] = ml[((slot0 + k) * 16 + r) * 2];
     sl[k] = ml[((slot0 + k) * 16 + r) * 2 + 1];
   }
-  constexpr int BATCH = 16;
-  float v[BATCH];
-  float o = 0.f;
   __syncthreads();
   float M = -INFINITY;
   for (int k = 0; k < splits; ++k) M = fmaxf(M, sw[k]);
   float Lsum = 0.f;
   for (int k = 0; k < splits; ++k) Lsum += (sw[k] == -INFINITY ? 0.f : exp2f(sw[k] - M)) * sl[k];
-  for (int k0 = 0; k0 < splits; k0 += BATCH) {
+  float o = 0.f;
+  for (int k0 = 0; k0 < splits; k0 += kMergeBatch) {
+    if (k0) {
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-      v[k] = (k0 + k < splits && d < HD) ? acc[((slot0 + k0 + k) * 16 + r) * HD + d] : 0.f;
+      for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k0 + k, last) * STRIDE];
+    }
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k)
-      if (k0 + k < splits && sw[k0 + k] != -INFINITY) o += exp2f(sw[k0 + k] - M) * v[k];
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float m = sw[min(k0 + k, last)];
+      const float wgt = (k0 + k < splits && m != -INFINITY) ? exp2f(m - M) : 0.f;
+      o += wgt * v[k];
+    }
   }
   if (d < HD) {
     const size_t i = ((size_t)(s * Bl + r) * Hq + a) * HD + d;
@@ -280,14 +294,15 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   p.seqs = *L.seqs;
   const int G = L.Hq / L.Hkv;
   const dim3 grid(L.att_splits, L.Hkv, L.n_seqs);
-  // G query-head waves; groups of up to 4 heads also get two key columns
-  // (head_dim 128 in 512-thread groups keeps a single register stage: two
-  // stages would not fit the 256 registers a wave gets there)
+  // G query-head waves; groups of one or two heads also get two key columns.
+  // Up to 256 threads per workgroup keep two register stages (the next chunk
+  // in flight while one is processed); 512-thread groups of head_dim 128
+  // keep one, as two would not fit the 256 registers a wave gets there.
   constexpr bool P2 = HD < 128;
   switch (G) {
     case 1: hipLaunchKernelGGL((attn_split<HD, 1, 2, true>), grid, dim3(128), 0, st, p); break;
     case 2: hipLaunchKernelGGL((attn_split<HD, 2, 2, true>), grid, dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_split<HD, 4, 2, P2>), grid, dim3(512), 0, st, p); break;
+    case 4: hipLaunchKernelGGL((attn_split<HD, 4, 1, true>), grid, dim3(256), 0, st, p); break;
     case 8: hipLaunchKernelGGL((attn_split<HD, 8, 1, P2>), grid, dim3(512), 0, st, p); break;
     case 16: hipLaunchKernelGGL((attn_split<HD, 16, 1, false>), grid, dim3(1024), 0, st, p); break;
     default: return hipErrorInvalidValue;

@@ -66,6 +66,9 @@ hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* w
                          hipStream_t st);
 hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
                      hipStream_t st);
+// drafted tokens from the LM head's output (split sums, logits, argmax)
+hipError_t launch_lm_argmax(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
+                            hipStream_t st);
 
 // Context fusion: y = [f_0 .. f_{n-1}] W_c^T (bf16 into out), then RMSNorm.
 struct FuseLaunch {
@@ -113,5 +116,8 @@ struct VerifyLaunch {
 };
 hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
+
+// reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)
+hipError_t launch_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 }  // namespace dfl

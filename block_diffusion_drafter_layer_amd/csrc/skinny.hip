@@ -790,40 +790,6 @@ lm_argmax_reduce(const uint64_t* __restrict__ part, int n_tiles, int M_lm, int B
   }
 }
 
-// ---------------------------------------------------------------------------
-// launchers
-// ---------------------------------------------------------------------------
-
-namespace {
-constexpr int kNW = 8;
-
-// Column tiles per wave and the K split: few rows take wide tiles (the
-// activation fragments are reused across NCT weight tiles) and narrow
-// matrices split K so that the grid holds ~512-1024 workgroups.
-template <class Epi, bool LO, int MT, int NCT, int U>
-hipError_t launch_cfg(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const SplitWs& ws,
-                      hipStream_t st) {
-  constexpr int VC = 16 * NCT, ROWS = 16 * MT;
-  const int blocks = (n_vcols + VC - 1) / VC;
-  const int row_blocks = (a.M + ROWS - 1) / ROWS;
-  const int KS = a.K / 32;
-  int ks = 1;
-  if (row_blocks == 1 && ws.part)
-    while (blocks * ks * 2 <= kSplitTargetWG && KS / (ks * 2) >= 2 * kNW &&
-           (size_t)blocks * ks * 2 * ROWS * VC <= ws.part_floats)
-      ks *= 2;
-  SplitK sk;
-  sk.ksplit = ks;
-  sk.steps = (KS + ks - 1) / ks;
-  sk.part = ws.part;
-  hipLaunchKernelGGL((skinny_gemm<MT, NCT, kNW, U, LO, Epi>), dim3(blocks * ks, row_blocks),
-                     dim3(kNW * 64), 0, st, a, ep, n_vcols, sk);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ks == 1) return e;
-  hipLaunchKernelGGL((skinny_finish<MT, NCT, Epi>), dim3(blocks), dim3(256), 0, st, a, ep, sk);
-  return hipGetLastError();
-}
-
 // Sum of a 32-column pair's slice partials of the LDS-staged kernel, in slice
 // order, then the epilogue. The row norms' sums of squares are fetched
 // together with the partials.
@@ -864,6 +830,101 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
+}
+
+// LM-head finisher: 256 vocabulary columns per workgroup, one per thread.
+// Sums the slice partials (16-byte loads of four rows each), applies the
+// final RMSNorm row scale, optionally writes the logits, and reduces each
+// row's argmax key over the workgroup's columns into part[block][row].
+__global__ void __launch_bounds__(256)
+lm_stream_finish(SkinnyA a, EpiLM::P ep, int ks, const float* __restrict__ part) {
+  __shared__ float rs[16];
+  __shared__ uint64_t keys[16][256 + 1];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int col = blockIdx.x * 256 + t;
+  const int tile = col >> 4, n = col & 15;
+  // row scales: wave w sums rows 4w..4w+3 (16 lanes each)
+  const int srow = 4 * w + (lane >> 4);
+  float sq = 0.f;
+  if (a.ssq && srow < a.M) {
+    const float* q = a.ssq + (size_t)in_row(a, srow) * a.ssq_ld;
+    for (int g = lane & 15; g < a.ssq_ld; g += 16) sq += q[g];
+  }
+  const int tiles = (ep.V + 15) >> 4;
+  const int tl = tile < tiles ? tile : tiles - 1;
+  // element (row 4g + e, column n) of a tile sits at [lane 16g + n][e]
+  const float* src = part + (size_t)tl * ks * 256 + n * 4;
+  f32x4 z[4] = {};
+  for (int k0 = 0; k0 < ks; k0 += 4) {
+    f32x4 v[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        v[k][g] = k0 + k < ks ? *reinterpret_cast<const f32x4*>(src + (size_t)(k0 + k) * 256 + g * 64)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // slice order
+#pragma unroll
+      for (int g = 0; g < 4; ++g) z[g] += v[k][g];
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+  if ((lane & 15) == 0) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
+  __syncthreads();
+  const bool valid = col < ep.V;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const float zm = z[m >> 2][m & 3] * rs[m];
+    if (ep.logits && valid && m < a.M) ep.logits[(size_t)m * ep.V + col] = zm;
+    keys[m][t] = valid ? argmax_key(zm, (uint32_t)col) : 0;
+  }
+  __syncthreads();
+  // thread t: row t / 16 over columns 16 (t % 16) .. +15, then the 16 lanes
+  // of the row
+  {
+    const int m = t >> 4, j = t & 15;
+    uint64_t best = 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) best = umax64(best, keys[m][16 * j + c]);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) best = umax64(best, (uint64_t)__shfl_xor(best, o, kWave));
+    if (j == 0 && m < a.M) ep.part[(size_t)blockIdx.x * a.M + m] = best;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+namespace {
+constexpr int kNW = 8;
+
+// Column tiles per wave and the K split: few rows take wide tiles (the
+// activation fragments are reused across NCT weight tiles) and narrow
+// matrices split K so that the grid holds ~512-1024 workgroups.
+template <class Epi, bool LO, int MT, int NCT, int U>
+hipError_t launch_cfg(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const SplitWs& ws,
+                      hipStream_t st) {
+  constexpr int VC = 16 * NCT, ROWS = 16 * MT;
+  const int blocks = (n_vcols + VC - 1) / VC;
+  const int row_blocks = (a.M + ROWS - 1) / ROWS;
+  const int KS = a.K / 32;
+  int ks = 1;
+  if (row_blocks == 1 && ws.part)
+    while (blocks * ks * 2 <= kSplitTargetWG && KS / (ks * 2) >= 2 * kNW &&
+           (size_t)blocks * ks * 2 * ROWS * VC <= ws.part_floats)
+      ks *= 2;
+  SplitK sk;
+  sk.ksplit = ks;
+  sk.steps = (KS + ks - 1) / ks;
+  sk.part = ws.part;
+  hipLaunchKernelGGL((skinny_gemm<MT, NCT, kNW, U, LO, Epi>), dim3(blocks * ks, row_blocks),
+                     dim3(kNW * 64), 0, st, a, ep, n_vcols, sk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  hipLaunchKernelGGL((skinny_finish<MT, NCT, Epi>), dim3(blocks), dim3(256), 0, st, a, ep, sk);
+  return hipGetLastError();
 }
 
 // Split of K for the LDS-staged kernel: slices of whole ring slots and at
@@ -1002,39 +1063,60 @@ hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* w
   return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, L.split, st);
 }
 
+namespace {
+struct LmPlan {
+  SkinnyA a;
+  EpiLM::P p;
+  int M_lm;
+  bool stream;
+  int ks;   // K slices of the LDS-staged kernel
+  int vc;   // vocabulary columns per argmax key
+};
+
+LmPlan lm_plan(const DraftLaunch& L, const bf16_t* w_lm, float* logits) {
+  LmPlan q;
+  const int g = L.Bl - 1;
+  q.M_lm = L.n_seqs * g;
+  q.a = make_a(L.xh, L.xl, L.D, q.M_lm, L.D, L.ssq, L.D / 32, L.eps);
+  q.a.a_group = g; q.a.a_stride = L.Bl; q.a.a_off = 1;
+  q.p.w = w_lm; q.p.K = L.D; q.p.V = L.V; q.p.logits = logits; q.p.part = L.lm_part;
+  q.ks = 0;
+  q.stream = uses_stream(q.a, L.V, L.split, q.ks);
+  q.vc = q.stream ? 256 : q.M_lm <= 16 ? 128 : q.M_lm <= 32 ? 64 : 32;
+  return q;
+}
+}  // namespace
+
 hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
                      hipStream_t st) {
-  const int g = L.Bl - 1;
-  const int M_lm = L.n_seqs * g;
-  SkinnyA a = make_a(L.xh, L.xl, L.D, M_lm, L.D, L.ssq, L.D / 32, L.eps);
-  a.a_group = g; a.a_stride = L.Bl; a.a_off = 1;
-  EpiLM::P p;
-  p.w = w_lm; p.K = L.D; p.V = L.V; p.logits = logits; p.part = L.lm_part;
-  hipError_t e;
-  int vc, ks;
-  if (uses_stream(a, L.V, L.split, ks)) {
-    // LDS-staged kernel and finisher: one argmax key per 32 columns and row
-    e = launch_stream<EpiLM, true>(a, p, L.V, ks, L.split, st);
-    vc = 32;
-  } else if (M_lm <= 16) {
-    // the register-streaming kernel never splits the LM head's K (its vocab
-    // gives thousands of column blocks); one key per column block and row
-    const SplitWs none{};
-    e = launch_cfg<EpiLM, true, 1, 8, 2>(a, p, L.V, none, st);
-    vc = 128;
-  } else if (M_lm <= 32) {
-    const SplitWs none{};
-    e = launch_cfg<EpiLM, true, 2, 4, 2>(a, p, L.V, none, st);
-    vc = 64;
-  } else {
-    const SplitWs none{};
-    e = launch_cfg<EpiLM, true, 4, 2, 2>(a, p, L.V, none, st);
-    vc = 32;
+  const LmPlan q = lm_plan(L, w_lm, logits);
+  if (q.stream) {  // partial logits; the argmax launch finishes them
+    hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, true, EpiLM>),
+                       dim3(stream_grid(q.ks)), dim3(kSW * 64), 0, st, q.a, q.p, L.V, q.ks,
+                       L.D / q.ks, L.split.part);
+    return hipGetLastError();
   }
-  if (e != hipSuccess) return e;
-  const int tiles = (L.V + vc - 1) / vc;
-  hipLaunchKernelGGL(lm_argmax_reduce, dim3(M_lm), dim3(256), 0, st, L.lm_part,
-                     tiles, M_lm, L.Bl, L.block_out);
+  // the register-streaming kernel never splits the LM head's K (its vocab
+  // gives thousands of column blocks); its epilogue leaves one argmax key per
+  // column block and row
+  const SplitWs none{};
+  if (q.M_lm <= 16) return launch_cfg<EpiLM, true, 1, 8, 2>(q.a, q.p, L.V, none, st);
+  if (q.M_lm <= 32) return launch_cfg<EpiLM, true, 2, 4, 2>(q.a, q.p, L.V, none, st);
+  return launch_cfg<EpiLM, true, 4, 2, 2>(q.a, q.p, L.V, none, st);
+}
+
+hipError_t launch_lm_argmax(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
+                            hipStream_t st) {
+  const LmPlan q = lm_plan(L, w_lm, logits);
+  if (q.stream) {  // slice sums, row scale, logits, one key per 256 columns
+    hipLaunchKernelGGL(lm_stream_finish, dim3((L.V + q.vc - 1) / q.vc), dim3(256), 0, st, q.a, q.p,
+                       q.ks, L.split.part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int tiles = (L.V + q.vc - 1) / q.vc;
+  hipLaunchKernelGGL(lm_argmax_reduce, dim3(q.M_lm), dim3(256), 0, st, L.lm_part, tiles, q.M_lm,
+                     L.Bl, L.block_out);
   return hipGetLastError();
 }
 

@@ -244,8 +244,9 @@ dflash_status dflash_target_layer_ids(int32_t n_target_layers, int32_t n_feat,
 /*
  * Optional timing of the launches a handle makes (tracing). Stages:
  *   0 embed, 1 qkv, 2 attention (split + merge), 3 o_proj, 4 gate_up,
- *   5 down_proj, 6 lm_head (GEMM + argmax reduction), 7 fuse_context,
- *   8 inject_kv, 9 verify.
+ *   5 down_proj, 6 lm_head (the LM-head GEMM kernel alone), 7 fuse_context,
+ *   8 inject_kv, 9 verify, 10 lm_argmax (split sums, optional logits and the
+ *   argmax reduction that writes the drafted tokens).
  * With bit k of stage_mask set, every launch of stage k is bracketed by two
  * hipEvents recorded on the handle's stream, up to max_records launches
  * (later ones are not recorded). The events are host-side objects created
@@ -262,6 +263,18 @@ dflash_status dflash_profile_enable(dflash_handle* h, uint32_t stage_mask,
 dflash_status dflash_profile_read(dflash_handle* h, int32_t cap, int32_t* stage_out,
                                   float* ms_out, int32_t* n_out);
 const char* dflash_stage_name(int32_t stage);
+
+/*
+ * Measurement reference, not part of the drafting method: copy `bytes` from
+ * device memory src to device memory dst on `stream` (a hipStream_t, NULL =
+ * the default stream) with the access shape of the weight streams (16-byte
+ * vector loads and stores, a contiguous kilobyte per wave instruction).
+ * Byte counters read for this copy calibrate the traffic measured for the
+ * other kernels. Both pointers 16-byte aligned and bytes a multiple of 16,
+ * else DFLASH_E_ALIGN; null pointers with bytes > 0 give DFLASH_E_NULL. The
+ * buffers must not overlap. Nothing is allocated.
+ */
+dflash_status dflash_copy_bytes(void* dst, const void* src, size_t bytes, void* stream);
 
 const char* dflash_status_str(dflash_status s);
 const char* dflash_last_error(void);

@@ -160,3 +160,19 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_kv_trim, h, kv, 37) == 0
     assert kv.len == 37
     B.dflash_destroy(h)
+
+
+def test_stage_names_are_the_documented_ones():
+    assert tuple(B._lib.dflash_stage_name(i).decode() for i in range(len(B.STAGES))) == B.STAGES
+    assert B._lib.dflash_stage_name(len(B.STAGES)).decode() == "unknown"
+    assert B._lib.dflash_stage_name(-1).decode() == "unknown"
+
+
+def test_reference_copy_argument_checks():
+    # every case returns during host-side validation: no GPU work
+    # (status codes: 1 = DFLASH_E_NULL, 5 = DFLASH_E_ALIGN)
+    assert B._lib.dflash_copy_bytes(None, None, 0, None) == B.DFLASH_OK
+    assert B._lib.dflash_copy_bytes(None, C.c_void_p(256), 64, None) == 1
+    assert B._lib.dflash_copy_bytes(C.c_void_p(256), None, 64, None) == 1
+    assert B._lib.dflash_copy_bytes(C.c_void_p(264), C.c_void_p(256), 64, None) == 5
+    assert B._lib.dflash_copy_bytes(C.c_void_p(256), C.c_void_p(512), 72, None) == 5
