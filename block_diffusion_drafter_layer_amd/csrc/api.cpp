@@ -95,6 +95,7 @@ size_t split_floats(const dflash_config& c) {
 
 struct Layout {
   size_t split_part, x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
+  size_t gemm_part, gemm_ctr;   // context-GEMM split-K partials and counters (0 bytes if unused)
   size_t total;
 };
 
@@ -121,10 +122,14 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.att_acc = take((size_t)kAttnSlotCap * G * 16 * c.head_dim * 4);
   L.att_ml = take((size_t)kAttnSlotCap * G * 16 * 2 * 4);
   L.vpart = take(2 * Mmax * kVerifyMaxSplits * 16);
-  // per-row partial sums of y^2: 128-column tiles (tiled GEMM) or 32-column
+  // per-row partial sums of y^2: 256-column tiles (tiled GEMM) or 32-column
   // groups (streaming path for few rows)
-  L.fuse_ssq = take(std::max((size_t)max_tokens * ((D + kGemmTile - 1) / kGemmTile),
+  L.fuse_ssq = take(std::max((size_t)max_tokens * ((D + kFuseTileN - 1) / kFuseTileN),
                              (size_t)std::min(max_tokens, kContextRowsStreaming) * (D / 32)) * 4);
+  // the tiled context GEMMs run only for more rows than the streaming path takes
+  const bool tiled = max_tokens > kContextRowsStreaming;
+  L.gemm_part = take(tiled ? ctx_gemm_part_floats() * 4 : 0);
+  L.gemm_ctr = take(tiled ? (size_t)kGemmMaxCounters * 4 : 0);
   L.total = o;
   return L;
 }
@@ -185,6 +190,17 @@ static SplitWs split_ws(const dflash_handle* h) {
   w.part = (float*)(h->ws + h->lay.split_part);
   w.part_floats = split_floats(h->cfg);
   return w;
+}
+
+static GemmWs gemm_ws(const dflash_handle* h) {
+  GemmWs g{};
+  if (h->max_tokens > kContextRowsStreaming) {
+    g.part = (float*)(h->ws + h->lay.gemm_part);
+    g.part_floats = ctx_gemm_part_floats();
+    g.ctr = (int32_t*)(h->ws + h->lay.gemm_ctr);
+    g.n_ctr = kGemmMaxCounters;
+  }
+  return g;
 }
 
 extern "C" {
@@ -345,6 +361,12 @@ dflash_status dflash_set_workspace(dflash_handle* h, void* ws, size_t bytes, int
   const Layout L = make_layout(h->cfg, max_seqs, max_tokens);
   if (bytes < L.total)
     return fail(DFLASH_E_CAPACITY, "workspace of %zu bytes, %zu needed", bytes, L.total);
+  if (max_tokens > kContextRowsStreaming) {
+    // the split-K arrival counters start at zero; every launch leaves them so
+    hipError_t e = hipMemsetAsync((unsigned char*)ws + L.gemm_ctr, 0, (size_t)kGemmMaxCounters * 4,
+                                  h->stream);
+    if (e != hipSuccess) return dev_fail(e, "hipMemsetAsync");
+  }
   h->ws = (unsigned char*)ws;
   h->ws_bytes = bytes;
   h->max_seqs = max_seqs;
@@ -378,6 +400,7 @@ dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats, in
   F.out = (bf16_t*)ctx_out;
   F.ssq = (float*)(h->ws + h->lay.fuse_ssq);
   F.split = split_ws(h);
+  F.gemm = gemm_ws(h);
   const bool rows = n_tokens <= kContextRowsStreaming;
   hipError_t e = timed(h, ST_FUSE, [&] {
     return rows ? launch_fuse_rows(F, h->stream) : launch_fuse(F, h->stream);
@@ -418,6 +441,7 @@ dflash_status dflash_inject_kv(dflash_handle* h, dflash_kv* kv, const void* ctx_
   }
   I.kv = (bf16_t*)kv->base;
   I.split = split_ws(h);
+  I.gemm = gemm_ws(h);
   const bool rows = n_tokens <= kContextRowsStreaming;
   hipError_t e = timed(h, ST_INJECT, [&] {
     return rows ? launch_inject_rows(I, h->stream) : launch_inject(I, h->stream);

@@ -1,17 +1,34 @@
 // Dense context-side GEMMs on bf16 MFMA: C[m][n] = sum_k A[m][k] B[n][k] with
-// both operands K-contiguous. Output tiles of BM x 128 (BM = 256 or 128),
-// BK = 64, LDS double buffering, four waves in a 2x2 arrangement each owning
-// a (BM/2) x 64 block of 32x32x16 MFMA tiles: a 128x64 wave block reads
-// 6 KB of LDS per 262 kFLOP, which keeps the LDS under its bandwidth at full
-// MFMA rate. LDS rows are padded to 72 elements (144 bytes). The output tile
-// goes through LDS in 128-row halves for the epilogue.
+// both operands K-contiguous.
+//
+// Output tiles of 256 x BN (BN = 256 for the fusion, 320 for the injection),
+// eight waves (two per SIMD), each owning a block of 32x32x16 MFMA tiles:
+// 128 x 64 for BN = 256, 64 x 160 for BN = 320. Large tiles keep the global
+// load traffic at ~30 B/clk per CU at full MFMA rate, half of what the
+// CU's load path sustains (a 256 x 128 tile needs ~47 B/clk and is bound by
+// it). Operands go straight from global memory into LDS
+// (global_load_lds_dwordx4, no register staging) through a ring of 32-wide k
+// stages, 4 or 5 of them, so 3-4 stages are in flight while one is
+// multiplied. Each 1 KB load instruction covers sixteen 64-byte tile rows;
+// 16-byte chunk c of row r is stored at chunk c ^ ((r >> 2) & 3), so a
+// fragment read (sixteen consecutive lanes on sixteen rows, same chunk)
+// touches 64 distinct banks. Fragment reads for the next 16-wide k step are
+// issued before the MFMAs of the current one.
+//
+// Split K: when the tiles alone would leave CUs idle, S workgroups share a
+// tile, each over K/S. They sit on one XCD (workgroups go to XCDs round-robin
+// by id, and the S of a tile have ids 8 apart), so their partial sums meet in
+// that XCD's L2: each writes its partial, waits for the stores, and counts
+// itself in on the tile's counter; the last to arrive adds the others'
+// partials (read past the CU's L1) and runs the epilogue. Nobody waits for
+// anybody, so there is no co-residency requirement.
 //
 // A is read through a segmented loader so the fusion GEMM never materialises
-// the concatenation of the target layers (A3-dflash tutorial section 2.1.1:
+// the concatenation of the target layers (A3-dflash tutorial, section 2.1.1:
 // concat along the hidden axis): k in [j*D, (j+1)*D) reads layer j's array.
 //
-// Epilogues (the output tile is staged through LDS as fp32):
-//   fuse   - y as bf16 plus per-(row, 128-column tile) sums of y^2; a second
+// Epilogues run on 64-row slices of the fp32 tile staged through LDS:
+//   fuse   - y as bf16 plus per-(row, 256-column tile) sums of y^2; a second
 //            kernel applies RMSNorm and the gain (tutorial section 2.1.2);
 //   inject - every draft layer's K (RoPE at position pos0 + row) and V,
 //            written into the KV-cache layout (txtmix article section 5).
@@ -21,15 +38,35 @@
 namespace dfl {
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
-constexpr int kThreads = 256;
-}
+constexpr int BM = 256, BK = 32;
+constexpr int kRow = BK * 2;         // bytes per tile row and stage
+constexpr int kLds = 160 * 1024;
+constexpr int kSlice = 64;           // epilogue rows per LDS pass
+
+template <int BN>
+struct TileCfg;
+template <>
+struct TileCfg<256> {
+  static constexpr int W = 8, WGM = 2, NS = 5;  // waves, waves along M, ring stages
+};
+template <>
+struct TileCfg<320> {
+  static constexpr int W = 8, WGM = 4, NS = 4;
+};
+}  // namespace
 
 struct GemmA {
   const bf16_t* seg[kMaxFeat];
   int64_t ld;      // row stride of every segment (elements)
   int seg_k;       // k extent of one segment
   int M, K;
+};
+
+// split-K bookkeeping of one launch
+struct GemmSplit {
+  int S;           // workgroups per tile
+  float* part;     // [tile][S][BM * BN] fp32 partials in MFMA register order
+  int32_t* ctr;    // [tile] arrival counters, zero between launches
 };
 
 struct EpiFuse {
@@ -41,21 +78,64 @@ struct EpiFuse {
     int n_tiles;
   };
   __device__ static const bf16_t* wrow(const P& p, int n) { return p.w + (size_t)n * p.K; }
-  __device__ static void run(const P& p, float (*C)[BN + 1], int m0, int n0, int M) {
-    for (int e = threadIdx.x; e < BM * BN; e += kThreads) {
-      const int r = e / BN, c = e % BN;
+  // rows [m0, m0 + kSlice) of the tile starting at column n0, C[r][c] at C[r * ld + c]
+  template <int BN>
+  __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
+    // bf16 y, 8 columns (16 bytes) per thread-step where the row allows
+    for (int e = threadIdx.x; e < kSlice * (BN / 8); e += blockDim.x) {
+      const int r = e / (BN / 8), c = 8 * (e % (BN / 8));
       const int m = m0 + r, n = n0 + c;
-      if (m < M && n < p.N) p.out[(size_t)m * p.N + n] = f2bf(C[r][c]);
+      if (m >= M || n >= p.N) continue;
+      const float* y = C + r * ld + c;
+      if (n + 8 <= p.N && (p.N & 7) == 0) {
+        u32x4 o;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) o[h] = f2bf2(y[2 * h], y[2 * h + 1]);
+        *reinterpret_cast<u32x4*>(p.out + (size_t)m * p.N + n) = o;
+      } else {
+        for (int h = 0; h < 8 && n + h < p.N; ++h) p.out[(size_t)m * p.N + n + h] = f2bf(y[h]);
+      }
     }
-    for (int r = threadIdx.x; r < BM && n0 < p.N; r += kThreads) {
-      const int m = m0 + r;
-      if (m >= M) continue;
+    // per-row sum of squares over the tile's columns: 8 lanes per row
+    for (int e = threadIdx.x; e < kSlice * 8; e += blockDim.x) {
+      const int r = e >> 3, q = e & 7;
       float s = 0.f;
-      for (int c = 0; c < BN && n0 + c < p.N; ++c) s += C[r][c] * C[r][c];
-      p.ssq[(size_t)m * p.n_tiles + n0 / BN] = s;
+      for (int c = q; c < BN && n0 + c < p.N; c += 8) s += C[r * ld + c] * C[r * ld + c];
+      s += __shfl_xor(s, 1, kWave);
+      s += __shfl_xor(s, 2, kWave);
+      s += __shfl_xor(s, 4, kWave);
+      const int m = m0 + r;
+      if (q == 0 && m < M) p.ssq[(size_t)m * p.n_tiles + n0 / BN] = s;
     }
   }
 };
+
+// Virtual column order of the injection GEMM: per layer, the K columns then
+// the V columns; inside a K head, groups of PW = min(hd, 64) columns each
+// hold PW/2 RoPE pairs, virtual o and o + PW/2 being dims d and d + hd/2.
+// Tiles are multiples of 64 columns wide, so a pair never straddles two.
+struct InjectCol {
+  int layer, head, dim;
+  bool is_k;
+};
+__device__ __forceinline__ InjectCol inject_col(int vc, int Hkv, int hd) {
+  const int kvd = Hkv * hd;
+  InjectCol c;
+  c.layer = vc / (2 * kvd);
+  int r = vc - c.layer * 2 * kvd;
+  c.is_k = r < kvd;
+  if (!c.is_k) r -= kvd;
+  c.head = r / hd;
+  const int q = r - c.head * hd;
+  if (c.is_k) {
+    const int PW = hd < 64 ? hd : 64, hw = PW >> 1;
+    const int s = q / PW, o = q - s * PW;
+    c.dim = o < hw ? s * hw + o : (hd >> 1) + s * hw + (o - hw);
+  } else {
+    c.dim = q;
+  }
+  return c;
+}
 
 struct EpiInject {
   struct P {
@@ -67,41 +147,40 @@ struct EpiInject {
     bf16_t* kv;
   };
   __device__ static const bf16_t* wrow(const P& p, int n) {
-    const int kvd = p.Hkv * p.hd;
-    const int i = n / (2 * kvd), r = n % (2 * kvd);
-    return (r < kvd ? p.wk[i] + (size_t)r * p.K : p.wv[i] + (size_t)(r - kvd) * p.K);
+    const InjectCol c = inject_col(n, p.Hkv, p.hd);
+    return (c.is_k ? p.wk[c.layer] : p.wv[c.layer]) + (size_t)(c.head * p.hd + c.dim) * p.K;
   }
-  __device__ static void run(const P& p, float (*C)[BN + 1], int m0, int n0, int M) {
-    const int kvd = p.Hkv * p.hd, half = p.hd / 2;
+  template <int BN>
+  __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
     const size_t plane = (size_t)p.cap * p.hd;
-    // K columns: RoPE pairs (d, d + hd/2), consecutive threads along d
-    for (int e = threadIdx.x; e < BM * (BN / 2); e += kThreads) {
-      const int r = e / (BN / 2), cp = e % (BN / 2);
-      const int head_in_tile = cp / half, d = cp % half;
-      const int c = head_in_tile * p.hd + d;  // column of the pair's first half
-      const int n = n0 + c, m = m0 + r;
-      if (m >= M || n >= p.N || c + half >= BN) continue;
-      const int i = n / (2 * kvd), rr = n % (2 * kvd);
-      if (rr >= kvd) continue;  // V column
-      const int h = rr / p.hd;
-      const int pos = p.pos0 + m;
-      float cs, sn;
-      rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
-      const float x1 = C[r][c], x2 = C[r][c + half];
-      bf16_t* k = p.kv + (size_t)((2 * i) * p.Hkv + h) * plane + (size_t)pos * p.hd;
-      k[d] = f2bf(x1 * cs - x2 * sn);
-      k[d + half] = f2bf(x2 * cs + x1 * sn);
-    }
-    // V columns: dim-major plane, consecutive threads along positions
-    for (int e = threadIdx.x; e < BM * BN; e += kThreads) {
-      const int c = e / BM, r = e % BM;
-      const int n = n0 + c, m = m0 + r;
+    const int PW = p.hd < 64 ? p.hd : 64, hw = PW >> 1;
+    // pair slots: slot k covers virtual columns g*PW + o and g*PW + o + PW/2
+    // (g = k / hw, o = k % hw); K pairs get RoPE, V pairs are two plain
+    // columns. Consecutive threads take consecutive slots of one row.
+    for (int e = threadIdx.x; e < kSlice * (BN / 2); e += blockDim.x) {
+      const int r = e / (BN / 2), k = e % (BN / 2);
+      const int g = k / hw, o = k - g * hw;
+      const int c1 = g * PW + o, c2 = c1 + hw;
+      const int m = m0 + r, n = n0 + c1;
       if (m >= M || n >= p.N) continue;
-      const int i = n / (2 * kvd), rr = n % (2 * kvd);
-      if (rr < kvd) continue;
-      const int h = (rr - kvd) / p.hd, d = (rr - kvd) % p.hd;
-      bf16_t* v = p.kv + (size_t)((2 * i + 1) * p.Hkv + h) * plane;
-      v[(size_t)d * p.cap + p.pos0 + m] = f2bf(C[r][c]);
+      const InjectCol ci = inject_col(n, p.Hkv, p.hd);
+      const int pos = p.pos0 + m;
+      const float x1 = C[r * ld + c1], x2 = C[r * ld + c2];
+      if (ci.is_k) {
+        float cs, sn;
+        rope_cs(pos, ci.dim, p.hd, p.log2_theta, cs, sn);
+        bf16_t* kp = p.kv + (size_t)((2 * ci.layer) * p.Hkv + ci.head) * plane + (size_t)pos * p.hd;
+        kp[ci.dim] = f2bf(x1 * cs - x2 * sn);
+        kp[ci.dim + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
+      } else {
+        bf16_t* vp = p.kv + (size_t)((2 * ci.layer + 1) * p.Hkv + ci.head) * plane + pos;
+        vp[(size_t)ci.dim * p.cap] = f2bf(x1);
+        if (n0 + c2 < p.N) {
+          const InjectCol c2i = inject_col(n0 + c2, p.Hkv, p.hd);
+          bf16_t* vp2 = p.kv + (size_t)((2 * c2i.layer + 1) * p.Hkv + c2i.head) * plane + pos;
+          vp2[(size_t)c2i.dim * p.cap] = f2bf(x2);
+        }
+      }
     }
   }
 };
@@ -115,62 +194,180 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int TBM, class Epi>
-__global__ void __launch_bounds__(kThreads)
-gemm_tile(GemmA a, typename Epi::P p, int N) {
-  constexpr int WM = TBM / 2;          // rows per wave
-  constexpr int TI = WM / 32, TJ = 2;  // 32x32 tiles per wave
-  constexpr int ALD = TBM * BK / 8 / kThreads;  // 16-byte chunks per thread
-  constexpr int BLD = BN * BK / 8 / kThreads;
-  constexpr int STAGE = (TBM + BN) * LDK;        // bf16 elements per stage
-  static_assert(128 * (BN + 1) * 4 <= 2 * STAGE * 2, "epilogue half tile fits");
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * STAGE];
+// One 16-byte fragment read at addr + OFF, issued without waiting. Inline
+// assembly: the compiler's wait-count pass would otherwise treat it as
+// aliasing the direct loads in flight into the other stages and drain those
+// first. Reads are ordered among themselves (volatile) and complete in order.
+template <int OFF>
+__device__ __forceinline__ void ds_frag(u32x4& f, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "n"(OFF) : "memory");
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int m0 = blockIdx.y * TBM, n0 = blockIdx.x * BN;
-  const int KT = a.K / BK;
-  auto As = [&](int st, int r, int k) -> bf16_t* { return smem + st * STAGE + r * LDK + k; };
-  auto Bs = [&](int st, int r, int k) -> bf16_t* { return smem + st * STAGE + (TBM + r) * LDK + k; };
+// Wait until at most N LDS reads are outstanding; the fragments passed through
+// become usable only after this point.
+template <int N>
+__device__ __forceinline__ void frag_wait(u32x4 (&f)[6]) {
+  asm volatile("s_waitcnt lgkmcnt(%6)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5])
+               : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void frag_wait(u32x4 (&f)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6]), "+v"(f[7])
+               : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void frag_wait(u32x4 (&f)[7]) {
+  asm volatile("s_waitcnt lgkmcnt(%7)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
+                 "+v"(f[6])
+               : "n"(N));
+}
 
-  int arow[ALD], acol[ALD], brow_i[BLD], bcol[BLD];
-  int64_t aoff[ALD];
-  const bf16_t* bptr[BLD];
+// the TI A fragments (32-row blocks 2 KB apart) then the TJ B fragments
+template <int TI, int TJ>
+__device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint32_t b) {
+  ds_frag<0>(f[0], a);
+  ds_frag<2048>(f[1], a);
+  if constexpr (TI > 2) {
+    ds_frag<4096>(f[2], a);
+    ds_frag<6144>(f[3], a);
+  }
+  ds_frag<0>(f[TI], b);
+  ds_frag<2048>(f[TI + 1], b);
+  if constexpr (TJ > 2) {
+    ds_frag<4096>(f[TI + 2], b);
+    ds_frag<6144>(f[TI + 3], b);
+  }
+  if constexpr (TJ > 4) ds_frag<8192>(f[TI + 4], b);
+}
+
+// 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
+// wave-uniform).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// s_waitcnt immediate: vmcnt <= n with the other counters open
+#define DFL_VM(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0xF70)
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(DFL_VM(N)); }
+
+// wait until at most `stages` whole stages of this wave's loads (L each) are
+// in flight
+template <int L>
+__device__ __forceinline__ void wait_stages(int stages) {
+  switch (stages) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<L>(); break;
+    case 2: wait_vm<2 * L>(); break;
+    default: wait_vm<3 * L>(); break;
+  }
+}
+
+// Workgroup -> (tile, split). With a multiple of 8 tiles, XCD x (workgroup id
+// % 8) takes a contiguous chunk of tiles, walked in groups of 4 tile rows
+// column by column, so the workgroups an XCD runs share A row blocks and B
+// column blocks through its L2; the S splits of a tile are consecutive on
+// that XCD.
+__device__ __forceinline__ void tile_of(int id, int tm, int tn, int S, int& rt, int& ct, int& s) {
+  const int nt = tm * tn;
+  int t;
+  if ((nt & 7) == 0) {
+    const int local = id >> 3;
+    s = local % S;
+    t = (id & 7) * (nt >> 3) + local / S;
+  } else {
+    s = id % S;
+    t = id / S;
+  }
+  constexpr int GR = 4;
+  const int g = t / (GR * tn);
+  const int rows = min(GR, tm - g * GR);
+  const int i = t - g * GR * tn;
+  rt = g * GR + i % rows;
+  ct = i / rows;
+}
+
+template <int BN, class Epi>
+__global__ void __launch_bounds__(TileCfg<BN>::W * 64)
+ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
+  using Cfg = TileCfg<BN>;
+  constexpr int kWaves = Cfg::W;
+  constexpr int NS = Cfg::NS;
+  constexpr int WGM = Cfg::WGM, WGN = kWaves / WGM;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TI = WM / 32, TJ = WN / 32;
+  constexpr int kStage = (BM + BN) * kRow;
+  constexpr int kLoadsA = BM / 16 / kWaves;           // A loads per wave and stage
+  constexpr int kLoadsBTot = BN / 16;                 // B loads per stage
+  constexpr int kLoadsBMax = (kLoadsBTot + kWaves - 1) / kWaves;
+  static_assert(NS * kStage <= kLds, "ring fits in LDS");
+  static_assert(kSlice * (BN + 8) * 4 <= NS * kStage, "epilogue slice fits in the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w / WGN, wn = w % WGN;
+  const int tm = (a.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  int rt, ct, sidx;
+  tile_of(blockIdx.x, tm, tn, sp.S, rt, ct, sidx);
+  const int m0 = rt * BM, n0 = ct * BN;
+  const int KT_all = a.K / BK;
+  const int kt_per = (KT_all + sp.S - 1) / sp.S;
+  const int kt0 = sidx * kt_per;
+  const int KT = max(0, min(KT_all - kt0, kt_per));
+
+  // Loads: instruction b covers tile rows 16b .. 16b+15 (of A, then of B);
+  // wave w issues A instructions w, w + 8 and B instructions w, w + 8, ...
+  // Lane l fetches row 16b + l/4, chunk (l%4) ^ ((l/16) & 3), and lands at
+  // byte 16 l of the instruction's kilobyte.
+  const int lrow = lane >> 2;
+  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  const int nb = (kLoadsBTot % kWaves == 0 || w < kLoadsBTot % kWaves) ? kLoadsBMax : kLoadsBMax - 1;
+  int64_t aoff[kLoadsA];
+  const bf16_t* bptr[kLoadsBMax];
 #pragma unroll
-  for (int i = 0; i < ALD; ++i) {
-    const int c = tid + i * kThreads;
-    arow[i] = c >> 3;
-    acol[i] = (c & 7) * 8;
-    int m = m0 + arow[i];
+  for (int q = 0; q < kLoadsA; ++q) {
+    int m = m0 + 16 * (w + kWaves * q) + lrow;
     m = m < a.M ? m : a.M - 1;
-    aoff[i] = (int64_t)m * a.ld + acol[i];
+    aoff[q] = (int64_t)m * a.ld + lchunk;
   }
 #pragma unroll
-  for (int i = 0; i < BLD; ++i) {
-    const int c = tid + i * kThreads;
-    brow_i[i] = c >> 3;
-    bcol[i] = (c & 7) * 8;
-    int n = n0 + brow_i[i];
+  for (int q = 0; q < kLoadsBMax; ++q) {
+    int n = n0 + 16 * (w + kWaves * q) + lrow;
     n = n < N ? n : N - 1;
-    bptr[i] = Epi::wrow(p, n) + bcol[i];
+    bptr[q] = Epi::wrow(p, n) + lchunk;
   }
+  auto issue = [&](int kt) {
+    uint8_t* st = smem + (kt % NS) * kStage;
+    const int k0 = (kt0 + kt) * BK;
+    const int sg = k0 / a.seg_k;
+    const bf16_t* base = a.seg[sg] + (k0 - sg * a.seg_k);
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q) dma16(base + aoff[q], st + (w + kWaves * q) * 1024);
+#pragma unroll
+    for (int q = 0; q < kLoadsBMax; ++q)
+      if (q < nb) dma16(bptr[q] + k0, st + BM * kRow + (w + kWaves * q) * 1024);
+  };
+  auto wait_tiles = [&](int stages) {  // this wave's loads per stage differ by wave
+    if (nb == kLoadsBMax) wait_stages<kLoadsA + kLoadsBMax>(stages);
+    else wait_stages<kLoadsA + kLoadsBMax - 1>(stages);
+  };
 
-  u32x4 ra[ALD], rb[BLD];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    const int sgi = k0 / a.seg_k, kin = k0 - sgi * a.seg_k;
-    const bf16_t* base = a.seg[sgi] + kin;
+  // fragment addresses: lane l reads row l % 32 of a 32-row block at chunk
+  // (2 kk + l / 32) ^ ((l / 4) & 3), kk the 16-wide step within the stage
+  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
+  const int fr = lane & 31;
+  uint32_t foff[2];
 #pragma unroll
-    for (int i = 0; i < ALD; ++i) ra[i] = *reinterpret_cast<const u32x4*>(base + aoff[i]);
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bptr[i] + k0);
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < ALD; ++i) *reinterpret_cast<u32x4*>(As(st, arow[i], acol[i])) = ra[i];
-#pragma unroll
-    for (int i = 0; i < BLD; ++i) *reinterpret_cast<u32x4*>(Bs(st, brow_i[i], bcol[i])) = rb[i];
-  };
+  for (int kk = 0; kk < 2; ++kk)
+    foff[kk] = fr * kRow + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 4);
+  const uint32_t a_f = sbase + (uint32_t)(wm * WM) * kRow;
+  const uint32_t b_f = sbase + (uint32_t)(BM * kRow) + (uint32_t)(wn * WN) * kRow;
 
   f32x16 acc[TI][TJ];
 #pragma unroll
@@ -180,64 +377,154 @@ gemm_tile(GemmA a, typename Epi::P p, int N) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  const int lr = lane & 31, lk = 8 * (lane >> 5);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+  // Per stage t (ring slot t % NS): two 16-wide k steps; each issues the
+  // next step's fragment reads before its own MFMAs. The second step waits
+  // for this wave's loads of stage t+1 and meets the other waves at a
+  // barrier: past it, stage t+1 is in LDS and nobody reads slot (t-1) % NS
+  // any more, so stage t+NS-1 is loaded into it, and stage t+1's first
+  // fragments are read under the MFMAs of stage t's second step. (A plain
+  // barrier: a fence would also wait for the loads still in flight.)
+  if (KT > 0) {
+    const int pre = min(KT, NS - 1);
+    for (int t = 0; t < pre; ++t) issue(t);
+    wait_tiles(pre - 1);
+    __builtin_amdgcn_s_barrier();
+    u32x4 f[2][TI + TJ];
+    frag_issue<TI, TJ>(f[0], a_f + foff[0], b_f + foff[0]);
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint32_t st = (uint32_t)((kt % NS) * kStage);
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[TI], bfr[TJ];
+      for (int kk = 0; kk < 2; ++kk) {
+        if (kk == 0) {
+          frag_issue<TI, TJ>(f[1], a_f + st + foff[1], b_f + st + foff[1]);
+          frag_wait<TI + TJ>(f[0]);
+        } else {
+          frag_wait<0>(f[1]);
+          if (kt + 1 < KT) {
+            // stages issued so far: up to min(kt + NS - 2, KT - 1)
+            wait_tiles(min(NS - 3, KT - kt - 2));
+            __builtin_amdgcn_s_barrier();
+            if (kt + NS - 1 < KT) issue(kt + NS - 1);
+            const uint32_t sn = (uint32_t)(((kt + 1) % NS) * kStage);
+            frag_issue<TI, TJ>(f[0], a_f + sn + foff[0], b_f + sn + foff[0]);
+          }
+        }
+        // the MFMAs go out at raised priority, so that the other wave on the
+        // SIMD issues its reads and loads around them rather than the two
+        // waves' MFMA bursts queueing behind each other
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
-        af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As(cur, wm * WM + i * 32 + lr, ks * 16 + lk)));
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs(cur, wn * 64 + j * 32 + lr, ks * 16 + lk)));
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+          for (int j = 0; j < TJ; ++j)
+            acc[i][j] = mfma32x32x16(__builtin_bit_cast(bf16x8, f[kk][i]),
+                                     __builtin_bit_cast(bf16x8, f[kk][TI + j]), acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+        // keep this step's MFMAs ahead of the next step's reads and waits
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
   }
 
-  // epilogue in 128-row halves of the tile
-  float (*C)[BN + 1] = reinterpret_cast<float (*)[BN + 1]>(smem);
+  if (sp.S > 1) {
+    // publish this split's partial (lane-major: 1 KB per store instruction),
+    // then count in; the last to arrive sums every partial in split order
+    const int tile = rt * tn + ct;
+    float* mine = sp.part + ((size_t)tile * sp.S + sidx) * (BM * BN);
 #pragma unroll
-  for (int half = 0; half < TBM / 128; ++half) {
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(mine + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
+        }
+    __builtin_amdgcn_s_waitcnt(DFL_VM(0));  // the partial has reached L2
+    __syncthreads();  // (also: every wave is done with the ring)
+    int32_t* arrived = reinterpret_cast<int32_t*>(smem);
+    if (tid == 0)
+      *arrived = __hip_atomic_fetch_add(sp.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*arrived != sp.S - 1) return;
+    if (tid == 0) __hip_atomic_store(sp.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the other splits' partials are in this XCD's L2; drop any stale copy
+    // from this CU's L1 before reading them
+    asm volatile("buffer_inv sc0" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        f32x16 sum;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum[v] = 0.f;
+        for (int s = 0; s < sp.S; ++s) {
+          const float* src = sp.part + ((size_t)tile * sp.S + s) * (BM * BN);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(
+                src + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4);
+            sum[4 * q] += v[0];
+            sum[4 * q + 1] += v[1];
+            sum[4 * q + 2] += v[2];
+            sum[4 * q + 3] += v[3];
+          }
+        }
+        acc[i][j] = sum;
+      }
+  }
+
+  // epilogue: 64-row slices through LDS
+  constexpr int CLD = BN + 8;
+  float* C = reinterpret_cast<float*>(smem);
+  __syncthreads();  // every wave is done with the ring
+#pragma unroll
+  for (int sl = 0; sl < BM / kSlice; ++sl) {
 #pragma unroll
     for (int i = 0; i < TI; ++i) {
-      const int r0 = wm * WM + i * 32;  // tile row of this 32x32 block
-      if (r0 / 128 != half) continue;
+      const int r0 = wm * WM + i * 32;
+      if (r0 / kSlice != sl) continue;
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          C[r0 % 128 + 8 * (v / 4) + 4 * (lane >> 5) + (v & 3)][wn * 64 + j * 32 + lr] = acc[i][j][v];
+        for (int v = 0; v < 16; ++v) {
+          const int r = r0 % kSlice + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          C[r * CLD + wn * WN + j * 32 + fr] = acc[i][j][v];
+        }
     }
     __syncthreads();
-    Epi::run(p, C, m0 + half * 128, n0, a.M);
+    Epi::template run<BN>(p, C, CLD, m0 + sl * kSlice, n0, a.M);
     __syncthreads();
   }
 }
 
+// Split count: the smallest S in {1, 2, 4} that gives the grid at least 256
+// workgroups, when the tiles are a multiple of 8 (so the splits of a tile
+// share an XCD) and each split keeps at least 32 k stages.
+static int choose_split(int tiles, int K) {
+  if (tiles % 8) return 1;
+  int S = 1;
+  while (S < kGemmMaxSplit && tiles * S < 256 && K / BK / (2 * S) >= 32) S *= 2;
+  return S;
+}
 
-// 256-row tiles when the grid still fills the chip evenly, else 128-row tiles
-template <class Epi>
-static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, int M,
+template <int BN, class Epi>
+static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, const GemmWs& ws,
                                hipStream_t st) {
-  const int nb = (N + BN - 1) / BN;
-  const int t256 = nb * ((M + 255) / 256);
-  if (t256 >= 1024 || (t256 >= 256 && t256 % 256 == 0))
-    hipLaunchKernelGGL((gemm_tile<256, Epi>), dim3(nb, (M + 255) / 256), dim3(kThreads), 0, st, a, p, N);
-  else
-    hipLaunchKernelGGL((gemm_tile<128, Epi>), dim3(nb, (M + 127) / 128), dim3(kThreads), 0, st, a, p, N);
+  const int tiles = ((a.M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  GemmSplit sp;
+  sp.S = choose_split(tiles, a.K);
+  if (sp.S > 1 && (!ws.part || !ws.ctr || (size_t)tiles * sp.S * BM * BN > ws.part_floats ||
+                   tiles > ws.n_ctr))
+    sp.S = 1;
+  sp.part = ws.part;
+  sp.ctr = ws.ctr;
+  hipLaunchKernelGGL((ctx_gemm<BN, Epi>), dim3(tiles * sp.S), dim3(TileCfg<BN>::W * 64), 0, st, a, p,
+                     N, sp);
   return hipGetLastError();
 }
+
+size_t ctx_gemm_part_floats() { return (size_t)256 * BM * 320; }
 
 __global__ void __launch_bounds__(256)
 fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ ssq, int n_tiles, int D,
@@ -265,8 +552,8 @@ hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st) {
   a.ld = F.ld; a.seg_k = F.D; a.M = F.T; a.K = F.n_feat * F.D;
   EpiFuse::P p;
   p.w = F.w_c; p.K = a.K; p.N = F.D; p.out = F.out; p.ssq = F.ssq;
-  p.n_tiles = (F.D + BN - 1) / BN;
-  hipError_t e = launch_tiled<EpiFuse>(a, p, F.D, F.T, st);
+  p.n_tiles = (F.D + kFuseTileN - 1) / kFuseTileN;
+  hipError_t e = launch_tiled<kFuseTileN, EpiFuse>(a, p, F.D, F.gemm, st);
   if (e != hipSuccess) return e;
   return launch_fuse_normalize(F.out, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
 }
@@ -288,7 +575,8 @@ hipError_t launch_inject(const InjectLaunch& I, hipStream_t st) {
   }
   p.K = I.D; p.N = I.L * 2 * I.Hkv * I.hd; p.Hkv = I.Hkv; p.hd = I.hd; p.pos0 = I.pos0;
   p.cap = I.cap; p.log2_theta = I.log2_theta; p.kv = I.kv;
-  return launch_tiled<EpiInject>(a, p, p.N, I.T, st);
+  if (p.N % 320 == 0) return launch_tiled<320, EpiInject>(a, p, p.N, I.gemm, st);
+  return launch_tiled<256, EpiInject>(a, p, p.N, I.gemm, st);
 }
 
 }  // namespace dfl

@@ -15,7 +15,19 @@ constexpr int kMaxFeat = 8;
 constexpr int kAttnMaxSplits = 128;
 constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots
 constexpr int kVerifyMaxSplits = 64;
-constexpr int kGemmTile = 128;
+constexpr int kFuseTileN = 256;     // output columns per fusion GEMM tile
+constexpr int kGemmMaxSplit = 4;    // workgroups sharing one context-GEMM tile
+constexpr int kGemmMaxCounters = 1024;
+
+// Split-K scratch of the context GEMMs: fp32 partial tiles and the tiles'
+// arrival counters (zero between launches).
+struct GemmWs {
+  float* part;
+  size_t part_floats;
+  int32_t* ctr;
+  int n_ctr;
+};
+size_t ctx_gemm_part_floats();
 
 // Split-K scratch of the streaming GEMMs: fp32 partial tiles.
 constexpr int kSplitMaxWG = 1024;     // capacity: partial tiles of <= 32 x 64
@@ -80,8 +92,9 @@ struct FuseLaunch {
   const bf16_t* gain;
   float eps;
   bf16_t* out;        // [T][D]
-  float* ssq;         // [T][ceil(D/128)] (tiled) or [T][D/32] (few rows)
+  float* ssq;         // [T][ceil(D/256)] (tiled) or [T][D/32] (few rows)
   SplitWs split;
+  GemmWs gemm;
 };
 hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
@@ -97,6 +110,7 @@ struct InjectLaunch {
   const bf16_t* wv[kMaxLayers];
   bf16_t* kv;
   SplitWs split;
+  GemmWs gemm;
 };
 hipError_t launch_inject(const InjectLaunch& I, hipStream_t st);       // tiled MFMA GEMM
 hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st);  // few rows: streaming
