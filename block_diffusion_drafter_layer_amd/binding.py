@@ -90,6 +90,7 @@ def _load():
         "dflash_kv_trim": (C.c_int, [P, kvp, I32]),
         "dflash_draft_block": (C.c_int, [P, I32, C.POINTER(kvp), P, I32, P, P, P]),
         "dflash_verify": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
+        "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
         "dflash_target_layer_ids": (C.c_int, [I32, I32, C.POINTER(I32)]),
         "dflash_profile_enable": (C.c_int, [P, C.c_uint32, I32]),
         "dflash_profile_read": (C.c_int, [P, I32, C.POINTER(I32), C.POINTER(F32), C.POINTER(I32)]),
@@ -177,6 +178,13 @@ def dflash_verify(h, n_seqs: int, block_len: int, block_ids: int, target_logits:
                                      C.c_void_p(tau_out), C.c_void_p(bonus_out)))
 
 
+def dflash_sample_draft(h, n_seqs: int, block_len: int, draft_logits: int, temperature: float,
+                        seed: int, philox_offset: int, block_ids: int):
+    return _check(_lib.dflash_sample_draft(h, n_seqs, block_len, C.c_void_p(draft_logits),
+                                           float(temperature), seed, philox_offset,
+                                           C.c_void_p(block_ids)))
+
+
 def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
     out = (C.c_int32 * n_feat)()
     _check(_lib.dflash_target_layer_ids(n_target_layers, n_feat, out))
@@ -184,7 +192,7 @@ def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
 
 
 STAGES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down_proj", "lm_head",
-          "fuse_context", "inject_kv", "verify", "lm_argmax")
+          "fuse_context", "inject_kv", "verify", "lm_argmax", "sample_draft")
 
 
 def dflash_copy_bytes(dst: int, src: int, nbytes: int, stream: int = 0):

@@ -137,10 +137,10 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
 }  // namespace
 
 enum Stage { ST_EMBED, ST_QKV, ST_ATTN, ST_OPROJ, ST_GATEUP, ST_DOWN, ST_LM, ST_FUSE, ST_INJECT,
-             ST_VERIFY, ST_LM_ARGMAX, ST_COUNT };
+             ST_VERIFY, ST_LM_ARGMAX, ST_SAMPLE, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"embed", "qkv", "attention", "o_proj", "gate_up",
                                      "down_proj", "lm_head", "fuse_context", "inject_kv", "verify",
-                                     "lm_argmax"};
+                                     "lm_argmax", "sample_draft"};
 
 struct Profiler {
   uint32_t mask = 0;
@@ -588,6 +588,33 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
     return greedy ? launch_verify_greedy(P, h->stream) : launch_verify_pq(P, h->stream);
   });
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "verify");
+}
+
+dflash_status dflash_sample_draft(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  const float* draft_logits, float temperature, uint64_t seed,
+                                  uint64_t philox_offset, int32_t* block_ids) {
+  if (!h || !draft_logits || !block_ids)
+    return fail(DFLASH_E_NULL, "handle, draft_logits and block_ids are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "temperature must be finite and > 0 (use argmax drafting at 0)");
+  if (block_len == 1) return DFLASH_OK;  // nothing drafted
+  VerifyLaunch P{};
+  P.n_seqs = n_seqs; P.Bl = block_len - 1; P.V = c.vocab;
+  P.target = draft_logits; P.temperature = (double)temperature;
+  P.seed = seed; P.offset = philox_offset;
+  P.part = h->ws + h->lay.vpart;
+  const int rows = n_seqs * (block_len - 1);
+  P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
+  hipError_t e = timed(h, ST_SAMPLE, [&] {
+    return launch_sample_draft(P, block_ids, block_len, h->stream);
+  });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "sample_draft");
 }
 
 }  // extern "C"

@@ -130,6 +130,10 @@ struct VerifyLaunch {
 };
 hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
+// draft tokens sampled from softmax(rows / T): P.target = the draft logits,
+// P.n_seqs * P.Bl rows (P.Bl = drafted rows per sequence); writes
+// block[s * Bl + 1 + j]
+hipError_t launch_sample_draft(const VerifyLaunch& P, int32_t* block, int Bl, hipStream_t st);
 
 // reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)
 hipError_t launch_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t st);

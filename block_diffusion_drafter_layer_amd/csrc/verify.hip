@@ -14,6 +14,9 @@
 // fp64 over the vocab in index order. Uniforms come from Philox4x64-10
 // (Salmon et al., SC 2011) with key (seed, 0) and counter
 // (offset + row, sequence, purpose, 0).
+//
+// Sampling-mode drafting draws the block's tokens from the draft's own
+// distribution the same way (purpose 2), so that the p/q rule sees x ~ q.
 #include "common.h"
 #include "launch.h"
 
@@ -240,6 +243,81 @@ pq_accept_sample(VerifyLaunch P, const RowStat* part) {
     P.bonus[s] = P.V - 1;
     P.tau[s] = jr + 1;
   }
+}
+
+// ---------------------------------------------------------------------------
+// sampling-mode drafting: x_j ~ softmax(draft_logits[j] / T)
+// ---------------------------------------------------------------------------
+// One workgroup per drafted row: the row's slice statistics are merged, the
+// weights exp(x/T - m)/Z are summed per contiguous vocab chunk (one per
+// thread), the chunk totals are prefix-summed in thread order, and the
+// thread whose chunk brackets u * total finds the token by running its
+// chunk in vocab order. Here the launch's "target" rows are the draft rows
+// ([n_seqs * gamma] of them, P.Bl = gamma) and the output is the block.
+__global__ void __launch_bounds__(kPQThreads)
+draft_sample(VerifyLaunch P, const RowStat* part, int32_t* __restrict__ block, int Bl) {
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int gamma = P.Bl, s = row / gamma, j = row - s * gamma;
+  __shared__ double csum[kPQThreads];
+  __shared__ double stat_sh[3];
+  __shared__ int found;
+  if (tid == 0) {
+    const RowStat* p = part + (size_t)row * P.splits;
+    double M = -INFINITY;
+    for (int k = 0; k < P.splits; ++k) M = fmax(M, p[k].m);
+    double Z = 0.0;
+    for (int k = 0; k < P.splits; ++k)
+      if (p[k].m != -INFINITY) Z += p[k].z * exp(p[k].m - M);
+    stat_sh[0] = M;
+    stat_sh[1] = Z;
+    found = 0;
+  }
+  __syncthreads();
+  const double m = stat_sh[0], z = stat_sh[1];
+  const float* x = P.target + (size_t)row * P.V;
+  const int chunk = (P.V + kPQThreads - 1) / kPQThreads;
+  const int v0 = tid * chunk, v1 = min(v0 + chunk, P.V);
+  auto weight = [&](int v) -> double { return exp((double)x[v] / P.temperature - m) / z; };
+  double local = 0.0;
+  for (int v = v0; v < v1; ++v) local += weight(v);
+  csum[tid] = local;
+  __syncthreads();
+  if (tid == 0) {  // exclusive running sums of the chunk totals, in thread order
+    double run = 0.0;
+    for (int t = 0; t < kPQThreads; ++t) {
+      const double c = csum[t];
+      csum[t] = run;
+      run += c;
+    }
+    stat_sh[2] = run;
+  }
+  __syncthreads();
+  const double u = philox_uniform(P.seed, P.offset + j, s, 2);
+  const double target = u * stat_sh[2];
+  const double before = csum[tid];
+  int32_t* out = block + (size_t)s * Bl + 1 + j;
+  if (v0 < v1 && before <= target && target < before + local) {
+    double run = before;
+    int pick = v1 - 1;
+    for (int v = v0; v < v1; ++v) {
+      run += weight(v);
+      if (run > target) { pick = v; break; }
+    }
+    found = 1;
+    *out = pick;
+  }
+  __syncthreads();
+  if (tid == 0 && !found) *out = P.V - 1;  // target at or beyond the total: last index
+}
+
+hipError_t launch_sample_draft(const VerifyLaunch& P, int32_t* block, int Bl, hipStream_t st) {
+  RowStat* part = reinterpret_cast<RowStat*>(P.part);
+  const int rows = P.n_seqs * P.Bl;
+  hipLaunchKernelGGL(row_softmax_part, dim3(P.splits, rows), dim3(256), 0, st, P, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(draft_sample, dim3(rows), dim3(kPQThreads), 0, st, P, part, block, Bl);
+  return hipGetLastError();
 }
 
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st) {

@@ -99,6 +99,14 @@ class Drafter:
                              lg.data_ptr() if lg is not None else 0)
         return block_out, hid, lg
 
+    def sample_draft(self, block_ids: torch.Tensor, draft_logits: torch.Tensor, temperature: float,
+                     seed: int = 0, philox_offset: int = 0):
+        """Overwrite block_ids[:, 1:] with tokens sampled from the draft logits."""
+        n, bl = block_ids.shape
+        B.dflash_sample_draft(self.h, n, bl, draft_logits.data_ptr(), temperature, seed,
+                              philox_offset, block_ids.data_ptr())
+        return block_ids
+
     def verify(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
                draft_logits: Optional[torch.Tensor] = None, temperature: float = 0.0,
                seed: int = 0, philox_offset: int = 0, tau: Optional[torch.Tensor] = None,

@@ -208,6 +208,28 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs,
                                  float* logits_out);
 
 /*
+ * Sampling-mode drafting ([Code] section 6: away from greedy decoding the
+ * masked positions take tokens sampled from the draft's distribution; the
+ * p/q rule of dflash_verify needs x ~ q): for each sequence s and drafted row
+ * j < block_len-1, block_ids[s][j+1] becomes the token drawn from
+ * q = softmax(draft_logits[s][j] / temperature) (fp64) as the smallest v whose
+ * running sum in vocab order exceeds u * total, with u the Philox4x64-10
+ * uniform of counter (philox_offset + j, s, 2, 0), key (seed, 0),
+ * u = (word0 >> 11) * 2^-53.
+ * draft_logits: device fp32 [n_seqs, block_len-1, vocab] (dflash_draft_block's
+ *               logits_out);
+ * block_ids:    device int32 [n_seqs, block_len]; column 0 (the anchor) is
+ *               left as it is.
+ * temperature > 0 (finite); 1 <= n_seqs <= max_seqs; 1 <= block_len <=
+ * block_size (block_len == 1: nothing to do). Errors as for the other calls:
+ * checked on the host before any launch, nothing written on error.
+ */
+dflash_status dflash_sample_draft(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  const float* draft_logits, float temperature,
+                                  uint64_t seed, uint64_t philox_offset,
+                                  int32_t* block_ids);
+
+/*
  * Verification of n_seqs drafted blocks against the target's logits.
  * temperature == 0: greedy ([Code] section 8): posterior = argmax of each
  *   target row (lowest index on ties); accepted a = length of the prefix with

@@ -117,6 +117,7 @@ def test_calls_before_workspace_and_workspace_checks():
     kv = B.dflash_kv(FAKE, 2048, 100)
     assert _status(B.dflash_draft_block, h, [kv], FAKE, 16, FAKE) == 7
     assert _status(B.dflash_fuse_context, h, [FAKE] * 5, c.hidden, 10, FAKE) == 7
+    assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, 1.0, 0, 0, FAKE) == 7
     need = B.dflash_workspace_bytes(c, 2, 64)
     assert _status(B.dflash_set_workspace, h, FAKE, need - 1, 2, 64) == 4
     assert _status(B.dflash_set_workspace, h, FAKE + 16, need, 2, 64) == 5
@@ -154,6 +155,14 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE, 0, 1.0, 0, 0, FAKE, FAKE) == 1
     assert _status(B.dflash_verify, h, 3, 16, FAKE, FAKE, 0, 0.0, 0, 0, FAKE, FAKE) == 3
     assert _status(B.dflash_verify, h, 1, 16, FAKE, FAKE + 4, 0, 0.0, 0, 0, FAKE, FAKE) == 5
+    # sample_draft: temperature, shapes, pointers; block_len 1 draws nothing
+    assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, 0.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, float("nan"), 0, 0, FAKE) == 3
+    assert _status(B.dflash_sample_draft, h, 3, 16, FAKE, 1.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_sample_draft, h, 1, 17, FAKE, 1.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_sample_draft, h, 1, 16, 0, 1.0, 0, 0, FAKE) == 1
+    assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, 1.0, 0, 0, 0) == 1
+    assert _status(B.dflash_sample_draft, h, 1, 1, FAKE, 1.0, 0, 0, FAKE) == 0
     # trim is host metadata only
     assert _status(B.dflash_kv_trim, h, kv, 101) == 3
     assert kv.len == 100

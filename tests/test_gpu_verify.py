@@ -1,4 +1,5 @@
-"""GPU parity of verification (greedy and p/q) against the oracle.
+"""GPU parity of verification (greedy and p/q) and of sampling-mode drafting
+against the oracle.
 
 tau and bonus must be bit-exact; for p/q, rows whose accept test has
 |p/q - u| < 1e-4 or whose final draw lies within 1e-12 (relative) of a CDF
@@ -97,3 +98,75 @@ def test_pq_matches_oracle(ci, bl, temp):
             assert (tau[s], bonus[s]) == (t, b), (trial, s, diag)
             checked += 1
     assert checked >= 12
+
+
+def _sampled_rows_match(got, logits, temp, seed, off, n_seqs, bl):
+    """Compare sampled block columns 1.. with the oracle's draws; rows whose draw
+    lies within 1e-12 of a CDF boundary are skipped. Returns rows compared."""
+    checked = 0
+    for s in range(n_seqs):
+        x, margin = O.sample_draft_tokens(logits[s], temp, seed, off, s)
+        for j in range(bl - 1):
+            if margin[j] < 1e-12:
+                continue
+            assert int(got[s, 1 + j]) == int(x[j]), (s, j, margin[j])
+            checked += 1
+    return checked
+
+
+@pytest.mark.parametrize("ci,n_seqs,bl,temp", [(0, 2, 4, 1.0), (0, 1, 4, 0.5), (4, 2, 8, 1.0),
+                                               (1, 1, 16, 1.0), (1, 3, 5, 2.0)])
+def test_sample_draft_matches_oracle(ci, n_seqs, bl, temp):
+    dc = CONFIGS[ci]
+    say(f"sample_draft: config {dc.name} n_seqs={n_seqs} block_len={bl} temperature={temp}")
+    d, _ = make(dc, max_seqs=n_seqs)
+    checked = 0
+    for trial in range(3):
+        g = torch.Generator().manual_seed(500 + 17 * trial + ci)
+        lg = torch.randn(n_seqs, bl - 1, dc.vocab, generator=g) * (1.0 + trial)
+        anchors = torch.arange(n_seqs, dtype=torch.int32) * 7 + 1
+        blk = torch.full((n_seqs, bl), -1, dtype=torch.int32)
+        blk[:, 0] = anchors
+        blk = blk.to(DEV)
+        seed, off = 3 + trial, 5 * trial
+        d.sample_draft(blk, lg.to(DEV), temp, seed=seed, philox_offset=off)
+        got = blk.cpu().numpy()
+        assert (got[:, 0] == anchors.numpy()).all()
+        assert ((got[:, 1:] >= 0) & (got[:, 1:] < dc.vocab)).all()
+        checked += _sampled_rows_match(got, lg.numpy(), temp, seed, off, n_seqs, bl)
+    assert checked >= 3 * n_seqs * (bl - 1) - 2
+
+
+def test_sampling_round_from_draft_logits():
+    """A whole sampling-mode round at the tiny shape: draft forward with logits,
+    tokens sampled from them, p/q verification against target logits; the
+    oracle takes the same logits and uniforms at every step."""
+    from gpu_helpers import fill_context
+    dc = CONFIGS[0]
+    d, w = make(dc, max_seqs=2)
+    g = torch.Generator().manual_seed(77)
+    kvs = []
+    for s in range(2):
+        kv = d.new_kv(64)
+        fill_context(kv, [(torch.randn(10 + s, dc.n_kv_heads, dc.head_dim, generator=g).to(torch.bfloat16).to(DEV),
+                           torch.randn(10 + s, dc.n_kv_heads, dc.head_dim, generator=g).to(torch.bfloat16).to(DEV))
+                          for _ in range(dc.n_layers)])
+        kvs.append(kv)
+    anchors = torch.tensor([5, 9], dtype=torch.int32, device=DEV)
+    temp, seed = 1.0, 21
+    checked = 0
+    for rnd in range(4):
+        blk, _, dl = d.draft_block(kvs, anchors, logits=True)
+        d.sample_draft(blk, dl, temp, seed=seed, philox_offset=4 * rnd)
+        tl = torch.randn(2, dc.block_size, dc.vocab, generator=g)
+        tau, bonus = d.verify(blk, tl.to(DEV), dl, temperature=temp, seed=seed, philox_offset=4 * rnd)
+        got, dln = blk.cpu().numpy(), dl.cpu().numpy()
+        n = _sampled_rows_match(got, dln, temp, seed, 4 * rnd, 2, dc.block_size)
+        for s in range(2):
+            t, b, diag = O.verify_pq(got[s], tl[s].numpy(), dln[s], temp, seed, 4 * rnd, s)
+            if min(diag["ratio_margin"] or [1.0]) < 1e-4 or diag["cdf_margin"] < 1e-12:
+                continue
+            assert (int(tau[s]), int(bonus[s])) == (t, b), (rnd, s, diag)
+            checked += 1
+        checked += n
+    assert checked >= 20
