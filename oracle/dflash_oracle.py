@@ -21,7 +21,11 @@ Readings taken where the pages are silent (also listed in the design notes):
   * RoPE is rotate-half over pairs (d, d + hd/2), inv_freq_d = theta^(-2d/hd);
   * GQA: query head a reads kv head a // (Hq/Hkv);
   * argmax ties go to the lowest index (numpy.argmax / torch.argmax rule);
-  * Philox4x64-10 counter layout and the inverse-CDF sampler of verify_pq.
+  * Philox4x64-10 counter layout and the inverse-CDF sampler of verify_pq;
+  * a cache built with bf16_kv=True stores its K/V rows, and the block's own
+    K/V rows, rounded to bf16: [Code] section 5 sizes the model's weights and
+    activations at two bytes each (BF16). With bf16_kv=False (the default)
+    every row is kept in fp64.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
@@ -44,6 +48,16 @@ def target_layer_ids(n_target_layers: int, n_feat: int) -> List[int]:
     lo, hi = 1.0, float(n_target_layers - 3)
     step = (hi - lo) / (n_feat - 1)
     return [int(np.floor(lo + i * step + 0.5)) for i in range(n_feat)]
+
+
+def round_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even (the top 16 bits of
+    the IEEE binary32 pattern after adding 0x7FFF plus the lowest kept bit).
+    Inputs are first rounded to binary32; finite values only."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(F64)
 
 
 def rms_norm(x, gain, eps):
@@ -146,10 +160,13 @@ class DraftCache:
     in the draft model's KV cache and reused across drafting rounds; [Code]
     section 9: after verification the cache is cropped back to the accepted
     prefix. Rows at positions >= len are not part of the cache.
+
+    bf16_kv: rows are rounded to bf16 when stored (see store()).
     """
     n_layers: int
     k: List[np.ndarray] = field(default_factory=list)
     v: List[np.ndarray] = field(default_factory=list)
+    bf16_kv: bool = False
 
     def __post_init__(self):
         if not self.k:
@@ -168,8 +185,13 @@ class DraftCache:
                 self.k[i] = self.k[i][:keep]
                 self.v[i] = self.v[i][:keep]
 
+    def store(self, x):
+        """The value a row holds once written to this cache."""
+        return round_bf16(x) if self.bf16_kv else np.asarray(x, F64)
+
     def append(self, layer: int, k, v, pos0: int):
         """Write rows at positions pos0.. after dropping everything >= pos0."""
+        k, v = self.store(k), self.store(v)
         if self.k[layer] is None:
             if pos0 != 0:
                 raise ValueError("first append must start at position 0")
@@ -229,7 +251,8 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
     target's, shared and frozen).
 
     caches[s] holds sequence s's context K/V; its length S_s is the anchor's
-    position. Returns a dict with
+    position. The block's own K/V rows take the precision the cache stores
+    rows in (DraftCache.store). Returns a dict with
       draft  [n_seq, block_len-1] int   argmax tokens of rows 1..block_len-1
       hidden [L, n_seq, block_len, D]   residual stream after each layer
       logits [n_seq, block_len-1, V]
@@ -256,7 +279,8 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
             kb = linear(h, lw["wk"]).reshape(B, Hkv, hd)
             vb = linear(h, lw["wv"]).reshape(B, Hkv, hd)
             q = apply_rope(q, pos, theta)
-            kb = apply_rope(kb, pos, theta)
+            kb = caches[s].store(apply_rope(kb, pos, theta))
+            vb = caches[s].store(vb)
             if S > 0:
                 k_all = np.concatenate([caches[s].k[i], kb])
                 v_all = np.concatenate([caches[s].v[i], vb])

@@ -34,7 +34,7 @@ def _torch_rope(x, pos, theta):
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def _torch_forward(cfg, w, ctx_k, ctx_v, anchor, S):
+def _torch_forward(cfg, w, ctx_k, ctx_v, anchor, S, bf16_block=False):
     t = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.float64)  # noqa: E731
     B, Hq, Hkv, hd = cfg.block_size, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
     ids = torch.tensor([anchor] + [cfg.mask_token_id] * (B - 1))
@@ -46,6 +46,9 @@ def _torch_forward(cfg, w, ctx_k, ctx_v, anchor, S):
         q = _torch_rope((h @ t(lw["wq"]).T).view(B, Hq, hd), pos, cfg.rope_theta)
         kb = _torch_rope((h @ t(lw["wk"]).T).view(B, Hkv, hd), pos, cfg.rope_theta)
         vb = (h @ t(lw["wv"]).T).view(B, Hkv, hd)
+        if bf16_block:  # the block's rows as a bf16 cache holds them
+            kb = kb.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+            vb = vb.to(torch.float32).to(torch.bfloat16).to(torch.float64)
         k = torch.cat([t(ctx_k[i]), kb]) if S else kb
         v = torch.cat([t(ctx_v[i]), vb]) if S else vb
         G = Hq // Hkv
@@ -93,6 +96,21 @@ def test_forward_reduced_qwen_shape():
     hs, logits, draft = _torch_forward(cfg, w, ck, cv, 5, 19)
     np.testing.assert_allclose(out["hidden"][:, 0], hs, rtol=1e-10, atol=1e-12)
     np.testing.assert_array_equal(out["draft"][0], draft)
+
+
+def test_bf16_cache_rounds_the_block_rows():
+    # with a bf16 cache the block's own K/V rows enter attention as bf16
+    # values; the composition rounds them with torch's conversion
+    cfg = CONFIGS[0].shrink(n_layers=2)
+    w, ck, cv, _ = _setup(cfg, 10)
+    anchor = int(synth.make_anchor(cfg)[0])
+    cache = O.DraftCache(cfg.n_layers, k=ck, v=cv, bf16_kv=True)
+    out = O.draft_block(cfg, w, [cache], [anchor])
+    hs, logits, _ = _torch_forward(cfg, w, ck, cv, anchor, 10, bf16_block=True)
+    np.testing.assert_allclose(out["hidden"][:, 0], hs, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(out["logits"][0], logits, rtol=1e-10, atol=1e-10)
+    plain = O.draft_block(cfg, w, [O.DraftCache(cfg.n_layers, k=ck, v=cv)], [anchor])
+    assert np.abs(plain["hidden"] - out["hidden"]).max() > 1e-6
 
 
 def test_argmax_ties_take_lowest_index():

@@ -3,6 +3,7 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle as O
 from synth import CONFIGS
@@ -125,3 +126,33 @@ def test_trim_then_append_rounds():
     np.testing.assert_allclose(c.v[0], ref.v[0], atol=1e-14)
     with pytest.raises(ValueError):
         c.trim(S + 1)
+
+
+def test_round_bf16_matches_library_conversion():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(50000) * 10.0 ** rng.uniform(-30, 30, 50000)
+    # exact ties: the 16 dropped bits are 0x8000, upper halves odd and even
+    hi = rng.integers(0x0080, 0x7F00, 20000, dtype=np.uint32)
+    ties = ((hi << 16) | 0x8000).view(np.float32).astype(np.float64)
+    ties = np.concatenate([ties, -ties, [0.0, -0.0, 1.0]])
+    for v in (x, ties):
+        ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(O.round_bf16(v), ref)
+
+
+def test_bf16_cache_stores_rounded_rows():
+    cfg = CONFIGS[0].shrink(n_layers=2)
+    rng = np.random.default_rng(13)
+    layers = _tiny_layers(cfg, rng)
+    ctx = rng.standard_normal((9, cfg.hidden))
+    exact = O.DraftCache(cfg.n_layers)
+    O.cache_inject(exact, ctx, layers, cfg, 0)
+    low = O.DraftCache(cfg.n_layers, bf16_kv=True)
+    O.cache_inject(low, ctx[:4], layers, cfg, 0)
+    O.cache_inject(low, ctx[4:], layers, cfg, 4)
+    for i in range(cfg.n_layers):
+        kk = torch.from_numpy(exact.k[i].astype(np.float32)).to(torch.bfloat16).double().numpy()
+        vv = torch.from_numpy(exact.v[i].astype(np.float32)).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(low.k[i], kk)
+        np.testing.assert_array_equal(low.v[i], vv)
+        assert not np.array_equal(low.k[i], exact.k[i])
