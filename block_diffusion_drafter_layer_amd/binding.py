@@ -91,6 +91,9 @@ def _load():
         "dflash_draft_block": (C.c_int, [P, I32, C.POINTER(kvp), P, I32, P, P, P]),
         "dflash_verify": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
         "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
+        "dflash_draft_block_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, I32, P, P, P]),
+        "dflash_append_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, C.POINTER(P), I64, I32]),
+        "dflash_kv_trim_dev": (C.c_int, [P, I32, P, I32]),
         "dflash_target_layer_ids": (C.c_int, [I32, I32, C.POINTER(I32)]),
         "dflash_profile_enable": (C.c_int, [P, C.c_uint32, I32]),
         "dflash_profile_read": (C.c_int, [P, I32, C.POINTER(I32), C.POINTER(F32), C.POINTER(I32)]),
@@ -176,6 +179,27 @@ def dflash_verify(h, n_seqs: int, block_len: int, block_ids: int, target_logits:
                                      C.c_void_p(target_logits), C.c_void_p(draft_logits or None),
                                      float(temperature), seed, philox_offset,
                                      C.c_void_p(tau_out), C.c_void_p(bonus_out)))
+
+
+def dflash_draft_block_dev(h, kvs: Sequence[dflash_kv], len_dev: int, anchor_ids: int,
+                           block_len: int, block_out: int, hidden_out: int = 0, logits_out: int = 0):
+    arr = (C.POINTER(dflash_kv) * len(kvs))(*[C.pointer(k) for k in kvs])
+    return _check(_lib.dflash_draft_block_dev(h, len(kvs), arr, C.c_void_p(len_dev),
+                                              C.c_void_p(anchor_ids), block_len,
+                                              C.c_void_p(block_out), C.c_void_p(hidden_out or None),
+                                              C.c_void_p(logits_out or None)))
+
+
+def dflash_append_dev(h, kvs: Sequence[dflash_kv], len_dev: int, tau_dev: int,
+                      feats: Sequence[int], ld: int, rows_per_seq: int):
+    arr = (C.POINTER(dflash_kv) * len(kvs))(*[C.pointer(k) for k in kvs])
+    fa = (C.c_void_p * len(feats))(*feats)
+    return _check(_lib.dflash_append_dev(h, len(kvs), arr, C.c_void_p(len_dev), C.c_void_p(tau_dev),
+                                         fa, ld, rows_per_seq))
+
+
+def dflash_kv_trim_dev(h, n_seqs: int, len_dev: int, keep_len: int):
+    return _check(_lib.dflash_kv_trim_dev(h, n_seqs, C.c_void_p(len_dev), keep_len))
 
 
 def dflash_sample_draft(h, n_seqs: int, block_len: int, draft_logits: int, temperature: float,

@@ -15,7 +15,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 
-SOURCES = ["api.cpp", "skinny.hip", "attention.hip", "gemm.hip", "verify.hip", "calibrate.hip"]
+SOURCES = ["api.cpp", "skinny.hip", "attention.hip", "gemm.hip", "verify.hip", "rounds.hip",
+           "calibrate.hip"]
 HEADERS = ["common.h", "launch.h"]
 
 FLAGS = [

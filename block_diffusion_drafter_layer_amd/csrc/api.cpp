@@ -96,6 +96,8 @@ size_t split_floats(const dflash_config& c) {
 struct Layout {
   size_t split_part, x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
   size_t gemm_part, gemm_ctr;   // context-GEMM split-K partials and counters (0 bytes if unused)
+  size_t app_ctx;               // fused rows of a device-resident append
+  size_t fuse_y;                // fp32 projection of the fused rows before the norm
   size_t total;
 };
 
@@ -130,6 +132,8 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   const bool tiled = max_tokens > kContextRowsStreaming;
   L.gemm_part = take(tiled ? ctx_gemm_part_floats() * 4 : 0);
   L.gemm_ctr = take(tiled ? (size_t)kGemmMaxCounters * 4 : 0);
+  L.app_ctx = take(std::min((size_t)max_tokens, Mmax) * D * 2);
+  L.fuse_y = take((size_t)max_tokens * D * 4);
   L.total = o;
   return L;
 }
@@ -399,6 +403,7 @@ dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats, in
   F.eps = c.rms_eps;
   F.out = (bf16_t*)ctx_out;
   F.ssq = (float*)(h->ws + h->lay.fuse_ssq);
+  F.y = (float*)(h->ws + h->lay.fuse_y);
   F.split = split_ws(h);
   F.gemm = gemm_ws(h);
   const bool rows = n_tokens <= kContextRowsStreaming;
@@ -461,9 +466,15 @@ dflash_status dflash_kv_trim(dflash_handle* h, dflash_kv* kv, int32_t keep_len) 
   return DFLASH_OK;
 }
 
-dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
-                                 const int32_t* anchor_ids, int32_t block_len, int32_t* block_out,
-                                 float* hidden_out, float* logits_out) {
+}  // extern "C"
+
+// The draft forward; len_dev == NULL: the host lengths kvs[s]->len, else the
+// device lengths len_dev[s] (attention is then planned for the buffers' full
+// capacity, the kernels skip key ranges past the actual length).
+static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                const int32_t* len_dev, const int32_t* anchor_ids,
+                                int32_t block_len, int32_t* block_out, float* hidden_out,
+                                float* logits_out) {
   if (!h || !kvs || !anchor_ids || !block_out)
     return fail(DFLASH_E_NULL, "handle, kvs, anchor_ids and block_out are required");
   if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
@@ -482,8 +493,10 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* co
     seqs.s[s].kv = (bf16_t*)kvs[s]->base;
     seqs.s[s].cap = row_capacity(c, kvs[s]->max_ctx);
     seqs.s[s].len = kvs[s]->len;
-    max_keys = std::max(max_keys, kvs[s]->len + block_len);
+    seqs.s[s].max_ctx = kvs[s]->max_ctx;
+    max_keys = std::max(max_keys, (len_dev ? kvs[s]->max_ctx : kvs[s]->len) + block_len);
   }
+  seqs.len_dev = len_dev;
   const Layout& Ly = h->lay;
   unsigned char* ws = h->ws;
   DraftLaunch L{};
@@ -553,6 +566,91 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* co
     if (e != hipSuccess) return dev_fail(e, "lm_argmax");
   }
   return DFLASH_OK;
+}
+
+extern "C" {
+
+dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                 const int32_t* anchor_ids, int32_t block_len, int32_t* block_out,
+                                 float* hidden_out, float* logits_out) {
+  return draft_impl(h, n_seqs, kvs, nullptr, anchor_ids, block_len, block_out, hidden_out,
+                    logits_out);
+}
+
+dflash_status dflash_draft_block_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                     const int32_t* len_dev, const int32_t* anchor_ids,
+                                     int32_t block_len, int32_t* block_out, float* hidden_out,
+                                     float* logits_out) {
+  if (!len_dev) return fail(DFLASH_E_NULL, "len_dev is required");
+  if (!aligned(len_dev, 4)) return fail(DFLASH_E_ALIGN, "len_dev not 4-byte aligned");
+  return draft_impl(h, n_seqs, kvs, len_dev, anchor_ids, block_len, block_out, hidden_out,
+                    logits_out);
+}
+
+dflash_status dflash_append_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                int32_t* len_dev, const int32_t* tau_dev,
+                                const void* const* feats, int64_t ld, int32_t rows_per_seq) {
+  if (!h || !kvs || !len_dev || !tau_dev || !feats)
+    return fail(DFLASH_E_NULL, "handle, kvs, len_dev, tau_dev and feats are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (rows_per_seq < 1 || rows_per_seq > c.block_size)
+    return fail(DFLASH_E_SHAPE, "rows_per_seq=%d outside 1..%d", rows_per_seq, c.block_size);
+  const int T = n_seqs * rows_per_seq;
+  if (T > h->max_tokens)
+    return fail(DFLASH_E_SHAPE, "n_seqs*rows_per_seq=%d exceeds max_tokens=%d", T, h->max_tokens);
+  if (ld < c.hidden || ld % 8) return fail(DFLASH_E_ALIGN, "ld=%lld must be >= hidden and a multiple of 8", (long long)ld);
+  if (!aligned(len_dev, 4) || !aligned(tau_dev, 4)) return fail(DFLASH_E_ALIGN, "len_dev/tau_dev not 4-byte aligned");
+  FuseLaunch F{};
+  for (int i = 0; i < c.n_feat_layers; ++i) {
+    if (!feats[i]) return fail(DFLASH_E_NULL, "feats[%d] is NULL", i);
+    if (!aligned(feats[i], 16)) return fail(DFLASH_E_ALIGN, "feats[%d] not 16-byte aligned", i);
+    F.feats[i] = (const bf16_t*)feats[i];
+  }
+  SeqTable seqs{};
+  for (int s = 0; s < n_seqs; ++s) {
+    dflash_status st = check_kv(h, kvs[s], "append_dev");
+    if (st != DFLASH_OK) return st;
+    seqs.s[s].kv = (bf16_t*)kvs[s]->base;
+    seqs.s[s].cap = row_capacity(c, kvs[s]->max_ctx);
+    seqs.s[s].len = kvs[s]->len;
+    seqs.s[s].max_ctx = kvs[s]->max_ctx;
+  }
+  seqs.len_dev = len_dev;
+  bf16_t* ctx = (bf16_t*)(h->ws + h->lay.app_ctx);
+  F.n_feat = c.n_feat_layers; F.ld = ld; F.T = T; F.D = c.hidden;
+  F.w_c = (const bf16_t*)h->w.w_c; F.gain = (const bf16_t*)h->w.ctx_norm; F.eps = c.rms_eps;
+  F.out = ctx; F.ssq = (float*)(h->ws + h->lay.fuse_ssq); F.y = (float*)(h->ws + h->lay.fuse_y);
+  F.split = split_ws(h); F.gemm = gemm_ws(h);
+  AppendLaunch A{};
+  A.ctx = ctx; A.T = T; A.rps = rows_per_seq; A.D = c.hidden; A.L = c.n_layers;
+  A.Hkv = c.n_kv_heads; A.hd = c.head_dim; A.log2_theta = std::log2((double)c.rope_theta);
+  for (int i = 0; i < c.n_layers; ++i) {
+    A.wk[i] = (const bf16_t*)h->layers[i].wk;
+    A.wv[i] = (const bf16_t*)h->layers[i].wv;
+  }
+  A.tau = tau_dev; A.seqs = &seqs; A.split = split_ws(h);
+  hipStream_t st = h->stream;
+  hipError_t e = timed(h, ST_FUSE, [&] {
+    return T <= kContextRowsStreaming ? launch_fuse_rows(F, st) : launch_fuse(F, st);
+  });
+  if (e != hipSuccess) return dev_fail(e, "append_dev fuse");
+  e = timed(h, ST_INJECT, [&] { return launch_append_inject(A, st); });
+  if (e != hipSuccess) return dev_fail(e, "append_dev inject");
+  e = launch_advance_len(len_dev, tau_dev, seqs, n_seqs, st);
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "append_dev lengths");
+}
+
+dflash_status dflash_kv_trim_dev(dflash_handle* h, int32_t n_seqs, int32_t* len_dev,
+                                 int32_t keep_len) {
+  if (!h || !len_dev) return fail(DFLASH_E_NULL, "handle and len_dev are required");
+  if (n_seqs < 1 || n_seqs > kMaxSeqs) return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, kMaxSeqs);
+  if (keep_len < 0) return fail(DFLASH_E_SHAPE, "keep_len=%d < 0", keep_len);
+  if (!aligned(len_dev, 4)) return fail(DFLASH_E_ALIGN, "len_dev not 4-byte aligned");
+  hipError_t e = launch_trim_len(len_dev, n_seqs, keep_len, h->stream);
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "kv_trim_dev");
 }
 
 dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,

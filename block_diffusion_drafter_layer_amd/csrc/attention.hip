@@ -136,7 +136,7 @@ attn_split(AttnArgs p) {
   const int a = g * G + gi;
   const int ql = lane & 15, lg = lane >> 4;
   const SeqDesc sd = p.seqs.s[s];
-  const int n_keys = sd.len + p.Bl;
+  const int n_keys = seq_len(p.seqs, s) + p.Bl;
   const int kb = split * p.kps;
   const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);  // last: the rest
   const size_t plane = (size_t)sd.cap * HD;

@@ -134,12 +134,24 @@ __device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_thet
 
 // One sequence of a draft call: its KV buffer and the context length.
 struct SeqDesc {
-  bf16_t* kv;     // base of the sequence's KV buffer
-  int32_t cap;    // row capacity of each head plane
-  int32_t len;    // context positions (the anchor sits at position len)
+  bf16_t* kv;       // base of the sequence's KV buffer
+  int32_t cap;      // row capacity of each head plane
+  int32_t len;      // context positions (the anchor sits at position len)
+  int32_t max_ctx;  // context positions the buffer holds
 };
 struct SeqTable {
   SeqDesc s[kMaxSeqs];
+  // device-resident rounds: the lengths live in device memory (int32 per
+  // sequence) and override s[i].len
+  const int32_t* len_dev;
 };
+
+// context length of sequence s: the host value, or the device one clamped to
+// the buffer (a length past max_ctx would put the block's rows out of it)
+__device__ __forceinline__ int seq_len(const SeqTable& t, int s) {
+  if (!t.len_dev) return t.s[s].len;
+  const int l = t.len_dev[s];
+  return l < 0 ? 0 : (l > t.s[s].max_ctx ? t.s[s].max_ctx : l);
+}
 
 }  // namespace dfl

@@ -73,7 +73,7 @@ struct EpiFuse {
   struct P {
     const bf16_t* w;  // [N][K]
     int K, N;
-    bf16_t* out;      // [M][N]
+    float* y;         // [M][N] fp32, normalised and rounded once afterwards
     float* ssq;       // [M][n_tiles]
     int n_tiles;
   };
@@ -81,19 +81,17 @@ struct EpiFuse {
   // rows [m0, m0 + kSlice) of the tile starting at column n0, C[r][c] at C[r * ld + c]
   template <int BN>
   __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
-    // bf16 y, 8 columns (16 bytes) per thread-step where the row allows
-    for (int e = threadIdx.x; e < kSlice * (BN / 8); e += blockDim.x) {
-      const int r = e / (BN / 8), c = 8 * (e % (BN / 8));
+    // fp32 y, 4 columns (16 bytes) per thread-step where the row allows
+    for (int e = threadIdx.x; e < kSlice * (BN / 4); e += blockDim.x) {
+      const int r = e / (BN / 4), c = 4 * (e % (BN / 4));
       const int m = m0 + r, n = n0 + c;
       if (m >= M || n >= p.N) continue;
       const float* y = C + r * ld + c;
-      if (n + 8 <= p.N && (p.N & 7) == 0) {
-        u32x4 o;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) o[h] = f2bf2(y[2 * h], y[2 * h + 1]);
-        *reinterpret_cast<u32x4*>(p.out + (size_t)m * p.N + n) = o;
+      float* dst = p.y + (size_t)m * p.N + n;
+      if (n + 4 <= p.N && (p.N & 3) == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
       } else {
-        for (int h = 0; h < 8 && n + h < p.N; ++h) p.out[(size_t)m * p.N + n + h] = f2bf(y[h]);
+        for (int h = 0; h < 4 && n + h < p.N; ++h) dst[h] = y[h];
       }
     }
     // per-row sum of squares over the tile's columns: 8 lanes per row
@@ -526,9 +524,11 @@ static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, 
 
 size_t ctx_gemm_part_floats() { return (size_t)256 * BM * 320; }
 
+// H_t row m = bf16(y[m] * rsqrt(mean(y[m]^2) + eps) * gain): the fp32
+// projection is rounded to bf16 once, here.
 __global__ void __launch_bounds__(256)
-fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ ssq, int n_tiles, int D,
-               const bf16_t* __restrict__ gain, float eps) {
+fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ y, const float* __restrict__ ssq,
+               int n_tiles, int D, const bf16_t* __restrict__ gain, float eps) {
   const int m = blockIdx.x;
   __shared__ float rs;
   if (threadIdx.x < 64) {
@@ -539,10 +539,16 @@ fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ ssq, int n_ti
   }
   __syncthreads();
   const float r = rs;
-#pragma unroll 4
-  for (int n = threadIdx.x; n < D; n += 256) {
-    bf16_t* o = out + (size_t)m * D + n;
-    *o = f2bf(bf2f(*o) * r * bf2f(gain[n]));
+  // D is a multiple of 64: 4 columns per thread-step
+  const float* yr = y + (size_t)m * D;
+  bf16_t* orow = out + (size_t)m * D;
+  for (int n = 4 * threadIdx.x; n < D; n += 4 * 256) {
+    const float4 v = *reinterpret_cast<const float4*>(yr + n);
+    const uint2 g = *reinterpret_cast<const uint2*>(gain + n);
+    const float g0 = bf2f((bf16_t)(g.x & 0xffff)), g1 = bf2f((bf16_t)(g.x >> 16));
+    const float g2 = bf2f((bf16_t)(g.y & 0xffff)), g3 = bf2f((bf16_t)(g.y >> 16));
+    *reinterpret_cast<uint2*>(orow + n) =
+        make_uint2(f2bf2(v.x * r * g0, v.y * r * g1), f2bf2(v.z * r * g2, v.w * r * g3));
   }
 }
 
@@ -551,16 +557,16 @@ hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st) {
   for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = i < F.n_feat ? F.feats[i] : F.feats[0];
   a.ld = F.ld; a.seg_k = F.D; a.M = F.T; a.K = F.n_feat * F.D;
   EpiFuse::P p;
-  p.w = F.w_c; p.K = a.K; p.N = F.D; p.out = F.out; p.ssq = F.ssq;
+  p.w = F.w_c; p.K = a.K; p.N = F.D; p.y = F.y; p.ssq = F.ssq;
   p.n_tiles = (F.D + kFuseTileN - 1) / kFuseTileN;
   hipError_t e = launch_tiled<kFuseTileN, EpiFuse>(a, p, F.D, F.gemm, st);
   if (e != hipSuccess) return e;
-  return launch_fuse_normalize(F.out, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
+  return launch_fuse_normalize(F.out, F.y, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
 }
 
-hipError_t launch_fuse_normalize(bf16_t* out, const float* ssq, int n_parts, int T, int D,
-                                 const bf16_t* gain, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(fuse_normalize, dim3(T), dim3(256), 0, st, out, ssq, n_parts, D, gain, eps);
+hipError_t launch_fuse_normalize(bf16_t* out, const float* y, const float* ssq, int n_parts, int T,
+                                 int D, const bf16_t* gain, float eps, hipStream_t st) {
+  hipLaunchKernelGGL(fuse_normalize, dim3(T), dim3(256), 0, st, out, y, ssq, n_parts, D, gain, eps);
   return hipGetLastError();
 }
 

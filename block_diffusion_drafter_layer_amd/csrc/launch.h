@@ -91,15 +91,16 @@ struct FuseLaunch {
   const bf16_t* w_c;
   const bf16_t* gain;
   float eps;
-  bf16_t* out;        // [T][D]
+  bf16_t* out;        // [T][D] H_t, the one rounding to bf16
+  float* y;           // [T][D] fp32 projection before the norm (workspace)
   float* ssq;         // [T][ceil(D/256)] (tiled) or [T][D/32] (few rows)
   SplitWs split;
   GemmWs gemm;
 };
 hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
-hipError_t launch_fuse_normalize(bf16_t* out, const float* ssq, int n_parts, int T, int D,
-                                 const bf16_t* gain, float eps, hipStream_t st);
+hipError_t launch_fuse_normalize(bf16_t* out, const float* y, const float* ssq, int n_parts, int T,
+                                 int D, const bf16_t* gain, float eps, hipStream_t st);
 
 // KV injection of T context rows at positions pos0.. into every layer.
 struct InjectLaunch {
@@ -115,6 +116,25 @@ struct InjectLaunch {
 hipError_t launch_inject(const InjectLaunch& I, hipStream_t st);       // tiled MFMA GEMM
 hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st);  // few rows: streaming
 constexpr int kContextRowsStreaming = 64;  // row counts up to this use the streaming kernels
+
+// Device-resident rounds: fused accepted rows of several sequences injected
+// at their device lengths, then the lengths advanced by tau.
+struct AppendLaunch {
+  const bf16_t* ctx;   // [T][D] fused rows, sequence s at rows s*rps ..
+  int T, rps, D, L, Hkv, hd;
+  double log2_theta;
+  const bf16_t* wk[kMaxLayers];
+  const bf16_t* wv[kMaxLayers];
+  const int32_t* tau;  // [n_seqs] device
+  const SeqTable* seqs;  // kv bases, capacities, len_dev
+  SplitWs split;
+};
+hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st);
+// len[s] = min(len[s] + tau[s], max_ctx[s]) for s < n_seqs
+hipError_t launch_advance_len(int32_t* len, const int32_t* tau, const SeqTable& seqs, int n_seqs,
+                              hipStream_t st);
+// len[s] = min(len[s], keep) for s < n
+hipError_t launch_trim_len(int32_t* len, int n, int32_t keep, hipStream_t st);
 
 // Verification.
 struct VerifyLaunch {

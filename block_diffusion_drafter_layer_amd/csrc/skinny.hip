@@ -106,7 +106,7 @@ struct EpiQKV {
       if (m >= M) continue;
       const int s = m / p.Bl, r = m % p.Bl;
       const SeqDesc sd = p.seqs.s[s];
-      const int pos = sd.len + r;
+      const int pos = seq_len(p.seqs, s) + r;
       const float x1 = tile[ml][c * 16 + j] * rs[ml];
       const float x2 = tile[ml][c * 16 + j + 8] * rs[ml];
       const int vc = vc0 + c * 16;
@@ -259,13 +259,13 @@ struct EpiLM {
 };
 
 // Context fusion for a few rows (the accepted rows appended each round):
-// y = [h_1 .. h_n] W_c^T as bf16 plus per-32-column sums of y^2; the RMSNorm
-// pass runs afterwards.
+// y = [h_1 .. h_n] W_c^T in fp32 plus per-32-column sums of y^2; the RMSNorm
+// pass runs afterwards and rounds to bf16 once.
 struct EpiFuseRows {
   struct P {
     const bf16_t* w;  // W_c [D][K]
     int K, D;
-    bf16_t* out;      // [M][D]
+    float* y;         // [M][D]
     float* ssq;       // [M][D/32]
     int n_vcols;      // D
   };
@@ -282,7 +282,7 @@ struct EpiFuseRows {
       const int m = m0 + ml;
       if (m >= M || vc0 + c >= p.n_vcols) continue;
       const float y = tile[ml][c];
-      p.out[(size_t)m * p.D + vc0 + c] = f2bf(y);
+      p.y[(size_t)m * p.D + vc0 + c] = y;
       tile[ml][c] = y * y;
     }
     __syncthreads();
@@ -352,6 +352,75 @@ struct EpiInjectRows {
         bf16_t* v = p.kv + (size_t)((2 * i + 1) * p.Hkv + h) * plane;
         v[(size_t)d0 * p.cap + pos] = f2bf(x1);
         v[(size_t)(d0 + 8) * p.cap + pos] = f2bf(x2);
+      }
+    }
+  }
+};
+
+// KV injection of the accepted rows of several sequences at their device
+// lengths (device-resident rounds): output row m is row r = m % rps of
+// sequence s = m / rps; it is written at position len[s] + r when
+// r < tau[s] and that position lies inside the buffer, and dropped
+// otherwise. Column order and RoPE pairing as in EpiInjectRows.
+struct EpiAppendRows {
+  struct P {
+    const bf16_t* wk[kMaxLayers];
+    const bf16_t* wv[kMaxLayers];
+    int D, Hkv, hd, rps;
+    double log2_theta;
+    const int32_t* tau;   // [n_seqs] device
+    SeqTable seqs;        // with len_dev
+    int n_vcols;          // L * 2 * Hkv * hd
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    const int kvd = p.Hkv * p.hd;
+    const int i = vc / (2 * kvd), r = vc % (2 * kvd);
+    if (r < kvd) {
+      const int h = r / p.hd, d = paired_dim(r % p.hd, p.hd);
+      return p.wk[i] + (size_t)(h * p.hd + d) * p.D;
+    }
+    return p.wv[i] + (size_t)(r - kvd) * p.D;
+  }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    const int kvd = p.Hkv * p.hd;
+    const int i = vc8 / (2 * kvd), r = vc8 % (2 * kvd);
+    if (r < kvd) {
+      const int h = r / p.hd, d = paired_dim(r % p.hd + r8, p.hd);
+      return p.wk[i] + (size_t)(h * p.hd + d) * p.D;
+    }
+    return p.wv[i] + (size_t)(r - kvd + r8) * p.D;
+  }
+  template <int ROWS, int VC>
+  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+                             int M) {
+    const int kvd = p.Hkv * p.hd;
+    constexpr int NG = VC / 16;
+    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
+      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+      const int m = m0 + ml;
+      if (m >= M) continue;
+      const int s = m / p.rps, rr = m % p.rps;
+      if (rr >= p.tau[s]) continue;
+      const SeqDesc sd = p.seqs.s[s];
+      const int pos = seq_len(p.seqs, s) + rr;
+      if (pos >= sd.max_ctx) continue;
+      const int vc = vc0 + c * 16;
+      if (vc >= p.n_vcols) continue;
+      const size_t plane = (size_t)sd.cap * p.hd;
+      const int i = vc / (2 * kvd), r = vc % (2 * kvd);
+      const float x1 = tile[ml][c * 16 + j], x2 = tile[ml][c * 16 + j + 8];
+      if (r < kvd) {
+        const int h = r / p.hd, d = ((r % p.hd) >> 1) + j;
+        float cs, sn;
+        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        bf16_t* k = sd.kv + (size_t)((2 * i) * p.Hkv + h) * plane + (size_t)pos * p.hd;
+        k[d] = f2bf(x1 * cs - x2 * sn);
+        k[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
+      } else {
+        const int h = (r - kvd) / p.hd, d0 = (r - kvd) % p.hd + j;
+        bf16_t* v = sd.kv + (size_t)((2 * i + 1) * p.Hkv + h) * plane;
+        v[(size_t)d0 * sd.cap + pos] = f2bf(x1);
+        v[(size_t)(d0 + 8) * sd.cap + pos] = f2bf(x2);
       }
     }
   }
@@ -1010,10 +1079,10 @@ hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
   for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = i < F.n_feat ? F.feats[i] : F.feats[0];
   a.seg_k = F.D;
   EpiFuseRows::P p;
-  p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.out = F.out; p.ssq = F.ssq; p.n_vcols = F.D;
+  p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.y = F.y; p.ssq = F.ssq; p.n_vcols = F.D;
   hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, F.split, st);
   if (e != hipSuccess) return e;
-  return launch_fuse_normalize(F.out, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
+  return launch_fuse_normalize(F.out, F.y, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
 }
 
 hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
@@ -1026,6 +1095,18 @@ hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
   p.D = I.D; p.Hkv = I.Hkv; p.hd = I.hd; p.pos0 = I.pos0; p.cap = I.cap;
   p.log2_theta = I.log2_theta; p.kv = I.kv; p.n_vcols = I.L * 2 * I.Hkv * I.hd;
   return launch_skinny<EpiInjectRows, false>(a, p, I.L * 2 * I.Hkv * I.hd, I.split, st);
+}
+
+hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st) {
+  SkinnyA a = make_a(A.ctx, nullptr, A.D, A.T, A.D, nullptr, 0, 0.f);
+  EpiAppendRows::P p;
+  for (int i = 0; i < kMaxLayers; ++i) {
+    p.wk[i] = i < A.L ? A.wk[i] : A.wk[0];
+    p.wv[i] = i < A.L ? A.wv[i] : A.wv[0];
+  }
+  p.D = A.D; p.Hkv = A.Hkv; p.hd = A.hd; p.rps = A.rps; p.log2_theta = A.log2_theta;
+  p.tau = A.tau; p.seqs = *A.seqs; p.n_vcols = A.L * 2 * A.Hkv * A.hd;
+  return launch_skinny<EpiAppendRows, false>(a, p, p.n_vcols, A.split, st);
 }
 
 hipError_t launch_embed(const DraftLaunch& L, hipStream_t st) {

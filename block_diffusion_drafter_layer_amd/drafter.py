@@ -99,6 +99,24 @@ class Drafter:
                              lg.data_ptr() if lg is not None else 0)
         return block_out, hid, lg
 
+    # --- device-resident rounds: lengths in a device int32 tensor -------------
+    def draft_block_dev(self, kvs: Sequence[KVCache], len_dev: torch.Tensor, anchors: torch.Tensor,
+                        block_out: torch.Tensor, hidden: Optional[torch.Tensor] = None,
+                        logits: Optional[torch.Tensor] = None):
+        B.dflash_draft_block_dev(self.h, [k.kv for k in kvs], len_dev.data_ptr(), anchors.data_ptr(),
+                                 block_out.shape[1], block_out.data_ptr(),
+                                 hidden.data_ptr() if hidden is not None else 0,
+                                 logits.data_ptr() if logits is not None else 0)
+        return block_out
+
+    def append_dev(self, kvs: Sequence[KVCache], len_dev: torch.Tensor, tau_dev: torch.Tensor,
+                   feats: Sequence[torch.Tensor], rows_per_seq: int):
+        B.dflash_append_dev(self.h, [k.kv for k in kvs], len_dev.data_ptr(), tau_dev.data_ptr(),
+                            [f.data_ptr() for f in feats], feats[0].stride(0), rows_per_seq)
+
+    def kv_trim_dev(self, len_dev: torch.Tensor, keep: int):
+        B.dflash_kv_trim_dev(self.h, len_dev.shape[0], len_dev.data_ptr(), keep)
+
     def sample_draft(self, block_ids: torch.Tensor, draft_logits: torch.Tensor, temperature: float,
                      seed: int = 0, philox_offset: int = 0):
         """Overwrite block_ids[:, 1:] with tokens sampled from the draft logits."""

@@ -161,8 +161,9 @@ dflash_status dflash_set_workspace(dflash_handle* h, void* ws, size_t bytes,
  *   square root.
  * feats: host array of n_feat_layers device pointers, each bf16 [n_tokens, ld]
  * (row stride ld elements, ld >= D, ld % 8 == 0), in increasing layer order;
- * the concatenation is never materialised. ctx_out: bf16 [n_tokens, D].
- * 1 <= n_tokens <= max_tokens of the workspace.
+ * the concatenation is never materialised. ctx_out: bf16 [n_tokens, D]; the
+ * projection stays fp32 until the norm, so each output is rounded to bf16
+ * once. 1 <= n_tokens <= max_tokens of the workspace.
  */
 dflash_status dflash_fuse_context(dflash_handle* h, const void* const* feats,
                                   int64_t ld, int32_t n_tokens, void* ctx_out);
@@ -206,6 +207,44 @@ dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs,
                                  const int32_t* anchor_ids, int32_t block_len,
                                  int32_t* block_out, float* hidden_out,
                                  float* logits_out);
+
+/*
+ * Device-resident speculative rounds ([Code] section 9: draft, verify, crop
+ * the cache to the accepted prefix, append the accepted rows' features).
+ * Here the context length of each sequence lives in device memory
+ * (len_dev: device int32 [n_seqs], one per kvs[s]) instead of kvs[s]->len,
+ * so that tau never has to come back to the host and a whole round can be
+ * captured into a graph. kvs[s]->base and ->max_ctx are still read on the
+ * host; kvs[s]->len is not used by these calls. A device length outside
+ * 0..max_ctx is clamped into it.
+ *
+ * dflash_draft_block_dev: dflash_draft_block with the lengths read from
+ *   len_dev (attention is planned for the buffers' capacity; key ranges past
+ *   a sequence's length are skipped). len_dev is not changed.
+ * dflash_append_dev: the append after verification. feats: n_feat_layers
+ *   device bf16 arrays [n_seqs * rows_per_seq, hidden] (row stride ld) with
+ *   the target's hidden states of each sequence's verified block rows,
+ *   sequence s at rows s*rows_per_seq ...; the rows are fused
+ *   (dflash_fuse_context), the first tau_dev[s] rows of sequence s are
+ *   injected (dflash_inject_kv) at positions len_dev[s] ..., rows that would
+ *   land at or past max_ctx are dropped, and len_dev[s] becomes
+ *   min(len_dev[s] + tau_dev[s], max_ctx). tau_dev: device int32 [n_seqs]
+ *   (dflash_verify's tau_out). 1 <= rows_per_seq <= block_size;
+ *   n_seqs * rows_per_seq <= max_tokens of the workspace.
+ * dflash_kv_trim_dev: len_dev[s] = min(len_dev[s], keep_len), s < n_seqs.
+ * Errors as for the other calls: checked on the host before any launch.
+ */
+dflash_status dflash_draft_block_dev(dflash_handle* h, int32_t n_seqs,
+                                     dflash_kv* const* kvs, const int32_t* len_dev,
+                                     const int32_t* anchor_ids, int32_t block_len,
+                                     int32_t* block_out, float* hidden_out,
+                                     float* logits_out);
+dflash_status dflash_append_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* const* kvs,
+                                int32_t* len_dev, const int32_t* tau_dev,
+                                const void* const* feats, int64_t ld,
+                                int32_t rows_per_seq);
+dflash_status dflash_kv_trim_dev(dflash_handle* h, int32_t n_seqs, int32_t* len_dev,
+                                 int32_t keep_len);
 
 /*
  * Sampling-mode drafting ([Code] section 6: away from greedy decoding the

@@ -10,6 +10,13 @@ Tolerances:
   * fused context / K / V: max-abs error <= 3e-2 x RMS as well (bf16 outputs
     of fp32-accumulated bf16 products);
   * verification: tau and bonus bit-exact (p/q: outside the exclusion bands).
+
+Storage precision: the library stores the fused context H_t and every K/V
+cache row as bf16, as the pages' BF16 model does (the txtmix article,
+section 5, sizes the projection's output and the weights at two bytes per
+element). The oracle's caches here are built with bf16_kv=True and the
+oracle's own H_t is rounded to bf16 before it is injected; everything else
+on the oracle side stays fp64.
 """
 import numpy as np
 import torch
@@ -64,7 +71,9 @@ def synthetic_context(dc, S, seq=0):
 
 
 def oracle_cache(dc, layer_kv):
-    c = O.DraftCache(dc.n_layers)
+    """The oracle's cache for the given bf16 context rows. It stores rows as
+    bf16, as the library's cache does (the pages' model is BF16)."""
+    c = O.DraftCache(dc.n_layers, bf16_kv=True)
     if layer_kv[0][0].shape[0] == 0:
         return c
     c.k = [np32(k).astype(np.float64) for k, _ in layer_kv]

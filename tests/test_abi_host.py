@@ -163,6 +163,20 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_sample_draft, h, 1, 16, 0, 1.0, 0, 0, FAKE) == 1
     assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, 1.0, 0, 0, 0) == 1
     assert _status(B.dflash_sample_draft, h, 1, 1, FAKE, 1.0, 0, 0, FAKE) == 0
+    # device-resident rounds: pointers, shapes, alignment
+    assert _status(B.dflash_draft_block_dev, h, [kv], 0, FAKE, 16, FAKE) == 1
+    assert _status(B.dflash_draft_block_dev, h, [kv], FAKE + 2, FAKE, 16, FAKE) == 5
+    assert _status(B.dflash_draft_block_dev, h, [kv], FAKE, FAKE, 17, FAKE) == 3
+    assert _status(B.dflash_append_dev, h, [kv], FAKE, FAKE, [FAKE] * 5, c.hidden, 17) == 3
+    assert _status(B.dflash_append_dev, h, [kv], FAKE, FAKE, [FAKE] * 5, c.hidden, 0) == 3
+    assert _status(B.dflash_append_dev, h, [kv], 0, FAKE, [FAKE] * 5, c.hidden, 16) == 1
+    assert _status(B.dflash_append_dev, h, [kv], FAKE, FAKE, [FAKE] * 4 + [0], c.hidden, 16) == 1
+    assert _status(B.dflash_append_dev, h, [kv], FAKE, FAKE, [FAKE] * 5, c.hidden - 8, 16) == 5
+    assert _status(B.dflash_append_dev, h, [kv, kv, kv], FAKE, FAKE, [FAKE] * 5, c.hidden, 16) == 3
+    assert _status(B.dflash_kv_trim_dev, h, 0, FAKE, 5) == 3
+    assert _status(B.dflash_kv_trim_dev, h, 1, FAKE, -1) == 3
+    assert _status(B.dflash_kv_trim_dev, h, 1, 0, 5) == 1
+    assert kv.len == 100
     # trim is host metadata only
     assert _status(B.dflash_kv_trim, h, kv, 101) == 3
     assert kv.len == 100

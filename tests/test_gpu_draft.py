@@ -109,8 +109,8 @@ def test_chained_fuse_inject_draft_tiny():
     torch.cuda.synchronize()
     wn = weights_np(w)
     H = O.fuse_context([np32(f) for f in feats], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
-    cache = O.DraftCache(dc.n_layers)
-    O.cache_inject(cache, H, wn["layers"], dc, 0)
+    cache = O.DraftCache(dc.n_layers, bf16_kv=True)
+    O.cache_inject(cache, O.round_bf16(H), wn["layers"], dc, 0)  # H_t is stored as bf16
     orc = O.draft_block(dc, wn, [cache], [int(anchors[0])])
     assert_hidden(np32(hid), orc["hidden"])
     assert_tokens(block.cpu().numpy(), orc)

@@ -1,5 +1,7 @@
 """GPU parity of speculative rounds: draft -> verify -> trim -> append, at the
-long-context workload (8192 context tokens, 4 rounds, block 16).
+long-context workload (8192 context tokens, 4 rounds, block 16), and of the
+device-resident rounds (lengths, tau and anchors kept on the GPU, a round
+captured into a graph).
 
 The initial 8192 context rows are seeded synthetic K/V written into both
 caches; each round's accepted rows are then fused from fresh target hidden
@@ -55,7 +57,7 @@ def _rounds(dc, S0, n_rounds):
         d.inject_kv(kv, H, S)
         Ho = O.fuse_context([np32(f) for f in feats], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
         assert_close_rms(np32(H), Ho, what=f"round {r} fused rows")
-        O.cache_inject(ocache, Ho, wn["layers"], dc, S)
+        O.cache_inject(ocache, O.round_bf16(Ho), wn["layers"], dc, S)
         S += tau
         anchor = bonus
         assert kv.len == S == ocache.len
@@ -77,3 +79,133 @@ def test_rounds_long_context_qwen_shape():
     dc = CONFIGS[2]
     S = _rounds(dc, dc.ctx_len, dc.rounds)
     assert S > dc.ctx_len
+
+
+def _rounds_dev(dc, S0s, n_rounds, salt=0):
+    """Device-resident rounds over len(S0s) sequences: each round drafts from
+    the device lengths, verifies the oracle's blocks against planted target
+    logits (tau and bonus stay on the device), appends the first tau rows of
+    each sequence's fresh target features and advances the device lengths.
+    The next anchors are the bonus tokens, read by the next draft from device
+    memory. The oracle runs the same rounds; nothing is read back to drive
+    the GPU loop."""
+    B = dc.block_size
+    n = len(S0s)
+    d, w = make(dc, max_seqs=n, max_tokens=max(n * B, 16))
+    wn = weights_np(w)
+    kvs, ocaches = [], []
+    for s, S0 in enumerate(S0s):
+        kv = poisoned_kv(d, S0 + B * (n_rounds + 1))
+        ctx = synthetic_context(dc, S0, seq=s)
+        fill_context(kv, ctx)
+        kvs.append(kv)
+        ocaches.append(oracle_cache(dc, ctx))
+    len_dev = torch.tensor(S0s, dtype=torch.int32, device=DEV)
+    anchors = [int(a) for a in synth.make_anchor(dc, n=n)]
+    anchor_dev = torch.tensor(anchors, dtype=torch.int32, device=DEV)
+    blk_dev = torch.empty(n, B, dtype=torch.int32, device=DEV)
+    hid = torch.empty(dc.n_layers, n * B, dc.hidden, dtype=torch.float32, device=DEV)
+    tau_dev = torch.empty(n, dtype=torch.int32, device=DEV)
+    bonus_dev = torch.empty(n, dtype=torch.int32, device=DEV)
+    taus = synth.planted_taus(dc, n_rounds * n, salt=11 + salt).reshape(n_rounds, n)
+    S = list(S0s)
+    for r in range(n_rounds):
+        say(f"device round {r}: contexts {S}")
+        d.draft_block_dev(kvs, len_dev, anchor_dev, blk_dev, hidden=hid)
+        orc = O.draft_block(dc, wn, ocaches, anchors)
+        # verify the oracle's blocks (no oracle input from the GPU path)
+        oblk = np.concatenate([np.array(anchors)[:, None], orc["draft"]], axis=1).astype(np.int32)
+        lg = torch.stack([synth.make_target_logits(dc, B, round_index=40 + 7 * r + s) for s in range(n)])
+        for s in range(n):
+            synth.plant_agreement(lg[s], oblk[s], int(taus[r, s]) - 1)
+        d.verify(torch.from_numpy(oblk).to(DEV), lg.to(DEV), tau=tau_dev, bonus=bonus_dev)
+        feats = synth.make_feats(dc, n * B, round_index=60 + r, device=DEV)
+        d.append_dev(kvs, len_dev, tau_dev, feats, B)
+        anchor_dev.copy_(bonus_dev)
+        # oracle: same round
+        fn = [np32(f) for f in feats]
+        for s in range(n):
+            t, b = O.verify_greedy(oblk[s], lg[s].numpy())
+            assert t == taus[r, s]
+            Ho = O.fuse_context([f[s * B:s * B + t] for f in fn], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
+            O.cache_inject(ocaches[s], O.round_bf16(Ho), wn["layers"], dc, S[s])
+            S[s] += t
+            anchors[s] = b
+        # checks (read-back only to compare)
+        assert_hidden(np32(hid), orc["hidden"], what=f"device round {r}")
+        assert_tokens(blk_dev.cpu().numpy(), orc, what=f"device round {r}")
+        assert len_dev.cpu().tolist() == S
+        assert anchor_dev.cpu().tolist() == anchors
+        assert [k.len for k in kvs] == list(S0s)  # the host lengths are not used
+    torch.cuda.synchronize()
+    for s in range(n):
+        for i in range(dc.n_layers):
+            gk = np32(kvs[s].k_view(i)[:, S0s[s]:S[s], :]).transpose(1, 0, 2)
+            gv = np32(kvs[s].v_view(i)[:, :, S0s[s]:S[s]]).transpose(2, 0, 1)
+            assert_close_rms(gk, ocaches[s].k[i][S0s[s]:S[s]], what=f"seq {s} appended K layer {i}")
+            assert_close_rms(gv, ocaches[s].v[i][S0s[s]:S[s]], what=f"seq {s} appended V layer {i}")
+    return d, kvs, len_dev
+
+
+def test_device_rounds_tiny_two_sequences():
+    _rounds_dev(CONFIGS[0].shrink(index=97), [10, 13], 4)
+
+
+def test_device_rounds_qwen_shape_two_sequences():
+    dc = CONFIGS[1]
+    _rounds_dev(dc, [dc.ctx_len, dc.ctx_len - 37], 3, salt=1)
+
+
+def test_device_round_graph_replays_match_eager():
+    """One device-resident round captured into a graph (draft from device
+    lengths, verify, append, trim back) and replayed; every replay must give
+    the eager round's block, tau and appended cache rows."""
+    dc = CONFIGS[0].shrink(index=96)
+    B = dc.block_size
+    d, w = make(dc, max_seqs=2, max_tokens=2 * B)
+    kvs = []
+    for s, S0 in enumerate((10, 12)):
+        kv = poisoned_kv(d, 64)
+        fill_context(kv, synthetic_context(dc, S0, seq=s))
+        kvs.append(kv)
+    S0 = torch.tensor([10, 12], dtype=torch.int32, device=DEV)
+    len_dev = S0.clone()
+    anchor = torch.tensor([3, 8], dtype=torch.int32, device=DEV)
+    blk = torch.empty(2, B, dtype=torch.int32, device=DEV)
+    tau = torch.empty(2, dtype=torch.int32, device=DEV)
+    bonus = torch.empty(2, dtype=torch.int32, device=DEV)
+    lg = synth.make_target_logits(dc, B, round_index=3).expand(2, B, dc.vocab).contiguous().to(DEV)
+    feats = synth.make_feats(dc, 2 * B, round_index=4, device=DEV)
+
+    def round_():
+        d.draft_block_dev(kvs, len_dev, anchor, blk)
+        d.verify(blk, lg, tau=tau, bonus=bonus)
+        d.append_dev(kvs, len_dev, tau, feats, B)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return (blk.cpu().clone(), tau.cpu().clone(), len_dev.cpu().clone(),
+                [k.buf.float().cpu().nan_to_num(123.0) for k in kvs])
+
+    round_()
+    ref = snapshot()
+    len_dev.copy_(S0)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        B_ = __import__("block_diffusion_drafter_layer_amd.binding", fromlist=["x"])
+        B_.dflash_set_stream(d.h, stream.cuda_stream)
+        with torch.cuda.graph(g, stream=stream):
+            round_()
+        B_.dflash_set_stream(d.h, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(stream)
+    for rep in range(3):
+        len_dev.copy_(S0)      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), rep
+        assert torch.equal(got[2], ref[2]), rep
+        for a, b in zip(got[3], ref[3]):
+            assert torch.equal(a, b), rep
