@@ -66,16 +66,23 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
                                               const bf16x8* qfl, float scale_log2, int lg,
                                               float& m_run, float& l_run, f32x4* acc) {
   constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
-  f32x4 st[2];
+  // hi and lo products in separate accumulators: four independent MFMA
+  // chains of KSTEPS instead of two of 2 * KSTEPS
+  f32x4 st[2], stl[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      st[t] = mfma16x16x32(c.kf[t][ks], qf[ks], st[t]);
-      st[t] = mfma16x16x32(c.kf[t][ks], qfl[ks], st[t]);
-    }
+    stl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = mfma16x16x32(c.kf[t][ks], qf[ks], st[t]);
+      stl[t] = mfma16x16x32(c.kf[t][ks], qfl[ks], stl[t]);
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) st[t] += stl[t];
   const int kl = c0 + 8 * lg;
   float sc[8];
   float mloc = -INFINITY;
@@ -131,7 +138,9 @@ attn_split(AttnArgs p) {
   __shared__ float lds_acc[(W > 1 ? W - 1 : 1) * G][16 * HD];
   __shared__ float lds_ml[(W > 1 ? W - 1 : 1) * G][16][2];
   const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the wave index in a scalar register: the key-column loop then branches
+  // uniformly and the wait counts on its loads stay exact
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gi = w % G, wi = w / G;
   const int a = g * G + gi;
   const int ql = lane & 15, lg = lane >> 4;
@@ -168,20 +177,23 @@ attn_split(AttnArgs p) {
     }
   }
   // two register stages: the next chunk of this column is in flight while
-  // the current one is processed
+  // the current one is processed. The next load is issued unconditionally
+  // (past the column's last chunk it re-reads that chunk, a cache hit), so
+  // that every wait on a chunk is an exact count rather than a full drain.
   Chunk<HD> ca, cb;
-  if (PIPE && c0 < ke) load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
-  while (PIPE && c0 < ke) {
-    const bool n1 = c0 + STEP < ke;
-    if (n1) load_chunk<HD>(cb, c0 + STEP, n_keys, kbase, vbase, sd.cap, ql, lg);
-    process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
-    if (!n1) break;
-    c0 += STEP;
-    const bool n2 = c0 + STEP < ke;
-    if (n2) load_chunk<HD>(ca, c0 + STEP, n_keys, kbase, vbase, sd.cap, ql, lg);
-    process_chunk<HD>(cb, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
-    if (!n2) break;
-    c0 += STEP;
+  if (PIPE && c0 < ke) {
+    const int last = c0 + (ke - 1 - c0) / STEP * STEP;  // the column's last chunk
+    load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
+    for (;;) {
+      load_chunk<HD>(cb, min(c0 + STEP, last), n_keys, kbase, vbase, sd.cap, ql, lg);
+      process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+      c0 += STEP;
+      if (c0 > last) break;
+      load_chunk<HD>(ca, min(c0 + STEP, last), n_keys, kbase, vbase, sd.cap, ql, lg);
+      process_chunk<HD>(cb, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+      c0 += STEP;
+      if (c0 > last) break;
+    }
   }
   l_run += __shfl_xor(l_run, 16, kWave);
   l_run += __shfl_xor(l_run, 32, kWave);
@@ -232,39 +244,48 @@ attn_split(AttnArgs p) {
 }
 
 // One workgroup per (block row, query head, sequence), one thread per output
-// dim (at least one wave): every split's (m, l) goes through LDS and every
-// split's accumulator value is requested before any is used.
-// One workgroup per (block row, query head, sequence), one thread per output
-// dim (at least one wave). The (m, l) pairs go through LDS; the first
-// kMergeBatch accumulator values are requested before the barrier, from
-// clamped indices so that the loads are straight-line code (the weights of
-// indices past the last split are zero).
+// dim (at least one wave). The first kMergeBatch accumulator values are
+// requested first, from clamped indices so that the loads are straight-line
+// code; meanwhile wave 0 holds split k's (m, l) in lane k (and k + 64), forms
+// the running max and the normaliser with wave reductions and leaves each
+// split's weight 2^(m_k - M) / L in LDS.
 constexpr int kMergeBatch = 32;
+static_assert(kAttnMaxSplits <= 128, "two splits per lane of wave 0");
 template <int HD>
 __global__ void __launch_bounds__(HD < 64 ? 64 : HD)
 attn_merge(const float* __restrict__ acc, const float* __restrict__ ml, int Hq, int Bl,
            int splits, bf16_t* __restrict__ ob_h, bf16_t* __restrict__ ob_l) {
-  constexpr int NT = HD < 64 ? 64 : HD;
   constexpr int STRIDE = 16 * HD;  // floats between the splits of one (row, dim)
   const int r = blockIdx.x, a = blockIdx.y, s = blockIdx.z;
   const int d = threadIdx.x;
-  __shared__ float sw[kAttnMaxSplits];
-  __shared__ float sl[kAttnMaxSplits];
+  __shared__ float wts[kAttnMaxSplits];
   const size_t slot0 = (size_t)(s * Hq + a) * splits;
   const float* pb = acc + (slot0 * 16 + r) * HD + (d < HD ? d : HD - 1);
   const int last = splits - 1;
   float v[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k, last) * STRIDE];
-  for (int k = threadIdx.x; k < splits; k += NT) {
-    sw[k] = ml[((slot0 + k) * 16 + r) * 2];
-    sl[k] = ml[((slot0 + k) * 16 + r) * 2 + 1];
+  if (threadIdx.x < 64) {
+    float mk[2], lk[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = threadIdx.x + 64 * j;
+      const bool in = k < splits;
+      mk[j] = in ? ml[((slot0 + k) * 16 + r) * 2] : -INFINITY;
+      lk[j] = in ? ml[((slot0 + k) * 16 + r) * 2 + 1] : 0.f;
+    }
+    const float M = wave_max(fmaxf(mk[0], mk[1]));
+    float e[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) e[j] = mk[j] == -INFINITY ? 0.f : exp2f(mk[j] - M);
+    const float inv = 1.f / wave_sum(e[0] * lk[0] + e[1] * lk[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = threadIdx.x + 64 * j;
+      if (k < splits) wts[k] = e[j] * inv;
+    }
   }
   __syncthreads();
-  float M = -INFINITY;
-  for (int k = 0; k < splits; ++k) M = fmaxf(M, sw[k]);
-  float Lsum = 0.f;
-  for (int k = 0; k < splits; ++k) Lsum += (sw[k] == -INFINITY ? 0.f : exp2f(sw[k] - M)) * sl[k];
   float o = 0.f;
   for (int k0 = 0; k0 < splits; k0 += kMergeBatch) {
     if (k0) {
@@ -272,15 +293,11 @@ attn_merge(const float* __restrict__ acc, const float* __restrict__ ml, int Hq, 
       for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k0 + k, last) * STRIDE];
     }
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
-      const float m = sw[min(k0 + k, last)];
-      const float wgt = (k0 + k < splits && m != -INFINITY) ? exp2f(m - M) : 0.f;
-      o += wgt * v[k];
-    }
+    for (int k = 0; k < kMergeBatch; ++k) o += (k0 + k < splits ? wts[k0 + k] : 0.f) * v[k];
   }
   if (d < HD) {
     const size_t i = ((size_t)(s * Bl + r) * Hq + a) * HD + d;
-    split_bf16(o / Lsum, ob_h[i], ob_l[i]);
+    split_bf16(o, ob_h[i], ob_l[i]);
   }
 }
 
