@@ -28,8 +28,9 @@
 // concat along the hidden axis): k in [j*D, (j+1)*D) reads layer j's array.
 //
 // Epilogues run on 64-row slices of the fp32 tile staged through LDS:
-//   fuse   - y as bf16 plus per-(row, 256-column tile) sums of y^2; a second
-//            kernel applies RMSNorm and the gain (tutorial section 2.1.2);
+//   fuse   - y in fp32 plus per-(row, 256-column tile) sums of y^2; a second
+//            kernel applies RMSNorm and the gain and rounds to bf16 once
+//            (tutorial section 2.1.2);
 //   inject - every draft layer's K (RoPE at position pos0 + row) and V,
 //            written into the KV-cache layout (txtmix article section 5).
 #include "common.h"
