@@ -526,7 +526,9 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   int splits = std::min(max_splits, std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves)));
   int kps = std::max(32, max_keys / splits / 32 * 32);
   if (max_keys / kps > max_splits) kps = (int)align_up((size_t)((max_keys + max_splits - 1) / max_splits), 32);
-  splits = std::max(1, max_keys / kps);
+  // never more workgroups than the target: with device-resident lengths
+  // max_keys covers the whole cache, and the last split absorbs the rest
+  splits = std::max(1, std::min(splits, max_keys / kps));
   L.att_splits = splits; L.att_keys_per_split = kps;
 
   hipStream_t st = h->stream;

@@ -41,21 +41,23 @@ struct Chunk {
 
 // K rows of the chunk as the A operand of S^T = K Q^T (keys permuted so each
 // lane group ends up with 8 consecutive keys) and the V^T rows for the same
-// keys. Addresses stay inside the cache; out-of-range keys are masked later.
+// keys. Addresses stay inside the cache's cap rows, so they do not depend on
+// the context length (which may still be on its way from device memory);
+// keys past the range are masked when the chunk is processed.
 template <int HD>
-__device__ __forceinline__ void load_chunk(Chunk<HD>& c, int c0, int n_keys, const bf16_t* kbase,
+__device__ __forceinline__ void load_chunk(Chunk<HD>& c, int c0, const bf16_t* kbase,
                                            const bf16_t* vbase, int cap, int ql, int lg) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     int key = c0 + (ql >> 2) * 8 + t * 4 + (ql & 3);
-    key = key < n_keys ? key : n_keys - 1;
+    key = key < cap ? key : cap - 1;
     const bf16_t* kr = kbase + (size_t)key * HD + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < Chunk<HD>::KSTEPS; ++ks)
       c.kf[t][ks] = (ks * 32 + 8 * lg < HD) ? ld_bf16x8(kr + ks * 32) : zero_bf16x8();
   }
   const int kl = c0 + 8 * lg;
-  const int kl_ld = kl < n_keys ? kl : 0;
+  const int kl_ld = kl < cap ? kl : 0;  // cap is a multiple of 64: 8 keys stay in the row
 #pragma unroll
   for (int h = 0; h < Chunk<HD>::HT; ++h)
     c.v[h] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(h * 16 + ql) * cap + kl_ld);
@@ -145,9 +147,7 @@ attn_split(AttnArgs p) {
   const int a = g * G + gi;
   const int ql = lane & 15, lg = lane >> 4;
   const SeqDesc sd = p.seqs.s[s];
-  const int n_keys = seq_len(p.seqs, s) + p.Bl;
   const int kb = split * p.kps;
-  const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);  // last: the rest
   const size_t plane = (size_t)sd.cap * HD;
   const bf16_t* kbase = sd.kv + (size_t)((2 * p.layer) * p.Hkv + g) * plane;
   const bf16_t* vbase = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + g) * plane;
@@ -162,34 +162,38 @@ attn_split(AttnArgs p) {
     qf[ks] = in ? ld_bf16x8(p.q + qoff + ks * 32) : zero_bf16x8();
     qfl[ks] = in ? ld_bf16x8(p.q_lo + qoff + ks * 32) : zero_bf16x8();
   }
+  constexpr int STEP = 32 * W;
+  int c0 = kb + 32 * wi;
+  Chunk<HD> ca, cb;
+  if (PIPE) load_chunk<HD>(ca, c0, kbase, vbase, sd.cap, ql, lg);
+  // the context length (host value or device memory) is needed only now
+  const int n_keys = seq_len(p.seqs, s) + p.Bl;
+  const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);  // last: the rest
+
   f32x4 acc[HT];
 #pragma unroll
   for (int h = 0; h < HT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-
-  constexpr int STEP = 32 * W;
-  int c0 = kb + 32 * wi;
   if (!PIPE) {  // one register stage
     for (; c0 < ke; c0 += STEP) {
       Chunk<HD> ca;
-      load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
-      process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+      Chunk<HD> cs;
+      load_chunk<HD>(cs, c0, kbase, vbase, sd.cap, ql, lg);
+      process_chunk<HD>(cs, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
     }
   }
   // two register stages: the next chunk of this column is in flight while
   // the current one is processed. The next load is issued unconditionally
   // (past the column's last chunk it re-reads that chunk, a cache hit), so
   // that every wait on a chunk is an exact count rather than a full drain.
-  Chunk<HD> ca, cb;
   if (PIPE && c0 < ke) {
     const int last = c0 + (ke - 1 - c0) / STEP * STEP;  // the column's last chunk
-    load_chunk<HD>(ca, c0, n_keys, kbase, vbase, sd.cap, ql, lg);
     for (;;) {
-      load_chunk<HD>(cb, min(c0 + STEP, last), n_keys, kbase, vbase, sd.cap, ql, lg);
+      load_chunk<HD>(cb, min(c0 + STEP, last), kbase, vbase, sd.cap, ql, lg);
       process_chunk<HD>(ca, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
       c0 += STEP;
       if (c0 > last) break;
-      load_chunk<HD>(ca, min(c0 + STEP, last), n_keys, kbase, vbase, sd.cap, ql, lg);
+      load_chunk<HD>(ca, min(c0 + STEP, last), kbase, vbase, sd.cap, ql, lg);
       process_chunk<HD>(cb, c0, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
       c0 += STEP;
       if (c0 > last) break;

@@ -20,6 +20,7 @@
 // Also here: the block embedding (section 6: anchor + mask tokens) and the
 // argmax reduction that writes the drafted block.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -867,6 +868,12 @@ __global__ void __launch_bounds__(256)
 stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ part) {
   __shared__ float tile[16][33];
   __shared__ float rs[16];
+  // device-resident lengths: request them before the partials, so the
+  // epilogue's reads of them hit this CU's cache instead of waiting on a
+  // round trip of their own (the value is kept live to the end)
+  int warm = 0;
+  if constexpr (std::is_same<Epi, EpiQKV>::value)
+    if (ep.seqs.len_dev && (int)threadIdx.x < a.M / ep.Bl) warm = ep.seqs.len_dev[threadIdx.x];
   const int t = threadIdx.x, pair = blockIdx.x;
   // thread t: element t of both tiles of the pair ([lane][4] order)
   const int ln = t >> 2, e = t & 3;
@@ -899,6 +906,7 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
+  asm volatile("" ::"v"(warm));
 }
 
 // LM-head finisher: 256 vocabulary columns per workgroup, one per thread.
