@@ -874,6 +874,16 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   int warm = 0;
   if constexpr (std::is_same<Epi, EpiQKV>::value)
     if (ep.seqs.len_dev && (int)threadIdx.x < a.M / ep.Bl) warm = ep.seqs.len_dev[threadIdx.x];
+  // the residual epilogue reads x and the norm gain of its elements: request
+  // them now as well (the epilogue's thread-to-element map, 2 per thread)
+  float warm_f = 0.f;
+  if constexpr (std::is_same<Epi, EpiResid>::value) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = threadIdx.x + 256 * k, ml = e / 32, n = blockIdx.x * 32 + e % 32;
+      if (ml < a.M && n < ep.n_vcols) warm_f += ep.x[(size_t)ml * ep.D + n] + bf2f(ep.gain[n]);
+    }
+  }
   const int t = threadIdx.x, pair = blockIdx.x;
   // thread t: element t of both tiles of the pair ([lane][4] order)
   const int ln = t >> 2, e = t & 3;
@@ -906,7 +916,7 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
-  asm volatile("" ::"v"(warm));
+  asm volatile("" ::"v"(warm), "v"(warm_f));
 }
 
 // LM-head finisher: 256 vocabulary columns per workgroup, one per thread.
