@@ -123,13 +123,18 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 // RoPE angle for position `pos` and pair index d of a head of size hd:
 // pos * theta^(-2d/hd), formed and reduced modulo 2*pi in fp64, then cos/sin
 // in fp32 of the reduced angle.
-__device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_theta,
-                                        float& c, float& s) {
-  double inv = exp2(-2.0 * (double)d / (double)hd * log2_theta);
+__device__ __forceinline__ double rope_inv_freq(int d, int hd, double log2_theta) {
+  return exp2(-2.0 * (double)d / (double)hd * log2_theta);
+}
+__device__ __forceinline__ void rope_cs_inv(int pos, double inv, float& c, float& s) {
   double a = (double)pos * inv;
   const double two_pi = 6.283185307179586476925286766559;
   a -= two_pi * rint(a / two_pi);
   sincosf((float)a, &s, &c);
+}
+__device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_theta,
+                                        float& c, float& s) {
+  rope_cs_inv(pos, rope_inv_freq(d, hd, log2_theta), c, s);
 }
 
 // One sequence of a draft call: its KV buffer and the context length.

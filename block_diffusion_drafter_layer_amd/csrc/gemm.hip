@@ -149,10 +149,29 @@ struct EpiInject {
     const InjectCol c = inject_col(n, p.Hkv, p.hd);
     return (c.is_k ? p.wk[c.layer] : p.wv[c.layer]) + (size_t)(c.head * p.hd + c.dim) * p.K;
   }
+  static constexpr int kVFlag = 1 << 16;  // column-table dim entries of V columns
   template <int BN>
   __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
     const size_t plane = (size_t)p.cap * p.hd;
     const int PW = p.hd < 64 ? p.hd : 64, hw = PW >> 1;
+    // the tile's column table, in LDS after the slice (16 bytes a column),
+    // once per slice: plane index (-1 past N), dim (| kVFlag for V), RoPE
+    // frequency; the per-element work is then a table read
+    int* col_plane = reinterpret_cast<int*>(const_cast<float*>(C) + kSlice * ld);
+    int* col_dim = col_plane + BN;
+    double* col_inv = reinterpret_cast<double*>(col_dim + BN);
+    for (int c = threadIdx.x; c < BN; c += blockDim.x) {
+      const int n = n0 + c;
+      if (n < p.N) {
+        const InjectCol ci = inject_col(n, p.Hkv, p.hd);
+        col_plane[c] = (2 * ci.layer + (ci.is_k ? 0 : 1)) * p.Hkv + ci.head;
+        col_dim[c] = ci.dim | (ci.is_k ? 0 : kVFlag);
+        col_inv[c] = ci.is_k ? rope_inv_freq(ci.dim, p.hd, p.log2_theta) : 0.0;
+      } else {
+        col_plane[c] = -1;
+      }
+    }
+    __syncthreads();
     // pair slots: slot k covers virtual columns g*PW + o and g*PW + o + PW/2
     // (g = k / hw, o = k % hw); K pairs get RoPE, V pairs are two plain
     // columns. Consecutive threads take consecutive slots of one row.
@@ -160,25 +179,24 @@ struct EpiInject {
       const int r = e / (BN / 2), k = e % (BN / 2);
       const int g = k / hw, o = k - g * hw;
       const int c1 = g * PW + o, c2 = c1 + hw;
-      const int m = m0 + r, n = n0 + c1;
-      if (m >= M || n >= p.N) continue;
-      const InjectCol ci = inject_col(n, p.Hkv, p.hd);
+      const int m = m0 + r;
+      const int pl = col_plane[c1];
+      if (m >= M || pl < 0) continue;
       const int pos = p.pos0 + m;
       const float x1 = C[r * ld + c1], x2 = C[r * ld + c2];
-      if (ci.is_k) {
+      const int dv = col_dim[c1], d = dv & (kVFlag - 1);
+      if (!(dv & kVFlag)) {
         float cs, sn;
-        rope_cs(pos, ci.dim, p.hd, p.log2_theta, cs, sn);
-        bf16_t* kp = p.kv + (size_t)((2 * ci.layer) * p.Hkv + ci.head) * plane + (size_t)pos * p.hd;
-        kp[ci.dim] = f2bf(x1 * cs - x2 * sn);
-        kp[ci.dim + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
+        rope_cs_inv(pos, col_inv[c1], cs, sn);
+        bf16_t* kp = p.kv + (size_t)pl * plane + (size_t)pos * p.hd;
+        kp[d] = f2bf(x1 * cs - x2 * sn);
+        kp[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
       } else {
-        bf16_t* vp = p.kv + (size_t)((2 * ci.layer + 1) * p.Hkv + ci.head) * plane + pos;
-        vp[(size_t)ci.dim * p.cap] = f2bf(x1);
-        if (n0 + c2 < p.N) {
-          const InjectCol c2i = inject_col(n0 + c2, p.Hkv, p.hd);
-          bf16_t* vp2 = p.kv + (size_t)((2 * c2i.layer + 1) * p.Hkv + c2i.head) * plane + pos;
-          vp2[(size_t)c2i.dim * p.cap] = f2bf(x2);
-        }
+        bf16_t* vp = p.kv + (size_t)pl * plane + pos;
+        vp[(size_t)d * p.cap] = f2bf(x1);
+        const int pl2 = col_plane[c2];
+        if (pl2 >= 0)
+          p.kv[(size_t)pl2 * plane + pos + (size_t)(col_dim[c2] & (kVFlag - 1)) * p.cap] = f2bf(x2);
       }
     }
   }
@@ -305,7 +323,8 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   constexpr int kLoadsBTot = BN / 16;                 // B loads per stage
   constexpr int kLoadsBMax = (kLoadsBTot + kWaves - 1) / kWaves;
   static_assert(NS * kStage <= kLds, "ring fits in LDS");
-  static_assert(kSlice * (BN + 8) * 4 <= NS * kStage, "epilogue slice fits in the ring");
+  static_assert(kSlice * (BN + 8) * 4 + 16 * BN <= NS * kStage,
+                "epilogue slice and column table fit in the ring");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
