@@ -209,3 +209,51 @@ def test_device_round_graph_replays_match_eager():
         assert torch.equal(got[2], ref[2]), rep
         for a, b in zip(got[3], ref[3]):
             assert torch.equal(a, b), rep
+
+
+def test_device_rounds_qwen_shape_one_sequence():
+    # 16 draft rows: the streaming kernels (the fallback takes more rows)
+    dc = CONFIGS[1]
+    _rounds_dev(dc, [dc.ctx_len], 3, salt=2)
+
+
+def test_device_trim_and_length_clamp():
+    """dflash_kv_trim_dev lowers lengths to keep_len and leaves shorter ones;
+    an append whose accepted rows run past the cache's max_ctx writes only the
+    rows that fit and stops the length at max_ctx (txtmix article section 9:
+    the cache holds the accepted prefix)."""
+    dc = CONFIGS[0].shrink(index=95)
+    B = dc.block_size
+    d, w = make(dc, max_seqs=2, max_tokens=2 * B)
+    wn = weights_np(w)
+    max_ctx = 14
+    kvs, ocaches = [], []
+    for s, S0 in enumerate((10, 13)):
+        kv = poisoned_kv(d, max_ctx)
+        ctx = synthetic_context(dc, S0, seq=s)
+        fill_context(kv, ctx)
+        kvs.append(kv)
+        ocaches.append(oracle_cache(dc, ctx))
+    len_dev = torch.tensor([10, 13], dtype=torch.int32, device=DEV)
+    d.kv_trim_dev(len_dev, 12)
+    assert len_dev.cpu().tolist() == [10, 12]
+    tau = torch.tensor([B, B], dtype=torch.int32, device=DEV)
+    feats = synth.make_feats(dc, 2 * B, round_index=7, device=DEV)
+    d.append_dev(kvs, len_dev, tau, feats, B)
+    torch.cuda.synchronize()
+    assert len_dev.cpu().tolist() == [max_ctx, max_ctx]
+    fn = [np32(f) for f in feats]
+    for s, S in enumerate((10, 12)):
+        n_fit = max_ctx - S
+        Ho = O.fuse_context([f[s * B:s * B + n_fit] for f in fn], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
+        ocaches[s].trim(S)
+        O.cache_inject(ocaches[s], O.round_bf16(Ho), wn["layers"], dc, S)
+        for i in range(dc.n_layers):
+            gk = np32(kvs[s].k_view(i)[:, S:max_ctx, :]).transpose(1, 0, 2)
+            gv = np32(kvs[s].v_view(i)[:, :, S:max_ctx]).transpose(2, 0, 1)
+            assert_close_rms(gk, ocaches[s].k[i][S:max_ctx], what=f"seq {s} K layer {i}")
+            assert_close_rms(gv, ocaches[s].v[i][S:max_ctx], what=f"seq {s} V layer {i}")
+        # rows past max_ctx (up to the capacity) were not written: still poisoned
+        rest = kvs[s].k_view(0)[:, max_ctx:max_ctx + 2, :].float()
+        if rest.numel():
+            assert torch.isnan(rest).all()
