@@ -145,6 +145,163 @@ def draft_block_bytes(dc, ctx):
     return L * per_layer + V * D * 2 + kv
 
 
+def _ev_time(fn, reps, torch):
+    """Median, p10 and p90 of fn() over reps runs, in microseconds (HIP events)."""
+    import numpy as np
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)))
+
+
+def _fill_context(kv, dc, S, seq, synth):
+    """Seeded synthetic context K/V rows [S, Hkv, hd] straight into the cache."""
+    for i in range(dc.n_layers):
+        k, v = synth.gen.make_context_kv(dc, i, S, device=kv.buf.device, seq=seq)
+        kv.k_view(i)[:, :S, :] = k.transpose(0, 1)
+        kv.v_view(i)[:, :, :S] = v.permute(1, 2, 0)
+    kv.kv.len = S
+
+
+def roof(nbytes, flops):
+    """Time at the binding MI355X roof (8 TB/s, 2.5 PFLOP/s bf16), us, and its name."""
+    t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e3), flops / (MFMA_BF16_PEAK_TFLOPS * 1e6)
+    return (t_hbm, "hbm") if t_hbm >= t_mfma else (t_mfma, "mfma")
+
+
+def draft_flops(dc, rows, ctx_total):
+    D, F, V, L = dc.hidden, dc.ffn, dc.vocab, dc.n_layers
+    qd, kvd = dc.q_dim, dc.kv_dim
+    per_layer = (qd + 2 * kvd) * D + D * qd + 2 * F * D + D * F
+    g = dc.block_size - 1
+    attn = 4.0 * dc.n_heads * dc.head_dim * dc.block_size * ctx_total  # QK^T and PV
+    return 2.0 * rows * L * per_layer + 2.0 * (rows // dc.block_size) * g * V * D + L * attn
+
+
+def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
+    """The other workloads' timed units (one GPU): the 32-sequence ragged
+    batch (one draft call, 512 rows), the D=2048 block-8 drafter (draft,
+    prefill fuse/inject, p/q verify) and the 8192-token context over 4
+    trim/append rounds. Each against its binding roof."""
+    import numpy as np
+    out = {}
+
+    # D=2048, block 8, p/q verification at temperature 1
+    dc = synth.CONFIGS[4]
+    w = synth.make_weights(dc, device=dev)
+    d = Drafter(config_from(dc), w, max_seqs=1, max_tokens=dc.ctx_len, device=dev)
+    kv = d.new_kv(dc.ctx_len + 64)
+    feats = synth.make_feats(dc, dc.ctx_len, device=dev)
+    fu = _ev_time(lambda: d.fuse_context(feats), 3, torch)
+    ctx = d.fuse_context(feats)
+    inj = _ev_time(lambda: d.inject_kv(kv, ctx, 0), 3, torch)
+    anchors = torch.from_numpy(synth.make_anchor(dc)).to(dev)
+    blk = torch.empty(1, dc.block_size, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        d.draft_block([kv], anchors, block_out=blk)
+    dr = _ev_time(lambda: d.draft_block([kv], anchors, block_out=blk), reps, torch)
+    tl = synth.make_target_logits(dc, dc.block_size, device=dev).unsqueeze(0).contiguous()
+    dlog = synth.make_target_logits(dc, dc.block_size - 1, device=dev, draft=True).unsqueeze(0).contiguous()
+    tau, bonus = torch.empty(1, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev)
+    vq = _ev_time(lambda: d.verify(blk, tl, dlog, temperature=1.0, seed=0, tau=tau, bonus=bonus), reps, torch)
+    T = dc.ctx_len
+    t_roof, bound = roof(draft_block_bytes(dc, T), draft_flops(dc, dc.block_size, T + dc.block_size))
+    f_fl = 2.0 * T * dc.n_feat * dc.hidden * dc.hidden
+    i_fl = 2.0 * T * dc.hidden * 2 * dc.kv_dim * dc.n_layers
+    out[dc.name] = {
+        "draft_block_us": round(dr[0], 1), "draft_block_us_p10_p90": [round(dr[1], 1), round(dr[2], 1)],
+        "blocks_per_s": round(1e6 / dr[0], 1), "draft_roofline": {"bound": bound, "frac": round(t_roof / dr[0], 4)},
+        "prefill_fuse_us": round(fu[0], 1), "prefill_fuse_mfma_frac": round(f_fl / (fu[0] * 1e6) / MFMA_BF16_PEAK_TFLOPS, 4),
+        "prefill_inject_us": round(inj[0], 1),
+        "prefill_inject_mfma_frac": round(i_fl / (inj[0] * 1e6) / MFMA_BF16_PEAK_TFLOPS, 4),
+        "pq_verify_us": round(vq[0], 1)}
+    d.close()
+    del w, d, kv, feats, ctx, tl, dlog
+    torch.cuda.empty_cache()
+
+    # 32 sequences, ragged contexts uniform in [512, 4096], one draft call
+    dc = synth.CONFIGS[3]
+    w = synth.make_weights(dc, device=dev)
+    n = dc.n_seqs
+    lens = [int(x) for x in synth.gen.ragged_lengths(n)]
+    d = Drafter(config_from(dc), w, max_seqs=n, max_tokens=n * dc.block_size, device=dev)
+    kvs = []
+    for s_, S in enumerate(lens):
+        kv = d.new_kv(S + 64)
+        _fill_context(kv, dc, S, s_, synth)
+        kvs.append(kv)
+    anchors = torch.from_numpy(synth.make_anchor(dc, n=n)).to(dev)
+    blk = torch.empty(n, dc.block_size, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        d.draft_block(kvs, anchors, block_out=blk)
+    dr = _ev_time(lambda: d.draft_block(kvs, anchors, block_out=blk), max(3, reps // 3), torch)
+    kv_bytes = sum(dc.n_layers * 2 * (S + dc.block_size) * dc.kv_dim * 2 for S in lens)
+    nbytes = draft_block_bytes(dc, 0) + kv_bytes
+    t_roof, bound = roof(nbytes, draft_flops(dc, n * dc.block_size, sum(lens) + n * dc.block_size))
+    out[dc.name] = {"draft_block_us": round(dr[0], 1),
+                    "draft_block_us_p10_p90": [round(dr[1], 1), round(dr[2], 1)],
+                    "blocks_per_s": round(n * 1e6 / dr[0], 1),
+                    "draft_roofline": {"bound": bound, "frac": round(t_roof / dr[0], 4)},
+                    "context_lengths": "32 uniform in [512, 4096], mean %d" % int(np.mean(lens))}
+    d.close()
+    del d, kvs
+    torch.cuda.empty_cache()
+
+    # 8192-token context, 4 host-driven rounds of draft, verify, trim, append
+    dc = synth.CONFIGS[2]
+    w2 = w  # same shapes as the 32-sequence drafter; the timing does not depend on the values
+    S0, Bs = dc.ctx_len, dc.block_size
+    d = Drafter(config_from(dc), w2, max_seqs=1, max_tokens=S0, device=dev)
+    kv = d.new_kv(S0 + Bs * (dc.rounds + 1))
+    feats = synth.make_feats(dc, S0, device=dev)
+    fu = _ev_time(lambda: d.fuse_context(feats), 2, torch)
+    ctx = d.fuse_context(feats)
+    d.inject_kv(kv, ctx, 0)
+    anchors = torch.from_numpy(synth.make_anchor(dc)).to(dev)
+    blk = torch.empty(1, Bs, dtype=torch.int32, device=dev)
+    taus = synth.planted_taus(dc, dc.rounds)
+    rounds_us, drafts_us = [], []
+    for r in range(dc.rounds):
+        S = kv.len
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        lg = synth.make_target_logits(dc, Bs, round_index=10 + r)
+        app = synth.make_feats(dc, Bs, round_index=20 + r, device=dev)
+        torch.cuda.synchronize()
+        e[0].record()
+        d.draft_block([kv], anchors, block_out=blk)
+        e[1].record()
+        torch.cuda.synchronize()
+        synth.plant_agreement(lg, blk[0].cpu().numpy(), int(taus[r]) - 1)
+        lgd = lg.unsqueeze(0).to(dev)
+        torch.cuda.synchronize()
+        e[2].record()
+        t_, b_ = d.verify(blk, lgd)
+        tau = int(t_.item())
+        d.kv_trim(kv, S)
+        d.inject_kv(kv, d.fuse_context([f[:tau] for f in app]), S)
+        e3 = torch.cuda.Event(enable_timing=True)
+        e3.record()
+        torch.cuda.synchronize()
+        drafts_us.append(e[0].elapsed_time(e[1]) * 1e3)
+        rounds_us.append(e[0].elapsed_time(e[1]) * 1e3 + e[2].elapsed_time(e3) * 1e3)
+        anchors = b_.to(torch.int32)
+    t_roof, bound = roof(draft_block_bytes(dc, S0 + Bs), draft_flops(dc, Bs, S0 + 2 * Bs))
+    out[dc.name] = {"prefill_fuse_us_T8192": round(fu[0], 1),
+                    "prefill_fuse_mfma_frac": round(2.0 * S0 * dc.n_feat * dc.hidden ** 2 / (fu[0] * 1e6)
+                                                    / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "round_us": [round(x, 1) for x in rounds_us],
+                    "draft_block_us": [round(x, 1) for x in drafts_us],
+                    "draft_roofline": {"bound": bound, "frac": round(t_roof / float(np.median(drafts_us)), 4)},
+                    "final_context": kv.len}
+    d.close()
+    return out
+
+
 def cpu_baseline(dc, w, feats_np, ctx_cache_fn, planted, budget_s=30.0):
     """One speculative round of the oracle on host cores: draft forward at the
     2048-token context, greedy verify, fuse + inject of the accepted rows."""
@@ -186,6 +343,8 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="time only the headline workload")
     ap.add_argument("--profile-all", action="store_true",
                     help="also time every stage once after the timed region")
     ap.add_argument("--copy-reference", action="store_true",
@@ -375,10 +534,13 @@ def main():
         # every round did its work: the planted agreement lengths come back
         assert dt == sum(int(taus[j % n_plant]) for j in range(args.steps)), dt
         assert int(len_dev.item()) == S0 and kv.len == S0
-        return el, dt, float(np.median([a.elapsed_time(b) for a, b in zip(ev0, ev1)])) * 1e3
+        dts = [a.elapsed_time(b) * 1e3 for a, b in zip(ev0, ev1)]
+        timed_rounds.spread = (float(np.percentile(dts, 10)), float(np.percentile(dts, 90)))
+        return el, dt, float(np.median(dts))
 
     # device-resident rounds launched directly
     el_e, tau_e, draft_e = timed_rounds(lambda: d.draft_block_dev([kv], len_dev, anchors, blk_out), dev_rest)
+    draft_spread = timed_rounds.spread
     eager_loop = {"blocks_per_s": round(args.steps / el_e, 2), "ms_per_step": round(el_e * 1e3 / args.steps, 4),
                   "draft_block_us": round(draft_e, 1)}
 
@@ -402,6 +564,17 @@ def main():
     # the headline: device-resident rounds launched directly
     assert tau_e == tau_sum, (tau_e, tau_sum)
     elapsed, dev_tau, draft_us = el_e, tau_e, draft_e
+
+    # the achieved peak of a plain device copy (the library's reference copy,
+    # 1 GiB read + 1 GiB written), reported beside the 8 TB/s figure
+    nb = 1 << 30
+    src = torch.ones(nb // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    cst = torch.cuda.current_stream().cuda_stream
+    B.dflash_copy_bytes(dst.data_ptr(), src.data_ptr(), nb, cst)
+    cp = _ev_time(lambda: B.dflash_copy_bytes(dst.data_ptr(), src.data_ptr(), nb, cst), 5, torch)
+    copy_gbs = 2.0 * nb / (cp[0] * 1e3)
+    del src, dst
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps / elapsed
@@ -431,7 +604,13 @@ def main():
                      "traffic": counter_traffic(dom, dc.name), "avg_launch_us": round(avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": sb[dom]},
         "draft_block_us": round(draft_us, 1),
+        "draft_block_us_p10_p90": [round(draft_spread[0], 1), round(draft_spread[1], 1)],
         "draft_block_hbm_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "draft_block_copy_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / copy_gbs, 4),
+        "copy_peak_GBs": round(copy_gbs, 1),
+        # the pages' per-token latency L = (T_draft + T_verify) / tau, with
+        # this path's side only: the target's verify forward is not part of it
+        "round_us_per_accepted_token": round(ms_per_step * 1e3 / max(dev_tau / args.steps, 1e-9), 1),
         "mean_tau": round(dev_tau / args.steps, 3),
         "host_loop": host_loop,
         "graph_loop": graph_loop,
@@ -442,6 +621,10 @@ def main():
     }
     if stages_all:
         result["stage_us_per_step"] = stages_all
+
+    if not args.no_other_workloads:
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        result["other_workloads"] = other_workloads(args.steps, torch, synth, B, Drafter, config_from, dev)
 
     if not args.no_cpu_baseline:
         import oracle as O
