@@ -98,6 +98,7 @@ struct Layout {
   size_t gemm_part, gemm_ctr;   // context-GEMM split-K partials and counters (0 bytes if unused)
   size_t app_ctx;               // fused rows of a device-resident append
   size_t fuse_y;                // fp32 projection of the fused rows before the norm
+  size_t vcdf;                  // verify / sampling draws: merged row statistics and slice sums
   size_t total;
 };
 
@@ -134,6 +135,7 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.gemm_ctr = take(tiled ? (size_t)kGemmMaxCounters * 4 : 0);
   L.app_ctx = take(std::min((size_t)max_tokens, Mmax) * D * 2);
   L.fuse_y = take((size_t)max_tokens * D * 4);
+  L.vcdf = take(2 * Mmax * 16 + Mmax * kVerifyMaxSplits * 8);
   L.total = o;
   return L;
 }
@@ -682,6 +684,8 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
   P.temperature = (double)temperature; P.seed = seed; P.offset = philox_offset;
   P.tau = tau_out; P.bonus = bonus_out;
   P.part = h->ws + h->lay.vpart;
+  P.part2 = h->ws + h->lay.vcdf;
+  P.max_rows = 2 * h->max_seqs * c.block_size;
   const int rows = greedy ? n_seqs * block_len : n_seqs * (2 * block_len - 1);
   P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
   hipError_t e = timed(h, ST_VERIFY, [&] {
@@ -709,6 +713,8 @@ dflash_status dflash_sample_draft(dflash_handle* h, int32_t n_seqs, int32_t bloc
   P.target = draft_logits; P.temperature = (double)temperature;
   P.seed = seed; P.offset = philox_offset;
   P.part = h->ws + h->lay.vpart;
+  P.part2 = h->ws + h->lay.vcdf;
+  P.max_rows = 2 * h->max_seqs * c.block_size;
   const int rows = n_seqs * (block_len - 1);
   P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
   hipError_t e = timed(h, ST_SAMPLE, [&] {

@@ -147,6 +147,8 @@ struct VerifyLaunch {
   int32_t *tau, *bonus;
   void* part;          // workspace for per-split partials
   int splits;
+  void* part2;         // merged row statistics [max_rows] then slice sums [max_rows / 2][splits]
+  int max_rows;
 };
 hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);

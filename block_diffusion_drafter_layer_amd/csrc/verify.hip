@@ -8,10 +8,10 @@
 // tau = a + 1 and bonus = posterior[a].
 //
 // p/q: per-row softmax statistics in fp64 (max and sum of exp) over vocab
-// slices, merged per row; one workgroup per sequence runs the accept tests
-// u_j < p_j(x)/q_j(x) in order and draws the replacement token from
-// max(p - q, 0), or the bonus from the last target row, by an inverse CDF in
-// fp64 over the vocab in index order. Uniforms come from Philox4x64-10
+// slices, merged per row; the accept tests u_j < p_j(x)/q_j(x) run in order
+// and the replacement token is drawn from max(p - q, 0), or the bonus from
+// the last target row, by an inverse CDF in fp64 over the vocab in index
+// order, spread over vocab slices (see cdf_slice_sums / cdf_pick below). Uniforms come from Philox4x64-10
 // (Salmon et al., SC 2011) with key (seed, 0) and counter
 // (offset + row, sequence, purpose, 0).
 //
@@ -150,183 +150,256 @@ row_softmax_part(VerifyLaunch P, RowStat* part) {
   }
 }
 
-constexpr int kPQThreads = 1024;
+// Draws by inverse CDF over many workgroups. Stage 1 (row_softmax_part)
+// leaves per-slice softmax statistics. Stage 2 (cdf_slice_sums), one
+// workgroup per (vocab slice, candidate row): the weights of the slice are
+// summed per contiguous thread chunk in vocab order and the chunk sums in
+// thread order; split 0 also leaves the merged (M, Z) of the rows it read.
+// Stage 3 (cdf_pick), one workgroup per draw: the slice totals are scanned in
+// slice order to find the slice holding u * total, the chunk sums of that
+// slice are recomputed and scanned in thread order (the same operations in
+// the same order, so the slice total is reproduced exactly), and the thread
+// whose chunk holds the target runs it in vocab order. The result is the
+// smallest v whose running sum exceeds u * total, up to the association of
+// the running sum.
+//
+// Candidate rows: p/q - row c = s * Bl + j, j < gamma: max(p_j - q_j, 0); j =
+// gamma: p_gamma (the bonus row). Draft sampling - row r: q_r.
+constexpr int kCdfThreads = 256;
 
-__global__ void __launch_bounds__(kPQThreads)
-pq_accept_sample(VerifyLaunch P, const RowStat* part) {
-  const int s = blockIdx.x, tid = threadIdx.x;
-  const int Bl = P.Bl, gamma = Bl - 1;
-  const int nt = P.n_seqs * Bl;
-  __shared__ double rm[2 * 16], rz[2 * 16];  // target rows then draft rows
-  __shared__ int jr_sh;
-  __shared__ double csum[kPQThreads];
-  __shared__ double total_sh;
-  __shared__ int found;
+struct Merged {
+  double m, z;
+};
 
-  // merge slice statistics: one thread per row of this sequence
-  if (tid < Bl + gamma) {
-    const int row = tid < Bl ? s * Bl + tid : nt + s * gamma + (tid - Bl);
-    const RowStat* p = part + (size_t)row * P.splits;
-    double M = -INFINITY;
-    for (int k = 0; k < P.splits; ++k) M = fmax(M, p[k].m);
-    double Z = 0.0;
-    for (int k = 0; k < P.splits; ++k)
-      if (p[k].m != -INFINITY) Z += p[k].z * exp(p[k].m - M);
-    rm[tid] = M;
-    rz[tid] = Z;
+// (M, Z) of row `row` from its split statistics, by wave 0 (splits <= 64);
+// the same operations wherever it is called
+__device__ __forceinline__ Merged merge_row(const RowStat* part, int row, int splits) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < splits;
+  const RowStat r = in ? part[(size_t)row * splits + lane] : RowStat{-INFINITY, 0.0};
+  double M = r.m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, kWave));
+  const double z = (in && r.m != -INFINITY) ? r.z * exp(r.m - M) : 0.0;
+  return Merged{M, wave_sum_d(z)};
+}
+
+// the weight of candidate row c at v
+struct CdfRow {
+  const float* t;  // p (or q when drawing from the draft) source row
+  const float* d;  // q row of a p/q residual, else null
+  double mt, zt, mq, zq, inv_temp;
+  __device__ double w(int v) const {
+    const double p = exp((double)t[v] * inv_temp - mt) / zt;
+    if (!d) return p;
+    const double r = p - exp((double)d[v] * inv_temp - mq) / zq;
+    return r > 0.0 ? r : 0.0;
+  }
+};
+
+// stats rows and logits of candidate row c (PQ: p/q residual or bonus row)
+template <bool PQ>
+__device__ __forceinline__ void cand_rows(const VerifyLaunch& P, int c, int& trow, int& drow) {
+  if (PQ) {
+    const int Bl = P.Bl, gamma = Bl - 1, s = c / Bl, j = c - s * Bl;
+    trow = c;
+    drow = j < gamma ? P.n_seqs * Bl + s * gamma + j : -1;
+  } else {
+    trow = c;
+    drow = -1;
+  }
+}
+
+__device__ __forceinline__ const float* logits_row(const VerifyLaunch& P, int stat_row) {
+  const int nt = P.n_seqs * P.Bl;
+  return stat_row < nt ? P.target + (size_t)stat_row * P.V
+                       : P.draft + (size_t)(stat_row - nt) * P.V;
+}
+
+// chunk sums of slice `split` in thread order: local[t] for every thread;
+// returns this thread's chunk bounds
+__device__ __forceinline__ void slice_chunk(const VerifyLaunch& P, int split, int& v0, int& v1) {
+  const int sl = (P.V + P.splits - 1) / P.splits;
+  const int a = split * sl, b = min(a + sl, P.V);
+  const int ch = (b - a + kCdfThreads - 1) / kCdfThreads;
+  v0 = min(a + (int)threadIdx.x * ch, b);
+  v1 = min(v0 + ch, b);
+}
+
+template <bool PQ>
+__global__ void __launch_bounds__(kCdfThreads)
+cdf_slice_sums(VerifyLaunch P, const RowStat* part, Merged* merged, double* sums) {
+  const int split = blockIdx.x, c = blockIdx.y;
+  __shared__ Merged st[2];
+  __shared__ double loc[kCdfThreads];
+  int trow, drow;
+  cand_rows<PQ>(P, c, trow, drow);
+  if (threadIdx.x < 64) {
+    const Merged a = merge_row(part, trow, P.splits);
+    const Merged b = drow >= 0 ? merge_row(part, drow, P.splits) : Merged{0.0, 1.0};
+    if (threadIdx.x == 0) {
+      st[0] = a;
+      st[1] = b;
+      if (split == 0) {
+        merged[trow] = a;
+        if (drow >= 0) merged[drow] = b;
+      }
+    }
   }
   __syncthreads();
+  CdfRow R{logits_row(P, trow), drow >= 0 ? logits_row(P, drow) : nullptr,
+           st[0].m, st[0].z, st[1].m, st[1].z, 1.0 / P.temperature};
+  int v0, v1;
+  slice_chunk(P, split, v0, v1);
+  double local = 0.0;
+  for (int v = v0; v < v1; ++v) local += R.w(v);
+  loc[threadIdx.x] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double run = 0.0;
+    for (int t = 0; t < kCdfThreads; ++t) run += loc[t];
+    sums[(size_t)c * P.splits + split] = run;
+  }
+}
+
+// inverse-CDF draw on candidate row c with uniform u; returns the index.
+// loc: LDS [kCdfThreads]; sh: LDS int[3]; dsh: LDS double[1].
+__device__ int cdf_draw(const VerifyLaunch& P, const CdfRow& R, const double* sums, int c, double u,
+                        double* loc, int* sh, double* dsh) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const double* sr = sums + (size_t)c * P.splits;
+    double total = 0.0;
+    for (int k = 0; k < P.splits; ++k) total += sr[k];
+    const double target = u * total;
+    int ks = -1;
+    double run = 0.0;
+    for (int k = 0; k < P.splits; ++k) {
+      if (run + sr[k] > target) { ks = k; break; }
+      run += sr[k];
+    }
+    sh[0] = ks;
+    sh[1] = -1;
+    sh[2] = -1;
+    dsh[0] = target - run;
+  }
+  __syncthreads();
+  const int ks = sh[0];
+  if (ks < 0) return P.V - 1;  // target at or beyond the total: last index
+  const double target = dsh[0];
+  int v0, v1;
+  slice_chunk(P, ks, v0, v1);
+  double local = 0.0;
+  for (int v = v0; v < v1; ++v) local += R.w(v);
+  loc[tid] = local;
+  __syncthreads();
+  if (tid == 0) {  // exclusive running sums of the chunk sums, in thread order
+    double run = 0.0;
+    for (int t = 0; t < kCdfThreads; ++t) {
+      const double x = loc[t];
+      loc[t] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const double before = loc[tid];
+  if (v0 < v1 && before <= target && target < before + local) {
+    double run = before;
+    int pick = v1 - 1;
+    for (int v = v0; v < v1; ++v) {
+      run += R.w(v);
+      if (run > target) { pick = v; break; }
+    }
+    sh[1] = pick;
+  }
+  __syncthreads();
+  if (sh[1] >= 0) return sh[1];
+  // rounding left the target past the slice's last chunk boundary: take the
+  // slice's last index with a nonzero weight
+  int last = -1;
+  if (local > 0.0)
+    for (int v = v0; v < v1; ++v)
+      if (R.w(v) > 0.0) last = v;
+  if (last >= 0) atomicMax(sh + 2, last);
+  __syncthreads();
+  return sh[2] >= 0 ? sh[2] : P.V - 1;
+}
+
+// one workgroup per sequence: the accept tests in order, then the draw from
+// the first rejected row's residual or from the bonus row
+__global__ void __launch_bounds__(kCdfThreads)
+pq_pick(VerifyLaunch P, const Merged* merged, const double* sums) {
+  const int s = blockIdx.x, tid = threadIdx.x;
+  const int Bl = P.Bl, gamma = Bl - 1, nt = P.n_seqs * Bl;
+  __shared__ double loc[kCdfThreads];
+  __shared__ int sh[3];
+  __shared__ double dsh[1];
+  __shared__ int jr_sh;
+  const double inv_t = 1.0 / P.temperature;
   if (tid == 0) {
     int jr = gamma;
     for (int j = 0; j < gamma; ++j) {
       int x = P.block_ids[(size_t)s * Bl + j + 1];
       x = x < 0 ? 0 : (x >= P.V ? P.V - 1 : x);  // keep the read in bounds
-      const float* tr = P.target + (size_t)(s * Bl + j) * P.V;
-      const float* dr = P.draft + (size_t)(s * gamma + j) * P.V;
-      const double p = exp((double)tr[x] / P.temperature - rm[j]) / rz[j];
-      const double q = exp((double)dr[x] / P.temperature - rm[Bl + j]) / rz[Bl + j];
+      const Merged a = merged[s * Bl + j], b = merged[nt + s * gamma + j];
+      const double p = exp((double)P.target[(size_t)(s * Bl + j) * P.V + x] * inv_t - a.m) / a.z;
+      const double q = exp((double)P.draft[(size_t)(s * gamma + j) * P.V + x] * inv_t - b.m) / b.z;
       const double u = philox_uniform(P.seed, P.offset + j, s, 0);
       if (!(u < p / q)) { jr = j; break; }
     }
     jr_sh = jr;
-    found = 0;
   }
   __syncthreads();
   const int jr = jr_sh;
+  const int c = s * Bl + jr;
+  const Merged a = merged[c];
   const bool resid = jr < gamma;
-  const float* tr = P.target + (size_t)(s * Bl + jr) * P.V;
-  const float* dr = resid ? P.draft + (size_t)(s * gamma + jr) * P.V : nullptr;
-  const double mT = rm[jr], zT = rz[jr];
-  const double mQ = resid ? rm[Bl + jr] : 0.0, zQ = resid ? rz[Bl + jr] : 1.0;
-
-  // contiguous chunk per thread; weights summed in vocab order inside a chunk
-  const int chunk = (P.V + kPQThreads - 1) / kPQThreads;
-  const int v0 = tid * chunk, v1 = min(v0 + chunk, P.V);
-  auto weight = [&](int v) -> double {
-    const double p = exp((double)tr[v] / P.temperature - mT) / zT;
-    if (!resid) return p;
-    const double q = exp((double)dr[v] / P.temperature - mQ) / zQ;
-    const double r = p - q;
-    return r > 0.0 ? r : 0.0;
-  };
-  double local = 0.0;
-  for (int v = v0; v < v1; ++v) local += weight(v);
-  csum[tid] = local;
-  __syncthreads();
-  if (tid == 0) {  // exclusive running sums of the chunk totals, in thread order
-    double run = 0.0;
-    for (int t = 0; t < kPQThreads; ++t) {
-      const double c = csum[t];
-      csum[t] = run;
-      run += c;
-    }
-    total_sh = run;
-  }
-  __syncthreads();
-  const double total = total_sh;
-  const double u2 = philox_uniform(P.seed, P.offset + jr, s, 1);
-  const double target = u2 * total;
-  const double before = csum[tid];
-  if (v0 < v1 && before <= target && target < before + local) {
-    double run = before;
-    int pick = v1 - 1;
-    for (int v = v0; v < v1; ++v) {
-      run += weight(v);
-      if (run > target) { pick = v; break; }
-    }
-    found = 1;
+  const Merged b = resid ? merged[nt + s * gamma + jr] : Merged{0.0, 1.0};
+  CdfRow R{P.target + (size_t)c * P.V, resid ? P.draft + (size_t)(s * gamma + jr) * P.V : nullptr,
+           a.m, a.z, b.m, b.z, inv_t};
+  const int pick = cdf_draw(P, R, sums, c, philox_uniform(P.seed, P.offset + jr, s, 1), loc, sh, dsh);
+  if (tid == 0) {
     P.bonus[s] = pick;
-    P.tau[s] = jr + 1;
-  }
-  __syncthreads();
-  if (tid == 0 && !found) {  // target at or beyond the total: last index
-    P.bonus[s] = P.V - 1;
     P.tau[s] = jr + 1;
   }
 }
 
-// ---------------------------------------------------------------------------
-// sampling-mode drafting: x_j ~ softmax(draft_logits[j] / T)
-// ---------------------------------------------------------------------------
-// One workgroup per drafted row: the row's slice statistics are merged, the
-// weights exp(x/T - m)/Z are summed per contiguous vocab chunk (one per
-// thread), the chunk totals are prefix-summed in thread order, and the
-// thread whose chunk brackets u * total finds the token by running its
-// chunk in vocab order. Here the launch's "target" rows are the draft rows
-// ([n_seqs * gamma] of them, P.Bl = gamma) and the output is the block.
-__global__ void __launch_bounds__(kPQThreads)
-draft_sample(VerifyLaunch P, const RowStat* part, int32_t* __restrict__ block, int Bl) {
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int gamma = P.Bl, s = row / gamma, j = row - s * gamma;
-  __shared__ double csum[kPQThreads];
-  __shared__ double stat_sh[3];
-  __shared__ int found;
-  if (tid == 0) {
-    const RowStat* p = part + (size_t)row * P.splits;
-    double M = -INFINITY;
-    for (int k = 0; k < P.splits; ++k) M = fmax(M, p[k].m);
-    double Z = 0.0;
-    for (int k = 0; k < P.splits; ++k)
-      if (p[k].m != -INFINITY) Z += p[k].z * exp(p[k].m - M);
-    stat_sh[0] = M;
-    stat_sh[1] = Z;
-    found = 0;
-  }
-  __syncthreads();
-  const double m = stat_sh[0], z = stat_sh[1];
-  const float* x = P.target + (size_t)row * P.V;
-  const int chunk = (P.V + kPQThreads - 1) / kPQThreads;
-  const int v0 = tid * chunk, v1 = min(v0 + chunk, P.V);
-  auto weight = [&](int v) -> double { return exp((double)x[v] / P.temperature - m) / z; };
-  double local = 0.0;
-  for (int v = v0; v < v1; ++v) local += weight(v);
-  csum[tid] = local;
-  __syncthreads();
-  if (tid == 0) {  // exclusive running sums of the chunk totals, in thread order
-    double run = 0.0;
-    for (int t = 0; t < kPQThreads; ++t) {
-      const double c = csum[t];
-      csum[t] = run;
-      run += c;
-    }
-    stat_sh[2] = run;
-  }
-  __syncthreads();
-  const double u = philox_uniform(P.seed, P.offset + j, s, 2);
-  const double target = u * stat_sh[2];
-  const double before = csum[tid];
-  int32_t* out = block + (size_t)s * Bl + 1 + j;
-  if (v0 < v1 && before <= target && target < before + local) {
-    double run = before;
-    int pick = v1 - 1;
-    for (int v = v0; v < v1; ++v) {
-      run += weight(v);
-      if (run > target) { pick = v; break; }
-    }
-    found = 1;
-    *out = pick;
-  }
-  __syncthreads();
-  if (tid == 0 && !found) *out = P.V - 1;  // target at or beyond the total: last index
+// sampling-mode drafting: one workgroup per drafted row r = s * gamma + j
+// (here P.target holds the draft logits, P.Bl = gamma); writes the block
+__global__ void __launch_bounds__(kCdfThreads)
+draft_pick(VerifyLaunch P, const Merged* merged, const double* sums, int32_t* __restrict__ block,
+           int Bl) {
+  const int r = blockIdx.x, gamma = P.Bl, s = r / gamma, j = r - s * gamma;
+  __shared__ double loc[kCdfThreads];
+  __shared__ int sh[3];
+  __shared__ double dsh[1];
+  const Merged a = merged[r];
+  CdfRow R{P.target + (size_t)r * P.V, nullptr, a.m, a.z, 0.0, 1.0, 1.0 / P.temperature};
+  const int pick = cdf_draw(P, R, sums, r, philox_uniform(P.seed, P.offset + j, s, 2), loc, sh, dsh);
+  if (threadIdx.x == 0) block[(size_t)s * Bl + 1 + j] = pick;
 }
 
 hipError_t launch_sample_draft(const VerifyLaunch& P, int32_t* block, int Bl, hipStream_t st) {
   RowStat* part = reinterpret_cast<RowStat*>(P.part);
+  Merged* merged = reinterpret_cast<Merged*>(P.part2);
+  double* sums = reinterpret_cast<double*>(merged + P.max_rows);
   const int rows = P.n_seqs * P.Bl;
   hipLaunchKernelGGL(row_softmax_part, dim3(P.splits, rows), dim3(256), 0, st, P, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(draft_sample, dim3(rows), dim3(kPQThreads), 0, st, P, part, block, Bl);
+  hipLaunchKernelGGL(cdf_slice_sums<false>, dim3(P.splits, rows), dim3(kCdfThreads), 0, st, P, part,
+                     merged, sums);
+  hipLaunchKernelGGL(draft_pick, dim3(rows), dim3(kCdfThreads), 0, st, P, merged, sums, block, Bl);
   return hipGetLastError();
 }
 
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st) {
   RowStat* part = reinterpret_cast<RowStat*>(P.part);
+  Merged* merged = reinterpret_cast<Merged*>(P.part2);
+  double* sums = reinterpret_cast<double*>(merged + P.max_rows);
   const int rows = P.n_seqs * P.Bl + P.n_seqs * (P.Bl - 1);
   hipLaunchKernelGGL(row_softmax_part, dim3(P.splits, rows), dim3(256), 0, st, P, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pq_accept_sample, dim3(P.n_seqs), dim3(kPQThreads), 0, st, P, part);
+  hipLaunchKernelGGL(cdf_slice_sums<true>, dim3(P.splits, P.n_seqs * P.Bl), dim3(kCdfThreads), 0, st,
+                     P, part, merged, sums);
+  hipLaunchKernelGGL(pq_pick, dim3(P.n_seqs), dim3(kCdfThreads), 0, st, P, merged, sums);
   return hipGetLastError();
 }
 
