@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libdflash.so")
 
 SOURCES = ["api.cpp", "skinny.hip", "attention.hip", "gemm.hip", "verify.hip", "rounds.hip",
            "calibrate.hip"]
-HEADERS = ["common.h", "launch.h"]
+HEADERS = ["common.h", "launch.h", "tiled_gemm.h"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -122,8 +122,9 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.act_h = take(Mmax * F * 2);
   L.act_l = take(Mmax * F * 2);
   L.lm_part = take(lm_tiles * Mmax * 8);
-  L.att_acc = take((size_t)kAttnSlotCap * G * 16 * c.head_dim * 4);
-  L.att_ml = take((size_t)kAttnSlotCap * G * 16 * 2 * 4);
+  const size_t slots = attn_slots(max_seqs, c.n_kv_heads);
+  L.att_acc = take(slots * G * 16 * c.head_dim * 4);
+  L.att_ml = take(slots * G * 16 * 2 * 4);
   L.vpart = take(2 * Mmax * kVerifyMaxSplits * 16);
   // per-row partial sums of y^2: 256-column tiles (tiled GEMM) or 32-column
   // groups (streaming path for few rows)
@@ -516,16 +517,21 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   L.lm_part = (uint64_t*)(ws + Ly.lm_part);
   L.att_acc = (float*)(ws + Ly.att_acc); L.att_ml = (float*)(ws + Ly.att_ml);
   L.split = split_ws(h);
+  L.gemm = gemm_ws(h);
   // split each sequence's keys so that the grid holds ~1024 waves (one per
   // SIMD) where the context allows, in whole 32-key chunks; each workgroup
   // runs G query-head waves, times 2 key columns when G <= 2
   const int pairs = n_seqs * c.n_kv_heads;
   const int G = c.n_heads / c.n_kv_heads;
   const int WG_waves = G <= 2 ? 2 * G : G;
-  const int max_splits = std::max(1, std::min(kAttnMaxSplits, kAttnSlotCap / pairs));
+  const int max_splits =
+      std::max(1, std::min(kAttnMaxSplits, attn_slots(h->max_seqs, c.n_kv_heads) / pairs));
   // (the last split also takes the remainder, so the block's own keys do not
-  // add a nearly empty split)
-  int splits = std::min(max_splits, std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves)));
+  // add a nearly empty split); long key ranges are split further when the
+  // grid is full already (many sequences), since a wave's chunks are serial
+  int splits = std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves));
+  splits = std::max(splits, (max_keys + kAttnMaxKeysPerSplit - 1) / kAttnMaxKeysPerSplit);
+  splits = std::min(max_splits, splits);
   int kps = std::max(32, max_keys / splits / 32 * 32);
   if (max_keys / kps > max_splits) kps = (int)align_up((size_t)((max_keys + max_splits - 1) / max_splits), 32);
   // never more workgroups than the target: with device-resident lengths

@@ -106,10 +106,25 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
     pr[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
     psum += pr[i];
   }
+  // the accumulators are rescaled only when some lane's running max moved
+  // (wave-uniform test; before the first chunk they are zero anyway)
+  if (__any(m_run > -INFINITY && alpha < 1.f)) {
+#pragma unroll
+    for (int h = 0; h < HT; ++h) acc[h] *= alpha;
+  }
   l_run = l_run * alpha + psum;
   m_run = m_new;
   bf16x8 pf, pfl;
   pack_split_bf16x8(pr, pf, pfl);
+  if (ke - c0 >= 32) {  // a whole chunk of valid keys (wave-uniform)
+#pragma unroll
+    for (int h = 0; h < HT; ++h) {
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, c.v[h]);
+      acc[h] = mfma16x16x32(vf, pf, acc[h]);
+      acc[h] = mfma16x16x32(vf, pfl, acc[h]);
+    }
+    return;
+  }
   // keys past the range contribute zero V, never NaN
   const int nvalid = ke - kl;
   uint32_t keep[4];
@@ -118,7 +133,6 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
     keep[i] = ((2 * i < nvalid) ? 0x0000ffffu : 0u) | ((2 * i + 1 < nvalid) ? 0xffff0000u : 0u);
 #pragma unroll
   for (int h = 0; h < HT; ++h) {
-    acc[h] *= alpha;
     u32x4 raw = c.v[h];
 #pragma unroll
     for (int i = 0; i < 4; ++i) raw[i] &= keep[i];

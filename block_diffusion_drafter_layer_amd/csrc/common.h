@@ -151,6 +151,12 @@ struct SeqTable {
   const int32_t* len_dev;
 };
 
+// 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
+// wave-uniform): a direct load, no register staging.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
 // context length of sequence s: the host value, or the device one clamped to
 // the buffer (a length past max_ctx would put the block's rows out of it)
 __device__ __forceinline__ int seq_len(const SeqTable& t, int s) {

@@ -1,27 +1,5 @@
-// Dense context-side GEMMs on bf16 MFMA: C[m][n] = sum_k A[m][k] B[n][k] with
-// both operands K-contiguous.
-//
-// Output tiles of 256 x BN (BN = 256 for the fusion, 320 for the injection),
-// eight waves (two per SIMD), each owning a block of 32x32x16 MFMA tiles:
-// 128 x 64 for BN = 256, 64 x 160 for BN = 320. Large tiles keep the global
-// load traffic at ~30 B/clk per CU at full MFMA rate, half of what the
-// CU's load path sustains (a 256 x 128 tile needs ~47 B/clk and is bound by
-// it). Operands go straight from global memory into LDS
-// (global_load_lds_dwordx4, no register staging) through a ring of 32-wide k
-// stages, 4 or 5 of them, so 3-4 stages are in flight while one is
-// multiplied. Each 1 KB load instruction covers sixteen 64-byte tile rows;
-// 16-byte chunk c of row r is stored at chunk c ^ ((r >> 2) & 3), so a
-// fragment read (sixteen consecutive lanes on sixteen rows, same chunk)
-// touches 64 distinct banks. Fragment reads for the next 16-wide k step are
-// issued before the MFMAs of the current one.
-//
-// Split K: when the tiles alone would leave CUs idle, S workgroups share a
-// tile, each over K/S. They sit on one XCD (workgroups go to XCDs round-robin
-// by id, and the S of a tile have ids 8 apart), so their partial sums meet in
-// that XCD's L2: each writes its partial, waits for the stores, and counts
-// itself in on the tile's counter; the last to arrive adds the others'
-// partials (read past the CU's L1) and runs the epilogue. Nobody waits for
-// anybody, so there is no co-residency requirement.
+// The context-side GEMMs of the prefill on the tiled MFMA kernel of
+// tiled_gemm.h.
 //
 // A is read through a segmented loader so the fusion GEMM never materialises
 // the concatenation of the target layers (A3-dflash tutorial, section 2.1.1:
@@ -35,40 +13,9 @@
 //            written into the KV-cache layout (txtmix article section 5).
 #include "common.h"
 #include "launch.h"
+#include "tiled_gemm.h"
 
 namespace dfl {
-
-namespace {
-constexpr int BM = 256, BK = 32;
-constexpr int kRow = BK * 2;         // bytes per tile row and stage
-constexpr int kLds = 160 * 1024;
-constexpr int kSlice = 64;           // epilogue rows per LDS pass
-
-template <int BN>
-struct TileCfg;
-template <>
-struct TileCfg<256> {
-  static constexpr int W = 8, WGM = 2, NS = 5;  // waves, waves along M, ring stages
-};
-template <>
-struct TileCfg<320> {
-  static constexpr int W = 8, WGM = 4, NS = 4;
-};
-}  // namespace
-
-struct GemmA {
-  const bf16_t* seg[kMaxFeat];
-  int64_t ld;      // row stride of every segment (elements)
-  int seg_k;       // k extent of one segment
-  int M, K;
-};
-
-// split-K bookkeeping of one launch
-struct GemmSplit {
-  int S;           // workgroups per tile
-  float* part;     // [tile][S][BM * BN] fp32 partials in MFMA register order
-  int32_t* ctr;    // [tile] arrival counters, zero between launches
-};
 
 struct EpiFuse {
   struct P {
@@ -202,346 +149,6 @@ struct EpiInject {
   }
 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// D[i][j] += sum_k A[i][k] B[k][j], 32x32x16, bf16 inputs, fp32 accumulate.
-// Lane l supplies A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32] and
-// holds D[8*(v/4) + 4*(l/32) + v%4][l%32] in item v.
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// One 16-byte fragment read at addr + OFF, issued without waiting. Inline
-// assembly: the compiler's wait-count pass would otherwise treat it as
-// aliasing the direct loads in flight into the other stages and drain those
-// first. Reads are ordered among themselves (volatile) and complete in order.
-template <int OFF>
-__device__ __forceinline__ void ds_frag(u32x4& f, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(addr), "n"(OFF) : "memory");
-}
-
-// Wait until at most N LDS reads are outstanding; the fragments passed through
-// become usable only after this point.
-template <int N>
-__device__ __forceinline__ void frag_wait(u32x4 (&f)[6]) {
-  asm volatile("s_waitcnt lgkmcnt(%6)"
-               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5])
-               : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void frag_wait(u32x4 (&f)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(%8)"
-               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
-                 "+v"(f[6]), "+v"(f[7])
-               : "n"(N));
-}
-template <int N>
-__device__ __forceinline__ void frag_wait(u32x4 (&f)[7]) {
-  asm volatile("s_waitcnt lgkmcnt(%7)"
-               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
-                 "+v"(f[6])
-               : "n"(N));
-}
-
-// the TI A fragments (32-row blocks 2 KB apart) then the TJ B fragments
-template <int TI, int TJ>
-__device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint32_t b) {
-  ds_frag<0>(f[0], a);
-  ds_frag<2048>(f[1], a);
-  if constexpr (TI > 2) {
-    ds_frag<4096>(f[2], a);
-    ds_frag<6144>(f[3], a);
-  }
-  ds_frag<0>(f[TI], b);
-  ds_frag<2048>(f[TI + 1], b);
-  if constexpr (TJ > 2) {
-    ds_frag<4096>(f[TI + 2], b);
-    ds_frag<6144>(f[TI + 3], b);
-  }
-  if constexpr (TJ > 4) ds_frag<8192>(f[TI + 4], b);
-}
-
-// 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
-// wave-uniform).
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
-// s_waitcnt immediate: vmcnt <= n with the other counters open
-#define DFL_VM(n) ((((n) & 15) | (((n) >> 4) << 14)) | 0xF70)
-
-template <int N>
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(DFL_VM(N)); }
-
-// wait until at most `stages` whole stages of this wave's loads (L each) are
-// in flight
-template <int L>
-__device__ __forceinline__ void wait_stages(int stages) {
-  switch (stages) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<L>(); break;
-    case 2: wait_vm<2 * L>(); break;
-    default: wait_vm<3 * L>(); break;
-  }
-}
-
-// Workgroup -> (tile, split). With a multiple of 8 tiles, XCD x (workgroup id
-// % 8) takes a contiguous chunk of tiles, walked in groups of 4 tile rows
-// column by column, so the workgroups an XCD runs share A row blocks and B
-// column blocks through its L2; the S splits of a tile are consecutive on
-// that XCD.
-__device__ __forceinline__ void tile_of(int id, int tm, int tn, int S, int& rt, int& ct, int& s) {
-  const int nt = tm * tn;
-  int t;
-  if ((nt & 7) == 0) {
-    const int local = id >> 3;
-    s = local % S;
-    t = (id & 7) * (nt >> 3) + local / S;
-  } else {
-    s = id % S;
-    t = id / S;
-  }
-  constexpr int GR = 4;
-  const int g = t / (GR * tn);
-  const int rows = min(GR, tm - g * GR);
-  const int i = t - g * GR * tn;
-  rt = g * GR + i % rows;
-  ct = i / rows;
-}
-
-template <int BN, class Epi>
-__global__ void __launch_bounds__(TileCfg<BN>::W * 64)
-ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
-  using Cfg = TileCfg<BN>;
-  constexpr int kWaves = Cfg::W;
-  constexpr int NS = Cfg::NS;
-  constexpr int WGM = Cfg::WGM, WGN = kWaves / WGM;
-  constexpr int WM = BM / WGM, WN = BN / WGN;
-  constexpr int TI = WM / 32, TJ = WN / 32;
-  constexpr int kStage = (BM + BN) * kRow;
-  constexpr int kLoadsA = BM / 16 / kWaves;           // A loads per wave and stage
-  constexpr int kLoadsBTot = BN / 16;                 // B loads per stage
-  constexpr int kLoadsBMax = (kLoadsBTot + kWaves - 1) / kWaves;
-  static_assert(NS * kStage <= kLds, "ring fits in LDS");
-  static_assert(kSlice * (BN + 8) * 4 + 16 * BN <= NS * kStage,
-                "epilogue slice and column table fit in the ring");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * kStage];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w / WGN, wn = w % WGN;
-  const int tm = (a.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  int rt, ct, sidx;
-  tile_of(blockIdx.x, tm, tn, sp.S, rt, ct, sidx);
-  const int m0 = rt * BM, n0 = ct * BN;
-  const int KT_all = a.K / BK;
-  const int kt_per = (KT_all + sp.S - 1) / sp.S;
-  const int kt0 = sidx * kt_per;
-  const int KT = max(0, min(KT_all - kt0, kt_per));
-
-  // Loads: instruction b covers tile rows 16b .. 16b+15 (of A, then of B);
-  // wave w issues A instructions w, w + 8 and B instructions w, w + 8, ...
-  // Lane l fetches row 16b + l/4, chunk (l%4) ^ ((l/16) & 3), and lands at
-  // byte 16 l of the instruction's kilobyte.
-  const int lrow = lane >> 2;
-  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
-  const int nb = (kLoadsBTot % kWaves == 0 || w < kLoadsBTot % kWaves) ? kLoadsBMax : kLoadsBMax - 1;
-  int64_t aoff[kLoadsA];
-  const bf16_t* bptr[kLoadsBMax];
-#pragma unroll
-  for (int q = 0; q < kLoadsA; ++q) {
-    int m = m0 + 16 * (w + kWaves * q) + lrow;
-    m = m < a.M ? m : a.M - 1;
-    aoff[q] = (int64_t)m * a.ld + lchunk;
-  }
-#pragma unroll
-  for (int q = 0; q < kLoadsBMax; ++q) {
-    int n = n0 + 16 * (w + kWaves * q) + lrow;
-    n = n < N ? n : N - 1;
-    bptr[q] = Epi::wrow(p, n) + lchunk;
-  }
-  auto issue = [&](int kt) {
-    uint8_t* st = smem + (kt % NS) * kStage;
-    const int k0 = (kt0 + kt) * BK;
-    const int sg = k0 / a.seg_k;
-    const bf16_t* base = a.seg[sg] + (k0 - sg * a.seg_k);
-#pragma unroll
-    for (int q = 0; q < kLoadsA; ++q) dma16(base + aoff[q], st + (w + kWaves * q) * 1024);
-#pragma unroll
-    for (int q = 0; q < kLoadsBMax; ++q)
-      if (q < nb) dma16(bptr[q] + k0, st + BM * kRow + (w + kWaves * q) * 1024);
-  };
-  auto wait_tiles = [&](int stages) {  // this wave's loads per stage differ by wave
-    if (nb == kLoadsBMax) wait_stages<kLoadsA + kLoadsBMax>(stages);
-    else wait_stages<kLoadsA + kLoadsBMax - 1>(stages);
-  };
-
-  // fragment addresses: lane l reads row l % 32 of a 32-row block at chunk
-  // (2 kk + l / 32) ^ ((l / 4) & 3), kk the 16-wide step within the stage
-  const uint32_t sbase = (uint32_t)(uintptr_t)smem;
-  const int fr = lane & 31;
-  uint32_t foff[2];
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    foff[kk] = fr * kRow + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 4);
-  const uint32_t a_f = sbase + (uint32_t)(wm * WM) * kRow;
-  const uint32_t b_f = sbase + (uint32_t)(BM * kRow) + (uint32_t)(wn * WN) * kRow;
-
-  f32x16 acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // Per stage t (ring slot t % NS): two 16-wide k steps; each issues the
-  // next step's fragment reads before its own MFMAs. The second step waits
-  // for this wave's loads of stage t+1 and meets the other waves at a
-  // barrier: past it, stage t+1 is in LDS and nobody reads slot (t-1) % NS
-  // any more, so stage t+NS-1 is loaded into it, and stage t+1's first
-  // fragments are read under the MFMAs of stage t's second step. (A plain
-  // barrier: a fence would also wait for the loads still in flight.)
-  if (KT > 0) {
-    const int pre = min(KT, NS - 1);
-    for (int t = 0; t < pre; ++t) issue(t);
-    wait_tiles(pre - 1);
-    __builtin_amdgcn_s_barrier();
-    u32x4 f[2][TI + TJ];
-    frag_issue<TI, TJ>(f[0], a_f + foff[0], b_f + foff[0]);
-    for (int kt = 0; kt < KT; ++kt) {
-      const uint32_t st = (uint32_t)((kt % NS) * kStage);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 0) {
-          frag_issue<TI, TJ>(f[1], a_f + st + foff[1], b_f + st + foff[1]);
-          frag_wait<TI + TJ>(f[0]);
-        } else {
-          frag_wait<0>(f[1]);
-          if (kt + 1 < KT) {
-            // stages issued so far: up to min(kt + NS - 2, KT - 1)
-            wait_tiles(min(NS - 3, KT - kt - 2));
-            __builtin_amdgcn_s_barrier();
-            if (kt + NS - 1 < KT) issue(kt + NS - 1);
-            const uint32_t sn = (uint32_t)(((kt + 1) % NS) * kStage);
-            frag_issue<TI, TJ>(f[0], a_f + sn + foff[0], b_f + sn + foff[0]);
-          }
-        }
-        // the MFMAs go out at raised priority, so that the other wave on the
-        // SIMD issues its reads and loads around them rather than the two
-        // waves' MFMA bursts queueing behind each other
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j)
-            acc[i][j] = mfma32x32x16(__builtin_bit_cast(bf16x8, f[kk][i]),
-                                     __builtin_bit_cast(bf16x8, f[kk][TI + j]), acc[i][j]);
-        __builtin_amdgcn_s_setprio(0);
-        // keep this step's MFMAs ahead of the next step's reads and waits
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-
-  if (sp.S > 1) {
-    // publish this split's partial (lane-major: 1 KB per store instruction),
-    // then count in; the last to arrive sums every partial in split order
-    const int tile = rt * tn + ct;
-    float* mine = sp.part + ((size_t)tile * sp.S + sidx) * (BM * BN);
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(mine + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
-        }
-    __builtin_amdgcn_s_waitcnt(DFL_VM(0));  // the partial has reached L2
-    __syncthreads();  // (also: every wave is done with the ring)
-    int32_t* arrived = reinterpret_cast<int32_t*>(smem);
-    if (tid == 0)
-      *arrived = __hip_atomic_fetch_add(sp.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (*arrived != sp.S - 1) return;
-    if (tid == 0) __hip_atomic_store(sp.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the other splits' partials are in this XCD's L2; drop any stale copy
-    // from this CU's L1 before reading them
-    asm volatile("buffer_inv sc0" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        f32x16 sum;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sum[v] = 0.f;
-        for (int s = 0; s < sp.S; ++s) {
-          const float* src = sp.part + ((size_t)tile * sp.S + s) * (BM * BN);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(
-                src + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4);
-            sum[4 * q] += v[0];
-            sum[4 * q + 1] += v[1];
-            sum[4 * q + 2] += v[2];
-            sum[4 * q + 3] += v[3];
-          }
-        }
-        acc[i][j] = sum;
-      }
-  }
-
-  // epilogue: 64-row slices through LDS
-  constexpr int CLD = BN + 8;
-  float* C = reinterpret_cast<float*>(smem);
-  __syncthreads();  // every wave is done with the ring
-#pragma unroll
-  for (int sl = 0; sl < BM / kSlice; ++sl) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int r0 = wm * WM + i * 32;
-      if (r0 / kSlice != sl) continue;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = r0 % kSlice + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          C[r * CLD + wn * WN + j * 32 + fr] = acc[i][j][v];
-        }
-    }
-    __syncthreads();
-    Epi::template run<BN>(p, C, CLD, m0 + sl * kSlice, n0, a.M);
-    __syncthreads();
-  }
-}
-
-// Split count: the smallest S in {1, 2, 4} that gives the grid at least 256
-// workgroups, when the tiles are a multiple of 8 (so the splits of a tile
-// share an XCD) and each split keeps at least 32 k stages.
-static int choose_split(int tiles, int K) {
-  if (tiles % 8) return 1;
-  int S = 1;
-  while (S < kGemmMaxSplit && tiles * S < 256 && K / BK / (2 * S) >= 32) S *= 2;
-  return S;
-}
-
-template <int BN, class Epi>
-static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, const GemmWs& ws,
-                               hipStream_t st) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  GemmSplit sp;
-  sp.S = choose_split(tiles, a.K);
-  if (sp.S > 1 && (!ws.part || !ws.ctr || (size_t)tiles * sp.S * BM * BN > ws.part_floats ||
-                   tiles > ws.n_ctr))
-    sp.S = 1;
-  sp.part = ws.part;
-  sp.ctr = ws.ctr;
-  hipLaunchKernelGGL((ctx_gemm<BN, Epi>), dim3(tiles * sp.S), dim3(TileCfg<BN>::W * 64), 0, st, a, p,
-                     N, sp);
-  return hipGetLastError();
-}
-
 size_t ctx_gemm_part_floats() { return (size_t)256 * BM * 320; }
 
 // H_t row m = bf16(y[m] * rsqrt(mean(y[m]^2) + eps) * gain): the fp32
@@ -576,6 +183,7 @@ hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st) {
   GemmA a;
   for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = i < F.n_feat ? F.feats[i] : F.feats[0];
   a.ld = F.ld; a.seg_k = F.D; a.M = F.T; a.K = F.n_feat * F.D;
+  gemm_a_plain(a);
   EpiFuse::P p;
   p.w = F.w_c; p.K = a.K; p.N = F.D; p.y = F.y; p.ssq = F.ssq;
   p.n_tiles = (F.D + kFuseTileN - 1) / kFuseTileN;
@@ -594,6 +202,7 @@ hipError_t launch_inject(const InjectLaunch& I, hipStream_t st) {
   GemmA a;
   for (int i = 0; i < kMaxFeat; ++i) a.seg[i] = I.ctx;
   a.ld = I.D; a.seg_k = I.D; a.M = I.T; a.K = I.D;
+  gemm_a_plain(a);
   EpiInject::P p;
   for (int i = 0; i < kMaxLayers; ++i) {
     p.wk[i] = i < I.L ? I.wk[i] : I.wk[0];

@@ -13,7 +13,13 @@ namespace dfl {
 constexpr int kMaxLayers = 16;
 constexpr int kMaxFeat = 8;
 constexpr int kAttnMaxSplits = 128;
-constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots
+constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots, at least
+constexpr int kAttnMinSplitsPerPair = 8;  // slots per (sequence, kv head) the workspace keeps
+constexpr int kAttnMaxKeysPerSplit = 512; // longer key ranges are split when slots allow
+inline int attn_slots(int max_seqs, int n_kv_heads) {
+  const int s = max_seqs * n_kv_heads * kAttnMinSplitsPerPair;
+  return s > kAttnSlotCap ? s : kAttnSlotCap;
+}
 constexpr int kVerifyMaxSplits = 64;
 constexpr int kFuseTileN = 256;     // output columns per fusion GEMM tile
 constexpr int kGemmMaxSplit = 4;    // workgroups sharing one context-GEMM tile
@@ -55,11 +61,12 @@ struct DraftLaunch {
   bf16_t *q, *q_lo;         // [M][Hq*hd] query after RoPE, hi/lo
   bf16_t *ob_h, *ob_l;      // [M][Hq*hd]
   bf16_t *act_h, *act_l;    // [M][F]
-  uint64_t* lm_part;        // [ceil(V/32)][M]
+  uint64_t* lm_part;        // [ceil(V/32)][M] argmax keys per column block and row
   float* att_acc;           // [slots*G][16][hd]
   float* att_ml;            // [slots*G][16][2]
   int att_splits, att_keys_per_split;
   SplitWs split;
+  GemmWs gemm;              // the tiled GEMM's split-K scratch (batches of more than 64 rows)
 };
 
 int skinny_tile_cols();

@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "tiled_gemm.h"
 
 namespace dfl {
 
@@ -96,8 +97,8 @@ struct EpiQKV {
     }
     return p.wv + (size_t)(vc8 - qd - kvd + r8) * p.D;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs,
                              int vc0, int m0, int M) {
     const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
@@ -160,8 +161,8 @@ struct EpiResid {
   __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
     return p.w + (size_t)(vc8 + r8) * p.K;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float*,
                              int vc0, int m0, int M) {
     static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
     for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
@@ -204,8 +205,8 @@ struct EpiSwiglu {
   __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
     return ((vc8 & 8) ? p.wu : p.wg) + (size_t)((vc8 >> 4) * 8 + r8) * p.K;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs,
                              int vc0, int m0, int M) {
     constexpr int NG = VC / 16;
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
@@ -235,8 +236,8 @@ struct EpiLM {
   __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
     return wrow(p, vc8 + r8);
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float* rs,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs,
                              int vc0, int m0, int M) {
     for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
       const int ml = e / VC, c = e % VC;
@@ -274,8 +275,8 @@ struct EpiFuseRows {
   __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
     return p.w + (size_t)(vc8 + r8) * p.K;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
                              int M) {
     static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
     for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
@@ -326,8 +327,8 @@ struct EpiInjectRows {
     }
     return p.wv[i] + (size_t)(r - kvd + r8) * p.D;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
                              int M) {
     const int kvd = p.Hkv * p.hd;
     const size_t plane = (size_t)p.cap * p.hd;
@@ -391,8 +392,8 @@ struct EpiAppendRows {
     }
     return p.wv[i] + (size_t)(r - kvd + r8) * p.D;
   }
-  template <int ROWS, int VC>
-  __device__ static void run(const P& p, float (*tile)[VC + 1], const float*, int vc0, int m0,
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
                              int M) {
     const int kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
@@ -648,12 +649,6 @@ __device__ __forceinline__ void ring_read8(u32x4 (&b)[8], const uint8_t* row, in
       : "memory");
 }
 
-// 16 bytes per lane from global memory to LDS at lds + 16 * lane (lds is
-// wave-uniform). A plain function: inside a kernel template the builtin
-// keeps the host pass from emitting the launch stub.
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
 
 // wait until at most n direct loads (whole slots) are in flight
 __device__ __forceinline__ void wait_vm_slots(int slots_after) {
@@ -1060,11 +1055,78 @@ bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
   return (size_t)((n_vcols + 31) / 32) * 2 * ks * 256 <= ws.part_floats;
 }
 
+// A draft epilogue on the tiled MFMA GEMM, for batches of more than 64
+// rows: the weights are read once per 256-row tile instead of once per
+// 64-row block. The activations' bf16 hi and lo halves are the A operand's
+// two k segments against the weight rows read twice (B's k wraps at K), so
+// one GEMM over 2K gives hi.W + lo.W. The slice's RMSNorm row scales come
+// from the producer's per-32-column sums of x^2, then the epilogue runs on
+// the 64-row slice in place.
+template <class E>
+struct EpiTiled {
+  struct P {
+    typename E::P ep;
+    const float* ssq;  // optional: per-row partial sums of x^2 [rows_in][ssq_ld]
+    int ssq_ld, K;
+    float eps;
+    int a_group, a_stride, a_off;  // output row -> input row (as SkinnyA)
+  };
+  __device__ static const bf16_t* wrow(const P& p, int n) { return E::wrow(p.ep, n); }
+  // C: the slice, row pitch BN + 8 (the tiled kernel's); 64 floats of LDS
+  // after it hold the row scales
+  template <int BN>
+  __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
+    float* tile = const_cast<float*>(C);
+    float* rs = tile + kSlice * ld;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    for (int r = w; r < kSlice; r += nw) {
+      float s = 0.f;
+      const int m = m0 + r;
+      if (p.ssq && m < M) {
+        const int mi = (m / p.a_group) * p.a_stride + p.a_off + m % p.a_group;
+        const float* q = p.ssq + (size_t)mi * p.ssq_ld;
+        for (int g = lane; g < p.ssq_ld; g += 64) s += q[g];
+        s = wave_sum(s);
+      }
+      if (lane == 0) rs[r] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
+    }
+    __syncthreads();
+    E::template run<kSlice, BN, BN + 8>(p.ep, reinterpret_cast<float (*)[BN + 8]>(tile), rs, n0, m0, M);
+  }
+};
+
+constexpr int kTallBN = 256;
+
+template <class Epi>
+hipError_t launch_tall(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const GemmWs& gw,
+                       hipStream_t st) {
+  GemmA g;
+  g.seg[0] = a.xh;
+  g.seg[1] = a.xl;
+  for (int i = 2; i < kMaxFeat; ++i) g.seg[i] = a.xh;
+  g.ld = a.lda; g.seg_k = a.K; g.M = a.M; g.K = 2 * a.K; g.b_k = a.K;
+  g.a_group = a.a_group; g.a_stride = a.a_stride; g.a_off = a.a_off;
+  typename EpiTiled<Epi>::P p;
+  p.ep = ep; p.ssq = a.ssq; p.ssq_ld = a.ssq_ld; p.K = a.K; p.eps = a.eps;
+  p.a_group = a.a_group; p.a_stride = a.a_stride; p.a_off = a.a_off;
+  // the draft's few-tile products (o_proj, down at 512 rows: 32 tiles) split
+  // K up to 8 ways
+  return launch_tiled<kTallBN, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 16);
+}
+
+// true when launch_skinny takes the tiled GEMM for this shape: more rows
+// than one register-streaming block of 64 (which would stream the weights
+// once per block)
+bool uses_tall(const SkinnyA& a, const GemmWs* tall) {
+  return tall && a.M > 64 && a.xl && a.K % 32 == 0 && a.seg_k == a.K;
+}
+
 template <class Epi, bool LO = true>
 hipError_t launch_skinny(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
-                         const SplitWs& ws, hipStream_t st) {
+                         const SplitWs& ws, hipStream_t st, const GemmWs* tall = nullptr) {
   int ks;
   if (uses_stream(a, n_vcols, ws, ks)) return launch_stream<Epi, LO>(a, ep, n_vcols, ks, ws, st);
+  if (LO && uses_tall(a, tall)) return launch_tall<Epi>(a, ep, n_vcols, *tall, st);
   if (a.M <= 16) return launch_cfg<Epi, LO, 1, 4, 4>(a, ep, n_vcols, ws, st);
   if (a.M <= 32) return launch_cfg<Epi, LO, 2, 4, 2>(a, ep, n_vcols, ws, st);
   // more rows: 64-row blocks over grid.y, each streaming the weights again
@@ -1141,7 +1203,7 @@ hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
   p.wq = wq; p.wk = wk; p.wv = wv; p.D = L.D; p.Hq = L.Hq; p.Hkv = L.Hkv;
   p.hd = L.hd; p.Bl = L.Bl; p.layer = layer; p.log2_theta = L.log2_theta;
   p.q_out = L.q; p.q_lo = L.q_lo; p.seqs = *L.seqs;
-  return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, L.split, st);
+  return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, L.split, st, &L.gemm);
 }
 
 hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
@@ -1151,7 +1213,7 @@ hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
   EpiResid::P p;
   p.w = w; p.K = K; p.D = L.D; p.x = L.x; p.xh = L.xh; p.xl = L.xl;
   p.gain = gain_next; p.ssq = L.ssq; p.hidden = hidden; p.n_vcols = L.D;
-  return launch_skinny<EpiResid>(a, p, L.D, L.split, st);
+  return launch_skinny<EpiResid>(a, p, L.D, L.split, st, &L.gemm);
 }
 
 hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
@@ -1159,7 +1221,7 @@ hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* w
   SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
   EpiSwiglu::P p;
   p.wg = wg; p.wu = wu; p.K = L.D; p.F = L.F; p.ah = L.act_h; p.al = L.act_l; p.n_vcols = 2 * L.F;
-  return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, L.split, st);
+  return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, L.split, st, &L.gemm);
 }
 
 namespace {
@@ -1168,6 +1230,7 @@ struct LmPlan {
   EpiLM::P p;
   int M_lm;
   bool stream;
+  bool tall;  // the tiled GEMM (more than 64 rows)
   int ks;   // K slices of the LDS-staged kernel
   int vc;   // vocabulary columns per argmax key
 };
@@ -1181,7 +1244,8 @@ LmPlan lm_plan(const DraftLaunch& L, const bf16_t* w_lm, float* logits) {
   q.p.w = w_lm; q.p.K = L.D; q.p.V = L.V; q.p.logits = logits; q.p.part = L.lm_part;
   q.ks = 0;
   q.stream = uses_stream(q.a, L.V, L.split, q.ks);
-  q.vc = q.stream ? 256 : q.M_lm <= 16 ? 128 : q.M_lm <= 32 ? 64 : 32;
+  q.tall = !q.stream && uses_tall(q.a, &L.gemm);
+  q.vc = q.stream ? 256 : q.tall ? kTallBN : q.M_lm <= 16 ? 128 : q.M_lm <= 32 ? 64 : 32;
   return q;
 }
 }  // namespace
@@ -1195,6 +1259,7 @@ hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
                        L.D / q.ks, L.split.part);
     return hipGetLastError();
   }
+  if (q.tall) return launch_tall<EpiLM>(q.a, q.p, L.V, L.gemm, st);
   // the register-streaming kernel never splits the LM head's K (its vocab
   // gives thousands of column blocks); its epilogue leaves one argmax key per
   // column block and row
