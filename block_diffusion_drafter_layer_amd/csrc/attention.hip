@@ -261,6 +261,168 @@ attn_split(AttnArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// head_dim 128, G = 4 or 8 query heads per kv head: the workgroup's waves
+// share every 32-key chunk through LDS. Each chunk (K rows, then V^T rows:
+// 16 KB) is loaded once by direct global->LDS loads into a ring of
+// kRingSlots slots, kRingSlots - 1 chunks in flight, instead of once per
+// wave into registers with one chunk in flight. Each wave issues 16 / G of a
+// chunk's sixteen 1 KB loads; a barrier per chunk makes the chunk visible to
+// all waves and frees the slot read in the previous step. In a K slot,
+// 16-byte chunk c of key row k sits at c ^ kswz(k), kswz(k) = (k & 3) |
+// ((k >> 3) & 3) << 2: the sixteen keys an A-fragment read touches map to
+// sixteen distinct bank groups. In a V slot (dim rows of 64 bytes), key chunk
+// kc of dim d sits at kc ^ ((d >> 2) & 3). The math per chunk is
+// process_chunk's. Past the split's last chunk the loads re-read that chunk
+// (in-bounds, unread), so every wait is an exact count.
+constexpr int kRingSlots = 4;
+constexpr int kSlotBytes = 2 * 32 * 128 * 2;  // K rows then V^T rows of one chunk
+
+__device__ __forceinline__ int kswz(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vm() {
+  // vmcnt <= N, the other counters open
+  __builtin_amdgcn_s_waitcnt(((N & 15) | ((N >> 4) << 14)) | 0xF70);
+}
+
+// 16 fragment reads of one slot (8 K, 8 V), complete on return, in one
+// inline-assembly block (the compiler would otherwise wait for every direct
+// load in flight into the other slots before each read, and must not touch
+// the results before the closing wait). K rows of score tile 1 sit 1 KB after
+// those of tile 0 and V rows of dim tile h 1 KB * h after tile 0, so four K
+// addresses and one V address with immediate offsets cover all reads.
+__device__ __forceinline__ void slot_read(Chunk<128>& c, uint32_t base, const uint32_t (&ko)[4],
+                                          uint32_t vo) {
+  u32x4 k[8], v[8];
+  asm volatile(
+      "ds_read_b128 %0, %16\n\t"
+      "ds_read_b128 %1, %17\n\t"
+      "ds_read_b128 %2, %18\n\t"
+      "ds_read_b128 %3, %19\n\t"
+      "ds_read_b128 %4, %16 offset:1024\n\t"
+      "ds_read_b128 %5, %17 offset:1024\n\t"
+      "ds_read_b128 %6, %18 offset:1024\n\t"
+      "ds_read_b128 %7, %19 offset:1024\n\t"
+      "ds_read_b128 %8, %20\n\t"
+      "ds_read_b128 %9, %20 offset:1024\n\t"
+      "ds_read_b128 %10, %20 offset:2048\n\t"
+      "ds_read_b128 %11, %20 offset:3072\n\t"
+      "ds_read_b128 %12, %20 offset:4096\n\t"
+      "ds_read_b128 %13, %20 offset:5120\n\t"
+      "ds_read_b128 %14, %20 offset:6144\n\t"
+      "ds_read_b128 %15, %20 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+        "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(base + ko[0]), "v"(base + ko[1]), "v"(base + ko[2]), "v"(base + ko[3]),
+        "v"(base + vo)
+      : "memory");
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) c.kf[t][ks] = __builtin_bit_cast(bf16x8, k[t * 4 + ks]);
+#pragma unroll
+  for (int h = 0; h < 8; ++h) c.v[h] = v[h];
+}
+
+template <int G>
+__global__ void __launch_bounds__(G * 64)
+attn_lds(AttnArgs p) {
+  constexpr int HD = 128, KSTEPS = 4, HT = 8;
+  constexpr int NQ = 16 / G;  // load instructions per wave and chunk
+  static_assert(16 % G == 0, "whole load instructions per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kRingSlots][kSlotBytes];
+  const int split = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int a = g * G + w;
+  const int ql = lane & 15, lg = lane >> 4;
+  const SeqDesc sd = p.seqs.s[s];
+  const int kb = split * p.kps;
+  const size_t plane = (size_t)sd.cap * HD;
+  const bf16_t* kbase = sd.kv + (size_t)((2 * p.layer) * p.Hkv + g) * plane;
+  const bf16_t* vbase = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + g) * plane;
+
+  // chunk j of the split into slot j % kRingSlots; jj: the chunk actually read
+  auto issue = [&](int j, int jj) {
+    const int c0 = kb + 32 * jj;
+    uint8_t* slot = &ring[j % kRingSlots][0];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int q = w * NQ + u;  // wave-uniform
+      if (q < 8) {               // K rows 4q .. 4q+3, 256 bytes each
+        const int kl = 4 * q + (lane >> 4);
+        int key = c0 + kl;
+        key = key < sd.cap ? key : sd.cap - 1;
+        dma16(kbase + (size_t)key * HD + (((lane & 15) ^ kswz(kl)) << 3), slot + q * 1024);
+      } else {                   // V^T rows (dims) 16(q-8) .. +15, 64 bytes each
+        const int d = 16 * (q - 8) + (lane >> 2);
+        int key0 = c0 + 8 * ((lane & 3) ^ ((d >> 2) & 3));
+        key0 = key0 < sd.cap ? key0 : sd.cap - 8;
+        dma16(vbase + (size_t)d * sd.cap + key0, slot + q * 1024);
+      }
+    }
+  };
+  // queries and the context length first: a wait for them then leaves the
+  // ring's loads, issued after them, in flight
+  bf16x8 qf[KSTEPS], qfl[KSTEPS];
+  const bool qv = ql < p.Bl;
+  const size_t qoff = ((size_t)(s * p.Bl + (qv ? ql : 0)) * p.Hq + a) * HD + 8 * lg;
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = qv ? ld_bf16x8(p.q + qoff + ks * 32) : zero_bf16x8();
+    qfl[ks] = qv ? ld_bf16x8(p.q_lo + qoff + ks * 32) : zero_bf16x8();
+  }
+  const int n_keys = seq_len(p.seqs, s) + p.Bl;
+  constexpr int R = kRingSlots;
+#pragma unroll
+  for (int j = 0; j < R - 1; ++j) issue(j, j);
+  attn_wait_vm<NQ * (R - 1)>();  // queries and length in, the ring's loads in flight
+
+  // fragment offsets inside a slot (lane-dependent, the same for every
+  // slot): A row ql of score tile 0 is key kl, that of tile 1 key kl + 4
+  // (same swizzle, 1 KB further); the V row of dim 16 h + ql is 1 KB * h
+  // after that of dim ql (same swizzle)
+  uint32_t ko[KSTEPS];
+  const int kl0 = 8 * (ql >> 2) + (ql & 3);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) ko[ks] = kl0 * 256 + (((4 * ks + lg) ^ kswz(kl0)) << 4);
+  const uint32_t vo = 8192 + ql * 64 + ((lg ^ ((ql >> 2) & 3)) << 4);
+
+  const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);
+  const int nch = ke > kb ? (ke - kb + 31) / 32 : 0;
+
+  f32x4 acc[HT];
+#pragma unroll
+  for (int h = 0; h < HT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[0][0];
+  for (int i = 0; i < nch; ++i) {
+    // this wave's loads of chunk i are done (R - 2 chunks issued after it),
+    // then everyone's; past the barrier nobody reads slot (i - 1) % R
+    attn_wait_vm<NQ * (R - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(i + R - 1, min(i + R - 1, nch - 1));
+    Chunk<HD> c;
+    slot_read(c, ring0 + (uint32_t)((i % R) * kSlotBytes), ko, vo);
+    process_chunk<HD>(c, kb + 32 * i, ke, qf, qfl, p.scale_log2, lg, m_run, l_run, acc);
+  }
+  // no direct load may still be writing the ring when the workgroup ends
+  attn_wait_vm<0>();
+  l_run += __shfl_xor(l_run, 16, kWave);
+  l_run += __shfl_xor(l_run, 32, kWave);
+  const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
+  float* out = p.acc + slot * 16 * HD + (size_t)ql * HD;
+#pragma unroll
+  for (int h = 0; h < HT; ++h)
+    *reinterpret_cast<f32x4*>(out + h * 16 + 4 * lg) = acc[h];
+  if (lg == 0) {
+    p.ml[(slot * 16 + ql) * 2 + 0] = m_run;
+    p.ml[(slot * 16 + ql) * 2 + 1] = l_run;
+  }
+}
+
 // One workgroup per (block row, query head, sequence), one thread per output
 // dim (at least one wave). The first kMergeBatch accumulator values are
 // requested first, from clamped indices so that the loads are straight-line
@@ -337,8 +499,18 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   switch (G) {
     case 1: hipLaunchKernelGGL((attn_split<HD, 1, 2, true>), grid, dim3(128), 0, st, p); break;
     case 2: hipLaunchKernelGGL((attn_split<HD, 2, 2, true>), grid, dim3(256), 0, st, p); break;
-    case 4: hipLaunchKernelGGL((attn_split<HD, 4, 1, true>), grid, dim3(256), 0, st, p); break;
-    case 8: hipLaunchKernelGGL((attn_split<HD, 8, 1, P2>), grid, dim3(512), 0, st, p); break;
+    case 4:
+      if constexpr (HD == 128)
+        hipLaunchKernelGGL((attn_lds<4>), grid, dim3(256), 0, st, p);
+      else
+        hipLaunchKernelGGL((attn_split<HD, 4, 1, true>), grid, dim3(256), 0, st, p);
+      break;
+    case 8:
+      if constexpr (HD == 128)
+        hipLaunchKernelGGL((attn_lds<8>), grid, dim3(512), 0, st, p);
+      else
+        hipLaunchKernelGGL((attn_split<HD, 8, 1, P2>), grid, dim3(512), 0, st, p);
+      break;
     case 16: hipLaunchKernelGGL((attn_split<HD, 16, 1, false>), grid, dim3(1024), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }

@@ -82,6 +82,14 @@ def test_mid_shape_head_dim_64_group_8():
     _run(dc, [77], gains="random")
 
 
+def test_mid_shape_head_dim_128_group_8():
+    # eight query heads share each kv head's chunks through LDS; contexts of
+    # 0, a ragged tail, and several splits per (sequence, kv head)
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=16, n_kv_heads=2, ffn=1024,
+                           vocab=2000, index=92)
+    _run(dc, [0, 45, 2900], gains="random")
+
+
 def test_mid_shape_tall_batch():
     # 6 sequences x 16 rows = 96 draft rows: the tiled MFMA GEMMs (hi and lo
     # activations as two k segments), ragged contexts, logits checked
