@@ -26,6 +26,10 @@ Readings taken where the pages are silent (also listed in the design notes):
     K/V rows, rounded to bf16: [Code] section 5 sizes the model's weights and
     activations at two bytes each (BF16). With bf16_kv=False (the default)
     every row is kept in fp64.
+  * candidate selector: the top-k order (value descending, then index
+    ascending), no bias in the hidden projection, the walk's hidden state is
+    the LM head's input (final RMSNorm applied), and sampling draws from
+    softmax(scores / T) over the k candidates with Philox purpose 3.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
@@ -443,3 +447,88 @@ def sample_draft_tokens(draft_logits, temperature: float, seed: int,
         toks.append(t)
         margins.append(m)
     return np.array(toks, dtype=np.int64), np.array(margins)
+
+
+# ----------------------------------------------------------------------------
+# DFlash 2 candidate selector
+# ----------------------------------------------------------------------------
+
+PURPOSE_SELECT = 3
+
+
+def top_k_candidates(logits_row, k: int):
+    """[Code] section 14 (CandidateSelector.select starts from the top-k of
+    each drafted row's logits): the k largest entries of one row, ordered by
+    value descending and, among equal values, by index ascending.
+    Returns (token ids [k], values [k])."""
+    z = np.asarray(logits_row, dtype=F64)
+    order = sorted(range(len(z)), key=lambda i: (-z[i], i))[:k]
+    idx = np.array(order, dtype=np.int64)
+    return idx, z[idx]
+
+
+def select_candidates(logits, final_hidden, anchor: int, w_proj, pred_codebook,
+                      succ_codebook, k: int, temperature: float = 0.0,
+                      uniforms=None):
+    """The DFlash 2 candidate selector over one drafted block.
+
+    [Code] section 13: every adjacent pair of candidates is scored as
+    S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>: U_t the drafter's own logit of
+    b at position t, A and B two embedding tables (predecessor and successor
+    codes), H(h_t) a projection of the position's hidden state that gates the
+    product; the scores are computed in parallel and one greedy walk over them
+    is the only serial step. [Code] section 14: the walk starts from the
+    anchor (the last confirmed token), takes at each position the top-k
+    candidates of that row's logits, moves to the candidate of highest score
+    given the current predecessor, and samples from the scores instead when
+    the temperature is above zero.
+
+    logits       [P, V]  drafted rows' logits (block rows 1 .. P)
+    final_hidden [P, D]  the same rows' hidden states as the LM head reads
+                         them (final RMSNorm applied)
+    w_proj [r, D], pred_codebook [V, r], succ_codebook [V, r]
+    temperature 0: argmax (lowest candidate position on ties); > 0: the
+    candidate is drawn from softmax(S / T) over the k candidates with
+    uniforms[t] (sample_inverse_cdf in candidate order).
+    Returns a dict: path [P] token ids, cand [P, k], scores [P, k] (the scores
+    of the step actually taken), q [P, k] (softmax(S / T); one-hot of the
+    choice at T = 0), gap [P] (top-1 minus top-2 score at T = 0), margin [P]
+    (inverse-CDF margin relative to the total at T > 0).
+    """
+    Z = np.asarray(logits, dtype=F64)
+    P = Z.shape[0]
+    A = np.asarray(pred_codebook, dtype=F64)
+    Bc = np.asarray(succ_codebook, dtype=F64)
+    g = linear(np.asarray(final_hidden, dtype=F64), w_proj)   # H(h_t): [P, r]
+    out = {"path": np.zeros(P, np.int64), "cand": np.zeros((P, k), np.int64),
+           "scores": np.zeros((P, k)), "q": np.zeros((P, k)), "gap": np.full(P, np.inf),
+           "margin": np.full(P, np.inf)}
+    pred = int(anchor)
+    for t in range(P):
+        cand, unary = top_k_candidates(Z[t], k)
+        s = unary + (A[pred] * g[t]) @ Bc[cand].T
+        if temperature == 0.0:
+            i = int(np.argmax(s))
+            q = np.zeros(k)
+            q[i] = 1.0
+            if k > 1:
+                top2 = np.sort(s)[-2:]
+                out["gap"][t] = top2[1] - top2[0]
+        else:
+            q = softmax(s / temperature)
+            i, m = sample_inverse_cdf(q, float(uniforms[t]))
+            out["margin"][t] = m / q.sum()
+        pred = int(cand[i])
+        out["path"][t], out["cand"][t], out["scores"][t], out["q"][t] = pred, cand, s, q
+    return out
+
+
+def select_candidates_philox(logits, final_hidden, anchor: int, w_proj, pred_codebook,
+                             succ_codebook, k: int, temperature: float, seed: int,
+                             row_offset: int = 0, seq: int = 0):
+    """select_candidates with the walk's uniforms from
+    philox_uniform(seed, row_offset + t, seq, 3)."""
+    P = np.asarray(logits).shape[0]
+    u = [philox_uniform(seed, row_offset + t, seq, PURPOSE_SELECT) for t in range(P)]
+    return select_candidates(logits, final_hidden, anchor, w_proj, pred_codebook,
+                             succ_codebook, k, temperature, u)
