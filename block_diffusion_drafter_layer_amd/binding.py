@@ -40,6 +40,11 @@ class dflash_weights(C.Structure):
                 ("layers", C.POINTER(dflash_layer_weights))]
 
 
+class dflash_selector(C.Structure):
+    _fields_ = [("hidden_proj", C.c_void_p), ("pred_codebook", C.c_void_p),
+                ("succ_codebook", C.c_void_p), ("rank", C.c_int32), ("top_k", C.c_int32)]
+
+
 class dflash_kv(C.Structure):
     _fields_ = [("base", C.c_void_p), ("max_ctx", C.c_int32), ("len", C.c_int32)]
 
@@ -91,6 +96,8 @@ def _load():
         "dflash_draft_block": (C.c_int, [P, I32, C.POINTER(kvp), P, I32, P, P, P]),
         "dflash_verify": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
         "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
+        "dflash_set_selector": (C.c_int, [P, C.POINTER(dflash_selector)]),
+        "dflash_select_block": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P, P]),
         "dflash_draft_block_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, I32, P, P, P]),
         "dflash_append_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, C.POINTER(P), I64, I32]),
         "dflash_kv_trim_dev": (C.c_int, [P, I32, P, I32]),
@@ -209,6 +216,21 @@ def dflash_sample_draft(h, n_seqs: int, block_len: int, draft_logits: int, tempe
                                            C.c_void_p(block_ids)))
 
 
+def dflash_set_selector(h, sel):
+    """sel: a dflash_selector, or None to remove the selector."""
+    return _check(_lib.dflash_set_selector(h, C.byref(sel) if sel is not None else None))
+
+
+def dflash_select_block(h, n_seqs: int, block_len: int, last_hidden: int, draft_logits: int,
+                        anchor_ids: int, temperature: float, seed: int, philox_offset: int,
+                        block_ids: int, cand_out: int = 0, q_out: int = 0):
+    return _check(_lib.dflash_select_block(h, n_seqs, block_len, C.c_void_p(last_hidden),
+                                           C.c_void_p(draft_logits), C.c_void_p(anchor_ids),
+                                           float(temperature), seed, philox_offset,
+                                           C.c_void_p(block_ids), C.c_void_p(cand_out or None),
+                                           C.c_void_p(q_out or None)))
+
+
 def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
     out = (C.c_int32 * n_feat)()
     _check(_lib.dflash_target_layer_ids(n_target_layers, n_feat, out))
@@ -216,7 +238,7 @@ def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
 
 
 STAGES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down_proj", "lm_head",
-          "fuse_context", "inject_kv", "verify", "lm_argmax", "sample_draft")
+          "fuse_context", "inject_kv", "verify", "lm_argmax", "sample_draft", "select")
 
 
 def dflash_copy_bytes(dst: int, src: int, nbytes: int, stream: int = 0):

@@ -16,7 +16,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 
 SOURCES = ["api.cpp", "skinny.hip", "attention.hip", "gemm.hip", "verify.hip", "rounds.hip",
-           "calibrate.hip"]
+           "calibrate.hip", "select.hip"]
 HEADERS = ["common.h", "launch.h", "tiled_gemm.h"]
 
 FLAGS = [

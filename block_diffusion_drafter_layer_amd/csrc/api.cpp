@@ -99,6 +99,7 @@ struct Layout {
   size_t app_ctx;               // fused rows of a device-resident append
   size_t fuse_y;                // fp32 projection of the fused rows before the norm
   size_t vcdf;                  // verify / sampling draws: merged row statistics and slice sums
+  size_t sel_keys, sel_gpart, sel_spart, sel_S, sel_cand;  // candidate selector
   size_t total;
 };
 
@@ -137,6 +138,12 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.app_ctx = take(std::min((size_t)max_tokens, Mmax) * D * 2);
   L.fuse_y = take((size_t)max_tokens * D * 4);
   L.vcdf = take(2 * Mmax * 16 + Mmax * kVerifyMaxSplits * 8);
+  const size_t sel_rows = (size_t)max_seqs * (c.block_size > 1 ? c.block_size - 1 : 1);
+  L.sel_keys = take(sel_rows * sel_slices(c.vocab) * kSelMaxK * 8);
+  L.sel_gpart = take((size_t)sel_kz(c.hidden) * sel_rows * kSelMaxRank * 4);
+  L.sel_spart = take((size_t)sel_kz(c.hidden) * sel_rows * 4);
+  L.sel_S = take(sel_rows * kSelMaxK * kSelMaxK * 4);
+  L.sel_cand = take(sel_rows * kSelMaxK * 4);
   L.total = o;
   return L;
 }
@@ -144,10 +151,10 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
 }  // namespace
 
 enum Stage { ST_EMBED, ST_QKV, ST_ATTN, ST_OPROJ, ST_GATEUP, ST_DOWN, ST_LM, ST_FUSE, ST_INJECT,
-             ST_VERIFY, ST_LM_ARGMAX, ST_SAMPLE, ST_COUNT };
+             ST_VERIFY, ST_LM_ARGMAX, ST_SAMPLE, ST_SELECT, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"embed", "qkv", "attention", "o_proj", "gate_up",
                                      "down_proj", "lm_head", "fuse_context", "inject_kv", "verify",
-                                     "lm_argmax", "sample_draft"};
+                                     "lm_argmax", "sample_draft", "select"};
 
 struct Profiler {
   uint32_t mask = 0;
@@ -166,6 +173,7 @@ struct dflash_handle {
   size_t ws_bytes = 0;
   int32_t max_seqs = 0, max_tokens = 0;
   Layout lay{};
+  dflash_selector sel{};         // candidate selector tables (rank 0: none)
 };
 
 // Launch `fn` as stage `st`, bracketed by timing events when that stage is
@@ -727,6 +735,74 @@ dflash_status dflash_sample_draft(dflash_handle* h, int32_t n_seqs, int32_t bloc
     return launch_sample_draft(P, block_ids, block_len, h->stream);
   });
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "sample_draft");
+}
+
+dflash_status dflash_set_selector(dflash_handle* h, const dflash_selector* sel) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is required");
+  if (!sel) {
+    h->sel = dflash_selector{};
+    return DFLASH_OK;
+  }
+  if (!sel->hidden_proj || !sel->pred_codebook || !sel->succ_codebook)
+    return fail(DFLASH_E_NULL, "hidden_proj, pred_codebook and succ_codebook are required");
+  if (sel->top_k < 1 || sel->top_k > kSelMaxK || sel->top_k > h->cfg.vocab)
+    return fail(DFLASH_E_SHAPE, "top_k=%d outside 1..%d (and at most the vocabulary)", sel->top_k,
+                kSelMaxK);
+  if (sel->rank < 64 || sel->rank > kSelMaxRank || sel->rank % 64)
+    return fail(DFLASH_E_SHAPE, "rank=%d: 64..%d in steps of 64", sel->rank, kSelMaxRank);
+  if (sel_slices(h->cfg.vocab) * sel->top_k > sel_max_merge_keys())
+    return fail(DFLASH_E_SHAPE, "vocab=%d with top_k=%d exceeds the selector's merge", h->cfg.vocab,
+                sel->top_k);
+  if (h->cfg.hidden % 64)
+    return fail(DFLASH_E_SHAPE, "the selector needs hidden %% 64 == 0 (hidden=%d)", h->cfg.hidden);
+  if (!aligned(sel->hidden_proj, 16) || !aligned(sel->pred_codebook, 16) ||
+      !aligned(sel->succ_codebook, 16))
+    return fail(DFLASH_E_ALIGN, "selector tables must be 16-byte aligned");
+  h->sel = *sel;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_select_block(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  const float* last_hidden, const float* draft_logits,
+                                  const int32_t* anchor_ids, float temperature, uint64_t seed,
+                                  uint64_t philox_offset, int32_t* block_ids, int32_t* cand_out,
+                                  float* q_out) {
+  if (!h || !last_hidden || !draft_logits || !anchor_ids || !block_ids)
+    return fail(DFLASH_E_NULL, "handle, last_hidden, draft_logits, anchor_ids and block_ids are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  if (!h->sel.rank) return fail(DFLASH_E_STATE, "no selector set (dflash_set_selector)");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if (block_len - 1 > sel_max_walk_rows())
+    return fail(DFLASH_E_SHAPE, "block_len-1=%d exceeds the selector's %d rows", block_len - 1,
+                sel_max_walk_rows());
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "temperature must be finite and >= 0");
+  if (!aligned(last_hidden, 16) || !aligned(draft_logits, 4) || !aligned(anchor_ids, 4) ||
+      !aligned(block_ids, 4) || !aligned(cand_out, 4) || !aligned(q_out, 4))
+    return fail(DFLASH_E_ALIGN, "last_hidden must be 16-byte aligned, the other arrays 4-byte");
+  if (block_len == 1) return DFLASH_OK;  // nothing drafted
+  SelectLaunch L{};
+  L.n_seqs = n_seqs; L.Bl = block_len; L.P = block_len - 1;
+  L.V = c.vocab; L.D = c.hidden; L.k = h->sel.top_k; L.rank = h->sel.rank; L.eps = c.rms_eps;
+  L.logits = draft_logits; L.last_hidden = last_hidden;
+  L.gain = (const bf16_t*)h->w.final_norm;
+  L.w_proj = (const bf16_t*)h->sel.hidden_proj;
+  L.pred = (const bf16_t*)h->sel.pred_codebook;
+  L.succ = (const bf16_t*)h->sel.succ_codebook;
+  L.anchors = anchor_ids;
+  L.temperature = (double)temperature; L.seed = seed; L.offset = philox_offset;
+  L.block = block_ids; L.cand_out = cand_out; L.q_out = q_out;
+  L.keys = (uint64_t*)(h->ws + h->lay.sel_keys);
+  L.gpart = (float*)(h->ws + h->lay.sel_gpart);
+  L.spart = (float*)(h->ws + h->lay.sel_spart);
+  L.S = (float*)(h->ws + h->lay.sel_S);
+  L.cand = (int32_t*)(h->ws + h->lay.sel_cand);
+  hipError_t e = timed(h, ST_SELECT, [&] { return launch_select(L, h->stream); });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "select_block");
 }
 
 }  // extern "C"

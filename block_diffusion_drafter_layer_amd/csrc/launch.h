@@ -164,6 +164,38 @@ hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
 // block[s * Bl + 1 + j]
 hipError_t launch_sample_draft(const VerifyLaunch& P, int32_t* block, int Bl, hipStream_t st);
 
+// DFlash 2 candidate selector over drafted blocks.
+constexpr int kSelMaxK = 16;       // candidates per row
+constexpr int kSelMaxRank = 256;   // code width
+struct SelectLaunch {
+  int n_seqs, Bl, P;               // P = Bl - 1 drafted rows per sequence
+  int V, D, k, rank;
+  float eps;
+  const float* logits;             // [n_seqs * P][V]
+  const float* last_hidden;        // [n_seqs * Bl][D] residual after the last layer
+  const bf16_t* gain;              // final norm gain [D]
+  const bf16_t* w_proj;            // [rank][D]
+  const bf16_t* pred;              // [V][rank]
+  const bf16_t* succ;              // [V][rank]
+  const int32_t* anchors;          // [n_seqs]
+  double temperature;
+  uint64_t seed, offset;
+  int32_t* block;                  // [n_seqs][Bl], columns 1..
+  int32_t* cand_out;               // optional [n_seqs * P][k]
+  float* q_out;                    // optional [n_seqs * P][k]
+  // workspace
+  uint64_t* keys;                  // [rows][slices][k]
+  float* gpart;                    // [kz][rows][rank]
+  float* spart;                    // [kz][rows]
+  float* S;                        // [rows][16][16]
+  int32_t* cand;                   // [rows][16]
+};
+int sel_slices(int V);
+int sel_kz(int D);
+int sel_max_walk_rows();
+int sel_max_merge_keys();
+hipError_t launch_select(const SelectLaunch& L, hipStream_t st);
+
 // reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)
 hipError_t launch_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t st);
 

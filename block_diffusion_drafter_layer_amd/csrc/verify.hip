@@ -23,29 +23,6 @@
 namespace dfl {
 
 // ---------------------------------------------------------------------------
-// Philox4x64-10 from the Random123 paper's round function
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
-    k0 += W0; k1 += W1;
-  }
-}
-
-__device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t row, uint64_t seq,
-                                                 uint64_t purpose) {
-  uint64_t c[4] = {row, seq, purpose, 0ull};
-  philox4x64_10(c, seed, 0ull);
-  return (double)(c[0] >> 11) * 0x1.0p-53;
-}
-
-// ---------------------------------------------------------------------------
 // greedy
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)

@@ -125,6 +125,27 @@ class Drafter:
                               philox_offset, block_ids.data_ptr())
         return block_ids
 
+    # --- DFlash 2 candidate selector -------------------------------------------
+    def set_selector(self, hidden_proj: torch.Tensor, pred_codebook: torch.Tensor,
+                     succ_codebook: torch.Tensor, top_k: int):
+        """Borrow the selector's bf16 tables (kept alive by this object)."""
+        self._sel = (hidden_proj, pred_codebook, succ_codebook)
+        sel = B.dflash_selector(hidden_proj.data_ptr(), pred_codebook.data_ptr(),
+                                succ_codebook.data_ptr(), hidden_proj.shape[0], top_k)
+        B.dflash_set_selector(self.h, sel)
+
+    def select_block(self, block_ids: torch.Tensor, last_hidden: torch.Tensor,
+                     draft_logits: torch.Tensor, anchors: torch.Tensor, temperature: float = 0.0,
+                     seed: int = 0, philox_offset: int = 0, cand: Optional[torch.Tensor] = None,
+                     q: Optional[torch.Tensor] = None):
+        """Overwrite block_ids[:, 1:] with the selector's walk over the candidates."""
+        n, bl = block_ids.shape
+        B.dflash_select_block(self.h, n, bl, last_hidden.data_ptr(), draft_logits.data_ptr(),
+                              anchors.data_ptr(), temperature, seed, philox_offset,
+                              block_ids.data_ptr(), cand.data_ptr() if cand is not None else 0,
+                              q.data_ptr() if q is not None else 0)
+        return block_ids
+
     def verify(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
                draft_logits: Optional[torch.Tensor] = None, temperature: float = 0.0,
                seed: int = 0, philox_offset: int = 0, tau: Optional[torch.Tensor] = None,

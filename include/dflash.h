@@ -295,6 +295,62 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
                             int32_t* tau_out, int32_t* bonus_out);
 
 /*
+ * DFlash 2 candidate selector ([Code] section 13: the right token is usually
+ * among a drafted row's top candidates; each adjacent pair is scored as
+ * S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>, and one walk over the scores
+ * picks the block; [Code] section 14: CandidateSelector.select).
+ *
+ * dflash_set_selector: borrows the selector's tables for the handle's
+ *   lifetime (NULL sel removes them).
+ *   hidden_proj:   bf16 [rank, hidden]  H, no bias
+ *   pred_codebook: bf16 [vocab, rank]   A (predecessor codes)
+ *   succ_codebook: bf16 [vocab, rank]   B (successor codes)
+ *   1 <= top_k <= 16; 64 <= rank <= 256, rank % 64 == 0.
+ *
+ * dflash_select_block: for sequence s and drafted row j < block_len-1 (block
+ *   row j+1): the candidates are the top_k tokens of draft_logits[s][j]
+ *   (value descending, index ascending among equal values); g_j = H h_j with
+ *   h_j the LM head's input row (the final RMSNorm of last_hidden's block row
+ *   j+1, weighted by the final norm gain); the walk starts at a =
+ *   anchor_ids[s], scores every candidate b as
+ *   logit(b) + sum_x A[a][x] g_j[x] B[b][x] (fp32), and moves to
+ *   temperature == 0: the best candidate (first in candidate order on ties);
+ *   temperature > 0:  the candidate drawn from q = softmax(scores / T) in
+ *     fp64: the first whose running sum in candidate order exceeds u * total,
+ *     u the Philox4x64-10 uniform of counter (philox_offset + j, s, 3, 0),
+ *     key (seed, 0), u = (word0 >> 11) * 2^-53.
+ *   block_ids[s][j+1] becomes the chosen token (column 0 is left as it is).
+ * last_hidden: device fp32 [n_seqs * block_len, hidden] - the residual stream
+ *              after the last layer (dflash_draft_block's hidden_out, layer
+ *              n_layers-1), row s*block_len + r;
+ * draft_logits: device fp32 [n_seqs, block_len-1, vocab] (logits_out);
+ * anchor_ids:  device int32 [n_seqs] (a value outside the vocabulary is
+ *              clamped into it for the code lookup);
+ * block_ids:   device int32 [n_seqs, block_len];
+ * cand_out:    optional device int32 [n_seqs, block_len-1, top_k] - the
+ *              candidates of every row, in candidate order;
+ * q_out:       optional device fp32 [n_seqs, block_len-1, top_k] - the walk's
+ *              distribution at each row (one-hot of the choice at T == 0).
+ * A selector must be set; 1 <= n_seqs <= max_seqs; 1 <= block_len <=
+ * block_size, block_len - 1 <= 64; top_k <= vocab. Errors as for the other
+ * calls: checked on the host before any launch, nothing written on error.
+ */
+typedef struct dflash_selector {
+  const void* hidden_proj;
+  const void* pred_codebook;
+  const void* succ_codebook;
+  int32_t rank;
+  int32_t top_k;
+} dflash_selector;
+
+dflash_status dflash_set_selector(dflash_handle* h, const dflash_selector* sel);
+dflash_status dflash_select_block(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  const float* last_hidden, const float* draft_logits,
+                                  const int32_t* anchor_ids, float temperature,
+                                  uint64_t seed, uint64_t philox_offset,
+                                  int32_t* block_ids, int32_t* cand_out, float* q_out);
+
+/*
  * Host helper ([Code] section 5, build_target_layer_ids): n_feat target layer
  * indices spread evenly over 1 .. n_target_layers-3 (0-based), rounded to
  * nearest; the middle layer when n_feat == 1. out: host int32 [n_feat].

@@ -17,7 +17,9 @@ Recipe (one per workload, all seeded):
 * agreement lengths: tau = min(G, block_size) with G ~ Geometric(0.25) on
   {1, 2, ...}, a = tau - 1;
 * ragged context lengths for the batched workload: uniform integers in
-  [512, 4096].
+  [512, 4096];
+* candidate-selector tables (DFlash 2): hidden projection N(0, 1/D),
+  predecessor and successor codes N(0, 0.3^2), rank 256.
 
 Floating-point draws are made in fp32 and rounded once to bf16 (round to
 nearest even, torch's conversion) where the tensor is stored in bf16; the
@@ -26,6 +28,7 @@ same bf16 values are handed to both the GPU path and the oracle.
 from .configs import CONFIGS, DraftConfig, target_layer_ids_rule  # noqa: F401
 from .gen import (  # noqa: F401
     make_weights,
+    make_selector,
     make_feats,
     make_anchor,
     make_target_logits,

@@ -22,6 +22,7 @@ _DLOGIT_BASE = 600          # + round
 _TAU_BASE = 700
 _RAGGED = 800
 _CTXKV_BASE = 850           # + layer
+_SEL_BASE = 900             # + 0 hidden projection, 1 predecessor, 2 successor codes
 
 LAYER_SLOTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
                "attn_norm", "mlp_norm")
@@ -86,6 +87,18 @@ def make_weights(cfg: DraftConfig, device="cpu", gains: str = "ones",
                 lw[name] = _normal(shapes[name], std, t, device)
         w["layers"].append(lw)
     return w
+
+
+def make_selector(cfg: DraftConfig, rank: int = 256, device="cpu", code_std: float = 0.3) -> Dict:
+    """Tables of a DFlash 2 candidate selector, bf16: hidden_proj [rank, D] with
+    entries N(0, 1/D) (so the projected hidden state has entries of order 1),
+    pred_codebook and succ_codebook [V, rank] with entries N(0, code_std^2)."""
+    s = lambda t: seed_for(cfg.index, _SEL_BASE + t)  # noqa: E731
+    return {
+        "hidden_proj": _normal((rank, cfg.hidden), cfg.hidden ** -0.5, s(0), device),
+        "pred_codebook": _normal((cfg.vocab, rank), code_std, s(1), device),
+        "succ_codebook": _normal((cfg.vocab, rank), code_std, s(2), device),
+    }
 
 
 def make_feats(cfg: DraftConfig, n_tokens: int, round_index: int = 0,

@@ -163,6 +163,25 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_sample_draft, h, 1, 16, 0, 1.0, 0, 0, FAKE) == 1
     assert _status(B.dflash_sample_draft, h, 1, 16, FAKE, 1.0, 0, 0, 0) == 1
     assert _status(B.dflash_sample_draft, h, 1, 1, FAKE, 1.0, 0, 0, FAKE) == 0
+    # candidate selector: state, tables, shapes, pointers
+    sel = B.dflash_selector(FAKE, FAKE, FAKE, 256, 16)
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 7
+    assert _status(B.dflash_set_selector, h, B.dflash_selector(FAKE, FAKE, FAKE, 256, 17)) == 3
+    assert _status(B.dflash_set_selector, h, B.dflash_selector(FAKE, FAKE, FAKE, 96, 16)) == 3
+    assert _status(B.dflash_set_selector, h, B.dflash_selector(FAKE, FAKE, FAKE, 320, 16)) == 3
+    assert _status(B.dflash_set_selector, h, B.dflash_selector(FAKE, 0, FAKE, 256, 16)) == 1
+    assert _status(B.dflash_set_selector, h, B.dflash_selector(FAKE, FAKE + 8, FAKE, 256, 16)) == 5
+    assert _status(B.dflash_set_selector, h, sel) == 0
+    assert _status(B.dflash_select_block, h, 3, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_select_block, h, 1, 17, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, -1.0, 0, 0, FAKE) == 3
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, float("inf"), 0, 0, FAKE) == 3
+    assert _status(B.dflash_select_block, h, 1, 16, 0, FAKE, FAKE, 0.0, 0, 0, FAKE) == 1
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE + 4, FAKE, FAKE, 0.0, 0, 0, FAKE) == 5
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE, FAKE + 2) == 5
+    assert _status(B.dflash_select_block, h, 1, 1, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 0
+    assert _status(B.dflash_set_selector, h, None) == 0
+    assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 7
     # device-resident rounds: pointers, shapes, alignment
     assert _status(B.dflash_draft_block_dev, h, [kv], 0, FAKE, 16, FAKE) == 1
     assert _status(B.dflash_draft_block_dev, h, [kv], FAKE + 2, FAKE, 16, FAKE) == 5
