@@ -532,3 +532,55 @@ def select_candidates_philox(logits, final_hidden, anchor: int, w_proj, pred_cod
     u = [philox_uniform(seed, row_offset + t, seq, PURPOSE_SELECT) for t in range(P)]
     return select_candidates(logits, final_hidden, anchor, w_proj, pred_codebook,
                              succ_codebook, k, temperature, u)
+
+
+def verify_pq_candidates_with_uniforms(block_ids, target_logits, cand, q_rows,
+                                       temperature: float, u_accept, u_resample):
+    """p/q verification when the draft distribution lives on candidate sets.
+
+    [Code] section 14: with the candidate selector the draft distribution at
+    row j is not a softmax over the vocabulary but the walk's distribution over
+    that row's candidates, so q_j(x) is the sum of the row's q entries whose
+    candidate is x (zero for every other token) before the p/q rule of
+    [Code] section 8 applies unchanged: accept row j iff
+    u_accept[j] < p_j(x)/q_j(x) (always when q_j(x) is zero), replacement from
+    max(p_j - q_j, 0) renormalised, bonus from p_gamma when every row is kept.
+
+    cand [gamma, k] token ids, q_rows [gamma, k] probabilities.
+    Returns (tau, bonus, diag) as verify_pq_with_uniforms."""
+    T = np.asarray(target_logits, dtype=F64) / temperature
+    ids = [int(t) for t in block_ids]
+    gamma = len(ids) - 1
+    V = T.shape[1]
+    diag = {"ratio_margin": [], "cdf_margin": None}
+    for j in range(gamma):
+        p = softmax(T[j])
+        q = np.zeros(V)
+        for c, w in zip(np.asarray(cand[j]), np.asarray(q_rows[j], dtype=F64)):
+            q[int(c)] += w
+        tok = ids[j + 1]
+        u = float(u_accept[j])
+        if q[tok] > 0.0:
+            ratio = p[tok] / q[tok]
+            diag["ratio_margin"].append(abs(ratio - u))
+            if not (u < ratio):
+                resid = np.maximum(p - q, 0.0)
+                tok2, margin = sample_inverse_cdf(resid, float(u_resample[j]))
+                diag["cdf_margin"] = margin / resid.sum()
+                return j + 1, tok2, diag
+        else:
+            diag["ratio_margin"].append(np.inf)
+    p = softmax(T[gamma])
+    tok2, margin = sample_inverse_cdf(p, float(u_resample[gamma]))
+    diag["cdf_margin"] = margin / p.sum()
+    return gamma + 1, tok2, diag
+
+
+def verify_pq_candidates(block_ids, target_logits, cand, q_rows, temperature: float,
+                         seed: int, row_offset: int = 0, seq: int = 0):
+    """verify_pq_candidates_with_uniforms with the Philox uniforms of verify_pq."""
+    B = len(block_ids)
+    ua = [philox_uniform(seed, row_offset + j, seq, PURPOSE_ACCEPT) for j in range(B - 1)]
+    ur = [philox_uniform(seed, row_offset + j, seq, PURPOSE_RESAMPLE) for j in range(B)]
+    return verify_pq_candidates_with_uniforms(block_ids, target_logits, cand, q_rows,
+                                              temperature, ua, ur)

@@ -92,3 +92,57 @@ def test_sampled_step_frequencies_follow_q():
     assert abs(q.sum() - 1.0) < 1e-12
     for c, p in zip(cand, q):
         assert abs(counts.get(int(c), 0) / n - p) <= 1.0 / n + 1e-12
+
+
+def test_candidate_q_verify_with_the_whole_vocabulary_is_dense_verify():
+    # candidates = every token, q = softmax(draft / T): the dense p/q rule
+    rng = np.random.default_rng(6)
+    V, gamma, T = 9, 4, 0.7
+    tl = rng.standard_normal((gamma + 1, V))
+    dl = rng.standard_normal((gamma, V))
+    for trial in range(30):
+        block = [3] + rng.integers(0, V, gamma).tolist()
+        ua, ur = rng.random(gamma), rng.random(gamma + 1)
+        cand = np.array([rng.permutation(V) for _ in range(gamma)])
+        q = np.array([O.softmax(dl[j] / T)[cand[j]] for j in range(gamma)])
+        a = O.verify_pq_candidates_with_uniforms(block, tl, cand, q, T, ua, ur)
+        b = O.verify_pq_with_uniforms(block, tl, dl, T, ua, ur)
+        assert a[:2] == b[:2]
+
+
+def test_candidate_q_verify_is_lossless():
+    # speculative sampling keeps the target distribution: with x ~ q on a
+    # candidate set, the first emitted token (x if kept, else the
+    # replacement) is distributed as p
+    rng = np.random.default_rng(7)
+    V, k, T = 7, 3, 1.0
+    tl = rng.standard_normal((2, V))
+    p = O.softmax(tl[0] / T)
+    cand = np.array([[5, 1, 2]])
+    q = np.array([[0.5, 0.3, 0.2]])
+    n = 40000
+    counts = np.zeros(V)
+    for i in range(n):
+        x = int(cand[0][np.searchsorted(np.cumsum(q[0]), rng.random(), side="right")])
+        tau, bonus, _ = O.verify_pq_candidates_with_uniforms([0, x], tl, cand, q, T,
+                                                             [rng.random()], [rng.random(), rng.random()])
+        counts[x if tau == 2 else bonus] += 1
+    assert np.abs(counts / n - p).max() < 0.01
+
+
+def test_candidate_q_verify_accepts_tokens_outside_the_candidates_and_bounds_tau():
+    rng = np.random.default_rng(8)
+    V, gamma, T = 12, 5, 1.3
+    for _ in range(40):
+        tl = rng.standard_normal((gamma + 1, V))
+        cand = np.array([rng.choice(V, 4, replace=False) for _ in range(gamma)])
+        q = rng.dirichlet(np.ones(4), size=gamma)
+        block = [1] + rng.integers(0, V, gamma).tolist()
+        tau, bonus, _ = O.verify_pq_candidates_with_uniforms(block, tl, cand, q, T,
+                                                             rng.random(gamma), rng.random(gamma + 1))
+        assert 1 <= tau <= gamma + 1 and 0 <= bonus < V
+        # a row whose token is no candidate is always kept, so it is never
+        # the rejected row
+        outside = [j for j in range(gamma) if block[j + 1] not in cand[j]]
+        if tau <= gamma:
+            assert (tau - 1) not in outside
