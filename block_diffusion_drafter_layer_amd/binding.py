@@ -96,6 +96,7 @@ def _load():
         "dflash_draft_block": (C.c_int, [P, I32, C.POINTER(kvp), P, I32, P, P, P]),
         "dflash_verify": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
         "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
+        "dflash_verify_candidates": (C.c_int, [P, I32, I32, P, P, P, P, I32, F32, U64, U64, P, P]),
         "dflash_set_selector": (C.c_int, [P, C.POINTER(dflash_selector)]),
         "dflash_select_block": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P, P]),
         "dflash_draft_block_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, I32, P, P, P]),
@@ -229,6 +230,16 @@ def dflash_select_block(h, n_seqs: int, block_len: int, last_hidden: int, draft_
                                            float(temperature), seed, philox_offset,
                                            C.c_void_p(block_ids), C.c_void_p(cand_out or None),
                                            C.c_void_p(q_out or None)))
+
+
+def dflash_verify_candidates(h, n_seqs: int, block_len: int, block_ids: int, target_logits: int,
+                             cand: int, q_rows: int, top_k: int, temperature: float, seed: int,
+                             philox_offset: int, tau_out: int, bonus_out: int):
+    return _check(_lib.dflash_verify_candidates(h, n_seqs, block_len, C.c_void_p(block_ids),
+                                                C.c_void_p(target_logits), C.c_void_p(cand),
+                                                C.c_void_p(q_rows), top_k, float(temperature),
+                                                seed, philox_offset, C.c_void_p(tau_out),
+                                                C.c_void_p(bonus_out)))
 
 
 def dflash_target_layer_ids(n_target_layers: int, n_feat: int):

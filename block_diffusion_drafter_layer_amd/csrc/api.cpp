@@ -708,6 +708,44 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "verify");
 }
 
+dflash_status dflash_verify_candidates(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                      const int32_t* block_ids, const float* target_logits,
+                                      const int32_t* cand, const float* q_rows, int32_t top_k,
+                                      float temperature, uint64_t seed, uint64_t philox_offset,
+                                      int32_t* tau_out, int32_t* bonus_out) {
+  if (!h || !block_ids || !target_logits || !tau_out || !bonus_out)
+    return fail(DFLASH_E_NULL, "handle, block_ids, target_logits, tau_out and bonus_out are required");
+  if (block_len > 1 && (!cand || !q_rows))
+    return fail(DFLASH_E_NULL, "cand and q_rows are required when block_len > 1");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if (top_k < 1 || top_k > kSelMaxK)
+    return fail(DFLASH_E_SHAPE, "top_k=%d outside 1..%d", top_k, kSelMaxK);
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "temperature must be finite and > 0");
+  if (c.vocab % 4 == 0 && !aligned(target_logits, 16))
+    return fail(DFLASH_E_ALIGN, "target_logits not 16-byte aligned");
+  if (!aligned(cand, 4) || !aligned(q_rows, 4) || !aligned(block_ids, 4))
+    return fail(DFLASH_E_ALIGN, "cand, q_rows and block_ids must be 4-byte aligned");
+  VerifyLaunch P{};
+  P.n_seqs = n_seqs; P.Bl = block_len; P.V = c.vocab;
+  P.block_ids = block_ids; P.target = target_logits;
+  P.cand = cand; P.qc = q_rows; P.k = top_k;
+  P.temperature = (double)temperature; P.seed = seed; P.offset = philox_offset;
+  P.tau = tau_out; P.bonus = bonus_out;
+  P.part = h->ws + h->lay.vpart;
+  P.part2 = h->ws + h->lay.vcdf;
+  P.max_rows = 2 * h->max_seqs * c.block_size;
+  const int rows = n_seqs * block_len;
+  P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
+  hipError_t e = timed(h, ST_VERIFY, [&] { return launch_verify_pq_cand(P, h->stream); });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "verify_candidates");
+}
+
 dflash_status dflash_sample_draft(dflash_handle* h, int32_t n_seqs, int32_t block_len,
                                   const float* draft_logits, float temperature, uint64_t seed,
                                   uint64_t philox_offset, int32_t* block_ids) {

@@ -156,9 +156,16 @@ struct VerifyLaunch {
   int splits;
   void* part2;         // merged row statistics [max_rows] then slice sums [max_rows / 2][splits]
   int max_rows;
+  // draft distribution on candidate sets (instead of draft logits): row
+  // s * (Bl - 1) + j holds k candidates and their probabilities
+  const int32_t* cand;
+  const float* qc;
+  int k;
 };
 hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
+// p/q with P.cand / P.qc (P.draft unused)
+hipError_t launch_verify_pq_cand(const VerifyLaunch& P, hipStream_t st);
 // draft tokens sampled from softmax(rows / T): P.target = the draft logits,
 // P.n_seqs * P.Bl rows (P.Bl = drafted rows per sequence); writes
 // block[s * Bl + 1 + j]

@@ -166,13 +166,33 @@ struct CdfRow {
   const float* t;  // p (or q when drawing from the draft) source row
   const float* d;  // q row of a p/q residual, else null
   double mt, zt, mq, zq, inv_temp;
+  // q on a candidate set instead (LDS copies; cv == null: not used): q(v) is
+  // the sum of cq[c] over the candidates c with cv[c] == v
+  const int32_t* cv = nullptr;
+  const float* cq = nullptr;
+  int k = 0;
   __device__ double w(int v) const {
     const double p = exp((double)t[v] * inv_temp - mt) / zt;
+    if (cv) {
+      double q = 0.0;
+      for (int c = 0; c < k; ++c)
+        if (cv[c] == v) q += (double)cq[c];
+      const double r = p - q;
+      return r > 0.0 ? r : 0.0;
+    }
     if (!d) return p;
     const double r = p - exp((double)d[v] * inv_temp - mq) / zq;
     return r > 0.0 ? r : 0.0;
   }
 };
+
+// the candidate list and q row of drafted row r into LDS (k <= kSelMaxK)
+__device__ __forceinline__ void load_cand_row(const VerifyLaunch& P, int r, int32_t* cv, float* cq) {
+  if ((int)threadIdx.x < P.k) {
+    cv[threadIdx.x] = P.cand[(size_t)r * P.k + threadIdx.x];
+    cq[threadIdx.x] = P.qc[(size_t)r * P.k + threadIdx.x];
+  }
+}
 
 // stats rows and logits of candidate row c (PQ: p/q residual or bonus row)
 template <bool PQ>
@@ -180,7 +200,7 @@ __device__ __forceinline__ void cand_rows(const VerifyLaunch& P, int c, int& tro
   if (PQ) {
     const int Bl = P.Bl, gamma = Bl - 1, s = c / Bl, j = c - s * Bl;
     trow = c;
-    drow = j < gamma ? P.n_seqs * Bl + s * gamma + j : -1;
+    drow = j < gamma && !P.cand ? P.n_seqs * Bl + s * gamma + j : -1;
   } else {
     trow = c;
     drow = -1;
@@ -223,9 +243,19 @@ cdf_slice_sums(VerifyLaunch P, const RowStat* part, Merged* merged, double* sums
       }
     }
   }
+  __shared__ int32_t cv[kSelMaxK];
+  __shared__ float cq[kSelMaxK];
+  const int gamma = P.Bl - 1, s = c / P.Bl, j = c - s * P.Bl;
+  const bool sparse = PQ && P.cand && j < gamma;
+  if (sparse) load_cand_row(P, s * gamma + j, cv, cq);
   __syncthreads();
   CdfRow R{logits_row(P, trow), drow >= 0 ? logits_row(P, drow) : nullptr,
            st[0].m, st[0].z, st[1].m, st[1].z, 1.0 / P.temperature};
+  if (sparse) {
+    R.cv = cv;
+    R.cq = cq;
+    R.k = P.k;
+  }
   int v0, v1;
   slice_chunk(P, split, v0, v1);
   double local = 0.0;
@@ -312,17 +342,28 @@ pq_pick(VerifyLaunch P, const Merged* merged, const double* sums) {
   __shared__ int sh[3];
   __shared__ double dsh[1];
   __shared__ int jr_sh;
+  __shared__ int32_t cv[kSelMaxK];
+  __shared__ float cq[kSelMaxK];
   const double inv_t = 1.0 / P.temperature;
   if (tid == 0) {
     int jr = gamma;
     for (int j = 0; j < gamma; ++j) {
       int x = P.block_ids[(size_t)s * Bl + j + 1];
       x = x < 0 ? 0 : (x >= P.V ? P.V - 1 : x);  // keep the read in bounds
-      const Merged a = merged[s * Bl + j], b = merged[nt + s * gamma + j];
+      const Merged a = merged[s * Bl + j];
       const double p = exp((double)P.target[(size_t)(s * Bl + j) * P.V + x] * inv_t - a.m) / a.z;
-      const double q = exp((double)P.draft[(size_t)(s * gamma + j) * P.V + x] * inv_t - b.m) / b.z;
+      double q;
+      if (P.cand) {  // q on the row's candidate set (zero elsewhere: always kept)
+        q = 0.0;
+        for (int c = 0; c < P.k; ++c)
+          if (P.cand[(size_t)(s * gamma + j) * P.k + c] == x)
+            q += (double)P.qc[(size_t)(s * gamma + j) * P.k + c];
+      } else {
+        const Merged b = merged[nt + s * gamma + j];
+        q = exp((double)P.draft[(size_t)(s * gamma + j) * P.V + x] * inv_t - b.m) / b.z;
+      }
       const double u = philox_uniform(P.seed, P.offset + j, s, 0);
-      if (!(u < p / q)) { jr = j; break; }
+      if (q > 0.0 && !(u < p / q)) { jr = j; break; }
     }
     jr_sh = jr;
   }
@@ -331,9 +372,18 @@ pq_pick(VerifyLaunch P, const Merged* merged, const double* sums) {
   const int c = s * Bl + jr;
   const Merged a = merged[c];
   const bool resid = jr < gamma;
-  const Merged b = resid ? merged[nt + s * gamma + jr] : Merged{0.0, 1.0};
-  CdfRow R{P.target + (size_t)c * P.V, resid ? P.draft + (size_t)(s * gamma + jr) * P.V : nullptr,
+  const bool sparse = resid && P.cand;
+  if (sparse) load_cand_row(P, s * gamma + jr, cv, cq);
+  __syncthreads();
+  const Merged b = resid && !P.cand ? merged[nt + s * gamma + jr] : Merged{0.0, 1.0};
+  CdfRow R{P.target + (size_t)c * P.V,
+           resid && !P.cand ? P.draft + (size_t)(s * gamma + jr) * P.V : nullptr,
            a.m, a.z, b.m, b.z, inv_t};
+  if (sparse) {
+    R.cv = cv;
+    R.cq = cq;
+    R.k = P.k;
+  }
   const int pick = cdf_draw(P, R, sums, c, philox_uniform(P.seed, P.offset + jr, s, 1), loc, sh, dsh);
   if (tid == 0) {
     P.bonus[s] = pick;
@@ -365,6 +415,18 @@ hipError_t launch_sample_draft(const VerifyLaunch& P, int32_t* block, int Bl, hi
   hipLaunchKernelGGL(cdf_slice_sums<false>, dim3(P.splits, rows), dim3(kCdfThreads), 0, st, P, part,
                      merged, sums);
   hipLaunchKernelGGL(draft_pick, dim3(rows), dim3(kCdfThreads), 0, st, P, merged, sums, block, Bl);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_pq_cand(const VerifyLaunch& P, hipStream_t st) {
+  RowStat* part = reinterpret_cast<RowStat*>(P.part);
+  Merged* merged = reinterpret_cast<Merged*>(P.part2);
+  double* sums = reinterpret_cast<double*>(merged + P.max_rows);
+  const int rows = P.n_seqs * P.Bl;  // target rows only: q comes from the candidate sets
+  hipLaunchKernelGGL(row_softmax_part, dim3(P.splits, rows), dim3(256), 0, st, P, part);
+  hipLaunchKernelGGL(cdf_slice_sums<true>, dim3(P.splits, rows), dim3(kCdfThreads), 0, st, P, part,
+                     merged, sums);
+  hipLaunchKernelGGL(pq_pick, dim3(P.n_seqs), dim3(kCdfThreads), 0, st, P, merged, sums);
   return hipGetLastError();
 }
 

@@ -146,6 +146,19 @@ class Drafter:
                               q.data_ptr() if q is not None else 0)
         return block_ids
 
+    def verify_candidates(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
+                          cand: torch.Tensor, q_rows: torch.Tensor, temperature: float,
+                          seed: int = 0, philox_offset: int = 0):
+        """p/q verification with q on the selector's candidate sets."""
+        n, bl = block_ids.shape
+        tau = torch.empty(n, dtype=torch.int32, device=self.device)
+        bonus = torch.empty(n, dtype=torch.int32, device=self.device)
+        B.dflash_verify_candidates(self.h, n, bl, block_ids.data_ptr(), target_logits.data_ptr(),
+                                   cand.data_ptr(), q_rows.data_ptr(), cand.shape[-1],
+                                   temperature, seed, philox_offset, tau.data_ptr(),
+                                   bonus.data_ptr())
+        return tau, bonus
+
     def verify(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
                draft_logits: Optional[torch.Tensor] = None, temperature: float = 0.0,
                seed: int = 0, philox_offset: int = 0, tau: Optional[torch.Tensor] = None,

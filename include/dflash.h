@@ -351,6 +351,27 @@ dflash_status dflash_select_block(dflash_handle* h, int32_t n_seqs, int32_t bloc
                                   int32_t* block_ids, int32_t* cand_out, float* q_out);
 
 /*
+ * p/q verification with the draft distribution on candidate sets ([Code]
+ * section 14: with the candidate selector the draft's distribution at a row
+ * is the walk's distribution over that row's candidates, so q(x) is summed
+ * over the candidates equal to x, zero for any other token; without this the
+ * rule is no longer lossless). Otherwise dflash_verify at temperature > 0:
+ * row j is accepted iff u_j < p_j(x)/q_j(x) (always when q_j(x) == 0), the
+ * replacement is drawn from max(p_j - q_j, 0) normalised, the bonus from
+ * p_{block_len-1}; same Philox counters, inverse-CDF rule and outputs.
+ * cand:   device int32 [n_seqs, block_len-1, top_k] (dflash_select_block's
+ *         cand_out);
+ * q_rows: device fp32 [n_seqs, block_len-1, top_k] (its q_out);
+ * 1 <= top_k <= 16; temperature > 0 (finite); other arguments and errors as
+ * for dflash_verify.
+ */
+dflash_status dflash_verify_candidates(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                       const int32_t* block_ids, const float* target_logits,
+                                       const int32_t* cand, const float* q_rows, int32_t top_k,
+                                       float temperature, uint64_t seed, uint64_t philox_offset,
+                                       int32_t* tau_out, int32_t* bonus_out);
+
+/*
  * Host helper ([Code] section 5, build_target_layer_ids): n_feat target layer
  * indices spread evenly over 1 .. n_target_layers-3 (0-based), rounded to
  * nearest; the middle layer when n_feat == 1. out: host int32 [n_feat].

@@ -180,6 +180,12 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_select_block, h, 1, 16, FAKE + 4, FAKE, FAKE, 0.0, 0, 0, FAKE) == 5
     assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE, FAKE + 2) == 5
     assert _status(B.dflash_select_block, h, 1, 1, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 0
+    # candidate-set p/q verify
+    assert _status(B.dflash_verify_candidates, h, 1, 16, FAKE, FAKE, FAKE, FAKE, 16, 0.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify_candidates, h, 1, 16, FAKE, FAKE, FAKE, FAKE, 17, 1.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify_candidates, h, 1, 16, FAKE, FAKE, 0, FAKE, 16, 1.0, 0, 0, FAKE, FAKE) == 1
+    assert _status(B.dflash_verify_candidates, h, 3, 16, FAKE, FAKE, FAKE, FAKE, 16, 1.0, 0, 0, FAKE, FAKE) == 3
+    assert _status(B.dflash_verify_candidates, h, 1, 16, FAKE, FAKE, FAKE + 2, FAKE, 16, 1.0, 0, 0, FAKE, FAKE) == 5
     assert _status(B.dflash_set_selector, h, None) == 0
     assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 7
     # device-resident rounds: pointers, shapes, alignment

@@ -94,3 +94,71 @@ def test_tiny_vocab_short_block_and_anchor_outside_vocab():
 
 def test_qwen_shape_block16_ctx2048_full_size():
     _run(CONFIGS[1], [2048])
+
+
+def _cand_case(V, bl, k, rng):
+    gamma = bl - 1
+    cand = np.array([rng.choice(V, k, replace=False) for _ in range(gamma)],
+                    dtype=np.int32).reshape(gamma, k)
+    q = rng.dirichlet(np.ones(k), size=gamma).astype(np.float32).reshape(gamma, k)
+    x = [int(cand[j][np.searchsorted(np.cumsum(q[j].astype(np.float64)), rng.random(), side="right").clip(0, k - 1)])
+         for j in range(gamma)]
+    # now and then a drafted token that is no candidate (always kept)
+    if gamma and rng.random() < 0.3:
+        x[int(rng.integers(0, gamma))] = int(rng.integers(0, V))
+    tl = rng.standard_normal((bl, V)).astype(np.float32)
+    for j in range(gamma):
+        tl[j, cand[j]] += 4.0  # the target likes the candidates too: rows get kept
+    return cand, q, x, tl
+
+
+@pytest.mark.parametrize("ci,bl,k,temp", [(4, 8, 16, 1.0), (0, 4, 3, 0.7), (4, 3, 1, 1.5), (0, 1, 4, 1.0)])
+def test_candidate_verify_matches_oracle(ci, bl, k, temp):
+    dc = CONFIGS[ci]
+    say(f"candidate-set p/q verify: config {dc.name} block_len={bl} k={k} T={temp}")
+    d, _ = make(dc, max_seqs=2)
+    rng = np.random.default_rng(17)
+    checked, kept = 0, 0
+    for trial in range(10):
+        cases = [_cand_case(dc.vocab, bl, k, rng) for _ in range(2)]
+        ids = np.stack([np.array([int(rng.integers(0, dc.vocab))] + c[2], dtype=np.int32) for c in cases])
+        cand = torch.from_numpy(np.stack([c[0] for c in cases]).reshape(2, bl - 1, k)).to(DEV)
+        q = torch.from_numpy(np.stack([c[1] for c in cases]).reshape(2, bl - 1, k)).to(DEV)
+        tl = torch.from_numpy(np.stack([c[3] for c in cases])).to(DEV)
+        seed, off = 5 + trial, 2 * trial
+        tau, bonus = d.verify_candidates(torch.from_numpy(ids).to(DEV), tl, cand, q, temp, seed, off)
+        tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+        for s, (cd, qq, _, t) in enumerate(cases):
+            ref_tau, ref_bonus, diag = O.verify_pq_candidates(ids[s], t, cd, qq, temp, seed, off, s)
+            if min(diag["ratio_margin"] or [1.0]) < 1e-4 or diag["cdf_margin"] < 1e-12:
+                continue
+            assert (tau[s], bonus[s]) == (ref_tau, ref_bonus), (trial, s, diag)
+            checked += 1
+            kept += ref_tau - 1
+    say(f"  blocks compared: {checked}, rows kept: {kept}")
+    assert checked >= 14
+    if bl > 1:
+        assert kept > 0
+
+
+def test_sampled_selection_then_candidate_verify_full_size():
+    # draft -> sampled walk (candidates and q out) -> candidate-set p/q verify
+    dc = CONFIGS[1]
+    d, w = make(dc, max_seqs=1)
+    sel = synth.make_selector(dc, device=DEV)
+    d.set_selector(sel["hidden_proj"], sel["pred_codebook"], sel["succ_codebook"], 16)
+    kv = d.new_kv(2048 + 32)
+    fill_context(kv, synthetic_context(dc, 2048))
+    anc = torch.from_numpy(synth.make_anchor(dc)).to(DEV)
+    block, hid, lg = d.draft_block([kv], anc, hidden=True, logits=True)
+    cand = torch.empty(1, 15, 16, dtype=torch.int32, device=DEV)
+    q = torch.empty(1, 15, 16, dtype=torch.float32, device=DEV)
+    d.select_block(block, hid[dc.n_layers - 1].contiguous(), lg, anc, 1.0, 3, 0, cand, q)
+    tl = torch.cat([lg[0] * 3.0, torch.randn(1, dc.vocab, device=DEV)]).unsqueeze(0).contiguous()
+    tau, bonus = d.verify_candidates(block, tl, cand, q, 1.0, 9, 0)
+    torch.cuda.synchronize()
+    t, b, diag = O.verify_pq_candidates(block.cpu().numpy()[0], np32(tl[0]).astype(np.float64),
+                                        cand.cpu().numpy()[0], np32(q[0]), 1.0, 9, 0, 0)
+    say(f"  tau {int(tau[0])} (oracle {t}), bonus {int(bonus[0])} (oracle {b})")
+    if not (min(diag["ratio_margin"] or [1.0]) < 1e-4 or diag["cdf_margin"] < 1e-12):
+        assert (int(tau[0]), int(bonus[0])) == (t, b)
