@@ -576,6 +576,33 @@ def main():
     copy_gbs = 2.0 * nb / (cp[0] * 1e3)
     del src, dst
 
+    # DFlash 2 candidate selector on the headline block (top-16, rank 256):
+    # the greedy walk, and the sampled walk (T = 1) followed by p/q
+    # verification on the candidate sets
+    sel = synth.make_selector(dc, device=dev)
+    d.set_selector(sel["hidden_proj"], sel["pred_codebook"], sel["succ_codebook"], 16)
+    s_hid = torch.empty(dc.n_layers, Bsz, dc.hidden, dtype=torch.float32, device=dev)
+    s_lg = torch.empty(1, Bsz - 1, dc.vocab, dtype=torch.float32, device=dev)
+    s_blk = torch.empty(1, Bsz, dtype=torch.int32, device=dev)
+    d.draft_block_dev([kv], len_dev, anchors, s_blk, hidden=s_hid, logits=s_lg)
+    s_last = s_hid[dc.n_layers - 1]
+    s_cand = torch.empty(1, Bsz - 1, 16, dtype=torch.int32, device=dev)
+    s_q = torch.empty(1, Bsz - 1, 16, dtype=torch.float32, device=dev)
+    s_tl = torch.cat([s_lg[0] * 3.0, planted[0][0, -1:]]).unsqueeze(0).contiguous()
+    sel_g = _ev_time(lambda: d.select_block(s_blk, s_last, s_lg, anchors), args.steps, torch)
+    sel_s = _ev_time(lambda: d.select_block(s_blk, s_last, s_lg, anchors, 1.0, 1, 0, s_cand, s_q),
+                     args.steps, torch)
+    ver_c = _ev_time(lambda: d.verify_candidates(s_blk, s_tl, s_cand, s_q, 1.0, 2, 0), args.steps, torch)
+    B.dflash_set_selector(d.h, None)
+    # the selector's reads: the drafted rows' logits, the hidden projection,
+    # the last layer's rows and two codes per candidate pair row
+    sel_bytes = ((Bsz - 1) * dc.vocab * 4 + 256 * dc.hidden * 2 + (Bsz - 1) * dc.hidden * 4
+                 + (Bsz - 1) * 2 * 16 * 256 * 2)
+    selector = {"select_greedy_us": round(sel_g[0], 1), "select_sampled_us": round(sel_s[0], 1),
+                "verify_candidates_us": round(ver_c[0], 1), "top_k": 16, "rank": 256,
+                "select_hbm_frac": round(sel_bytes / (sel_g[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "select_over_draft": round(sel_g[0] / draft_e, 4)}
+
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps / elapsed
     dbytes = draft_block_bytes(dc, S0)
@@ -618,6 +645,7 @@ def main():
         "prefill_fuse_mfma_frac": round(fuse_flops / (fuse_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "prefill_inject_us": round(inject_us, 1),
         "prefill_inject_mfma_frac": round(inject_flops / (inject_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "selector": selector,
     }
     if stages_all:
         result["stage_us_per_step"] = stages_all
