@@ -24,6 +24,7 @@ constexpr int kVerifyMaxSplits = 64;
 constexpr int kFuseTileN = 256;     // output columns per fusion GEMM tile
 constexpr int kGemmMaxSplit = 4;    // workgroups sharing one context-GEMM tile
 constexpr int kGemmMaxCounters = 1024;
+constexpr int kTiledK = 64;        // k per stage of the tiled MFMA GEMM (K must be a multiple)
 
 // Split-K scratch of the context GEMMs: fp32 partial tiles and the tiles'
 // arrival counters (zero between launches).

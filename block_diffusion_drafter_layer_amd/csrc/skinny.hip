@@ -1110,15 +1110,15 @@ hipError_t launch_tall(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
   p.ep = ep; p.ssq = a.ssq; p.ssq_ld = a.ssq_ld; p.K = a.K; p.eps = a.eps;
   p.a_group = a.a_group; p.a_stride = a.a_stride; p.a_off = a.a_off;
   // the draft's few-tile products (o_proj, down at 512 rows: 32 tiles) split
-  // K up to 8 ways
-  return launch_tiled<kTallBN, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 16);
+  // K up to 8 ways, down to 512 k per split
+  return launch_tiled<kTallBN, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 512);
 }
 
 // true when launch_skinny takes the tiled GEMM for this shape: more rows
 // than one register-streaming block of 64 (which would stream the weights
 // once per block)
 bool uses_tall(const SkinnyA& a, const GemmWs* tall) {
-  return tall && a.M > 64 && a.xl && a.K % 32 == 0 && a.seg_k == a.K;
+  return tall && a.M > 64 && a.xl && a.K % kTiledK == 0 && a.seg_k == a.K;
 }
 
 template <class Epi, bool LO = true>

@@ -7,13 +7,15 @@
 // load traffic at ~30 B/clk per CU at full MFMA rate, half of what the
 // CU's load path sustains (a 256 x 128 tile needs ~47 B/clk and is bound by
 // it). Operands go straight from global memory into LDS
-// (global_load_lds_dwordx4, no register staging) through a ring of 32-wide k
-// stages, 4 or 5 of them, so 3-4 stages are in flight while one is
-// multiplied. Each 1 KB load instruction covers sixteen 64-byte tile rows;
-// 16-byte chunk c of row r is stored at chunk c ^ ((r >> 2) & 3), so a
-// fragment read (sixteen consecutive lanes on sixteen rows, same chunk)
-// touches 64 distinct banks. Fragment reads for the next 16-wide k step are
-// issued before the MFMAs of the current one.
+// (global_load_lds_dwordx4, no register staging) in 64-wide k stages, two of
+// them (64 or 72 KB each): while one is multiplied the next one loads. Each
+// 1 KB load instruction covers eight 128-byte tile rows: the load path keeps
+// a bounded number of requests in flight per CU, and 128-byte row pieces move
+// more bytes per request than 64-byte ones. 16-byte chunk c of row r is
+// stored at chunk c ^ ((r >> 1) & 7), so a fragment read (sixteen
+// consecutive lanes on sixteen rows, same chunk) touches 64 distinct banks.
+// Fragment reads for the next 16-wide k step are issued before the MFMAs of
+// the current one.
 //
 // Split K: when the tiles alone would leave CUs idle, S workgroups share a
 // tile, each over K/S. They sit on one XCD (workgroups go to XCDs round-robin
@@ -36,8 +38,9 @@
 namespace dfl {
 
 namespace {
-constexpr int BM = 256, BK = 32;
+constexpr int BM = 256, BK = kTiledK;
 constexpr int kRow = BK * 2;         // bytes per tile row and stage
+constexpr int NS = 2;                // stages in LDS
 constexpr int kLds = 160 * 1024;
 constexpr int kSlice = 64;           // epilogue rows per LDS pass
 
@@ -45,11 +48,11 @@ template <int BN>
 struct TileCfg;
 template <>
 struct TileCfg<256> {
-  static constexpr int W = 8, WGM = 2, NS = 5;  // waves, waves along M, ring stages
+  static constexpr int W = 8, WGM = 2;  // waves, waves along M
 };
 template <>
 struct TileCfg<320> {
-  static constexpr int W = 8, WGM = 4, NS = 4;
+  static constexpr int W = 8, WGM = 4;
 };
 }  // namespace
 
@@ -119,22 +122,24 @@ __device__ __forceinline__ void frag_wait(u32x4 (&f)[7]) {
                : "n"(N));
 }
 
-// the TI A fragments (32-row blocks 2 KB apart) then the TJ B fragments
+// the TI A fragments (32-row blocks 32 * kRow = 4 KB apart) then the TJ B
+// fragments
 template <int TI, int TJ>
 __device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint32_t b) {
+  static_assert(32 * kRow == 4096, "fragment block stride");
   ds_frag<0>(f[0], a);
-  ds_frag<2048>(f[1], a);
+  ds_frag<4096>(f[1], a);
   if constexpr (TI > 2) {
-    ds_frag<4096>(f[2], a);
-    ds_frag<6144>(f[3], a);
+    ds_frag<8192>(f[2], a);
+    ds_frag<12288>(f[3], a);
   }
   ds_frag<0>(f[TI], b);
-  ds_frag<2048>(f[TI + 1], b);
+  ds_frag<4096>(f[TI + 1], b);
   if constexpr (TJ > 2) {
-    ds_frag<4096>(f[TI + 2], b);
-    ds_frag<6144>(f[TI + 3], b);
+    ds_frag<8192>(f[TI + 2], b);
+    ds_frag<12288>(f[TI + 3], b);
   }
-  if constexpr (TJ > 4) ds_frag<8192>(f[TI + 4], b);
+  if constexpr (TJ > 4) ds_frag<16384>(f[TI + 4], b);
 }
 
 
@@ -143,18 +148,6 @@ __device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint
 
 template <int N>
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(DFL_VM(N)); }
-
-// wait until at most `stages` whole stages of this wave's loads (L each) are
-// in flight
-template <int L>
-__device__ __forceinline__ void wait_stages(int stages) {
-  switch (stages) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<L>(); break;
-    case 2: wait_vm<2 * L>(); break;
-    default: wait_vm<3 * L>(); break;
-  }
-}
 
 // Workgroup -> (tile, split). With a multiple of 8 tiles, XCD x (workgroup id
 // % 8) takes a contiguous chunk of tiles, walked in groups of 4 tile rows
@@ -185,13 +178,12 @@ __global__ void __launch_bounds__(TileCfg<BN>::W * 64)
 ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   using Cfg = TileCfg<BN>;
   constexpr int kWaves = Cfg::W;
-  constexpr int NS = Cfg::NS;
   constexpr int WGM = Cfg::WGM, WGN = kWaves / WGM;
   constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TI = WM / 32, TJ = WN / 32;
   constexpr int kStage = (BM + BN) * kRow;
-  constexpr int kLoadsA = BM / 16 / kWaves;           // A loads per wave and stage
-  constexpr int kLoadsBTot = BN / 16;                 // B loads per stage
+  constexpr int kLoadsA = BM / 8 / kWaves;            // A loads per wave and stage
+  constexpr int kLoadsBTot = BN / 8;                  // B loads per stage
   constexpr int kLoadsBMax = (kLoadsBTot + kWaves - 1) / kWaves;
   static_assert(NS * kStage <= kLds, "ring fits in LDS");
   static_assert(kSlice * (BN + 8) * 4 + 16 * BN <= NS * kStage,
@@ -210,33 +202,45 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   const int kt0 = sidx * kt_per;
   const int KT = max(0, min(KT_all - kt0, kt_per));
 
-  // Loads: instruction b covers tile rows 16b .. 16b+15 (of A, then of B);
-  // wave w issues A instructions w, w + 8 and B instructions w, w + 8, ...
-  // Lane l fetches row 16b + l/4, chunk (l%4) ^ ((l/16) & 3), and lands at
-  // byte 16 l of the instruction's kilobyte.
-  const int lrow = lane >> 2;
-  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  // Loads: instruction b covers tile rows 8b .. 8b+7 (of A, then of B);
+  // wave w issues A instructions w, w + 8, ... and B instructions w, w + 8,
+  // ... Lane l fetches row r = 8b + l/8, chunk (l%8) ^ ((r >> 1) & 7), and
+  // lands at byte 16 l of the instruction's kilobyte.
+  const int lrow = lane >> 3;
+  auto lchunk = [&](int b) { return ((lane & 7) ^ (((8 * b + lrow) >> 1) & 7)) * 8; };
   const int nb = (kLoadsBTot % kWaves == 0 || w < kLoadsBTot % kWaves) ? kLoadsBMax : kLoadsBMax - 1;
   int64_t aoff[kLoadsA];
   const bf16_t* bptr[kLoadsBMax];
 #pragma unroll
   for (int q = 0; q < kLoadsA; ++q) {
-    int m = m0 + 16 * (w + kWaves * q) + lrow;
+    const int b = w + kWaves * q;
+    int m = m0 + 8 * b + lrow;
     m = m < a.M ? m : a.M - 1;
     m = (m / a.a_group) * a.a_stride + a.a_off + m % a.a_group;
-    aoff[q] = (int64_t)m * a.ld + lchunk;
+    aoff[q] = (int64_t)m * a.ld + lchunk(b);
   }
 #pragma unroll
   for (int q = 0; q < kLoadsBMax; ++q) {
-    int n = n0 + 16 * (w + kWaves * q) + lrow;
+    const int b = w + kWaves * q;
+    int n = n0 + 8 * b + lrow;
     n = n < N ? n : N - 1;
-    bptr[q] = Epi::wrow(p, n) + lchunk;
+    bptr[q] = Epi::wrow(p, n) + lchunk(b);
   }
+  // the current A segment: its pointer is loaded only when a stage enters a
+  // new segment (a load of it every stage would come with a wait that also
+  // drains the fragment reads in flight)
+  int seg_cur = -1;
+  const bf16_t* seg_base = nullptr;
   auto issue = [&](int kt) {
     uint8_t* st = smem + (kt % NS) * kStage;
     const int k0 = (kt0 + kt) * BK;
     const int sg = k0 / a.seg_k;
-    const bf16_t* base = a.seg[sg] + (k0 - sg * a.seg_k);
+    if (sg != seg_cur) {
+      seg_cur = sg;
+      seg_base = a.seg[sg];
+      asm volatile("" : "+s"(seg_base));  // complete here, not at every stage's join
+    }
+    const bf16_t* base = seg_base + (k0 - sg * a.seg_k);
     const int kb = k0 < a.b_k ? k0 : k0 - a.b_k;
 #pragma unroll
     for (int q = 0; q < kLoadsA; ++q) dma16(base + aoff[q], st + (w + kWaves * q) * 1024);
@@ -244,19 +248,17 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
     for (int q = 0; q < kLoadsBMax; ++q)
       if (q < nb) dma16(bptr[q] + kb, st + BM * kRow + (w + kWaves * q) * 1024);
   };
-  auto wait_tiles = [&](int stages) {  // this wave's loads per stage differ by wave
-    if (nb == kLoadsBMax) wait_stages<kLoadsA + kLoadsBMax>(stages);
-    else wait_stages<kLoadsA + kLoadsBMax - 1>(stages);
-  };
-
   // fragment addresses: lane l reads row l % 32 of a 32-row block at chunk
-  // (2 kk + l / 32) ^ ((l / 4) & 3), kk the 16-wide step within the stage
+  // (2 kk + l / 32) ^ (((l % 32) >> 1) & 7), kk the 16-wide step within the
+  // stage (32-row blocks start at multiples of 32, so the swizzle of a row
+  // depends on l % 32 alone)
+  constexpr int KK = BK / 16;
   const uint32_t sbase = (uint32_t)(uintptr_t)smem;
   const int fr = lane & 31;
-  uint32_t foff[2];
+  uint32_t foff[KK];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-    foff[kk] = fr * kRow + (((2 * kk + (lane >> 5)) ^ ((lane >> 2) & 3)) << 4);
+  for (int kk = 0; kk < KK; ++kk)
+    foff[kk] = fr * kRow + (((2 * kk + (lane >> 5)) ^ ((fr >> 1) & 7)) << 4);
   const uint32_t a_f = sbase + (uint32_t)(wm * WM) * kRow;
   const uint32_t b_f = sbase + (uint32_t)(BM * kRow) + (uint32_t)(wn * WN) * kRow;
 
@@ -268,35 +270,35 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Per stage t (ring slot t % NS): two 16-wide k steps; each issues the
-  // next step's fragment reads before its own MFMAs. The second step waits
-  // for this wave's loads of stage t+1 and meets the other waves at a
-  // barrier: past it, stage t+1 is in LDS and nobody reads slot (t-1) % NS
-  // any more, so stage t+NS-1 is loaded into it, and stage t+1's first
-  // fragments are read under the MFMAs of stage t's second step. (A plain
-  // barrier: a fence would also wait for the loads still in flight.)
+  // Stage t sits in slot t % 2 and is multiplied in four 16-wide k steps;
+  // each step issues the next step's fragment reads before its own MFMAs.
+  // Stage t + 1 is loaded into the other slot from the start of stage t: its
+  // previous contents (stage t - 1) were read by every wave before the
+  // barrier that opened stage t. The last step waits for this wave's loads
+  // of stage t + 1 and meets the other waves at a barrier; past it stage
+  // t + 1 is in LDS, and its first fragments are read under the MFMAs of
+  // stage t's last step. (A plain barrier: a fence would also wait for loads
+  // still in flight.)
   if (KT > 0) {
-    const int pre = min(KT, NS - 1);
-    for (int t = 0; t < pre; ++t) issue(t);
-    wait_tiles(pre - 1);
+    issue(0);
+    wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     u32x4 f[2][TI + TJ];
     frag_issue<TI, TJ>(f[0], a_f + foff[0], b_f + foff[0]);
     for (int kt = 0; kt < KT; ++kt) {
-      const uint32_t st = (uint32_t)((kt % NS) * kStage);
+      const uint32_t st = (uint32_t)((kt & 1) * kStage);
+      if (kt + 1 < KT) issue(kt + 1);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 0) {
-          frag_issue<TI, TJ>(f[1], a_f + st + foff[1], b_f + st + foff[1]);
-          frag_wait<TI + TJ>(f[0]);
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          frag_issue<TI, TJ>(f[(kk + 1) & 1], a_f + st + foff[kk + 1], b_f + st + foff[kk + 1]);
+          frag_wait<TI + TJ>(f[kk & 1]);
         } else {
-          frag_wait<0>(f[1]);
+          frag_wait<0>(f[kk & 1]);
           if (kt + 1 < KT) {
-            // stages issued so far: up to min(kt + NS - 2, KT - 1)
-            wait_tiles(min(NS - 3, KT - kt - 2));
+            wait_vm<0>();
             __builtin_amdgcn_s_barrier();
-            if (kt + NS - 1 < KT) issue(kt + NS - 1);
-            const uint32_t sn = (uint32_t)(((kt + 1) % NS) * kStage);
+            const uint32_t sn = (uint32_t)(((kt + 1) & 1) * kStage);
             frag_issue<TI, TJ>(f[0], a_f + sn + foff[0], b_f + sn + foff[0]);
           }
         }
@@ -308,8 +310,8 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
         for (int i = 0; i < TI; ++i)
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
-            acc[i][j] = mfma32x32x16(__builtin_bit_cast(bf16x8, f[kk][i]),
-                                     __builtin_bit_cast(bf16x8, f[kk][TI + j]), acc[i][j]);
+            acc[i][j] = mfma32x32x16(__builtin_bit_cast(bf16x8, f[kk & 1][i]),
+                                     __builtin_bit_cast(bf16x8, f[kk & 1][TI + j]), acc[i][j]);
         __builtin_amdgcn_s_setprio(0);
         // keep this step's MFMAs ahead of the next step's reads and waits
         __builtin_amdgcn_sched_barrier(0);
@@ -389,25 +391,25 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   }
 }
 
-// Split count: the smallest S in {1, 2, 4} that gives the grid at least 256
-// workgroups, when the tiles are a multiple of 8 (so the splits of a tile
-// share an XCD) and each split keeps at least 32 k stages.
-// Split K while the doubled grid still fits one workgroup per CU and each
-// split keeps at least min_stages k stages (its prologue and epilogue are
-// then a small part of it).
-static int choose_split(int tiles, int K, int max_split, int min_stages) {
+// Split count: when the tiles are a multiple of 8 (so the splits of a tile
+// share an XCD), K is split while the doubled grid still fits one workgroup
+// per CU and each split keeps at least min_k of K (its prologue and epilogue
+// are then a small part of it).
+static int choose_split(int tiles, int K, int max_split, int min_k) {
   if (tiles % 8) return 1;
   int S = 1;
-  while (2 * S <= max_split && tiles * 2 * S <= 256 && K / BK / (2 * S) >= min_stages) S *= 2;
+  while (2 * S <= max_split && tiles * 2 * S <= 256 && K / (2 * S) >= min_k) S *= 2;
   return S;
 }
 
 template <int BN, class Epi>
 static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, const GemmWs& ws,
-                               hipStream_t st, int max_split = kGemmMaxSplit, int min_stages = 32) {
+                               hipStream_t st, int max_split = kGemmMaxSplit, int min_k = 1024) {
+  // whole 64-wide k stages, none straddling an A segment or B's wrap
+  if (a.K % BK || a.seg_k % BK || a.b_k % BK) return hipErrorInvalidValue;
   const int tiles = ((a.M + BM - 1) / BM) * ((N + BN - 1) / BN);
   GemmSplit sp;
-  sp.S = choose_split(tiles, a.K, max_split, min_stages);
+  sp.S = choose_split(tiles, a.K, max_split, min_k);
   if (sp.S > 1 && (!ws.part || !ws.ctr || (size_t)tiles * sp.S * BM * BN > ws.part_floats ||
                    tiles > ws.n_ctr))
     sp.S = 1;
