@@ -98,6 +98,15 @@ def test_mid_shape_tall_batch():
     _run(dc, [33, 300, 5, 1031, 64, 129], gains="random", logits=True)
 
 
+def test_mid_shape_tall_batch_ffn_not_a_multiple_of_64():
+    # ffn = 1056: the down projection's K is not a whole number of the tiled
+    # GEMM's 64-wide k stages, so those 80 rows take the register-streaming
+    # kernel while the other products stay on the tiled path
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=8, n_kv_heads=2, ffn=1056,
+                           vocab=3000, index=89)
+    _run(dc, [70, 3, 500, 0, 31], gains="random", logits=True)
+
+
 def test_d2048_block8_full_size():
     _run(CONFIGS[4], [2048], logits=True)
 
