@@ -82,7 +82,7 @@ def summarize_trace(db, out, cmd):
         f.write(f"# {'kernel':<78s} {'calls':>6s} {'total_us':>10s} {'avg_us':>9s} {'min_us':>9s} "
                 f"{'max_us':>9s} {'%':>6s}\n")
         for n, cnt, sm, av, mn, mx in rows:
-            short = re.sub(r"\(.*", "", n)[:78]
+            short = re.sub(r"\(.*", "", n.replace("(anonymous namespace)::", ""))[:78]
             f.write(f"{short:<80s} {cnt:6d} {sm / 1e3:10.1f} {av / 1e3:9.2f} {mn / 1e3:9.2f} "
                     f"{mx / 1e3:9.2f} {100 * sm / tot:6.2f}\n")
 
@@ -555,7 +555,9 @@ def main():
         for j in range(n_plant):
             with torch.cuda.graph(g_rest[j], stream=side):
                 dev_rest(j)
-        B.dflash_set_stream(d.h, torch.cuda.current_stream().cuda_stream)
+    # back on the default stream (outside the side-stream context, where the
+    # current stream is the default one again)
+    B.dflash_set_stream(d.h, torch.cuda.current_stream().cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     el_g, _, draft_g = timed_rounds(g_draft.replay, lambda j: g_rest[j].replay())
