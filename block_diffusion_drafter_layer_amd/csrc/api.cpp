@@ -788,9 +788,9 @@ dflash_status dflash_set_selector(dflash_handle* h, const dflash_selector* sel) 
                 kSelMaxK);
   if (sel->rank < 64 || sel->rank > kSelMaxRank || sel->rank % 64)
     return fail(DFLASH_E_SHAPE, "rank=%d: 64..%d in steps of 64", sel->rank, kSelMaxRank);
-  if (sel_slices(h->cfg.vocab) * sel->top_k > sel_max_merge_keys())
-    return fail(DFLASH_E_SHAPE, "vocab=%d with top_k=%d exceeds the selector's merge", h->cfg.vocab,
-                sel->top_k);
+  if (sel_slices(h->cfg.vocab) > sel_max_slices())
+    return fail(DFLASH_E_SHAPE, "vocab=%d exceeds the selector's %d vocab slices", h->cfg.vocab,
+                sel_max_slices());
   if (h->cfg.hidden % 64)
     return fail(DFLASH_E_SHAPE, "the selector needs hidden %% 64 == 0 (hidden=%d)", h->cfg.hidden);
   if (!aligned(sel->hidden_proj, 16) || !aligned(sel->pred_codebook, 16) ||

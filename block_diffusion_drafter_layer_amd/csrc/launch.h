@@ -201,7 +201,7 @@ struct SelectLaunch {
 int sel_slices(int V);
 int sel_kz(int D);
 int sel_max_walk_rows();
-int sel_max_merge_keys();
+int sel_max_slices();
 hipError_t launch_select(const SelectLaunch& L, hipStream_t st);
 
 // reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)

@@ -11,7 +11,7 @@
 // Kernels, in order:
 //   sel_topk_slices  (row, vocab slice): the slice's k largest (logit, index)
 //                    keys, in decreasing order
-//   sel_project      (64 outputs, 16 rows, 256-wide k slice): partial sums of
+//   sel_project      (64 outputs, 16 rows, 128-wide k slice): partial sums of
 //                    W_h (x * gain) and of x^2 for the final norm
 //   sel_pairs        (row, sequence): merges the slice lists of the row and of
 //                    the row before (the predecessors; the anchor for row 0),
@@ -25,10 +25,10 @@ namespace dfl {
 
 namespace {
 
-constexpr int kSelPer = 8;                      // logits per thread in a slice
-constexpr int kSelSlice = 256 * kSelPer;        // vocab entries per slice
-constexpr int kSelMergePer = 8;                 // slice keys per thread in a merge
-constexpr int kSelKSlice = 256;                 // k extent of one projection partial
+constexpr int kSelPer = 8;                      // logits per lane in a wave's part of a slice
+constexpr int kSelSlice = 4 * 64 * kSelPer;     // vocab entries per slice (4 waves)
+constexpr int kSelMaxSlices = 128;              // slice lists a row merge takes (two per lane)
+constexpr int kSelKSlice = 128;                 // k extent of one projection partial
 constexpr int kSelMaxWalkRows = 64;             // rows a walk keeps in LDS
 
 __device__ __forceinline__ float key_value(uint64_t key) {
@@ -37,39 +37,129 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float(u);
 }
 
-// Block-wide maximum of one key per thread (256 threads); wb: 4 slots of LDS.
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* wb) {
-  v = wave_max_u64(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) wb[w] = v;
-  __syncthreads();
-  v = umax64(umax64(wb[0], wb[1]), umax64(wb[2], wb[3]));
-  __syncthreads();  // wb is reused by the next call
-  return v;
+// Wave maximum of an unsigned 32-bit value: DPP shifts within each row of 16
+// lanes (lane 15 of a row ends with the row's maximum), then the four row
+// maxima through scalar registers.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  uint32_t t;
+  t = __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v = v > t ? v : t;
+  t = __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v = v > t ? v : t;
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47), r3 = __builtin_amdgcn_readlane(v, 63);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
 }
 
+// Wave maximum of a 64-bit key: the high words (the value) by DPP; the low
+// words (the index) only when several lanes hold that value. Every lane gets
+// the result.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  const uint32_t hv = (uint32_t)(v >> 32);
+  const uint32_t hi = wave_max_u32_dpp(hv);
+  const uint64_t holders = __ballot(hv == hi);
+  uint32_t lo;
+  if (__popcll(holders) == 1) {
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __ffsll((unsigned long long)holders) - 1);
+  } else {
+    lo = wave_max_u32_dpp(hv == hi ? (uint32_t)v : 0u);
+  }
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void cswap_desc(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = umax64(a, b), lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// the 8 keys of a lane in decreasing order (a 19-comparator sorting network)
+__device__ __forceinline__ void sort8_desc(uint64_t (&k)[8]) {
+  cswap_desc(k[0], k[1]); cswap_desc(k[2], k[3]); cswap_desc(k[4], k[5]); cswap_desc(k[6], k[7]);
+  cswap_desc(k[0], k[2]); cswap_desc(k[1], k[3]); cswap_desc(k[4], k[6]); cswap_desc(k[5], k[7]);
+  cswap_desc(k[1], k[2]); cswap_desc(k[5], k[6]); cswap_desc(k[0], k[4]); cswap_desc(k[3], k[7]);
+  cswap_desc(k[1], k[5]); cswap_desc(k[2], k[6]);
+  cswap_desc(k[1], k[4]); cswap_desc(k[3], k[6]);
+  cswap_desc(k[2], k[4]); cswap_desc(k[3], k[5]);
+  cswap_desc(k[3], k[4]);
+}
+
+// k rounds of wave maxima over sorted per-lane lists (each in decreasing
+// order, 0 = empty); the lane holding a round's key drops it by shifting its
+// list. Keys are unique (the index is part of them). out[r] by lane 0.
+template <int N>
+__device__ __forceinline__ void wave_top_k(uint64_t (&key)[N], int k, uint64_t* out) {
+  for (int r = 0; r < k; ++r) {
+    const uint64_t best = wave_max_key(key[0]);
+    if (key[0] == best && best != 0ull) {
+#pragma unroll
+      for (int i = 0; i + 1 < N; ++i) key[i] = key[i + 1];
+      key[N - 1] = 0;
+    }
+    if ((threadIdx.x & 63) == 0) out[r] = best;
+  }
+}
+
+// Two sorted lists per lane (the lane's two slices of a row): the round's
+// key leaves whichever list holds it.
+template <int N>
+__device__ __forceinline__ void wave_top_k2(uint64_t (&ka)[N], uint64_t (&kb)[N], int k,
+                                            uint64_t* out) {
+  for (int r = 0; r < k; ++r) {
+    const uint64_t best = wave_max_key(umax64(ka[0], kb[0]));
+    if (best != 0ull && ka[0] == best) {
+#pragma unroll
+      for (int i = 0; i + 1 < N; ++i) ka[i] = ka[i + 1];
+      ka[N - 1] = 0;
+    } else if (best != 0ull && kb[0] == best) {
+#pragma unroll
+      for (int i = 0; i + 1 < N; ++i) kb[i] = kb[i + 1];
+      kb[N - 1] = 0;
+    }
+    if ((threadIdx.x & 63) == 0) out[r] = best;
+  }
+}
+
+// (row, vocab slice): each wave takes the top k of its 512 logits, then wave 0
+// takes the top k of the four wave lists.
 __global__ void __launch_bounds__(256)
 sel_topk_slices(const float* __restrict__ logits, int V, int n_slices, int k,
                 uint64_t* __restrict__ part) {
-  __shared__ uint64_t wb[4];
+  __shared__ uint64_t wl[4][kSelMaxK];
   const int sl = blockIdx.x, row = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* z = logits + (size_t)row * V;
-  const int v0 = sl * kSelSlice;
+  const int v0 = sl * kSelSlice + w * 64 * kSelPer;
+  static_assert(kSelPer == 8, "sort8_desc sorts the lane's keys");
+  // every load from a clamped address first, all in flight together
+  float zv[kSelPer];
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int v = v0 + lane + 64 * i;
+    zv[i] = z[v < V ? v : V - 1];
+  }
   uint64_t key[kSelPer];
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int v = v0 + (int)threadIdx.x + 256 * i;
-    key[i] = v < V ? argmax_key(z[v], (uint32_t)v) : 0ull;  // 0: no entry (below every key)
+    const int v = v0 + lane + 64 * i;
+    key[i] = v < V ? argmax_key(zv[i], (uint32_t)v) : 0ull;  // 0: no entry (below every key)
   }
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
+  sort8_desc(key);
+  wave_top_k(key, k, wl[w]);
+  __syncthreads();
+  if (w == 0) {  // lanes 0..3 hold the four wave lists (already in decreasing order)
+    uint64_t m[kSelMaxK];
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i) best = umax64(best, key[i]);
-    best = block_max_u64(best, wb);
-#pragma unroll
-    for (int i = 0; i < kSelPer; ++i)
-      if (key[i] == best) key[i] = 0;  // keys are unique (the index is part of them)
-    if (threadIdx.x == 0) part[((size_t)row * n_slices + sl) * k + r] = best;
+    for (int i = 0; i < kSelMaxK; ++i) m[i] = lane < 4 && i < k ? wl[lane][i] : 0ull;
+    // the merged list goes to LDS round by round and to memory in one store
+    // at the end (a store per round would be waited for by the next one)
+    wave_top_k(m, k, wl[3]);
+    if (lane < k) part[((size_t)row * n_slices + sl) * k + lane] = wl[3][lane];
   }
 }
 
@@ -138,27 +228,26 @@ sel_project(const float* __restrict__ x, int D, int Bl, int P, int rows,
   }
 }
 
-// Top-k of one row from its slice lists: k rounds of a block-wide maximum
-// over n keys (n <= 256 * kSelMergePer). Returns the keys in decreasing order
-// in out[0..k).
-__device__ __forceinline__ void merge_row(const uint64_t* __restrict__ src, int n, int k,
-                                          uint64_t* out, uint64_t* wb) {
-  uint64_t key[kSelMergePer];
+// One wave: the top k of a row's slice lists (n_slices sorted lists of k
+// keys, n_slices <= 128): lane l holds lists l and l + 64.
+__device__ __forceinline__ void wave_merge_row(const uint64_t* __restrict__ src, int n_slices, int k,
+                                               uint64_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint64_t ka[kSelMaxK], kb[kSelMaxK];
+  const int la = lane < n_slices ? lane : n_slices - 1;
+  const int lb = lane + 64 < n_slices ? lane + 64 : n_slices - 1;
 #pragma unroll
-  for (int i = 0; i < kSelMergePer; ++i) {
-    const int e = (int)threadIdx.x + 256 * i;
-    key[i] = e < n ? src[e] : 0ull;
+  for (int i = 0; i < kSelMaxK; ++i) {  // clamped loads, all in flight together
+    const int ii = i < k ? i : k - 1;
+    ka[i] = src[(size_t)la * k + ii];
+    kb[i] = src[(size_t)lb * k + ii];
   }
-  for (int r = 0; r < k; ++r) {
-    uint64_t best = 0;
 #pragma unroll
-    for (int i = 0; i < kSelMergePer; ++i) best = umax64(best, key[i]);
-    best = block_max_u64(best, wb);
-#pragma unroll
-    for (int i = 0; i < kSelMergePer; ++i)
-      if (key[i] == best) key[i] = 0;
-    if (threadIdx.x == 0) out[r] = best;
+  for (int i = 0; i < kSelMaxK; ++i) {
+    ka[i] = lane < n_slices && i < k ? ka[i] : 0ull;
+    kb[i] = lane + 64 < n_slices && i < k ? kb[i] : 0ull;
   }
+  wave_top_k2(ka, kb, k, out);
 }
 
 __global__ void __launch_bounds__(256)
@@ -167,7 +256,6 @@ sel_pairs(const uint64_t* __restrict__ part, int n_slices, int k, const float* _
           const bf16_t* __restrict__ A, const bf16_t* __restrict__ B, int rank,
           const int32_t* __restrict__ anchors, int P, int V, float* __restrict__ S,
           int32_t* __restrict__ cand) {
-  __shared__ uint64_t wb[4];
   __shared__ uint64_t top[2][kSelMaxK];
   __shared__ int32_t pid[kSelMaxK], cid[kSelMaxK];
   __shared__ float unary[kSelMaxK];
@@ -175,21 +263,41 @@ sel_pairs(const uint64_t* __restrict__ part, int n_slices, int k, const float* _
   __shared__ float ta[kSelMaxK][kSelMaxRank + 1];  // A[pred a] * g
   __shared__ float tb[kSelMaxK][kSelMaxRank + 1];  // B[candidate b]
   const int j = blockIdx.x, s = blockIdx.y, m = s * P + j;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, w = t >> 6;
   const int n = n_slices * k;
-  if (j > 0) merge_row(part + (size_t)(m - 1) * n, n, k, top[0], wb);
-  merge_row(part + (size_t)m * n, n, k, top[1], wb);
-  __syncthreads();  // top[] complete
-  // g = rs * sum of the k-slice partials (slice order), rs the final norm's
-  // row scale of row m
-  float ss = 0.f;
-  for (int z = 0; z < kz_n; ++z) ss += spart[(size_t)z * rows + m];
-  const float rs = rsqrtf(ss / (float)D + eps);
-  for (int o = t; o < rank; o += 256) {
-    float acc = 0.f;
-    for (int z = 0; z < kz_n; ++z) acc += gpart[((size_t)z * rows + m) * rank + o];
-    g[o] = acc * rs;
+  // wave 0 merges this row's slice lists, wave 1 the previous row's (the
+  // predecessors); waves 2 and 3 form g meanwhile
+  if (w == 0) wave_merge_row(part + (size_t)m * n, n_slices, k, top[1]);
+  if (w == 1 && j > 0) wave_merge_row(part + (size_t)(m - 1) * n, n_slices, k, top[0]);
+  if (w >= 2) {
+    // g = rs * sum of the k-slice partials (slice order), rs the final norm's
+    // row scale of row m; the loads of 8 slices at a time are in flight
+    // together
+    const int tt = t - 128;
+    float ss = 0.f, acc0 = 0.f, acc1 = 0.f;
+    const int o0 = tt, o1 = tt + 128;
+    for (int z0 = 0; z0 < kz_n; z0 += 8) {
+      float sv[8], a0[8], a1[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int z = z0 + u < kz_n ? z0 + u : kz_n - 1;
+        sv[u] = spart[(size_t)z * rows + m];
+        a0[u] = gpart[((size_t)z * rows + m) * rank + (o0 < rank ? o0 : 0)];
+        a1[u] = gpart[((size_t)z * rows + m) * rank + (o1 < rank ? o1 : 0)];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (z0 + u < kz_n) {
+          ss += sv[u];
+          acc0 += a0[u];
+          acc1 += a1[u];
+        }
+    }
+    const float rs = rsqrtf(ss / (float)D + eps);
+    if (o0 < rank) g[o0] = acc0 * rs;
+    if (o1 < rank) g[o1] = acc1 * rs;
   }
+  __syncthreads();
   if (t < kSelMaxK) {
     const bool live = t < k;
     const uint64_t kb = top[1][live ? t : 0];
@@ -200,68 +308,115 @@ sel_pairs(const uint64_t* __restrict__ part, int n_slices, int k, const float* _
     pid[t] = j == 0 ? an : (live ? (int32_t)argmax_key_index(top[0][t]) : 0);
   }
   __syncthreads();
-  for (int e = t; e < kSelMaxK * rank; e += 256) {
-    const int row = e / rank, x = e - row * rank;
-    ta[row][x] = bf2f(A[(size_t)pid[row] * rank + x]) * g[x];
-    tb[row][x] = bf2f(B[(size_t)cid[row] * rank + x]);
+  // codes: 16-byte loads, rank / 8 per row and table
+  const int per_row = rank / 8;
+  for (int e = t; e < kSelMaxK * per_row; e += 256) {
+    const int row = e / per_row, x8 = (e - row * per_row) * 8;
+    const uint4 av = *reinterpret_cast<const uint4*>(A + (size_t)pid[row] * rank + x8);
+    const uint4 bv = *reinterpret_cast<const uint4*>(B + (size_t)cid[row] * rank + x8);
+    const uint32_t au[4] = {av.x, av.y, av.z, av.w}, bu[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ta[row][x8 + 2 * i] = __uint_as_float(au[i] << 16) * g[x8 + 2 * i];
+      ta[row][x8 + 2 * i + 1] = __uint_as_float(au[i] & 0xffff0000u) * g[x8 + 2 * i + 1];
+      tb[row][x8 + 2 * i] = __uint_as_float(bu[i] << 16);
+      tb[row][x8 + 2 * i + 1] = __uint_as_float(bu[i] & 0xffff0000u);
+    }
   }
   __syncthreads();
   const int a = t >> 4, b = t & 15;
-  float dot = 0.f;
-  for (int x = 0; x < rank; ++x) dot += ta[a][x] * tb[b][x];
+  float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+  for (int x = 0; x < rank; x += 4) {
+    d0 += ta[a][x] * tb[b][x];
+    d1 += ta[a][x + 1] * tb[b][x + 1];
+    d2 += ta[a][x + 2] * tb[b][x + 2];
+    d3 += ta[a][x + 3] * tb[b][x + 3];
+  }
+  const float dot = (d0 + d1) + (d2 + d3);
   S[((size_t)m * kSelMaxK + a) * kSelMaxK + b] = b < k ? unary[b] + dot : -INFINITY;
   if (t < kSelMaxK) cand[(size_t)m * kSelMaxK + t] = t < k ? cid[t] : -1;
+}
+
+// v of the lane CTRL (a DPP row shift) names, 0 where that lane lies outside
+// the row of 16
+template <int CTRL>
+__device__ __forceinline__ double row_shr_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 // One wave per sequence: row tables into LDS, then the walk. Greedy (inv_T
 // == 0): the candidate of largest score, lowest position on ties. Sampling:
 // q = softmax(S / T) over the k candidates in fp64, running sums in candidate
-// order, the first candidate whose running sum exceeds u * total, u the
-// Philox uniform of counter (offset + row, sequence, 3, 0).
+// order (a parallel scan: the association differs from a left-to-right sum
+// by rounding only), the first candidate whose running sum exceeds u * total, u the
+// Philox uniform of counter (offset + row, sequence, 3, 0) (drawn for every
+// row up front, one lane each).
 __global__ void __launch_bounds__(64)
 sel_walk(const float* __restrict__ S, const int32_t* __restrict__ cand, int P, int k, int Bl,
          double inv_T, uint64_t seed, uint64_t offset, int32_t* __restrict__ block,
          int32_t* __restrict__ cand_out, float* __restrict__ q_out) {
-  __shared__ float tab[kSelMaxWalkRows][kSelMaxK][kSelMaxK];
+  __shared__ float4 tab4[kSelMaxWalkRows * kSelMaxK * kSelMaxK / 4];
   __shared__ int32_t ct[kSelMaxWalkRows][kSelMaxK];
-  __shared__ double ex[kSelMaxK];
   const int s = blockIdx.x, lane = threadIdx.x;
-  const float* src = S + (size_t)s * P * kSelMaxK * kSelMaxK;
-  for (int e = lane; e < P * kSelMaxK * kSelMaxK; e += 64) (&tab[0][0][0])[e] = src[e];
-  for (int e = lane; e < P * kSelMaxK; e += 64) (&ct[0][0])[e] = cand[(size_t)s * P * kSelMaxK + e];
+  const float4* src = reinterpret_cast<const float4*>(S + (size_t)s * P * kSelMaxK * kSelMaxK);
+  const int n4 = P * kSelMaxK * kSelMaxK / 4, nc = P * kSelMaxK;
+  for (int e0 = 0; e0 < n4; e0 += 64 * 8) {  // 8 loads per lane in flight together
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + lane + 64 * u;
+      v[u] = src[e < n4 ? e : n4 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // clamped lanes rewrite the last entry with its own value
+      const int e = e0 + lane + 64 * u;
+      tab4[e < n4 ? e : n4 - 1] = v[u];
+    }
+  }
+  {
+    const int32_t* cs = cand + (size_t)s * P * kSelMaxK;
+    int32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {  // nc <= 64 * 16
+      const int e = lane + 64 * u;
+      v[u] = cs[e < nc ? e : nc - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = lane + 64 * u;
+      (&ct[0][0])[e < nc ? e : nc - 1] = v[u];
+    }
+  }
+  const double u_lane = inv_T != 0.0 && lane < P ? philox_uniform(seed, offset + lane, s, 3) : 0.0;
   __syncthreads();
+  const float* tab = reinterpret_cast<const float*>(tab4);
   int a = 0;
   for (int j = 0; j < P; ++j) {
-    const float x = lane < k ? tab[j][a][lane] : -INFINITY;
-    int pick;
+    const float x = lane < k ? tab[(j * kSelMaxK + a) * kSelMaxK + lane] : -INFINITY;
+    const uint64_t kx = lane < k ? argmax_key(x, (uint32_t)lane) : 0ull;
+    const int best = (int)argmax_key_index(wave_max_key(kx));
+    int pick = best;
     if (inv_T == 0.0) {
-      pick = (int)argmax_key_index(wave_max_u64(argmax_key(x, (uint32_t)lane)));
+      if (q_out && lane < k) q_out[((size_t)s * P + j) * k + lane] = lane == pick ? 1.f : 0.f;
     } else {
-      const float mx = __shfl(x, (int)argmax_key_index(wave_max_u64(argmax_key(x, (uint32_t)lane))), kWave);
+      const float mx = __shfl(x, best, kWave);
       const double e = lane < k ? exp(((double)x - (double)mx) * inv_T) : 0.0;
-      if (lane < kSelMaxK) ex[lane] = e;
-      __syncthreads();
-      if (lane == 0) {
-        double tot = 0.0;
-        for (int c = 0; c < k; ++c) tot += ex[c];
-        const double target = philox_uniform(seed, offset + j, s, 3) * tot;
-        double run = 0.0;
-        int c = 0;
-        for (; c < k; ++c) {
-          run += ex[c];
-          if (run > target) break;
-        }
-        ex[0] = (double)(c < k ? c : k - 1) + 0.25;  // hand the choice to the wave
-        ex[1] = tot;
-      }
-      __syncthreads();
-      pick = (int)ex[0];
-      const double tot = ex[1];
+      // running sums over the candidates (lanes 0..15, one DPP row): an
+      // inclusive scan; the draw is the first lane whose sum exceeds u * total
+      double run = e;
+      run += row_shr_d<0x111>(run);
+      run += row_shr_d<0x112>(run);
+      run += row_shr_d<0x114>(run);
+      run += row_shr_d<0x118>(run);
+      const double tot = __shfl(run, k - 1, kWave);
+      const double target = __shfl(u_lane, j, kWave) * tot;
+      const uint64_t over = __ballot(lane < k && run > target);
+      pick = over ? __ffsll((unsigned long long)over) - 1 : k - 1;
       if (q_out && lane < k) q_out[((size_t)s * P + j) * k + lane] = (float)(e / tot);
-      __syncthreads();  // ex is rewritten by the next row
     }
-    if (inv_T == 0.0 && q_out && lane < k)
-      q_out[((size_t)s * P + j) * k + lane] = lane == pick ? 1.f : 0.f;
     if (cand_out && lane < k) cand_out[((size_t)s * P + j) * k + lane] = ct[j][lane];
     if (lane == 0) block[(size_t)s * Bl + 1 + j] = ct[j][pick];
     a = pick;
@@ -273,7 +428,7 @@ sel_walk(const float* __restrict__ S, const int32_t* __restrict__ cand, int P, i
 int sel_slices(int V) { return (V + kSelSlice - 1) / kSelSlice; }
 int sel_kz(int D) { return (D + kSelKSlice - 1) / kSelKSlice; }
 int sel_max_walk_rows() { return kSelMaxWalkRows; }
-int sel_max_merge_keys() { return 256 * kSelMergePer; }
+int sel_max_slices() { return kSelMaxSlices; }
 
 hipError_t launch_select(const SelectLaunch& L, hipStream_t st) {
   const int rows = L.n_seqs * L.P;

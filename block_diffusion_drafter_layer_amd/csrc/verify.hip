@@ -171,12 +171,40 @@ struct CdfRow {
   const int32_t* cv = nullptr;
   const float* cq = nullptr;
   int k = 0;
+  // the candidates inside the calling thread's vocab chunk, in candidate
+  // order (nl < 0: more than 4, scan them all)
+  int nl = 0;
+  int lv[4] = {-1, -1, -1, -1};
+  double lq[4] = {0.0, 0.0, 0.0, 0.0};
+  __device__ void localize(int v0, int v1) {
+    if (!cv) return;
+    nl = 0;
+    for (int c = 0; c < k; ++c) {
+      const int v = cv[c];
+      if (v >= v0 && v < v1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i == nl) {
+            lv[i] = v;
+            lq[i] = (double)cq[c];
+          }
+        ++nl;
+      }
+    }
+    if (nl > 4) nl = -1;
+  }
   __device__ double w(int v) const {
     const double p = exp((double)t[v] * inv_temp - mt) / zt;
     if (cv) {
       double q = 0.0;
-      for (int c = 0; c < k; ++c)
-        if (cv[c] == v) q += (double)cq[c];
+      if (nl >= 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i < nl && lv[i] == v) q += lq[i];
+      } else {
+        for (int c = 0; c < k; ++c)
+          if (cv[c] == v) q += (double)cq[c];
+      }
       const double r = p - q;
       return r > 0.0 ? r : 0.0;
     }
@@ -258,6 +286,7 @@ cdf_slice_sums(VerifyLaunch P, const RowStat* part, Merged* merged, double* sums
   }
   int v0, v1;
   slice_chunk(P, split, v0, v1);
+  R.localize(v0, v1);
   double local = 0.0;
   for (int v = v0; v < v1; ++v) local += R.w(v);
   loc[threadIdx.x] = local;
@@ -271,8 +300,9 @@ cdf_slice_sums(VerifyLaunch P, const RowStat* part, Merged* merged, double* sums
 
 // inverse-CDF draw on candidate row c with uniform u; returns the index.
 // loc: LDS [kCdfThreads]; sh: LDS int[3]; dsh: LDS double[1].
-__device__ int cdf_draw(const VerifyLaunch& P, const CdfRow& R, const double* sums, int c, double u,
+__device__ int cdf_draw(const VerifyLaunch& P, const CdfRow& R0, const double* sums, int c, double u,
                         double* loc, int* sh, double* dsh) {
+  CdfRow R = R0;
   const int tid = threadIdx.x;
   if (tid == 0) {
     const double* sr = sums + (size_t)c * P.splits;
@@ -296,6 +326,7 @@ __device__ int cdf_draw(const VerifyLaunch& P, const CdfRow& R, const double* su
   const double target = dsh[0];
   int v0, v1;
   slice_chunk(P, ks, v0, v1);
+  R.localize(v0, v1);
   double local = 0.0;
   for (int v = v0; v < v1; ++v) local += R.w(v);
   loc[tid] = local;
@@ -345,26 +376,33 @@ pq_pick(VerifyLaunch P, const Merged* merged, const double* sums) {
   __shared__ int32_t cv[kSelMaxK];
   __shared__ float cq[kSelMaxK];
   const double inv_t = 1.0 / P.temperature;
+  // the accept tests of all rows at once, one thread each; the first
+  // rejected row ends the block (rows after it do not matter)
+  __shared__ int rej[64];
+  if (tid < gamma) {
+    const int j = tid;
+    int x = P.block_ids[(size_t)s * Bl + j + 1];
+    x = x < 0 ? 0 : (x >= P.V ? P.V - 1 : x);  // keep the read in bounds
+    const Merged a = merged[s * Bl + j];
+    const double p = exp((double)P.target[(size_t)(s * Bl + j) * P.V + x] * inv_t - a.m) / a.z;
+    double q;
+    if (P.cand) {  // q on the row's candidate set (zero elsewhere: always kept)
+      q = 0.0;
+      for (int c = 0; c < P.k; ++c)
+        if (P.cand[(size_t)(s * gamma + j) * P.k + c] == x)
+          q += (double)P.qc[(size_t)(s * gamma + j) * P.k + c];
+    } else {
+      const Merged b = merged[nt + s * gamma + j];
+      q = exp((double)P.draft[(size_t)(s * gamma + j) * P.V + x] * inv_t - b.m) / b.z;
+    }
+    const double u = philox_uniform(P.seed, P.offset + j, s, 0);
+    rej[j] = q > 0.0 && !(u < p / q);
+  }
+  __syncthreads();
   if (tid == 0) {
     int jr = gamma;
-    for (int j = 0; j < gamma; ++j) {
-      int x = P.block_ids[(size_t)s * Bl + j + 1];
-      x = x < 0 ? 0 : (x >= P.V ? P.V - 1 : x);  // keep the read in bounds
-      const Merged a = merged[s * Bl + j];
-      const double p = exp((double)P.target[(size_t)(s * Bl + j) * P.V + x] * inv_t - a.m) / a.z;
-      double q;
-      if (P.cand) {  // q on the row's candidate set (zero elsewhere: always kept)
-        q = 0.0;
-        for (int c = 0; c < P.k; ++c)
-          if (P.cand[(size_t)(s * gamma + j) * P.k + c] == x)
-            q += (double)P.qc[(size_t)(s * gamma + j) * P.k + c];
-      } else {
-        const Merged b = merged[nt + s * gamma + j];
-        q = exp((double)P.draft[(size_t)(s * gamma + j) * P.V + x] * inv_t - b.m) / b.z;
-      }
-      const double u = philox_uniform(P.seed, P.offset + j, s, 0);
-      if (q > 0.0 && !(u < p / q)) { jr = j; break; }
-    }
+    for (int j = 0; j < gamma; ++j)
+      if (rej[j]) { jr = j; break; }
     jr_sh = jr;
   }
   __syncthreads();
