@@ -20,7 +20,8 @@ SCORE_TOL = 1e-3
 CDF_TOL = 1e-6
 
 
-def _run(dc, lens, bl=None, k=16, rank=256, temperature=0.0, seed=0, offset=0, anchors=None):
+def _run(dc, lens, bl=None, k=16, rank=256, temperature=0.0, seed=0, offset=0, anchors=None,
+         oracle_seqs=None):
     bl = dc.block_size if bl is None else bl
     n = len(lens)
     say(f"select: config {dc.name} seqs={n} block_len={bl} k={k} rank={rank} T={temperature}")
@@ -50,7 +51,7 @@ def _run(dc, lens, bl=None, k=16, rank=256, temperature=0.0, seed=0, offset=0, a
     last_np = np32(last).astype(np.float64).reshape(n, bl, dc.hidden)
     logits_np = np32(lg).astype(np.float64)
     compared = 0
-    for s in range(n):
+    for s in (range(n) if oracle_seqs is None else oracle_seqs):
         z = O.rms_norm(last_np[s, 1:], wn["final_norm"], dc.rms_eps)
         an = int(min(max(int(anchors[s]), 0), dc.vocab - 1))
         ref = O.select_candidates_philox(logits_np[s], z, an, sn["hidden_proj"],
@@ -94,6 +95,15 @@ def test_tiny_vocab_short_block_and_anchor_outside_vocab():
 
 def test_qwen_shape_block16_ctx2048_full_size():
     _run(CONFIGS[1], [2048])
+
+
+def test_qwen_shape_32_sequences_sampled_and_greedy():
+    # the largest batch: 32 sequences x 15 drafted rows (480 rows of
+    # candidates); the oracle checks a sample of the sequences
+    dc = CONFIGS[3]
+    lens = [int(x) % 700 for x in synth.gen.ragged_lengths(dc.n_seqs)]
+    _run(dc, lens, temperature=0.9, seed=21, offset=5, oracle_seqs=[0, 13, 31])
+    _run(dc, lens, oracle_seqs=[1, 30])
 
 
 def _cand_case(V, bl, k, rng):
