@@ -98,6 +98,25 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// q[start] + q[start + stride] + ... over indices below n, added in that
+// order, with the loads of eight terms in flight together (a plain loop
+// would wait for each load before the next one is issued)
+__device__ __forceinline__ float strided_sum(const float* q, int n, int start, int stride) {
+  float s = 0.f;
+  for (int g0 = start; g0 < n; g0 += 8 * stride) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int g = g0 + u * stride;
+      v[u] = q[g < n ? g : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (g0 + u * stride < n) s += v[u];
+  }
+  return s;
+}
+
 // Order-preserving key for (value, index) argmax with the lowest index
 // winning ties: larger key <=> larger value, or equal value and lower index.
 __device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {

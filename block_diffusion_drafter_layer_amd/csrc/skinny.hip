@@ -447,7 +447,7 @@ __device__ __forceinline__ void row_scales(const SkinnyA& a, int m0, float* rs) 
     float s = 0.f;
     if (a.ssq && m0 + row < a.M) {
       const float* q = a.ssq + (size_t)in_row(a, m0 + row) * a.ssq_ld;
-      for (int g = lane; g < a.ssq_ld; g += 64) s += q[g];
+      s = strided_sum(q, a.ssq_ld, lane, 64);
       s = wave_sum(s);
     }
     if (lane == 0) rs[row] = a.ssq ? rsqrtf(s / (float)a.K + a.eps) : 1.f;
@@ -871,12 +871,17 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
     if (ep.seqs.len_dev && (int)threadIdx.x < a.M / ep.Bl) warm = ep.seqs.len_dev[threadIdx.x];
   // the residual epilogue reads x and the norm gain of its elements: request
   // them now as well (the epilogue's thread-to-element map, 2 per thread)
-  float warm_f = 0.f;
+  // (loaded into registers that are only named at the very end, so that no
+  // instruction waits for them before the epilogue)
+  float warm_x[2] = {0.f, 0.f};
+  uint32_t warm_g[2] = {0u, 0u};
   if constexpr (std::is_same<Epi, EpiResid>::value) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int e = threadIdx.x + 256 * k, ml = e / 32, n = blockIdx.x * 32 + e % 32;
-      if (ml < a.M && n < ep.n_vcols) warm_f += ep.x[(size_t)ml * ep.D + n] + bf2f(ep.gain[n]);
+      const int mc = ml < a.M ? ml : a.M - 1, nc = n < ep.n_vcols ? n : ep.n_vcols - 1;
+      warm_x[k] = ep.x[(size_t)mc * ep.D + nc];
+      warm_g[k] = ep.gain[nc];
     }
   }
   const int t = threadIdx.x, pair = blockIdx.x;
@@ -886,15 +891,27 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   // row scales: wave w sums rows 4w..4w+3 (16 lanes each)
   const int lane = t & 63, w = t >> 6;
   const int srow = 4 * w + (lane >> 4);
+  const float* p0 = part + ((size_t)(2 * pair) * ks) * 256 + t;
+  const float* p1 = p0 + (size_t)ks * 256;
+  // the first batch of slice partials and the row sums of x^2 are requested
+  // together (clamped addresses: no branch around any load)
+  float f0[kFinishBatch], f1[kFinishBatch];
+#pragma unroll
+  for (int k = 0; k < kFinishBatch; ++k) {
+    const int kk = k < ks ? k : ks - 1;
+    f0[k] = p0[(size_t)kk * 256];
+    f1[k] = p1[(size_t)kk * 256];
+  }
   float sq = 0.f;
   if (a.ssq && srow < a.M) {
     const float* q = a.ssq + (size_t)in_row(a, srow) * a.ssq_ld;
-    for (int g = lane & 15; g < a.ssq_ld; g += 16) sq += q[g];
+    sq = strided_sum(q, a.ssq_ld, lane & 15, 16);
   }
-  const float* p0 = part + ((size_t)(2 * pair) * ks) * 256 + t;
-  const float* p1 = p0 + (size_t)ks * 256;
   float s0 = 0.f, s1 = 0.f;
-  for (int k0 = 0; k0 < ks; k0 += kFinishBatch) {
+#pragma unroll
+  for (int k = 0; k < kFinishBatch; ++k)
+    if (k < ks) { s0 += f0[k]; s1 += f1[k]; }  // slice order
+  for (int k0 = kFinishBatch; k0 < ks; k0 += kFinishBatch) {
     float v0[kFinishBatch], v1[kFinishBatch];
 #pragma unroll
     for (int k = 0; k < kFinishBatch; ++k) {
@@ -911,7 +928,7 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
-  asm volatile("" ::"v"(warm), "v"(warm_f));
+  asm volatile("" ::"v"(warm), "v"(warm_x[0]), "v"(warm_x[1]), "v"(warm_g[0]), "v"(warm_g[1]));
 }
 
 // LM-head finisher: 256 vocabulary columns per workgroup, one per thread.
@@ -927,17 +944,30 @@ lm_stream_finish(SkinnyA a, EpiLM::P ep, int ks, const float* __restrict__ part)
   const int tile = col >> 4, n = col & 15;
   // row scales: wave w sums rows 4w..4w+3 (16 lanes each)
   const int srow = 4 * w + (lane >> 4);
-  float sq = 0.f;
-  if (a.ssq && srow < a.M) {
-    const float* q = a.ssq + (size_t)in_row(a, srow) * a.ssq_ld;
-    for (int g = lane & 15; g < a.ssq_ld; g += 16) sq += q[g];
-  }
   const int tiles = (ep.V + 15) >> 4;
   const int tl = tile < tiles ? tile : tiles - 1;
   // element (row 4g + e, column n) of a tile sits at [lane 16g + n][e]
   const float* src = part + (size_t)tl * ks * 256 + n * 4;
+  // the first four slices' partials and the row sums of x^2 are requested
+  // together (clamped addresses: no branch around any load)
+  f32x4 f[4][4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      f[k][g] = *reinterpret_cast<const f32x4*>(src + (size_t)(k < ks ? k : ks - 1) * 256 + g * 64);
+  float sq = 0.f;
+  if (a.ssq && srow < a.M) {
+    const float* q = a.ssq + (size_t)in_row(a, srow) * a.ssq_ld;
+    sq = strided_sum(q, a.ssq_ld, lane & 15, 16);
+  }
   f32x4 z[4] = {};
-  for (int k0 = 0; k0 < ks; k0 += 4) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)  // slice order
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      if (k < ks) z[g] += f[k][g];
+  for (int k0 = 4; k0 < ks; k0 += 4) {
     f32x4 v[4][4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
@@ -1085,7 +1115,7 @@ struct EpiTiled {
       if (p.ssq && m < M) {
         const int mi = (m / p.a_group) * p.a_stride + p.a_off + m % p.a_group;
         const float* q = p.ssq + (size_t)mi * p.ssq_ld;
-        for (int g = lane; g < p.ssq_ld; g += 64) s += q[g];
+        s = strided_sum(q, p.ssq_ld, lane, 64);
         s = wave_sum(s);
       }
       if (lane == 0) rs[r] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
