@@ -102,13 +102,29 @@ struct EpiQKV {
                              int vc0, int m0, int M) {
     const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
+    // each row's position and cache once, through LDS (read per element they
+    // would be loads that every iteration waits for behind the previous
+    // iteration's stores)
+    __shared__ int r_pos[ROWS], r_cap[ROWS];
+    __shared__ bf16_t* r_kv[ROWS];
+    for (int ml = threadIdx.x; ml < ROWS; ml += blockDim.x) {
+      const int m = m0 + ml;
+      if (m < M) {
+        const int s = m / p.Bl;
+        r_pos[ml] = seq_len(p.seqs, s) + m % p.Bl;
+        r_cap[ml] = p.seqs.s[s].cap;
+        r_kv[ml] = p.seqs.s[s].kv;
+      }
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
       const int m = m0 + ml;
       if (m >= M) continue;
-      const int s = m / p.Bl, r = m % p.Bl;
-      const SeqDesc sd = p.seqs.s[s];
-      const int pos = seq_len(p.seqs, s) + r;
+      SeqDesc sd;
+      sd.cap = r_cap[ml];
+      sd.kv = r_kv[ml];
+      const int pos = r_pos[ml];
       const float x1 = tile[ml][c * 16 + j] * rs[ml];
       const float x2 = tile[ml][c * 16 + j + 8] * rs[ml];
       const int vc = vc0 + c * 16;
@@ -165,17 +181,37 @@ struct EpiResid {
   __device__ static void run(const P& p, float (*tile)[LD], const float*,
                              int vc0, int m0, int M) {
     static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
-    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
-      const int ml = e / VC, c = e % VC;
-      const int m = m0 + ml;
-      const int n = vc0 + c;
-      if (m >= M || n >= p.n_vcols) continue;
-      const size_t i = (size_t)m * p.D + n;
-      const float xn = p.x[i] + tile[ml][c];
-      p.x[i] = xn;
-      if (p.hidden) p.hidden[i] = xn;
-      split_bf16(xn * bf2f(p.gain[n]), p.xh[i], p.xl[i]);
-      tile[ml][c] = xn * xn;
+    // eight elements per thread at a time: their x and gain loads go out
+    // together (clamped addresses), then the in-place updates (a
+    // load-update-store per iteration would wait for each load)
+    constexpr int U = 8;
+    for (int e0 = threadIdx.x; e0 < ROWS * VC; e0 += U * blockDim.x) {
+      float xo[U];
+      bf16_t go[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * blockDim.x;
+        const int ml = e / VC, c = e % VC;
+        int m = m0 + ml, n = vc0 + c;
+        m = m < M ? m : M - 1;
+        n = n < p.n_vcols ? n : p.n_vcols - 1;
+        xo[u] = p.x[(size_t)m * p.D + n];
+        go[u] = p.gain[n];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * blockDim.x;
+        const int ml = e / VC, c = e % VC;
+        const int m = m0 + ml;
+        const int n = vc0 + c;
+        if (e >= ROWS * VC || m >= M || n >= p.n_vcols) continue;
+        const size_t i = (size_t)m * p.D + n;
+        const float xn = xo[u] + tile[ml][c];
+        p.x[i] = xn;
+        if (p.hidden) p.hidden[i] = xn;
+        split_bf16(xn * bf2f(go[u]), p.xh[i], p.xl[i]);
+        tile[ml][c] = xn * xn;
+      }
     }
     __syncthreads();
     const int ng = p.D / 32;
@@ -397,15 +433,31 @@ struct EpiAppendRows {
                              int M) {
     const int kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
+    // each row's position (-1: not appended) and cache once, through LDS
+    __shared__ int r_pos[ROWS], r_cap[ROWS];
+    __shared__ bf16_t* r_kv[ROWS];
+    for (int ml = threadIdx.x; ml < ROWS; ml += blockDim.x) {
+      const int m = m0 + ml;
+      int pos = -1;
+      if (m < M) {
+        const int s = m / p.rps, rr = m % p.rps;
+        const int at = seq_len(p.seqs, s) + rr;
+        if (rr < p.tau[s] && at < p.seqs.s[s].max_ctx) pos = at;
+        r_cap[ml] = p.seqs.s[s].cap;
+        r_kv[ml] = p.seqs.s[s].kv;
+      }
+      r_pos[ml] = pos;
+    }
+    __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
       const int m = m0 + ml;
       if (m >= M) continue;
-      const int s = m / p.rps, rr = m % p.rps;
-      if (rr >= p.tau[s]) continue;
-      const SeqDesc sd = p.seqs.s[s];
-      const int pos = seq_len(p.seqs, s) + rr;
-      if (pos >= sd.max_ctx) continue;
+      const int pos = r_pos[ml];
+      if (pos < 0) continue;
+      SeqDesc sd;
+      sd.cap = r_cap[ml];
+      sd.kv = r_kv[ml];
       const int vc = vc0 + c * 16;
       if (vc >= p.n_vcols) continue;
       const size_t plane = (size_t)sd.cap * p.hd;
