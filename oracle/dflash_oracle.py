@@ -30,6 +30,14 @@ Readings taken where the pages are silent (also listed in the design notes):
     ascending), no bias in the hidden projection, the walk's hidden state is
     the LM head's input (final RMSNorm applied), and sampling draws from
     softmax(scores / T) over the k candidates with Philox purpose 3.
+  * grouped dynamic two-tap conv: the projection's 2*k*groups outputs are
+    laid out (call, tap, group) row-major, call 0 = "prepare", call 1 =
+    "finish"; both halves come from the hidden state the prepare call reads
+    (its own input), and the finish half is handed to the finish call; the
+    conv output replaces its input (no residual inside the module); the
+    block's first position reads a caller-given row standing for the last
+    confirmed token. Where the two calls sit in the layer is left to the
+    caller.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
@@ -584,3 +592,82 @@ def verify_pq_candidates(block_ids, target_logits, cand, q_rows, temperature: fl
     ur = [philox_uniform(seed, row_offset + j, seq, PURPOSE_RESAMPLE) for j in range(B)]
     return verify_pq_candidates_with_uniforms(block_ids, target_logits, cand, q_rows,
                                               temperature, ua, ur)
+
+
+# ----------------------------------------------------------------------------
+# DFlash 2 grouped dynamic two-tap causal conv
+# ----------------------------------------------------------------------------
+
+CONV_TAPS = 2
+
+
+def dynamic_conv_param_count(hidden: int, group_size: int, n_layers: int,
+                             instances_per_layer: int = 2) -> int:
+    """[Code] section 14 (GroupedDynamicCausalConv): each instance holds a base
+    kernel of shape (2, taps, hidden) and a bias-free projection from the
+    hidden state to 2 * taps * groups values, groups = hidden / group_size;
+    every layer has two instances (one by attention, one by the MLP)."""
+    groups = hidden // group_size
+    per = 2 * CONV_TAPS * hidden + hidden * 2 * CONV_TAPS * groups
+    return n_layers * instances_per_layer * per
+
+
+def dynamic_conv_coefficients(h_row, base_call, proj, group_size: int, call: int):
+    """Per-channel tap coefficients of one position for one call ([Code]
+    section 13: learned base kernel plus a correction computed from the
+    current hidden state, one correction per group of group_size channels).
+    h_row [D]; base_call [taps, D] = base[call]; proj [2 * taps * G, D].
+    Returns coef [taps, D]."""
+    D = len(h_row)
+    G = D // group_size
+    corr = np.asarray(proj, dtype=F64) @ np.asarray(h_row, dtype=F64)  # [2 * taps * G]
+    corr = corr.reshape(2, CONV_TAPS, G)[call]                          # [taps, G]
+    group_of = np.arange(D) // group_size
+    return np.asarray(base_call, dtype=F64) + corr[:, group_of]
+
+
+def _conv_block(x, prev, block_len: int, coef_rows):
+    """y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1} ([Code] section 13) over blocks
+    of block_len consecutive rows; the first row of block s reads prev[s]."""
+    x = np.asarray(x, dtype=F64)
+    prev = np.asarray(prev, dtype=F64)
+    y = np.empty_like(x)
+    for m in range(x.shape[0]):
+        s, t = divmod(m, block_len)
+        before = prev[s] if t == 0 else x[m - 1]
+        k = coef_rows[m]
+        y[m] = k[0] * x[m] + k[1] * before
+    return y
+
+
+def dynamic_conv_prepare(x, prev, block_len: int, base, proj, group_size: int):
+    """The "prepare" call of one conv instance over n_seqs blocks.
+
+    x [n_seqs * block_len, D]  the module's input rows, block by block
+    prev [n_seqs, D]           the row each block's first position reads
+    base [2, taps, D], proj [2 * taps * G, D]
+    Returns (y [rows, D], corr_finish [rows, taps * G]): the conv of x with
+    the call-0 coefficients, and the call-1 half of every row's correction
+    for the finish call."""
+    x = np.asarray(x, dtype=F64)
+    D = x.shape[1]
+    G = D // group_size
+    base = np.asarray(base, dtype=F64)
+    coef = [dynamic_conv_coefficients(x[m], base[0], proj, group_size, 0)
+            for m in range(x.shape[0])]
+    corr = (x @ np.asarray(proj, dtype=F64).T).reshape(-1, 2, CONV_TAPS, G)[:, 1]
+    return _conv_block(x, prev, block_len, coef), corr.reshape(-1, CONV_TAPS * G)
+
+
+def dynamic_conv_finish(z, prev, block_len: int, base, corr_finish, group_size: int):
+    """The "finish" call: the conv of z with base[1] plus the call-1
+    corrections the prepare call computed for the same rows.
+    z [rows, D], prev [n_seqs, D], corr_finish [rows, taps * G]."""
+    z = np.asarray(z, dtype=F64)
+    D = z.shape[1]
+    G = D // group_size
+    base = np.asarray(base, dtype=F64)
+    c = np.asarray(corr_finish, dtype=F64).reshape(-1, CONV_TAPS, G)
+    group_of = np.arange(D) // group_size
+    coef = [base[1] + c[m][:, group_of] for m in range(z.shape[0])]
+    return _conv_block(z, prev, block_len, coef)
