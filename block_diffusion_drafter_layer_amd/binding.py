@@ -99,6 +99,8 @@ def _load():
         "dflash_verify_candidates": (C.c_int, [P, I32, I32, P, P, P, P, I32, F32, U64, U64, P, P]),
         "dflash_set_selector": (C.c_int, [P, C.POINTER(dflash_selector)]),
         "dflash_select_block": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P, P]),
+        "dflash_conv_prepare": (C.c_int, [P, I32, I32, I32, P, P, P, P, P, P]),
+        "dflash_conv_finish": (C.c_int, [P, I32, I32, I32, P, P, P, P, P]),
         "dflash_draft_block_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, I32, P, P, P]),
         "dflash_append_dev": (C.c_int, [P, I32, C.POINTER(kvp), P, P, C.POINTER(P), I64, I32]),
         "dflash_kv_trim_dev": (C.c_int, [P, I32, P, I32]),
@@ -242,6 +244,20 @@ def dflash_verify_candidates(h, n_seqs: int, block_len: int, block_ids: int, tar
                                                 C.c_void_p(bonus_out)))
 
 
+def dflash_conv_prepare(h, n_seqs: int, block_len: int, group_size: int, base: int, proj: int,
+                        x: int, prev: int, y: int, corr_out: int):
+    return _check(_lib.dflash_conv_prepare(h, n_seqs, block_len, group_size, C.c_void_p(base),
+                                           C.c_void_p(proj), C.c_void_p(x), C.c_void_p(prev),
+                                           C.c_void_p(y), C.c_void_p(corr_out)))
+
+
+def dflash_conv_finish(h, n_seqs: int, block_len: int, group_size: int, base: int, z: int,
+                       prev: int, corr: int, y: int):
+    return _check(_lib.dflash_conv_finish(h, n_seqs, block_len, group_size, C.c_void_p(base),
+                                          C.c_void_p(z), C.c_void_p(prev), C.c_void_p(corr),
+                                          C.c_void_p(y)))
+
+
 def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
     out = (C.c_int32 * n_feat)()
     _check(_lib.dflash_target_layer_ids(n_target_layers, n_feat, out))
@@ -249,7 +265,8 @@ def dflash_target_layer_ids(n_target_layers: int, n_feat: int):
 
 
 STAGES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down_proj", "lm_head",
-          "fuse_context", "inject_kv", "verify", "lm_argmax", "sample_draft", "select")
+          "fuse_context", "inject_kv", "verify", "lm_argmax", "sample_draft", "select",
+          "conv")
 
 
 def dflash_copy_bytes(dst: int, src: int, nbytes: int, stream: int = 0):

@@ -100,6 +100,7 @@ struct Layout {
   size_t fuse_y;                // fp32 projection of the fused rows before the norm
   size_t vcdf;                  // verify / sampling draws: merged row statistics and slice sums
   size_t sel_keys, sel_gpart, sel_spart, sel_S, sel_cand;  // candidate selector
+  size_t conv_xh, conv_xl;      // the dynamic conv's hi/lo input rows
   size_t total;
 };
 
@@ -144,6 +145,8 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.sel_spart = take((size_t)sel_kz(c.hidden) * sel_rows * 4);
   L.sel_S = take(sel_rows * kSelMaxK * kSelMaxK * 4);
   L.sel_cand = take(sel_rows * kSelMaxK * 4);
+  L.conv_xh = take(Mmax * D * 2);
+  L.conv_xl = take(Mmax * D * 2);
   L.total = o;
   return L;
 }
@@ -151,10 +154,10 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
 }  // namespace
 
 enum Stage { ST_EMBED, ST_QKV, ST_ATTN, ST_OPROJ, ST_GATEUP, ST_DOWN, ST_LM, ST_FUSE, ST_INJECT,
-             ST_VERIFY, ST_LM_ARGMAX, ST_SAMPLE, ST_SELECT, ST_COUNT };
+             ST_VERIFY, ST_LM_ARGMAX, ST_SAMPLE, ST_SELECT, ST_CONV, ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"embed", "qkv", "attention", "o_proj", "gate_up",
                                      "down_proj", "lm_head", "fuse_context", "inject_kv", "verify",
-                                     "lm_argmax", "sample_draft", "select"};
+                                     "lm_argmax", "sample_draft", "select", "conv"};
 
 struct Profiler {
   uint32_t mask = 0;
@@ -841,6 +844,75 @@ dflash_status dflash_select_block(dflash_handle* h, int32_t n_seqs, int32_t bloc
   L.cand = (int32_t*)(h->ws + h->lay.sel_cand);
   hipError_t e = timed(h, ST_SELECT, [&] { return launch_select(L, h->stream); });
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "select_block");
+}
+
+}  // extern "C"
+
+namespace {
+dflash_status conv_check(dflash_handle* h, int32_t n_seqs, int32_t block_len, int32_t group_size,
+                         const void* base, const float* x, const float* prev, const float* corr,
+                         const float* y) {
+  if (!h || !base || !x || !prev || !corr || !y)
+    return fail(DFLASH_E_NULL, "handle, base, inputs, prev, corrections and y are required");
+  if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > h->max_seqs)
+    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
+  if (group_size < 1 || c.hidden % (16 * group_size))
+    return fail(DFLASH_E_SHAPE, "group_size=%d: hidden=%d must be a multiple of 16 * group_size",
+                group_size, c.hidden);
+  if (!aligned(base, 16) || !aligned(x, 16) || !aligned(prev, 4) || !aligned(corr, 4) ||
+      !aligned(y, 4))
+    return fail(DFLASH_E_ALIGN, "base and the input rows must be 16-byte aligned, the rest 4-byte");
+  const size_t rows = (size_t)n_seqs * block_len, D = c.hidden, G = D / group_size;
+  auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return pa < pb + nb && pb < pa + na;
+  };
+  const size_t ny = rows * D * 4;
+  if (overlap(y, ny, x, ny) || overlap(y, ny, prev, (size_t)n_seqs * D * 4) ||
+      overlap(y, ny, corr, rows * 2 * G * 4))
+    return fail(DFLASH_E_SHAPE, "y must not overlap the inputs or the corrections");
+  return DFLASH_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dflash_status dflash_conv_prepare(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  int32_t group_size, const void* base, const void* proj,
+                                  const float* x, const float* prev, float* y, float* corr_out) {
+  if (!proj) return fail(DFLASH_E_NULL, "proj is required");
+  dflash_status st = conv_check(h, n_seqs, block_len, group_size, base, x, prev, corr_out, y);
+  if (st != DFLASH_OK) return st;
+  if (!aligned(proj, 16)) return fail(DFLASH_E_ALIGN, "proj must be 16-byte aligned");
+  const size_t rows = (size_t)n_seqs * block_len, D = h->cfg.hidden;
+  if ((uintptr_t)corr_out < (uintptr_t)x + rows * D * 4 &&
+      (uintptr_t)x < (uintptr_t)corr_out + rows * 2 * (D / group_size) * 4)
+    return fail(DFLASH_E_SHAPE, "corr_out must not overlap x");
+  ConvLaunch C{};
+  C.n_seqs = n_seqs; C.Bl = block_len; C.D = (int)D; C.gs = group_size;
+  C.base = (const bf16_t*)base; C.proj = (const bf16_t*)proj;
+  C.x = x; C.prev = prev; C.y = y; C.corr = corr_out;
+  C.xh = (bf16_t*)(h->ws + h->lay.conv_xh);
+  C.xl = (bf16_t*)(h->ws + h->lay.conv_xl);
+  C.split = split_ws(h);
+  hipError_t e = timed(h, ST_CONV, [&] { return launch_conv_prepare(C, h->stream); });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "conv_prepare");
+}
+
+dflash_status dflash_conv_finish(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                 int32_t group_size, const void* base, const float* z,
+                                 const float* prev, const float* corr, float* y) {
+  dflash_status st = conv_check(h, n_seqs, block_len, group_size, base, z, prev, corr, y);
+  if (st != DFLASH_OK) return st;
+  ConvLaunch C{};
+  C.n_seqs = n_seqs; C.Bl = block_len; C.D = h->cfg.hidden; C.gs = group_size;
+  C.base = (const bf16_t*)base; C.x = z; C.prev = prev; C.y = y; C.corr = (float*)corr;
+  hipError_t e = timed(h, ST_CONV, [&] { return launch_conv_finish(C, h->stream); });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "conv_finish");
 }
 
 }  // extern "C"

@@ -204,6 +204,21 @@ int sel_max_walk_rows();
 int sel_max_slices();
 hipError_t launch_select(const SelectLaunch& L, hipStream_t st);
 
+// DFlash 2 grouped dynamic two-tap conv over n_seqs blocks of Bl rows.
+struct ConvLaunch {
+  int n_seqs, Bl, D, gs;
+  const bf16_t* base;   // [2][2][D]
+  const bf16_t* proj;   // [4 * D / gs][D] (prepare only)
+  const float* x;       // [n_seqs * Bl][D] input (z for the finish call)
+  const float* prev;    // [n_seqs][D]
+  float* y;             // [n_seqs * Bl][D]
+  float* corr;          // [n_seqs * Bl][2 * D / gs]: written by prepare, read by finish
+  bf16_t *xh, *xl;      // workspace [n_seqs * Bl][D] (prepare only)
+  SplitWs split;
+};
+hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st);
+hipError_t launch_conv_finish(const ConvLaunch& C, hipStream_t st);
+
 // reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)
 hipError_t launch_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t st);
 

@@ -484,6 +484,89 @@ struct EpiAppendRows {
 // the streaming GEMM
 // ---------------------------------------------------------------------------
 
+// DFlash 2 grouped dynamic two-tap conv ([Code] sections 13-14): the
+// projection of the hidden state to 2 x 2 x G corrections (call, tap, group;
+// call 0 "prepare", call 1 "finish") runs as a streaming GEMM over the rows.
+// Its virtual columns put both taps of 16 groups of one call in each
+// 32-column pair: column 32p + j is tap j / 16 of group 16p + j % 16. A
+// call-0 pair's epilogue applies the prepare conv to its 16 * gs channels,
+//   y_t = (b0 + c_{t,0}) * x_t + (b1 + c_{t,1}) * x_{t-1},
+// where a block's first row reads prev; a call-1 pair stores its
+// corrections for the finish call.
+struct EpiConv {
+  struct P {
+    const bf16_t* proj;  // [4G][D]
+    const bf16_t* base;  // [2][2][D] (call, tap, channel)
+    const float* x;      // [M][D] the conv input (also the GEMM's A, as hi/lo)
+    const float* prev;   // [n_seqs][D]
+    float* y;            // [M][D]
+    float* corr;         // [M][2G] finish corrections (tap, group)
+    int D, G, gs, Bl;
+    int n_vcols;         // 4G
+  };
+  __device__ static int prow(const P& p, int v) {
+    const int call = v / (2 * p.G), w = v - call * 2 * p.G;
+    return (call * 2 + ((w & 31) >> 4)) * p.G + (w >> 5) * 16 + (w & 15);
+  }
+  __device__ static const bf16_t* wrow(const P& p, int vc) {
+    return p.proj + (size_t)prow(p, vc) * p.D;
+  }
+  // an 8-aligned group of virtual columns maps to 8 consecutive projection rows
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return p.proj + (size_t)(prow(p, vc8) + r8) * p.D;
+  }
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
+                             int M) {
+    static_assert(VC % 32 == 0, "whole column pairs per workgroup");
+    for (int pl = 0; pl < VC / 32; ++pl) {
+      const int v0 = vc0 + pl * 32;
+      if (v0 >= p.n_vcols) break;
+      const int call = v0 / (2 * p.G);
+      const int g0 = ((v0 - call * 2 * p.G) >> 5) * 16;
+      if (call == 1) {
+        for (int e = threadIdx.x; e < ROWS * 32; e += blockDim.x) {
+          const int ml = e >> 5, j = e & 31, m = m0 + ml;
+          if (m < M)
+            p.corr[(size_t)m * 2 * p.G + (j >> 4) * p.G + g0 + (j & 15)] = tile[ml][pl * 32 + j];
+        }
+        continue;
+      }
+      // eight elements per thread at a time: their loads (clamped
+      // addresses) go out together before any use
+      constexpr int U = 8;
+      const int nch = 16 * p.gs, c0 = g0 * p.gs;
+      for (int e0 = threadIdx.x; e0 < ROWS * nch; e0 += U * blockDim.x) {
+        float xv[U], xb[U];
+        bf16_t b0[U], b1[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * blockDim.x;
+          int ml = e / nch;
+          const int c = c0 + (e - ml * nch);
+          int m = m0 + ml;
+          m = m < M ? m : M - 1;
+          const int t = m % p.Bl;
+          xv[u] = p.x[(size_t)m * p.D + c];
+          xb[u] = t == 0 ? p.prev[(size_t)(m / p.Bl) * p.D + c] : p.x[(size_t)(m - 1) * p.D + c];
+          b0[u] = p.base[c];
+          b1[u] = p.base[p.D + c];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = e0 + u * blockDim.x;
+          const int ml = e / nch, cl = e - ml * nch, m = m0 + ml;
+          if (e >= ROWS * nch || m >= M) continue;
+          const int gl = cl / p.gs;
+          const float k0 = bf2f(b0[u]) + tile[ml][pl * 32 + gl];
+          const float k1 = bf2f(b1[u]) + tile[ml][pl * 32 + 16 + gl];
+          p.y[(size_t)m * p.D + c0 + cl] = k0 * xv[u] + k1 * xb[u];
+        }
+      }
+    }
+  }
+};
+
 struct SplitK {
   int ksplit;        // workgroups sharing one column block's K range
   int steps;         // 32-wide k steps per split
@@ -1234,6 +1317,55 @@ size_t stream_part_floats(int n_vcols, int K) {
   int ks;
   if (!stream_plan(16, n_vcols, K, ks)) return 0;
   return (size_t)((n_vcols + 31) / 32) * 2 * ks * 256;
+}
+
+// fp32 rows -> bf16 hi/lo (the streaming GEMM's A operand); 4 elements per thread
+__global__ void __launch_bounds__(256)
+conv_split(const float* __restrict__ x, int D, bf16_t* __restrict__ xh, bf16_t* __restrict__ xl) {
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= D) return;
+  const size_t i = (size_t)blockIdx.y * D + c;
+  const float4 v = *reinterpret_cast<const float4*>(x + i);
+  const float a[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) split_bf16(a[k], xh[i + k], xl[i + k]);
+}
+
+// The finish call of the dynamic conv: base[1] plus the corrections the
+// prepare call stored, applied to z; one element per thread, every load
+// issued before any use.
+__global__ void __launch_bounds__(256)
+conv_finish(const float* __restrict__ z, const float* __restrict__ prev,
+            const bf16_t* __restrict__ base, const float* __restrict__ corr, int D, int G, int gs,
+            int Bl, float* __restrict__ y) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int m = blockIdx.y;
+  if (c >= D) return;
+  const int t = m % Bl, g = c / gs;
+  const float zv = z[(size_t)m * D + c];
+  const float zb = t == 0 ? prev[(size_t)(m / Bl) * D + c] : z[(size_t)(m - 1) * D + c];
+  const float k0 = bf2f(base[2 * D + c]) + corr[(size_t)m * 2 * G + g];
+  const float k1 = bf2f(base[3 * D + c]) + corr[(size_t)m * 2 * G + G + g];
+  y[(size_t)m * D + c] = k0 * zv + k1 * zb;
+}
+
+hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st) {
+  const int M = C.n_seqs * C.Bl;
+  hipLaunchKernelGGL(conv_split, dim3((C.D / 4 + 255) / 256, M), dim3(256), 0, st, C.x, C.D,
+                     C.xh, C.xl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  SkinnyA a = make_a(C.xh, C.xl, C.D, M, C.D, nullptr, 0, 0.f);
+  EpiConv::P p;
+  p.proj = C.proj; p.base = C.base; p.x = C.x; p.prev = C.prev; p.y = C.y; p.corr = C.corr;
+  p.D = C.D; p.G = C.D / C.gs; p.gs = C.gs; p.Bl = C.Bl; p.n_vcols = 4 * p.G;
+  return launch_skinny<EpiConv>(a, p, p.n_vcols, C.split, st);
+}
+
+hipError_t launch_conv_finish(const ConvLaunch& C, hipStream_t st) {
+  hipLaunchKernelGGL(conv_finish, dim3((C.D + 255) / 256, C.n_seqs * C.Bl), dim3(256), 0, st,
+                     C.x, C.prev, C.base, C.corr, C.D, C.D / C.gs, C.gs, C.Bl, C.y);
+  return hipGetLastError();
 }
 
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {

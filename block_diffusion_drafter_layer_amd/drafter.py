@@ -146,6 +146,27 @@ class Drafter:
                               q.data_ptr() if q is not None else 0)
         return block_ids
 
+    def conv_prepare(self, x: torch.Tensor, prev: torch.Tensor, base: torch.Tensor,
+                     proj: torch.Tensor, block_len: int, group_size: int = 16):
+        """DFlash 2 dynamic conv, prepare call: returns (y, the finish call's
+        corrections). x fp32 [n_seqs * block_len, hidden], prev [n_seqs, hidden],
+        base bf16 [2, 2, hidden], proj bf16 [4 * hidden / group_size, hidden]."""
+        n = prev.shape[0]
+        y = torch.empty_like(x)
+        corr = torch.empty(x.shape[0], 2 * (x.shape[1] // group_size), dtype=torch.float32,
+                           device=x.device)
+        B.dflash_conv_prepare(self.h, n, block_len, group_size, base.data_ptr(), proj.data_ptr(),
+                              x.data_ptr(), prev.data_ptr(), y.data_ptr(), corr.data_ptr())
+        return y, corr
+
+    def conv_finish(self, z: torch.Tensor, prev: torch.Tensor, base: torch.Tensor,
+                    corr: torch.Tensor, block_len: int, group_size: int = 16):
+        """DFlash 2 dynamic conv, finish call with the prepare call's corrections."""
+        y = torch.empty_like(z)
+        B.dflash_conv_finish(self.h, prev.shape[0], block_len, group_size, base.data_ptr(),
+                             z.data_ptr(), prev.data_ptr(), corr.data_ptr(), y.data_ptr())
+        return y
+
     def verify_candidates(self, block_ids: torch.Tensor, target_logits: torch.Tensor,
                           cand: torch.Tensor, q_rows: torch.Tensor, temperature: float,
                           seed: int = 0, philox_offset: int = 0):

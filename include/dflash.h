@@ -372,6 +372,50 @@ dflash_status dflash_verify_candidates(dflash_handle* h, int32_t n_seqs, int32_t
                                        int32_t* tau_out, int32_t* bonus_out);
 
 /*
+ * DFlash 2 grouped dynamic two-tap causal conv ([Code] section 13: each
+ * channel's output is k_{t,0} * x_t + k_{t,1} * x_{t-1}, every coefficient
+ * a learned base value plus a correction computed from the current hidden
+ * state, one correction shared by each group of channels, and a block's
+ * first position reading the last confirmed token's representation;
+ * [Code] section 14: GroupedDynamicCausalConv with a base kernel of shape
+ * (2, taps, hidden) whose first index separates the "prepare" and "finish"
+ * calls, and a bias-free projection to 2 * taps * groups values).
+ * Readings: two taps; the projection's outputs are ordered (call, tap,
+ * group) row-major; both calls' corrections come from the prepare call's
+ * input; the output replaces the input (no residual inside the module).
+ * Where the calls sit in a decoder layer is the caller's choice.
+ *
+ * Rows: n_seqs blocks of block_len consecutive rows (row s*block_len + t).
+ * G = hidden / group_size.
+ * base: device bf16 [2, 2, hidden] (call, tap, channel)
+ * proj: device bf16 [4 * G, hidden], row (call * 2 + tap) * G + g
+ *
+ * dflash_conv_prepare:
+ *   y[m][c] = (base[0][0][c] + P0[m][g]) * x[m][c]
+ *           + (base[0][1][c] + P1[m][g]) * (t > 0 ? x[m-1][c] : prev[s][c])
+ *   with P = proj . x[m] (fp32 accumulation of the bf16 weights against the
+ *   fp32 row split into bf16 high and low halves), g = c / group_size;
+ *   corr_out[m] = the call-1 corrections (tap, group): [2 * G] per row.
+ * dflash_conv_finish:
+ *   y[m][c] = (base[1][0][c] + corr[m][g]) * z[m][c]
+ *           + (base[1][1][c] + corr[m][G + g]) * (t > 0 ? z[m-1][c] : prev[s][c])
+ * x, z, y:     device fp32 [n_seqs * block_len, hidden], 16-byte aligned;
+ * prev:        device fp32 [n_seqs, hidden];
+ * corr_out / corr: device fp32 [n_seqs * block_len, 2 * G].
+ * 1 <= n_seqs <= max_seqs; 1 <= block_len <= block_size; group_size >= 1,
+ * hidden % (16 * group_size) == 0. y must not overlap the inputs. Errors are
+ * found on the host before any launch; nothing is written on error. The
+ * prepare call uses the handle's workspace (calls on one handle are ordered
+ * on its stream).
+ */
+dflash_status dflash_conv_prepare(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                  int32_t group_size, const void* base, const void* proj,
+                                  const float* x, const float* prev, float* y, float* corr_out);
+dflash_status dflash_conv_finish(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                 int32_t group_size, const void* base, const float* z,
+                                 const float* prev, const float* corr, float* y);
+
+/*
  * Host helper ([Code] section 5, build_target_layer_ids): n_feat target layer
  * indices spread evenly over 1 .. n_target_layers-3 (0-based), rounded to
  * nearest; the middle layer when n_feat == 1. out: host int32 [n_feat].

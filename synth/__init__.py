@@ -20,6 +20,8 @@ Recipe (one per workload, all seeded):
   [512, 4096];
 * candidate-selector tables (DFlash 2): hidden projection N(0, 1/D),
   predecessor and successor codes N(0, 0.3^2), rank 256.
+* dynamic two-tap conv (DFlash 2): base kernel N(0, 0.5^2), projection
+  N(0, 1/D), 16 channels per group, input rows N(0, 1) in fp32.
 
 Floating-point draws are made in fp32 and rounded once to bf16 (round to
 nearest even, torch's conversion) where the tensor is stored in bf16; the
@@ -29,6 +31,7 @@ from .configs import CONFIGS, DraftConfig, target_layer_ids_rule  # noqa: F401
 from .gen import (  # noqa: F401
     make_weights,
     make_selector,
+    make_conv,
     make_feats,
     make_anchor,
     make_target_logits,

@@ -23,6 +23,7 @@ _TAU_BASE = 700
 _RAGGED = 800
 _CTXKV_BASE = 850           # + layer
 _SEL_BASE = 900             # + 0 hidden projection, 1 predecessor, 2 successor codes
+_CONV_BASE = 950            # + 0 base kernel, 1 projection, 2..5 rows
 
 LAYER_SLOTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
                "attn_norm", "mlp_norm")
@@ -98,6 +99,25 @@ def make_selector(cfg: DraftConfig, rank: int = 256, device="cpu", code_std: flo
         "hidden_proj": _normal((rank, cfg.hidden), cfg.hidden ** -0.5, s(0), device),
         "pred_codebook": _normal((cfg.vocab, rank), code_std, s(1), device),
         "succ_codebook": _normal((cfg.vocab, rank), code_std, s(2), device),
+    }
+
+
+def make_conv(cfg: DraftConfig, n_seqs: int, block_len: int, group_size: int = 16,
+              device="cpu") -> Dict:
+    """One DFlash 2 dynamic-conv instance and its rows: base [2, 2, D] bf16 with
+    entries N(0, 0.5^2), projection [4 * D / group_size, D] bf16 with entries
+    N(0, 1/D) (corrections of order 1), and fp32 rows N(0, 1): x and z
+    [n_seqs * block_len, D], prev and zprev [n_seqs, D]."""
+    s = lambda t: seed_for(cfg.index, _CONV_BASE + t)  # noqa: E731
+    D, rows = cfg.hidden, n_seqs * block_len
+    f32 = torch.float32
+    return {
+        "base": _normal((2, 2, D), 0.5, s(0), device),
+        "proj": _normal((4 * (D // group_size), D), D ** -0.5, s(1), device),
+        "x": _normal((rows, D), 1.0, s(2), device, f32),
+        "prev": _normal((n_seqs, D), 1.0, s(3), device, f32),
+        "z": _normal((rows, D), 1.0, s(4), device, f32),
+        "zprev": _normal((n_seqs, D), 1.0, s(5), device, f32),
     }
 
 

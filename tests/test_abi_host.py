@@ -188,6 +188,22 @@ def test_argument_errors_leave_cache_lengths_unchanged():
     assert _status(B.dflash_verify_candidates, h, 1, 16, FAKE, FAKE, FAKE + 2, FAKE, 16, 1.0, 0, 0, FAKE, FAKE) == 5
     assert _status(B.dflash_set_selector, h, None) == 0
     assert _status(B.dflash_select_block, h, 1, 16, FAKE, FAKE, FAKE, 0.0, 0, 0, FAKE) == 7
+    # dynamic conv: pointers, shapes, group size, alignment, overlap
+    n_y = 16 * c.hidden * 4
+    Y, CR = FAKE + (1 << 24), FAKE + (1 << 23)
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, FAKE, 0, FAKE, FAKE, Y, CR) == 1
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, 0, FAKE, FAKE, FAKE, Y, CR) == 1
+    assert _status(B.dflash_conv_prepare, h, 3, 16, 16, FAKE, FAKE, FAKE, FAKE, Y, CR) == 3
+    assert _status(B.dflash_conv_prepare, h, 1, 17, 16, FAKE, FAKE, FAKE, FAKE, Y, CR) == 3
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 0, FAKE, FAKE, FAKE, FAKE, Y, CR) == 3
+    assert _status(B.dflash_conv_prepare, h, 1, 16, c.hidden, FAKE, FAKE, FAKE, FAKE, Y, CR) == 3
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, FAKE, FAKE + 8, FAKE, FAKE, Y, CR) == 5
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, FAKE, FAKE, FAKE + 4, FAKE, Y, CR) == 5
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, FAKE, FAKE, FAKE, FAKE, FAKE + n_y // 2, CR) == 3
+    assert _status(B.dflash_conv_finish, h, 1, 16, 16, FAKE, FAKE, FAKE, 0, Y) == 1
+    assert _status(B.dflash_conv_finish, h, 1, 16, 16, FAKE, FAKE, FAKE, CR, FAKE) == 3
+    assert _status(B.dflash_conv_finish, h, 1, 0, 16, FAKE, FAKE, FAKE, CR, Y) == 3
+    assert _status(B.dflash_conv_prepare, h, 1, 16, 16, FAKE, FAKE, FAKE, FAKE, Y, FAKE) == 3  # corr over x
     # device-resident rounds: pointers, shapes, alignment
     assert _status(B.dflash_draft_block_dev, h, [kv], 0, FAKE, 16, FAKE) == 1
     assert _status(B.dflash_draft_block_dev, h, [kv], FAKE + 2, FAKE, 16, FAKE) == 5

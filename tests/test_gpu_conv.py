@@ -1,0 +1,76 @@
+"""GPU parity of the DFlash 2 grouped dynamic two-tap conv against the oracle
+([Code] sections 13-14), on the same seeded bf16 tables and fp32 rows.
+
+Tolerance: the GPU forms each correction as an fp32 sum of bf16 weights
+times the row split into bf16 high and low halves (relative representation
+error 2^-17 per element), so a correction c = sum_i w_i x_i is off by about
+2^-17 * sqrt(sum_i (w_i x_i)^2) plus fp32 rounding of the sum: ~1e-5 for
+the N(0, 1/D) projection. An output element k0 x_t + k1 x_{t-1} then
+differs by at most ~1e-5 (|x_t| + |x_{t-1}|); the test allows
+2e-4 (|x_t| + |x_{t-1}|) + 1e-5 elementwise."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_helpers import DEV, make, np32, say
+from synth import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(got, ref, a, a_prev, bl):
+    rows = a.shape[0]
+    before = np.empty_like(a)
+    for m in range(rows):
+        s, t = divmod(m, bl)
+        before[m] = a_prev[s] if t == 0 else a[m - 1]
+    tol = 2e-4 * (np.abs(a) + np.abs(before)) + 1e-5
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), f"max excess {np.max(err - tol):.3e}"
+
+
+def _run(dc, n_seqs, bl, gs=16, max_seqs=None):
+    say(f"conv: config {dc.name} seqs={n_seqs} block_len={bl} group={gs}")
+    d, _ = make(dc, max_seqs=max_seqs or n_seqs)
+    cv = synth.make_conv(dc, n_seqs, bl, gs, device=DEV)
+    y, corr = d.conv_prepare(cv["x"], cv["prev"], cv["base"], cv["proj"], bl, gs)
+    y2 = d.conv_finish(cv["z"], cv["zprev"], cv["base"], corr, bl, gs)
+    torch.cuda.synchronize()
+    n = {k: np32(v).astype(np.float64) for k, v in cv.items()}
+    ry, rc = O.dynamic_conv_prepare(n["x"], n["prev"], bl, n["base"], n["proj"], gs)
+    _check(np32(y), ry, n["x"], n["prev"], bl)
+    G = dc.hidden // gs
+    np.testing.assert_allclose(np32(corr), rc, rtol=0, atol=2e-5 * np.sqrt(dc.hidden / 64))
+    # the finish call on the GPU's own corrections (the oracle reads the same fp32 values)
+    ry2 = O.dynamic_conv_finish(n["z"], n["zprev"], bl, n["base"], np32(corr), gs)
+    _check(np32(y2), ry2, n["z"], n["zprev"], bl)
+    assert corr.shape == (n_seqs * bl, 2 * G)
+
+
+def test_tiny_config():
+    # hidden 64: groups of 4 channels (hidden must hold 16 whole groups)
+    _run(CONFIGS[0], 1, 4, gs=4)
+
+
+def test_tiny_block_one_and_single_channel_groups():
+    _run(CONFIGS[0], 2, 1, gs=4)
+    _run(CONFIGS[0], 1, 3, gs=1)
+
+
+def test_qwen_shape_one_block():
+    # hidden 4096, 256 groups: the LDS-staged streaming GEMM (16 rows)
+    _run(CONFIGS[1], 1, 16)
+
+
+def test_qwen_shape_ragged_rows_and_many_sequences():
+    # 2 x 7 rows (the streaming GEMM's ragged tile), 3 x 7 rows and 32 x 16
+    # rows (the register-streaming kernel, one 32-row block / 64-row blocks)
+    _run(CONFIGS[1], 2, 7, max_seqs=32)
+    _run(CONFIGS[1], 3, 7, max_seqs=32)
+    _run(CONFIGS[3], 32, 16)
+
+
+def test_d2048_group_32():
+    _run(CONFIGS[4], 2, 8, gs=32)
