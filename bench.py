@@ -605,6 +605,35 @@ def main():
                 "select_hbm_frac": round(sel_bytes / (sel_g[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "select_over_draft": round(sel_g[0] / draft_e, 4)}
 
+    # DFlash 2 dynamic two-tap conv on the headline block's rows (16 channels
+    # per group): the prepare call (projection + conv) and the finish call;
+    # a layer holds two instances, each with both calls
+    cv = synth.make_conv(dc, 1, Bsz, 16, device=dev)
+    c_y, c_corr = d.conv_prepare(cv["x"], cv["prev"], cv["base"], cv["proj"], Bsz)
+    c_y2 = d.conv_finish(cv["z"], cv["zprev"], cv["base"], c_corr, Bsz)
+    cp_args = (d.h, 1, Bsz, 16, cv["base"].data_ptr(), cv["proj"].data_ptr(), cv["x"].data_ptr(),
+               cv["prev"].data_ptr(), c_y.data_ptr(), c_corr.data_ptr())
+    cf_args = (d.h, 1, Bsz, 16, cv["base"].data_ptr(), cv["z"].data_ptr(), cv["zprev"].data_ptr(),
+               c_corr.data_ptr(), c_y2.data_ptr())
+    # 20 calls back to back per timed interval: the device time of a call,
+    # not the host's call overhead
+    def _rep(fn, n=20):
+        def run():
+            for _ in range(n):
+                fn()
+        return run
+    cp_t = [t / 20 for t in _ev_time(_rep(lambda: B.dflash_conv_prepare(*cp_args)), args.steps, torch)]
+    cf_t = [t / 20 for t in _ev_time(_rep(lambda: B.dflash_conv_finish(*cf_args)), args.steps, torch)]
+    n_grp = dc.hidden // 16
+    # algorithmic bytes: the projection and base read once, the rows read and
+    # written once, the corrections written (prepare) or read (finish)
+    rows_b = Bsz * dc.hidden * 4
+    conv_p_bytes = 4 * n_grp * dc.hidden * 2 + 4 * dc.hidden * 2 + 2 * rows_b + dc.hidden * 4 + Bsz * 2 * n_grp * 4
+    conv = {"prepare_us": round(cp_t[0], 1), "finish_us": round(cf_t[0], 1), "group_size": 16,
+            "prepare_hbm_frac": round(conv_p_bytes / (cp_t[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_draft_over_draft": round(2 * dc.n_layers * (cp_t[0] + cf_t[0]) / draft_e, 4)}
+    del cv, c_y, c_y2, c_corr
+
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps / elapsed
     dbytes = draft_block_bytes(dc, S0)
@@ -648,6 +677,7 @@ def main():
         "prefill_inject_us": round(inject_us, 1),
         "prefill_inject_mfma_frac": round(inject_flops / (inject_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "selector": selector,
+        "dynamic_conv": conv,
     }
     if stages_all:
         result["stage_us_per_step"] = stages_all
