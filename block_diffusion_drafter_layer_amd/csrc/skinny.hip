@@ -503,6 +503,7 @@ struct EpiConv {
     float* corr;         // [M][2G] finish corrections (tap, group)
     int D, G, gs, Bl;
     int n_vcols;         // 4G
+    int parts;           // workgroups sharing a pair's channels (grid.y of the finisher), else 1
   };
   __device__ static int prow(const P& p, int v) {
     const int call = v / (2 * p.G), w = v - call * 2 * p.G;
@@ -524,7 +525,9 @@ struct EpiConv {
       if (v0 >= p.n_vcols) break;
       const int call = v0 / (2 * p.G);
       const int g0 = ((v0 - call * 2 * p.G) >> 5) * 16;
+      const int part = p.parts > 1 ? (int)blockIdx.y : 0;
       if (call == 1) {
+        if (part) continue;
         for (int e = threadIdx.x; e < ROWS * 32; e += blockDim.x) {
           const int ml = e >> 5, j = e & 31, m = m0 + ml;
           if (m < M)
@@ -535,7 +538,8 @@ struct EpiConv {
       // eight elements per thread at a time: their loads (clamped
       // addresses) go out together before any use
       constexpr int U = 8;
-      const int nch = 16 * p.gs, c0 = g0 * p.gs;
+      // this workgroup's share of the pair's 16 * gs channels
+      const int nch = 16 * p.gs / p.parts, c0 = g0 * p.gs + part * nch;
       for (int e0 = threadIdx.x; e0 < ROWS * nch; e0 += U * blockDim.x) {
         float xv[U], xb[U];
         bf16_t b0[U], b1[U];
@@ -557,7 +561,7 @@ struct EpiConv {
           const int e = e0 + u * blockDim.x;
           const int ml = e / nch, cl = e - ml * nch, m = m0 + ml;
           if (e >= ROWS * nch || m >= M) continue;
-          const int gl = cl / p.gs;
+          const int gl = (c0 - g0 * p.gs + cl) / p.gs;
           const float k0 = bf2f(b0[u]) + tile[ml][pl * 32 + gl];
           const float k1 = bf2f(b1[u]) + tile[ml][pl * 32 + 16 + gl];
           p.y[(size_t)m * p.D + c0 + cl] = k0 * xv[u] + k1 * xb[u];
@@ -1358,8 +1362,20 @@ hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st) {
   SkinnyA a = make_a(C.xh, C.xl, C.D, M, C.D, nullptr, 0, 0.f);
   EpiConv::P p;
   p.proj = C.proj; p.base = C.base; p.x = C.x; p.prev = C.prev; p.y = C.y; p.corr = C.corr;
-  p.D = C.D; p.G = C.D / C.gs; p.gs = C.gs; p.Bl = C.Bl; p.n_vcols = 4 * p.G;
-  return launch_skinny<EpiConv>(a, p, p.n_vcols, C.split, st);
+  p.D = C.D; p.G = C.D / C.gs; p.gs = C.gs; p.Bl = C.Bl; p.n_vcols = 4 * p.G; p.parts = 1;
+  int ks;
+  if (!uses_stream(a, p.n_vcols, C.split, ks)) return launch_skinny<EpiConv>(a, p, p.n_vcols, C.split, st);
+  // the LDS-staged GEMM, then a finisher whose pairs each spread their conv
+  // over 8 workgroups (a pair re-reads its 32 KB of partials per workgroup):
+  // the finisher grid grows from n_vcols / 32 to 8x that
+  p.parts = 8;
+  hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, true, EpiConv>), dim3(stream_grid(ks)),
+                     dim3(kSW * 64), 0, st, a, p, p.n_vcols, ks, C.D / ks, C.split.part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_finish<EpiConv>), dim3(p.n_vcols / 32, p.parts), dim3(256), 0, st, a, p,
+                     ks, C.split.part);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_finish(const ConvLaunch& C, hipStream_t st) {
