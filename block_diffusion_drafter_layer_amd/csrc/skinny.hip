@@ -856,14 +856,21 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
     const bool mv = m < a.M;
     const size_t row = (size_t)in_row(a, mv ? m : 0) * a.lda;
     // unconditional loads from clamped addresses, zeroed at the store, so
-    // that all of them are in flight together
+    // that all of them are in flight together; the dynamic conv reads its
+    // fp32 rows and splits them into bf16 high and low halves here
+    constexpr bool kF32A = std::is_same<Epi, EpiConv>::value;
+    float4 fv[kF32A ? PER : 1][2];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int fr = w + u * kSW, hl = fr & 1;
       const int st = min(fr >> 1, nsteps - 1);
       const int kst = k0 + st * 32;
       const int k = kst + 8 * (lane >> 4);
-      if (LO && hl) {
+      if constexpr (kF32A) {
+        const float4* src = reinterpret_cast<const float4*>(ep.x + row + k);
+        fv[u][0] = src[0];
+        fv[u][1] = src[1];
+      } else if (LO && hl) {
         v[u] = *reinterpret_cast<const u32x4*>(a.xl + row + k);
       } else {
         const int sg = kst / a.seg_k;
@@ -875,6 +882,13 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
     for (int u = 0; u < PER; ++u) {
       const int fr = w + u * kSW, hl = fr & 1;
       const bool keep = mv && (hl == 0 || LO);
+      if constexpr (kF32A) {
+        const float f[8] = {fv[u][0].x, fv[u][0].y, fv[u][0].z, fv[u][0].w,
+                            fv[u][1].x, fv[u][1].y, fv[u][1].z, fv[u][1].w};
+        bf16x8 h, l;
+        pack_split_bf16x8(f, h, l);
+        v[u] = __builtin_bit_cast(u32x4, hl ? l : h);
+      }
       As[fr >> 1][hl][lane] = keep ? v[u] : u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -1355,16 +1369,21 @@ conv_finish(const float* __restrict__ z, const float* __restrict__ prev,
 
 hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st) {
   const int M = C.n_seqs * C.Bl;
-  hipLaunchKernelGGL(conv_split, dim3((C.D / 4 + 255) / 256, M), dim3(256), 0, st, C.x, C.D,
-                     C.xh, C.xl);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   SkinnyA a = make_a(C.xh, C.xl, C.D, M, C.D, nullptr, 0, 0.f);
   EpiConv::P p;
   p.proj = C.proj; p.base = C.base; p.x = C.x; p.prev = C.prev; p.y = C.y; p.corr = C.corr;
   p.D = C.D; p.G = C.D / C.gs; p.gs = C.gs; p.Bl = C.Bl; p.n_vcols = 4 * p.G; p.parts = 1;
   int ks;
-  if (!uses_stream(a, p.n_vcols, C.split, ks)) return launch_skinny<EpiConv>(a, p, p.n_vcols, C.split, st);
+  hipError_t e;
+  if (!uses_stream(a, p.n_vcols, C.split, ks)) {
+    // the register-streaming kernel reads bf16 hi/lo rows from the workspace
+    hipLaunchKernelGGL(conv_split, dim3((C.D / 4 + 255) / 256, M), dim3(256), 0, st, C.x, C.D,
+                       C.xh, C.xl);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_skinny<EpiConv>(a, p, p.n_vcols, C.split, st);
+  }
+  // the LDS-staged kernel splits the fp32 rows itself as it stages them
   // the LDS-staged GEMM, then a finisher whose pairs each spread their conv
   // over 8 workgroups (a pair re-reads its 32 KB of partials per workgroup):
   // the finisher grid grows from n_vcols / 32 to 8x that
