@@ -72,5 +72,11 @@ def test_qwen_shape_ragged_rows_and_many_sequences():
     _run(CONFIGS[3], 32, 16)
 
 
+def test_qwen_shape_single_row_blocks():
+    # one row per block: every row reads its sequence's prev row
+    _run(CONFIGS[1], 1, 1, max_seqs=16)
+    _run(CONFIGS[1], 16, 1)
+
+
 def test_d2048_group_32():
     _run(CONFIGS[4], 2, 8, gs=32)
