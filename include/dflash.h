@@ -399,9 +399,11 @@ dflash_status dflash_verify_candidates(dflash_handle* h, int32_t n_seqs, int32_t
  * dflash_conv_finish:
  *   y[m][c] = (base[1][0][c] + corr[m][g]) * z[m][c]
  *           + (base[1][1][c] + corr[m][G + g]) * (t > 0 ? z[m-1][c] : prev[s][c])
- * x, z, y:     device fp32 [n_seqs * block_len, hidden], 16-byte aligned;
+ * x, z, y:     device fp32 [n_seqs * block_len, hidden] (x and z 16-byte
+ *              aligned, y 4-byte);
  * prev:        device fp32 [n_seqs, hidden];
- * corr_out / corr: device fp32 [n_seqs * block_len, 2 * G].
+ * corr_out / corr: device fp32 [n_seqs * block_len, 2 * G]; corr_out must
+ *              not overlap x. base and proj 16-byte aligned.
  * 1 <= n_seqs <= max_seqs; 1 <= block_len <= block_size; group_size >= 1,
  * hidden % (16 * group_size) == 0. y must not overlap the inputs. Errors are
  * found on the host before any launch; nothing is written on error. The
