@@ -22,10 +22,13 @@ Readings taken where the pages are silent (also listed in the design notes):
   * GQA: query head a reads kv head a // (Hq/Hkv);
   * argmax ties go to the lowest index (numpy.argmax / torch.argmax rule);
   * Philox4x64-10 counter layout and the inverse-CDF sampler of verify_pq;
-  * a cache built with bf16_kv=True stores its K/V rows, and the block's own
-    K/V rows, rounded to bf16: [Code] section 5 sizes the model's weights and
-    activations at two bytes each (BF16). With bf16_kv=False (the default)
-    every row is kept in fp64.
+  * a cache built with bf16_kv=True stores its context K/V rows rounded to
+    bf16 ([Code] section 5 sizes the model's weights and activations at two
+    bytes each, BF16); with bf16_kv=False (the default, the plain definition)
+    every row is kept in fp64. The block's own K/V rows are never stored in
+    the cache ([Code] section 5 concatenates them with the context's inside
+    the attention call; only the context rows persist across rounds), so they
+    are never rounded.
   * candidate selector: the top-k order (value descending, then index
     ascending), no bias in the hidden projection, the walk's hidden state is
     the LM head's input (final RMSNorm applied), and sampling draws from
@@ -263,8 +266,8 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
     target's, shared and frozen).
 
     caches[s] holds sequence s's context K/V; its length S_s is the anchor's
-    position. The block's own K/V rows take the precision the cache stores
-    rows in (DraftCache.store). Returns a dict with
+    position. The block's own K/V rows exist only inside this forward and
+    keep full precision. Returns a dict with
       draft  [n_seq, block_len-1] int   argmax tokens of rows 1..block_len-1
       hidden [L, n_seq, block_len, D]   residual stream after each layer
       logits [n_seq, block_len-1, V]
@@ -291,8 +294,7 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
             kb = linear(h, lw["wk"]).reshape(B, Hkv, hd)
             vb = linear(h, lw["wv"]).reshape(B, Hkv, hd)
             q = apply_rope(q, pos, theta)
-            kb = caches[s].store(apply_rope(kb, pos, theta))
-            vb = caches[s].store(vb)
+            kb = apply_rope(kb, pos, theta)
             if S > 0:
                 k_all = np.concatenate([caches[s].k[i], kb])
                 v_all = np.concatenate([caches[s].v[i], vb])

@@ -46,7 +46,7 @@ def _torch_forward(cfg, w, ctx_k, ctx_v, anchor, S, bf16_block=False):
         q = _torch_rope((h @ t(lw["wq"]).T).view(B, Hq, hd), pos, cfg.rope_theta)
         kb = _torch_rope((h @ t(lw["wk"]).T).view(B, Hkv, hd), pos, cfg.rope_theta)
         vb = (h @ t(lw["wv"]).T).view(B, Hkv, hd)
-        if bf16_block:  # the block's rows as a bf16 cache holds them
+        if bf16_block:  # the block's rows rounded to bf16 (a deliberately different model)
             kb = kb.to(torch.float32).to(torch.bfloat16).to(torch.float64)
             vb = vb.to(torch.float32).to(torch.bfloat16).to(torch.float64)
         k = torch.cat([t(ctx_k[i]), kb]) if S else kb
@@ -98,19 +98,23 @@ def test_forward_reduced_qwen_shape():
     np.testing.assert_array_equal(out["draft"][0], draft)
 
 
-def test_bf16_cache_rounds_the_block_rows():
-    # with a bf16 cache the block's own K/V rows enter attention as bf16
-    # values; the composition rounds them with torch's conversion
+def test_bf16_cache_leaves_the_block_rows_unrounded():
+    # a bf16 cache rounds the context rows it stores, never the block's own
+    # K/V rows (they exist only inside the forward): with context rows that
+    # are bf16 values already, the bf16 cache gives exactly the plain result,
+    # and the composition with the block rows rounded to bf16 differs from it
     cfg = CONFIGS[0].shrink(n_layers=2)
     w, ck, cv, _ = _setup(cfg, 10)
     anchor = int(synth.make_anchor(cfg)[0])
     cache = O.DraftCache(cfg.n_layers, k=ck, v=cv, bf16_kv=True)
     out = O.draft_block(cfg, w, [cache], [anchor])
-    hs, logits, _ = _torch_forward(cfg, w, ck, cv, anchor, 10, bf16_block=True)
+    hs, logits, _ = _torch_forward(cfg, w, ck, cv, anchor, 10)
     np.testing.assert_allclose(out["hidden"][:, 0], hs, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(out["logits"][0], logits, rtol=1e-10, atol=1e-10)
     plain = O.draft_block(cfg, w, [O.DraftCache(cfg.n_layers, k=ck, v=cv)], [anchor])
-    assert np.abs(plain["hidden"] - out["hidden"]).max() > 1e-6
+    np.testing.assert_array_equal(plain["hidden"], out["hidden"])
+    hs_rounded, _, _ = _torch_forward(cfg, w, ck, cv, anchor, 10, bf16_block=True)
+    assert np.abs(hs_rounded - out["hidden"][:, 0]).max() > 1e-6
 
 
 def test_argmax_ties_take_lowest_index():
