@@ -94,9 +94,9 @@ size_t split_floats(const dflash_config& c) {
 }
 
 struct Layout {
-  size_t split_part, x, xh, xl, ssq, q, q_lo, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
+  size_t split_part, x, xh, xl, ssq, q, q_lo, blk_k, blk_v, ob_h, ob_l, act_h, act_l, lm_part, att_acc, att_ml, vpart, fuse_ssq;
   size_t gemm_part, gemm_ctr;   // context-GEMM split-K partials and counters (0 bytes if unused)
-  size_t app_ctx;               // fused rows of a device-resident append
+  size_t app_ctx, app_ctx_lo;   // fused rows of a device-resident append (bf16 hi, lo)
   size_t fuse_y;                // fp32 projection of the fused rows before the norm
   size_t vcdf;                  // verify / sampling draws: merged row statistics and slice sums
   size_t sel_keys, sel_gpart, sel_spart, sel_S, sel_cand;  // candidate selector
@@ -119,6 +119,8 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.ssq = take(Mmax * (D / 32) * 4);
   L.q = take(Mmax * qd * 2);
   L.q_lo = take(Mmax * qd * 2);
+  L.blk_k = take(Mmax * c.n_kv_heads * c.head_dim * 4);
+  L.blk_v = take(Mmax * c.n_kv_heads * c.head_dim * 4);
   L.ob_h = take(Mmax * qd * 2);
   L.ob_l = take(Mmax * qd * 2);
   L.act_h = take(Mmax * F * 2);
@@ -137,6 +139,7 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.gemm_part = take(tiled ? ctx_gemm_part_floats() * 4 : 0);
   L.gemm_ctr = take(tiled ? (size_t)kGemmMaxCounters * 4 : 0);
   L.app_ctx = take(std::min((size_t)max_tokens, Mmax) * D * 2);
+  L.app_ctx_lo = take(std::min((size_t)max_tokens, Mmax) * D * 2);
   L.fuse_y = take((size_t)max_tokens * D * 4);
   L.vcdf = take(2 * Mmax * 16 + Mmax * kVerifyMaxSplits * 8);
   const size_t sel_rows = (size_t)max_seqs * (c.block_size > 1 ? c.block_size - 1 : 1);
@@ -508,7 +511,8 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
     seqs.s[s].cap = row_capacity(c, kvs[s]->max_ctx);
     seqs.s[s].len = kvs[s]->len;
     seqs.s[s].max_ctx = kvs[s]->max_ctx;
-    max_keys = std::max(max_keys, (len_dev ? kvs[s]->max_ctx : kvs[s]->len) + block_len);
+    // context keys: the block's own keys are added by the merge kernel
+    max_keys = std::max(max_keys, len_dev ? kvs[s]->max_ctx : kvs[s]->len);
   }
   seqs.len_dev = len_dev;
   const Layout& Ly = h->lay;
@@ -523,6 +527,7 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   L.anchors = anchor_ids; L.block_out = block_out; L.seqs = &seqs;
   L.x = (float*)(ws + Ly.x); L.xh = (bf16_t*)(ws + Ly.xh); L.xl = (bf16_t*)(ws + Ly.xl);
   L.ssq = (float*)(ws + Ly.ssq); L.q = (bf16_t*)(ws + Ly.q); L.q_lo = (bf16_t*)(ws + Ly.q_lo);
+  L.blk_k = (float*)(ws + Ly.blk_k); L.blk_v = (float*)(ws + Ly.blk_v);
   L.ob_h = (bf16_t*)(ws + Ly.ob_h); L.ob_l = (bf16_t*)(ws + Ly.ob_l);
   L.act_h = (bf16_t*)(ws + Ly.act_h); L.act_l = (bf16_t*)(ws + Ly.act_l);
   L.lm_part = (uint64_t*)(ws + Ly.lm_part);
@@ -537,8 +542,7 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   const int WG_waves = G <= 2 ? 2 * G : G;
   const int max_splits =
       std::max(1, std::min(kAttnMaxSplits, attn_slots(h->max_seqs, c.n_kv_heads) / pairs));
-  // (the last split also takes the remainder, so the block's own keys do not
-  // add a nearly empty split); long key ranges are split further when the
+  // (the last split also takes the remainder); long key ranges are split further when the
   // grid is full already (many sequences), since a wave's chunks are serial
   int splits = std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves));
   splits = std::max(splits, (max_keys + kAttnMaxKeysPerSplit - 1) / kAttnMaxKeysPerSplit);
@@ -640,13 +644,17 @@ dflash_status dflash_append_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* con
     seqs.s[s].max_ctx = kvs[s]->max_ctx;
   }
   seqs.len_dev = len_dev;
+  // the fused rows stay a bf16 hi/lo pair (~16 significant bits) until the
+  // injection: they never leave the call, and the injection's weight stream
+  // is HBM-bound either way
   bf16_t* ctx = (bf16_t*)(h->ws + h->lay.app_ctx);
+  bf16_t* ctx_lo = (bf16_t*)(h->ws + h->lay.app_ctx_lo);
   F.n_feat = c.n_feat_layers; F.ld = ld; F.T = T; F.D = c.hidden;
   F.w_c = (const bf16_t*)h->w.w_c; F.gain = (const bf16_t*)h->w.ctx_norm; F.eps = c.rms_eps;
-  F.out = ctx; F.ssq = (float*)(h->ws + h->lay.fuse_ssq); F.y = (float*)(h->ws + h->lay.fuse_y);
+  F.out = ctx; F.out_lo = ctx_lo; F.ssq = (float*)(h->ws + h->lay.fuse_ssq); F.y = (float*)(h->ws + h->lay.fuse_y);
   F.split = split_ws(h); F.gemm = gemm_ws(h);
   AppendLaunch A{};
-  A.ctx = ctx; A.T = T; A.rps = rows_per_seq; A.D = c.hidden; A.L = c.n_layers;
+  A.ctx = ctx; A.ctx_lo = ctx_lo; A.T = T; A.rps = rows_per_seq; A.D = c.hidden; A.L = c.n_layers;
   A.Hkv = c.n_kv_heads; A.hd = c.head_dim; A.log2_theta = std::log2((double)c.rope_theta);
   for (int i = 0; i < c.n_layers; ++i) {
     A.wk[i] = (const bf16_t*)h->layers[i].wk;

@@ -4,6 +4,10 @@
 // full-attention draft layers are not causal). Grouped-query heads: query
 // head a reads kv head a / G.
 //
+// The context keys come from the bf16 KV cache; the block's own keys never
+// enter the cache: the QKV epilogue leaves them in fp32 in the workspace and
+// the merge kernel adds them, in fp32, to the split partials of the context.
+//
 // One workgroup per (key range, kv head, sequence) with one wave per query
 // head of the group; each wave holds the 16 block rows of its head as the
 // MFMA columns. Scores are formed transposed, S^T = K Q^T, so that a lane's
@@ -15,7 +19,8 @@
 // Each workgroup keeps a running max / sum / accumulator over its keys and
 // writes them as a partial; a second kernel merges the partials of a head.
 // Q and P enter the MFMAs as bf16 hi/lo pairs (two MFMAs each), so the only
-// bf16 rounding left in attention is the KV cache's own storage format.
+// bf16 rounding left in attention is the KV cache's own storage format of the
+// context rows.
 #include "common.h"
 #include "launch.h"
 
@@ -181,7 +186,7 @@ attn_split(AttnArgs p) {
   Chunk<HD> ca, cb;
   if (PIPE) load_chunk<HD>(ca, c0, kbase, vbase, sd.cap, ql, lg);
   // the context length (host value or device memory) is needed only now
-  const int n_keys = seq_len(p.seqs, s) + p.Bl;
+  const int n_keys = seq_len(p.seqs, s);  // context keys only
   const int ke = split == p.splits - 1 ? n_keys : min(kb + p.kps, n_keys);  // last: the rest
 
   f32x4 acc[HT];
@@ -374,7 +379,7 @@ attn_lds(AttnArgs p) {
     qf[ks] = qv ? ld_bf16x8(p.q + qoff + ks * 32) : zero_bf16x8();
     qfl[ks] = qv ? ld_bf16x8(p.q_lo + qoff + ks * 32) : zero_bf16x8();
   }
-  const int n_keys = seq_len(p.seqs, s) + p.Bl;
+  const int n_keys = seq_len(p.seqs, s);  // context keys only
   constexpr int R = kRingSlots;
 #pragma unroll
   for (int j = 0; j < R - 1; ++j) issue(j, j);
@@ -424,60 +429,120 @@ attn_lds(AttnArgs p) {
 }
 
 // One workgroup per (block row, query head, sequence), one thread per output
-// dim (at least one wave). The first kMergeBatch accumulator values are
-// requested first, from clamped indices so that the loads are straight-line
-// code; meanwhile wave 0 holds split k's (m, l) in lane k (and k + 64), forms
-// the running max and the normaliser with wave reductions and leaves each
-// split's weight 2^(m_k - M) / L in LDS.
+// dim (at least one wave). Each thread first requests its dim of the first
+// kMergeBatch split accumulators and of the block's Bl fp32 values (clamped
+// indices, straight-line loads). Wave 0 then forms the block scores: lane
+// 4j + t holds a quarter of the dims of block key j and of the query (hi +
+// lo), so one dot product of HD/4 terms and two lane exchanges give q.k_j.
+// The same wave holds split k's (m, l) in lane k (and k + 64), takes the
+// running max over the splits and the block scores, and the normaliser
+//   L = sum_k 2^(m_k - M) l_k + sum_j 2^(s_j - M),
+// with one wave reduction each, and leaves each split's weight
+// 2^(m_k - M) / L and the block keys' weights 2^(s_j - M) / L in LDS.
+// Scores are in log2 units (scaled by log2(e)/sqrt(hd)), as in the split
+// kernels.
 constexpr int kMergeBatch = 32;
 static_assert(kAttnMaxSplits <= 128, "two splits per lane of wave 0");
+struct MergeArgs {
+  const float* acc;
+  const float* ml;
+  const bf16_t *q, *q_lo;     // [M][Hq][hd]
+  const float *blk_k, *blk_v; // [M][Hkv][hd]
+  int Hq, Hkv, Bl, splits;
+  float scale_log2;
+  bf16_t *ob_h, *ob_l;
+};
 template <int HD>
 __global__ void __launch_bounds__(HD < 64 ? 64 : HD)
-attn_merge(const float* __restrict__ acc, const float* __restrict__ ml, int Hq, int Bl,
-           int splits, bf16_t* __restrict__ ob_h, bf16_t* __restrict__ ob_l) {
+attn_merge(MergeArgs p) {
   constexpr int STRIDE = 16 * HD;  // floats between the splits of one (row, dim)
+  constexpr int DPL = HD / 4;      // dims per lane of a block score
+  static_assert(DPL % 4 == 0, "whole float4 pieces of a key per lane");
   const int r = blockIdx.x, a = blockIdx.y, s = blockIdx.z;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63, w = d >> 6;
+  const int g = a / (p.Hq / p.Hkv);
+  const int dc = d < HD ? d : HD - 1;
   __shared__ float wts[kAttnMaxSplits];
-  const size_t slot0 = (size_t)(s * Hq + a) * splits;
-  const float* pb = acc + (slot0 * 16 + r) * HD + (d < HD ? d : HD - 1);
-  const int last = splits - 1;
+  __shared__ float bw[16];
+  const size_t slot0 = (size_t)(s * p.Hq + a) * p.splits;
+  const float* pb = p.acc + (slot0 * 16 + r) * HD + dc;
+  const int last = p.splits - 1;
   float v[kMergeBatch];
 #pragma unroll
   for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k, last) * STRIDE];
-  if (threadIdx.x < 64) {
+  const size_t kvd = (size_t)p.Hkv * HD;
+  float vb[16];
+  {
+    const float* vr = p.blk_v + (size_t)s * p.Bl * kvd + (size_t)g * HD + dc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) vb[j] = vr[(size_t)(j < p.Bl ? j : p.Bl - 1) * kvd];
+  }
+  if (w == 0) {
+    const int j = lane >> 2, part = lane & 3;
+    const int jj = j < p.Bl ? j : p.Bl - 1;
+    const float4* kr = reinterpret_cast<const float4*>(
+        p.blk_k + (size_t)(s * p.Bl + jj) * kvd + (size_t)g * HD + part * DPL);
+    const size_t qi = ((size_t)(s * p.Bl + r) * p.Hq + a) * HD + part * DPL;
+    float4 kv4[DPL / 4];
+#pragma unroll
+    for (int i = 0; i < DPL / 4; ++i) kv4[i] = kr[i];
+    uint2 qh2[DPL / 4], ql2[DPL / 4];  // four bf16 per piece
+#pragma unroll
+    for (int i = 0; i < DPL / 4; ++i) {
+      qh2[i] = *reinterpret_cast<const uint2*>(p.q + qi + 4 * i);
+      ql2[i] = *reinterpret_cast<const uint2*>(p.q_lo + qi + 4 * i);
+    }
     float mk[2], lk[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int k = threadIdx.x + 64 * j;
-      const bool in = k < splits;
-      mk[j] = in ? ml[((slot0 + k) * 16 + r) * 2] : -INFINITY;
-      lk[j] = in ? ml[((slot0 + k) * 16 + r) * 2 + 1] : 0.f;
+    for (int jx = 0; jx < 2; ++jx) {
+      const int k = lane + 64 * jx;
+      const bool in = k < p.splits;
+      mk[jx] = in ? p.ml[((slot0 + k) * 16 + r) * 2] : -INFINITY;
+      lk[jx] = in ? p.ml[((slot0 + k) * 16 + r) * 2 + 1] : 0.f;
     }
-    const float M = wave_max(fmaxf(mk[0], mk[1]));
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < DPL / 4; ++i) {
+      const uint32_t hw[2] = {qh2[i].x, qh2[i].y}, lw[2] = {ql2[i].x, ql2[i].y};
+      const float kk[4] = {kv4[i].x, kv4[i].y, kv4[i].z, kv4[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hb = e & 1 ? hw[e >> 1] & 0xffff0000u : hw[e >> 1] << 16;
+        const uint32_t lb = e & 1 ? lw[e >> 1] & 0xffff0000u : lw[e >> 1] << 16;
+        dot += (__uint_as_float(hb) + __uint_as_float(lb)) * kk[e];
+      }
+    }
+    dot += __shfl_xor(dot, 1, kWave);
+    dot += __shfl_xor(dot, 2, kWave);
+    const float sj = j < p.Bl ? dot * p.scale_log2 : -INFINITY;
+    const float M = wave_max(fmaxf(fmaxf(mk[0], mk[1]), sj));  // finite: Bl >= 1
     float e[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) e[j] = mk[j] == -INFINITY ? 0.f : exp2f(mk[j] - M);
-    const float inv = 1.f / wave_sum(e[0] * lk[0] + e[1] * lk[1]);
+    for (int jx = 0; jx < 2; ++jx) e[jx] = mk[jx] == -INFINITY ? 0.f : exp2f(mk[jx] - M);
+    const float pj = (part == 0 && j < p.Bl) ? exp2f(sj - M) : 0.f;
+    const float inv = 1.f / wave_sum(e[0] * lk[0] + e[1] * lk[1] + pj);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int k = threadIdx.x + 64 * j;
-      if (k < splits) wts[k] = e[j] * inv;
+    for (int jx = 0; jx < 2; ++jx) {
+      const int k = lane + 64 * jx;
+      if (k < p.splits) wts[k] = e[jx] * inv;
     }
+    if (part == 0) bw[j] = pj * inv;
   }
   __syncthreads();
   float o = 0.f;
-  for (int k0 = 0; k0 < splits; k0 += kMergeBatch) {
+  for (int k0 = 0; k0 < p.splits; k0 += kMergeBatch) {
     if (k0) {
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) v[k] = pb[(size_t)min(k0 + k, last) * STRIDE];
     }
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) o += (k0 + k < splits ? wts[k0 + k] : 0.f) * v[k];
+    for (int k = 0; k < kMergeBatch; ++k) o += (k0 + k < p.splits ? wts[k0 + k] : 0.f) * v[k];
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o += bw[j] * vb[j];  // zero weight past Bl
   if (d < HD) {
-    const size_t i = ((size_t)(s * Bl + r) * Hq + a) * HD + d;
-    split_bf16(o, ob_h[i], ob_l[i]);
+    const size_t i = ((size_t)(s * p.Bl + r) * p.Hq + a) * HD + d;
+    split_bf16(o, p.ob_h[i], p.ob_l[i]);
   }
 }
 
@@ -516,8 +581,11 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge<HD>, dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st,
-                     L.att_acc, L.att_ml, L.Hq, L.Bl, L.att_splits, L.ob_h, L.ob_l);
+  MergeArgs m;
+  m.acc = L.att_acc; m.ml = L.att_ml; m.q = L.q; m.q_lo = L.q_lo; m.blk_k = L.blk_k; m.blk_v = L.blk_v;
+  m.Hq = L.Hq; m.Hkv = L.Hkv; m.Bl = L.Bl; m.splits = L.att_splits; m.scale_log2 = p.scale_log2;
+  m.ob_h = L.ob_h; m.ob_l = L.ob_l;
+  hipLaunchKernelGGL(attn_merge<HD>, dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
   return hipGetLastError();
 }
 

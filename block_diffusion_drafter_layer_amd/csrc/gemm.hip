@@ -152,10 +152,12 @@ struct EpiInject {
 size_t ctx_gemm_part_floats() { return (size_t)256 * BM * 320; }
 
 // H_t row m = bf16(y[m] * rsqrt(mean(y[m]^2) + eps) * gain): the fp32
-// projection is rounded to bf16 once, here.
+// projection is rounded to bf16 once, here. With out_lo the row is kept as a
+// bf16 hi/lo pair instead (out = hi).
 __global__ void __launch_bounds__(256)
-fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ y, const float* __restrict__ ssq,
-               int n_tiles, int D, const bf16_t* __restrict__ gain, float eps) {
+fuse_normalize(bf16_t* __restrict__ out, bf16_t* __restrict__ out_lo, const float* __restrict__ y,
+               const float* __restrict__ ssq, int n_tiles, int D, const bf16_t* __restrict__ gain,
+               float eps) {
   const int m = blockIdx.x;
   __shared__ float rs;
   if (threadIdx.x < 64) {
@@ -174,8 +176,14 @@ fuse_normalize(bf16_t* __restrict__ out, const float* __restrict__ y, const floa
     const uint2 g = *reinterpret_cast<const uint2*>(gain + n);
     const float g0 = bf2f((bf16_t)(g.x & 0xffff)), g1 = bf2f((bf16_t)(g.x >> 16));
     const float g2 = bf2f((bf16_t)(g.y & 0xffff)), g3 = bf2f((bf16_t)(g.y >> 16));
-    *reinterpret_cast<uint2*>(orow + n) =
-        make_uint2(f2bf2(v.x * r * g0, v.y * r * g1), f2bf2(v.z * r * g2, v.w * r * g3));
+    const float h0 = v.x * r * g0, h1 = v.y * r * g1, h2 = v.z * r * g2, h3 = v.w * r * g3;
+    const uint2 hi = make_uint2(f2bf2(h0, h1), f2bf2(h2, h3));
+    *reinterpret_cast<uint2*>(orow + n) = hi;
+    if (out_lo) {
+      const float l0 = h0 - __uint_as_float(hi.x << 16), l1 = h1 - __uint_as_float(hi.x & 0xffff0000u);
+      const float l2 = h2 - __uint_as_float(hi.y << 16), l3 = h3 - __uint_as_float(hi.y & 0xffff0000u);
+      *reinterpret_cast<uint2*>(out_lo + (size_t)m * D + n) = make_uint2(f2bf2(l0, l1), f2bf2(l2, l3));
+    }
   }
 }
 
@@ -189,12 +197,14 @@ hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st) {
   p.n_tiles = (F.D + kFuseTileN - 1) / kFuseTileN;
   hipError_t e = launch_tiled<kFuseTileN, EpiFuse>(a, p, F.D, F.gemm, st);
   if (e != hipSuccess) return e;
-  return launch_fuse_normalize(F.out, F.y, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
+  return launch_fuse_normalize(F.out, F.out_lo, F.y, F.ssq, p.n_tiles, F.T, F.D, F.gain, F.eps, st);
 }
 
-hipError_t launch_fuse_normalize(bf16_t* out, const float* y, const float* ssq, int n_parts, int T,
-                                 int D, const bf16_t* gain, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(fuse_normalize, dim3(T), dim3(256), 0, st, out, y, ssq, n_parts, D, gain, eps);
+hipError_t launch_fuse_normalize(bf16_t* out, bf16_t* out_lo, const float* y, const float* ssq,
+                                 int n_parts, int T, int D, const bf16_t* gain, float eps,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(fuse_normalize, dim3(T), dim3(256), 0, st, out, out_lo, y, ssq, n_parts, D,
+                     gain, eps);
   return hipGetLastError();
 }
 

@@ -60,6 +60,7 @@ struct DraftLaunch {
   bf16_t *xh, *xl;          // [M][D]
   float* ssq;               // [M][D/32]
   bf16_t *q, *q_lo;         // [M][Hq*hd] query after RoPE, hi/lo
+  float *blk_k, *blk_v;     // [M][Hkv*hd] the block's own K (after RoPE) and V, fp32
   bf16_t *ob_h, *ob_l;      // [M][Hq*hd]
   bf16_t *act_h, *act_l;    // [M][F]
   uint64_t* lm_part;        // [ceil(V/32)][M] argmax keys per column block and row
@@ -100,6 +101,7 @@ struct FuseLaunch {
   const bf16_t* gain;
   float eps;
   bf16_t* out;        // [T][D] H_t, the one rounding to bf16
+  bf16_t* out_lo;     // optional [T][D]: H_t - out rounded to bf16 (out then is the hi half)
   float* y;           // [T][D] fp32 projection before the norm (workspace)
   float* ssq;         // [T][ceil(D/256)] (tiled) or [T][D/32] (few rows)
   SplitWs split;
@@ -107,8 +109,9 @@ struct FuseLaunch {
 };
 hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
-hipError_t launch_fuse_normalize(bf16_t* out, const float* y, const float* ssq, int n_parts, int T,
-                                 int D, const bf16_t* gain, float eps, hipStream_t st);
+hipError_t launch_fuse_normalize(bf16_t* out, bf16_t* out_lo, const float* y, const float* ssq,
+                                 int n_parts, int T, int D, const bf16_t* gain, float eps,
+                                 hipStream_t st);
 
 // KV injection of T context rows at positions pos0.. into every layer.
 struct InjectLaunch {
@@ -128,7 +131,8 @@ constexpr int kContextRowsStreaming = 64;  // row counts up to this use the stre
 // Device-resident rounds: fused accepted rows of several sequences injected
 // at their device lengths, then the lengths advanced by tau.
 struct AppendLaunch {
-  const bf16_t* ctx;   // [T][D] fused rows, sequence s at rows s*rps ..
+  const bf16_t* ctx;   // [T][D] fused rows, sequence s at rows s*rps .. (bf16 hi)
+  const bf16_t* ctx_lo;  // [T][D] their lo halves
   int T, rps, D, L, Hkv, hd;
   double log2_theta;
   const bf16_t* wk[kMaxLayers];

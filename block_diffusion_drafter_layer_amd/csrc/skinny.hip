@@ -9,9 +9,9 @@
 // last-arriving-workgroup reduction inside one launch needs a device-scope
 // fence per workgroup, which on this chip writes back and invalidates an XCD's
 // L2 - far more costly than the extra launch.) Each use has its own epilogue:
-//   qkv    - RMSNorm row scale, RoPE on q/k, q to the workspace, k/v into the
-//            sequence's KV cache (txtmix article section 5: q from the draft
-//            tokens, k/v of the block appended after the context);
+//   qkv    - RMSNorm row scale, RoPE on q/k, q (bf16 hi/lo) and the block's
+//            own k/v (fp32) to the workspace (txtmix article section 5: q
+//            from the draft tokens, the block's k/v follow the context's);
 //   resid  - o_proj / down_proj: x += y, the next RMSNorm's input (x*gain as a
 //            bf16 hi/lo pair) and per-32-column sums of x^2;
 //   swiglu - gate/up pairs: silu(g)*u (spec decoder layer);
@@ -68,6 +68,8 @@ struct EpiQKV {
     double log2_theta;
     bf16_t* q_out;     // [M][Hq*hd] hi
     bf16_t* q_lo;      // [M][Hq*hd] lo
+    float* blk_k;      // [M][Hkv*hd] the block's own K after RoPE, fp32
+    float* blk_v;      // [M][Hkv*hd] the block's own V, fp32
     SeqTable seqs;
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
@@ -102,34 +104,24 @@ struct EpiQKV {
                              int vc0, int m0, int M) {
     const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
-    // each row's position and cache once, through LDS (read per element they
-    // would be loads that every iteration waits for behind the previous
-    // iteration's stores)
-    __shared__ int r_pos[ROWS], r_cap[ROWS];
-    __shared__ bf16_t* r_kv[ROWS];
+    // each row's position once, through LDS (read per element it would be a
+    // load that every iteration waits for behind the previous iteration's
+    // stores)
+    __shared__ int r_pos[ROWS];
     for (int ml = threadIdx.x; ml < ROWS; ml += blockDim.x) {
       const int m = m0 + ml;
-      if (m < M) {
-        const int s = m / p.Bl;
-        r_pos[ml] = seq_len(p.seqs, s) + m % p.Bl;
-        r_cap[ml] = p.seqs.s[s].cap;
-        r_kv[ml] = p.seqs.s[s].kv;
-      }
+      if (m < M) r_pos[ml] = seq_len(p.seqs, m / p.Bl) + m % p.Bl;
     }
     __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
       const int m = m0 + ml;
       if (m >= M) continue;
-      SeqDesc sd;
-      sd.cap = r_cap[ml];
-      sd.kv = r_kv[ml];
       const int pos = r_pos[ml];
       const float x1 = tile[ml][c * 16 + j] * rs[ml];
       const float x2 = tile[ml][c * 16 + j + 8] * rs[ml];
       const int vc = vc0 + c * 16;
       if (vc >= qd + 2 * kvd) continue;
-      const size_t plane = (size_t)sd.cap * p.hd;
       if (vc < qd + kvd) {
         const bool is_q = vc < qd;
         const int vcl = is_q ? vc : vc - qd;
@@ -144,17 +136,15 @@ struct EpiQKV {
           split_bf16(o1, p.q_out[qi], p.q_lo[qi]);
           split_bf16(o2, p.q_out[qi + p.hd / 2], p.q_lo[qi + p.hd / 2]);
         } else {
-          bf16_t* k = sd.kv + (size_t)((2 * p.layer) * p.Hkv + h) * plane +
-                      (size_t)pos * p.hd;
-          k[d] = f2bf(o1);
-          k[d + p.hd / 2] = f2bf(o2);
+          float* k = p.blk_k + (size_t)m * kvd + h * p.hd;
+          k[d] = o1;
+          k[d + p.hd / 2] = o2;
         }
       } else {
-        const int vi = vc - qd - kvd;
-        const int h = vi / p.hd, d0 = vi % p.hd + j;
-        bf16_t* v = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + h) * plane;
-        v[(size_t)d0 * sd.cap + pos] = f2bf(x1);
-        v[(size_t)(d0 + 8) * sd.cap + pos] = f2bf(x2);
+        const int vi = vc - qd - kvd + j;  // dims vi and vi + 8 of the row's V
+        float* v = p.blk_v + (size_t)m * kvd;
+        v[vi] = x1;
+        v[vi + 8] = x2;
       }
     }
   }
@@ -1411,7 +1401,7 @@ hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
   p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.y = F.y; p.ssq = F.ssq; p.n_vcols = F.D;
   hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, F.split, st);
   if (e != hipSuccess) return e;
-  return launch_fuse_normalize(F.out, F.y, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
+  return launch_fuse_normalize(F.out, F.out_lo, F.y, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
 }
 
 hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
@@ -1427,7 +1417,7 @@ hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
 }
 
 hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st) {
-  SkinnyA a = make_a(A.ctx, nullptr, A.D, A.T, A.D, nullptr, 0, 0.f);
+  SkinnyA a = make_a(A.ctx, A.ctx_lo, A.D, A.T, A.D, nullptr, 0, 0.f);
   EpiAppendRows::P p;
   for (int i = 0; i < kMaxLayers; ++i) {
     p.wk[i] = i < A.L ? A.wk[i] : A.wk[0];
@@ -1435,7 +1425,7 @@ hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st) {
   }
   p.D = A.D; p.Hkv = A.Hkv; p.hd = A.hd; p.rps = A.rps; p.log2_theta = A.log2_theta;
   p.tau = A.tau; p.seqs = *A.seqs; p.n_vcols = A.L * 2 * A.Hkv * A.hd;
-  return launch_skinny<EpiAppendRows, false>(a, p, p.n_vcols, A.split, st);
+  return launch_skinny<EpiAppendRows, true>(a, p, p.n_vcols, A.split, st);
 }
 
 hipError_t launch_embed(const DraftLaunch& L, hipStream_t st) {
@@ -1451,7 +1441,7 @@ hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
   EpiQKV::P p;
   p.wq = wq; p.wk = wk; p.wv = wv; p.D = L.D; p.Hq = L.Hq; p.Hkv = L.Hkv;
   p.hd = L.hd; p.Bl = L.Bl; p.layer = layer; p.log2_theta = L.log2_theta;
-  p.q_out = L.q; p.q_lo = L.q_lo; p.seqs = *L.seqs;
+  p.q_out = L.q; p.q_lo = L.q_lo; p.blk_k = L.blk_k; p.blk_v = L.blk_v; p.seqs = *L.seqs;
   return launch_skinny<EpiQKV>(a, p, (L.Hq + 2 * L.Hkv) * L.hd, L.split, st, &L.gemm);
 }
 

@@ -1,11 +1,18 @@
-"""GPU parity of context fusion, KV injection and trim/append of the draft KV cache."""
+"""GPU parity of context fusion, KV injection and trim/append of the draft KV cache.
+
+Fusion and injection compute in fp32 and round to bf16 once, so their outputs
+are checked at rounding exactness: equal to round_bf16 of the fp64 oracle
+except within a stated band around the bf16 rounding midpoints (the bands and
+their derivation are in gpu_helpers), where either bf16 neighbour is accepted;
+the number of banded values is printed."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import synth
-from gpu_helpers import DEV, assert_close_rms, make, np32, poisoned_kv, say
+from gpu_helpers import (DEV, fuse_band, inject_band, assert_bf16_rounding, assert_close_rms, make,
+                         np32, poisoned_kv, say)
 from synth import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -21,7 +28,8 @@ def _fuse_check(dc, T, rows=None, gains="random", ld_pad=0):
     torch.cuda.synchronize()
     rows = np.arange(T) if rows is None else rows
     ref = O.fuse_context([np32(f)[rows] for f in feats], np32(w["w_c"]), np32(w["ctx_norm"]), dc.rms_eps)
-    return assert_close_rms(np32(out)[rows], ref, what="fused context")
+    assert_close_rms(np32(out)[rows], ref, what="fused context")
+    return assert_bf16_rounding(np32(out)[rows], ref, fuse_band(dc), "fused context")
 
 
 def test_fuse_tiny():
@@ -73,10 +81,11 @@ def test_fuse_many_rows_narrow_hidden():
     _fuse_check(dc, T, rows=rows, gains="random")
 
 
-def _inject_check(dc, T, pos0_chunks, rows=None, gains="ones"):
-    say(f"inject: config {dc.name} T={T} chunks={pos0_chunks}")
+def _inject_check(dc, T, pos0_chunks, rows=None, gains="ones", seq=0):
+    say(f"inject: config {dc.name} T={T} chunks={pos0_chunks} seq={seq}")
     d, w = make(dc, max_tokens=max(pos0_chunks) if pos0_chunks else T, gains=gains)
-    ctx = synth.make_feats(dc, T, device=DEV)[0]  # any bf16 [T, D] context feature
+    # any bf16 [T, D] context feature (the sequence index picks another draw)
+    ctx = synth.make_feats(dc, T, round_index=seq, device=DEV)[0]
     kv = poisoned_kv(d, T + 32)
     p = 0
     for n in pos0_chunks:
@@ -84,18 +93,22 @@ def _inject_check(dc, T, pos0_chunks, rows=None, gains="ones"):
         p += n
     assert kv.len == T
     torch.cuda.synchronize()
-    rows = np.arange(T) if rows is None else rows
+    rows = np.arange(T) if rows is None else np.asarray(rows)
     ctx_np = np32(ctx)
-    worst = 0.0
+    gk_all, gv_all, ok_all, ov_all = [], [], [], []
     for i, lw in enumerate(w["layers"]):
         for t in rows:
             k, v = O.inject_kv(ctx_np[t:t + 1], np32(lw["wk"]), np32(lw["wv"]), int(t),
                                dc.n_kv_heads, dc.head_dim, dc.rope_theta)
-            gk = np32(kv.k_view(i)[:, t, :])
-            gv = np32(kv.v_view(i)[:, :, t])
-            worst = max(worst, assert_close_rms(gk, k[0], what=f"K layer {i} row {t}"),
-                        assert_close_rms(gv, v[0], what=f"V layer {i} row {t}"))
-    return worst
+            gk_all.append(np32(kv.k_view(i)[:, t, :]))
+            gv_all.append(np32(kv.v_view(i)[:, :, t]))
+            ok_all.append(k[0])
+            ov_all.append(v[0])
+    gk, gv, ok, ov = (np.stack(x) for x in (gk_all, gv_all, ok_all, ov_all))
+    assert_close_rms(gk, ok, what="K")
+    assert_close_rms(gv, ov, what="V")
+    return (assert_bf16_rounding(gk, ok, inject_band(dc), f"K ({len(rows)} rows x {dc.n_layers} layers)") +
+            assert_bf16_rounding(gv, ov, inject_band(dc), f"V ({len(rows)} rows x {dc.n_layers} layers)"))
 
 
 def test_inject_tiny_incremental():
@@ -119,6 +132,37 @@ def test_inject_qwen_shape_ragged_rows():
     rng = np.random.default_rng(6)
     rows = np.unique(np.concatenate([rng.choice(2048, 10, replace=False), [2047, 2048, 2100, 2147]]))
     _inject_check(dc, 2148, [2148], rows=rows)
+
+
+def test_inject_d2048_full_shape():
+    # D = 2048, 4 KV heads, 5 layers: N = 5 x 2 x 512 columns (16 tiles of 320)
+    dc = CONFIGS[4]
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([rng.choice(2048, 20, replace=False), [0, 2047]]))
+    _inject_check(dc, 2048, [2048], rows=rows)
+
+
+@pytest.mark.slow
+def test_inject_long_context_prefill_8192_sampled_rows():
+    # the long-context workload's prefill: 8192 rows in one call (32 row
+    # tiles of 256), sampled rows including the first and the last tile's
+    dc = CONFIGS[2]
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([rng.choice(8192, 16, replace=False), [0, 7936, 8191]]))
+    _inject_check(dc, 8192, [8192], rows=rows)
+
+
+def test_inject_ragged_batch_two_of_32_sequences():
+    # the 32-sequence workload: each sequence's context is injected into its
+    # own cache at its ragged length; checked on the first sequence and the
+    # longest one
+    dc = CONFIGS[3]
+    lens = synth.ragged_lengths(32)
+    for s in (0, int(np.argmax(lens))):
+        T = int(lens[s])
+        rng = np.random.default_rng(10 + s)
+        rows = np.unique(np.concatenate([rng.choice(T, 8, replace=False), [T - 1]]))
+        _inject_check(dc, T, [T], rows=rows, seq=s)
 
 
 def test_trim_then_append_overwrites_rejected_rows():

@@ -1,15 +1,18 @@
-"""GPU parity of the draft forward against the oracle: every layer's
-residual stream within 3e-2 x RMS, drafted tokens identical except where the
-oracle's top-2 gap is below 1e-2. KV buffers are filled with NaN first, so any
-read of a row outside [0, len + block_len) would show up as non-finite."""
+"""GPU parity of the draft forward against the plain oracle (fp64 throughout,
+fp64 context rows): every layer's residual stream within 3e-2 x RMS (the
+stated bound) - and, since the synthetic context rows are bf16 values that
+both sides hold exactly, also within the regression bound TIGHT_TOL x RMS -
+and drafted tokens identical except where the oracle's top-2 gap is below
+1e-2. KV buffers are filled with NaN first, so any read of a row outside
+[0, len) would show up as non-finite."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import synth
-from gpu_helpers import (DEV, assert_hidden, assert_tokens, fill_context, make, np32,
-                         oracle_cache, poisoned_kv, say, synthetic_context, weights_np)
+from gpu_helpers import (DEV, TIGHT_TOL, assert_hidden, assert_tokens, fill_context, hidden_errs,
+                         make, np32, oracle_cache, poisoned_kv, say, synthetic_context, weights_np)
 from synth import CONFIGS
 
 pytestmark = pytest.mark.gpu
@@ -40,8 +43,10 @@ def _run(dc, lens, bl=None, gains="ones", logits=False, max_ctx=None, oracle_seq
     worst, flips = 0.0, 0
     for s in sel:
         orc = O.draft_block(dc, wn, [oracle_cache(dc, ctxs[s])], [int(anchors[s])], bl)
-        worst = max(worst, assert_hidden(hid[:, s:s + 1].reshape(dc.n_layers, bl, -1), orc["hidden"],
-                                         what=f"seq {s}"))
+        g = hid[:, s:s + 1].reshape(dc.n_layers, bl, -1)
+        say(f"  seq {s}: hidden err / rms per layer " +
+            " ".join(f"{e:.2e}" for e in hidden_errs(g, orc["hidden"])))
+        worst = max(worst, assert_hidden(g, orc["hidden"], what=f"seq {s}", tol=TIGHT_TOL))
         if bl > 1:
             flips += assert_tokens(block[s:s + 1], orc, what=f"seq {s}")
             if logits:
@@ -122,6 +127,9 @@ def test_qwen_shape_32_ragged_sequences_sampled():
 
 
 def test_chained_fuse_inject_draft_tiny():
+    # fuse -> inject -> draft on the GPU; the plain oracle keeps H_t and the
+    # cache rows in fp64, the storage-model oracle rounds both to bf16 as the
+    # library stores them
     dc = CONFIGS[0]
     say("chained fuse -> inject -> draft: tiny")
     d, w = make(dc, gains="random")
@@ -134,8 +142,13 @@ def test_chained_fuse_inject_draft_tiny():
     torch.cuda.synchronize()
     wn = weights_np(w)
     H = O.fuse_context([np32(f) for f in feats], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
-    cache = O.DraftCache(dc.n_layers, bf16_kv=True)
-    O.cache_inject(cache, O.round_bf16(H), wn["layers"], dc, 0)  # H_t is stored as bf16
-    orc = O.draft_block(dc, wn, [cache], [int(anchors[0])])
+    plain = O.DraftCache(dc.n_layers)
+    O.cache_inject(plain, H, wn["layers"], dc, 0)
+    orc = O.draft_block(dc, wn, [plain], [int(anchors[0])])
+    say("  plain: " + " ".join(f"{e:.2e}" for e in hidden_errs(np32(hid), orc["hidden"])))
     assert_hidden(np32(hid), orc["hidden"])
     assert_tokens(block.cpu().numpy(), orc)
+    store = O.DraftCache(dc.n_layers, bf16_kv=True)
+    O.cache_inject(store, O.round_bf16(H), wn["layers"], dc, 0)
+    orc_s = O.draft_block(dc, wn, [store], [int(anchors[0])])
+    assert_hidden(np32(hid), orc_s["hidden"], tol=TIGHT_TOL, what="storage model")

@@ -3,24 +3,50 @@ long-context workload (8192 context tokens, 4 rounds, block 16), and of the
 device-resident rounds (lengths, tau and anchors kept on the GPU, a round
 captured into a graph).
 
-The initial 8192 context rows are seeded synthetic K/V written into both
-caches; each round's accepted rows are then fused from fresh target hidden
-states and injected by the library, exactly as a host loop would do after
-verification (txtmix article section 9). Verification runs on the oracle's
-drafted block (so no oracle input comes from the GPU path); the GPU's own
-drafted tokens are compared with the oracle's under the top-2 gap rule."""
+The initial context rows are seeded synthetic K/V written into every cache;
+each round's accepted rows are then fused from fresh target hidden states and
+injected by the library, exactly as a host loop would do after verification
+(txtmix article section 9). Verification runs on the oracle's drafted block
+(so no oracle input comes from the GPU path); the GPU's own drafted tokens
+are compared with the oracle's under the top-2 gap rule.
+
+Two oracles run every round:
+  * plain - the definition: the accepted rows' H_t unrounded, cache rows in
+    fp64; every layer's hidden state within 3e-2 x RMS;
+  * storage model - the rows the library stores rounded to bf16 (the
+    host-driven path also hands the fused H_t over as bf16, the
+    device-resident append keeps it unrounded); within TIGHT_TOL x RMS, a
+    regression check of the kernels' own arithmetic.
+The fused rows and the appended K/V are checked against round_bf16 of the
+oracle outside a band around the bf16 rounding midpoints."""
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import synth
-from gpu_helpers import (DEV, assert_close_rms, assert_hidden, assert_tokens, fill_context,
-                         make, np32, oracle_cache, poisoned_kv, say, synthetic_context,
-                         weights_np)
+from gpu_helpers import (DEV, append_band, fuse_band, inject_band, TIGHT_TOL, assert_bf16_rounding,
+                         assert_close_rms, assert_hidden, assert_tokens, fill_context, hidden_errs,
+                         make, np32, oracle_cache, poisoned_kv, say, synthetic_context, weights_np)
 from synth import CONFIGS
 
 pytestmark = pytest.mark.gpu
+
+# The host-driven append hands the fused rows over as bf16: where an exact
+# value lies within the fusion's fp32 error of a rounding midpoint the GPU
+# and round_bf16 of the oracle may pick different neighbours (both correct),
+# and the changed rows move the next drafts. This random-init drafter
+# amplifies small changes of a few context rows (rounding all 48 appended
+# rows of a 2048-token context moves the last layer by 1.4 % of its RMS), so
+# after appended rounds the storage-model bound is 5e-3 instead of TIGHT_TOL
+# (2.0e-3 measured at the long-context workload's third round).
+HOST_APPEND_TOL = 5e-3
+
+def _layer_rows(kv, i, a, b):
+    """K [rows, Hkv, hd] and V [rows, Hkv, hd] of positions a..b-1 of layer i."""
+    gk = np32(kv.k_view(i)[:, a:b, :]).transpose(1, 0, 2)
+    gv = np32(kv.v_view(i)[:, :, a:b]).transpose(2, 0, 1)
+    return gk, gv
 
 
 def _rounds(dc, S0, n_rounds):
@@ -30,19 +56,28 @@ def _rounds(dc, S0, n_rounds):
     kv = poisoned_kv(d, S0 + B * (n_rounds + 1))
     ctx = synthetic_context(dc, S0)
     fill_context(kv, ctx)
-    ocache = oracle_cache(dc, ctx)
+    plain = oracle_cache(dc, ctx)
+    store = oracle_cache(dc, ctx, bf16_kv=True)
+    # the appended rows' K/V from the bf16 H_t in fp64, before the cache's rounding
+    unr_k = [[] for _ in range(dc.n_layers)]
+    unr_v = [[] for _ in range(dc.n_layers)]
     taus = synth.planted_taus(dc, n_rounds, salt=5)
     anchor = int(synth.make_anchor(dc)[0])
     S = S0
+    exact_rows = []   # appended rows whose fused H_t the GPU rounded exactly as the oracle
     for r in range(n_rounds):
         say(f"round {r}: context {S}, planted tau {int(taus[r])}")
         block, hid, _ = d.draft_block([kv], torch.tensor([anchor], dtype=torch.int32, device=DEV),
                                       hidden=True)
         torch.cuda.synchronize()
         assert kv.len == S
-        orc = O.draft_block(dc, wn, [ocache], [anchor])
-        assert_hidden(np32(hid), orc["hidden"], what=f"round {r}")
+        orc = O.draft_block(dc, wn, [plain], [anchor])
+        say("  plain: " + " ".join(f"{e:.2e}" for e in hidden_errs(np32(hid), orc["hidden"])))
+        assert_hidden(np32(hid), orc["hidden"], what=f"round {r} (plain)")
         assert_tokens(block.cpu().numpy(), orc, what=f"round {r}")
+        orc_s = O.draft_block(dc, wn, [store], [anchor])
+        assert_hidden(np32(hid), orc_s["hidden"], tol=HOST_APPEND_TOL if r else TIGHT_TOL,
+                      what=f"round {r} (storage model)")
         # verification of the oracle's block against planted target logits
         blk = np.concatenate([[anchor], orc["draft"][0]]).astype(np.int32)
         lg = synth.make_target_logits(dc, B, round_index=10 + r)
@@ -56,18 +91,33 @@ def _rounds(dc, S0, n_rounds):
         H = d.fuse_context(feats)
         d.inject_kv(kv, H, S)
         Ho = O.fuse_context([np32(f) for f in feats], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
-        assert_close_rms(np32(H), Ho, what=f"round {r} fused rows")
-        O.cache_inject(ocache, O.round_bf16(Ho), wn["layers"], dc, S)
+        Hg = np32(H)
+        assert_bf16_rounding(Hg, Ho, fuse_band(dc), f"round {r} fused rows")
+        exact_rows += [S + t for t in range(tau) if np.array_equal(Hg[t], O.round_bf16(Ho[t]))]
+        O.cache_inject(plain, Ho, wn["layers"], dc, S)
+        O.cache_inject(store, O.round_bf16(Ho), wn["layers"], dc, S)
+        for i, lw in enumerate(wn["layers"]):
+            k, v = O.inject_kv(O.round_bf16(Ho), lw["wk"], lw["wv"], S, dc.n_kv_heads, dc.head_dim,
+                               dc.rope_theta)
+            unr_k[i].append(k)
+            unr_v[i].append(v)
         S += tau
         anchor = bonus
-        assert kv.len == S == ocache.len
+        assert kv.len == S == plain.len == store.len
     torch.cuda.synchronize()
-    # the appended rows of the cache, layer by layer
+    # the appended rows of the cache, layer by layer: against the plain
+    # oracle at the stated bound, and - rows whose fused input the GPU
+    # rounded exactly as round_bf16 of the oracle, so both sides project the
+    # same bf16 row - at rounding exactness
+    say(f"  appended rows {S - S0}, {len(exact_rows)} with an exactly rounded H_t")
+    ex = np.array(exact_rows, dtype=np.int64) - S0
     for i in range(dc.n_layers):
-        gk = np32(kv.k_view(i)[:, S0:S, :]).transpose(1, 0, 2)
-        gv = np32(kv.v_view(i)[:, :, S0:S]).transpose(2, 0, 1)
-        assert_close_rms(gk, ocache.k[i][S0:S], what=f"appended K layer {i}")
-        assert_close_rms(gv, ocache.v[i][S0:S], what=f"appended V layer {i}")
+        gk, gv = _layer_rows(kv, i, S0, S)
+        assert_close_rms(gk, plain.k[i][S0:S], what=f"appended K layer {i} (plain)")
+        assert_close_rms(gv, plain.v[i][S0:S], what=f"appended V layer {i} (plain)")
+        if len(ex):
+            assert_bf16_rounding(gk[ex], np.concatenate(unr_k[i])[ex], inject_band(dc), f"appended K layer {i}")
+            assert_bf16_rounding(gv[ex], np.concatenate(unr_v[i])[ex], inject_band(dc), f"appended V layer {i}")
     return S
 
 
@@ -88,18 +138,21 @@ def _rounds_dev(dc, S0s, n_rounds, salt=0):
     each sequence's fresh target features and advances the device lengths.
     The next anchors are the bonus tokens, read by the next draft from device
     memory. The oracle runs the same rounds; nothing is read back to drive
-    the GPU loop."""
+    the GPU loop. The append keeps the fused rows unrounded until the
+    injection, so the storage-model oracle injects the unrounded H_t into
+    bf16 rows."""
     B = dc.block_size
     n = len(S0s)
     d, w = make(dc, max_seqs=n, max_tokens=max(n * B, 16))
     wn = weights_np(w)
-    kvs, ocaches = [], []
+    kvs, plains, stores = [], [], []
     for s, S0 in enumerate(S0s):
         kv = poisoned_kv(d, S0 + B * (n_rounds + 1))
         ctx = synthetic_context(dc, S0, seq=s)
         fill_context(kv, ctx)
         kvs.append(kv)
-        ocaches.append(oracle_cache(dc, ctx))
+        plains.append(oracle_cache(dc, ctx))
+        stores.append(oracle_cache(dc, ctx, bf16_kv=True))
     len_dev = torch.tensor(S0s, dtype=torch.int32, device=DEV)
     anchors = [int(a) for a in synth.make_anchor(dc, n=n)]
     anchor_dev = torch.tensor(anchors, dtype=torch.int32, device=DEV)
@@ -109,10 +162,12 @@ def _rounds_dev(dc, S0s, n_rounds, salt=0):
     bonus_dev = torch.empty(n, dtype=torch.int32, device=DEV)
     taus = synth.planted_taus(dc, n_rounds * n, salt=11 + salt).reshape(n_rounds, n)
     S = list(S0s)
+    worst = 0.0
     for r in range(n_rounds):
         say(f"device round {r}: contexts {S}")
         d.draft_block_dev(kvs, len_dev, anchor_dev, blk_dev, hidden=hid)
-        orc = O.draft_block(dc, wn, ocaches, anchors)
+        orc = O.draft_block(dc, wn, plains, anchors)
+        orc_s = O.draft_block(dc, wn, stores, anchors)
         # verify the oracle's blocks (no oracle input from the GPU path)
         oblk = np.concatenate([np.array(anchors)[:, None], orc["draft"]], axis=1).astype(np.int32)
         lg = torch.stack([synth.make_target_logits(dc, B, round_index=40 + 7 * r + s) for s in range(n)])
@@ -122,28 +177,37 @@ def _rounds_dev(dc, S0s, n_rounds, salt=0):
         feats = synth.make_feats(dc, n * B, round_index=60 + r, device=DEV)
         d.append_dev(kvs, len_dev, tau_dev, feats, B)
         anchor_dev.copy_(bonus_dev)
-        # oracle: same round
+        # checks of the draft (read-back only to compare)
+        errs = hidden_errs(np32(hid), orc["hidden"])
+        say("  plain: " + " ".join(f"{e:.2e}" for e in errs))
+        worst = max(worst, max(errs))
+        assert_hidden(np32(hid), orc["hidden"], what=f"device round {r} (plain)")
+        assert_hidden(np32(hid), orc_s["hidden"], tol=TIGHT_TOL, what=f"device round {r} (storage model)")
+        assert_tokens(blk_dev.cpu().numpy(), orc, what=f"device round {r}")
+        # oracle: the same round's verification and append
         fn = [np32(f) for f in feats]
         for s in range(n):
             t, b = O.verify_greedy(oblk[s], lg[s].numpy())
             assert t == taus[r, s]
             Ho = O.fuse_context([f[s * B:s * B + t] for f in fn], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
-            O.cache_inject(ocaches[s], O.round_bf16(Ho), wn["layers"], dc, S[s])
+            O.cache_inject(plains[s], Ho, wn["layers"], dc, S[s])
+            O.cache_inject(stores[s], Ho, wn["layers"], dc, S[s])
             S[s] += t
             anchors[s] = b
-        # checks (read-back only to compare)
-        assert_hidden(np32(hid), orc["hidden"], what=f"device round {r}")
-        assert_tokens(blk_dev.cpu().numpy(), orc, what=f"device round {r}")
         assert len_dev.cpu().tolist() == S
         assert anchor_dev.cpu().tolist() == anchors
         assert [k.len for k in kvs] == list(S0s)  # the host lengths are not used
     torch.cuda.synchronize()
+    say(f"  worst plain hidden err / rms {worst:.2e}")
     for s in range(n):
+        a, b = S0s[s], S[s]
         for i in range(dc.n_layers):
-            gk = np32(kvs[s].k_view(i)[:, S0s[s]:S[s], :]).transpose(1, 0, 2)
-            gv = np32(kvs[s].v_view(i)[:, :, S0s[s]:S[s]]).transpose(2, 0, 1)
-            assert_close_rms(gk, ocaches[s].k[i][S0s[s]:S[s]], what=f"seq {s} appended K layer {i}")
-            assert_close_rms(gv, ocaches[s].v[i][S0s[s]:S[s]], what=f"seq {s} appended V layer {i}")
+            gk, gv = _layer_rows(kvs[s], i, a, b)
+            pk, pv = plains[s].k[i][a:b], plains[s].v[i][a:b]
+            assert_close_rms(gk, pk, what=f"seq {s} appended K layer {i} (plain)")
+            assert_close_rms(gv, pv, what=f"seq {s} appended V layer {i} (plain)")
+            assert_bf16_rounding(gk, pk, append_band(dc), f"seq {s} appended K layer {i}")
+            assert_bf16_rounding(gv, pv, append_band(dc), f"seq {s} appended V layer {i}")
     return d, kvs, len_dev
 
 
@@ -233,7 +297,7 @@ def test_device_trim_and_length_clamp():
         ctx = synthetic_context(dc, S0, seq=s)
         fill_context(kv, ctx)
         kvs.append(kv)
-        ocaches.append(oracle_cache(dc, ctx))
+        ocaches.append(oracle_cache(dc, ctx))   # plain: fp64 rows, H_t unrounded
     len_dev = torch.tensor([10, 13], dtype=torch.int32, device=DEV)
     d.kv_trim_dev(len_dev, 12)
     assert len_dev.cpu().tolist() == [10, 12]
@@ -247,12 +311,11 @@ def test_device_trim_and_length_clamp():
         n_fit = max_ctx - S
         Ho = O.fuse_context([f[s * B:s * B + n_fit] for f in fn], wn["w_c"], wn["ctx_norm"], dc.rms_eps)
         ocaches[s].trim(S)
-        O.cache_inject(ocaches[s], O.round_bf16(Ho), wn["layers"], dc, S)
+        O.cache_inject(ocaches[s], Ho, wn["layers"], dc, S)
         for i in range(dc.n_layers):
-            gk = np32(kvs[s].k_view(i)[:, S:max_ctx, :]).transpose(1, 0, 2)
-            gv = np32(kvs[s].v_view(i)[:, :, S:max_ctx]).transpose(2, 0, 1)
-            assert_close_rms(gk, ocaches[s].k[i][S:max_ctx], what=f"seq {s} K layer {i}")
-            assert_close_rms(gv, ocaches[s].v[i][S:max_ctx], what=f"seq {s} V layer {i}")
+            gk, gv = _layer_rows(kvs[s], i, S, max_ctx)
+            assert_bf16_rounding(gk, ocaches[s].k[i][S:max_ctx], append_band(dc), f"seq {s} K layer {i}")
+            assert_bf16_rounding(gv, ocaches[s].v[i][S:max_ctx], append_band(dc), f"seq {s} V layer {i}")
         # rows past max_ctx (up to the capacity) were not written: still poisoned
         rest = kvs[s].k_view(0)[:, max_ctx:max_ctx + 2, :].float()
         if rest.numel():

@@ -170,3 +170,57 @@ def test_sampling_round_from_draft_logits():
             checked += 1
         checked += n
     assert checked >= 20
+
+
+def test_greedy_32_sequences_in_one_call():
+    # the 32-sequence workload: every sequence's block verified in one call,
+    # planted agreement lengths k ~ Geometric(0.25) capped at the block
+    dc = CONFIGS[3]
+    n, bl = 32, dc.block_size
+    say(f"greedy verify: config {dc.name} n_seqs={n} in one call")
+    d, _ = make(dc, max_seqs=n)
+    rng = np.random.default_rng(31)
+    taus = synth.planted_taus(dc, n, salt=3)
+    ids, lg = _greedy_case(dc, n, bl, rng, [int(t) - 1 for t in taus])
+    tau, bonus = d.verify(torch.from_numpy(ids).to(DEV), lg.to(DEV))
+    tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+    for s in range(n):
+        t, b = O.verify_greedy(ids[s], lg[s].numpy())
+        assert (tau[s], bonus[s]) == (t, b), s
+        assert t == taus[s]
+
+
+def test_pq_d2048_block8_philox_seed0():
+    # the D=2048 workload's verification: temperature 1, target and draft
+    # logits N(0, 1) per row, draft tokens drawn from q, uniforms from Philox
+    # with seed 0; decisions with |p/q - u| < 1e-4 (or a draw within 1e-12 of
+    # a CDF boundary) are excluded and counted
+    dc = CONFIGS[4]
+    bl, temp, seed = dc.block_size, dc.temperature, 0
+    n = 4
+    say(f"p/q verify: config {dc.name} block_len={bl} seed={seed}")
+    d, _ = make(dc, max_seqs=n)
+    checked = excluded = 0
+    for trial in range(6):
+        g = torch.Generator().manual_seed(900 + trial)
+        T = torch.randn(n, bl, dc.vocab, generator=g)
+        Q = torch.randn(n, bl - 1, dc.vocab, generator=g)
+        off = bl * trial
+        ids = []
+        for s in range(n):
+            x, _ = O.sample_draft_tokens(Q[s].numpy(), temp, seed, off, s)
+            ids.append(np.concatenate([[7 + s], x]).astype(np.int32))
+        ids = np.stack(ids)
+        tau, bonus = d.verify(torch.from_numpy(ids).to(DEV), T.to(DEV), Q.to(DEV), temperature=temp,
+                              seed=seed, philox_offset=off)
+        tau, bonus = tau.cpu().numpy(), bonus.cpu().numpy()
+        for s in range(n):
+            t, b, diag = O.verify_pq(ids[s], T[s].numpy(), Q[s].numpy(), temp, seed, off, s)
+            assert 1 <= tau[s] <= bl
+            if min(diag["ratio_margin"] or [1.0]) < 1e-4 or diag["cdf_margin"] < 1e-12:
+                excluded += 1
+                continue
+            assert (tau[s], bonus[s]) == (t, b), (trial, s, diag)
+            checked += 1
+    say(f"  {checked} rounds compared, {excluded} excluded by the bands")
+    assert checked >= 20
