@@ -95,6 +95,7 @@ def _load():
         "dflash_kv_trim": (C.c_int, [P, kvp, I32]),
         "dflash_draft_block": (C.c_int, [P, I32, C.POINTER(kvp), P, I32, P, P, P]),
         "dflash_verify": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
+        "dflash_verify_noalloc": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P]),
         "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
         "dflash_verify_candidates": (C.c_int, [P, I32, I32, P, P, P, P, I32, F32, U64, U64, P, P]),
         "dflash_set_selector": (C.c_int, [P, C.POINTER(dflash_selector)]),
@@ -189,6 +190,16 @@ def dflash_verify(h, n_seqs: int, block_len: int, block_ids: int, target_logits:
                                      C.c_void_p(target_logits), C.c_void_p(draft_logits or None),
                                      float(temperature), seed, philox_offset,
                                      C.c_void_p(tau_out), C.c_void_p(bonus_out)))
+
+
+def dflash_verify_noalloc(h, n_seqs: int, block_len: int, block_ids: int, target_logits: int,
+                          draft_logits: int, temperature: float, seed: int, philox_offset: int,
+                          tau_out: int, bonus_out: int):
+    return _check(_lib.dflash_verify_noalloc(h, n_seqs, block_len, C.c_void_p(block_ids),
+                                             C.c_void_p(target_logits),
+                                             C.c_void_p(draft_logits or None), float(temperature),
+                                             seed, philox_offset, C.c_void_p(tau_out),
+                                             C.c_void_p(bonus_out)))
 
 
 def dflash_draft_block_dev(h, kvs: Sequence[dflash_kv], len_dev: int, anchor_ids: int,

@@ -682,6 +682,51 @@ dflash_status dflash_kv_trim_dev(dflash_handle* h, int32_t n_seqs, int32_t* len_
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "kv_trim_dev");
 }
 
+}  // extern "C"
+
+// The checks and launches of dflash_verify; the partials go to part / part2
+// (max_rows rows of merged statistics, then the slice sums).
+static dflash_status verify_impl(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                 const int32_t* block_ids, const float* target_logits,
+                                 const float* draft_logits, float temperature, uint64_t seed,
+                                 uint64_t philox_offset, int32_t* tau_out, int32_t* bonus_out,
+                                 void* part, void* part2, int max_rows, int seq_cap,
+                                 const char* name) {
+  const dflash_config& c = h->cfg;
+  if (n_seqs < 1 || n_seqs > seq_cap)
+    return fail(DFLASH_E_SHAPE, "%s: n_seqs=%d outside 1..%d", name, n_seqs, seq_cap);
+  if (block_len < 1 || block_len > c.block_size)
+    return fail(DFLASH_E_SHAPE, "%s: block_len=%d outside 1..%d", name, block_len, c.block_size);
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(DFLASH_E_SHAPE, "%s: temperature must be finite and >= 0", name);
+  const bool greedy = temperature == 0.f;
+  if (!greedy && block_len > 1 && !draft_logits)
+    return fail(DFLASH_E_NULL, "%s: draft_logits are required when temperature > 0", name);
+  if (greedy && draft_logits)
+    return fail(DFLASH_E_SHAPE, "%s: draft_logits must be NULL when temperature == 0", name);
+  if (c.vocab % 4 == 0 && !aligned(target_logits, 16))
+    return fail(DFLASH_E_ALIGN, "%s: target_logits not 16-byte aligned", name);
+  const int rows = greedy ? n_seqs * block_len : n_seqs * (2 * block_len - 1);
+  if (rows > max_rows)
+    return fail(DFLASH_E_CAPACITY, "%s: %d verification rows exceed the scratch's %d", name, rows,
+                max_rows);
+  VerifyLaunch P{};
+  P.n_seqs = n_seqs; P.Bl = block_len; P.V = c.vocab;
+  P.block_ids = block_ids; P.target = target_logits; P.draft = draft_logits;
+  P.temperature = (double)temperature; P.seed = seed; P.offset = philox_offset;
+  P.tau = tau_out; P.bonus = bonus_out;
+  P.part = part;
+  P.part2 = part2;
+  P.max_rows = max_rows;
+  P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
+  hipError_t e = timed(h, ST_VERIFY, [&] {
+    return greedy ? launch_verify_greedy(P, h->stream) : launch_verify_pq(P, h->stream);
+  });
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, name);
+}
+
+extern "C" {
+
 dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
                             const int32_t* block_ids, const float* target_logits,
                             const float* draft_logits, float temperature, uint64_t seed,
@@ -689,34 +734,27 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
   if (!h || !block_ids || !target_logits || !tau_out || !bonus_out)
     return fail(DFLASH_E_NULL, "handle, block_ids, target_logits, tau_out and bonus_out are required");
   if (!h->ws) return fail(DFLASH_E_STATE, "no workspace set");
-  const dflash_config& c = h->cfg;
-  if (n_seqs < 1 || n_seqs > h->max_seqs)
-    return fail(DFLASH_E_SHAPE, "n_seqs=%d outside 1..%d", n_seqs, h->max_seqs);
-  if (block_len < 1 || block_len > c.block_size)
-    return fail(DFLASH_E_SHAPE, "block_len=%d outside 1..%d", block_len, c.block_size);
-  if (!(temperature >= 0.f) || !std::isfinite(temperature))
-    return fail(DFLASH_E_SHAPE, "temperature must be finite and >= 0");
-  const bool greedy = temperature == 0.f;
-  if (!greedy && block_len > 1 && !draft_logits)
-    return fail(DFLASH_E_NULL, "draft_logits are required when temperature > 0");
-  if (greedy && draft_logits)
-    return fail(DFLASH_E_SHAPE, "draft_logits must be NULL when temperature == 0");
-  if (c.vocab % 4 == 0 && !aligned(target_logits, 16))
-    return fail(DFLASH_E_ALIGN, "target_logits not 16-byte aligned");
-  VerifyLaunch P{};
-  P.n_seqs = n_seqs; P.Bl = block_len; P.V = c.vocab;
-  P.block_ids = block_ids; P.target = target_logits; P.draft = draft_logits;
-  P.temperature = (double)temperature; P.seed = seed; P.offset = philox_offset;
-  P.tau = tau_out; P.bonus = bonus_out;
-  P.part = h->ws + h->lay.vpart;
-  P.part2 = h->ws + h->lay.vcdf;
-  P.max_rows = 2 * h->max_seqs * c.block_size;
-  const int rows = greedy ? n_seqs * block_len : n_seqs * (2 * block_len - 1);
-  P.splits = std::max(1, std::min(kVerifyMaxSplits, (1024 + rows - 1) / rows));
-  hipError_t e = timed(h, ST_VERIFY, [&] {
-    return greedy ? launch_verify_greedy(P, h->stream) : launch_verify_pq(P, h->stream);
-  });
-  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "verify");
+  return verify_impl(h, n_seqs, block_len, block_ids, target_logits, draft_logits, temperature,
+                     seed, philox_offset, tau_out, bonus_out, h->ws + h->lay.vpart,
+                     h->ws + h->lay.vcdf, 2 * h->max_seqs * h->cfg.block_size, h->max_seqs,
+                     "verify");
+}
+
+dflash_status dflash_verify_noalloc(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                    const int32_t* block_ids, const float* target_logits,
+                                    const float* draft_logits, float temperature, uint64_t seed,
+                                    uint64_t philox_offset, int32_t* tau_out, int32_t* bonus_out) {
+  if (!h || !block_ids || !target_logits || !tau_out || !bonus_out)
+    return fail(DFLASH_E_NULL, "handle, block_ids, target_logits, tau_out and bonus_out are required");
+  // the fixed scratch of the current device (its address is looked up on
+  // the first call on each device and kept)
+  void* scratch = nullptr;
+  hipError_t e = verify_scratch_ptr(&scratch);
+  if (e != hipSuccess) return dev_fail(e, "verify_noalloc: scratch address");
+  unsigned char* base = static_cast<unsigned char*>(scratch);
+  return verify_impl(h, n_seqs, block_len, block_ids, target_logits, draft_logits, temperature,
+                     seed, philox_offset, tau_out, bonus_out, base, base + kVerifyScratchPart,
+                     kVerifyScratchRows, kMaxSeqs, "verify_noalloc");
 }
 
 dflash_status dflash_verify_candidates(dflash_handle* h, int32_t n_seqs, int32_t block_len,

@@ -168,6 +168,17 @@ struct VerifyLaunch {
   int k;
 };
 hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st);
+// Fixed verification scratch for callers without a workspace: row partials
+// of up to kVerifyScratchRows rows x kVerifyMaxSplits splits (16 B each),
+// kVerifyScratchRows merged row statistics (16 B) and kVerifyScratchRows / 2
+// x kVerifyMaxSplits slice sums (8 B). verify_scratch_ptr returns the
+// current device's copy (looked up once per device).
+constexpr int kVerifyScratchRows = 2048;
+constexpr size_t kVerifyScratchPart = (size_t)kVerifyScratchRows * kVerifyMaxSplits * 16;
+constexpr size_t kVerifyScratchBytes =
+    kVerifyScratchPart + (size_t)kVerifyScratchRows * 16 + (size_t)kVerifyScratchRows / 2 * kVerifyMaxSplits * 8;
+constexpr int kVerifyScratchDevices = 64;
+hipError_t verify_scratch_ptr(void** out);
 hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st);
 // p/q with P.cand / P.qc (P.draft unused)
 hipError_t launch_verify_pq_cand(const VerifyLaunch& P, hipStream_t st);

@@ -17,6 +17,8 @@
 //
 // Sampling-mode drafting draws the block's tokens from the draft's own
 // distribution the same way (purpose 2), so that the p/q rule sees x ~ q.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -478,6 +480,38 @@ hipError_t launch_verify_pq(const VerifyLaunch& P, hipStream_t st) {
                      P, part, merged, sums);
   hipLaunchKernelGGL(pq_pick, dim3(P.n_seqs), dim3(kCdfThreads), 0, st, P, merged, sums);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// verification scratch without a workspace: a fixed device array per GPU
+// ---------------------------------------------------------------------------
+// The partials of verify_noalloc live in this file-scope array (each GPU the
+// library runs on holds its own copy until the process ends). Host code must
+// never pass the array's name to a kernel: in host code it is a host-side
+// stand-in, not a device address. Its device address is looked up once per
+// device, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[kVerifyScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kVerifyScratchDevices];
+}  // namespace
+
+hipError_t verify_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kVerifyScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dfl

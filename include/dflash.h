@@ -295,6 +295,29 @@ dflash_status dflash_verify(dflash_handle* h, int32_t n_seqs, int32_t block_len,
                             int32_t* tau_out, int32_t* bonus_out);
 
 /*
+ * dflash_verify without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments, checks and results as
+ * dflash_verify, but the handle needs no workspace (dflash_set_workspace is
+ * not required) and the kernels' partials live in a fixed scratch array of
+ * the library, one per GPU, 2.6 MiB, held until the process ends. Nothing is
+ * allocated and nothing in the scratch needs clearing (every partial is
+ * written before it is read).
+ * Limits: 1 <= n_seqs <= 64; the verification rows - n_seqs * block_len
+ * (greedy) or n_seqs * (2 * block_len - 1) (p/q) - at most 2048, else
+ * DFLASH_E_CAPACITY with nothing launched.
+ * All calls on one GPU share that GPU's scratch: calls that overlap on one
+ * GPU (concurrent streams, or several host threads) race and must not be
+ * made. The scratch's device address is looked up on the first call on each
+ * device (with that device current); a failure there is DFLASH_E_DEVICE.
+ */
+dflash_status dflash_verify_noalloc(dflash_handle* h, int32_t n_seqs, int32_t block_len,
+                                    const int32_t* block_ids, const float* target_logits,
+                                    const float* draft_logits, float temperature,
+                                    uint64_t seed, uint64_t philox_offset,
+                                    int32_t* tau_out, int32_t* bonus_out);
+
+/*
  * DFlash 2 candidate selector ([Code] section 13: the right token is usually
  * among a drafted row's top candidates; each adjacent pair is scored as
  * S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>, and one walk over the scores
