@@ -18,12 +18,15 @@
 // the current one.
 //
 // Split K: when the tiles alone would leave CUs idle, S workgroups share a
-// tile, each over K/S. They sit on one XCD (workgroups go to XCDs round-robin
-// by id, and the S of a tile have ids 8 apart), so their partial sums meet in
-// that XCD's L2: each writes its partial, waits for the stores, and counts
-// itself in on the tile's counter; the last to arrive adds the others'
-// partials (read past the CU's L1) and runs the epilogue. Nobody waits for
-// anybody, so there is no co-residency requirement.
+// tile, each over K/S. Each writes its fp32 partial and counts itself in on
+// the tile's counter with an agent-scope release (its partial is written back
+// past its XCD's L2 before the count); the last to arrive takes an
+// agent-scope acquire (stale lines of its L1 and L2 dropped) before it adds
+// the others' partials in split order and runs the epilogue. The splits may
+// therefore run on any XCDs. Workgroup ids are still laid out so that the S
+// of a tile are consecutive on one XCD (ids 8 apart), where their partials
+// meet in one L2. Nobody waits for anybody, so there is no co-residency
+// requirement.
 //
 // Users: the prefill fusion and injection (gemm.hip) and the draft GEMMs of
 // batches too tall for the weight-streaming kernels (skinny.hip). The A
@@ -333,17 +336,19 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
           f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           *reinterpret_cast<f32x4*>(mine + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
         }
-    __builtin_amdgcn_s_waitcnt(DFL_VM(0));  // the partial has reached L2
-    __syncthreads();  // (also: every wave is done with the ring)
+    __builtin_amdgcn_s_waitcnt(DFL_VM(0));  // this wave's partial has reached its L2
+    __syncthreads();  // every wave's has (also: every wave is done with the ring)
     int32_t* arrived = reinterpret_cast<int32_t*>(smem);
+    // agent-scope release: the workgroup's partial (all waves' stores, ordered
+    // before this point by the barrier) is visible on every XCD before the
+    // count; the last arriver's acquire makes the others' partials visible
+    // to it
     if (tid == 0)
-      *arrived = __hip_atomic_fetch_add(sp.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *arrived = __hip_atomic_fetch_add(sp.ctr + tile, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*arrived != sp.S - 1) return;
     if (tid == 0) __hip_atomic_store(sp.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the other splits' partials are in this XCD's L2; drop any stale copy
-    // from this CU's L1 before reading them
-    asm volatile("buffer_inv sc0" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
