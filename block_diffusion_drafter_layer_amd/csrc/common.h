@@ -198,6 +198,12 @@ struct SeqTable {
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
 }
+// the same with the non-temporal hint (nt): for data read exactly once, such
+// as streamed weights, so that it does not displace reused lines from the
+// caches
+__device__ __forceinline__ void dma16_nt(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 2);
+}
 
 // context length of sequence s: the host value, or the device one clamped to
 // the buffer (a length past max_ctx would put the block's rows out of it)

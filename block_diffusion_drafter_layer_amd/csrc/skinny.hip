@@ -829,7 +829,7 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
       vc8 = vc8 < n_vcols ? vc8 : ((n_vcols - 1) >> 3) << 3;
       int r8 = ((2 * q) & 7) + hi;
       r8 = vc8 + r8 < n_vcols ? r8 : n_vcols - 1 - vc8;  // ragged last group
-      dma16(Epi::wrow8(ep, vc8, r8) + kk + ((pos ^ r) << 3), slot + q * 1024);
+      dma16_nt(Epi::wrow8(ep, vc8, r8) + kk + ((pos ^ r) << 3), slot + q * 1024);
     }
   };
   // the weight stream starts before the activations are in place
