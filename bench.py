@@ -123,6 +123,112 @@ def summarize_pmc(fetch_db, write_db, copy_fetch_db, copy_write_db, pattern, sou
         f.write(f"source: {os.path.relpath(source, ROOT)}\nsource_sha256: {_sha256(source)}\n")
 
 
+def _pmc_all(db, pattern):
+    """{counter: (mean per dispatch, dispatches)} of the kernels matching
+    pattern. A counter arrives as one row per hardware instance (XCC, shader
+    engine); per dispatch they are summed, except GRBM_GUI_ACTIVE (active
+    cycles, the same clock on every instance), of which the maximum is taken."""
+    import re
+    import sqlite3
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, name, counter_name, counter_value from pmc_events").fetchall()
+    per = {}
+    for did, n, cn, v in rows:
+        if re.search(pattern, n):
+            key = (did, cn)
+            if cn == "GRBM_GUI_ACTIVE":
+                per[key] = max(per.get(key, 0.0), v)
+            else:
+                per[key] = per.get(key, 0.0) + v
+    acc = {}
+    for (did, cn), v in per.items():
+        acc.setdefault(cn, []).append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_mfma(counts_db, util_db, trace_db, out, cmds, kernels):
+    """MFMA utilisation of the context GEMMs from counter runs: per dispatch,
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = bf16 MFMA FLOPs executed,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, and rocprofv3's derived
+    MfmaUtil (busy cycles over active cycles x SIMDs); the average duration of
+    the same kernels from a kernel-trace run of the same command gives the
+    FLOP rate against the 2.5 PFLOP/s bf16 peak."""
+    import re
+    import sqlite3
+    tr = sqlite3.connect(trace_db).execute(
+        "select name, avg(end-start), count(*) from kernels group by name").fetchall()
+    with open(out, "w") as f:
+        f.write("# MFMA utilisation of the context GEMMs from rocprofv3 counters\n")
+        for c in cmds:
+            f.write(f"# command: {c}\n")
+        f.write("# per dispatch means; flops_counter = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512;\n"
+                "# tflops_counter = flops_counter / avg_us (trace run); frac = / 2500 TFLOP/s\n")
+        for label, pattern, alg_flops in kernels:
+            cnt = _pmc_all(counts_db, pattern)
+            ut = _pmc_all(util_db, pattern)
+            durs = [(av, n) for name, av, n in tr if re.search(pattern, name)]
+            avg_ns = sum(a * n for a, n in durs) / max(1, sum(n for _, n in durs))
+            mops = cnt.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", (0.0, 0))[0]
+            fl = mops * 512.0
+            f.write(f"\n[{label}] kernel_pattern: {pattern}\n")
+            for k in sorted(cnt):
+                f.write(f"  {k}: {cnt[k][0]:.6g} (n={cnt[k][1]})\n")
+            for k in sorted(ut):
+                f.write(f"  {k}: {ut[k][0]:.6g} (n={ut[k][1]})\n")
+            f.write(f"  avg_us (trace): {avg_ns / 1e3:.2f}\n")
+            busy = cnt.get("SQ_VALU_MFMA_BUSY_CYCLES", (0.0, 0))[0]
+            act = cnt.get("GRBM_GUI_ACTIVE", (0.0, 0))[0]
+            if act:
+                f.write(f"  mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs): "
+                        f"{busy / (act * 1024):.4f}\n")
+                if avg_ns:
+                    f.write(f"  clock_GHz = GRBM_GUI_ACTIVE / avg duration: {act / avg_ns:.3f}\n")
+            f.write(f"  flops_counter: {fl:.6g}  flops_algorithmic: {alg_flops:.6g}  "
+                    f"ratio: {fl / alg_flops:.4f}\n")
+            if avg_ns:
+                tf = fl / (avg_ns * 1e-9) / 1e12
+                f.write(f"  tflops_counter: {tf:.1f}  frac_of_peak_counter: {tf / MFMA_BF16_PEAK_TFLOPS:.4f}\n")
+                ta = alg_flops / (avg_ns * 1e-9) / 1e12
+                f.write(f"  tflops_timed_algorithmic: {ta:.1f}  frac_of_peak_timed: {ta / MFMA_BF16_PEAK_TFLOPS:.4f}\n")
+
+
+def summarize_traffic(fetch_db, write_db, copy_fetch_db, copy_write_db, out, cmds,
+                      copy_bytes=1 << 30):
+    """HBM traffic per dispatch of every library kernel: FETCH_SIZE and
+    WRITE_SIZE (KiB) scaled by what they read for the plain device copy of
+    copy_bytes read + copy_bytes written."""
+    import re
+    import sqlite3
+    cf, _ = _pmc(copy_fetch_db, "FETCH_SIZE", r"copy_bytes")
+    cw, _ = _pmc(copy_write_db, "WRITE_SIZE", r"copy_bytes")
+    fs, ws = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+
+    def per_kernel(db, counter):
+        rows = sqlite3.connect(db).execute(
+            "select name, counter_value from pmc_events where counter_name = ?", (counter,)).fetchall()
+        acc = {}
+        for n, v in rows:
+            if "dfl::" in n and "copy_bytes" not in n:
+                k = re.sub(r"\(.*", "", n.replace("(anonymous namespace)::", ""))
+                k = re.sub(r"^void ", "", k)
+                acc.setdefault(k, []).append(v)
+        return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+    fk, wk = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
+    with open(out, "w") as f:
+        f.write("# HBM traffic per dispatch of the library's kernels, from rocprofv3 counters\n"
+                "# (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, scaled by what the same counters read\n"
+                "#  for the library's plain device copy of 1 GiB read + 1 GiB written)\n")
+        for c in cmds:
+            f.write(f"# command: {c}\n")
+        f.write(f"fetch_scale: {fs:.4f}\nwrite_scale: {ws:.4f}\n")
+        f.write(f"# {'kernel':<70s} {'dispatches':>10s} {'fetch_MB':>9s} {'write_MB':>9s}\n")
+        for k in sorted(fk, key=lambda k: -fk[k][0]):
+            fmb = fk[k][0] * 1024.0 * fs / 1e6
+            wmb = wk.get(k, (0.0, 0))[0] * 1024.0 * ws / 1e6
+            f.write(f"{k[:70]:<72s} {fk[k][1]:10d} {fmb:9.2f} {wmb:9.2f}\n")
+
+
 def stage_bytes(dc, M):
     """Algorithmic HBM bytes of one launch per stage (weights + activations)."""
     D, F, V = dc.hidden, dc.ffn, dc.vocab
@@ -183,15 +289,8 @@ def draft_flops(dc, rows, ctx_total):
     return 2.0 * rows * L * per_layer + 2.0 * (rows // dc.block_size) * g * V * D + L * attn
 
 
-def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
-    """The other workloads' timed units (one GPU): the 32-sequence ragged
-    batch (one draft call, 512 rows), the D=2048 block-8 drafter (draft,
-    prefill fuse/inject, p/q verify) and the 8192-token context over 4
-    trim/append rounds. Each against its binding roof."""
-    import numpy as np
-    out = {}
-
-    # D=2048, block 8, p/q verification at temperature 1
+def wl_d2048(reps, torch, synth, B, Drafter, config_from, dev):
+    """The D=2048 block-8 drafter: draft, prefill fuse/inject, p/q verify."""
     dc = synth.CONFIGS[4]
     w = synth.make_weights(dc, device=dev)
     d = Drafter(config_from(dc), w, max_seqs=1, max_tokens=dc.ctx_len, device=dev)
@@ -213,7 +312,7 @@ def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
     t_roof, bound = roof(draft_block_bytes(dc, T), draft_flops(dc, dc.block_size, T + dc.block_size))
     f_fl = 2.0 * T * dc.n_feat * dc.hidden * dc.hidden
     i_fl = 2.0 * T * dc.hidden * 2 * dc.kv_dim * dc.n_layers
-    out[dc.name] = {
+    out = {
         "draft_block_us": round(dr[0], 1), "draft_block_us_p10_p90": [round(dr[1], 1), round(dr[2], 1)],
         "blocks_per_s": round(1e6 / dr[0], 1), "draft_roofline": {"bound": bound, "frac": round(t_roof / dr[0], 4)},
         "prefill_fuse_us": round(fu[0], 1), "prefill_fuse_mfma_frac": round(f_fl / (fu[0] * 1e6) / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -223,10 +322,14 @@ def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
     d.close()
     del w, d, kv, feats, ctx, tl, dlog
     torch.cuda.empty_cache()
+    return dc.name, out
 
-    # 32 sequences, ragged contexts uniform in [512, 4096], one draft call
+
+def wl_32seq(reps, torch, synth, B, Drafter, config_from, dev, w=None):
+    """32 sequences, ragged contexts uniform in [512, 4096], one draft call."""
+    import numpy as np
     dc = synth.CONFIGS[3]
-    w = synth.make_weights(dc, device=dev)
+    w = synth.make_weights(dc, device=dev) if w is None else w
     n = dc.n_seqs
     lens = [int(x) for x in synth.gen.ragged_lengths(n)]
     d = Drafter(config_from(dc), w, max_seqs=n, max_tokens=n * dc.block_size, device=dev)
@@ -243,18 +346,25 @@ def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
     kv_bytes = sum(dc.n_layers * 2 * (S + dc.block_size) * dc.kv_dim * 2 for S in lens)
     nbytes = draft_block_bytes(dc, 0) + kv_bytes
     t_roof, bound = roof(nbytes, draft_flops(dc, n * dc.block_size, sum(lens) + n * dc.block_size))
-    out[dc.name] = {"draft_block_us": round(dr[0], 1),
-                    "draft_block_us_p10_p90": [round(dr[1], 1), round(dr[2], 1)],
-                    "blocks_per_s": round(n * 1e6 / dr[0], 1),
-                    "draft_roofline": {"bound": bound, "frac": round(t_roof / dr[0], 4)},
-                    "context_lengths": "32 uniform in [512, 4096], mean %d" % int(np.mean(lens))}
+    out = {"draft_block_us": round(dr[0], 1),
+           "draft_block_us_p10_p90": [round(dr[1], 1), round(dr[2], 1)],
+           "blocks_per_s": round(n * 1e6 / dr[0], 1),
+           "draft_roofline": {"bound": bound, "frac": round(t_roof / dr[0], 4)},
+           "context_lengths": "32 uniform in [512, 4096], mean %d" % int(np.mean(lens))}
     d.close()
     del d, kvs
     torch.cuda.empty_cache()
+    return dc.name, out, w
 
-    # 8192-token context, 4 host-driven rounds of draft, verify, trim, append
+
+def wl_ctx8192(reps, torch, synth, B, Drafter, config_from, dev, w=None):
+    """The 8192-token context: prefill fuse, then 4 host-driven rounds of
+    draft, verify, trim and append."""
+    import numpy as np
     dc = synth.CONFIGS[2]
-    w2 = w  # same shapes as the 32-sequence drafter; the timing does not depend on the values
+    # the timing does not depend on the values: the Qwen-shaped weights of
+    # another workload serve when given
+    w2 = synth.make_weights(dc, device=dev) if w is None else w
     S0, Bs = dc.ctx_len, dc.block_size
     d = Drafter(config_from(dc), w2, max_seqs=1, max_tokens=S0, device=dev)
     kv = d.new_kv(S0 + Bs * (dc.rounds + 1))
@@ -291,14 +401,56 @@ def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
         rounds_us.append(e[0].elapsed_time(e[1]) * 1e3 + e[2].elapsed_time(e3) * 1e3)
         anchors = b_.to(torch.int32)
     t_roof, bound = roof(draft_block_bytes(dc, S0 + Bs), draft_flops(dc, Bs, S0 + 2 * Bs))
-    out[dc.name] = {"prefill_fuse_us_T8192": round(fu[0], 1),
-                    "prefill_fuse_mfma_frac": round(2.0 * S0 * dc.n_feat * dc.hidden ** 2 / (fu[0] * 1e6)
-                                                    / MFMA_BF16_PEAK_TFLOPS, 4),
-                    "round_us": [round(x, 1) for x in rounds_us],
-                    "draft_block_us": [round(x, 1) for x in drafts_us],
-                    "draft_roofline": {"bound": bound, "frac": round(t_roof / float(np.median(drafts_us)), 4)},
-                    "final_context": kv.len}
+    out = {"prefill_fuse_us_T8192": round(fu[0], 1),
+           "prefill_fuse_mfma_frac": round(2.0 * S0 * dc.n_feat * dc.hidden ** 2 / (fu[0] * 1e6)
+                                           / MFMA_BF16_PEAK_TFLOPS, 4),
+           "round_us": [round(x, 1) for x in rounds_us],
+           "draft_block_us": [round(x, 1) for x in drafts_us],
+           "draft_roofline": {"bound": bound, "frac": round(t_roof / float(np.median(drafts_us)), 4)},
+           "final_context": kv.len}
     d.close()
+    del d, kv
+    torch.cuda.empty_cache()
+    return dc.name, out
+
+
+def other_workloads(reps, torch, synth, B, Drafter, config_from, dev):
+    """The other workloads' timed units (one GPU): the 32-sequence ragged
+    batch (one draft call, 512 rows), the D=2048 block-8 drafter (draft,
+    prefill fuse/inject, p/q verify) and the 8192-token context over 4
+    trim/append rounds. Each against its binding roof."""
+    out = {}
+    name, r = wl_d2048(reps, torch, synth, B, Drafter, config_from, dev)
+    out[name] = r
+    name, r, w = wl_32seq(reps, torch, synth, B, Drafter, config_from, dev)
+    out[name] = r
+    name, r = wl_ctx8192(reps, torch, synth, B, Drafter, config_from, dev, w=w)
+    out[name] = r
+    return out
+
+
+def prefill_only(torch, synth, Drafter, config_from, dev, reps=3):
+    """Only the context GEMMs: fuse and inject of a 2048-token context at the
+    Qwen shape (for hardware-counter runs)."""
+    out = {}
+    for dc in (synth.CONFIGS[1],):
+        w = synth.make_weights(dc, device=dev)
+        d = Drafter(config_from(dc), w, max_seqs=1, max_tokens=dc.ctx_len, device=dev)
+        kv = d.new_kv(dc.ctx_len + 64)
+        feats = synth.make_feats(dc, dc.ctx_len, device=dev)
+        ctx = d.fuse_context(feats)
+        fu = _ev_time(lambda: d.fuse_context(feats, out=ctx), reps, torch)
+        inj = _ev_time(lambda: d.inject_kv(kv, ctx, 0), reps, torch)
+        T = dc.ctx_len
+        f_fl = 2.0 * T * dc.n_feat * dc.hidden * dc.hidden
+        i_fl = 2.0 * T * dc.hidden * 2 * dc.kv_dim * dc.n_layers
+        out[dc.name] = {"fuse_us": round(fu[0], 1), "fuse_flops": f_fl,
+                        "fuse_mfma_frac": round(f_fl / (fu[0] * 1e6) / MFMA_BF16_PEAK_TFLOPS, 4),
+                        "inject_us": round(inj[0], 1), "inject_flops": i_fl,
+                        "inject_mfma_frac": round(i_fl / (inj[0] * 1e6) / MFMA_BF16_PEAK_TFLOPS, 4)}
+        d.close()
+        del w, d, kv, feats, ctx
+        torch.cuda.empty_cache()
     return out
 
 
@@ -331,7 +483,18 @@ def cpu_baseline(dc, w, feats_np, ctx_cache_fn, planted, budget_s=30.0):
         el = time.perf_counter() - t0
         if el > budget_s or (rounds >= 3 and el > budget_s / 3):
             break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": rounds / el, "unit": "blocks/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model,
+            "oracle": "numpy fp64 (matrix products by the BLAS numpy links, on the threads above)",
             "sample": f"{rounds} full speculative round(s) of the numpy fp64 oracle at the "
                       f"same workload (draft forward at ctx {cache.len}, greedy verify, "
                       f"fuse+inject of the accepted rows), {el:.1f} s"}
@@ -349,8 +512,18 @@ def main():
                     help="also time every stage once after the timed region")
     ap.add_argument("--copy-reference", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--only", choices=["d2048_b8_ctx2048_pq", "qwen3_8b_shape_b16_32seq_ragged",
+                                       "qwen3_8b_shape_b16_ctx8192_4rounds", "prefill"],
+                    help="time only this workload (or only the context GEMMs) and print its "
+                         "figures; for profiler runs")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB", "OUT", "CMD"),
                     help="write a text summary of a rocprofv3 kernel-trace database")
+    ap.add_argument("--summarize-mfma", nargs=5, metavar=("COUNTS_DB", "UTIL_DB", "TRACE_DB", "OUT", "CMDS"),
+                    help="write the MFMA utilisation summary of the context GEMMs of a "
+                         "--only prefill run (CMDS: the commands joined by ' ;; ')")
+    ap.add_argument("--summarize-traffic", nargs=6,
+                    metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "OUT", "CMDS"),
+                    help="write the per-kernel HBM traffic summary of four counter runs")
     ap.add_argument("--summarize-pmc", nargs=8,
                     metavar=("FETCH_DB", "WRITE_DB", "COPY_FETCH_DB", "COPY_WRITE_DB", "PATTERN",
                              "SOURCE", "OUT", "CMDS"),
@@ -359,6 +532,20 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_traffic:
+        a = args.summarize_traffic
+        summarize_traffic(a[0], a[1], a[2], a[3], a[4], a[5].split(" ;; "))
+        return
+    if args.summarize_mfma:
+        a = args.summarize_mfma
+        f_fl = 2.0 * 2048 * 5 * 4096 * 4096
+        i_fl = 2.0 * 2048 * 4096 * 2 * 1024 * 5
+        ks = [("fuse, qwen3_8b_shape_b16_ctx2048 (T=2048, K=5D=20480, N=4096)",
+               r"ctx_gemm<256, dfl::EpiFuse>", f_fl),
+              ("inject, qwen3_8b_shape_b16_ctx2048 (T=2048, K=4096, N=5 layers x 2048)",
+               r"ctx_gemm<320, dfl::EpiInject>", i_fl)]
+        summarize_mfma(a[0], a[1], a[2], a[3], a[4].split(" ;; "), ks)
         return
     if args.summarize_pmc:
         a = args.summarize_pmc
@@ -392,6 +579,19 @@ def main():
         assert bool(torch.equal(dst, src))
         print(json.dumps({"copy_reference_bytes_read": n, "copy_reference_bytes_written": n,
                           "copies": 3}), flush=True)
+        return
+    if args.only:
+        print(f"[bench] only {args.only}", file=sys.stderr, flush=True)
+        if args.only == "prefill":
+            res = prefill_only(torch, synth, Drafter, config_from, dev)
+        elif args.only == "d2048_b8_ctx2048_pq":
+            res = dict([wl_d2048(args.steps, torch, synth, B, Drafter, config_from, dev)])
+        elif args.only == "qwen3_8b_shape_b16_32seq_ragged":
+            name, r, _ = wl_32seq(args.steps, torch, synth, B, Drafter, config_from, dev)
+            res = {name: r}
+        else:
+            res = dict([wl_ctx8192(args.steps, torch, synth, B, Drafter, config_from, dev)])
+        print(json.dumps({"only": args.only, **res}), flush=True)
         return
     dc = synth.CONFIGS[1]
     S0, Bsz = dc.ctx_len, dc.block_size
@@ -576,6 +776,41 @@ def main():
     B.dflash_copy_bytes(dst.data_ptr(), src.data_ptr(), nb, cst)
     cp = _ev_time(lambda: B.dflash_copy_bytes(dst.data_ptr(), src.data_ptr(), nb, cst), 5, torch)
     copy_gbs = 2.0 * nb / (cp[0] * 1e3)
+
+    # the read ceiling of the weight streams' access pattern (the library's
+    # read reference, nothing computed) on the LM head's weights, each time
+    # after 1 GiB of other data was read (so the memory-side cache holds none
+    # of it)
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    lm = w["lm_head"]
+    lm_bytes = lm.numel() * 2 // (128 * 1024) * (128 * 1024)
+
+    def flush():
+        B.dflash_read_bytes(src.data_ptr(), nb, sink.data_ptr(), cst)
+
+    rd = []
+    for _ in range(5):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        B.dflash_read_bytes(lm.data_ptr(), lm_bytes, sink.data_ptr(), cst)
+        e1.record()
+        torch.cuda.synchronize()
+        rd.append(e0.elapsed_time(e1) * 1e3)
+    read_gbs = lm_bytes / (float(np.median(rd)) * 1e3)
+
+    # the draft with a cold memory-side cache: 1 GiB of other data read
+    # before each timed draft
+    cold = []
+    for j in range(max(5, args.steps // 2)):
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        d.draft_block_dev([kv], len_dev, anchors, blk_out)
+        e1.record()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    draft_cold = (float(np.median(cold)), float(np.percentile(cold, 10)), float(np.percentile(cold, 90)))
     del src, dst
 
     # DFlash 2 candidate selector on the headline block (top-16, rank 256):
@@ -666,6 +901,11 @@ def main():
         "draft_block_hbm_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "draft_block_copy_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / copy_gbs, 4),
         "copy_peak_GBs": round(copy_gbs, 1),
+        "read_ceiling_GBs": round(read_gbs, 1),
+        "draft_block_read_ceiling_frac": round(dbytes / (draft_us * 1e-6) / 1e9 / read_gbs, 4),
+        "draft_block_cold_us": round(draft_cold[0], 1),
+        "draft_block_cold_us_p10_p90": [round(draft_cold[1], 1), round(draft_cold[2], 1)],
+        "draft_block_cold_hbm_frac": round(dbytes / (draft_cold[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         # the pages' per-token latency L = (T_draft + T_verify) / tau, with
         # this path's side only: the target's verify forward is not part of it
         "round_us_per_accepted_token": round(ms_per_step * 1e3 / max(dev_tau / args.steps, 1e-9), 1),

@@ -110,6 +110,7 @@ def _load():
         "dflash_profile_read": (C.c_int, [P, I32, C.POINTER(I32), C.POINTER(F32), C.POINTER(I32)]),
         "dflash_stage_name": (C.c_char_p, [I32]),
         "dflash_copy_bytes": (C.c_int, [P, P, SZ, P]),
+        "dflash_read_bytes": (C.c_int, [P, SZ, P, P]),
         "dflash_status_str": (C.c_char_p, [C.c_int]),
         "dflash_last_error": (C.c_char_p, []),
     }
@@ -282,6 +283,10 @@ STAGES = ("embed", "qkv", "attention", "o_proj", "gate_up", "down_proj", "lm_hea
 
 def dflash_copy_bytes(dst: int, src: int, nbytes: int, stream: int = 0):
     return _check(_lib.dflash_copy_bytes(C.c_void_p(dst), C.c_void_p(src), nbytes, C.c_void_p(stream)))
+
+
+def dflash_read_bytes(src: int, nbytes: int, sink: int, stream: int = 0):
+    return _check(_lib.dflash_read_bytes(C.c_void_p(src), nbytes, C.c_void_p(sink), C.c_void_p(stream)))
 
 
 def dflash_profile_enable(h, stage_mask: int, max_records: int = 0):

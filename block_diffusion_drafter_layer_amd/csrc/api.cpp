@@ -235,6 +235,15 @@ dflash_status dflash_copy_bytes(void* dst, const void* src, size_t bytes, void* 
   return e == hipSuccess ? DFLASH_OK : dev_fail(e, "copy");
 }
 
+dflash_status dflash_read_bytes(const void* src, size_t bytes, void* sink, void* stream) {
+  if (!bytes) return DFLASH_OK;
+  if (!src || !sink) return fail(DFLASH_E_NULL, "read: null pointer");
+  if (((uintptr_t)src & 15) || ((uintptr_t)sink & 3) || bytes % (128 * 1024))
+    return fail(DFLASH_E_ALIGN, "read: src 16-byte aligned, sink 4-byte aligned, size a multiple of 128 KiB");
+  hipError_t e = launch_read_bytes(src, bytes, (uint32_t*)sink, (hipStream_t)stream);
+  return e == hipSuccess ? DFLASH_OK : dev_fail(e, "read");
+}
+
 const char* dflash_stage_name(int32_t stage) {
   return stage >= 0 && stage < ST_COUNT ? kStageNames[stage] : "unknown";
 }

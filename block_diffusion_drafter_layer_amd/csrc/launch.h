@@ -236,5 +236,8 @@ hipError_t launch_conv_finish(const ConvLaunch& C, hipStream_t st);
 
 // reference copy for byte-counter calibration (16-byte aligned, bytes % 16 == 0)
 hipError_t launch_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t st);
+// read-ceiling reference: reads bytes (a multiple of 128 KiB, 16-byte
+// aligned) in the weight streams' access pattern; sink: >= 256 words
+hipError_t launch_read_bytes(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace dfl

@@ -483,6 +483,19 @@ const char* dflash_stage_name(int32_t stage);
  */
 dflash_status dflash_copy_bytes(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * Measurement reference, not part of the drafting method: read `bytes` of
+ * device memory src on `stream` with the access pattern of the weight
+ * streams (512-byte pieces of 16 rows of 8 KB, direct global-to-LDS loads
+ * with the non-temporal hint, one workgroup per CU), computing nothing; its
+ * rate is the read ceiling those kernels can reach. sink: device memory of at
+ * least 256 32-bit words, written only in a case that cannot occur (so the
+ * loads are not removed). src 16-byte aligned, sink 4-byte aligned, bytes a
+ * multiple of 128 KiB, else DFLASH_E_ALIGN; null pointers with bytes > 0
+ * give DFLASH_E_NULL. Nothing is allocated.
+ */
+dflash_status dflash_read_bytes(const void* src, size_t bytes, void* sink, void* stream);
+
 const char* dflash_status_str(dflash_status s);
 const char* dflash_last_error(void);
 
