@@ -254,7 +254,8 @@ def block_attention(q, k, v):
 # ----------------------------------------------------------------------------
 
 def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
-                anchors: Sequence[int], block_len: Optional[int] = None):
+                anchors: Sequence[int], block_len: Optional[int] = None,
+                conv: Optional[Dict] = None):
     """One parallel forward of the drafter over [anchor, mask x (block_len-1)].
 
     [Code] section 6 (block = last confirmed token + block_size-1 mask tokens,
@@ -267,7 +268,19 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
 
     caches[s] holds sequence s's context K/V; its length S_s is the anchor's
     position. The block's own K/V rows exist only inside this forward and
-    keep full precision. Returns a dict with
+    keep full precision.
+
+    conv (optional): the DFlash 2 grouped dynamic two-tap convs of every
+    layer ([Code] section 13: short-range in-block mixing that takes over
+    from block attention; section 14: one instance by attention and one by
+    the MLP, base_kernel[0] for the "prepare" call and base_kernel[1] for the
+    "finish" call). {"group_size": g, "layers": [{"attn_base", "attn_proj",
+    "mlp_base", "mlp_proj"} per layer]}. Reading of where the calls sit (the
+    pages do not say): prepare on the sublayer's normed input, whose
+    projection also yields the finish call's corrections, finish on the
+    sublayer's output before the residual add; the module carries no state
+    across steps, so the block's first row reads a zero row as its
+    predecessor. Returns a dict with
       draft  [n_seq, block_len-1] int   argmax tokens of rows 1..block_len-1
       hidden [L, n_seq, block_len, D]   residual stream after each layer
       logits [n_seq, block_len-1, V]
@@ -288,8 +301,13 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
         ids = [int(anchors[s])] + [cfg.mask_token_id] * (B - 1)
         x = np.asarray(embed[ids], dtype=F64)            # [B, D]
         pos = np.arange(S, S + B)
+        zero = np.zeros((1, D), dtype=F64)
         for i, lw in enumerate(weights["layers"]):
+            cw = conv["layers"][i] if conv is not None else None
             h = rms_norm(x, lw["attn_norm"], eps)
+            if cw is not None:
+                h, corr_a = dynamic_conv_prepare(h, zero, B, cw["attn_base"], cw["attn_proj"],
+                                                 conv["group_size"])
             q = linear(h, lw["wq"]).reshape(B, Hq, hd)
             kb = linear(h, lw["wk"]).reshape(B, Hkv, hd)
             vb = linear(h, lw["wv"]).reshape(B, Hkv, hd)
@@ -301,10 +319,18 @@ def draft_block(cfg, weights: Dict, caches: Sequence[DraftCache],
             else:
                 k_all, v_all = kb, vb
             o = block_attention(q, k_all, v_all).reshape(B, Hq * hd)
-            x = x + linear(o, lw["wo"])
+            a = linear(o, lw["wo"])
+            if cw is not None:
+                a = dynamic_conv_finish(a, zero, B, cw["attn_base"], corr_a, conv["group_size"])
+            x = x + a
             h2 = rms_norm(x, lw["mlp_norm"], eps)
-            x = x + linear(silu(linear(h2, lw["w_gate"])) * linear(h2, lw["w_up"]),
-                           lw["w_down"])
+            if cw is not None:
+                h2, corr_m = dynamic_conv_prepare(h2, zero, B, cw["mlp_base"], cw["mlp_proj"],
+                                                  conv["group_size"])
+            m = linear(silu(linear(h2, lw["w_gate"])) * linear(h2, lw["w_up"]), lw["w_down"])
+            if cw is not None:
+                m = dynamic_conv_finish(m, zero, B, cw["mlp_base"], corr_m, conv["group_size"])
+            x = x + m
             hidden[i, s] = x
         if B > 1:
             z = rms_norm(x[1:], weights["final_norm"], eps)

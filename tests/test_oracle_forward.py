@@ -155,3 +155,123 @@ def test_context_changes_every_block_row():
     cv2 = [v.copy() for v in cv]; cv2[0][3] += 1.0
     alt = O.draft_block(cfg, w, [O.DraftCache(cfg.n_layers, k=ck, v=cv2)], [7])["hidden"][0, 0]
     assert (np.abs(alt - base).max(axis=-1) > 1e-6).all()
+
+
+# ---------------------------------------------------------------------------
+# the DFlash 2 conv inside every layer
+# ---------------------------------------------------------------------------
+
+def _conv_weights(cfg, seed, gs=16, identity=False):
+    r = np.random.default_rng(seed)
+    D, G = cfg.hidden, cfg.hidden // gs
+    layers = []
+    for _ in range(cfg.n_layers):
+        lw = {}
+        for inst in ("attn", "mlp"):
+            if identity:
+                base = np.zeros((2, 2, D))
+                base[:, 0, :] = 1.0          # tap 0 passes x_t, tap 1 drops x_{t-1}
+                proj = np.zeros((4 * G, D))
+            else:
+                base = 0.5 * r.standard_normal((2, 2, D))
+                proj = r.standard_normal((4 * G, D)) / np.sqrt(D)
+            lw[inst + "_base"], lw[inst + "_proj"] = base, proj
+        layers.append(lw)
+    return {"group_size": gs, "layers": layers}
+
+
+def _brute_conv(rows, h, base_call, proj, call, gs):
+    """y_t = k_{t,0} x_t + k_{t,1} x_{t-1} with element loops: k_{t,j} of
+    channel c = base_call[j][c] + (proj row (call, j, c // gs)) . h_t; the
+    block's first row reads a zero row."""
+    T, D = len(rows), len(rows[0])
+    G = D // gs
+    out = []
+    for t in range(T):
+        y = []
+        for c in range(D):
+            g = c // gs
+            k = []
+            for j in range(2):
+                row = proj[call * 2 * G + j * G + g]
+                k.append(base_call[j][c] + sum(float(row[e]) * float(h[t][e]) for e in range(D)))
+            before = float(rows[t - 1][c]) if t > 0 else 0.0
+            y.append(k[0] * float(rows[t][c]) + k[1] * before)
+        out.append(y)
+    return torch.tensor(out, dtype=torch.float64)
+
+
+def _torch_forward_conv(cfg, w, ctx_k, ctx_v, anchor, S, conv):
+    """_torch_forward with the reading's conv placement, the conv by element loops."""
+    t = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.float64)  # noqa: E731
+    B, Hq, Hkv, hd = cfg.block_size, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    gs = conv["group_size"]
+    ids = torch.tensor([anchor] + [cfg.mask_token_id] * (B - 1))
+    x = t(w["embed"])[ids]
+    pos = torch.arange(S, S + B)
+    hs = []
+    for i, lw in enumerate(w["layers"]):
+        cw = conv["layers"][i]
+        h = F.rms_norm(x, (cfg.hidden,), t(lw["attn_norm"]), cfg.rms_eps)
+        hp = _brute_conv(h.tolist(), h.tolist(), cw["attn_base"][0], cw["attn_proj"], 0, gs)
+        q = _torch_rope((hp @ t(lw["wq"]).T).view(B, Hq, hd), pos, cfg.rope_theta)
+        kb = _torch_rope((hp @ t(lw["wk"]).T).view(B, Hkv, hd), pos, cfg.rope_theta)
+        vb = (hp @ t(lw["wv"]).T).view(B, Hkv, hd)
+        k = torch.cat([t(ctx_k[i]), kb]) if S else kb
+        v = torch.cat([t(ctx_v[i]), vb]) if S else vb
+        G = Hq // Hkv
+        kk = k.transpose(0, 1).repeat_interleave(G, dim=0)
+        vv = v.transpose(0, 1).repeat_interleave(G, dim=0)
+        o = F.scaled_dot_product_attention(q.transpose(0, 1), kk, vv)
+        a = o.transpose(0, 1).reshape(B, Hq * hd) @ t(lw["wo"]).T
+        a = _brute_conv(a.tolist(), h.tolist(), cw["attn_base"][1], cw["attn_proj"], 1, gs)
+        x = x + a
+        h2 = F.rms_norm(x, (cfg.hidden,), t(lw["mlp_norm"]), cfg.rms_eps)
+        h2p = _brute_conv(h2.tolist(), h2.tolist(), cw["mlp_base"][0], cw["mlp_proj"], 0, gs)
+        m = (F.silu(h2p @ t(lw["w_gate"]).T) * (h2p @ t(lw["w_up"]).T)) @ t(lw["w_down"]).T
+        m = _brute_conv(m.tolist(), h2.tolist(), cw["mlp_base"][1], cw["mlp_proj"], 1, gs)
+        x = x + m
+        hs.append(x.clone())
+    return torch.stack(hs).numpy()
+
+
+def test_conv_identity_kernels_give_the_plain_forward():
+    # base taps (1, 0) for both calls and a zero projection: every conv is the
+    # identity, so the forward equals the one without convs bit for bit
+    cfg = CONFIGS[0].shrink(n_layers=2)
+    w, ck, cv, cache = _setup(cfg, 10)
+    anchor = int(synth.make_anchor(cfg)[0])
+    plain = O.draft_block(cfg, w, [cache], [anchor])
+    ident = O.draft_block(cfg, w, [cache], [anchor], conv=_conv_weights(cfg, 0, identity=True))
+    np.testing.assert_array_equal(plain["hidden"], ident["hidden"])
+    np.testing.assert_array_equal(plain["logits"], ident["logits"])
+
+
+def test_conv_forward_matches_element_by_element_brute_force():
+    cfg = CONFIGS[0].shrink(n_layers=2)
+    w, ck, cv, cache = _setup(cfg, 10)
+    anchor = int(synth.make_anchor(cfg)[0])
+    conv = _conv_weights(cfg, 3)
+    out = O.draft_block(cfg, w, [cache], [anchor], conv=conv)
+    hs = _torch_forward_conv(cfg, w, ck, cv, anchor, 10, conv)
+    np.testing.assert_allclose(out["hidden"][:, 0], hs, rtol=1e-9, atol=1e-11)
+    plain = O.draft_block(cfg, w, [cache], [anchor])
+    assert np.abs(plain["hidden"] - out["hidden"]).max() > 1e-2
+
+
+def test_conv_instances_are_not_interchangeable():
+    # the attention instance and the MLP instance act at different places:
+    # swapping their weights moves the result
+    cfg = CONFIGS[0].shrink(n_layers=1)
+    w, ck, cv, cache = _setup(cfg, 10)
+    anchor = int(synth.make_anchor(cfg)[0])
+    conv = _conv_weights(cfg, 5)
+    ref = _torch_forward_conv(cfg, w, ck, cv, anchor, 10, conv)
+    out = O.draft_block(cfg, w, [cache], [anchor], conv=conv)
+    np.testing.assert_allclose(out["hidden"][:, 0], ref, rtol=1e-9, atol=1e-11)
+    # swapping the two instances' weights moves the result
+    swapped = {"group_size": 16, "layers": [{"attn_base": l["mlp_base"], "attn_proj": l["mlp_proj"],
+                                             "mlp_base": l["attn_base"], "mlp_proj": l["attn_proj"]}
+                                            for l in conv["layers"]]}
+    other = O.draft_block(cfg, w, [cache], [anchor], conv=swapped)
+    assert np.abs(other["hidden"] - out["hidden"]).max() > 1e-3
