@@ -868,6 +868,16 @@ def main():
             "prepare_hbm_frac": round(conv_p_bytes / (cp_t[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "per_draft_over_draft": round(2 * dc.n_layers * (cp_t[0] + cf_t[0]) / draft_e, 4)}
     del cv, c_y, c_y2, c_corr
+    # the draft with the convs inside every layer (two instances, both calls)
+    cl = synth.make_conv_layers(dc, 16, device=dev)
+    d.set_conv(cl)
+    for _ in range(3):
+        d.draft_block_dev([kv], len_dev, anchors, blk_out)
+    dct = _ev_time(lambda: d.draft_block_dev([kv], len_dev, anchors, blk_out), args.steps, torch)
+    d.set_conv(None)
+    conv["draft_with_convs_us"] = round(dct[0], 1)
+    conv["draft_with_convs_over_draft"] = round(dct[0] / draft_e - 1.0, 4)
+    del cl
 
     ms_per_step = elapsed * 1e3 / args.steps
     value = args.steps / elapsed

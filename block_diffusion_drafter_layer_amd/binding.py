@@ -45,6 +45,11 @@ class dflash_selector(C.Structure):
                 ("succ_codebook", C.c_void_p), ("rank", C.c_int32), ("top_k", C.c_int32)]
 
 
+class dflash_conv_layer(C.Structure):
+    _fields_ = [("attn_base", C.c_void_p), ("attn_proj", C.c_void_p), ("mlp_base", C.c_void_p),
+                ("mlp_proj", C.c_void_p)]
+
+
 class dflash_kv(C.Structure):
     _fields_ = [("base", C.c_void_p), ("max_ctx", C.c_int32), ("len", C.c_int32)]
 
@@ -99,6 +104,7 @@ def _load():
         "dflash_sample_draft": (C.c_int, [P, I32, I32, P, F32, U64, U64, P]),
         "dflash_verify_candidates": (C.c_int, [P, I32, I32, P, P, P, P, I32, F32, U64, U64, P, P]),
         "dflash_set_selector": (C.c_int, [P, C.POINTER(dflash_selector)]),
+        "dflash_set_conv": (C.c_int, [P, C.POINTER(dflash_conv_layer), I32]),
         "dflash_select_block": (C.c_int, [P, I32, I32, P, P, P, F32, U64, U64, P, P, P]),
         "dflash_conv_prepare": (C.c_int, [P, I32, I32, I32, P, P, P, P, P, P]),
         "dflash_conv_finish": (C.c_int, [P, I32, I32, I32, P, P, P, P, P]),
@@ -234,6 +240,15 @@ def dflash_sample_draft(h, n_seqs: int, block_len: int, draft_logits: int, tempe
 def dflash_set_selector(h, sel):
     """sel: a dflash_selector, or None to remove the selector."""
     return _check(_lib.dflash_set_selector(h, C.byref(sel) if sel is not None else None))
+
+
+def dflash_set_conv(h, layers, group_size: int):
+    """layers: a sequence of dflash_conv_layer (one per draft layer), or None
+    to remove the convs."""
+    if layers is None:
+        return _check(_lib.dflash_set_conv(h, None, 0))
+    arr = (dflash_conv_layer * len(layers))(*layers)
+    return _check(_lib.dflash_set_conv(h, arr, group_size))
 
 
 def dflash_select_block(h, n_seqs: int, block_len: int, last_hidden: int, draft_logits: int,

@@ -101,6 +101,7 @@ struct Layout {
   size_t vcdf;                  // verify / sampling draws: merged row statistics and slice sums
   size_t sel_keys, sel_gpart, sel_spart, sel_S, sel_cand;  // candidate selector
   size_t conv_xh, conv_xl;      // the dynamic conv's hi/lo input rows
+  size_t conv_h, conv_y, conv_ah, conv_al, conv_o, conv_corr_a, conv_corr_m;  // convs in the layers
   size_t total;
 };
 
@@ -150,6 +151,13 @@ Layout make_layout(const dflash_config& c, int32_t max_seqs, int32_t max_tokens)
   L.sel_cand = take(sel_rows * kSelMaxK * 4);
   L.conv_xh = take(Mmax * D * 2);
   L.conv_xl = take(Mmax * D * 2);
+  L.conv_h = take(Mmax * D * 4);
+  L.conv_y = take(Mmax * D * 4);
+  L.conv_ah = take(Mmax * D * 2);
+  L.conv_al = take(Mmax * D * 2);
+  L.conv_o = take(Mmax * D * 4);
+  L.conv_corr_a = take(Mmax * 2 * D * 4);  // 2 * D / group_size per row, any group size
+  L.conv_corr_m = take(Mmax * 2 * D * 4);
   L.total = o;
   return L;
 }
@@ -180,6 +188,8 @@ struct dflash_handle {
   int32_t max_seqs = 0, max_tokens = 0;
   Layout lay{};
   dflash_selector sel{};         // candidate selector tables (rank 0: none)
+  std::vector<dflash_conv_layer> conv;  // DFlash 2 convs of every layer (empty: none)
+  int32_t conv_gs = 0;
 };
 
 // Launch `fn` as stage `st`, bracketed by timing events when that stage is
@@ -543,6 +553,13 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   L.att_acc = (float*)(ws + Ly.att_acc); L.att_ml = (float*)(ws + Ly.att_ml);
   L.split = split_ws(h);
   L.gemm = gemm_ws(h);
+  const bool conv = !h->conv.empty();
+  L.conv_gs = conv ? h->conv_gs : 0;
+  L.conv_h = (float*)(ws + Ly.conv_h); L.conv_y = (float*)(ws + Ly.conv_y);
+  L.conv_ah = (bf16_t*)(ws + Ly.conv_ah); L.conv_al = (bf16_t*)(ws + Ly.conv_al);
+  L.conv_xh = (bf16_t*)(ws + Ly.conv_xh); L.conv_xl = (bf16_t*)(ws + Ly.conv_xl);
+  L.conv_o = (float*)(ws + Ly.conv_o);
+  L.conv_corr_a = (float*)(ws + Ly.conv_corr_a); L.conv_corr_m = (float*)(ws + Ly.conv_corr_m);
   // split each sequence's keys so that the grid holds ~1024 waves (one per
   // SIMD) where the context allows, in whole 32-key chunks; each workgroup
   // runs G query-head waves, times 2 key columns when G <= 2
@@ -568,6 +585,56 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   if (e != hipSuccess) return dev_fail(e, "embed");
   for (int i = 0; i < c.n_layers; ++i) {
     const dflash_layer_weights& lw = h->layers[i];
+    const bf16_t* gnext = (const bf16_t*)(i + 1 < c.n_layers ? h->layers[i + 1].attn_norm
+                                                              : h->w.final_norm);
+    float* hid = hidden_out ? hidden_out + (size_t)i * L.M * c.hidden : nullptr;
+    if (conv) {
+      // the layer with its two convs ([Code] sections 13-14): prepare on the
+      // sublayer's normed input, finish on its output before the residual add
+      const dflash_conv_layer& cw = h->conv[i];
+      e = timed(h, ST_CONV, [&] {
+        hipError_t r = launch_norm_rows(L, (const bf16_t*)lw.attn_norm, st);
+        return r != hipSuccess ? r
+                               : launch_conv_prepare_draft(L, (const bf16_t*)cw.attn_base,
+                                                           (const bf16_t*)cw.attn_proj, L.conv_corr_a, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "conv (attention, prepare)");
+      e = timed(h, ST_QKV, [&] {
+        return launch_qkv(L, i, (const bf16_t*)lw.wq, (const bf16_t*)lw.wk, (const bf16_t*)lw.wv, st,
+                          L.conv_ah, L.conv_al);
+      });
+      if (e != hipSuccess) return dev_fail(e, "qkv");
+      e = timed(h, ST_ATTN, [&] { return launch_attention(L, i, st); });
+      if (e != hipSuccess) return dev_fail(e, "attention");
+      e = timed(h, ST_OPROJ, [&] {
+        return launch_store(L, (const bf16_t*)lw.wo, L.ob_h, L.ob_l, c.n_heads * c.head_dim, L.conv_o, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "o_proj");
+      e = timed(h, ST_CONV, [&] {
+        hipError_t r = launch_conv_finish_resid(L, (const bf16_t*)cw.attn_base, L.conv_corr_a,
+                                                (const bf16_t*)lw.mlp_norm, nullptr, st);
+        if (r != hipSuccess) return r;
+        r = launch_norm_rows(L, (const bf16_t*)lw.mlp_norm, st);
+        return r != hipSuccess ? r
+                               : launch_conv_prepare_draft(L, (const bf16_t*)cw.mlp_base,
+                                                           (const bf16_t*)cw.mlp_proj, L.conv_corr_m, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "conv (attention finish, MLP prepare)");
+      e = timed(h, ST_GATEUP, [&] {
+        return launch_swiglu(L, (const bf16_t*)lw.w_gate, (const bf16_t*)lw.w_up, st, L.conv_ah,
+                             L.conv_al);
+      });
+      if (e != hipSuccess) return dev_fail(e, "gate_up");
+      e = timed(h, ST_DOWN, [&] {
+        return launch_store(L, (const bf16_t*)lw.w_down, L.act_h, L.act_l, c.ffn, L.conv_o, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "down_proj");
+      e = timed(h, ST_CONV, [&] {
+        return launch_conv_finish_resid(L, (const bf16_t*)cw.mlp_base, L.conv_corr_m, gnext, hid, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "conv (MLP finish)");
+      continue;
+    }
     e = timed(h, ST_QKV, [&] {
       return launch_qkv(L, i, (const bf16_t*)lw.wq, (const bf16_t*)lw.wk, (const bf16_t*)lw.wv, st);
     });
@@ -583,9 +650,6 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
       return launch_swiglu(L, (const bf16_t*)lw.w_gate, (const bf16_t*)lw.w_up, st);
     });
     if (e != hipSuccess) return dev_fail(e, "gate_up");
-    const bf16_t* gnext = (const bf16_t*)(i + 1 < c.n_layers ? h->layers[i + 1].attn_norm
-                                                              : h->w.final_norm);
-    float* hid = hidden_out ? hidden_out + (size_t)i * L.M * c.hidden : nullptr;
     e = timed(h, ST_DOWN, [&] {
       return launch_resid(L, (const bf16_t*)lw.w_down, L.act_h, L.act_l, c.ffn, gnext, hid, st);
     });
@@ -855,6 +919,30 @@ dflash_status dflash_set_selector(dflash_handle* h, const dflash_selector* sel) 
       !aligned(sel->succ_codebook, 16))
     return fail(DFLASH_E_ALIGN, "selector tables must be 16-byte aligned");
   h->sel = *sel;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_set_conv(dflash_handle* h, const dflash_conv_layer* layers, int32_t group_size) {
+  if (!h) return fail(DFLASH_E_NULL, "handle is required");
+  if (!layers) {
+    h->conv.clear();
+    h->conv_gs = 0;
+    return DFLASH_OK;
+  }
+  const dflash_config& c = h->cfg;
+  if (group_size < 1 || c.hidden % (16 * group_size))
+    return fail(DFLASH_E_SHAPE, "group_size=%d: hidden=%d must be a multiple of 16 * group_size",
+                group_size, c.hidden);
+  for (int i = 0; i < c.n_layers; ++i) {
+    const dflash_conv_layer& l = layers[i];
+    const void* ps[] = {l.attn_base, l.attn_proj, l.mlp_base, l.mlp_proj};
+    for (const void* p : ps) {
+      if (!p) return fail(DFLASH_E_NULL, "conv layer %d has a NULL table", i);
+      if (!aligned(p, 16)) return fail(DFLASH_E_ALIGN, "conv layer %d table not 16-byte aligned", i);
+    }
+  }
+  h->conv.assign(layers, layers + c.n_layers);
+  h->conv_gs = group_size;
   return DFLASH_OK;
 }
 

@@ -69,6 +69,14 @@ struct DraftLaunch {
   int att_splits, att_keys_per_split;
   SplitWs split;
   GemmWs gemm;              // the tiled GEMM's split-K scratch (batches of more than 64 rows)
+  // DFlash 2 convs in every layer (conv_gs == 0: none)
+  int conv_gs;
+  float* conv_h;            // [M][D] a sublayer's normed input
+  float* conv_y;            // [M][D] its conv (prepare call)
+  bf16_t *conv_ah, *conv_al;  // [M][D] conv_y as the sublayer GEMM's hi/lo input
+  bf16_t *conv_xh, *conv_xl;  // [M][D] split scratch of the prepare projection
+  float* conv_o;            // [M][D] a sublayer's output before the finish call
+  float *conv_corr_a, *conv_corr_m;  // [M][2 * D / conv_gs] finish corrections
 };
 
 int skinny_tile_cols();
@@ -77,14 +85,28 @@ int skinny_max_rows();
 size_t stream_part_floats(int n_vcols, int K);
 
 hipError_t launch_embed(const DraftLaunch& L, hipStream_t st);
+// ah/al: the layer's input rows as a bf16 hi/lo pair with no norm to apply
+// (the conv's output); null: the residual's next-norm input and its row scale
 hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
-                      const bf16_t* wk, const bf16_t* wv, hipStream_t st);
+                      const bf16_t* wk, const bf16_t* wv, hipStream_t st,
+                      const bf16_t* ah = nullptr, const bf16_t* al = nullptr);
 hipError_t launch_attention(const DraftLaunch& L, int layer, hipStream_t st);
 hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
                         const bf16_t* al, int K, const bf16_t* gain_next,
                         float* hidden, hipStream_t st);
 hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
-                         hipStream_t st);
+                         hipStream_t st, const bf16_t* ah = nullptr, const bf16_t* al = nullptr);
+// DFlash 2 convs in the layer: the fp32 norm of the residual rows into conv_h,
+// the prepare call on conv_h (conv_y, its hi/lo copy, the finish corrections
+// into corr), the plain product into out, and the finish call + residual add
+// + next-norm input
+hipError_t launch_norm_rows(const DraftLaunch& L, const bf16_t* gain, hipStream_t st);
+hipError_t launch_conv_prepare_draft(const DraftLaunch& L, const bf16_t* base, const bf16_t* proj,
+                                     float* corr, hipStream_t st);
+hipError_t launch_store(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah, const bf16_t* al,
+                        int K, float* out, hipStream_t st);
+hipError_t launch_conv_finish_resid(const DraftLaunch& L, const bf16_t* base, const float* corr,
+                                    const bf16_t* gain_next, float* hidden, hipStream_t st);
 hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
                      hipStream_t st);
 // drafted tokens from the LM head's output (split sums, logits, argmax)

@@ -286,6 +286,29 @@ struct EpiLM {
   }
 };
 
+// Plain fp32 store of the product (the draft's sublayer outputs when a conv
+// follows them: the residual add happens after the conv's finish call).
+struct EpiStore {
+  struct P {
+    const bf16_t* w;   // [N][K]
+    int K, N;
+    float* out;        // [M][N]
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return p.w + (size_t)(vc8 + r8) * p.K;
+  }
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs, int vc0, int m0,
+                             int M) {
+    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
+      const int ml = e / VC, c = e % VC;
+      const int m = m0 + ml, n = vc0 + c;
+      if (m < M && n < p.N) p.out[(size_t)m * p.N + n] = tile[ml][c] * rs[ml];
+    }
+  }
+};
+
 // Context fusion for a few rows (the accepted rows appended each round):
 // y = [h_1 .. h_n] W_c^T in fp32 plus per-32-column sums of y^2; the RMSNorm
 // pass runs afterwards and rounds to bf16 once.
@@ -488,7 +511,7 @@ struct EpiConv {
     const bf16_t* proj;  // [4G][D]
     const bf16_t* base;  // [2][2][D] (call, tap, channel)
     const float* x;      // [M][D] the conv input (also the GEMM's A, as hi/lo)
-    const float* prev;   // [n_seqs][D]
+    const float* prev;   // [n_seqs][D]; null: a zero row
     float* y;            // [M][D]
     float* corr;         // [M][2G] finish corrections (tap, group)
     int D, G, gs, Bl;
@@ -542,7 +565,8 @@ struct EpiConv {
           m = m < M ? m : M - 1;
           const int t = m % p.Bl;
           xv[u] = p.x[(size_t)m * p.D + c];
-          xb[u] = t == 0 ? p.prev[(size_t)(m / p.Bl) * p.D + c] : p.x[(size_t)(m - 1) * p.D + c];
+          xb[u] = t == 0 ? (p.prev ? p.prev[(size_t)(m / p.Bl) * p.D + c] : 0.f)
+                         : p.x[(size_t)(m - 1) * p.D + c];
           b0[u] = p.base[c];
           b1[u] = p.base[p.D + c];
         }
@@ -1351,10 +1375,94 @@ conv_finish(const float* __restrict__ z, const float* __restrict__ prev,
   if (c >= D) return;
   const int t = m % Bl, g = c / gs;
   const float zv = z[(size_t)m * D + c];
-  const float zb = t == 0 ? prev[(size_t)(m / Bl) * D + c] : z[(size_t)(m - 1) * D + c];
+  const float zb = t == 0 ? (prev ? prev[(size_t)(m / Bl) * D + c] : 0.f) : z[(size_t)(m - 1) * D + c];
   const float k0 = bf2f(base[2 * D + c]) + corr[(size_t)m * 2 * G + g];
   const float k1 = bf2f(base[3 * D + c]) + corr[(size_t)m * 2 * G + G + g];
   y[(size_t)m * D + c] = k0 * zv + k1 * zb;
+}
+
+// RMSNorm of the residual rows in fp32: h = x * gain * rsqrt(mean(x^2) + eps),
+// the mean from the producer's per-32-column sums of x^2. One workgroup per
+// (row, 1024 columns), four columns per thread.
+__global__ void __launch_bounds__(256)
+norm_rows(const float* __restrict__ x, const bf16_t* __restrict__ gain,
+          const float* __restrict__ ssq, int D, float eps, float* __restrict__ h) {
+  const int m = blockIdx.y;
+  __shared__ float rs;
+  if (threadIdx.x < 64) {
+    float s = strided_sum(ssq + (size_t)m * (D / 32), D / 32, threadIdx.x, 64);
+    s = wave_sum(s);
+    if (threadIdx.x == 0) rs = rsqrtf(s / (float)D + eps);
+  }
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  float4 xv = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint2 gv = make_uint2(0u, 0u);
+  if (n < D) {
+    xv = *reinterpret_cast<const float4*>(x + (size_t)m * D + n);
+    gv = *reinterpret_cast<const uint2*>(gain + n);
+  }
+  __syncthreads();
+  if (n >= D) return;
+  const float r = rs;
+  float4 o;
+  o.x = xv.x * bf2f((bf16_t)(gv.x & 0xffff)) * r;
+  o.y = xv.y * bf2f((bf16_t)(gv.x >> 16)) * r;
+  o.z = xv.z * bf2f((bf16_t)(gv.y & 0xffff)) * r;
+  o.w = xv.w * bf2f((bf16_t)(gv.y >> 16)) * r;
+  *reinterpret_cast<float4*>(h + (size_t)m * D + n) = o;
+}
+
+// The finish call of a layer's conv followed by the residual add: for row m
+// (position t of its block) and channel c,
+//   y = (b1[0][c] + corr[m][0][g]) z_t[c] + (b1[1][c] + corr[m][1][g]) z_{t-1}[c],
+// z_{-1} = 0, g = c / gs; then x += y, the optional hidden copy, the next
+// RMSNorm's input x * gain as a bf16 hi/lo pair and per-32-column sums of
+// x^2 (as the residual epilogue of the GEMMs leaves them). One workgroup per
+// (row, 1024 columns), four columns per thread, eight threads per 32-column
+// group.
+__global__ void __launch_bounds__(256)
+conv_finish_resid(const float* __restrict__ z, const bf16_t* __restrict__ base,
+                  const float* __restrict__ corr, int D, int G, int gs, int Bl,
+                  const bf16_t* __restrict__ gain, float* __restrict__ x,
+                  float* __restrict__ hidden, bf16_t* __restrict__ xh, bf16_t* __restrict__ xl,
+                  float* __restrict__ ssq) {
+  const int m = blockIdx.y, t = m % Bl;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  float sq = 0.f;
+  if (n < D) {
+    const size_t i = (size_t)m * D + n;
+    const float4 zv = *reinterpret_cast<const float4*>(z + i);
+    const float4 zp = t > 0 ? *reinterpret_cast<const float4*>(z + i - D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 xv = *reinterpret_cast<const float4*>(x + i);
+    const uint2 b0 = *reinterpret_cast<const uint2*>(base + 2 * D + n);  // base[1][0]
+    const uint2 b1 = *reinterpret_cast<const uint2*>(base + 3 * D + n);  // base[1][1]
+    const uint2 gv = *reinterpret_cast<const uint2*>(gain + n);
+    const float* cr = corr + (size_t)m * 2 * G;
+    const float zc[4] = {zv.x, zv.y, zv.z, zv.w}, zq[4] = {zp.x, zp.y, zp.z, zp.w};
+    const uint32_t bb0[2] = {b0.x, b0.y}, bb1[2] = {b1.x, b1.y}, gg[2] = {gv.x, gv.y};
+    float* xp = reinterpret_cast<float*>(&xv);
+    bf16_t hi[4], lo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int gk = (n + k) / gs;
+      const float k0 = bf2f((bf16_t)(k & 1 ? bb0[k >> 1] >> 16 : bb0[k >> 1] & 0xffff)) + cr[gk];
+      const float k1 = bf2f((bf16_t)(k & 1 ? bb1[k >> 1] >> 16 : bb1[k >> 1] & 0xffff)) + cr[G + gk];
+      const float gn = bf2f((bf16_t)(k & 1 ? gg[k >> 1] >> 16 : gg[k >> 1] & 0xffff));
+      xp[k] += k0 * zc[k] + k1 * zq[k];
+      split_bf16(xp[k] * gn, hi[k], lo[k]);
+      sq += xp[k] * xp[k];
+    }
+    *reinterpret_cast<float4*>(x + i) = xv;
+    if (hidden) *reinterpret_cast<float4*>(hidden + i) = xv;
+    *reinterpret_cast<uint2*>(xh + i) =
+        make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+    *reinterpret_cast<uint2*>(xl + i) =
+        make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+  }
+  sq += __shfl_xor(sq, 1, kWave);
+  sq += __shfl_xor(sq, 2, kWave);
+  sq += __shfl_xor(sq, 4, kWave);
+  if (n < D && (threadIdx.x & 7) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
 }
 
 hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st) {
@@ -1436,8 +1544,12 @@ hipError_t launch_embed(const DraftLaunch& L, hipStream_t st) {
 }
 
 hipError_t launch_qkv(const DraftLaunch& L, int layer, const bf16_t* wq,
-                      const bf16_t* wk, const bf16_t* wv, hipStream_t st) {
-  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+                      const bf16_t* wk, const bf16_t* wv, hipStream_t st, const bf16_t* ah,
+                      const bf16_t* al) {
+  // the residual's next-norm input with the norm's row scale, or (ah/al) rows
+  // that are already the layer's input
+  SkinnyA a = ah ? make_a(ah, al, L.D, L.M, L.D, nullptr, 0, L.eps)
+                 : make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
   EpiQKV::P p;
   p.wq = wq; p.wk = wk; p.wv = wv; p.D = L.D; p.Hq = L.Hq; p.Hkv = L.Hkv;
   p.hd = L.hd; p.Bl = L.Bl; p.layer = layer; p.log2_theta = L.log2_theta;
@@ -1456,11 +1568,48 @@ hipError_t launch_resid(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
 }
 
 hipError_t launch_swiglu(const DraftLaunch& L, const bf16_t* wg, const bf16_t* wu,
-                         hipStream_t st) {
-  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+                         hipStream_t st, const bf16_t* ah, const bf16_t* al) {
+  SkinnyA a = ah ? make_a(ah, al, L.D, L.M, L.D, nullptr, 0, L.eps)
+                 : make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
   EpiSwiglu::P p;
   p.wg = wg; p.wu = wu; p.K = L.D; p.F = L.F; p.ah = L.act_h; p.al = L.act_l; p.n_vcols = 2 * L.F;
   return launch_skinny<EpiSwiglu>(a, p, 2 * L.F, L.split, st, &L.gemm);
+}
+
+hipError_t launch_store(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah, const bf16_t* al,
+                        int K, float* out, hipStream_t st) {
+  SkinnyA a = make_a(ah, al, K, L.M, K, nullptr, 0, L.eps);
+  EpiStore::P p;
+  p.w = w; p.K = K; p.N = L.D; p.out = out;
+  return launch_skinny<EpiStore>(a, p, L.D, L.split, st, &L.gemm);
+}
+
+hipError_t launch_norm_rows(const DraftLaunch& L, const bf16_t* gain, hipStream_t st) {
+  hipLaunchKernelGGL(norm_rows, dim3((L.D + 1023) / 1024, L.M), dim3(256), 0, st, L.x, gain, L.ssq, L.D,
+                     L.eps, L.conv_h);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_prepare_draft(const DraftLaunch& L, const bf16_t* base, const bf16_t* proj,
+                                     float* corr, hipStream_t st) {
+  ConvLaunch C{};
+  C.n_seqs = L.n_seqs; C.Bl = L.Bl; C.D = L.D; C.gs = L.conv_gs;
+  C.base = base; C.proj = proj; C.x = L.conv_h; C.prev = nullptr; C.y = L.conv_y; C.corr = corr;
+  C.xh = L.conv_xh; C.xl = L.conv_xl; C.split = L.split;
+  hipError_t e = launch_conv_prepare(C, st);
+  if (e != hipSuccess) return e;
+  // the conv's output as the sublayer GEMM's bf16 hi/lo input
+  hipLaunchKernelGGL(conv_split, dim3((L.D / 4 + 255) / 256, L.M), dim3(256), 0, st, L.conv_y, L.D,
+                     L.conv_ah, L.conv_al);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_finish_resid(const DraftLaunch& L, const bf16_t* base, const float* corr,
+                                    const bf16_t* gain_next, float* hidden, hipStream_t st) {
+  hipLaunchKernelGGL(conv_finish_resid, dim3((L.D + 1023) / 1024, L.M), dim3(256), 0, st, L.conv_o,
+                     base, corr, L.D, L.D / L.conv_gs, L.conv_gs, L.Bl, gain_next, L.x, hidden, L.xh,
+                     L.xl, L.ssq);
+  return hipGetLastError();
 }
 
 namespace {

@@ -125,6 +125,21 @@ class Drafter:
                               philox_offset, block_ids.data_ptr())
         return block_ids
 
+    # --- DFlash 2 convs inside every layer --------------------------------------
+    def set_conv(self, conv: Optional[Dict]):
+        """Borrow the convs' bf16 tables ({"group_size", "layers": [{attn_base,
+        attn_proj, mlp_base, mlp_proj}]}, kept alive by this object); None
+        removes them."""
+        if conv is None:
+            self._conv = None
+            B.dflash_set_conv(self.h, None, 0)
+            return
+        self._conv = conv
+        layers = [B.dflash_conv_layer(l["attn_base"].data_ptr(), l["attn_proj"].data_ptr(),
+                                      l["mlp_base"].data_ptr(), l["mlp_proj"].data_ptr())
+                  for l in conv["layers"]]
+        B.dflash_set_conv(self.h, layers, conv["group_size"])
+
     # --- DFlash 2 candidate selector -------------------------------------------
     def set_selector(self, hidden_proj: torch.Tensor, pred_codebook: torch.Tensor,
                      succ_codebook: torch.Tensor, top_k: int):

@@ -318,6 +318,39 @@ dflash_status dflash_verify_noalloc(dflash_handle* h, int32_t n_seqs, int32_t bl
                                     int32_t* tau_out, int32_t* bonus_out);
 
 /*
+ * DFlash 2 grouped dynamic two-tap causal conv inside every draft layer
+ * ([Code] section 13: y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1} per channel,
+ * each coefficient a learned base plus a correction computed from the hidden
+ * state, one correction per group_size channels, acting only inside the
+ * block with no state across steps; section 14: two instances per layer, one
+ * by attention and one by the MLP, base kernel (2, taps, hidden) whose first
+ * index separates the "prepare" and "finish" calls, a bias-free projection
+ * to 2 * taps * groups corrections).
+ * dflash_set_conv borrows one dflash_conv_layer per draft layer (layers[i]
+ * for layer i; NULL layers removes the convs); from then on
+ * dflash_draft_block and dflash_draft_block_dev run each layer as
+ *   h = RMSNorm(x); (h', c) = prepare(h); attention on h';
+ *   x += finish(o_proj output; c); h2 = RMSNorm(x); (h2', c2) = prepare(h2);
+ *   x += finish(MLP(h2'); c2)
+ * where prepare(v) convolves v with base[0] plus the call-0 corrections of
+ * the projection of v and returns the call-1 corrections c; finish(z; c)
+ * convolves z with base[1] plus c; the block's first row reads a zero row as
+ * its predecessor. (That the calls sit on the sublayer's normed input and
+ * output is this library's reading; the pages do not place them.)
+ * Tables: *_base bf16 [2, 2, hidden] (call, tap, channel); *_proj bf16
+ * [4 * hidden / group_size, hidden], rows ordered (call, tap, group), as
+ * dflash_conv_prepare. hidden % (16 * group_size) == 0; tables 16-byte
+ * aligned. The handle keeps the pointers; nothing is copied or allocated.
+ */
+typedef struct {
+  const void* attn_base;
+  const void* attn_proj;
+  const void* mlp_base;
+  const void* mlp_proj;
+} dflash_conv_layer;
+dflash_status dflash_set_conv(dflash_handle* h, const dflash_conv_layer* layers, int32_t group_size);
+
+/*
  * DFlash 2 candidate selector ([Code] section 13: the right token is usually
  * among a drafted row's top candidates; each adjacent pair is scored as
  * S_t(a, b) = U_t(b) + <A(a) * H(h_t), B(b)>, and one walk over the scores

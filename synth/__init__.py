@@ -21,7 +21,8 @@ Recipe (one per workload, all seeded):
 * candidate-selector tables (DFlash 2): hidden projection N(0, 1/D),
   predecessor and successor codes N(0, 0.3^2), rank 256.
 * dynamic two-tap conv (DFlash 2): base kernel N(0, 0.5^2), projection
-  N(0, 1/D), 16 channels per group, input rows N(0, 1) in fp32.
+  N(0, 1/D), 16 channels per group, input rows N(0, 1) in fp32; the same
+  draws for the two instances of every draft layer (make_conv_layers).
 
 Floating-point draws are made in fp32 and rounded once to bf16 (round to
 nearest even, torch's conversion) where the tensor is stored in bf16; the
@@ -32,6 +33,7 @@ from .gen import (  # noqa: F401
     make_weights,
     make_selector,
     make_conv,
+    make_conv_layers,
     make_feats,
     make_anchor,
     make_target_logits,

@@ -24,6 +24,7 @@ _RAGGED = 800
 _CTXKV_BASE = 850           # + layer
 _SEL_BASE = 900             # + 0 hidden projection, 1 predecessor, 2 successor codes
 _CONV_BASE = 950            # + 0 base kernel, 1 projection, 2..5 rows
+_CONV_LAYER_BASE = 200      # + 10 * layer + 2 * instance + (0 base, 1 projection)
 
 LAYER_SLOTS = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down",
                "attn_norm", "mlp_norm")
@@ -119,6 +120,24 @@ def make_conv(cfg: DraftConfig, n_seqs: int, block_len: int, group_size: int = 1
         "z": _normal((rows, D), 1.0, s(4), device, f32),
         "zprev": _normal((n_seqs, D), 1.0, s(5), device, f32),
     }
+
+
+def make_conv_layers(cfg: DraftConfig, group_size: int = 16, device="cpu") -> Dict:
+    """The DFlash 2 convs of every draft layer (one by attention, one by the
+    MLP): per layer attn_base / mlp_base [2, 2, D] bf16 with entries
+    N(0, 0.5^2) and attn_proj / mlp_proj [4 * D / group_size, D] bf16 with
+    entries N(0, 1/D), as make_conv draws one instance."""
+    D = cfg.hidden
+    layers = []
+    for i in range(cfg.n_layers):
+        lw = {}
+        for j, inst in enumerate(("attn", "mlp")):
+            t = _CONV_LAYER_BASE + 10 * i + 2 * j
+            lw[inst + "_base"] = _normal((2, 2, D), 0.5, seed_for(cfg.index, t), device)
+            lw[inst + "_proj"] = _normal((4 * (D // group_size), D), D ** -0.5,
+                                         seed_for(cfg.index, t + 1), device)
+        layers.append(lw)
+    return {"group_size": group_size, "layers": layers}
 
 
 def make_feats(cfg: DraftConfig, n_tokens: int, round_index: int = 0,

@@ -80,3 +80,59 @@ def test_qwen_shape_single_row_blocks():
 
 def test_d2048_group_32():
     _run(CONFIGS[4], 2, 8, gs=32)
+
+
+# ---------------------------------------------------------------------------
+# the convs inside every draft layer (dflash_set_conv)
+# ---------------------------------------------------------------------------
+
+def _conv_np(conv):
+    return {"group_size": conv["group_size"],
+            "layers": [{k: np32(v).astype(np.float64) for k, v in l.items()} for l in conv["layers"]]}
+
+
+def _draft_with_convs(dc, S, gs, bl=None, gains="random"):
+    from gpu_helpers import (TIGHT_TOL, assert_hidden, assert_tokens, fill_context, hidden_errs,
+                             oracle_cache, poisoned_kv, synthetic_context, weights_np)
+    bl = dc.block_size if bl is None else bl
+    say(f"draft with convs: config {dc.name} S={S} group_size={gs} block_len={bl}")
+    d, w = make(dc, gains=gains)
+    conv = synth.make_conv_layers(dc, gs, device=DEV)
+    d.set_conv(conv)
+    kv = poisoned_kv(d, S + 8)
+    ctx = synthetic_context(dc, S)
+    if S:
+        fill_context(kv, ctx)
+    anchors = synth.make_anchor(dc)
+    block, hid, _ = d.draft_block([kv], torch.from_numpy(anchors).to(DEV), bl, hidden=True)
+    torch.cuda.synchronize()
+    wn = weights_np(w)
+    orc = O.draft_block(dc, wn, [oracle_cache(dc, ctx)], [int(anchors[0])], bl, conv=_conv_np(conv))
+    g = np32(hid).reshape(dc.n_layers, bl, -1)
+    say("  plain: " + " ".join(f"{e:.2e}" for e in hidden_errs(g, orc["hidden"])))
+    assert_hidden(g, orc["hidden"], what="conv draft")
+    assert_hidden(g, orc["hidden"], what="conv draft", tol=TIGHT_TOL)
+    if bl > 1:
+        assert_tokens(block.cpu().numpy(), orc, what="conv draft")
+    # removing the convs gives the plain draft back
+    d.set_conv(None)
+    block2, hid2, _ = d.draft_block([kv], torch.from_numpy(anchors).to(DEV), bl, hidden=True)
+    torch.cuda.synchronize()
+    orc2 = O.draft_block(dc, wn, [oracle_cache(dc, ctx)], [int(anchors[0])], bl)
+    assert_hidden(np32(hid2).reshape(dc.n_layers, bl, -1), orc2["hidden"], what="plain draft",
+                  tol=TIGHT_TOL)
+    d.close()
+
+
+def test_draft_with_convs_tiny():
+    # hidden 64: four channels per correction group
+    _draft_with_convs(CONFIGS[0].shrink(n_layers=2, index=94), 10, 4)
+
+
+def test_draft_with_convs_tiny_empty_context_short_block():
+    _draft_with_convs(CONFIGS[0].shrink(n_layers=2, index=94), 0, 4, bl=3)
+
+
+def test_draft_with_convs_qwen_shape_full_size():
+    dc = CONFIGS[1]
+    _draft_with_convs(dc, dc.ctx_len, 16, gains="ones")
