@@ -588,9 +588,51 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
     const bf16_t* gnext = (const bf16_t*)(i + 1 < c.n_layers ? h->layers[i + 1].attn_norm
                                                               : h->w.final_norm);
     float* hid = hidden_out ? hidden_out + (size_t)i * L.M * c.hidden : nullptr;
+    if (conv && conv_fused(L)) {
+      // the layer with its two convs ([Code] sections 13-14), fused into the
+      // GEMMs' finishers: prepare on the sublayer's normed input (the
+      // projection's finisher forms the norm and the conv), finish on the
+      // sublayer's output before the residual add (in its finisher)
+      const dflash_conv_layer& cw = h->conv[i];
+      e = timed(h, ST_CONV, [&] {
+        return launch_conv_prepare_fused(L, (const bf16_t*)lw.attn_norm, (const bf16_t*)cw.attn_base,
+                                         (const bf16_t*)cw.attn_proj, L.conv_corr_a, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "conv (attention, prepare)");
+      e = timed(h, ST_QKV, [&] {
+        return launch_qkv(L, i, (const bf16_t*)lw.wq, (const bf16_t*)lw.wk, (const bf16_t*)lw.wv, st,
+                          L.conv_ah, L.conv_al);
+      });
+      if (e != hipSuccess) return dev_fail(e, "qkv");
+      e = timed(h, ST_ATTN, [&] { return launch_attention(L, i, st); });
+      if (e != hipSuccess) return dev_fail(e, "attention");
+      e = timed(h, ST_OPROJ, [&] {
+        return launch_conv_resid_fused(L, (const bf16_t*)lw.wo, L.ob_h, L.ob_l, c.n_heads * c.head_dim,
+                                       (const bf16_t*)cw.attn_base, L.conv_corr_a,
+                                       (const bf16_t*)lw.mlp_norm, nullptr, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "o_proj + conv finish");
+      e = timed(h, ST_CONV, [&] {
+        return launch_conv_prepare_fused(L, (const bf16_t*)lw.mlp_norm, (const bf16_t*)cw.mlp_base,
+                                         (const bf16_t*)cw.mlp_proj, L.conv_corr_m, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "conv (MLP, prepare)");
+      e = timed(h, ST_GATEUP, [&] {
+        return launch_swiglu(L, (const bf16_t*)lw.w_gate, (const bf16_t*)lw.w_up, st, L.conv_ah,
+                             L.conv_al);
+      });
+      if (e != hipSuccess) return dev_fail(e, "gate_up");
+      e = timed(h, ST_DOWN, [&] {
+        return launch_conv_resid_fused(L, (const bf16_t*)lw.w_down, L.act_h, L.act_l, c.ffn,
+                                       (const bf16_t*)cw.mlp_base, L.conv_corr_m, gnext, hid, st);
+      });
+      if (e != hipSuccess) return dev_fail(e, "down_proj + conv finish");
+      continue;
+    }
     if (conv) {
       // the layer with its two convs ([Code] sections 13-14): prepare on the
       // sublayer's normed input, finish on its output before the residual add
+      // (separate kernels: more rows than one tile)
       const dflash_conv_layer& cw = h->conv[i];
       e = timed(h, ST_CONV, [&] {
         hipError_t r = launch_norm_rows(L, (const bf16_t*)lw.attn_norm, st);

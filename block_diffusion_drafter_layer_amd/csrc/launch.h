@@ -107,6 +107,17 @@ hipError_t launch_store(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
                         int K, float* out, hipStream_t st);
 hipError_t launch_conv_finish_resid(const DraftLaunch& L, const bf16_t* base, const float* corr,
                                     const bf16_t* gain_next, float* hidden, hipStream_t st);
+// the same two steps fused into the GEMMs' finishers, when every row fits one
+// 16-row tile: the prepare call's projection with the norm and the conv in its
+// finisher (the conv output straight to conv_ah / conv_al), and the
+// sublayer's output product with the finish call and the residual add in its
+// finisher
+bool conv_fused(const DraftLaunch& L);
+hipError_t launch_conv_prepare_fused(const DraftLaunch& L, const bf16_t* gain, const bf16_t* base,
+                                     const bf16_t* proj, float* corr, hipStream_t st);
+hipError_t launch_conv_resid_fused(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
+                                   const bf16_t* al, int K, const bf16_t* base, const float* corr,
+                                   const bf16_t* gain_next, float* hidden, hipStream_t st);
 hipError_t launch_lm(const DraftLaunch& L, const bf16_t* w_lm, float* logits,
                      hipStream_t st);
 // drafted tokens from the LM head's output (split sums, logits, argmax)

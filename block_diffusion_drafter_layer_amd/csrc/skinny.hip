@@ -517,6 +517,12 @@ struct EpiConv {
     int D, G, gs, Bl;
     int n_vcols;         // 4G
     int parts;           // workgroups sharing a pair's channels (grid.y of the finisher), else 1
+    // inside a draft layer (EpiConvNorm): x is the residual stream and the
+    // conv input the normed row x * gain * rs (rs the GEMM's row scale, which
+    // also scales the corrections); the output goes to yh / yl as the
+    // sublayer GEMM's bf16 hi/lo input instead of y. All rows in one tile.
+    const bf16_t* gain;  // null: x is the conv input itself
+    bf16_t *yh, *yl;
   };
   __device__ static int prow(const P& p, int v) {
     const int call = v / (2 * p.G), w = v - call * 2 * p.G;
@@ -530,7 +536,7 @@ struct EpiConv {
     return p.proj + (size_t)(prow(p, vc8) + r8) * p.D;
   }
   template <int ROWS, int VC, int LD = VC + 1>
-  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs, int vc0, int m0,
                              int M) {
     static_assert(VC % 32 == 0, "whole column pairs per workgroup");
     for (int pl = 0; pl < VC / 32; ++pl) {
@@ -544,7 +550,7 @@ struct EpiConv {
         for (int e = threadIdx.x; e < ROWS * 32; e += blockDim.x) {
           const int ml = e >> 5, j = e & 31, m = m0 + ml;
           if (m < M)
-            p.corr[(size_t)m * 2 * p.G + (j >> 4) * p.G + g0 + (j & 15)] = tile[ml][pl * 32 + j];
+            p.corr[(size_t)m * 2 * p.G + (j >> 4) * p.G + g0 + (j & 15)] = tile[ml][pl * 32 + j] * rs[ml];
         }
         continue;
       }
@@ -555,7 +561,7 @@ struct EpiConv {
       const int nch = 16 * p.gs / p.parts, c0 = g0 * p.gs + part * nch;
       for (int e0 = threadIdx.x; e0 < ROWS * nch; e0 += U * blockDim.x) {
         float xv[U], xb[U];
-        bf16_t b0[U], b1[U];
+        bf16_t b0[U], b1[U], gn[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int e = e0 + u * blockDim.x;
@@ -569,6 +575,7 @@ struct EpiConv {
                          : p.x[(size_t)(m - 1) * p.D + c];
           b0[u] = p.base[c];
           b1[u] = p.base[p.D + c];
+          gn[u] = p.gain ? p.gain[c] : (bf16_t)0;
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -576,11 +583,86 @@ struct EpiConv {
           const int ml = e / nch, cl = e - ml * nch, m = m0 + ml;
           if (e >= ROWS * nch || m >= M) continue;
           const int gl = (c0 - g0 * p.gs + cl) / p.gs;
-          const float k0 = bf2f(b0[u]) + tile[ml][pl * 32 + gl];
-          const float k1 = bf2f(b1[u]) + tile[ml][pl * 32 + 16 + gl];
-          p.y[(size_t)m * p.D + c0 + cl] = k0 * xv[u] + k1 * xb[u];
+          const float k0 = bf2f(b0[u]) + tile[ml][pl * 32 + gl] * rs[ml];
+          const float k1 = bf2f(b1[u]) + tile[ml][pl * 32 + 16 + gl] * rs[ml];
+          const size_t i = (size_t)m * p.D + c0 + cl;
+          if (p.gain) {  // normed rows: the previous row's scale is rs[ml - 1] (one tile)
+            const float g = bf2f(gn[u]);
+            const float ht = xv[u] * g * rs[ml];
+            const float hp = m % p.Bl ? xb[u] * g * rs[ml - 1] : 0.f;
+            split_bf16(k0 * ht + k1 * hp, p.yh[i], p.yl[i]);
+          } else {
+            p.y[i] = k0 * xv[u] + k1 * xb[u];
+          }
         }
       }
+    }
+  }
+};
+
+// The prepare call inside a draft layer: EpiConv in its fused mode, with the
+// GEMM's A operand staged as usual (the residual's next-norm input x * gain as
+// a bf16 hi/lo pair and its row scale) instead of fp32 conv input rows.
+struct EpiConvNorm : EpiConv {};
+
+// The finish call of a layer's conv fused with the residual add (the
+// sublayer's output product, one tile holding every row): per row m
+// (position t of its block) and column c of the tile, z = the product,
+//   y = (base[1][0][c] + corr[m][0][g]) z_t + (base[1][1][c] + corr[m][1][g]) z_{t-1},
+// z_{-1} = 0, g = c / gs; then x += y, the optional hidden copy, the next
+// RMSNorm's input x * gain as a bf16 hi/lo pair and per-32-column sums of
+// x^2, as EpiResid leaves them.
+struct EpiConvResid {
+  struct P {
+    const bf16_t* w;     // [N=D][K]
+    int K, D;
+    const bf16_t* base;  // [2][2][D]
+    const float* corr;   // [M][2G]
+    int G, gs, Bl;
+    float* x;            // [M][D]
+    bf16_t *xh, *xl;     // [M][D]
+    const bf16_t* gain;  // [D] the next norm's gain
+    float* ssq;          // [M][D/32]
+    float* hidden;       // optional [M][D]
+    int n_vcols;         // D
+  };
+  __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
+  __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
+    return p.w + (size_t)(vc8 + r8) * p.K;
+  }
+  template <int ROWS, int VC, int LD = VC + 1>
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs, int vc0, int m0,
+                             int M) {
+    static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
+    __shared__ float sq[ROWS][VC + 1];
+    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
+      const int ml = e / VC, c = e % VC;
+      const int m = m0 + ml, n = vc0 + c;
+      float v = 0.f;
+      if (m < M && n < p.n_vcols) {
+        const int t = m % p.Bl, g = n / p.gs;
+        const float zt = tile[ml][c] * rs[ml];
+        const float zp = t ? tile[ml - 1][c] * rs[ml - 1] : 0.f;
+        const float k0 = bf2f(p.base[2 * p.D + n]) + p.corr[(size_t)m * 2 * p.G + g];
+        const float k1 = bf2f(p.base[3 * p.D + n]) + p.corr[(size_t)m * 2 * p.G + p.G + g];
+        const size_t i = (size_t)m * p.D + n;
+        const float xn = p.x[i] + k0 * zt + k1 * zp;
+        p.x[i] = xn;
+        if (p.hidden) p.hidden[i] = xn;
+        split_bf16(xn * bf2f(p.gain[n]), p.xh[i], p.xl[i]);
+        v = xn * xn;
+      }
+      sq[ml][c] = v;
+    }
+    __syncthreads();
+    const int ng = p.D / 32;
+    for (int e = threadIdx.x; e < ROWS * (VC / 32); e += blockDim.x) {
+      const int ml = e / (VC / 32), g = e % (VC / 32);
+      if (m0 + ml >= M || vc0 + g * 32 >= p.n_vcols) continue;
+      float sum = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < 32; ++c) sum += sq[ml][g * 32 + c];
+      p.ssq[(size_t)(m0 + ml) * ng + vc0 / 32 + g] = sum;
     }
   }
 };
@@ -1471,6 +1553,7 @@ hipError_t launch_conv_prepare(const ConvLaunch& C, hipStream_t st) {
   EpiConv::P p;
   p.proj = C.proj; p.base = C.base; p.x = C.x; p.prev = C.prev; p.y = C.y; p.corr = C.corr;
   p.D = C.D; p.G = C.D / C.gs; p.gs = C.gs; p.Bl = C.Bl; p.n_vcols = 4 * p.G; p.parts = 1;
+  p.gain = nullptr; p.yh = nullptr; p.yl = nullptr;
   int ks;
   hipError_t e;
   if (!uses_stream(a, p.n_vcols, C.split, ks)) {
@@ -1602,6 +1685,47 @@ hipError_t launch_conv_prepare_draft(const DraftLaunch& L, const bf16_t* base, c
   hipLaunchKernelGGL(conv_split, dim3((L.D / 4 + 255) / 256, L.M), dim3(256), 0, st, L.conv_y, L.D,
                      L.conv_ah, L.conv_al);
   return hipGetLastError();
+}
+
+bool conv_fused(const DraftLaunch& L) {
+  // one tile holds every row (the finishers read the previous row of a block
+  // from their own tile) and the projection takes the LDS-staged kernel
+  if (L.M > 16) return false;
+  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+  int ks;
+  return uses_stream(a, 4 * (L.D / L.conv_gs), L.split, ks);
+}
+
+hipError_t launch_conv_prepare_fused(const DraftLaunch& L, const bf16_t* gain, const bf16_t* base,
+                                     const bf16_t* proj, float* corr, hipStream_t st) {
+  SkinnyA a = make_a(L.xh, L.xl, L.D, L.M, L.D, L.ssq, L.D / 32, L.eps);
+  EpiConvNorm::P p;
+  p.proj = proj; p.base = base; p.x = L.x; p.prev = nullptr; p.y = nullptr; p.corr = corr;
+  p.D = L.D; p.G = L.D / L.conv_gs; p.gs = L.conv_gs; p.Bl = L.Bl; p.n_vcols = 4 * p.G;
+  p.parts = 8; p.gain = gain; p.yh = L.conv_ah; p.yl = L.conv_al;
+  int ks;
+  if (!uses_stream(a, p.n_vcols, L.split, ks)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, true, EpiConvNorm>), dim3(stream_grid(ks)),
+                     dim3(kSW * 64), 0, st, a, p, p.n_vcols, ks, L.D / ks, L.split.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((stream_finish<EpiConvNorm>), dim3(p.n_vcols / 32, p.parts), dim3(256), 0, st, a,
+                     p, ks, L.split.part);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv_resid_fused(const DraftLaunch& L, const bf16_t* w, const bf16_t* ah,
+                                   const bf16_t* al, int K, const bf16_t* base, const float* corr,
+                                   const bf16_t* gain_next, float* hidden, hipStream_t st) {
+  SkinnyA a = make_a(ah, al, K, L.M, K, nullptr, 0, L.eps);
+  EpiConvResid::P p;
+  p.w = w; p.K = K; p.D = L.D; p.base = base; p.corr = corr;
+  p.G = L.D / L.conv_gs; p.gs = L.conv_gs; p.Bl = L.Bl;
+  p.x = L.x; p.xh = L.xh; p.xl = L.xl; p.gain = gain_next; p.ssq = L.ssq; p.hidden = hidden;
+  p.n_vcols = L.D;
+  int ks;
+  if (uses_stream(a, L.D, L.split, ks)) return launch_stream<EpiConvResid, true>(a, p, L.D, ks, L.split, st);
+  return launch_cfg<EpiConvResid, true, 1, 4, 4>(a, p, L.D, L.split, st);
 }
 
 hipError_t launch_conv_finish_resid(const DraftLaunch& L, const bf16_t* base, const float* corr,

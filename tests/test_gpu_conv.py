@@ -91,24 +91,32 @@ def _conv_np(conv):
             "layers": [{k: np32(v).astype(np.float64) for k, v in l.items()} for l in conv["layers"]]}
 
 
-def _draft_with_convs(dc, S, gs, bl=None, gains="random"):
+def _draft_with_convs(dc, lens, gs, bl=None, gains="random"):
     from gpu_helpers import (TIGHT_TOL, assert_hidden, assert_tokens, fill_context, hidden_errs,
                              oracle_cache, poisoned_kv, synthetic_context, weights_np)
     bl = dc.block_size if bl is None else bl
-    say(f"draft with convs: config {dc.name} S={S} group_size={gs} block_len={bl}")
-    d, w = make(dc, gains=gains)
+    lens = [lens] if isinstance(lens, int) else list(lens)
+    n = len(lens)
+    say(f"draft with convs: config {dc.name} contexts {lens} group_size={gs} block_len={bl}")
+    d, w = make(dc, max_seqs=n, gains=gains)
     conv = synth.make_conv_layers(dc, gs, device=DEV)
     d.set_conv(conv)
-    kv = poisoned_kv(d, S + 8)
-    ctx = synthetic_context(dc, S)
-    if S:
-        fill_context(kv, ctx)
-    anchors = synth.make_anchor(dc)
-    block, hid, _ = d.draft_block([kv], torch.from_numpy(anchors).to(DEV), bl, hidden=True)
+    kvs, ctxs = [], []
+    for s_, S in enumerate(lens):
+        kv = poisoned_kv(d, S + 8)
+        ctx = synthetic_context(dc, S, seq=s_)
+        if S:
+            fill_context(kv, ctx)
+        kvs.append(kv)
+        ctxs.append(ctx)
+    anchors = synth.make_anchor(dc, n=n)
+    block, hid, _ = d.draft_block(kvs, torch.from_numpy(anchors).to(DEV), bl, hidden=True)
     torch.cuda.synchronize()
     wn = weights_np(w)
-    orc = O.draft_block(dc, wn, [oracle_cache(dc, ctx)], [int(anchors[0])], bl, conv=_conv_np(conv))
-    g = np32(hid).reshape(dc.n_layers, bl, -1)
+    cn = _conv_np(conv)
+    orc = O.draft_block(dc, wn, [oracle_cache(dc, c) for c in ctxs], [int(a) for a in anchors], bl,
+                        conv=cn)
+    g = np32(hid).reshape(dc.n_layers, n * bl, -1)
     say("  plain: " + " ".join(f"{e:.2e}" for e in hidden_errs(g, orc["hidden"])))
     assert_hidden(g, orc["hidden"], what="conv draft")
     assert_hidden(g, orc["hidden"], what="conv draft", tol=TIGHT_TOL)
@@ -116,10 +124,10 @@ def _draft_with_convs(dc, S, gs, bl=None, gains="random"):
         assert_tokens(block.cpu().numpy(), orc, what="conv draft")
     # removing the convs gives the plain draft back
     d.set_conv(None)
-    block2, hid2, _ = d.draft_block([kv], torch.from_numpy(anchors).to(DEV), bl, hidden=True)
+    block2, hid2, _ = d.draft_block(kvs, torch.from_numpy(anchors).to(DEV), bl, hidden=True)
     torch.cuda.synchronize()
-    orc2 = O.draft_block(dc, wn, [oracle_cache(dc, ctx)], [int(anchors[0])], bl)
-    assert_hidden(np32(hid2).reshape(dc.n_layers, bl, -1), orc2["hidden"], what="plain draft",
+    orc2 = O.draft_block(dc, wn, [oracle_cache(dc, c) for c in ctxs], [int(a) for a in anchors], bl)
+    assert_hidden(np32(hid2).reshape(dc.n_layers, n * bl, -1), orc2["hidden"], what="plain draft",
                   tol=TIGHT_TOL)
     d.close()
 
@@ -131,6 +139,27 @@ def test_draft_with_convs_tiny():
 
 def test_draft_with_convs_tiny_empty_context_short_block():
     _draft_with_convs(CONFIGS[0].shrink(n_layers=2, index=94), 0, 4, bl=3)
+
+
+def test_draft_with_convs_mid_shape_one_sequence():
+    # 16 rows: the convs fused into the GEMMs' finishers
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024, vocab=4096,
+                           index=93)
+    _draft_with_convs(dc, 300, 16)
+
+
+def test_draft_with_convs_mid_shape_two_sequences():
+    # 32 rows: the convs as separate kernels
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024, vocab=4096,
+                           index=93)
+    _draft_with_convs(dc, [300, 45], 16)
+
+
+def test_draft_with_convs_mid_shape_short_block_fused():
+    # 5 rows in one tile; group size 32
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024, vocab=4096,
+                           index=93)
+    _draft_with_convs(dc, 77, 32, bl=5)
 
 
 def test_draft_with_convs_qwen_shape_full_size():
