@@ -895,12 +895,15 @@ __device__ __forceinline__ void wait_vm_slots(int slots_after) {
   }
 }
 
-template <int R, int UB, bool LO, class Epi>
+// R ring slots per wave; KSL the largest K slice the activation buffer holds
+// (the slices of the short products leave room for a deeper ring)
+template <int R, int UB, bool LO, class Epi, int KSL = kSliceMax>
 __global__ void __launch_bounds__(kSW * 64)
 stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* __restrict__ part) {
   static_assert(R >= 2 && R - 1 <= 3, "slots in flight handled by wait_vm_slots");
   static_assert(kItemK == 256, "ring_read8 covers 8 k steps per slot");
-  __shared__ __attribute__((aligned(16))) u32x4 As[kSliceMax / 32][2][64];  // [k step][hi, lo][lane]
+  static_assert(KSL * 64 + kSW * R * kItem <= 160 * 1024, "activation slice and ring fit in LDS");
+  __shared__ __attribute__((aligned(16))) u32x4 As[KSL / 32][2][64];  // [k step][hi, lo][lane]
   __shared__ __attribute__((aligned(16))) uint8_t ring[kSW][R][kItem];
   const int lane = threadIdx.x & 63;
   // wave-uniform in a scalar register: the matrix and segment choices below
@@ -946,7 +949,7 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
   // fragments w, w + kSW, ... (each one k step, hi or lo); every load is
   // issued before the first store
   {
-    constexpr int PER = kSliceMax / 32 * 2 / kSW;
+    constexpr int PER = KSL / 32 * 2 / kSW;
     u32x4 v[PER];
     const int m = lane & 15;
     const bool mv = m < a.M;
@@ -973,7 +976,7 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
         v[u] = *reinterpret_cast<const u32x4*>(a.seg[sg] + row + (k - sg * a.seg_k));
       }
     }
-    // steps past the slice land in unused slots (fr / 2 < kSliceMax / 32)
+    // steps past the slice land in unused slots (fr / 2 < KSL / 32)
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int fr = w + u * kSW, hl = fr & 1;
@@ -1319,8 +1322,14 @@ template <class Epi, bool LO>
 hipError_t launch_stream(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, int ks,
                          const SplitWs& ws, hipStream_t st) {
   const int kc = a.K / ks;
-  hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, LO, Epi>), dim3(stream_grid(ks)),
-                     dim3(kSW * 64), 0, st, a, ep, n_vcols, ks, kc, ws.part);
+  // slices of at most 512 k (the short products) leave LDS for a fourth ring
+  // slot per wave: three slots in flight instead of two
+  if (kc <= kSliceMax / 2)
+    hipLaunchKernelGGL((stream_gemm<kStreamRing + 1, kStreamBatch, LO, Epi, kSliceMax / 2>),
+                       dim3(stream_grid(ks)), dim3(kSW * 64), 0, st, a, ep, n_vcols, ks, kc, ws.part);
+  else
+    hipLaunchKernelGGL((stream_gemm<kStreamRing, kStreamBatch, LO, Epi>), dim3(stream_grid(ks)),
+                       dim3(kSW * 64), 0, st, a, ep, n_vcols, ks, kc, ws.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((stream_finish<Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, ks,
