@@ -15,6 +15,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kMaxSeqs = 64;
+constexpr int kMaxHeadDim = 128;  // the largest head size the library accepts
 
 __device__ __forceinline__ float bf2f(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);

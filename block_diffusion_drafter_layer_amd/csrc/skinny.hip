@@ -74,17 +74,24 @@ struct EpiQKV {
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) {
     const int qd = p.Hq * p.hd, kvd = p.Hkv * p.hd;
+    // the three matrix pointers are read as values first: a choice between
+    // the fields' addresses (what the compiler would otherwise form from the
+    // branches below) makes it copy the whole argument block to scratch
+    const bf16_t* wq = p.wq;
+    const bf16_t* wk = p.wk;
+    const bf16_t* wv = p.wv;
+    asm volatile("" : "+s"(wq), "+s"(wk), "+s"(wv));
     if (vc < qd) {
       int h = vc / p.hd, d = paired_dim(vc % p.hd, p.hd);
-      return p.wq + (size_t)(h * p.hd + d) * p.D;
+      return wq + (size_t)(h * p.hd + d) * p.D;
     }
     vc -= qd;
     if (vc < kvd) {
       int h = vc / p.hd, d = paired_dim(vc % p.hd, p.hd);
-      return p.wk + (size_t)(h * p.hd + d) * p.D;
+      return wk + (size_t)(h * p.hd + d) * p.D;
     }
     vc -= kvd;
-    return p.wv + (size_t)vc * p.D;
+    return wv + (size_t)vc * p.D;
   }
   // row r8 of the 8-column group starting at vc8 (a multiple of 8): the
   // matrix and head follow from vc8 alone
@@ -108,10 +115,21 @@ struct EpiQKV {
     // load that every iteration waits for behind the previous iteration's
     // stores)
     __shared__ int r_pos[ROWS];
-    for (int ml = threadIdx.x; ml < ROWS; ml += blockDim.x) {
-      const int m = m0 + ml;
-      if (m < M) r_pos[ml] = seq_len(p.seqs, m / p.Bl) + m % p.Bl;
+    // the rotation frequencies once per call (an fp64 exp2 per element would
+    // cost more than the tall path's whole k loop)
+    __shared__ double inv_f[kMaxHeadDim / 2];
+    // sequences walked with a uniform index: a per-lane index into the
+    // sequence table would make the compiler copy the whole table (kernel
+    // arguments) into per-lane scratch memory
+    const int s_end = (min(M, m0 + ROWS) + p.Bl - 1) / p.Bl;
+    for (int sq = m0 / p.Bl; sq < s_end; ++sq) {
+      const int len = seq_len(p.seqs, sq);
+      const int ml = sq * p.Bl - m0 + (int)threadIdx.x;
+      if (threadIdx.x < (unsigned)p.Bl && ml >= 0 && ml < ROWS && m0 + ml < M)
+        r_pos[ml] = len + (int)threadIdx.x;
     }
+    for (int d = threadIdx.x; d < p.hd / 2; d += blockDim.x)
+      inv_f[d] = rope_inv_freq(d, p.hd, p.log2_theta);
     __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
@@ -128,7 +146,7 @@ struct EpiQKV {
         const int h = vcl / p.hd;
         const int d = ((vcl % p.hd) >> 1) + j;  // group t covers dims 8t+j
         float cs, sn;
-        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        rope_cs_inv(pos, inv_f[d], cs, sn);
         const float o1 = x1 * cs - x2 * sn;
         const float o2 = x2 * cs + x1 * sn;
         if (is_q) {
@@ -275,13 +293,27 @@ struct EpiLM {
       if (p.logits && v < p.V) p.logits[(size_t)m * p.V + v] = z;
     }
     __syncthreads();
-    for (int ml = threadIdx.x; ml < ROWS && m0 + ml < M; ml += blockDim.x) {
+    // eight threads per row, thread q taking columns q, q + 8, ... (the
+    // eight rows and eight column offsets of a wave's reads fall in distinct
+    // banks for any row pitch of 8 mod 64 words), then a max over the eight
+    constexpr int TPR = 8;
+    static_assert(ROWS * TPR % 64 == 0, "whole waves per pass");
+    for (int e0 = 0; e0 < ROWS * TPR; e0 += blockDim.x) {
+      const int e = e0 + threadIdx.x;
+      const int ml = e / TPR, q = e % TPR;
+      const bool live = e < ROWS * TPR && m0 + ml < M;
       uint64_t best = 0;
-      for (int c = 0; c < VC; ++c) {
-        const int v = vc0 + c;
-        if (v < p.V) best = umax64(best, argmax_key(tile[ml][c], (uint32_t)v));
+      if (live)
+        for (int c = q; c < VC; c += TPR) {
+          const int v = vc0 + c;
+          if (v < p.V) best = umax64(best, argmax_key(tile[ml][c], (uint32_t)v));
+        }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) {
+        const uint64_t other = __shfl_xor(best, o, kWave);
+        best = umax64(best, other);
       }
-      p.part[(size_t)(vc0 / VC) * M + m0 + ml] = best;
+      if (live && q == 0) p.part[(size_t)(vc0 / VC) * M + m0 + ml] = best;
     }
   }
 };
@@ -1344,12 +1376,11 @@ bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
 }
 
 // A draft epilogue on the tiled MFMA GEMM, for batches of more than 64
-// rows: the weights are read once per 256-row tile instead of once per
-// 64-row block. The activations' bf16 hi and lo halves are the A operand's
-// two k segments against the weight rows read twice (B's k wraps at K), so
-// one GEMM over 2K gives hi.W + lo.W. The slice's RMSNorm row scales come
-// from the producer's per-32-column sums of x^2, then the epilogue runs on
-// the 64-row slice in place.
+// rows: the weights are read once per 128-row tile instead of once per
+// 64-row block. The activations' bf16 hi and lo halves are stacked in the
+// tile's A rows (hi.W + lo.W summed in the epilogue). The slice's RMSNorm
+// row scales come from the producer's per-32-column sums of x^2, then the
+// epilogue runs on the 64-row slice in place.
 template <class E>
 struct EpiTiled {
   struct P {
@@ -1367,16 +1398,31 @@ struct EpiTiled {
     float* tile = const_cast<float*>(C);
     float* rs = tile + kSlice * ld;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    for (int r = w; r < kSlice; r += nw) {
-      float s = 0.f;
-      const int m = m0 + r;
-      if (p.ssq && m < M) {
+    // a wave's rows at once: the first 128 partial sums of each of its rows
+    // are requested before any is added (one memory latency per slice, not
+    // one per row)
+    constexpr int kRowsAtOnce = 8;
+    for (int r0 = 0; r0 < kSlice; r0 += nw * kRowsAtOnce) {
+      float v[kRowsAtOnce][2];
+      const float* q[kRowsAtOnce];
+      bool ok[kRowsAtOnce];
+#pragma unroll
+      for (int t = 0; t < kRowsAtOnce; ++t) {
+        const int r = r0 + w + t * nw, m = m0 + r;
+        ok[t] = p.ssq && r < kSlice && m < M;
         const int mi = (m / p.a_group) * p.a_stride + p.a_off + m % p.a_group;
-        const float* q = p.ssq + (size_t)mi * p.ssq_ld;
-        s = strided_sum(q, p.ssq_ld, lane, 64);
-        s = wave_sum(s);
+        q[t] = ok[t] ? p.ssq + (size_t)mi * p.ssq_ld : nullptr;
+        v[t][0] = ok[t] && lane < p.ssq_ld ? q[t][lane] : 0.f;
+        v[t][1] = ok[t] && lane + 64 < p.ssq_ld ? q[t][lane + 64] : 0.f;
       }
-      if (lane == 0) rs[r] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
+#pragma unroll
+      for (int t = 0; t < kRowsAtOnce; ++t) {
+        const int r = r0 + w + t * nw;
+        float s = v[t][0] + v[t][1];
+        if (ok[t] && p.ssq_ld > 128) s += strided_sum(q[t], p.ssq_ld, 128 + lane, 64);
+        s = wave_sum(s);
+        if (lane == 0 && r < kSlice) rs[r] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
+      }
     }
     __syncthreads();
     E::template run<kSlice, BN, BN + 8>(p.ep, reinterpret_cast<float (*)[BN + 8]>(tile), rs, n0, m0, M);
@@ -1389,15 +1435,17 @@ template <class Epi>
 hipError_t launch_tall(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const GemmWs& gw,
                        hipStream_t st) {
   GemmA g;
-  g.seg[0] = a.xh;
-  g.seg[1] = a.xl;
-  for (int i = 2; i < kMaxFeat; ++i) g.seg[i] = a.xh;
-  g.ld = a.lda; g.seg_k = a.K; g.M = a.M; g.K = 2 * a.K; g.b_k = a.K;
+  for (int i = 0; i < kMaxFeat; ++i) g.seg[i] = a.xh;
+  g.ld = a.lda; g.seg_k = a.K; g.M = a.M; g.K = a.K; g.b_k = a.K;
+  g.stack = 1;
+  // both halves have the same row pitch; the offset between the two buffers
+  // in elements (both are 2-byte aligned)
+  g.lo_off = ((intptr_t)a.xl - (intptr_t)a.xh) / (intptr_t)sizeof(bf16_t);
   g.a_group = a.a_group; g.a_stride = a.a_stride; g.a_off = a.a_off;
   typename EpiTiled<Epi>::P p;
   p.ep = ep; p.ssq = a.ssq; p.ssq_ld = a.ssq_ld; p.K = a.K; p.eps = a.eps;
   p.a_group = a.a_group; p.a_stride = a.a_stride; p.a_off = a.a_off;
-  // the draft's few-tile products (o_proj, down at 512 rows: 32 tiles) split
+  // the draft's few-tile products (o_proj, down at 512 rows: 64 tiles) split
   // K up to 8 ways, down to 512 k per split
   return launch_tiled<kTallBN, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 512);
 }

@@ -32,8 +32,12 @@
 // batches too tall for the weight-streaming kernels (skinny.hip). The A
 // operand may be read through segments (k in [j*seg_k, (j+1)*seg_k) reads
 // seg[j]) and a row map; B rows are Epi::wrow(p, n) and their k index wraps
-// at b_k, so a bf16 hi/lo pair of activations becomes one GEMM over
-// [hi | lo] x [W | W].
+// at b_k. A bf16 hi/lo pair of activations is multiplied "stacked": the
+// tile's upper 128 A rows are the hi halves of 128 output rows and its lower
+// 128 the lo halves of the same rows, against one B tile, and the epilogue
+// adds the two halves. Each B tile is then read once per 128 output rows
+// (the alternative, [hi | lo] x [W | W] over 2K, reads it twice per 256 rows
+// with the two reads K apart, which no cache keeps).
 #pragma once
 #include "common.h"
 #include "launch.h"
@@ -67,6 +71,11 @@ struct GemmA {
   int b_k;         // B's k extent: B's k index is k for k < b_k, k - b_k above (K <= 2 b_k)
   // output row m reads A row (m / a_group) * a_stride + a_off + m % a_group
   int a_group, a_stride, a_off;
+  // stacked hi/lo (stack = 1): the tile holds BM / 2 output rows; its A rows
+  // BM / 2 .. BM - 1 repeat rows 0 .. BM / 2 - 1 at element offset lo_off
+  // (the lo halves' buffer minus the hi halves')
+  int stack = 0;
+  int64_t lo_off = 0;
 };
 
 // A read in place: row m is row m, B's k index is k
@@ -152,28 +161,26 @@ __device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint
 template <int N>
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(DFL_VM(N)); }
 
-// Workgroup -> (tile, split). With a multiple of 8 tiles, XCD x (workgroup id
-// % 8) takes a contiguous chunk of tiles, walked in groups of 4 tile rows
-// column by column, so the workgroups an XCD runs share A row blocks and B
-// column blocks through its L2; the S splits of a tile are consecutive on
-// that XCD.
-__device__ __forceinline__ void tile_of(int id, int tm, int tn, int S, int& rt, int& ct, int& s) {
+// Workgroup -> (tile, split). The tile count is padded to a multiple of 8
+// (the launch's grid covers the padding; those workgroups return at once).
+// XCD x (workgroup id % 8) takes a contiguous chunk of tiles, walked in
+// groups of 4 tile rows column by column, so the workgroups an XCD runs at
+// one time share A row blocks and B column blocks through its L2; the S
+// splits of a tile are consecutive on that XCD. Returns false for padding.
+__device__ __forceinline__ bool tile_of(int id, int tm, int tn, int S, int& rt, int& ct, int& s) {
   const int nt = tm * tn;
-  int t;
-  if ((nt & 7) == 0) {
-    const int local = id >> 3;
-    s = local % S;
-    t = (id & 7) * (nt >> 3) + local / S;
-  } else {
-    s = id % S;
-    t = id / S;
-  }
+  const int nt8 = (nt + 7) & ~7;
+  const int local = id >> 3;
+  s = local % S;
+  const int t = (id & 7) * (nt8 >> 3) + local / S;
+  if (t >= nt) return false;
   constexpr int GR = 4;
   const int g = t / (GR * tn);
   const int rows = min(GR, tm - g * GR);
   const int i = t - g * GR * tn;
   rt = g * GR + i % rows;
   ct = i / rows;
+  return true;
 }
 
 template <int BN, class Epi>
@@ -196,10 +203,12 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WGN, wn = w % WGN;
-  const int tm = (a.M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  constexpr int BMH = BM / 2;
+  const int bm_out = a.stack ? BMH : BM;  // output rows per tile
+  const int tm = (a.M + bm_out - 1) / bm_out, tn = (N + BN - 1) / BN;
   int rt, ct, sidx;
-  tile_of(blockIdx.x, tm, tn, sp.S, rt, ct, sidx);
-  const int m0 = rt * BM, n0 = ct * BN;
+  if (!tile_of(blockIdx.x, tm, tn, sp.S, rt, ct, sidx)) return;
+  const int m0 = rt * bm_out, n0 = ct * BN;
   const int KT_all = a.K / BK;
   const int kt_per = (KT_all + sp.S - 1) / sp.S;
   const int kt0 = sidx * kt_per;
@@ -217,10 +226,12 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
 #pragma unroll
   for (int q = 0; q < kLoadsA; ++q) {
     const int b = w + kWaves * q;
-    int m = m0 + 8 * b + lrow;
+    const int r = 8 * b + lrow;
+    const bool lo = a.stack && r >= BMH;
+    int m = m0 + (a.stack ? r % BMH : r);
     m = m < a.M ? m : a.M - 1;
     m = (m / a.a_group) * a.a_stride + a.a_off + m % a.a_group;
-    aoff[q] = (int64_t)m * a.ld + lchunk(b);
+    aoff[q] = (int64_t)m * a.ld + lchunk(b) + (lo ? a.lo_off : 0);
   }
 #pragma unroll
   for (int q = 0; q < kLoadsBMax; ++q) {
@@ -349,33 +360,67 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
     if (*arrived != sp.S - 1) return;
     if (tid == 0) __hip_atomic_store(sp.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // split by split, a row block's loads of a split's partial all issued
+    // before its adds (the loop over splits outermost, so that the loads of
+    // the next blocks can go out under the adds of this one)
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        f32x16 sum;
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sum[v] = 0.f;
-        for (int s = 0; s < sp.S; ++s) {
-          const float* src = sp.part + ((size_t)tile * sp.S + s) * (BM * BN);
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int s = 0; s < sp.S; ++s) {
+      const float* src = sp.part + ((size_t)tile * sp.S + s) * (BM * BN);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(
+      for (int i = 0; i < TI; ++i) {
+        f32x4 v[TJ][4];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[j][q] = *reinterpret_cast<const f32x4*>(
                 src + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4);
-            sum[4 * q] += v[0];
-            sum[4 * q + 1] += v[1];
-            sum[4 * q + 2] += v[2];
-            sum[4 * q + 3] += v[3];
-          }
-        }
-        acc[i][j] = sum;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j][q][e];
       }
+    }
   }
 
   // epilogue: 64-row slices through LDS
   constexpr int CLD = BN + 8;
   float* C = reinterpret_cast<float*>(smem);
   __syncthreads();  // every wave is done with the ring
+  if (a.stack) {
+    // slice sl: the hi rows' products are stored, then the lo rows' added
+    // (each element has one writer per phase)
+#pragma unroll
+    for (int sl = 0; sl < BMH / kSlice; ++sl) {
+#pragma unroll
+      for (int ph = 0; ph < 2; ++ph) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int r0 = wm * WM + i * 32;
+          if (r0 / BMH != ph || (r0 % BMH) / kSlice != sl) continue;
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = r0 % kSlice + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+              float& c = C[r * CLD + wn * WN + j * 32 + fr];
+              c = ph ? c + acc[i][j][v] : acc[i][j][v];
+            }
+        }
+        __syncthreads();
+      }
+      Epi::template run<BN>(p, C, CLD, m0 + sl * kSlice, n0, a.M);
+      __syncthreads();
+    }
+    return;
+  }
 #pragma unroll
   for (int sl = 0; sl < BM / kSlice; ++sl) {
 #pragma unroll
@@ -396,12 +441,12 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   }
 }
 
-// Split count: when the tiles are a multiple of 8 (so the splits of a tile
-// share an XCD), K is split while the doubled grid still fits one workgroup
+// Split count: K is split while the doubled grid still fits one workgroup
 // per CU and each split keeps at least min_k of K (its prologue and epilogue
-// are then a small part of it).
+// are then a small part of it). The splits of a tile run on one XCD
+// (tile_of), which keeps their partials in one L2; the counter's
+// release/acquire does not depend on that placement.
 static int choose_split(int tiles, int K, int max_split, int min_k) {
-  if (tiles % 8) return 1;
   int S = 1;
   while (2 * S <= max_split && tiles * 2 * S <= 256 && K / (2 * S) >= min_k) S *= 2;
   return S;
@@ -412,7 +457,8 @@ static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, 
                                hipStream_t st, int max_split = kGemmMaxSplit, int min_k = 1024) {
   // whole 64-wide k stages, none straddling an A segment or B's wrap
   if (a.K % BK || a.seg_k % BK || a.b_k % BK) return hipErrorInvalidValue;
-  const int tiles = ((a.M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int bm_out = a.stack ? BM / 2 : BM;
+  const int tiles = ((a.M + bm_out - 1) / bm_out) * ((N + BN - 1) / BN);
   GemmSplit sp;
   sp.S = choose_split(tiles, a.K, max_split, min_k);
   if (sp.S > 1 && (!ws.part || !ws.ctr || (size_t)tiles * sp.S * BM * BN > ws.part_floats ||
@@ -420,8 +466,9 @@ static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, 
     sp.S = 1;
   sp.part = ws.part;
   sp.ctr = ws.ctr;
-  hipLaunchKernelGGL((ctx_gemm<BN, Epi>), dim3(tiles * sp.S), dim3(TileCfg<BN>::W * 64), 0, st, a, p,
-                     N, sp);
+  const int grid = ((tiles + 7) & ~7) * sp.S;  // tile_of's padding to whole XCD chunks
+  hipLaunchKernelGGL((ctx_gemm<BN, Epi>), dim3(grid), dim3(TileCfg<BN>::W * 64), 0, st, a, p, N,
+                     sp);
   return hipGetLastError();
 }
 
