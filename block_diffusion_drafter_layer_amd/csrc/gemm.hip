@@ -119,31 +119,48 @@ struct EpiInject {
       }
     }
     __syncthreads();
-    // pair slots: slot k covers virtual columns g*PW + o and g*PW + o + PW/2
-    // (g = k / hw, o = k % hw); K pairs get RoPE, V pairs are two plain
-    // columns. Consecutive threads take consecutive slots of one row.
-    for (int e = threadIdx.x; e < kSlice * (BN / 2); e += blockDim.x) {
-      const int r = e / (BN / 2), k = e % (BN / 2);
+    // K: quads of pair slots (slot k covers virtual columns g*PW + o and
+    // g*PW + o + PW/2, g = k / hw, o = k % hw); a quad is four consecutive
+    // dims of one head (hw is a multiple of 4), rotated and stored as two
+    // 8-byte pieces of the position's row. Consecutive threads take
+    // consecutive quads of one row.
+    const int hd2 = p.hd >> 1;
+    for (int e = threadIdx.x; e < kSlice * (BN / 8); e += blockDim.x) {
+      const int r = e / (BN / 8), k = 4 * (e % (BN / 8));
       const int g = k / hw, o = k - g * hw;
       const int c1 = g * PW + o, c2 = c1 + hw;
       const int m = m0 + r;
-      const int pl = col_plane[c1];
-      if (m >= M || pl < 0) continue;
-      const int pos = p.pos0 + m;
-      const float x1 = C[r * ld + c1], x2 = C[r * ld + c2];
-      const int dv = col_dim[c1], d = dv & (kVFlag - 1);
-      if (!(dv & kVFlag)) {
+      const int pl = col_plane[c1], dv = col_dim[c1];
+      if (m >= M || pl < 0 || (dv & kVFlag)) continue;
+      const int pos = p.pos0 + m, d = dv;
+      float o1[4], o2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
         float cs, sn;
-        rope_cs_inv(pos, col_inv[c1], cs, sn);
-        bf16_t* kp = p.kv + (size_t)pl * plane + (size_t)pos * p.hd;
-        kp[d] = f2bf(x1 * cs - x2 * sn);
-        kp[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
+        rope_cs_inv(pos, col_inv[c1 + i], cs, sn);
+        const float x1 = C[r * ld + c1 + i], x2 = C[r * ld + c2 + i];
+        o1[i] = x1 * cs - x2 * sn;
+        o2[i] = x2 * cs + x1 * sn;
+      }
+      bf16_t* kp = p.kv + (size_t)pl * plane + (size_t)pos * p.hd;
+      *reinterpret_cast<uint2*>(kp + d) = make_uint2(f2bf2(o1[0], o1[1]), f2bf2(o1[2], o1[3]));
+      *reinterpret_cast<uint2*>(kp + d + hd2) = make_uint2(f2bf2(o2[0], o2[1]), f2bf2(o2[2], o2[3]));
+    }
+    // V (dim-major planes: a dim's positions are contiguous): four
+    // consecutive rows of one column per thread, one 8-byte store where the
+    // position allows; sixteen threads cover a column's 64 rows
+    for (int e = threadIdx.x; e < (kSlice / 4) * BN; e += blockDim.x) {
+      const int c = e / (kSlice / 4), r = 4 * (e % (kSlice / 4));
+      const int pl = col_plane[c], dv = col_dim[c];
+      const int m = m0 + r;
+      if (m >= M || pl < 0 || !(dv & kVFlag)) continue;
+      const int pos = p.pos0 + m;
+      bf16_t* vp = p.kv + (size_t)pl * plane + (size_t)(dv & (kVFlag - 1)) * p.cap + pos;
+      const float* x = C + r * ld + c;
+      if (m + 4 <= M && (pos & 3) == 0) {
+        *reinterpret_cast<uint2*>(vp) = make_uint2(f2bf2(x[0], x[ld]), f2bf2(x[2 * ld], x[3 * ld]));
       } else {
-        bf16_t* vp = p.kv + (size_t)pl * plane + pos;
-        vp[(size_t)d * p.cap] = f2bf(x1);
-        const int pl2 = col_plane[c2];
-        if (pl2 >= 0)
-          p.kv[(size_t)pl2 * plane + pos + (size_t)(col_dim[c2] & (kVFlag - 1)) * p.cap] = f2bf(x2);
+        for (int i = 0; i < 4 && m + i < M; ++i) vp[i] = f2bf(x[i * ld]);
       }
     }
   }
