@@ -26,6 +26,7 @@ struct EpiFuse {
     int n_tiles;
   };
   __device__ static const bf16_t* wrow(const P& p, int n) { return p.w + (size_t)n * p.K; }
+  __device__ static void prologue(const P&, int, int, int) {}
   // rows [m0, m0 + kSlice) of the tile starting at column n0, C[r][c] at C[r * ld + c]
   template <int BN>
   __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
@@ -96,6 +97,7 @@ struct EpiInject {
     const InjectCol c = inject_col(n, p.Hkv, p.hd);
     return (c.is_k ? p.wk[c.layer] : p.wv[c.layer]) + (size_t)(c.head * p.hd + c.dim) * p.K;
   }
+  __device__ static void prologue(const P&, int, int, int) {}
   static constexpr int kVFlag = 1 << 16;  // column-table dim entries of V columns
   template <int BN>
   __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {

@@ -283,19 +283,11 @@ struct EpiLM {
   template <int ROWS, int VC, int LD = VC + 1>
   __device__ static void run(const P& p, float (*tile)[LD], const float* rs,
                              int vc0, int m0, int M) {
-    for (int e = threadIdx.x; e < ROWS * VC; e += blockDim.x) {
-      const int ml = e / VC, c = e % VC;
-      const int m = m0 + ml;
-      if (m >= M) continue;
-      const int v = vc0 + c;
-      const float z = tile[ml][c] * rs[ml];
-      tile[ml][c] = z;
-      if (p.logits && v < p.V) p.logits[(size_t)m * p.V + v] = z;
-    }
-    __syncthreads();
-    // eight threads per row, thread q taking columns q, q + 8, ... (the
-    // eight rows and eight column offsets of a wave's reads fall in distinct
-    // banks for any row pitch of 8 mod 64 words), then a max over the eight
+    // one pass: the row scale applied as the keys are formed (and the
+    // optional logits written); eight threads per row, thread q taking
+    // columns q, q + 8, ... (the eight rows and eight column offsets of a
+    // wave's reads fall in distinct banks for any row pitch of 8 mod 64
+    // words), then a max over the eight
     constexpr int TPR = 8;
     static_assert(ROWS * TPR % 64 == 0, "whole waves per pass");
     for (int e0 = 0; e0 < ROWS * TPR; e0 += blockDim.x) {
@@ -303,11 +295,17 @@ struct EpiLM {
       const int ml = e / TPR, q = e % TPR;
       const bool live = e < ROWS * TPR && m0 + ml < M;
       uint64_t best = 0;
-      if (live)
+      if (live) {
+        const float sc = rs[ml];
+        float* lrow = p.logits ? p.logits + (size_t)(m0 + ml) * p.V : nullptr;
         for (int c = q; c < VC; c += TPR) {
           const int v = vc0 + c;
-          if (v < p.V) best = umax64(best, argmax_key(tile[ml][c], (uint32_t)v));
+          if (v >= p.V) continue;
+          const float z = tile[ml][c] * sc;
+          if (lrow) lrow[v] = z;
+          best = umax64(best, argmax_key(z, (uint32_t)v));
         }
+      }
 #pragma unroll
       for (int o = 1; o < TPR; o <<= 1) {
         const uint64_t other = __shfl_xor(best, o, kWave);
@@ -1378,9 +1376,10 @@ bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
 // A draft epilogue on the tiled MFMA GEMM, for batches of more than 64
 // rows: the weights are read once per 128-row tile instead of once per
 // 64-row block. The activations' bf16 hi and lo halves are stacked in the
-// tile's A rows (hi.W + lo.W summed in the epilogue). The slice's RMSNorm
-// row scales come from the producer's per-32-column sums of x^2, then the
-// epilogue runs on the 64-row slice in place.
+// tile's A rows (hi.W + lo.W summed in the epilogue). The RMSNorm row
+// scales of the tile's rows come from the producer's per-32-column sums of
+// x^2, read in the GEMM's prologue; the epilogue runs on each 64-row slice
+// in place.
 template <class E>
 struct EpiTiled {
   struct P {
@@ -1391,40 +1390,51 @@ struct EpiTiled {
     int a_group, a_stride, a_off;  // output row -> input row (as SkinnyA)
   };
   __device__ static const bf16_t* wrow(const P& p, int n) { return E::wrow(p.ep, n); }
-  // C: the slice, row pitch BN + 8 (the tiled kernel's); 64 floats of LDS
-  // after it hold the row scales
+  // the RMSNorm row scales of every row of the tile, indexed by row % 256
+  __device__ static float* rs_buf() {
+    __shared__ float rs[256];
+    return rs;
+  }
+  // Row scales of the tile's rows, computed once per workgroup before its
+  // main loop: eight threads per row, each summing every eighth pair of the
+  // row's partial sums (all requested before any is added), then three lane
+  // exchanges. (Per 64-row slice in the epilogue, with a wave reduction per
+  // row, this cost more than the rest of the epilogue: the loads wait behind
+  // the other workgroups' operand streams.)
+  __device__ static void prologue(const P& p, int m0, int rows, int M) {
+    float* rs = rs_buf();
+    constexpr int TPR = 8;
+    for (int e0 = 0; e0 < rows * TPR; e0 += blockDim.x) {
+      const int e = e0 + threadIdx.x;
+      const int r = e / TPR, q = e % TPR, m = m0 + r;
+      const bool ok = p.ssq && e < rows * TPR && m < M;
+      float s = 0.f;
+      if (ok) {
+        const int mi = (m / p.a_group) * p.a_stride + p.a_off + m % p.a_group;
+        const float2* row = reinterpret_cast<const float2*>(p.ssq + (size_t)mi * p.ssq_ld);
+        const int n2 = p.ssq_ld >> 1;  // the row holds D / 32 sums, D a multiple of 64
+        for (int c0 = q; c0 < n2; c0 += 8 * TPR) {
+          float2 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int c = c0 + u * TPR;
+            v[u] = row[c < n2 ? c : n2 - 1];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (c0 + u * TPR < n2) s += v[u].x + v[u].y;
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, kWave);
+      if (q == 0 && e < rows * TPR) rs[m & 255] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
+    }
+  }
+  // C: the slice, row pitch BN + 8 (the tiled kernel's)
   template <int BN>
   __device__ static void run(const P& p, const float* C, int ld, int m0, int n0, int M) {
     float* tile = const_cast<float*>(C);
-    float* rs = tile + kSlice * ld;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    // a wave's rows at once: the first 128 partial sums of each of its rows
-    // are requested before any is added (one memory latency per slice, not
-    // one per row)
-    constexpr int kRowsAtOnce = 8;
-    for (int r0 = 0; r0 < kSlice; r0 += nw * kRowsAtOnce) {
-      float v[kRowsAtOnce][2];
-      const float* q[kRowsAtOnce];
-      bool ok[kRowsAtOnce];
-#pragma unroll
-      for (int t = 0; t < kRowsAtOnce; ++t) {
-        const int r = r0 + w + t * nw, m = m0 + r;
-        ok[t] = p.ssq && r < kSlice && m < M;
-        const int mi = (m / p.a_group) * p.a_stride + p.a_off + m % p.a_group;
-        q[t] = ok[t] ? p.ssq + (size_t)mi * p.ssq_ld : nullptr;
-        v[t][0] = ok[t] && lane < p.ssq_ld ? q[t][lane] : 0.f;
-        v[t][1] = ok[t] && lane + 64 < p.ssq_ld ? q[t][lane + 64] : 0.f;
-      }
-#pragma unroll
-      for (int t = 0; t < kRowsAtOnce; ++t) {
-        const int r = r0 + w + t * nw;
-        float s = v[t][0] + v[t][1];
-        if (ok[t] && p.ssq_ld > 128) s += strided_sum(q[t], p.ssq_ld, 128 + lane, 64);
-        s = wave_sum(s);
-        if (lane == 0 && r < kSlice) rs[r] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
-      }
-    }
-    __syncthreads();
+    const float* rs = rs_buf() + (m0 & 255);  // slices start at multiples of 64
     E::template run<kSlice, BN, BN + 8>(p.ep, reinterpret_cast<float (*)[BN + 8]>(tile), rs, n0, m0, M);
   }
 };

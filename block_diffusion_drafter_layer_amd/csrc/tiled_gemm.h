@@ -28,6 +28,11 @@
 // meet in one L2. Nobody waits for anybody, so there is no co-residency
 // requirement.
 //
+// Epi supplies wrow(p, n) (B row n), prologue(p, m0, rows, M) (run by every
+// workgroup after its first loads are issued; it may read memory and write
+// LDS of its own for the epilogue) and run<BN>(p, C, ld, m0, n0, M) (a
+// 64-row slice of the tile in LDS).
+//
 // Users: the prefill fusion and injection (gemm.hip) and the draft GEMMs of
 // batches too tall for the weight-streaming kernels (skinny.hip). The A
 // operand may be read through segments (k in [j*seg_k, (j+1)*seg_k) reads
@@ -293,8 +298,11 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   // t + 1 is in LDS, and its first fragments are read under the MFMAs of
   // stage t's last step. (A plain barrier: a fence would also wait for loads
   // still in flight.)
+  // the epilogue's own inputs (e.g. row scales) are requested here, so that
+  // their latency overlaps the first stage's loads instead of the end
+  if (KT > 0) issue(0);
+  Epi::prologue(p, m0, bm_out, a.M);
   if (KT > 0) {
-    issue(0);
     wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     u32x4 f[2][TI + TJ];
