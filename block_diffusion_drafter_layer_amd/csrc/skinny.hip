@@ -289,21 +289,29 @@ struct EpiLM {
     // wave's reads fall in distinct banks for any row pitch of 8 mod 64
     // words), then a max over the eight
     constexpr int TPR = 8;
-    static_assert(ROWS * TPR % 64 == 0, "whole waves per pass");
+    static_assert(ROWS * TPR % 64 == 0 && VC % TPR == 0, "whole waves per pass, whole column strides");
     for (int e0 = 0; e0 < ROWS * TPR; e0 += blockDim.x) {
       const int e = e0 + threadIdx.x;
       const int ml = e / TPR, q = e % TPR;
       const bool live = e < ROWS * TPR && m0 + ml < M;
       uint64_t best = 0;
       if (live) {
+        // every read of the row's columns issued before the first key
+        constexpr int NC = VC / TPR;
         const float sc = rs[ml];
-        float* lrow = p.logits ? p.logits + (size_t)(m0 + ml) * p.V : nullptr;
-        for (int c = q; c < VC; c += TPR) {
-          const int v = vc0 + c;
-          if (v >= p.V) continue;
-          const float z = tile[ml][c] * sc;
-          if (lrow) lrow[v] = z;
-          best = umax64(best, argmax_key(z, (uint32_t)v));
+        float z[NC];
+#pragma unroll
+        for (int i = 0; i < NC; ++i) z[i] = tile[ml][q + i * TPR] * sc;
+        if (p.logits) {
+          float* lrow = p.logits + (size_t)(m0 + ml) * p.V;
+#pragma unroll
+          for (int i = 0; i < NC; ++i)
+            if (vc0 + q + i * TPR < p.V) lrow[vc0 + q + i * TPR] = z[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int v = vc0 + q + i * TPR;
+          if (v < p.V) best = umax64(best, argmax_key(z[i], (uint32_t)v));
         }
       }
 #pragma unroll
@@ -1441,6 +1449,33 @@ struct EpiTiled {
 
 constexpr int kTallBN = 256;
 
+// Products whose epilogue works on 16-column groups of any tile width take
+// 192-wide tiles where that fills the CUs better: at 512 draft rows qkv's
+// 96 tiles of 256 (x 2 splits) leave a quarter of the CUs idle and gate/up's
+// 384 tiles take two rounds of which the second is half empty, while 192-wide
+// tiles give 128 x 2 and 512 (two full rounds).
+template <class E>
+struct TallNarrow {
+  static constexpr bool ok = false;
+};
+template <>
+struct TallNarrow<EpiQKV> {
+  static constexpr bool ok = true;
+};
+template <>
+struct TallNarrow<EpiSwiglu> {
+  static constexpr bool ok = true;
+};
+
+// rounds of workgroups x work per workgroup, for a tile width (stacked hi/lo
+// tiles: 128 output rows)
+double tall_cost(int M, int N, int K, int BN) {
+  const int tiles = ((M + 127) / 128) * ((N + BN - 1) / BN);
+  const int S = choose_split(tiles, K, 8, 512);
+  const int rounds = (((tiles + 7) & ~7) * S + kCUs - 1) / kCUs;
+  return (double)rounds * BN * ((double)K / S);
+}
+
 template <class Epi>
 hipError_t launch_tall(const SkinnyA& a, const typename Epi::P& ep, int n_vcols, const GemmWs& gw,
                        hipStream_t st) {
@@ -1457,6 +1492,10 @@ hipError_t launch_tall(const SkinnyA& a, const typename Epi::P& ep, int n_vcols,
   p.a_group = a.a_group; p.a_stride = a.a_stride; p.a_off = a.a_off;
   // the draft's few-tile products (o_proj, down at 512 rows: 64 tiles) split
   // K up to 8 ways, down to 512 k per split
+  if constexpr (TallNarrow<Epi>::ok) {
+    if (tall_cost(a.M, n_vcols, a.K, 192) < tall_cost(a.M, n_vcols, a.K, kTallBN))
+      return launch_tiled<192, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 512);
+  }
   return launch_tiled<kTallBN, EpiTiled<Epi>>(g, p, n_vcols, gw, st, 8, 512);
 }
 

@@ -1,9 +1,10 @@
 // Dense GEMMs on bf16 MFMA: C[m][n] = sum_k A[m][k] B[n][k] with both operands
 // K-contiguous.
 //
-// Output tiles of 256 x BN (BN = 256 for the fusion, 320 for the injection),
-// eight waves (two per SIMD), each owning a block of 32x32x16 MFMA tiles:
-// 128 x 64 for BN = 256, 64 x 160 for BN = 320. Large tiles keep the global
+// Output tiles of 256 x BN (BN = 256 for the fusion, 320 for the injection,
+// 192 or 256 for the draft's tall products), eight waves (two per SIMD), each
+// owning a block of 32x32x16 MFMA tiles: 128 x 64 for BN = 256, 64 x 160 for
+// BN = 320, 64 x 96 for BN = 192. Large tiles keep the global
 // load traffic at ~30 B/clk per CU at full MFMA rate, half of what the
 // CU's load path sustains (a 256 x 128 tile needs ~47 B/clk and is bound by
 // it). Operands go straight from global memory into LDS
@@ -65,6 +66,10 @@ struct TileCfg<256> {
 template <>
 struct TileCfg<320> {
   static constexpr int W = 8, WGM = 4;
+};
+template <>
+struct TileCfg<192> {
+  static constexpr int W = 8, WGM = 4;  // 64 x 96 per wave
 };
 }  // namespace
 
@@ -132,6 +137,12 @@ __device__ __forceinline__ void frag_wait(u32x4 (&f)[8]) {
                : "n"(N));
 }
 template <int N>
+__device__ __forceinline__ void frag_wait(u32x4 (&f)[5]) {
+  asm volatile("s_waitcnt lgkmcnt(%5)"
+               : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4])
+               : "n"(N));
+}
+template <int N>
 __device__ __forceinline__ void frag_wait(u32x4 (&f)[7]) {
   asm volatile("s_waitcnt lgkmcnt(%7)"
                : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]),
@@ -152,10 +163,8 @@ __device__ __forceinline__ void frag_issue(u32x4 (&f)[TI + TJ], uint32_t a, uint
   }
   ds_frag<0>(f[TI], b);
   ds_frag<4096>(f[TI + 1], b);
-  if constexpr (TJ > 2) {
-    ds_frag<8192>(f[TI + 2], b);
-    ds_frag<12288>(f[TI + 3], b);
-  }
+  if constexpr (TJ > 2) ds_frag<8192>(f[TI + 2], b);
+  if constexpr (TJ > 3) ds_frag<12288>(f[TI + 3], b);
   if constexpr (TJ > 4) ds_frag<16384>(f[TI + 4], b);
 }
 
