@@ -103,6 +103,16 @@ def test_mid_shape_tall_batch():
     _run(dc, [33, 300, 5, 1031, 64, 129], gains="random", logits=True)
 
 
+def test_mid_shape_tall_batch_two_row_tiles():
+    # 13 sequences x 16 rows = 208 draft rows: two stacked hi/lo row tiles of
+    # the tiled GEMM (128 output rows each), the second one partial; qkv and
+    # gate/up take 192-wide tiles (the last gate/up tile ragged: 2048 / 192)
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024,
+                           vocab=4096, index=95)
+    lens = [17, 300, 5, 1031, 64, 129, 0, 2, 777, 45, 512, 33, 96]
+    _run(dc, lens, gains="random", logits=True)
+
+
 def test_mid_shape_tall_batch_ffn_not_a_multiple_of_64():
     # ffn = 1056: the down projection's K is not a whole number of the tiled
     # GEMM's 64-wide k stages, so those 80 rows take the register-streaming
