@@ -768,6 +768,9 @@ dflash_status dflash_append_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   F.w_c = (const bf16_t*)h->w.w_c; F.gain = (const bf16_t*)h->w.ctx_norm; F.eps = c.rms_eps;
   F.out = ctx; F.out_lo = ctx_lo; F.ssq = (float*)(h->ws + h->lay.fuse_ssq); F.y = (float*)(h->ws + h->lay.fuse_y);
   F.split = split_ws(h); F.gemm = gemm_ws(h);
+  // few rows: the fusion's norm moves into the injection's epilogue (the row
+  // scale commutes with the products), which saves the normalisation pass
+  F.norm_in_consumer = T <= kContextRowsStreaming;
   AppendLaunch A{};
   A.ctx = ctx; A.ctx_lo = ctx_lo; A.T = T; A.rps = rows_per_seq; A.D = c.hidden; A.L = c.n_layers;
   A.Hkv = c.n_kv_heads; A.hd = c.head_dim; A.log2_theta = std::log2((double)c.rope_theta);
@@ -776,6 +779,10 @@ dflash_status dflash_append_dev(dflash_handle* h, int32_t n_seqs, dflash_kv* con
     A.wv[i] = (const bf16_t*)h->layers[i].wv;
   }
   A.tau = tau_dev; A.seqs = &seqs; A.split = split_ws(h);
+  if (F.norm_in_consumer) {
+    A.ssq = F.ssq;
+    A.eps = c.rms_eps;
+  }
   hipStream_t st = h->stream;
   hipError_t e = timed(h, ST_FUSE, [&] {
     return T <= kContextRowsStreaming ? launch_fuse_rows(F, st) : launch_fuse(F, st);

@@ -139,6 +139,10 @@ struct FuseLaunch {
   float* ssq;         // [T][ceil(D/256)] (tiled) or [T][D/32] (few rows)
   SplitWs split;
   GemmWs gemm;
+  // few rows only: leave the norm to the consumer - out/out_lo receive the
+  // bf16 hi/lo halves of y * gain (not normalised) and ssq the per-32-column
+  // sums of y^2, from which the consumer's epilogue applies the row scale
+  bool norm_in_consumer = false;
 };
 hipError_t launch_fuse(const FuseLaunch& F, hipStream_t st);        // tiled MFMA GEMM
 hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st);   // few rows: streaming
@@ -173,6 +177,8 @@ struct AppendLaunch {
   const int32_t* tau;  // [n_seqs] device
   const SeqTable* seqs;  // kv bases, capacities, len_dev
   SplitWs split;
+  const float* ssq = nullptr;  // optional [T][D/32] sums of y^2: ctx holds y * gain, not yet normalised
+  float eps = 0.f;
 };
 hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st);
 // len[s] = min(len[s] + tau[s], max_ctx[s]) for s < n_seqs

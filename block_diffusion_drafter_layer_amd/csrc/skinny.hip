@@ -354,9 +354,11 @@ struct EpiFuseRows {
   struct P {
     const bf16_t* w;  // W_c [D][K]
     int K, D;
-    float* y;         // [M][D]
+    float* y;         // [M][D] (or, with yh: not written)
     float* ssq;       // [M][D/32]
     int n_vcols;      // D
+    bf16_t *yh = nullptr, *yl = nullptr;  // optional: hi/lo of y * gain instead of y
+    const bf16_t* gain = nullptr;
   };
   __device__ static const bf16_t* wrow(const P& p, int vc) { return p.w + (size_t)vc * p.K; }
   __device__ static const bf16_t* wrow8(const P& p, int vc8, int r8) {
@@ -371,7 +373,11 @@ struct EpiFuseRows {
       const int m = m0 + ml;
       if (m >= M || vc0 + c >= p.n_vcols) continue;
       const float y = tile[ml][c];
-      p.y[(size_t)m * p.D + vc0 + c] = y;
+      const size_t i = (size_t)m * p.D + vc0 + c;
+      if (p.yh)
+        split_bf16(y * bf2f(p.gain[vc0 + c]), p.yh[i], p.yl[i]);
+      else
+        p.y[i] = y;
       tile[ml][c] = y * y;
     }
     __syncthreads();
@@ -480,7 +486,7 @@ struct EpiAppendRows {
     return p.wv[i] + (size_t)(r - kvd + r8) * p.D;
   }
   template <int ROWS, int VC, int LD = VC + 1>
-  __device__ static void run(const P& p, float (*tile)[LD], const float*, int vc0, int m0,
+  __device__ static void run(const P& p, float (*tile)[LD], const float* rs, int vc0, int m0,
                              int M) {
     const int kvd = p.Hkv * p.hd;
     constexpr int NG = VC / 16;
@@ -513,7 +519,7 @@ struct EpiAppendRows {
       if (vc >= p.n_vcols) continue;
       const size_t plane = (size_t)sd.cap * p.hd;
       const int i = vc / (2 * kvd), r = vc % (2 * kvd);
-      const float x1 = tile[ml][c * 16 + j], x2 = tile[ml][c * 16 + j + 8];
+      const float x1 = tile[ml][c * 16 + j] * rs[ml], x2 = tile[ml][c * 16 + j + 8] * rs[ml];
       if (r < kvd) {
         const int h = r / p.hd, d = ((r % p.hd) >> 1) + j;
         float cs, sn;
@@ -1696,8 +1702,11 @@ hipError_t launch_fuse_rows(const FuseLaunch& F, hipStream_t st) {
   a.seg_k = F.D;
   EpiFuseRows::P p;
   p.w = F.w_c; p.K = F.n_feat * F.D; p.D = F.D; p.y = F.y; p.ssq = F.ssq; p.n_vcols = F.D;
+  if (F.norm_in_consumer) {
+    p.yh = F.out; p.yl = F.out_lo; p.gain = F.gain;
+  }
   hipError_t e = launch_skinny<EpiFuseRows, false>(a, p, F.D, F.split, st);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || F.norm_in_consumer) return e;
   return launch_fuse_normalize(F.out, F.out_lo, F.y, F.ssq, F.D / 32, F.T, F.D, F.gain, F.eps, st);
 }
 
@@ -1714,7 +1723,9 @@ hipError_t launch_inject_rows(const InjectLaunch& I, hipStream_t st) {
 }
 
 hipError_t launch_append_inject(const AppendLaunch& A, hipStream_t st) {
-  SkinnyA a = make_a(A.ctx, A.ctx_lo, A.D, A.T, A.D, nullptr, 0, 0.f);
+  // with ssq the fused rows are y * gain and the RMSNorm's row scale is
+  // applied to the products (it commutes with them)
+  SkinnyA a = make_a(A.ctx, A.ctx_lo, A.D, A.T, A.D, A.ssq, A.D / 32, A.eps);
   EpiAppendRows::P p;
   for (int i = 0; i < kMaxLayers; ++i) {
     p.wk[i] = i < A.L ? A.wk[i] : A.wk[0];

@@ -15,7 +15,9 @@ Two oracles run every round:
     fp64; every layer's hidden state within 3e-2 x RMS;
   * storage model - the rows the library stores rounded to bf16 (the
     host-driven path also hands the fused H_t over as bf16, the
-    device-resident append keeps it unrounded); within TIGHT_TOL x RMS, a
+    device-resident append keeps it unrounded: y * gain as a bf16 hi/lo
+    pair, the norm's row scale applied to the injection's products); within
+    TIGHT_TOL x RMS, a
     regression check of the kernels' own arithmetic.
 The fused rows and the appended K/V are checked against round_bf16 of the
 oracle outside a band around the bf16 rounding midpoints."""
