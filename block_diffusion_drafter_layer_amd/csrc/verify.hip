@@ -53,26 +53,47 @@ row_argmax_part(const float* __restrict__ logits, int V, int splits, uint64_t* _
     part[(size_t)row * splits + split] = umax64(umax64(wb[0], wb[1]), umax64(wb[2], wb[3]));
 }
 
-__global__ void __launch_bounds__(64)
+// One workgroup per sequence. Each row's argmax from its split partials:
+// sixteen threads per row, each taking every sixteenth split (all loads
+// issued before the max), then four lane exchanges. The accepted prefix
+// in one step: a ballot of the rows whose target argmax differs from the
+// next drafted token, the first of them ends it ([Code] section 8: the
+// cumulative product of matches, plus the bonus token).
+__global__ void __launch_bounds__(256)
 greedy_accept(const uint64_t* __restrict__ part, int splits, int Bl,
               const int32_t* __restrict__ block, int32_t* __restrict__ tau,
               int32_t* __restrict__ bonus) {
-  const int s = blockIdx.x, j = threadIdx.x;
+  static_assert(kVerifyMaxSplits <= 64, "four splits per thread");
+  const int s = blockIdx.x, t = threadIdx.x;
   __shared__ int32_t post[64];
-  if (j < Bl) {
+  for (int j0 = 0; j0 < Bl; j0 += 16) {  // wave-uniform
+    const int j = j0 + (t >> 4), q = t & 15;
     uint64_t best = 0;
-    const uint64_t* p = part + (size_t)(s * Bl + j) * splits;
-#pragma unroll 8
-    for (int k = 0; k < splits; ++k) best = umax64(best, p[k]);
-    post[j] = (int32_t)argmax_key_index(best);
+    if (j < Bl) {
+      const uint64_t* p = part + (size_t)(s * Bl + j) * splits;
+      uint64_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = q + 16 * u < splits ? p[q + 16 * u] : 0ull;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) best = umax64(best, v[u]);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) {
+      const uint64_t other = __shfl_xor(best, o, kWave);
+      best = umax64(best, other);
+    }
+    if (j < Bl && q == 0) post[j] = (int32_t)argmax_key_index(best);
   }
   __syncthreads();
-  if (j == 0) {
-    const int32_t* b = block + (size_t)s * Bl;
-    int a = 0;
-    while (a < Bl - 1 && b[a + 1] == post[a]) ++a;
-    tau[s] = a + 1;
-    bonus[s] = post[a];
+  if (t < 64) {
+    // row j < Bl - 1 verifies drafted token j + 1
+    const bool miss = t < Bl - 1 && block[(size_t)s * Bl + t + 1] != post[t];
+    const uint64_t m = __ballot(miss);
+    const int a = m ? __ffsll((unsigned long long)m) - 1 : Bl - 1;
+    if (t == 0) {
+      tau[s] = a + 1;
+      bonus[s] = post[a];
+    }
   }
 }
 
@@ -82,7 +103,7 @@ hipError_t launch_verify_greedy(const VerifyLaunch& P, hipStream_t st) {
                      P.target, P.V, P.splits, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(greedy_accept, dim3(P.n_seqs), dim3(64), 0, st, part, P.splits, P.Bl,
+  hipLaunchKernelGGL(greedy_accept, dim3(P.n_seqs), dim3(256), 0, st, part, P.splits, P.Bl,
                      P.block_ids, P.tau, P.bonus);
   return hipGetLastError();
 }
