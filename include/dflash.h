@@ -113,8 +113,9 @@ typedef struct dflash_weights {
  *   V:              layer i, head g, position p, dim d at
  *       ((2*i + 1)*H + g)*cap*hd + d*cap + p
  * i.e. K is position-major and V dim-major within each head. Positions
- * len .. len+block_size-1 are scratch rows used by dflash_draft_block for the
- * block's own K/V; positions >= len are never part of the context.
+ * >= len are never part of the context; dflash_draft_block writes nothing
+ * into the cache (the block's own K/V stay in the workspace, in fp32). Rows
+ * past max_ctx (cap >= max_ctx + block_size) are never written or read.
  * `len` is host metadata: the number of context positions held.
  */
 typedef struct dflash_kv {
@@ -200,7 +201,8 @@ dflash_status dflash_kv_trim(dflash_handle* h, dflash_kv* kv, int32_t keep_len);
  *             stream after every layer (row s*block_len + r).
  * logits_out: optional device fp32 [n_seqs, block_len-1, vocab].
  * 1 <= n_seqs <= max_seqs; 1 <= block_len <= block_size; each kvs[s]->len is
- * left unchanged (the block's K/V go to scratch rows).
+ * left unchanged and the cache is only read (the block's own K/V are kept in
+ * the workspace in fp32 and enter attention in its merge step).
  */
 dflash_status dflash_draft_block(dflash_handle* h, int32_t n_seqs,
                                  dflash_kv* const* kvs,

@@ -97,7 +97,8 @@ def test_mid_shape_head_dim_128_group_8():
 
 def test_mid_shape_tall_batch():
     # 6 sequences x 16 rows = 96 draft rows: the tiled MFMA GEMMs (hi and lo
-    # activations as two k segments), ragged contexts, logits checked
+    # activations stacked in one partial row tile), ragged contexts, logits
+    # checked
     dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024,
                            vocab=4096, index=93)
     _run(dc, [33, 300, 5, 1031, 64, 129], gains="random", logits=True)
