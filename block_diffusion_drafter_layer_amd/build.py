@@ -35,9 +35,16 @@ def hipcc() -> str:
     return p
 
 
+# per-source additions: attention keeps its MFMA accumulators (the running
+# P.V sums, rescaled by VALU code every chunk) in the VGPR form of the MFMA
+# instructions; in the AGPR form the compiler copied all of them in and out
+# of the accumulation registers around every chunk
+EXTRA_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + FLAGS + EXTRA_FLAGS.get(src, [])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
