@@ -114,6 +114,17 @@ def test_mid_shape_tall_batch_two_row_tiles():
     _run(dc, lens, gains="random", logits=True)
 
 
+def test_mid_shape_maximum_sequence_count():
+    # 64 sequences (the most one call takes) x 16 rows = 1024 draft rows:
+    # eight stacked row tiles, 128 (sequence, kv head) attention pairs,
+    # contexts from empty to ~1k; every sequence checked
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024,
+                           vocab=4096, index=97)
+    rng = np.random.default_rng(97)
+    lens = [0, 1, 31, 32, 33] + [int(v) for v in rng.integers(0, 1100, size=59)]
+    _run(dc, lens, gains="random", logits=True)
+
+
 def test_mid_shape_tall_batch_ffn_not_a_multiple_of_64():
     # ffn = 1056: the down projection's K is not a whole number of the tiled
     # GEMM's 64-wide k stages, so those 80 rows take the register-streaming
