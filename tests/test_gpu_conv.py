@@ -155,6 +155,14 @@ def test_draft_with_convs_mid_shape_two_sequences():
     _draft_with_convs(dc, [300, 45], 16)
 
 
+def test_draft_with_convs_mid_shape_tall_batch():
+    # 6 sequences x 16 = 96 rows: the projections, the plain products before
+    # the finish calls and the layer products on the tiled (tall) GEMM
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024, vocab=4096,
+                           index=93)
+    _draft_with_convs(dc, [300, 45, 0, 129, 7, 64], 16)
+
+
 def test_draft_with_convs_mid_shape_short_block_fused():
     # 5 rows in one tile; group size 32
     dc = CONFIGS[1].shrink(hidden=512, n_layers=2, n_heads=8, n_kv_heads=2, ffn=1024, vocab=4096,
