@@ -125,12 +125,38 @@ __device__ __forceinline__ void wave_top_k2(uint64_t (&ka)[N], uint64_t (&kb)[N]
   }
 }
 
+// Lanes below the wave's first set bit of m (the slot of this lane among the
+// lanes whose bit is set)
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Each lane of the wave holds at most one of n <= 64 distinct nonzero keys
+// (zero: none); out[r] receives the key of rank r (decreasing) for r < k.
+// The rank of a key is the number of keys above it, counted against every
+// key of cand[0 .. n) (LDS, read as broadcasts).
+__device__ __forceinline__ void rank_select(uint64_t my, const uint64_t* cand, int n, int k,
+                                            uint64_t* out) {
+  int rank = 0;
+  for (int i = 0; i < n; ++i) rank += cand[i] > my ? 1 : 0;
+  if (my != 0ull && rank < k) out[rank] = my;
+}
+
 // (row, vocab slice): each wave takes the top k of its 512 logits, then wave 0
-// takes the top k of the four wave lists.
+// takes the top k of the four wave lists. A wave first bounds its top k from
+// below: T, the largest 32-bit value word such that at least k lanes hold a
+// key whose value word is >= T (a bitwise binary search over the lanes'
+// maxima, one ballot per bit). The k largest lane maxima are k distinct
+// keys >= T, so every key of the top k is too; the keys >= T (typically
+// ~20 of 512) are gathered into LDS and ranked against each other. More
+// than 64 of them (heavy ties) take the general path: a sorting network per
+// lane and k rounds of wave maxima.
 __global__ void __launch_bounds__(256)
 sel_topk_slices(const float* __restrict__ logits, int V, int n_slices, int k,
                 uint64_t* __restrict__ part) {
   __shared__ uint64_t wl[4][kSelMaxK];
+  __shared__ uint64_t cand[4][64];
+  __shared__ uint64_t merged[kSelMaxK];
   const int sl = blockIdx.x, row = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* z = logits + (size_t)row * V;
@@ -144,22 +170,48 @@ sel_topk_slices(const float* __restrict__ logits, int V, int n_slices, int k,
     zv[i] = z[v < V ? v : V - 1];
   }
   uint64_t key[kSelPer];
+  uint64_t kmax = 0ull;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int v = v0 + lane + 64 * i;
     key[i] = v < V ? argmax_key(zv[i], (uint32_t)v) : 0ull;  // 0: no entry (below every key)
+    kmax = umax64(kmax, key[i]);
   }
-  sort8_desc(key);
-  wave_top_k(key, k, wl[w]);
-  __syncthreads();
-  if (w == 0) {  // lanes 0..3 hold the four wave lists (already in decreasing order)
-    uint64_t m[kSelMaxK];
+  if (lane < kSelMaxK) wl[w][lane] = 0ull;
+  // the threshold on the value word: with fewer than k lanes holding keys,
+  // every key is a candidate
+  const uint32_t hmax = (uint32_t)(kmax >> 32);
+  uint32_t T = 1u;
+  if (__popcll(__ballot(kmax != 0ull)) >= k) {
+    T = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t t = T | (1u << b);
+      if (__popcll(__ballot(hmax >= t)) >= k) T = t;
+    }
+  }
+  int n = 0;
 #pragma unroll
-    for (int i = 0; i < kSelMaxK; ++i) m[i] = lane < 4 && i < k ? wl[lane][i] : 0ull;
-    // the merged list goes to LDS round by round and to memory in one store
-    // at the end (a store per round would be waited for by the next one)
-    wave_top_k(m, k, wl[3]);
-    if (lane < k) part[((size_t)row * n_slices + sl) * k + lane] = wl[3][lane];
+  for (int i = 0; i < kSelPer; ++i) {
+    const bool take = key[i] != 0ull && (uint32_t)(key[i] >> 32) >= T;
+    const uint64_t m = __ballot(take);
+    const int at = n + lanes_below(m);
+    if (take && at < 64) cand[w][at] = key[i];
+    n += __popcll(m);
+  }
+  if (n <= 64) {
+    const uint64_t my = lane < n ? cand[w][lane] : 0ull;
+    rank_select(my, cand[w], n, k, wl[w]);
+  } else {
+    sort8_desc(key);
+    wave_top_k(key, k, wl[w]);
+  }
+  __syncthreads();
+  if (w == 0) {  // the four wave lists: 4 x k distinct keys (or zeros)
+    const int nk = 4 * k;
+    const uint64_t my = lane < nk ? wl[lane / k][lane % k] : 0ull;
+    if (lane < kSelMaxK) merged[lane] = 0ull;
+    rank_select(my, &wl[0][0], 4 * kSelMaxK, k, merged);
+    if (lane < k) part[((size_t)row * n_slices + sl) * k + lane] = merged[lane];
   }
 }
 
