@@ -281,9 +281,12 @@ sel_project(const float* __restrict__ x, int D, int Bl, int P, int rows,
 }
 
 // One wave: the top k of a row's slice lists (n_slices sorted lists of k
-// keys, n_slices <= 128): lane l holds lists l and l + 64.
+// keys, n_slices <= 128): lane l holds lists l and l + 64. As in the top-k
+// kernel, the lanes' list heads give a lower bound T on the value word of
+// the top k; the keys >= T (list prefixes) are gathered into cand (64 keys
+// of LDS) and ranked, or, if more than 64, merged by k rounds of wave maxima.
 __device__ __forceinline__ void wave_merge_row(const uint64_t* __restrict__ src, int n_slices, int k,
-                                               uint64_t* out) {
+                                               uint64_t* out, uint64_t* cand) {
   const int lane = threadIdx.x & 63;
   uint64_t ka[kSelMaxK], kb[kSelMaxK];
   const int la = lane < n_slices ? lane : n_slices - 1;
@@ -299,7 +302,44 @@ __device__ __forceinline__ void wave_merge_row(const uint64_t* __restrict__ src,
     ka[i] = lane < n_slices && i < k ? ka[i] : 0ull;
     kb[i] = lane + 64 < n_slices && i < k ? kb[i] : 0ull;
   }
-  wave_top_k2(ka, kb, k, out);
+  if (lane < kSelMaxK) out[lane] = 0ull;
+  const uint64_t head = umax64(ka[0], kb[0]);
+  const uint32_t hh = (uint32_t)(head >> 32);
+  uint32_t T = 1u;
+  if (__popcll(__ballot(head != 0ull)) >= k) {
+    T = 0u;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t t = T | (1u << b);
+      if (__popcll(__ballot(hh >= t)) >= k) T = t;
+    }
+  }
+  int n = 0;
+  // the lists are in decreasing order: once no lane takes slot i, none takes
+  // a later one
+#pragma unroll
+  for (int i = 0; i < kSelMaxK; ++i) {
+    const bool take = ka[i] != 0ull && (uint32_t)(ka[i] >> 32) >= T;
+    const uint64_t m = __ballot(take);
+    if (m == 0ull) break;
+    const int at = n + lanes_below(m);
+    if (take && at < 64) cand[at] = ka[i];
+    n += __popcll(m);
+  }
+#pragma unroll
+  for (int i = 0; i < kSelMaxK; ++i) {
+    const bool take = kb[i] != 0ull && (uint32_t)(kb[i] >> 32) >= T;
+    const uint64_t m = __ballot(take);
+    if (m == 0ull) break;
+    const int at = n + lanes_below(m);
+    if (take && at < 64) cand[at] = kb[i];
+    n += __popcll(m);
+  }
+  if (n <= 64) {
+    const uint64_t my = lane < n ? cand[lane] : 0ull;
+    rank_select(my, cand, n, k, out);
+  } else {
+    wave_top_k2(ka, kb, k, out);
+  }
 }
 
 __global__ void __launch_bounds__(256)
@@ -309,6 +349,7 @@ sel_pairs(const uint64_t* __restrict__ part, int n_slices, int k, const float* _
           const int32_t* __restrict__ anchors, int P, int V, float* __restrict__ S,
           int32_t* __restrict__ cand) {
   __shared__ uint64_t top[2][kSelMaxK];
+  __shared__ uint64_t mcand[2][64];
   __shared__ int32_t pid[kSelMaxK], cid[kSelMaxK];
   __shared__ float unary[kSelMaxK];
   __shared__ float g[kSelMaxRank];
@@ -319,8 +360,8 @@ sel_pairs(const uint64_t* __restrict__ part, int n_slices, int k, const float* _
   const int n = n_slices * k;
   // wave 0 merges this row's slice lists, wave 1 the previous row's (the
   // predecessors); waves 2 and 3 form g meanwhile
-  if (w == 0) wave_merge_row(part + (size_t)m * n, n_slices, k, top[1]);
-  if (w == 1 && j > 0) wave_merge_row(part + (size_t)(m - 1) * n, n_slices, k, top[0]);
+  if (w == 0) wave_merge_row(part + (size_t)m * n, n_slices, k, top[1], mcand[0]);
+  if (w == 1 && j > 0) wave_merge_row(part + (size_t)(m - 1) * n, n_slices, k, top[0], mcand[1]);
   if (w >= 2) {
     // g = rs * sum of the k-slice partials (slice order), rs the final norm's
     // row scale of row m; the loads of 8 slices at a time are in flight
