@@ -552,7 +552,7 @@ def main():
         summarize_pmc(a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7].split(" ;; "))
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library "
               "has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 

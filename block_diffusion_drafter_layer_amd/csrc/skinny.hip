@@ -14,7 +14,7 @@
 //            from the draft tokens, the block's k/v follow the context's);
 //   resid  - o_proj / down_proj: x += y, the next RMSNorm's input (x*gain as a
 //            bf16 hi/lo pair) and per-32-column sums of x^2;
-//   swiglu - gate/up pairs: silu(g)*u (spec decoder layer);
+//   swiglu - gate/up pairs: silu(g)*u (the decoder layer's SwiGLU MLP);
 //   lm     - final RMSNorm row scale, optional logits, per-tile argmax keys
 //            (txtmix article section 9: LM head on the rows after the anchor).
 // Also here: the block embedding (section 6: anchor + mask tokens) and the
