@@ -430,7 +430,7 @@ attn_lds(AttnArgs p) {
 
 // One workgroup per (block row, query head, sequence), one thread per output
 // dim (at least one wave). Each thread first requests its dim of the first
-// kMergeBatch split accumulators and of the block's Bl fp32 values (clamped
+// MB split accumulators and of the block's Bl fp32 values (clamped
 // indices, straight-line loads). Wave 0 then forms the block scores: lane
 // 4j + t holds a quarter of the dims of block key j and of the query (hi +
 // lo), so one dot product of HD/4 terms and two lane exchanges give q.k_j.
@@ -441,7 +441,6 @@ attn_lds(AttnArgs p) {
 // 2^(m_k - M) / L and the block keys' weights 2^(s_j - M) / L in LDS.
 // Scores are in log2 units (scaled by log2(e)/sqrt(hd)), as in the split
 // kernels.
-constexpr int kMergeBatch = 32;
 static_assert(kAttnMaxSplits <= 128, "two splits per lane of wave 0");
 struct MergeArgs {
   const float* acc;
@@ -452,9 +451,12 @@ struct MergeArgs {
   float scale_log2;
   bf16_t *ob_h, *ob_l;
 };
-template <int HD>
+// MB: split accumulators requested per batch (8 when the splits are that
+// few, so that no loads of clamped duplicates are issued)
+template <int HD, int MB>
 __global__ void __launch_bounds__(HD < 64 ? 64 : HD)
 attn_merge(MergeArgs p) {
+  constexpr int kMergeBatch = MB;
   constexpr int STRIDE = 16 * HD;  // floats between the splits of one (row, dim)
   constexpr int DPL = HD / 4;      // dims per lane of a block score
   static_assert(DPL % 4 == 0, "whole float4 pieces of a key per lane");
@@ -585,7 +587,10 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   m.acc = L.att_acc; m.ml = L.att_ml; m.q = L.q; m.q_lo = L.q_lo; m.blk_k = L.blk_k; m.blk_v = L.blk_v;
   m.Hq = L.Hq; m.Hkv = L.Hkv; m.Bl = L.Bl; m.splits = L.att_splits; m.scale_log2 = p.scale_log2;
   m.ob_h = L.ob_h; m.ob_l = L.ob_l;
-  hipLaunchKernelGGL(attn_merge<HD>, dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+  if (L.att_splits <= 8)
+    hipLaunchKernelGGL((attn_merge<HD, 8>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+  else
+    hipLaunchKernelGGL((attn_merge<HD, 32>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
   return hipGetLastError();
 }
 
