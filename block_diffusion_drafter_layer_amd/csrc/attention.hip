@@ -93,16 +93,25 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
   const int kl = c0 + 8 * lg;
   float sc[8];
   float mloc = -INFINITY;
+  if (ke - c0 >= 32) {  // every key of the chunk in range (wave-uniform)
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = (kl + 4 * t + e < ke) ? st[t][e] * scale_log2 : -INFINITY;
-      sc[4 * t + e] = v;
-      mloc = fmaxf(mloc, v);
-    }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+      for (int e = 0; e < 4; ++e) {
+        sc[4 * t + e] = st[t][e] * scale_log2;
+        mloc = fmaxf(mloc, sc[4 * t + e]);
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = (kl + 4 * t + e < ke) ? st[t][e] * scale_log2 : -INFINITY;
+        sc[4 * t + e] = v;
+        mloc = fmaxf(mloc, v);
+      }
+  }
+  mloc = rows4_max(mloc);
   const float m_new = fmaxf(m_run, mloc);
   const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
   float pr[8], psum = 0.f;
@@ -218,8 +227,7 @@ attn_split(AttnArgs p) {
       if (c0 > last) break;
     }
   }
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = rows4_sum(l_run);
 
   if (W > 1) {
     if (wi > 0) {
@@ -349,25 +357,33 @@ attn_lds(AttnArgs p) {
   const bf16_t* kbase = sd.kv + (size_t)((2 * p.layer) * p.Hkv + g) * plane;
   const bf16_t* vbase = sd.kv + (size_t)((2 * p.layer + 1) * p.Hkv + g) * plane;
 
-  // chunk j of the split into slot j % kRingSlots; jj: the chunk actually read
+  // Load instruction q of a chunk: K rows 4q .. 4q+3 (256 bytes each) for q
+  // < 8, else V^T rows (dims) 16(q-8) .. +15 (64 bytes each). A wave's
+  // instructions are all of one kind; each lane's address for chunk start
+  // c0 is a fixed per-lane pointer plus c0 * HD (K) or c0 (V^T).
+  const bool kload = w * NQ < 8;  // wave-uniform
+  const bf16_t* lp[NQ];
+#pragma unroll
+  for (int u = 0; u < NQ; ++u) {
+    const int q = w * NQ + u;
+    if (kload) {
+      const int kl = 4 * q + (lane >> 4);
+      lp[u] = kbase + (size_t)kl * HD + (((lane & 15) ^ kswz(kl)) << 3);
+    } else {
+      const int d = 16 * (q - 8) + (lane >> 2);
+      lp[u] = vbase + (size_t)d * sd.cap + 8 * ((lane & 3) ^ ((d >> 2) & 3));
+    }
+  }
+  // chunk j of the split into slot j % kRingSlots; jj: the chunk actually
+  // read. Its start is clamped to cap - 32 (cap is a multiple of 64): a
+  // chunk of the range starts at most there anyway, and the reads issued
+  // before the range is known (or for an empty split) stay in the planes.
   auto issue = [&](int j, int jj) {
-    const int c0 = kb + 32 * jj;
+    const int c0 = min(kb + 32 * jj, sd.cap - 32);
+    const size_t step = kload ? (size_t)c0 * HD : (size_t)c0;
     uint8_t* slot = &ring[j % kRingSlots][0];
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int q = w * NQ + u;  // wave-uniform
-      if (q < 8) {               // K rows 4q .. 4q+3, 256 bytes each
-        const int kl = 4 * q + (lane >> 4);
-        int key = c0 + kl;
-        key = key < sd.cap ? key : sd.cap - 1;
-        dma16(kbase + (size_t)key * HD + (((lane & 15) ^ kswz(kl)) << 3), slot + q * 1024);
-      } else {                   // V^T rows (dims) 16(q-8) .. +15, 64 bytes each
-        const int d = 16 * (q - 8) + (lane >> 2);
-        int key0 = c0 + 8 * ((lane & 3) ^ ((d >> 2) & 3));
-        key0 = key0 < sd.cap ? key0 : sd.cap - 8;
-        dma16(vbase + (size_t)d * sd.cap + key0, slot + q * 1024);
-      }
-    }
+    for (int u = 0; u < NQ; ++u) dma16(lp[u] + step, slot + (w * NQ + u) * 1024);
   };
   // queries and the context length first: a wait for them then leaves the
   // ring's loads, issued after them, in flight
@@ -415,8 +431,7 @@ attn_lds(AttnArgs p) {
   }
   // no direct load may still be writing the ring when the workgroup ends
   attn_wait_vm<0>();
-  l_run += __shfl_xor(l_run, 16, kWave);
-  l_run += __shfl_xor(l_run, 32, kWave);
+  l_run = rows4_sum(l_run);
   const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
   float* out = p.acc + slot * 16 * HD + (size_t)ql * HD;
 #pragma unroll

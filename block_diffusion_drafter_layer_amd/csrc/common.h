@@ -93,6 +93,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max and sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48),
+// with gfx950's row-swap instructions: each returns the pair {x_l, x_l^16}
+// (resp. {x_l, x_l^32}) in some order, so every lane of a quartet ends with
+// the same bits. VALU only: no LDS round trip as with a lane shuffle.
+__device__ __forceinline__ float rows4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -178,6 +195,21 @@ __device__ __forceinline__ void rope_cs_inv(int pos, double inv, float& c, float
 __device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_theta,
                                         float& c, float& s) {
   rope_cs_inv(pos, rope_inv_freq(d, hd, log2_theta), c, s);
+}
+// The same rotation from the frequency in revolutions per position
+// (theta^(-2d/hd) / 2 pi): the angle pos * f is formed and reduced to
+// [-1/2, 1/2] revolution in fp64, then the hardware sine and cosine, which
+// take revolutions (max abs error ~1.2e-7 on that range, measured against
+// fp64), in place of a library sincosf of the reduced angle.
+__device__ __forceinline__ double rope_rev_freq(int d, int hd, double log2_theta) {
+  return rope_inv_freq(d, hd, log2_theta) * 0.15915494309189533577;  // 1 / (2 pi)
+}
+__device__ __forceinline__ void rope_cs_rev(int pos, double f_rev, float& c, float& s) {
+  double r = (double)pos * f_rev;
+  r -= rint(r);
+  const float x = (float)r;
+  s = __builtin_amdgcn_sinf(x);
+  c = __builtin_amdgcn_cosf(x);
 }
 
 // One sequence of a draft call: its KV buffer and the context length.

@@ -115,8 +115,8 @@ struct EpiQKV {
     // load that every iteration waits for behind the previous iteration's
     // stores)
     __shared__ int r_pos[ROWS];
-    // the rotation frequencies once per call (an fp64 exp2 per element would
-    // cost more than the tall path's whole k loop)
+    // the rotation frequencies (revolutions per position) once per call (an
+    // fp64 exp2 per element would cost more than the tall path's whole k loop)
     __shared__ double inv_f[kMaxHeadDim / 2];
     // sequences walked with a uniform index: a per-lane index into the
     // sequence table would make the compiler copy the whole table (kernel
@@ -129,7 +129,7 @@ struct EpiQKV {
         r_pos[ml] = len + (int)threadIdx.x;
     }
     for (int d = threadIdx.x; d < p.hd / 2; d += blockDim.x)
-      inv_f[d] = rope_inv_freq(d, p.hd, p.log2_theta);
+      inv_f[d] = rope_rev_freq(d, p.hd, p.log2_theta);
     __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
@@ -146,7 +146,7 @@ struct EpiQKV {
         const int h = vcl / p.hd;
         const int d = ((vcl % p.hd) >> 1) + j;  // group t covers dims 8t+j
         float cs, sn;
-        rope_cs_inv(pos, inv_f[d], cs, sn);
+        rope_cs_rev(pos, inv_f[d], cs, sn);
         const float o1 = x1 * cs - x2 * sn;
         const float o2 = x2 * cs + x1 * sn;
         if (is_q) {
@@ -189,10 +189,11 @@ struct EpiResid {
   __device__ static void run(const P& p, float (*tile)[LD], const float*,
                              int vc0, int m0, int M) {
     static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
-    // eight elements per thread at a time: their x and gain loads go out
+    // U elements per thread at a time: their x and gain loads go out
     // together (clamped addresses), then the in-place updates (a
-    // load-update-store per iteration would wait for each load)
-    constexpr int U = 8;
+    // load-update-store per iteration would wait for each load); the tall
+    // path's 64-row slices (512 threads) take them in two batches
+    constexpr int U = ROWS >= 64 ? 16 : 8;
     for (int e0 = threadIdx.x; e0 < ROWS * VC; e0 += U * blockDim.x) {
       float xo[U];
       bf16_t go[U];
@@ -259,7 +260,9 @@ struct EpiSwiglu {
       if (m >= M || vc0 + c * 16 >= p.n_vcols) continue;
       const float g = tile[ml][c * 16 + j] * rs[ml];
       const float u = tile[ml][c * 16 + j + 8] * rs[ml];
-      const float a = g / (1.f + expf(-g)) * u;
+      // silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (each
+      // within about an ulp); -g past the exponent range gives 1/inf = 0
+      const float a = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f)) * u;
       const int f = ((vc0 >> 4) + c) * 8 + j;
       const size_t i = (size_t)m * p.F + f;
       split_bf16(a, p.ah[i], p.al[i]);
