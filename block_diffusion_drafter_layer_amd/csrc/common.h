@@ -238,6 +238,16 @@ __device__ __forceinline__ void dma16_nt(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 2);
 }
 
+// 16-byte store with the system-coherent cache policy (sc0 sc1): written
+// through the L2, so partial results that a later kernel reads leave no dirty
+// lines behind for the write-back at the kernel's end. byte_off < 2^31.
+__device__ __forceinline__ void store16_wt(float* base, uint32_t byte_off, f32x4 v) {
+  // raw buffer, 32-bit elements (descriptor word 3 of this GPU family)
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 17);
+}
+
 // context length of sequence s: the host value, or the device one clamped to
 // the buffer (a length past max_ctx would put the block's rows out of it)
 __device__ __forceinline__ int seq_len(const SeqTable& t, int s) {

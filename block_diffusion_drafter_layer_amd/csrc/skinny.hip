@@ -1071,7 +1071,8 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
   };
   // units in batches of UB whose partial tiles are stored together, each as
   // one contiguous kilobyte in MFMA lane order (layout [tile][split][lane][4]:
-  // lane l, item e holds row 4 (l / 16) + e, column l % 16): a store makes the
+  // lane l, item e holds row 4 (l / 16) + e, column l % 16), written through
+  // the L2 (the finisher, a separate launch, reads them): a store makes the
   // following ring waits wait for it as well, so fewer, larger batches keep
   // the stream flowing
   for (int jb = 0; jb < units; jb += UB) {
@@ -1086,7 +1087,7 @@ stream_gemm(SkinnyA a, typename Epi::P ep, int n_vcols, int ks, int kc, float* _
     for (int u = 0; u < UB; ++u) {
       if (jb + u < units) {
         const int tile = gw + (jb + u) * Wg;
-        *reinterpret_cast<f32x4*>(part + ((size_t)tile * ks + slice) * 256 + lane * 4) = acc[u];
+        store16_wt(part, (uint32_t)(((tile * ks + slice) * 256 + lane * 4) * 4), acc[u]);
       }
     }
   }
@@ -1387,7 +1388,9 @@ hipError_t launch_stream(const SkinnyA& a, const typename Epi::P& ep, int n_vcol
 // true when launch_skinny takes the LDS-staged kernel for this shape
 bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
   if (!ws.part || !stream_plan(a.M, n_vcols, a.K, ks)) return false;
-  return (size_t)((n_vcols + 31) / 32) * 2 * ks * 256 <= ws.part_floats;
+  const size_t floats = (size_t)((n_vcols + 31) / 32) * 2 * ks * 256;
+  // partial stores take 32-bit byte offsets
+  return floats <= ws.part_floats && floats * 4 < ((size_t)1 << 31);
 }
 
 // A draft epilogue on the tiled MFMA GEMM, for batches of more than 64
