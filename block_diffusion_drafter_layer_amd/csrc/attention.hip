@@ -432,11 +432,12 @@ attn_lds(AttnArgs p) {
   // no direct load may still be writing the ring when the workgroup ends
   attn_wait_vm<0>();
   l_run = rows4_sum(l_run);
+  // the partial, written through the L2 (the merge is another launch)
   const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
-  float* out = p.acc + slot * 16 * HD + (size_t)ql * HD;
+  float* out = p.acc + slot * 16 * HD;
 #pragma unroll
   for (int h = 0; h < HT; ++h)
-    *reinterpret_cast<f32x4*>(out + h * 16 + 4 * lg) = acc[h];
+    store16_wt(out, (uint32_t)((ql * HD + h * 16 + 4 * lg) * 4), acc[h]);
   if (lg == 0) {
     p.ml[(slot * 16 + ql) * 2 + 0] = m_run;
     p.ml[(slot * 16 + ql) * 2 + 1] = l_run;

@@ -362,9 +362,11 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(mine + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4) = v;
+          store16_wt(mine, (uint32_t)(((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 16), v);
         }
-    __builtin_amdgcn_s_waitcnt(DFL_VM(0));  // this wave's partial has reached its L2
+    // this wave's partial is written (through the L2: the release below then
+    // has little to write back)
+    __builtin_amdgcn_s_waitcnt(DFL_VM(0));
     __syncthreads();  // every wave's has (also: every wave is done with the ring)
     int32_t* arrived = reinterpret_cast<int32_t*>(smem);
     // agent-scope release: the workgroup's partial (all waves' stores, ordered
