@@ -530,8 +530,7 @@ attn_merge(MergeArgs p) {
         dot += (__uint_as_float(hb) + __uint_as_float(lb)) * kk[e];
       }
     }
-    dot += __shfl_xor(dot, 1, kWave);
-    dot += __shfl_xor(dot, 2, kWave);
+    dot = quad_sum(dot);
     const float sj = j < p.Bl ? dot * p.scale_log2 : -INFINITY;
     const float M = wave_max(fmaxf(fmaxf(mk[0], mk[1]), sj));  // finite: Bl >= 1
     float e[2];

@@ -81,16 +81,18 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// x of another lane of the same 16-lane row, by a DPP lane pattern
+// (quad_perm 0xB1: lane ^ 1; quad_perm 0x4E: lane ^ 2; 0x141: mirror within
+// 8 lanes; 0x140: mirror within 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp_lane(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// sum over lanes l, l ^ 1, l ^ 2, l ^ 3 (each lane pairs with a partner
+// that computes the same sum in the other operand order: the quartet agrees)
+__device__ __forceinline__ float quad_sum(float v) {
+  v += dpp_lane<0xB1>(v);
+  return v + dpp_lane<0x4E>(v);
 }
 
 // Max and sum over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48),
@@ -108,6 +110,29 @@ __device__ __forceinline__ float rows4_sum(float x) {
   x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// sums over aligned groups of 8 and of 16 lanes (the quartets, then the
+// mirrored halves), every lane of a group with the same bits
+__device__ __forceinline__ float row8_sum(float v) {
+  v = quad_sum(v);
+  return v + dpp_lane<0x141>(v);
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = row8_sum(v);
+  return v + dpp_lane<0x140>(v);
+}
+
+// Whole-wave sum and max: DPP steps inside each 16-lane row (the pairs at
+// distance 1 and 2, then the mirrored halves of 8 and of 16 lanes), then the
+// row swaps; VALU only, and every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) { return rows4_sum(row16_sum(v)); }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_lane<0xB1>(v));
+  v = fmaxf(v, dpp_lane<0x4E>(v));
+  v = fmaxf(v, dpp_lane<0x141>(v));
+  v = fmaxf(v, dpp_lane<0x140>(v));
+  return rows4_max(v);
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {

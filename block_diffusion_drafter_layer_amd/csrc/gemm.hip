@@ -48,9 +48,7 @@ struct EpiFuse {
       const int r = e >> 3, q = e & 7;
       float s = 0.f;
       for (int c = q; c < BN && n0 + c < p.N; c += 8) s += C[r * ld + c] * C[r * ld + c];
-      s += __shfl_xor(s, 1, kWave);
-      s += __shfl_xor(s, 2, kWave);
-      s += __shfl_xor(s, 4, kWave);
+      s = row8_sum(s);
       const int m = m0 + r;
       if (q == 0 && m < M) p.ssq[(size_t)m * p.n_tiles + n0 / BN] = s;
     }

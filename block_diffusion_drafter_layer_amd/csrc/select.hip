@@ -269,8 +269,7 @@ sel_project(const float* __restrict__ x, int D, int Bl, int P, int rows,
     __syncthreads();
   }
   // the 16 threads of a row hold its squares: sum them (16-lane groups)
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+  sq = row16_sum(sq);
   const int m = m0 + orow;
   if (m < rows) {
     float* g = gpart + ((size_t)kz * rows + m) * rank + o0 + ocol;

@@ -1131,9 +1131,7 @@ embed_block(const bf16_t* __restrict__ E, int V, int D, const int32_t* __restric
     *reinterpret_cast<uint2*>(xh + o) = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
     *reinterpret_cast<uint2*>(xl + o) = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
   }
-  sq += __shfl_xor(sq, 1, kWave);
-  sq += __shfl_xor(sq, 2, kWave);
-  sq += __shfl_xor(sq, 4, kWave);
+  sq = row8_sum(sq);
   if (n < D && (threadIdx.x & 7) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
 }
 
@@ -1223,8 +1221,7 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   }
   tile[m][n] = s0;
   tile[m][16 + n] = s1;
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+  sq = row16_sum(sq);
   if ((lane & 15) == 0 && srow < 16) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   Epi::template run<16, 32>(ep, tile, rs, pair * 32, 0, a.M);
@@ -1280,8 +1277,7 @@ lm_stream_finish(SkinnyA a, EpiLM::P ep, int ks, const float* __restrict__ part)
 #pragma unroll
       for (int g = 0; g < 4; ++g) z[g] += v[k][g];
   }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, kWave);
+  sq = row16_sum(sq);
   if ((lane & 15) == 0) rs[srow] = a.ssq ? rsqrtf(sq / (float)a.K + a.eps) : 1.f;
   __syncthreads();
   const bool valid = col < ep.V;
@@ -1445,8 +1441,8 @@ struct EpiTiled {
             if (c0 + u * TPR < n2) s += v[u].x + v[u].y;
         }
       }
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) s += __shfl_xor(s, o, kWave);
+      static_assert(TPR == 8, "eight-lane groups");
+      s = row8_sum(s);
       if (q == 0 && e < rows * TPR) rs[m & 255] = p.ssq ? rsqrtf(s / (float)p.K + p.eps) : 1.f;
     }
   }
@@ -1659,9 +1655,7 @@ conv_finish_resid(const float* __restrict__ z, const bf16_t* __restrict__ base,
     *reinterpret_cast<uint2*>(xl + i) =
         make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
   }
-  sq += __shfl_xor(sq, 1, kWave);
-  sq += __shfl_xor(sq, 2, kWave);
-  sq += __shfl_xor(sq, 4, kWave);
+  sq = row8_sum(sq);
   if (n < D && (threadIdx.x & 7) == 0) ssq[(size_t)m * (D / 32) + n / 32] = sq;
 }
 
