@@ -567,7 +567,7 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   const int G = c.n_heads / c.n_kv_heads;
   const int WG_waves = G <= 2 ? 2 * G : G;
   const int max_splits =
-      std::max(1, std::min(kAttnMaxSplits, attn_slots(h->max_seqs, c.n_kv_heads) / pairs));
+      std::max(1, std::min(kAttnMaxSplits, attn_slots(h->max_seqs, c.n_kv_heads) / pairs - 1));
   // (the last split also takes the remainder); long key ranges are split further when the
   // grid is full already (many sequences), since a wave's chunks are serial
   int splits = std::max(1, (1024 + pairs * WG_waves - 1) / (pairs * WG_waves));
@@ -579,6 +579,7 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   // max_keys covers the whole cache, and the last split absorbs the rest
   splits = std::max(1, std::min(splits, max_keys / kps));
   L.att_splits = splits; L.att_keys_per_split = kps;
+  L.att_blk_wg = kps >= kAttnBlockWgKeys;
 
   hipStream_t st = h->stream;
   hipError_t e = timed(h, ST_EMBED, [&] { return launch_embed(L, st); });

@@ -5,8 +5,9 @@
 // head a reads kv head a / G.
 //
 // The context keys come from the bf16 KV cache; the block's own keys never
-// enter the cache: the QKV epilogue leaves them in fp32 in the workspace and
-// the merge kernel adds them, in fp32, to the split partials of the context.
+// enter the cache: the QKV epilogue leaves them in fp32 in the workspace, and
+// the split that holds the context's last key takes them as one more chunk
+// (K and V as bf16 hi/lo pairs).
 //
 // One workgroup per (key range, kv head, sequence) with one wave per query
 // head of the group; each wave holds the 16 block rows of its head as the
@@ -29,9 +30,14 @@ namespace dfl {
 struct AttnArgs {
   const bf16_t* q;       // [M][Hq][HD] after RoPE, hi
   const bf16_t* q_lo;    // lo
+  const float* blk_k;    // [M][Hkv][HD] the block's own K after RoPE, fp32
+  const float* blk_v;    // [M][Hkv][HD] the block's own V, fp32
   float* acc;            // [(s*Hq + a)*splits + split][16][HD]
   float* ml;             // [(s*Hq + a)*splits + split][16][2]
   int Hq, Hkv, Bl, layer, splits, kps;
+  // blk_wg: workgroup x = splits takes the block's own keys (else the merge
+  // does); slots: partial slots per (sequence, query head), splits + blk_wg
+  int blk_wg, slots;
   float scale_log2;      // log2(e) / sqrt(HD)
   SeqTable seqs;
 };
@@ -68,28 +74,14 @@ __device__ __forceinline__ void load_chunk(Chunk<HD>& c, int c0, const bf16_t* k
     c.v[h] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(h * 16 + ql) * cap + kl_ld);
 }
 
-template <int HD>
-__device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke, const bf16x8* qf,
-                                              const bf16x8* qfl, float scale_log2, int lg,
-                                              float& m_run, float& l_run, f32x4* acc) {
-  constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
-  // hi and lo products in separate accumulators: four independent MFMA
-  // chains of KSTEPS instead of two of 2 * KSTEPS
-  f32x4 st[2], stl[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    stl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st[t] = mfma16x16x32(c.kf[t][ks], qf[ks], st[t]);
-      stl[t] = mfma16x16x32(c.kf[t][ks], qfl[ks], stl[t]);
-    }
-#pragma unroll
-  for (int t = 0; t < 2; ++t) st[t] += stl[t];
+// Online-softmax step for one 32-key chunk whose transposed scores are in st
+// (lane (ql, lg): keys c0 + 8 lg .. +7 of query row ql): keys at or past ke
+// masked, the running max over the row's four lanes, the rescale of the
+// accumulators, and P (unnormalised, <= 1) as a bf16 hi/lo pair.
+template <int HT>
+__device__ __forceinline__ void softmax_step(f32x4 (&st)[2], int c0, int ke, float scale_log2,
+                                             int lg, float& m_run, float& l_run, f32x4* acc,
+                                             bf16x8& pf, bf16x8& pfl) {
   const int kl = c0 + 8 * lg;
   float sc[8];
   float mloc = -INFINITY;
@@ -128,8 +120,33 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
   }
   l_run = l_run * alpha + psum;
   m_run = m_new;
-  bf16x8 pf, pfl;
   pack_split_bf16x8(pr, pf, pfl);
+}
+
+template <int HD>
+__device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke, const bf16x8* qf,
+                                              const bf16x8* qfl, float scale_log2, int lg,
+                                              float& m_run, float& l_run, f32x4* acc) {
+  constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
+  // hi and lo products in separate accumulators: four independent MFMA
+  // chains of KSTEPS instead of two of 2 * KSTEPS
+  f32x4 st[2], stl[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    stl[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = mfma16x16x32(c.kf[t][ks], qf[ks], st[t]);
+      stl[t] = mfma16x16x32(c.kf[t][ks], qfl[ks], stl[t]);
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) st[t] += stl[t];
+  bf16x8 pf, pfl;
+  softmax_step<HT>(st, c0, ke, scale_log2, lg, m_run, l_run, acc, pf, pfl);
   if (ke - c0 >= 32) {  // a whole chunk of valid keys (wave-uniform)
 #pragma unroll
     for (int h = 0; h < HT; ++h) {
@@ -140,7 +157,7 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
     return;
   }
   // keys past the range contribute zero V, never NaN
-  const int nvalid = ke - kl;
+  const int nvalid = ke - (c0 + 8 * lg);
   uint32_t keep[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -154,6 +171,111 @@ __device__ __forceinline__ void process_chunk(const Chunk<HD>& c, int c0, int ke
     acc[h] = mfma16x16x32(vf, pf, acc[h]);
     acc[h] = mfma16x16x32(vf, pfl, acc[h]);
   }
+}
+
+// The block's own Bl keys (<= 16, fp32 rows of the workspace: key j of this
+// kv head at bk + j * kvd, its value at bv + j * kvd) as one more chunk of
+// the running softmax, laid out like a context chunk. K and V enter the
+// MFMAs as bf16 hi/lo pairs like Q and P (the lo x lo term dropped), so the
+// products keep about fp32 accuracy.
+template <int HD>
+__device__ __forceinline__ void process_block(const float* bk, const float* bv, int kvd, int Bl,
+                                              const bf16x8* qf, const bf16x8* qfl, float scale_log2,
+                                              int ql, int lg, float& m_run, float& l_run,
+                                              f32x4* acc) {
+  constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
+  // every load first (one round trip): K rows as the A operand of each
+  // score tile and k step, then the V^T values (dim 16 h + ql, keys 8 lg ..
+  // 8 lg + 7), zero past Bl
+  float kf[2][KSTEPS][8], vf[HT][8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = 8 * (ql >> 2) + 4 * t + (ql & 3);  // A row ql of score tile t
+    const bool kv = key < Bl;
+    const float* kr = bk + (size_t)(kv ? key : 0) * kvd + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const bool in = kv && ks * 32 + 8 * lg < HD;
+      const float4 a = in ? *reinterpret_cast<const float4*>(kr + ks * 32) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 b = in ? *reinterpret_cast<const float4*>(kr + ks * 32 + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+      kf[t][ks][0] = a.x; kf[t][ks][1] = a.y; kf[t][ks][2] = a.z; kf[t][ks][3] = a.w;
+      kf[t][ks][4] = b.x; kf[t][ks][5] = b.y; kf[t][ks][6] = b.z; kf[t][ks][7] = b.w;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < HT; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = 8 * lg + e;
+      vf[h][e] = key < Bl ? bv[(size_t)key * kvd + h * 16 + ql] : 0.f;
+    }
+  f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      bf16x8 kh, klo;
+      pack_split_bf16x8(kf[t][ks], kh, klo);
+      st[t] = mfma16x16x32(kh, qf[ks], st[t]);
+      st[t] = mfma16x16x32(kh, qfl[ks], st[t]);
+      st[t] = mfma16x16x32(klo, qf[ks], st[t]);
+    }
+  }
+  bf16x8 pf, pfl;
+  softmax_step<HT>(st, 0, Bl, scale_log2, lg, m_run, l_run, acc, pf, pfl);
+#pragma unroll
+  for (int h = 0; h < HT; ++h) {
+    bf16x8 vh, vlo;
+    pack_split_bf16x8(vf[h], vh, vlo);
+    acc[h] = mfma16x16x32(vh, pf, acc[h]);
+    acc[h] = mfma16x16x32(vh, pfl, acc[h]);
+    acc[h] = mfma16x16x32(vlo, pf, acc[h]);
+  }
+}
+
+// A wave's partial (running max, sum and accumulator of its query head's 16
+// rows; l already summed over the row's lanes), written through the L2: the
+// merge is another launch.
+template <int HD>
+__device__ __forceinline__ void write_partial(const AttnArgs& p, size_t slot, int ql, int lg,
+                                              const f32x4* acc, float m_run, float l_run) {
+  constexpr int HT = Chunk<HD>::HT;
+  float* out = p.acc + slot * 16 * HD;
+#pragma unroll
+  for (int h = 0; h < HT; ++h)
+    store16_wt(out, (uint32_t)((ql * HD + h * 16 + 4 * lg) * 4), acc[h]);
+  if (lg == 0) {
+    p.ml[(slot * 16 + ql) * 2 + 0] = m_run;
+    p.ml[(slot * 16 + ql) * 2 + 1] = l_run;
+  }
+}
+
+// The workgroup past the context's splits: each query-head wave takes only
+// the block's own keys, into the head's last partial slot. It runs beside
+// the context splits, so the block adds no step to their chains.
+template <int HD>
+__device__ __forceinline__ void block_partial(const AttnArgs& p, int s, int g, int a, int ql, int lg) {
+  constexpr int KSTEPS = Chunk<HD>::KSTEPS, HT = Chunk<HD>::HT;
+  bf16x8 qf[KSTEPS], qfl[KSTEPS];
+  const bool qv = ql < p.Bl;
+  const size_t qoff = ((size_t)(s * p.Bl + (qv ? ql : 0)) * p.Hq + a) * HD + 8 * lg;
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const bool in = qv && ks * 32 + 8 * lg < HD;
+    qf[ks] = in ? ld_bf16x8(p.q + qoff + ks * 32) : zero_bf16x8();
+    qfl[ks] = in ? ld_bf16x8(p.q_lo + qoff + ks * 32) : zero_bf16x8();
+  }
+  f32x4 acc[HT];
+#pragma unroll
+  for (int h = 0; h < HT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const size_t kvd = (size_t)p.Hkv * HD;
+  const size_t b0 = (size_t)(s * p.Bl) * kvd + (size_t)g * HD;
+  process_block<HD>(p.blk_k + b0, p.blk_v + b0, (int)kvd, p.Bl, qf, qfl, p.scale_log2, ql, lg,
+                    m_run, l_run, acc);
+  l_run = rows4_sum(l_run);
+  write_partial<HD>(p, (size_t)(s * p.Hq + a) * p.slots + p.splits, ql, lg, acc, m_run, l_run);
 }
 
 // Workgroup = G query-head waves x W key columns for one (key range, kv head,
@@ -174,6 +296,10 @@ attn_split(AttnArgs p) {
   const int gi = w % G, wi = w / G;
   const int a = g * G + gi;
   const int ql = lane & 15, lg = lane >> 4;
+  if (p.blk_wg && split == p.splits) {  // the block's own keys (whole workgroup)
+    if (wi == 0) block_partial<HD>(p, s, g, a, ql, lg);
+    return;
+  }
   const SeqDesc sd = p.seqs.s[s];
   const int kb = split * p.kps;
   const size_t plane = (size_t)sd.cap * HD;
@@ -263,15 +389,7 @@ attn_split(AttnArgs p) {
     }
     m_run = M;
   }
-  const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
-  float* out = p.acc + slot * 16 * HD + (size_t)ql * HD;
-#pragma unroll
-  for (int h = 0; h < HT; ++h)
-    *reinterpret_cast<f32x4*>(out + h * 16 + 4 * lg) = acc[h];
-  if (lg == 0) {
-    p.ml[(slot * 16 + ql) * 2 + 0] = m_run;
-    p.ml[(slot * 16 + ql) * 2 + 1] = l_run;
-  }
+  write_partial<HD>(p, (size_t)(s * p.Hq + a) * p.slots + split, ql, lg, acc, m_run, l_run);
 }
 
 // ---------------------------------------------------------------------------
@@ -351,6 +469,10 @@ attn_lds(AttnArgs p) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int a = g * G + w;
   const int ql = lane & 15, lg = lane >> 4;
+  if (p.blk_wg && split == p.splits) {  // the block's own keys (whole workgroup)
+    block_partial<HD>(p, s, g, a, ql, lg);
+    return;
+  }
   const SeqDesc sd = p.seqs.s[s];
   const int kb = split * p.kps;
   const size_t plane = (size_t)sd.cap * HD;
@@ -432,20 +554,71 @@ attn_lds(AttnArgs p) {
   // no direct load may still be writing the ring when the workgroup ends
   attn_wait_vm<0>();
   l_run = rows4_sum(l_run);
-  // the partial, written through the L2 (the merge is another launch)
-  const size_t slot = ((size_t)(s * p.Hq + a) * p.splits + split);
-  float* out = p.acc + slot * 16 * HD;
-#pragma unroll
-  for (int h = 0; h < HT; ++h)
-    store16_wt(out, (uint32_t)((ql * HD + h * 16 + 4 * lg) * 4), acc[h]);
-  if (lg == 0) {
-    p.ml[(slot * 16 + ql) * 2 + 0] = m_run;
-    p.ml[(slot * 16 + ql) * 2 + 1] = l_run;
-  }
+  write_partial<HD>(p, (size_t)(s * p.Hq + a) * p.slots + split, ql, lg, acc, m_run, l_run);
 }
 
-// One workgroup per (block row, query head, sequence), one thread per output
-// dim (at least one wave). Each thread first requests its dim of the first
+// Merge of a head's partials, one thread per (block row, query head, dim):
+// with M the largest of the partials' running maxima,
+//   o = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
+// The block's own keys (the last slot; never empty, so M is finite) are
+// requested together with the first NB context splits, and the splits are
+// taken in order, NB per batch, folded into a running max (an empty split
+// has m = -inf and weight 0). The threads of a (row, head) read the same
+// (m, l) words, one request per wave. Scores are in log2 units (scaled by
+// log2(e)/sqrt(hd)), as in the split kernels.
+struct MergeArgs {
+  const float* acc;
+  const float* ml;
+  int Hq, Bl, splits, n_rows;  // splits: context splits (slots: splits + 1)
+  bf16_t *ob_h, *ob_l;
+};
+template <int HD, int NB>
+__global__ void __launch_bounds__(256)
+attn_merge(MergeArgs p) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int rh = t / HD, d = t % HD;  // rh = row * Hq + head
+  if (rh >= p.n_rows * p.Hq) return;
+  const int row = rh / p.Hq, a = rh % p.Hq;
+  const int s = row / p.Bl, r = row % p.Bl;
+  const size_t slot0 = (size_t)(s * p.Hq + a) * (p.splits + 1);
+  const float* pa = p.acc + (slot0 * 16 + r) * HD + d;
+  const float* pm = p.ml + (slot0 * 16 + r) * 2;
+  const size_t blk = (size_t)p.splits;
+  // the block's partial
+  float M = pm[blk * 32], L = pm[blk * 32 + 1], o = pa[blk * 16 * HD];
+  const int last = p.splits - 1;
+  for (int k0 = 0; k0 < p.splits; k0 += NB) {
+    float mk[NB], lk[NB], ak[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const size_t kk = (size_t)min(k0 + k, last);
+      mk[k] = pm[kk * 32];
+      lk[k] = pm[kk * 32 + 1];
+      ak[k] = pa[kk * 16 * HD];
+    }
+    float bm = M;
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+      if (k0 + k < p.splits) bm = fmaxf(bm, mk[k]);
+    const float c = __builtin_amdgcn_exp2f(M - bm);
+    L *= c;
+    o *= c;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const float wk = (k0 + k < p.splits && mk[k] != -INFINITY) ? __builtin_amdgcn_exp2f(mk[k] - bm) : 0.f;
+      L += wk * lk[k];
+      o += wk * ak[k];
+    }
+    M = bm;
+  }
+  const size_t i = (size_t)rh * HD + d;
+  split_bf16(o / L, p.ob_h[i], p.ob_l[i]);
+}
+
+// Merge that also takes the block's own keys (used when the context splits
+// are short, where a separate workgroup for the block would lengthen the
+// attention launch): one workgroup per (block row, query head, sequence),
+// one thread per output dim (at least one wave). Each thread first requests its dim of the first
 // MB split accumulators and of the block's Bl fp32 values (clamped
 // indices, straight-line loads). Wave 0 then forms the block scores: lane
 // 4j + t holds a quarter of the dims of block key j and of the query (hi +
@@ -458,7 +631,7 @@ attn_lds(AttnArgs p) {
 // Scores are in log2 units (scaled by log2(e)/sqrt(hd)), as in the split
 // kernels.
 static_assert(kAttnMaxSplits <= 128, "two splits per lane of wave 0");
-struct MergeArgs {
+struct MergeBlkArgs {
   const float* acc;
   const float* ml;
   const bf16_t *q, *q_lo;     // [M][Hq][hd]
@@ -471,7 +644,7 @@ struct MergeArgs {
 // few, so that no loads of clamped duplicates are issued)
 template <int HD, int MB>
 __global__ void __launch_bounds__(HD < 64 ? 64 : HD)
-attn_merge(MergeArgs p) {
+attn_merge_blk(MergeBlkArgs p) {
   constexpr int kMergeBatch = MB;
   constexpr int STRIDE = 16 * HD;  // floats between the splits of one (row, dim)
   constexpr int DPL = HD / 4;      // dims per lane of a block score
@@ -567,12 +740,14 @@ template <int HD>
 static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st) {
   AttnArgs p;
   p.q = L.q; p.q_lo = L.q_lo; p.acc = L.att_acc; p.ml = L.att_ml;
+  p.blk_k = L.blk_k; p.blk_v = L.blk_v;
   p.Hq = L.Hq; p.Hkv = L.Hkv; p.Bl = L.Bl; p.layer = layer;
   p.splits = L.att_splits; p.kps = L.att_keys_per_split;
+  p.blk_wg = L.att_blk_wg ? 1 : 0; p.slots = L.att_splits + p.blk_wg;
   p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)HD));
   p.seqs = *L.seqs;
   const int G = L.Hq / L.Hkv;
-  const dim3 grid(L.att_splits, L.Hkv, L.n_seqs);
+  const dim3 grid(p.slots, L.Hkv, L.n_seqs);
   // G query-head waves; groups of one or two heads also get two key columns.
   // Up to 256 threads per workgroup keep two register stages (the next chunk
   // in flight while one is processed); 512-thread groups of head_dim 128
@@ -598,14 +773,29 @@ static hipError_t launch_attn_hd(const DraftLaunch& L, int layer, hipStream_t st
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!p.blk_wg) {
+    MergeBlkArgs m;
+    m.acc = L.att_acc; m.ml = L.att_ml; m.q = L.q; m.q_lo = L.q_lo; m.blk_k = L.blk_k; m.blk_v = L.blk_v;
+    m.Hq = L.Hq; m.Hkv = L.Hkv; m.Bl = L.Bl; m.splits = L.att_splits; m.scale_log2 = p.scale_log2;
+    m.ob_h = L.ob_h; m.ob_l = L.ob_l;
+    if (L.att_splits <= 8)
+      hipLaunchKernelGGL((attn_merge_blk<HD, 8>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+    else
+      hipLaunchKernelGGL((attn_merge_blk<HD, 32>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+    return hipGetLastError();
+  }
   MergeArgs m;
-  m.acc = L.att_acc; m.ml = L.att_ml; m.q = L.q; m.q_lo = L.q_lo; m.blk_k = L.blk_k; m.blk_v = L.blk_v;
-  m.Hq = L.Hq; m.Hkv = L.Hkv; m.Bl = L.Bl; m.splits = L.att_splits; m.scale_log2 = p.scale_log2;
-  m.ob_h = L.ob_h; m.ob_l = L.ob_l;
-  if (L.att_splits <= 8)
-    hipLaunchKernelGGL((attn_merge<HD, 8>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+  m.acc = L.att_acc; m.ml = L.att_ml; m.Hq = L.Hq; m.Bl = L.Bl; m.splits = L.att_splits;
+  m.n_rows = L.n_seqs * L.Bl; m.ob_h = L.ob_h; m.ob_l = L.ob_l;
+  const int blocks = (m.n_rows * L.Hq * HD + 255) / 256;
+  // batches no wider than the splits need (a clamped duplicate is a request
+  // too), at most 32
+  if (m.splits <= 8)
+    hipLaunchKernelGGL((attn_merge<HD, 8>), dim3(blocks), dim3(256), 0, st, m);
+  else if (m.splits <= 16)
+    hipLaunchKernelGGL((attn_merge<HD, 16>), dim3(blocks), dim3(256), 0, st, m);
   else
-    hipLaunchKernelGGL((attn_merge<HD, 32>), dim3(L.Bl, L.Hq, L.n_seqs), dim3(HD < 64 ? 64 : HD), 0, st, m);
+    hipLaunchKernelGGL((attn_merge<HD, 32>), dim3(blocks), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 

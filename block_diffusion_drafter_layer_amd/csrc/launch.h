@@ -14,8 +14,14 @@ constexpr int kMaxLayers = 16;
 constexpr int kMaxFeat = 8;
 constexpr int kAttnMaxSplits = 128;
 constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots, at least
-constexpr int kAttnMinSplitsPerPair = 8;  // slots per (sequence, kv head) the workspace keeps
+// slots per (sequence, kv head) the workspace keeps: up to 8 context splits
+// and the block's own keys
+constexpr int kAttnMinSplitsPerPair = 9;
 constexpr int kAttnMaxKeysPerSplit = 512; // longer key ranges are split when slots allow
+// key ranges from which the block's own keys get a workgroup of their own
+// (it then runs beside splits at least this long); shorter ones leave the
+// block to the merge
+constexpr int kAttnBlockWgKeys = 128;
 inline int attn_slots(int max_seqs, int n_kv_heads) {
   const int s = max_seqs * n_kv_heads * kAttnMinSplitsPerPair;
   return s > kAttnSlotCap ? s : kAttnSlotCap;
@@ -67,6 +73,7 @@ struct DraftLaunch {
   float* att_acc;           // [slots*G][16][hd]
   float* att_ml;            // [slots*G][16][2]
   int att_splits, att_keys_per_split;
+  bool att_blk_wg;          // a workgroup of its own for the block's keys (else the merge)
   SplitWs split;
   GemmWs gemm;              // the tiled GEMM's split-K scratch (batches of more than 64 rows)
   // DFlash 2 convs in every layer (conv_gs == 0: none)
