@@ -1155,8 +1155,9 @@ lm_argmax_reduce(const uint64_t* __restrict__ part, int n_tiles, int M_lm, int B
 
 // Sum of a 32-column pair's slice partials of the LDS-staged kernel, in slice
 // order, then the epilogue. The row norms' sums of squares are fetched
-// together with the partials.
-template <class Epi>
+// together with the partials. FB: partials requested per batch (16 where
+// the slices are that many: one round trip instead of two).
+template <class Epi, int FB = kFinishBatch>
 __global__ void __launch_bounds__(256)
 stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ part) {
   __shared__ float tile[16][33];
@@ -1193,9 +1194,9 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   const float* p1 = p0 + (size_t)ks * 256;
   // the first batch of slice partials and the row sums of x^2 are requested
   // together (clamped addresses: no branch around any load)
-  float f0[kFinishBatch], f1[kFinishBatch];
+  float f0[FB], f1[FB];
 #pragma unroll
-  for (int k = 0; k < kFinishBatch; ++k) {
+  for (int k = 0; k < FB; ++k) {
     const int kk = k < ks ? k : ks - 1;
     f0[k] = p0[(size_t)kk * 256];
     f1[k] = p1[(size_t)kk * 256];
@@ -1207,17 +1208,17 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   }
   float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-  for (int k = 0; k < kFinishBatch; ++k)
+  for (int k = 0; k < FB; ++k)
     if (k < ks) { s0 += f0[k]; s1 += f1[k]; }  // slice order
-  for (int k0 = kFinishBatch; k0 < ks; k0 += kFinishBatch) {
-    float v0[kFinishBatch], v1[kFinishBatch];
+  for (int k0 = FB; k0 < ks; k0 += FB) {
+    float v0[FB], v1[FB];
 #pragma unroll
-    for (int k = 0; k < kFinishBatch; ++k) {
+    for (int k = 0; k < FB; ++k) {
       v0[k] = k0 + k < ks ? p0[(size_t)(k0 + k) * 256] : 0.f;
       v1[k] = k0 + k < ks ? p1[(size_t)(k0 + k) * 256] : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < kFinishBatch; ++k) { s0 += v0[k]; s1 += v1[k]; }  // slice order
+    for (int k = 0; k < FB; ++k) { s0 += v0[k]; s1 += v1[k]; }  // slice order
   }
   tile[m][n] = s0;
   tile[m][16 + n] = s1;
@@ -1376,8 +1377,12 @@ hipError_t launch_stream(const SkinnyA& a, const typename Epi::P& ep, int n_vcol
                        dim3(kSW * 64), 0, st, a, ep, n_vcols, ks, kc, ws.part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((stream_finish<Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, ks,
-                     ws.part);
+  if (ks > kFinishBatch)
+    hipLaunchKernelGGL((stream_finish<Epi, 2 * kFinishBatch>), dim3((n_vcols + 31) / 32), dim3(256), 0,
+                       st, a, ep, ks, ws.part);
+  else
+    hipLaunchKernelGGL((stream_finish<Epi>), dim3((n_vcols + 31) / 32), dim3(256), 0, st, a, ep, ks,
+                       ws.part);
   return hipGetLastError();
 }
 
