@@ -579,7 +579,7 @@ static dflash_status draft_impl(dflash_handle* h, int32_t n_seqs, dflash_kv* con
   // max_keys covers the whole cache, and the last split absorbs the rest
   splits = std::max(1, std::min(splits, max_keys / kps));
   L.att_splits = splits; L.att_keys_per_split = kps;
-  L.att_blk_wg = kps >= kAttnBlockWgKeys;
+  L.att_blk_wg = kps >= kAttnBlockWgKeys && (int64_t)splits * pairs > kAttnBlockWgMinWGs;
 
   hipStream_t st = h->stream;
   hipError_t e = timed(h, ST_EMBED, [&] { return launch_embed(L, st); });

@@ -18,10 +18,13 @@ constexpr int kAttnSlotCap = 1024;   // (sequence, kv head, split) partial slots
 // and the block's own keys
 constexpr int kAttnMinSplitsPerPair = 9;
 constexpr int kAttnMaxKeysPerSplit = 512; // longer key ranges are split when slots allow
-// key ranges from which the block's own keys get a workgroup of their own
-// (it then runs beside splits at least this long); shorter ones leave the
-// block to the merge
+// The block's own keys get a workgroup of their own per (sequence, kv head)
+// when the splits hold at least kAttnBlockWgKeys keys and the context's
+// workgroups already fill more than a round of the GPU (kAttnBlockWgMinWGs:
+// two per CU); otherwise the extra workgroups would share CUs with context
+// splits and lengthen the launch, and the merge takes the block keys.
 constexpr int kAttnBlockWgKeys = 128;
+constexpr int kAttnBlockWgMinWGs = 512;
 inline int attn_slots(int max_seqs, int n_kv_heads) {
   const int s = max_seqs * n_kv_heads * kAttnMinSplitsPerPair;
   return s > kAttnSlotCap ? s : kAttnSlotCap;

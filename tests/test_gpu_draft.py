@@ -95,24 +95,28 @@ def test_mid_shape_head_dim_128_group_8():
     _run(dc, [0, 45, 2900], gains="random")
 
 
+def _many_long_contexts(seed):
+    # 32 sequences up to 4500 keys: 64 (sequence, kv head) pairs x 9 splits
+    # of 480 keys, more context workgroups than two per CU, so the block's
+    # own keys take a workgroup of their own and the merge sums plain
+    # partials; an empty and a one-key context in the same call
+    rng = np.random.default_rng(seed)
+    return [4500, 0, 1] + [int(v) for v in rng.integers(0, 4500, size=29)]
+
+
 def test_mid_shape_head_dim_64_block_workgroup():
-    # head_dim 64 (the register-staged split kernel) with key ranges of
-    # >= 128 per split: the block's own keys take a workgroup of their own
-    # and the merge sums plain partials; an empty context in the same call
+    # head_dim 64: the register-staged split kernel
     dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=16, n_kv_heads=2, head_dim=64,
                            ffn=1024, vocab=2000, block_size=8, index=91)
-    _run(dc, [4100, 0, 4500], gains="random")
+    _run(dc, _many_long_contexts(91), gains="random", oracle_seqs=[0, 1, 2, 9])
 
 
 def test_mid_shape_group_2_block_workgroup():
-    # two query heads per kv head (two key columns per workgroup), 16
-    # sequences: splits of >= 128 keys, so the block's keys run in their own
-    # workgroup (one of its two key columns idle)
+    # two query heads per kv head: two key columns per workgroup, one of them
+    # idle in the block's workgroup
     dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=4, n_kv_heads=2, head_dim=64,
                            ffn=1024, vocab=2000, index=90)
-    rng = np.random.default_rng(90)
-    lens = [1100, 0, 1] + [int(v) for v in rng.integers(0, 1100, size=13)]
-    _run(dc, lens, gains="random", oracle_seqs=[0, 1, 2, 7])
+    _run(dc, _many_long_contexts(90), gains="random", oracle_seqs=[0, 1, 2, 7])
 
 
 def test_mid_shape_tall_batch():
