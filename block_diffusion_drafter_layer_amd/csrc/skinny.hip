@@ -131,38 +131,58 @@ struct EpiQKV {
     for (int d = threadIdx.x; d < p.hd / 2; d += blockDim.x)
       inv_f[d] = rope_rev_freq(d, p.hd, p.log2_theta);
     __syncthreads();
-    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
-      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+    // one thread per (row, 16-column group): the group's 8 RoPE pairs (or
+    // 16 V dims) are contiguous in the outputs, so each output is written
+    // with 16-byte stores
+    for (int e = threadIdx.x; e < ROWS * NG; e += blockDim.x) {
+      const int ml = e / NG, c = e % NG;
       const int m = m0 + ml;
       if (m >= M) continue;
-      const int pos = r_pos[ml];
-      const float x1 = tile[ml][c * 16 + j] * rs[ml];
-      const float x2 = tile[ml][c * 16 + j + 8] * rs[ml];
       const int vc = vc0 + c * 16;
       if (vc >= qd + 2 * kvd) continue;
+      const float r = rs[ml];
+      float x1[8], x2[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x1[j] = tile[ml][c * 16 + j] * r;
+        x2[j] = tile[ml][c * 16 + j + 8] * r;
+      }
       if (vc < qd + kvd) {
         const bool is_q = vc < qd;
         const int vcl = is_q ? vc : vc - qd;
         const int h = vcl / p.hd;
-        const int d = ((vcl % p.hd) >> 1) + j;  // group t covers dims 8t+j
-        float cs, sn;
-        rope_cs_rev(pos, inv_f[d], cs, sn);
-        const float o1 = x1 * cs - x2 * sn;
-        const float o2 = x2 * cs + x1 * sn;
+        const int d0 = (vcl % p.hd) >> 1;  // group t covers dims 8t .. 8t+7
+        const int pos = r_pos[ml];
+        float o1[8], o2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float cs, sn;
+          rope_cs_rev(pos, inv_f[d0 + j], cs, sn);
+          o1[j] = x1[j] * cs - x2[j] * sn;
+          o2[j] = x2[j] * cs + x1[j] * sn;
+        }
         if (is_q) {
-          const size_t qi = (size_t)m * qd + h * p.hd + d;
-          split_bf16(o1, p.q_out[qi], p.q_lo[qi]);
-          split_bf16(o2, p.q_out[qi + p.hd / 2], p.q_lo[qi + p.hd / 2]);
+          const size_t qi = (size_t)m * qd + h * p.hd + d0;
+          bf16x8 hi, lo;
+          pack_split_bf16x8(o1, hi, lo);
+          *reinterpret_cast<bf16x8*>(p.q_out + qi) = hi;
+          *reinterpret_cast<bf16x8*>(p.q_lo + qi) = lo;
+          pack_split_bf16x8(o2, hi, lo);
+          *reinterpret_cast<bf16x8*>(p.q_out + qi + p.hd / 2) = hi;
+          *reinterpret_cast<bf16x8*>(p.q_lo + qi + p.hd / 2) = lo;
         } else {
-          float* k = p.blk_k + (size_t)m * kvd + h * p.hd;
-          k[d] = o1;
-          k[d + p.hd / 2] = o2;
+          float* k = p.blk_k + (size_t)m * kvd + h * p.hd + d0;
+          *reinterpret_cast<float4*>(k) = make_float4(o1[0], o1[1], o1[2], o1[3]);
+          *reinterpret_cast<float4*>(k + 4) = make_float4(o1[4], o1[5], o1[6], o1[7]);
+          *reinterpret_cast<float4*>(k + p.hd / 2) = make_float4(o2[0], o2[1], o2[2], o2[3]);
+          *reinterpret_cast<float4*>(k + p.hd / 2 + 4) = make_float4(o2[4], o2[5], o2[6], o2[7]);
         }
       } else {
-        const int vi = vc - qd - kvd + j;  // dims vi and vi + 8 of the row's V
-        float* v = p.blk_v + (size_t)m * kvd;
-        v[vi] = x1;
-        v[vi + 8] = x2;
+        float* v = p.blk_v + (size_t)m * kvd + (vc - qd - kvd);  // dims vi .. vi + 15
+        *reinterpret_cast<float4*>(v) = make_float4(x1[0], x1[1], x1[2], x1[3]);
+        *reinterpret_cast<float4*>(v + 4) = make_float4(x1[4], x1[5], x1[6], x1[7]);
+        *reinterpret_cast<float4*>(v + 8) = make_float4(x2[0], x2[1], x2[2], x2[3]);
+        *reinterpret_cast<float4*>(v + 12) = make_float4(x2[4], x2[5], x2[6], x2[7]);
       }
     }
   }
@@ -254,18 +274,28 @@ struct EpiSwiglu {
   __device__ static void run(const P& p, float (*tile)[LD], const float* rs,
                              int vc0, int m0, int M) {
     constexpr int NG = VC / 16;
-    for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
-      const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
+    // one thread per (row, 16-column group): its 8 gate/up pairs are 8
+    // consecutive activation columns, written as 16-byte stores (F is a
+    // multiple of 8 on every path that gets here: checked on the host)
+    for (int e = threadIdx.x; e < ROWS * NG; e += blockDim.x) {
+      const int ml = e / NG, c = e % NG;
       const int m = m0 + ml;
       if (m >= M || vc0 + c * 16 >= p.n_vcols) continue;
-      const float g = tile[ml][c * 16 + j] * rs[ml];
-      const float u = tile[ml][c * 16 + j + 8] * rs[ml];
-      // silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal (each
-      // within about an ulp); -g past the exponent range gives 1/inf = 0
-      const float a = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f)) * u;
-      const int f = ((vc0 >> 4) + c) * 8 + j;
-      const size_t i = (size_t)m * p.F + f;
-      split_bf16(a, p.ah[i], p.al[i]);
+      const float r = rs[ml];
+      float a[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float g = tile[ml][c * 16 + j] * r;
+        const float u = tile[ml][c * 16 + j + 8] * r;
+        // silu(g) = g / (1 + e^-g) from the hardware exp2 and reciprocal
+        // (each within about an ulp); -g past the exponent range gives 1/inf = 0
+        a[j] = g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f)) * u;
+      }
+      const size_t i = (size_t)m * p.F + ((vc0 >> 4) + c) * 8;
+      bf16x8 hi, lo;
+      pack_split_bf16x8(a, hi, lo);
+      *reinterpret_cast<bf16x8*>(p.ah + i) = hi;
+      *reinterpret_cast<bf16x8*>(p.al + i) = lo;
     }
   }
 };
