@@ -209,48 +209,65 @@ struct EpiResid {
   __device__ static void run(const P& p, float (*tile)[LD], const float*,
                              int vc0, int m0, int M) {
     static_assert(VC % 32 == 0, "whole 32-column norm groups per workgroup");
-    // U elements per thread at a time: their x and gain loads go out
-    // together (clamped addresses), then the in-place updates (a
-    // load-update-store per iteration would wait for each load); the tall
-    // path's 64-row slices (512 threads) take them in two batches
-    constexpr int U = ROWS >= 64 ? 16 : 8;
-    for (int e0 = threadIdx.x; e0 < ROWS * VC; e0 += U * blockDim.x) {
-      float xo[U];
-      bf16_t go[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * blockDim.x;
-        const int ml = e / VC, c = e % VC;
-        int m = m0 + ml, n = vc0 + c;
-        m = m < M ? m : M - 1;
-        n = n < p.n_vcols ? n : p.n_vcols - 1;
-        xo[u] = p.x[(size_t)m * p.D + n];
-        go[u] = p.gain[n];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * blockDim.x;
-        const int ml = e / VC, c = e % VC;
-        const int m = m0 + ml;
-        const int n = vc0 + c;
-        if (e >= ROWS * VC || m >= M || n >= p.n_vcols) continue;
-        const size_t i = (size_t)m * p.D + n;
-        const float xn = xo[u] + tile[ml][c];
-        p.x[i] = xn;
-        if (p.hidden) p.hidden[i] = xn;
-        split_bf16(xn * bf2f(go[u]), p.xh[i], p.xl[i]);
-        tile[ml][c] = xn * xn;
-      }
-    }
-    __syncthreads();
+    // one thread per (row, 8 consecutive columns): x and the gain read and x,
+    // the hidden copy and the next norm's hi/lo input written as 16- and
+    // 32-byte pieces; the four threads of a 32-column norm group are a DPP
+    // quartet, which sums the group's x^2. U items per thread have their
+    // loads in flight together (clamped addresses); the tall path's 64-row
+    // slices (512 threads) take all of theirs in one batch. (D is a multiple
+    // of 32, so an 8-column piece is wholly inside or outside the matrix.)
+    constexpr int C8 = VC / 8;
+    constexpr int U = ROWS >= 64 ? 4 : 1;
     const int ng = p.D / 32;
-    for (int e = threadIdx.x; e < ROWS * (VC / 32); e += blockDim.x) {
-      const int ml = e / (VC / 32), g = e % (VC / 32);
-      if (m0 + ml >= M || vc0 + g * 32 >= p.n_vcols) continue;
-      float s = 0.f;
-#pragma unroll 8
-      for (int c = 0; c < 32; ++c) s += tile[ml][g * 32 + c];
-      p.ssq[(size_t)(m0 + ml) * ng + vc0 / 32 + g] = s;
+    for (int e0 = threadIdx.x; e0 < ROWS * C8; e0 += U * blockDim.x) {
+      float4 xo[U][2];
+      u32x4 go[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * blockDim.x;
+        const int ml = e / C8, c8 = e % C8;
+        int m = m0 + ml, n = vc0 + 8 * c8;
+        m = m < M ? m : M - 1;
+        n = n < p.n_vcols ? n : p.n_vcols - 8;
+        const float4* xr = reinterpret_cast<const float4*>(p.x + (size_t)m * p.D + n);
+        xo[u][0] = xr[0];
+        xo[u][1] = xr[1];
+        go[u] = *reinterpret_cast<const u32x4*>(p.gain + n);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * blockDim.x;
+        const int ml = e / C8, c8 = e % C8;
+        const int m = m0 + ml;
+        const int n = vc0 + 8 * c8;
+        const bool live = e < ROWS * C8 && m < M && n < p.n_vcols;
+        const float x8[8] = {xo[u][0].x, xo[u][0].y, xo[u][0].z, xo[u][0].w,
+                             xo[u][1].x, xo[u][1].y, xo[u][1].z, xo[u][1].w};
+        float xn[8], xg[8], sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          xn[j] = x8[j] + tile[live ? ml : 0][8 * c8 + j];
+          const uint32_t gw = go[u][j >> 1];
+          xg[j] = xn[j] * __uint_as_float(j & 1 ? gw & 0xffff0000u : gw << 16);
+          sq += xn[j] * xn[j];
+        }
+        sq = quad_sum(sq);  // the row's 32-column group (all four lanes take part)
+        if (!live) continue;
+        const size_t i = (size_t)m * p.D + n;
+        float4* xw = reinterpret_cast<float4*>(p.x + i);
+        xw[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
+        xw[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
+        if (p.hidden) {
+          float4* hw = reinterpret_cast<float4*>(p.hidden + i);
+          hw[0] = make_float4(xn[0], xn[1], xn[2], xn[3]);
+          hw[1] = make_float4(xn[4], xn[5], xn[6], xn[7]);
+        }
+        bf16x8 hi, lo;
+        pack_split_bf16x8(xg, hi, lo);
+        *reinterpret_cast<bf16x8*>(p.xh + i) = hi;
+        *reinterpret_cast<bf16x8*>(p.xl + i) = lo;
+        if ((c8 & 3) == 0) p.ssq[(size_t)m * ng + n / 32] = sq;
+      }
     }
   }
 };
@@ -1198,9 +1215,9 @@ stream_finish(SkinnyA a, typename Epi::P ep, int ks, const float* __restrict__ p
   int warm = 0;
   if constexpr (std::is_same<Epi, EpiQKV>::value)
     if (ep.seqs.len_dev && (int)threadIdx.x < a.M / ep.Bl) warm = ep.seqs.len_dev[threadIdx.x];
-  // the residual epilogue reads x and the norm gain of its elements: request
-  // them now as well (the epilogue's thread-to-element map, 2 per thread)
-  // (loaded into registers that are only named at the very end, so that no
+  // the residual epilogue reads x and the norm gain of the pair's columns:
+  // request their cache lines now as well, two elements per thread (loaded
+  // into registers that are only named at the very end, so that no
   // instruction waits for them before the epilogue)
   float warm_x[2] = {0.f, 0.f};
   uint32_t warm_g[2] = {0u, 0u};
