@@ -119,23 +119,23 @@ struct EpiInject {
       }
     }
     __syncthreads();
-    // K: quads of pair slots (slot k covers virtual columns g*PW + o and
-    // g*PW + o + PW/2, g = k / hw, o = k % hw); a quad is four consecutive
-    // dims of one head (hw is a multiple of 4), rotated and stored as two
-    // 8-byte pieces of the position's row. Consecutive threads take
-    // consecutive quads of one row.
+    // K: octets of pair slots (slot k covers virtual columns g*PW + o and
+    // g*PW + o + PW/2, g = k / hw, o = k % hw); an octet is eight consecutive
+    // dims of one head (hw is a multiple of 8), rotated and stored as two
+    // 16-byte pieces of the position's row. Consecutive threads take
+    // consecutive octets of one row.
     const int hd2 = p.hd >> 1;
-    for (int e = threadIdx.x; e < kSlice * (BN / 8); e += blockDim.x) {
-      const int r = e / (BN / 8), k = 4 * (e % (BN / 8));
+    for (int e = threadIdx.x; e < kSlice * (BN / 16); e += blockDim.x) {
+      const int r = e / (BN / 16), k = 8 * (e % (BN / 16));
       const int g = k / hw, o = k - g * hw;
       const int c1 = g * PW + o, c2 = c1 + hw;
       const int m = m0 + r;
       const int pl = col_plane[c1], dv = col_dim[c1];
       if (m >= M || pl < 0 || (dv & kVFlag)) continue;
       const int pos = p.pos0 + m, d = dv;
-      float o1[4], o2[4];
+      float o1[8], o2[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 8; ++i) {
         float cs, sn;
         rope_cs_inv(pos, col_inv[c1 + i], cs, sn);
         const float x1 = C[r * ld + c1 + i], x2 = C[r * ld + c2 + i];
@@ -143,24 +143,29 @@ struct EpiInject {
         o2[i] = x2 * cs + x1 * sn;
       }
       bf16_t* kp = p.kv + (size_t)pl * plane + (size_t)pos * p.hd;
-      *reinterpret_cast<uint2*>(kp + d) = make_uint2(f2bf2(o1[0], o1[1]), f2bf2(o1[2], o1[3]));
-      *reinterpret_cast<uint2*>(kp + d + hd2) = make_uint2(f2bf2(o2[0], o2[1]), f2bf2(o2[2], o2[3]));
+      *reinterpret_cast<bf16x8*>(kp + d) = pack_bf16x8(o1);
+      *reinterpret_cast<bf16x8*>(kp + d + hd2) = pack_bf16x8(o2);
     }
-    // V (dim-major planes: a dim's positions are contiguous): four
-    // consecutive rows of one column per thread, one 8-byte store where the
-    // position allows; sixteen threads cover a column's 64 rows
-    for (int e = threadIdx.x; e < (kSlice / 4) * BN; e += blockDim.x) {
-      const int c = e / (kSlice / 4), r = 4 * (e % (kSlice / 4));
+    // V (dim-major planes: a dim's positions are contiguous): eight
+    // consecutive rows of one column per thread, one 16-byte store where the
+    // position allows (two 8-byte ones at a multiple of 4); eight threads
+    // cover a column's 64 rows
+    for (int e = threadIdx.x; e < (kSlice / 8) * BN; e += blockDim.x) {
+      const int c = e / (kSlice / 8), r = 8 * (e % (kSlice / 8));
       const int pl = col_plane[c], dv = col_dim[c];
       const int m = m0 + r;
       if (m >= M || pl < 0 || !(dv & kVFlag)) continue;
       const int pos = p.pos0 + m;
       bf16_t* vp = p.kv + (size_t)pl * plane + (size_t)(dv & (kVFlag - 1)) * p.cap + pos;
       const float* x = C + r * ld + c;
-      if (m + 4 <= M && (pos & 3) == 0) {
+      if (m + 8 <= M && (pos & 7) == 0) {
+        *reinterpret_cast<u32x4*>(vp) = u32x4{f2bf2(x[0], x[ld]), f2bf2(x[2 * ld], x[3 * ld]),
+                                              f2bf2(x[4 * ld], x[5 * ld]), f2bf2(x[6 * ld], x[7 * ld])};
+      } else if (m + 8 <= M && (pos & 3) == 0) {
         *reinterpret_cast<uint2*>(vp) = make_uint2(f2bf2(x[0], x[ld]), f2bf2(x[2 * ld], x[3 * ld]));
+        *reinterpret_cast<uint2*>(vp + 4) = make_uint2(f2bf2(x[4 * ld], x[5 * ld]), f2bf2(x[6 * ld], x[7 * ld]));
       } else {
-        for (int i = 0; i < 4 && m + i < M; ++i) vp[i] = f2bf(x[i * ld]);
+        for (int i = 0; i < 8 && m + i < M; ++i) vp[i] = f2bf(x[i * ld]);
       }
     }
   }
