@@ -222,6 +222,18 @@ def test_device_rounds_qwen_shape_two_sequences():
     _rounds_dev(dc, [dc.ctx_len, dc.ctx_len - 37], 3, salt=1)
 
 
+def test_device_rounds_many_sequences_block_workgroup():
+    # 32 sequences with caches of up to ~4.25k rows: with device-resident
+    # lengths the attention is planned for the caches' capacity (9 splits of
+    # 448 keys x 64 (sequence, kv head) pairs), so the block's own keys run in
+    # a workgroup of their own; the contexts grow by the appended rows
+    dc = CONFIGS[1].shrink(hidden=512, n_layers=1, n_heads=8, n_kv_heads=2, ffn=1024,
+                           vocab=4096, index=88)
+    rng = np.random.default_rng(88)
+    S0s = [4200, 1, 33] + [int(v) for v in rng.integers(1, 4200, size=29)]
+    _rounds_dev(dc, S0s, 2, salt=5)
+
+
 def test_device_round_graph_replays_match_eager():
     """One device-resident round captured into a graph (draft from device
     lengths, verify, append, trim back) and replayed; every replay must give
