@@ -206,26 +206,15 @@ __device__ __forceinline__ double philox_uniform(uint64_t seed, uint64_t row, ui
 }
 
 // RoPE angle for position `pos` and pair index d of a head of size hd:
-// pos * theta^(-2d/hd), formed and reduced modulo 2*pi in fp64, then cos/sin
-// in fp32 of the reduced angle.
+// pos * theta^(-2d/hd) radians. The rotation is formed from the frequency in
+// revolutions per position (theta^(-2d/hd) / 2 pi): the angle pos * f is
+// formed and reduced to [-1/2, 1/2] revolution in fp64, then the hardware
+// sine and cosine, which take revolutions (max abs error ~1.2e-7 on that
+// range, measured against fp64), in place of a library sincosf of the
+// reduced angle.
 __device__ __forceinline__ double rope_inv_freq(int d, int hd, double log2_theta) {
   return exp2(-2.0 * (double)d / (double)hd * log2_theta);
 }
-__device__ __forceinline__ void rope_cs_inv(int pos, double inv, float& c, float& s) {
-  double a = (double)pos * inv;
-  const double two_pi = 6.283185307179586476925286766559;
-  a -= two_pi * rint(a / two_pi);
-  sincosf((float)a, &s, &c);
-}
-__device__ __forceinline__ void rope_cs(int pos, int d, int hd, double log2_theta,
-                                        float& c, float& s) {
-  rope_cs_inv(pos, rope_inv_freq(d, hd, log2_theta), c, s);
-}
-// The same rotation from the frequency in revolutions per position
-// (theta^(-2d/hd) / 2 pi): the angle pos * f is formed and reduced to
-// [-1/2, 1/2] revolution in fp64, then the hardware sine and cosine, which
-// take revolutions (max abs error ~1.2e-7 on that range, measured against
-// fp64), in place of a library sincosf of the reduced angle.
 __device__ __forceinline__ double rope_rev_freq(int d, int hd, double log2_theta) {
   return rope_inv_freq(d, hd, log2_theta) * 0.15915494309189533577;  // 1 / (2 pi)
 }

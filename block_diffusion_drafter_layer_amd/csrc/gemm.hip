@@ -103,7 +103,9 @@ struct EpiInject {
     const int PW = p.hd < 64 ? p.hd : 64, hw = PW >> 1;
     // the tile's column table, in LDS after the slice (16 bytes a column),
     // once per slice: plane index (-1 past N), dim (| kVFlag for V), RoPE
-    // frequency; the per-element work is then a table read
+    // frequency in revolutions per position; the per-element work is then a
+    // table read, an fp64 product reduced to [-1/2, 1/2] revolution and the
+    // hardware sine and cosine
     int* col_plane = reinterpret_cast<int*>(const_cast<float*>(C) + kSlice * ld);
     int* col_dim = col_plane + BN;
     double* col_inv = reinterpret_cast<double*>(col_dim + BN);
@@ -113,7 +115,7 @@ struct EpiInject {
         const InjectCol ci = inject_col(n, p.Hkv, p.hd);
         col_plane[c] = (2 * ci.layer + (ci.is_k ? 0 : 1)) * p.Hkv + ci.head;
         col_dim[c] = ci.dim | (ci.is_k ? 0 : kVFlag);
-        col_inv[c] = ci.is_k ? rope_inv_freq(ci.dim, p.hd, p.log2_theta) : 0.0;
+        col_inv[c] = ci.is_k ? rope_rev_freq(ci.dim, p.hd, p.log2_theta) : 0.0;
       } else {
         col_plane[c] = -1;
       }
@@ -137,7 +139,7 @@ struct EpiInject {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float cs, sn;
-        rope_cs_inv(pos, col_inv[c1 + i], cs, sn);
+        rope_cs_rev(pos, col_inv[c1 + i], cs, sn);
         const float x1 = C[r * ld + c1 + i], x2 = C[r * ld + c2 + i];
         o1[i] = x1 * cs - x2 * sn;
         o2[i] = x2 * cs + x1 * sn;

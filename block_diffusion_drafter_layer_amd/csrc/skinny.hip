@@ -476,6 +476,10 @@ struct EpiInjectRows {
     const int kvd = p.Hkv * p.hd;
     const size_t plane = (size_t)p.cap * p.hd;
     constexpr int NG = VC / 16;
+    // the rotation frequencies (revolutions per position) once per call
+    __shared__ double inv_f[kMaxHeadDim / 2];
+    for (int d = threadIdx.x; d < p.hd / 2; d += blockDim.x) inv_f[d] = rope_rev_freq(d, p.hd, p.log2_theta);
+    __syncthreads();
     for (int e = threadIdx.x; e < ROWS * NG * 8; e += blockDim.x) {
       const int ml = e / (NG * 8), c = (e / 8) % NG, j = e % 8;
       const int m = m0 + ml;
@@ -488,7 +492,7 @@ struct EpiInjectRows {
       if (r < kvd) {
         const int h = r / p.hd, d = ((r % p.hd) >> 1) + j;
         float cs, sn;
-        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        rope_cs_rev(pos, inv_f[d], cs, sn);
         bf16_t* k = p.kv + (size_t)((2 * i) * p.Hkv + h) * plane + (size_t)pos * p.hd;
         k[d] = f2bf(x1 * cs - x2 * sn);
         k[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
@@ -543,6 +547,9 @@ struct EpiAppendRows {
     // each row's position (-1: not appended) and cache once, through LDS
     __shared__ int r_pos[ROWS], r_cap[ROWS];
     __shared__ bf16_t* r_kv[ROWS];
+    // and the rotation frequencies (revolutions per position)
+    __shared__ double inv_f[kMaxHeadDim / 2];
+    for (int d = threadIdx.x; d < p.hd / 2; d += blockDim.x) inv_f[d] = rope_rev_freq(d, p.hd, p.log2_theta);
     for (int ml = threadIdx.x; ml < ROWS; ml += blockDim.x) {
       const int m = m0 + ml;
       int pos = -1;
@@ -573,7 +580,7 @@ struct EpiAppendRows {
       if (r < kvd) {
         const int h = r / p.hd, d = ((r % p.hd) >> 1) + j;
         float cs, sn;
-        rope_cs(pos, d, p.hd, p.log2_theta, cs, sn);
+        rope_cs_rev(pos, inv_f[d], cs, sn);
         bf16_t* k = sd.kv + (size_t)((2 * i) * p.Hkv + h) * plane + (size_t)pos * p.hd;
         k[d] = f2bf(x1 * cs - x2 * sn);
         k[d + p.hd / 2] = f2bf(x2 * cs + x1 * sn);
