@@ -166,6 +166,14 @@ def test_qwen_shape_block16_ctx2048_full_size():
     _run(CONFIGS[1], [2048], logits=True)
 
 
+def test_qwen_shape_two_sequences_block8_and_short_block():
+    # 16 and 7 rows at the Qwen shape on the weight-streaming kernels: two
+    # sequences' RoPE positions in one 16-row tile, and a tile with rows past
+    # the block's end
+    _run(CONFIGS[1], [2048, 1500], bl=8)
+    _run(CONFIGS[1], [777], bl=7, logits=True)
+
+
 def test_qwen_shape_32_ragged_sequences_sampled():
     dc = CONFIGS[3]
     lens = synth.ragged_lengths(32)
