@@ -39,9 +39,9 @@
 // operand may be read through segments (k in [j*seg_k, (j+1)*seg_k) reads
 // seg[j]) and a row map; B rows are Epi::wrow(p, n) and their k index wraps
 // at b_k. A bf16 hi/lo pair of activations is multiplied "stacked": the
-// tile's upper 128 A rows are the hi halves of 128 output rows and its lower
-// 128 the lo halves of the same rows, against one B tile, and the epilogue
-// adds the two halves. Each B tile is then read once per 128 output rows
+// tile's A rows 2j and 2j + 1 are the hi and lo halves of output row j (128
+// output rows per tile), against one B tile; the two products land in
+// adjacent items of one lane, and the epilogue adds them in registers. Each B tile is then read once per 128 output rows
 // (the alternative, [hi | lo] x [W | W] over 2K, reads it twice per 256 rows
 // with the two reads K apart, which no cache keeps).
 #pragma once
@@ -241,8 +241,8 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   for (int q = 0; q < kLoadsA; ++q) {
     const int b = w + kWaves * q;
     const int r = 8 * b + lrow;
-    const bool lo = a.stack && r >= BMH;
-    int m = m0 + (a.stack ? r % BMH : r);
+    const bool lo = a.stack && (r & 1);
+    int m = m0 + (a.stack ? r >> 1 : r);
     m = m < a.M ? m : a.M - 1;
     m = (m / a.a_group) * a.a_stride + a.a_off + m % a.a_group;
     aoff[q] = (int64_t)m * a.ld + lchunk(b) + (lo ? a.lo_off : 0);
@@ -414,27 +414,23 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   float* C = reinterpret_cast<float*>(smem);
   __syncthreads();  // every wave is done with the ring
   if (a.stack) {
-    // slice sl: the hi rows' products are stored, then the lo rows' added
-    // (each element has one writer per phase)
+    // tile rows 2j and 2j + 1 (the hi and lo halves of output row j) sit in
+    // items v and v + 1 of one lane: their sum is stored once per slice
 #pragma unroll
     for (int sl = 0; sl < BMH / kSlice; ++sl) {
 #pragma unroll
-      for (int ph = 0; ph < 2; ++ph) {
+      for (int i = 0; i < TI; ++i) {
+        const int r0 = wm * WM + i * 32;
+        if ((r0 >> 1) / kSlice != sl) continue;
 #pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int r0 = wm * WM + i * 32;
-          if (r0 / BMH != ph || (r0 % BMH) / kSlice != sl) continue;
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = r0 % kSlice + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-              float& c = C[r * CLD + wn * WN + j * 32 + fr];
-              c = ph ? c + acc[i][j][v] : acc[i][j][v];
-            }
-        }
-        __syncthreads();
+          for (int v = 0; v < 16; v += 2) {
+            const int r = r0 % (2 * kSlice) + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            C[(r >> 1) * CLD + wn * WN + j * 32 + fr] = acc[i][j][v] + acc[i][j][v + 1];
+          }
       }
+      __syncthreads();
       Epi::template run<BN>(p, C, CLD, m0 + sl * kSlice, n0, a.M);
       __syncthreads();
     }
