@@ -353,17 +353,34 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   if (sp.S > 1) {
     // publish this split's partial (lane-major: 1 KB per store instruction),
     // then count in; the last to arrive sums every partial in split order
+    // (stacked tiles: the hi + lo sums only, items 2k + 1 left at zero by the
+    // last arriver, so half the partial bytes)
     const int tile = rt * tn + ct;
     float* mine = sp.part + ((size_t)tile * sp.S + sidx) * (BM * BN);
+    const int NQ = a.stack ? 2 : 4;  // 16-byte pieces per lane and 32x32 block
+    if (a.stack) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          store16_wt(mine, (uint32_t)(((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 16), v);
-        }
+          for (int q = 0; q < 2; ++q) {
+            const int b = 8 * q;
+            f32x4 v = {acc[i][j][b] + acc[i][j][b + 1], acc[i][j][b + 2] + acc[i][j][b + 3],
+                       acc[i][j][b + 4] + acc[i][j][b + 5], acc[i][j][b + 6] + acc[i][j][b + 7]};
+            store16_wt(mine, (uint32_t)(((((w * TI + i) * TJ + j) * 2 + q) * 64 + lane) * 16), v);
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            store16_wt(mine, (uint32_t)(((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 16), v);
+          }
+    }
     // this wave's partial is written (through the L2: the release below then
     // has little to write back)
     __builtin_amdgcn_s_waitcnt(DFL_VM(0));
@@ -397,14 +414,24 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
         for (int j = 0; j < TJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            v[j][q] = *reinterpret_cast<const f32x4*>(
-                src + ((((w * TI + i) * TJ + j) * 4 + q) * 64 + lane) * 4);
+            if (q < NQ)
+              v[j][q] = *reinterpret_cast<const f32x4*>(
+                  src + ((((w * TI + i) * TJ + j) * NQ + q) * 64 + lane) * 4);
+        if (a.stack) {
 #pragma unroll
-        for (int j = 0; j < TJ; ++j)
+          for (int j = 0; j < TJ; ++j)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j][q][e];
+              for (int e = 0; e < 4; ++e) acc[i][j][8 * q + 2 * e] += v[j][q][e];
+        } else {
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[j][q][e];
+        }
       }
     }
   }
