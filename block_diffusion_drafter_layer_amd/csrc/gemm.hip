@@ -18,6 +18,7 @@
 namespace dfl {
 
 struct EpiFuse {
+  static constexpr bool kStack = false;
   struct P {
     const bf16_t* w;  // [N][K]
     int K, N;
@@ -83,6 +84,7 @@ __device__ __forceinline__ InjectCol inject_col(int vc, int Hkv, int hd) {
 }
 
 struct EpiInject {
+  static constexpr bool kStack = false;
   struct P {
     const bf16_t* wk[kMaxLayers];
     const bf16_t* wv[kMaxLayers];

@@ -1457,6 +1457,7 @@ bool uses_stream(const SkinnyA& a, int n_vcols, const SplitWs& ws, int& ks) {
 // in place.
 template <class E>
 struct EpiTiled {
+  static constexpr bool kStack = true;  // the draft's hi/lo activations
   struct P {
     typename E::P ep;
     const float* ssq;  // optional: per-row partial sums of x^2 [rows_in][ssq_ld]

@@ -29,7 +29,8 @@
 // meet in one L2. Nobody waits for anybody, so there is no co-residency
 // requirement.
 //
-// Epi supplies wrow(p, n) (B row n), prologue(p, m0, rows, M) (run by every
+// Epi supplies kStack (whether its tiles are stacked hi/lo pairs, below),
+// wrow(p, n) (B row n), prologue(p, m0, rows, M) (run by every
 // workgroup after its first loads are issued; it may read memory and write
 // LDS of its own for the epilogue) and run<BN>(p, C, ld, m0, n0, M) (a
 // 64-row slice of the tile in LDS).
@@ -218,7 +219,10 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / WGN, wn = w % WGN;
   constexpr int BMH = BM / 2;
-  const int bm_out = a.stack ? BMH : BM;  // output rows per tile
+  // stacked hi/lo tiles are a property of the epilogue type, so that each
+  // instantiation holds one layout's code (both in one kernel spilled)
+  constexpr bool ST = Epi::kStack;
+  const int bm_out = ST ? BMH : BM;  // output rows per tile
   const int tm = (a.M + bm_out - 1) / bm_out, tn = (N + BN - 1) / BN;
   int rt, ct, sidx;
   if (!tile_of(blockIdx.x, tm, tn, sp.S, rt, ct, sidx)) return;
@@ -241,8 +245,8 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   for (int q = 0; q < kLoadsA; ++q) {
     const int b = w + kWaves * q;
     const int r = 8 * b + lrow;
-    const bool lo = a.stack && (r & 1);
-    int m = m0 + (a.stack ? r >> 1 : r);
+    const bool lo = ST && (r & 1);
+    int m = m0 + (ST ? r >> 1 : r);
     m = m < a.M ? m : a.M - 1;
     m = (m / a.a_group) * a.a_stride + a.a_off + m % a.a_group;
     aoff[q] = (int64_t)m * a.ld + lchunk(b) + (lo ? a.lo_off : 0);
@@ -357,8 +361,8 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
     // last arriver, so half the partial bytes)
     const int tile = rt * tn + ct;
     float* mine = sp.part + ((size_t)tile * sp.S + sidx) * (BM * BN);
-    const int NQ = a.stack ? 2 : 4;  // 16-byte pieces per lane and 32x32 block
-    if (a.stack) {
+    constexpr int NQ = ST ? 2 : 4;  // 16-byte pieces per lane and 32x32 block
+    if constexpr (ST) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -417,7 +421,7 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
             if (q < NQ)
               v[j][q] = *reinterpret_cast<const f32x4*>(
                   src + ((((w * TI + i) * TJ + j) * NQ + q) * 64 + lane) * 4);
-        if (a.stack) {
+        if constexpr (ST) {
 #pragma unroll
           for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -440,7 +444,7 @@ ctx_gemm(GemmA a, typename Epi::P p, int N, GemmSplit sp) {
   constexpr int CLD = BN + 8;
   float* C = reinterpret_cast<float*>(smem);
   __syncthreads();  // every wave is done with the ring
-  if (a.stack) {
+  if constexpr (ST) {
     // tile rows 2j and 2j + 1 (the hi and lo halves of output row j) sit in
     // items v and v + 1 of one lane: their sum is stored once per slice
 #pragma unroll
@@ -499,6 +503,7 @@ static hipError_t launch_tiled(const GemmA& a, const typename Epi::P& p, int N, 
                                hipStream_t st, int max_split = kGemmMaxSplit, int min_k = 1024) {
   // whole 64-wide k stages, none straddling an A segment or B's wrap
   if (a.K % BK || a.seg_k % BK || a.b_k % BK) return hipErrorInvalidValue;
+  if ((a.stack != 0) != Epi::kStack) return hipErrorInvalidValue;
   const int bm_out = a.stack ? BM / 2 : BM;
   const int tiles = ((a.M + bm_out - 1) / bm_out) * ((N + BN - 1) / BN);
   GemmSplit sp;
