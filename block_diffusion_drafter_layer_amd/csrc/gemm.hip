@@ -123,28 +123,38 @@ struct EpiInject {
       }
     }
     __syncthreads();
-    // K: octets of pair slots (slot k covers virtual columns g*PW + o and
-    // g*PW + o + PW/2, g = k / hw, o = k % hw); an octet is eight consecutive
-    // dims of one head (hw is a multiple of 8), rotated and stored as two
-    // 16-byte pieces of the position's row. Consecutive threads take
-    // consecutive octets of one row.
+    // K: octets of pair slots (the slots of column group g cover virtual
+    // columns g*PW + o and g*PW + o + PW/2, o < hw); an octet is eight
+    // consecutive dims of one head (hw is a multiple of 8), rotated and
+    // stored as two 16-byte pieces of the position's row. A wave takes the
+    // octets of one column group on consecutive rows, and each thread reads
+    // the two 16-byte halves of an octet in the order of its lane's parity:
+    // with the slice's row pitch at 8 words mod 64, one read instruction then
+    // starts at 16 distinct bank quartets (octets of one row side by side
+    // started at only the 8 multiples of 8, a 15-way conflict).
     const int hd2 = p.hd >> 1;
+    const int opg = hw >> 3;  // octets per column group
     for (int e = threadIdx.x; e < kSlice * (BN / 16); e += blockDim.x) {
-      const int r = e / (BN / 16), k = 8 * (e % (BN / 16));
-      const int g = k / hw, o = k - g * hw;
-      const int c1 = g * PW + o, c2 = c1 + hw;
+      const int oi = e % opg, r = (e / opg) % kSlice, g = e / (opg * kSlice);
+      const int c1 = g * PW + 8 * oi, c2 = c1 + hw;
       const int m = m0 + r;
       const int pl = col_plane[c1], dv = col_dim[c1];
       if (m >= M || pl < 0 || (dv & kVFlag)) continue;
       const int pos = p.pos0 + m, d = dv;
+      const int h = e & 1;
+      const float4* q1 = reinterpret_cast<const float4*>(C + r * ld + c1);
+      const float4* q2 = reinterpret_cast<const float4*>(C + r * ld + c2);
+      const float4 a0 = q1[h], a1 = q1[h ^ 1], b0 = q2[h], b1 = q2[h ^ 1];
+      const float4 x1l = h ? a1 : a0, x1h = h ? a0 : a1, x2l = h ? b1 : b0, x2h = h ? b0 : b1;
+      const float x1[8] = {x1l.x, x1l.y, x1l.z, x1l.w, x1h.x, x1h.y, x1h.z, x1h.w};
+      const float x2[8] = {x2l.x, x2l.y, x2l.z, x2l.w, x2h.x, x2h.y, x2h.z, x2h.w};
       float o1[8], o2[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float cs, sn;
         rope_cs_rev(pos, col_inv[c1 + i], cs, sn);
-        const float x1 = C[r * ld + c1 + i], x2 = C[r * ld + c2 + i];
-        o1[i] = x1 * cs - x2 * sn;
-        o2[i] = x2 * cs + x1 * sn;
+        o1[i] = x1[i] * cs - x2[i] * sn;
+        o2[i] = x2[i] * cs + x1[i] * sn;
       }
       bf16_t* kp = p.kv + (size_t)pl * plane + (size_t)pos * p.hd;
       *reinterpret_cast<bf16x8*>(kp + d) = pack_bf16x8(o1);
