@@ -131,7 +131,8 @@ struct EpiInject {
     // the two 16-byte halves of an octet in the order of its lane's parity:
     // with the slice's row pitch at 8 words mod 64, one read instruction then
     // starts at 16 distinct bank quartets (octets of one row side by side
-    // started at only the 8 multiples of 8, a 15-way conflict).
+    // started at only the 8 multiples of 8, a 15-way conflict). The halves
+    // are 16-byte aligned: the pitch (the tile width + 8) is a multiple of 4.
     const int hd2 = p.hd >> 1;
     const int opg = hw >> 3;  // octets per column group
     for (int e = threadIdx.x; e < kSlice * (BN / 16); e += blockDim.x) {
